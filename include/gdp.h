@@ -1,0 +1,167 @@
+/*
+ * gdp.h -- C ABI of the MI355X (gfx950) chunked Gated DeltaProduct prefill library.
+ *
+ * The operation (FlashInfer docs, "flashinfer.gdp_prefill.chunk_gated_delta_product",
+ * the recurrence display): for every sequence and every state head, per real
+ * token t the K x V state S is first scaled by alpha_t = exp(g_log_t); then for
+ * j = 0..n-1 on sub-token row r = t*n + j
+ *     v_new_r = beta_r * (v_r - S^T k_r),   S += k_r v_new_r^T;
+ * and after the last update o_t = scale * S^T q_t.  n = 1 is the gated delta rule.
+ * The argument list follows the Megatron Core API docs, core.ssm.ops.gdp.chunk,
+ * chunk_gated_delta_product_varlen (parameter list and the graph-capture note
+ * after it), with outputs, workspace and stream appended.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or synchronises, never reads device memory on
+ *     the host, and launches only on the stream it is given (a hipStream_t
+ *     passed as void*; NULL is the default stream).  A call is therefore
+ *     capturable into a HIP graph.
+ *   - Return value: GDP_OK (0) or a negative gdp_status.  No exception ever
+ *     crosses the ABI.  On failure gdp_last_error() returns a message (per
+ *     calling thread).  Errors are detected from shapes, dtypes, strides and
+ *     pointer ranges only; the contents of cu_seqlens, state_indices and
+ *     caller-built descriptors are not checked (that would need a device to
+ *     host read).  The kernels clamp what they index with them: sequence
+ *     bounds to [0, T], cache slots outside [0, S) and chunk-state rows past
+ *     the buffer are skipped, so bad contents give wrong numbers, never an
+ *     out-of-bounds access.
+ *   - Chunk size is fixed at 64 (Megatron Core page, the two-chunkings
+ *     paragraph and the chunk_states description).
+ */
+#ifndef GDP_H
+#define GDP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of gdp_tensor. */
+enum gdp_dtype { GDP_F32 = 0, GDP_BF16 = 1, GDP_I32 = 2, GDP_I64 = 3 };
+
+/* Return codes. */
+enum gdp_status {
+  GDP_OK = 0,
+  GDP_EINVAL = -1,       /* bad shape, dtype, stride, n < 1, Hv % Hqk != 0, missing argument */
+  GDP_EUNSUPPORTED = -2, /* valid request this build does not serve (head dims, dtype mix) */
+  GDP_EALIAS = -3,       /* an output overlaps an input or another output */
+  GDP_EWORKSPACE = -4,   /* workspace missing or smaller than gdp_workspace_bytes() */
+  GDP_EHIP = -5          /* a HIP launch failed; message from hipGetErrorString */
+};
+
+/* A strided view of device memory.  data == NULL means "absent" (None).
+ * shape/stride hold ndim valid entries; strides are in ELEMENTS.  The
+ * innermost dimension must be contiguous (stride 1). */
+typedef struct gdp_tensor {
+  void *data;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} gdp_tensor;
+
+/* Chunk descriptors of the two chunkings (Megatron Core page: chunk_indices,
+ * chunk_indices_dp, chunk_offsets).  Sequence i of length L_i has
+ * ceil(L_i/64) token chunks and ceil(n*L_i/64) expanded chunks.
+ *   chunk_indices    [nt_cap, 2]   int32 rows (i, c), sequence-major, c ascending,
+ *                                  rows past the real count hold (-1, -1)
+ *   chunk_indices_dp [ntdp_cap, 2] the same for the expanded stream
+ *   chunk_offsets    [N+1]         int32 exclusive prefix sums of token-chunk counts
+ *   chunk_offsets_dp [N+1]         the same for expanded-chunk counts
+ * All four arrays are device memory owned by the caller. */
+typedef struct gdp_descriptors {
+  int32_t *chunk_indices;
+  int32_t *chunk_indices_dp;
+  int32_t *chunk_offsets;
+  int32_t *chunk_offsets_dp;
+  int64_t nt_cap;
+  int64_t ntdp_cap;
+} gdp_descriptors;
+
+/* Host-only.  Capacities that bound the descriptor row counts for any
+ * cu_seqlens with N sequences and T real tokens:
+ *   nt_cap = floor((T + 63 N) / 64),  ntdp_cap = floor((n T + 63 N) / 64).
+ * Padding to these makes every grid depend on (T, N, n) only (Megatron Core
+ * page, the graph-capture note).  Returns GDP_EINVAL for negative sizes or n < 1. */
+int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t num_householder,
+                            int64_t *nt_cap, int64_t *ntdp_cap);
+
+/* Device.  Builds the descriptors of cu_seqlens ([N+1], int32 or int64,
+ * device, contiguous) into out->*, padded to out->nt_cap / out->ntdp_cap, with
+ * one kernel launch on `stream`.  T is the caller's real-token count; the
+ * capacities must be at least gdp_descriptor_capacity(T, N, n) (GDP_EINVAL
+ * otherwise).  Capturable; "built once per step" in the Megatron Core
+ * page's words. */
+int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t num_householder, int64_t T,
+                          const gdp_descriptors *out, void *stream);
+
+/* Host-only.  Workspace bytes gdp_chunk_prefill needs when it builds the
+ * descriptors itself (desc == NULL) for T real tokens and N sequences.  The
+ * other arguments are accepted for forward compatibility; the value depends
+ * on (T, N, n) today.  Returns 0 for invalid sizes. */
+size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk,
+                           int32_t Hv, int32_t K, int32_t V);
+
+/* Device.  The chunked GDP prefill forward pass.
+ *
+ * Inputs (T real tokens, N sequences, n = num_householder, Hqk q/k heads,
+ * Hv state heads = v/g/beta/output heads, head dims K and V):
+ *   q            [T, Hqk, K]      bf16 or f32; rows may be strided
+ *   k            [T*n, Hqk, K]    same dtype as q; rows t*n..t*n+n-1 belong to token t
+ *   v            [T*n, Hv, V]     same dtype as q
+ *   g_log        [T, Hv]          f32 log decays (alpha_t = exp(g_log_t))
+ *   beta         [T*n, Hv]        f32
+ *   cu_seqlens   [N+1]            int32 or int64, contiguous, required
+ *   scale        readout scale; 0 means K^-1/2 (FlashInfer page, scale)
+ *   initial_state [N, Hv, K, V]   f32 contiguous, or data == NULL for zeros
+ *   output_final_state            write final_state when nonzero
+ *   use_qk_l2norm                 divide every q row and k sub-token row by
+ *                                 sqrt(sum x^2 + 1e-6) inside the kernel
+ *   state_cache  [S, Hv, K, V]    f32 contiguous, or NULL; when given, the final
+ *                                 state of sequence i is written in place at
+ *                                 slot state_indices[i]; -1 writes nothing
+ *   state_indices [N]             int32 or int64; required with state_cache
+ *   return_chunk_states           write chunk_states when nonzero
+ * Outputs (caller-allocated device memory):
+ *   o            [T, Hv, V]       same dtype as q; rows may be strided
+ *   final_state  [N, Hv, K, V]    f32 contiguous; required iff output_final_state
+ *   chunk_states [R, Hv, K, V]    f32 contiguous, R >= gdp_descriptor_capacity's
+ *                                 nt_cap; row chunk_offsets[i] + c is the state of
+ *                                 sequence i entering its token chunk c, i.e. after
+ *                                 its first 64*c tokens (Megatron Core page,
+ *                                 return_chunk_states).  Rows past the real count
+ *                                 are left untouched.
+ *   desc         caller-built descriptors (gdp_build_descriptors) or NULL; when
+ *                NULL they are built into the workspace on `stream`
+ *   workspace    device scratch of workspace_bytes >= gdp_workspace_bytes(...)
+ *                when desc == NULL (may be NULL otherwise)
+ * Ownership/aliasing: no output may overlap an input or another output; in
+ * particular final_state must not alias initial_state, because one sequence's
+ * state is split over several workgroups (FlashInfer page, output_state).
+ * Supported today: K, V in {64, 128}; f32 inputs need K = 64 (GDP_EUNSUPPORTED
+ * otherwise).  Calls that overlap on one stream are ordered; calls on
+ * different streams sharing an output race. */
+int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                      const gdp_tensor *g_log, const gdp_tensor *beta,
+                      int32_t num_householder, const gdp_tensor *cu_seqlens, float scale,
+                      const gdp_tensor *initial_state, int32_t output_final_state,
+                      int32_t use_qk_l2norm, const gdp_tensor *state_cache,
+                      const gdp_tensor *state_indices, int32_t return_chunk_states,
+                      const gdp_tensor *o, const gdp_tensor *final_state,
+                      const gdp_tensor *chunk_states, const gdp_descriptors *desc,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *gdp_last_error(void);
+
+/* Library version string. */
+const char *gdp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDP_H */

@@ -1,0 +1,156 @@
+"""fp64 CPU oracle for chunked Gated DeltaProduct prefill.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The library path never imports this
+package, and this package imports nothing from the library.
+
+The arithmetic lives in ``gdp_oracle.c`` (a plain token-by-token recurrence,
+FlashInfer docs "flashinfer.gdp_prefill.chunk_gated_delta_product", the
+recurrence display); this module only marshals numpy arrays into it.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+brute-force Householder products, closed forms and invariants.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.compile_oracle()
+        _LIB = load(_build.LIB)
+    return _LIB
+
+
+def load(path):
+    """Load an oracle shared library (the real one or a test-built variant)."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.gdpo_prefill.restype = ctypes.c_int
+    lib.gdpo_prefill.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int,
+        dp, dp, dp, dp, dp, i64p, ctypes.c_double, dp, ctypes.c_int, dp, dp, dp,
+        i64p, dp, i64p, ctypes.c_int64, dp, ctypes.c_int]
+    lib.gdpo_descriptors.restype = ctypes.c_int
+    lib.gdpo_descriptors.argtypes = [i64p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_int64, i32p, i32p, i32p, i32p]
+    return lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a, ctype=ctypes.c_double):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads():
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def descriptor_capacity(T, N, n):
+    """Upper bounds on the token-stream and expanded-stream chunk counts
+    that depend only on (T, N, n): sum ceil(L/64) <= floor((T + 63 N)/64)."""
+    return (T + 63 * N) // 64, (n * T + 63 * N) // 64
+
+
+def descriptors(cu_seqlens, n, nt_cap=None, ntdp_cap=None, lib=None):
+    """Chunk descriptors of both chunkings (Megatron Core page, the
+    chunk_indices / chunk_indices_dp / chunk_offsets arguments)."""
+    lib = lib or _lib()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    T = int(cu[-1])
+    cap_t, cap_d = descriptor_capacity(T, N, n)
+    nt_cap = cap_t if nt_cap is None else nt_cap
+    ntdp_cap = cap_d if ntdp_cap is None else ntdp_cap
+    ci = np.zeros((max(nt_cap, 1), 2), np.int32)
+    cid = np.zeros((max(ntdp_cap, 1), 2), np.int32)
+    off = np.zeros(N + 1, np.int32)
+    offd = np.zeros(N + 1, np.int32)
+    rc = lib.gdpo_descriptors(_ptr(cu, ctypes.c_int64), N, n, nt_cap, ntdp_cap,
+                              _ptr(ci, ctypes.c_int32), _ptr(cid, ctypes.c_int32),
+                              _ptr(off, ctypes.c_int32), _ptr(offd, ctypes.c_int32))
+    if rc != 0:
+        raise ValueError("gdpo_descriptors rejected its arguments")
+    return {"chunk_indices": ci[:nt_cap], "chunk_indices_dp": cid[:ntdp_cap],
+            "chunk_offsets": off, "chunk_offsets_dp": offd}
+
+
+def prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None,
+            initial_state=None, use_qk_l2norm=False, return_chunk_states=False,
+            state_cache=None, state_indices=None, dump_vnew=False, threads=None,
+            lib=None):
+    """Run the fp64 token loop.
+
+    Shapes (leading batch dim of 1 not accepted here):
+      q [T, Hqk, K], k [T*n, Hqk, K], v [T*n, Hv, V], g_log [T, Hv] (log decays),
+      beta [T*n, Hv], cu_seqlens [N+1], initial_state [N, Hv, K, V] or None,
+      state_cache [S, Hv, K, V] (copied, then written at state_indices) or None.
+    Returns a dict with o, final_state and, on request, chunk_states,
+    chunk_offsets, state_cache and vnew (every e_r).
+    """
+    lib = lib or _lib()
+    n = int(num_householder)
+    q = _f64(q); k = _f64(k); v = _f64(v); g = _f64(g_log); b = _f64(beta)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    T, Hqk, K = q.shape
+    V = v.shape[2]
+    Hv = v.shape[1]
+    N = cu.shape[0] - 1
+    if k.shape != (T * n, Hqk, K) or v.shape != (T * n, Hv, V):
+        raise ValueError("k/v shapes do not match q and num_householder")
+    if g.shape != (T, Hv) or b.shape != (T * n, Hv):
+        raise ValueError("g_log/beta shapes")
+    s0 = None if initial_state is None else _f64(initial_state)
+    if s0 is not None and s0.shape != (N, Hv, K, V):
+        raise ValueError("initial_state shape")
+    o = np.zeros((T, Hv, V), np.float64)
+    fin = np.zeros((N, Hv, K, V), np.float64)
+    cs = offs = None
+    if return_chunk_states:
+        d = descriptors(cu, n, lib=lib)
+        offs = d["chunk_offsets"].astype(np.int64)
+        cs = np.zeros((int(offs[-1]), Hv, K, V), np.float64)
+    cache = slots = None
+    nslots = 0
+    if state_cache is not None:
+        cache = _f64(state_cache).copy()
+        slots = np.ascontiguousarray(np.asarray(state_indices, dtype=np.int64))
+        nslots = cache.shape[0]
+    vn = np.zeros((T * n, Hv, V), np.float64) if dump_vnew else None
+    sc = 0.0 if scale is None else float(scale)
+    rc = lib.gdpo_prefill(T, N, n, Hqk, Hv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                          _ptr(b), _ptr(cu, ctypes.c_int64), sc, _ptr(s0),
+                          int(bool(use_qk_l2norm)), _ptr(o), _ptr(fin), _ptr(cs),
+                          _ptr(offs, ctypes.c_int64), _ptr(cache),
+                          _ptr(slots, ctypes.c_int64), nslots, _ptr(vn),
+                          int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"gdpo_prefill failed with code {rc}")
+    out = {"o": o, "final_state": fin,
+           "scale": (1.0 / math.sqrt(K)) if sc == 0.0 else sc}
+    if return_chunk_states:
+        out["chunk_states"] = cs
+        out["chunk_offsets"] = offs
+    if cache is not None:
+        out["state_cache"] = cache
+    if vn is not None:
+        out["vnew"] = vn
+    return out
