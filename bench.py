@@ -1,0 +1,201 @@
+"""Throughput of chunked Gated DeltaProduct prefill on one MI355X.
+
+Workload: the long-context prefill -- 8 sequences x 65536 tokens (524,288 real
+tokens), n = 2 Householder rows per token, 16 q/k heads shared by 32 state
+heads, K = V = 128, bf16 q/k/v, fp32 g/beta/state, q/k L2-normalised in the
+kernel, random initial state, final state returned.  Inputs are seeded
+synthetic tensors resident in HBM before timing starts.
+
+One step = one whole forward pass over the batch: the descriptor build and
+the fused prefill kernel (both C-ABI calls, on torch's current stream).
+Prints one JSON line (metric, throughput in real tokens/s, roofline of the
+dominant kernel measured with HIP events on its stream, and the CPU oracle's
+rate on a bounded sample).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_long_context_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_deltaproduct_recurrence_amd", "csrc", "gdp_kernels.hip")
+
+
+def algorithmic_bytes(w):
+    """Each input read once, each output written once, no intermediates.
+    Per real token: q, k (Hqk*K*(1+n) bf16), v, o (Hv*V*(1+n) bf16), g, beta
+    (Hv*(1+n) fp32); per sequence: initial and final state (Hv*K*V fp32 each)."""
+    per_tok = 2 * w.K * w.Hqk * (1 + w.n) + 2 * w.V * w.Hv * (1 + w.n) + 4 * w.Hv * (1 + w.n)
+    per_seq = 4 * w.Hv * w.K * w.V * ((1 if w.init_std > 0 else 0) + (1 if w.output_final_state else 0))
+    return per_tok * w.T + per_seq * w.N
+
+
+def source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, tokens_per_seq, threads):
+    """The fp64 oracle on the first `tokens_per_seq` tokens of every sequence
+    (all heads), timed on the host cores; returns (record, oracle outputs)."""
+    import torch
+
+    import oracle
+    n = w.n
+    cu = inp["cu_seqlens"].cpu().numpy()
+    idx_t, idx_s = [], []
+    for i in range(w.N):
+        t0 = int(cu[i])
+        L = min(tokens_per_seq, int(cu[i + 1]) - t0)
+        idx_t.append(np.arange(t0, t0 + L))
+        idx_s.append(np.arange(t0 * n, (t0 + L) * n))
+    it = torch.tensor(np.concatenate(idx_t), device=inp["q"].device)
+    isub = torch.tensor(np.concatenate(idx_s), device=inp["q"].device)
+
+    def host(x, rows):
+        return x.index_select(0, rows).to("cpu", torch.float64).numpy()
+
+    q, k, v = host(inp["q"], it), host(inp["k"], isub), host(inp["v"], isub)
+    g, b = host(inp["g_log"], it), host(inp["beta"], isub)
+    lens = [len(x) for x in idx_t]
+    cus = np.concatenate([[0], np.cumsum(lens)])
+    s0 = inp["initial_state"].cpu().double().numpy() if inp["initial_state"] is not None else None
+    t_start = time.perf_counter()
+    ref = oracle.prefill(q, k, v, g, b, n, cus, initial_state=s0, use_qk_l2norm=w.l2norm_in_kernel,
+                         threads=threads)
+    dt = time.perf_counter() - t_start
+    rec = {"value": float(cus[-1] / dt), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {tokens_per_seq} tokens of each of the {w.N} sequences, all {w.Hv} heads "
+                     f"({int(cus[-1])} real tokens), fp64 token loop, {dt:.2f} s"}
+    return rec, ref, it
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, help="workload id (4 = long-context prefill)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample: tokens per sequence")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the op shards across GPUs by sequence or head with no exchange, which is not built here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_deltaproduct_recurrence_amd import binding as gdp
+    from gated_deltaproduct_recurrence_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.workload(args.workload)
+    inp = workloads.generate(w, dev)
+    T, N, n = w.T, w.N, w.n
+    Hqk, Hv, K, V = w.Hqk, w.Hv, w.K, w.V
+    o = torch.empty((T, Hv, V), dtype=w.dtype, device=dev)
+    fs = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if w.output_final_state else None
+    cache = inp["state_cache"]
+    cs = None
+    nt_cap, ntdp_cap = gdp.gdp_descriptor_capacity(T, N, n)
+    if w.return_chunk_states:
+        cs = torch.empty((nt_cap, Hv, K, V), dtype=torch.float32, device=dev)
+    desc = {"chunk_indices": torch.empty((max(nt_cap, 1), 2), dtype=torch.int32, device=dev),
+            "chunk_indices_dp": torch.empty((max(ntdp_cap, 1), 2), dtype=torch.int32, device=dev),
+            "chunk_offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+            "chunk_offsets_dp": torch.empty(N + 1, dtype=torch.int32, device=dev)}
+    d = gdp._descs(desc, nt_cap, ntdp_cap)
+    cu_t = gdp.as_gdp_tensor(inp["cu_seqlens"])
+    import ctypes
+    stream = torch.cuda.current_stream(dev)
+
+    def build_desc():
+        rc = gdp.LIB.gdp_build_descriptors(ctypes.byref(cu_t), n, T, ctypes.byref(d), stream.cuda_stream)
+        if rc != 0:
+            raise gdp.GdpError(rc, gdp.gdp_last_error())
+
+    def prefill():
+        gdp.gdp_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, inp["cu_seqlens"],
+                              inp["scale"] or 0.0, inp["initial_state"], w.output_final_state,
+                              w.l2norm_in_kernel, cache, inp["state_indices"], w.return_chunk_states, o, fs, cs,
+                              desc, None, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        build_desc()
+        prefill()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        build_desc()
+        ev[s][1].record(stream)
+        prefill()
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    fused_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    desc_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    value = T / (ms_per_step * 1e-3)
+
+    alg = algorithmic_bytes(w)
+    fused_avg_s = float(np.mean(fused_ms)) * 1e-3
+    achieved = alg / fused_avg_s / 1e9
+    traffic = measured_traffic()
+
+    line = {
+        "metric": "real tokens/s, chunked GDP prefill (bf16, d=128) + % of MFMA/HBM roofline",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "sequences": N, "tokens_per_sequence": w.lens[0] if N else 0,
+                   "real_tokens": T, "num_householder": n, "q_k_heads": Hqk, "state_heads": Hv, "K": K,
+                   "V": V, "use_qk_l2norm": w.l2norm_in_kernel, "initial_state": w.init_std > 0,
+                   "output_final_state": w.output_final_state},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdp_fused_kernel", "kernel_ms": float(np.mean(fused_ms)),
+                     "algorithmic_bytes_per_launch": alg},
+        "timing_detail": {"event_step_ms_median": float(np.median(step_ms)),
+                          "descriptor_kernel_ms": float(np.mean(desc_ms))},
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        rec, ref, it = cpu_baseline(inp, w, args.cpu_tokens, threads)
+        line["cpu_baseline"] = rec
+        got = o.index_select(0, it).to("cpu", torch.float64).numpy()
+        err = float(np.max(np.abs(got - ref["o"]))) / max(1.0, float(np.sqrt(np.mean(ref["o"] ** 2))))
+        print(f"bench: sampled outputs vs oracle err {err:.3e}", file=sys.stderr)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

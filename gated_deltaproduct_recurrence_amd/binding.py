@@ -1,0 +1,220 @@
+"""ctypes binding of libgdp.so (include/gdp.h), same names as the C ABI.
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.  If
+the library is missing this module raises on import -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdp.so")
+
+GDP_F32, GDP_BF16, GDP_I32, GDP_I64 = 0, 1, 2, 3
+GDP_OK, GDP_EINVAL, GDP_EUNSUPPORTED, GDP_EALIAS, GDP_EWORKSPACE, GDP_EHIP = 0, -1, -2, -3, -4, -5
+STATUS_NAMES = {GDP_EINVAL: "GDP_EINVAL", GDP_EUNSUPPORTED: "GDP_EUNSUPPORTED", GDP_EALIAS: "GDP_EALIAS",
+                GDP_EWORKSPACE: "GDP_EWORKSPACE", GDP_EHIP: "GDP_EHIP"}
+
+EXPORTED = ("gdp_descriptor_capacity", "gdp_build_descriptors", "gdp_workspace_bytes",
+            "gdp_chunk_prefill", "gdp_last_error", "gdp_version")
+
+
+class gdp_tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class gdp_descriptors(ctypes.Structure):
+    _fields_ = [("chunk_indices", ctypes.c_void_p), ("chunk_indices_dp", ctypes.c_void_p),
+                ("chunk_offsets", ctypes.c_void_p), ("chunk_offsets_dp", ctypes.c_void_p),
+                ("nt_cap", ctypes.c_int64), ("ntdp_cap", ctypes.c_int64)]
+
+
+class GdpError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(gated_deltaproduct_recurrence_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    T = ctypes.POINTER(gdp_tensor)
+    D = ctypes.POINTER(gdp_descriptors)
+    lib.gdp_descriptor_capacity.restype = ctypes.c_int
+    lib.gdp_descriptor_capacity.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.gdp_build_descriptors.restype = ctypes.c_int
+    lib.gdp_build_descriptors.argtypes = [T, ctypes.c_int32, ctypes.c_int64, D, ctypes.c_void_p]
+    lib.gdp_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdp_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.gdp_chunk_prefill.restype = ctypes.c_int
+    lib.gdp_chunk_prefill.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
+                                      ctypes.c_int32, T, T, ctypes.c_int32, T, T, T, D, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.gdp_last_error.restype = ctypes.c_char_p
+    lib.gdp_last_error.argtypes = []
+    lib.gdp_version.restype = ctypes.c_char_p
+    lib.gdp_version.argtypes = []
+    return lib
+
+
+LIB = _load()
+
+_DT = {torch.float32: GDP_F32, torch.bfloat16: GDP_BF16, torch.int32: GDP_I32, torch.int64: GDP_I64}
+
+
+def as_gdp_tensor(t):
+    """gdp_tensor view of a torch tensor (None -> absent)."""
+    g = gdp_tensor()
+    if t is None:
+        return g
+    if t.dim() > 4:
+        raise ValueError("at most 4 dims")
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    g.data = t.data_ptr() if t.numel() > 0 else None
+    g.dtype = _DT[t.dtype]
+    g.ndim = t.dim()
+    for d in range(t.dim()):
+        g.shape[d] = t.shape[d]
+        g.stride[d] = t.stride(d)
+    if t.numel() == 0:
+        # an empty tensor is still "present"; give it a non-null dummy address
+        g.data = 16
+    return g
+
+
+def _check(rc):
+    if rc != GDP_OK:
+        raise GdpError(rc, LIB.gdp_last_error().decode())
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# ---------------------------------------------------------------- C ABI names
+
+def gdp_version():
+    return LIB.gdp_version().decode()
+
+
+def gdp_last_error():
+    return LIB.gdp_last_error().decode()
+
+
+def gdp_descriptor_capacity(T, N, num_householder):
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(LIB.gdp_descriptor_capacity(T, N, num_householder, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V):
+    return int(LIB.gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V))
+
+
+def gdp_build_descriptors(cu_seqlens, num_householder, T, nt_cap=None, ntdp_cap=None):
+    """Device-built descriptors of both chunkings (int32 tensors), padded to capacity."""
+    N = cu_seqlens.shape[0] - 1
+    ct, cd = gdp_descriptor_capacity(T, N, num_householder)
+    nt_cap = ct if nt_cap is None else nt_cap
+    ntdp_cap = cd if ntdp_cap is None else ntdp_cap
+    dev = cu_seqlens.device
+    out = {"chunk_indices": torch.empty((max(nt_cap, 1), 2), dtype=torch.int32, device=dev),
+           "chunk_indices_dp": torch.empty((max(ntdp_cap, 1), 2), dtype=torch.int32, device=dev),
+           "chunk_offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+           "chunk_offsets_dp": torch.empty(N + 1, dtype=torch.int32, device=dev)}
+    d = _descs(out, nt_cap, ntdp_cap)
+    cu = as_gdp_tensor(cu_seqlens)
+    _check(LIB.gdp_build_descriptors(ctypes.byref(cu), num_householder, T, ctypes.byref(d), _stream(dev)))
+    out["chunk_indices"] = out["chunk_indices"][:nt_cap]
+    out["chunk_indices_dp"] = out["chunk_indices_dp"][:ntdp_cap]
+    return out
+
+
+def _descs(dct, nt_cap, ntdp_cap):
+    d = gdp_descriptors()
+    d.chunk_indices = dct["chunk_indices"].data_ptr()
+    d.chunk_indices_dp = dct["chunk_indices_dp"].data_ptr()
+    d.chunk_offsets = dct["chunk_offsets"].data_ptr()
+    d.chunk_offsets_dp = dct["chunk_offsets_dp"].data_ptr()
+    d.nt_cap = nt_cap
+    d.ntdp_cap = ntdp_cap
+    return d
+
+
+def gdp_chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=0.0, initial_state=None,
+                      output_final_state=False, use_qk_l2norm=False, state_cache=None, state_indices=None,
+                      return_chunk_states=False, o=None, final_state=None, chunk_states=None,
+                      descriptors=None, workspace=None, stream=None):
+    """Direct call of the C entry point with caller-allocated outputs (all torch tensors).
+
+    ``descriptors`` is a dict as returned by gdp_build_descriptors (or None, in
+    which case ``workspace`` must be a uint8 device tensor of at least
+    gdp_workspace_bytes(...) bytes)."""
+    args = [as_gdp_tensor(x) for x in (q, k, v, g_log, beta)]
+    cu = as_gdp_tensor(cu_seqlens)
+    s0 = as_gdp_tensor(initial_state)
+    cache = as_gdp_tensor(state_cache)
+    slots = as_gdp_tensor(state_indices)
+    ot, ft, ct = as_gdp_tensor(o), as_gdp_tensor(final_state), as_gdp_tensor(chunk_states)
+    dptr = None
+    if descriptors is not None:
+        d = _descs(descriptors, descriptors["chunk_indices"].shape[0], descriptors["chunk_indices_dp"].shape[0])
+        dptr = ctypes.byref(d)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _stream(q.device) if stream is None else stream
+    rc = LIB.gdp_chunk_prefill(*[ctypes.byref(a) for a in args], int(num_householder), ctypes.byref(cu),
+                               float(scale or 0.0), ctypes.byref(s0), int(bool(output_final_state)),
+                               int(bool(use_qk_l2norm)), ctypes.byref(cache), ctypes.byref(slots),
+                               int(bool(return_chunk_states)), ctypes.byref(ot), ctypes.byref(ft),
+                               ctypes.byref(ct), dptr, ws_ptr, ws_bytes, st)
+    _check(rc)
+
+
+# ---------------------------------------------------------------- convenience wrapper
+
+def chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None, initial_state=None,
+                  output_final_state=False, use_qk_l2norm=False, state_cache=None, state_indices=None,
+                  return_chunk_states=False, descriptors=None, out=None):
+    """Allocating front end in the Megatron Core argument order.
+
+    Accepts an optional leading batch dim of 1 on q/k/v/g/beta (THD packing).
+    Returns (o, final_state or None) or, with return_chunk_states,
+    (o, final_state or None, chunk_states, chunk_offsets): chunk_states has the
+    capacity row count; rows >= chunk_offsets[N] are unwritten padding.
+    """
+    squeeze = q.dim() == 4
+    if squeeze:
+        q, k, v, g_log, beta = q[0], k[0], v[0], g_log[0], beta[0]
+    T, Hqk, K = q.shape
+    Hv, V = v.shape[1], v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    dev = q.device
+    o = out if out is not None else torch.empty((T, Hv, V), dtype=q.dtype, device=dev)
+    fs = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    cs = None
+    ws = None
+    if return_chunk_states and descriptors is None:
+        descriptors = gdp_build_descriptors(cu_seqlens, num_householder, T)
+    if descriptors is None:
+        ws = torch.empty(max(gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V), 256),
+                         dtype=torch.uint8, device=dev)
+    if return_chunk_states:
+        nt_cap, _ = gdp_descriptor_capacity(T, N, num_householder)
+        cs = torch.empty((max(nt_cap, 1), Hv, K, V), dtype=torch.float32, device=dev)
+    gdp_chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale or 0.0, initial_state,
+                      output_final_state, use_qk_l2norm, state_cache, state_indices, return_chunk_states,
+                      o, fs, cs, descriptors, ws)
+    if squeeze:
+        o = o.unsqueeze(0)
+    if return_chunk_states:
+        return o, fs, cs, descriptors["chunk_offsets"]
+    return o, fs

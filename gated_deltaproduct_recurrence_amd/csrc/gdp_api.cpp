@@ -1,0 +1,308 @@
+// gdp_api.cpp -- C ABI of the chunked Gated DeltaProduct prefill library
+// (declared in include/gdp.h).  Host-side validation reads shapes, dtypes,
+// strides and pointer ranges only -- never device memory -- then launches on
+// the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdp.h"
+#include "gdp_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool present(const gdp_tensor *t) { return t != nullptr && t->data != nullptr; }
+
+int elem_size(int32_t dt) {
+  switch (dt) {
+    case GDP_F32: return 4;
+    case GDP_BF16: return 2;
+    case GDP_I32: return 4;
+    case GDP_I64: return 8;
+    default: return 0;
+  }
+}
+
+// Checks ndim, the exact shape and that the innermost stride is 1.
+int check_shape(const gdp_tensor *t, const char *name, int ndim, const int64_t *shape) {
+  if (t->ndim != ndim) return fail(GDP_EINVAL, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  for (int d = 0; d < ndim; ++d)
+    if (shape[d] >= 0 && t->shape[d] != shape[d])
+      return fail(GDP_EINVAL, "%s: dim %d is %lld, expected %lld", name, d, (long long)t->shape[d],
+                  (long long)shape[d]);
+  if (ndim > 0 && t->stride[ndim - 1] != 1)
+    return fail(GDP_EINVAL, "%s: innermost dimension must be contiguous", name);
+  return GDP_OK;
+}
+
+bool contiguous(const gdp_tensor *t) {
+  int64_t expect = 1;
+  for (int d = t->ndim - 1; d >= 0; --d) {
+    if (t->shape[d] != 1 && t->stride[d] != expect) return false;
+    expect *= t->shape[d];
+  }
+  return true;
+}
+
+// [lo, hi) byte range a tensor may touch (strides are non-negative here).
+struct Range { uintptr_t lo, hi; const char *name; };
+
+Range range_of(const gdp_tensor *t, const char *name) {
+  Range r{0, 0, name};
+  if (!present(t)) return r;
+  int64_t last = 0;
+  for (int d = 0; d < t->ndim; ++d) {
+    if (t->shape[d] == 0) return r;
+    last += (t->shape[d] - 1) * t->stride[d];
+  }
+  r.lo = (uintptr_t)t->data;
+  r.hi = r.lo + (uintptr_t)((last + 1) * elem_size(t->dtype));
+  return r;
+}
+
+bool overlap(const Range &a, const Range &b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool nonneg_strides(const gdp_tensor *t) {
+  for (int d = 0; d < t->ndim; ++d)
+    if (t->stride[d] < 0) return false;
+  return true;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t desc_bytes(int64_t N, int64_t nt_cap, int64_t ntdp_cap) {
+  return align256((size_t)nt_cap * 8) + align256((size_t)ntdp_cap * 8) + 2 * align256((size_t)(N + 1) * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdp_last_error(void) { return g_last_error.c_str(); }
+
+const char *gdp_version(void) { return "gdp-mi355x 0.1.0 (gfx950)"; }
+
+int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t n, int64_t *nt_cap, int64_t *ntdp_cap) {
+  if (T < 0 || N < 0 || n < 1) return fail(GDP_EINVAL, "descriptor capacity: bad sizes");
+  if (nt_cap) *nt_cap = (T + 63 * N) / 64;
+  if (ntdp_cap) *ntdp_cap = (n * T + 63 * N) / 64;
+  return GDP_OK;
+}
+
+size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V) {
+  (void)Hqk; (void)Hv; (void)K; (void)V;
+  int64_t ct, cd;
+  if (gdp_descriptor_capacity(T, N, n, &ct, &cd) != GDP_OK) return 0;
+  return desc_bytes(N, ct, cd);
+}
+
+int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t n, int64_t T, const gdp_descriptors *out,
+                          void *stream) {
+  if (!present(cu_seqlens) || !out) return fail(GDP_EINVAL, "build_descriptors: cu_seqlens and out are required");
+  if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1 || cu_seqlens->stride[0] != 1)
+    return fail(GDP_EINVAL, "cu_seqlens must be a contiguous [N+1] vector");
+  if (cu_seqlens->dtype != GDP_I32 && cu_seqlens->dtype != GDP_I64)
+    return fail(GDP_EINVAL, "cu_seqlens must be int32 or int64");
+  if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1");
+  const int64_t N = cu_seqlens->shape[0] - 1;
+  int64_t ct, cd;
+  if (gdp_descriptor_capacity(T, N, n, &ct, &cd) != GDP_OK) return GDP_EINVAL;
+  if (out->nt_cap < ct || out->ntdp_cap < cd)
+    return fail(GDP_EINVAL, "descriptor capacities (%lld, %lld) below the bound (%lld, %lld)",
+                (long long)out->nt_cap, (long long)out->ntdp_cap, (long long)ct, (long long)cd);
+  if (!out->chunk_indices || !out->chunk_indices_dp || !out->chunk_offsets || !out->chunk_offsets_dp)
+    return fail(GDP_EINVAL, "descriptor arrays must all be given");
+  gdp::DescArgs a;
+  a.cu = cu_seqlens->data;
+  a.cu_is64 = cu_seqlens->dtype == GDP_I64;
+  a.N = N;
+  a.n = n;
+  a.nt_cap = out->nt_cap;
+  a.ntdp_cap = out->ntdp_cap;
+  a.chunk_indices = out->chunk_indices;
+  a.chunk_indices_dp = out->chunk_indices_dp;
+  a.chunk_offsets = out->chunk_offsets;
+  a.chunk_offsets_dp = out->chunk_offsets_dp;
+  hipError_t e = gdp::launch_descriptors(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDP_EHIP, "descriptor launch: %s", hipGetErrorString(e));
+  return GDP_OK;
+}
+
+int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
+                      const gdp_tensor *beta, int32_t n, const gdp_tensor *cu_seqlens, float scale,
+                      const gdp_tensor *initial_state, int32_t output_final_state, int32_t use_qk_l2norm,
+                      const gdp_tensor *state_cache, const gdp_tensor *state_indices, int32_t return_chunk_states,
+                      const gdp_tensor *o, const gdp_tensor *final_state, const gdp_tensor *chunk_states,
+                      const gdp_descriptors *desc, void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  if (!present(q) || !present(k) || !present(v) || !present(g_log) || !present(beta) || !present(o))
+    return fail(GDP_EINVAL, "q, k, v, g_log, beta and o are required");
+  if (!present(cu_seqlens)) return fail(GDP_EINVAL, "cu_seqlens is required (varlen input only)");
+  if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1, got %d", n);
+  if (q->ndim != 3) return fail(GDP_EINVAL, "q must be [T, Hqk, K]");
+  if (v->ndim != 3) return fail(GDP_EINVAL, "v must be [T*n, Hv, V]");
+  const int64_t T = q->shape[0], Hqk = q->shape[1], K = q->shape[2];
+  const int64_t Hv = v->shape[1], V = v->shape[2];
+  if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1 || cu_seqlens->stride[0] != 1)
+    return fail(GDP_EINVAL, "cu_seqlens must be a contiguous [N+1] vector");
+  if (cu_seqlens->dtype != GDP_I32 && cu_seqlens->dtype != GDP_I64)
+    return fail(GDP_EINVAL, "cu_seqlens must be int32 or int64");
+  const int64_t N = cu_seqlens->shape[0] - 1;
+  if (Hqk < 1 || Hv < 1 || K < 1 || V < 1) return fail(GDP_EINVAL, "head counts and dims must be positive");
+  if (Hv % Hqk != 0) return fail(GDP_EINVAL, "Hv (%lld) must be a multiple of Hqk (%lld)", (long long)Hv, (long long)Hqk);
+  if (N > INT32_MAX || Hv > 65535) return fail(GDP_EINVAL, "too many sequences or heads");
+
+  const int32_t dt = q->dtype;
+  if (dt != GDP_F32 && dt != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q must be float32 or bfloat16");
+  if (k->dtype != dt || v->dtype != dt || o->dtype != dt)
+    return fail(GDP_EUNSUPPORTED, "q, k, v and o must share one dtype");
+  if (g_log->dtype != GDP_F32 || beta->dtype != GDP_F32)
+    return fail(GDP_EUNSUPPORTED, "g_log and beta must be float32");
+
+  int rc;
+  const int64_t sq[3] = {T, Hqk, K}, sk[3] = {T * n, Hqk, K}, sv[3] = {T * n, Hv, V};
+  const int64_t sg[2] = {T, Hv}, sb[2] = {T * n, Hv}, so[3] = {T, Hv, V};
+  if ((rc = check_shape(q, "q", 3, sq)) || (rc = check_shape(k, "k", 3, sk)) || (rc = check_shape(v, "v", 3, sv)) ||
+      (rc = check_shape(g_log, "g_log", 2, sg)) || (rc = check_shape(beta, "beta", 2, sb)) ||
+      (rc = check_shape(o, "o", 3, so)))
+    return rc;
+  for (const gdp_tensor *t : {q, k, v, g_log, beta, o})
+    if (!nonneg_strides(t)) return fail(GDP_EINVAL, "negative strides are not supported");
+
+  const int64_t st_shape[4] = {N, Hv, K, V};
+  if (present(initial_state)) {
+    if (initial_state->dtype != GDP_F32) return fail(GDP_EUNSUPPORTED, "initial_state must be float32");
+    if ((rc = check_shape(initial_state, "initial_state", 4, st_shape))) return rc;
+    if (!contiguous(initial_state)) return fail(GDP_EINVAL, "initial_state must be contiguous");
+  }
+  if (output_final_state) {
+    if (!present(final_state)) return fail(GDP_EINVAL, "output_final_state needs a final_state buffer");
+    if (final_state->dtype != GDP_F32) return fail(GDP_EUNSUPPORTED, "final_state must be float32");
+    if ((rc = check_shape(final_state, "final_state", 4, st_shape))) return rc;
+    if (!contiguous(final_state)) return fail(GDP_EINVAL, "final_state must be contiguous");
+  }
+  if (present(state_cache) != present(state_indices))
+    return fail(GDP_EINVAL, "state_cache and state_indices go together");
+  int64_t num_slots = 0;
+  if (present(state_cache)) {
+    if (state_cache->dtype != GDP_F32) return fail(GDP_EUNSUPPORTED, "state_cache must be float32");
+    const int64_t cs[4] = {-1, Hv, K, V};
+    if ((rc = check_shape(state_cache, "state_cache", 4, cs))) return rc;
+    if (!contiguous(state_cache)) return fail(GDP_EINVAL, "state_cache must be contiguous");
+    num_slots = state_cache->shape[0];
+    if (state_indices->dtype != GDP_I32 && state_indices->dtype != GDP_I64)
+      return fail(GDP_EINVAL, "state_indices must be int32 or int64");
+    const int64_t si[1] = {N};
+    if ((rc = check_shape(state_indices, "state_indices", 1, si))) return rc;
+  }
+  int64_t nt_cap, ntdp_cap;
+  gdp_descriptor_capacity(T, N, n, &nt_cap, &ntdp_cap);
+  if (return_chunk_states) {
+    if (!present(chunk_states)) return fail(GDP_EINVAL, "return_chunk_states needs a chunk_states buffer");
+    if (chunk_states->dtype != GDP_F32) return fail(GDP_EUNSUPPORTED, "chunk_states must be float32");
+    const int64_t cs[4] = {-1, Hv, K, V};
+    if ((rc = check_shape(chunk_states, "chunk_states", 4, cs))) return rc;
+    if (!contiguous(chunk_states)) return fail(GDP_EINVAL, "chunk_states must be contiguous");
+    if (chunk_states->shape[0] < nt_cap)
+      return fail(GDP_EINVAL, "chunk_states has %lld rows; %lld needed", (long long)chunk_states->shape[0],
+                  (long long)nt_cap);
+  }
+  if (!gdp::fused_supported(dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V))
+    return fail(GDP_EUNSUPPORTED, "head dims K=%lld V=%lld with %s inputs are not served", (long long)K,
+                (long long)V, dt == GDP_BF16 ? "bf16" : "f32");
+
+  // 16-byte vector loads of q/k/v rows need aligned bases and row strides.
+  const int es = elem_size(dt), eps = 16 / es;
+  for (const gdp_tensor *t : {q, k, v})
+    if (((uintptr_t)t->data & 15) || (t->stride[0] % eps) || (t->stride[1] % eps))
+      return fail(GDP_EUNSUPPORTED, "q/k/v need 16-byte aligned data and row/head strides");
+
+  // aliasing: outputs must not overlap inputs or each other
+  Range ins[] = {range_of(q, "q"), range_of(k, "k"), range_of(v, "v"), range_of(g_log, "g_log"),
+                 range_of(beta, "beta"), range_of(cu_seqlens, "cu_seqlens"),
+                 range_of(initial_state, "initial_state"), range_of(state_indices, "state_indices")};
+  Range outs[] = {range_of(o, "o"), output_final_state ? range_of(final_state, "final_state") : Range{0, 0, ""},
+                  present(state_cache) ? range_of(state_cache, "state_cache") : Range{0, 0, ""},
+                  return_chunk_states ? range_of(chunk_states, "chunk_states") : Range{0, 0, ""}};
+  for (const Range &ro : outs) {
+    for (const Range &ri : ins)
+      if (overlap(ro, ri)) return fail(GDP_EALIAS, "%s overlaps input %s", ro.name, ri.name);
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDP_EALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+
+  // descriptors: caller-built, or built into the workspace
+  gdp_descriptors local;
+  const gdp_descriptors *d = desc;
+  if (!d) {
+    const size_t need = desc_bytes(N, nt_cap, ntdp_cap);
+    if (!workspace || workspace_bytes < need)
+      return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
+    char *p = (char *)workspace;
+    local.chunk_indices = (int32_t *)p;
+    p += align256((size_t)nt_cap * 8);
+    local.chunk_indices_dp = (int32_t *)p;
+    p += align256((size_t)ntdp_cap * 8);
+    local.chunk_offsets = (int32_t *)p;
+    p += align256((size_t)(N + 1) * 4);
+    local.chunk_offsets_dp = (int32_t *)p;
+    local.nt_cap = nt_cap;
+    local.ntdp_cap = ntdp_cap;
+    gdp_tensor cu = *cu_seqlens;
+    if ((rc = gdp_build_descriptors(&cu, n, T, &local, stream)) != GDP_OK) return rc;
+    d = &local;
+  } else if (return_chunk_states && !d->chunk_offsets) {
+    return fail(GDP_EINVAL, "caller descriptors lack chunk_offsets");
+  }
+
+  gdp::FusedArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q->data; a.q_st = q->stride[0]; a.q_sh = q->stride[1];
+  a.k = k->data; a.k_st = k->stride[0]; a.k_sh = k->stride[1];
+  a.v = v->data; a.v_st = v->stride[0]; a.v_sh = v->stride[1];
+  a.g = (const float *)g_log->data; a.g_st = g_log->stride[0]; a.g_sh = g_log->stride[1];
+  a.beta = (const float *)beta->data; a.b_st = beta->stride[0]; a.b_sh = beta->stride[1];
+  a.cu = cu_seqlens->data; a.cu_is64 = cu_seqlens->dtype == GDP_I64;
+  a.T = T; a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv;
+  a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
+  a.l2norm = use_qk_l2norm ? 1 : 0;
+  a.s0 = present(initial_state) ? (const float *)initial_state->data : nullptr;
+  a.final_state = output_final_state ? (float *)final_state->data : nullptr;
+  if (present(state_cache)) {
+    a.cache = (float *)state_cache->data;
+    a.slots = state_indices->data;
+    a.slots_is64 = state_indices->dtype == GDP_I64;
+    a.num_slots = num_slots;
+  }
+  if (return_chunk_states) {
+    a.chunk_states = (float *)chunk_states->data;
+    a.cs_rows = chunk_states->shape[0];
+    a.chunk_offsets = d->chunk_offsets;
+  }
+  a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
+  hipError_t e = gdp::launch_fused(a, dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDP_EHIP, "prefill launch: %s", hipGetErrorString(e));
+  return GDP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// gdp_launch.h -- internal interface between the C ABI (gdp_api.cpp) and the
+// gfx950 kernels (gdp_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdp {
+
+// Arguments of the descriptor builder (both chunkings).
+struct DescArgs {
+  const void *cu;  // [N+1] int32 or int64
+  int cu_is64;
+  int64_t N;
+  int n;
+  int64_t nt_cap, ntdp_cap;
+  int32_t *chunk_indices, *chunk_indices_dp, *chunk_offsets, *chunk_offsets_dp;
+};
+
+// Arguments of the fused prefill kernel.  Strides are in elements.
+struct FusedArgs {
+  const void *q; int64_t q_st, q_sh;
+  const void *k; int64_t k_st, k_sh;
+  const void *v; int64_t v_st, v_sh;
+  const float *g; int64_t g_st, g_sh;
+  const float *beta; int64_t b_st, b_sh;
+  const void *cu; int cu_is64;
+  int64_t T;
+  int N, n, Hqk, Hv;
+  float scale;
+  int l2norm;
+  const float *s0;       // [N, Hv, K, V] or null
+  float *final_state;    // [N, Hv, K, V] or null
+  float *cache;          // [num_slots, Hv, K, V] or null
+  const void *slots; int slots_is64; int64_t num_slots;
+  float *chunk_states;   // [cs_rows, Hv, K, V] or null
+  int64_t cs_rows;
+  const int32_t *chunk_offsets;  // [N+1], needed with chunk_states
+  void *o; int64_t o_st, o_sh;
+};
+
+enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
+
+// Returns hipErrorInvalidValue for an instantiation this build does not have.
+bool fused_supported(int dtype, int K, int V);
+hipError_t launch_fused(const FusedArgs &a, int dtype, int K, int V, hipStream_t stream);
+hipError_t launch_descriptors(const DescArgs &a, hipStream_t stream);
+
+}  // namespace gdp

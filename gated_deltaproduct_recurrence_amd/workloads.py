@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for chunked GDP prefill.
+
+Input generation only -- this module holds none of the method's arithmetic.
+It serves both the GPU path's tests and benchmark and the oracle-side checks
+(the same tensors go to both).  The distributions are the ones stated for the
+five workloads: q, k ~ N(0,1) (unit-normalised rows when the in-kernel L2 norm
+is off), v ~ N(0,1), g_log = -softplus(N(0,1) - shift) (so alpha = exp(g_log)
+lies in (0,1)), beta = sigmoid(N(0,1)), initial states ~ N(0, sigma^2).
+
+Generation order is fixed: lengths and slot indices, q, k, v, g, beta,
+initial state, cache sentinel; seed = 1000 + workload id.  Large workloads are
+drawn on the device with torch's device generator.
+"""
+from dataclasses import dataclass, field
+
+import torch
+
+CHUNK = 64
+
+
+@dataclass
+class Workload:
+    name: str
+    lens: list
+    n: int
+    Hqk: int
+    Hv: int
+    K: int
+    V: int
+    dtype: torch.dtype
+    l2norm_in_kernel: bool
+    g_shift: float = 0.0
+    init_std: float = 0.0          # 0 -> no initial state
+    output_final_state: bool = True
+    scale: float = None
+    state_cache_slots: int = 0     # 0 -> no state cache
+    pad_sequences: int = 0         # zero-length sequences appended (slot -1)
+    return_chunk_states: bool = False
+    seed: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def T(self):
+        return int(sum(self.lens))
+
+    @property
+    def N(self):
+        return len(self.lens) + self.pad_sequences
+
+
+def _lens_c3(gen):
+    return (torch.randint(1, 4097, (64,), generator=gen, device=gen.device)).cpu().tolist()
+
+
+def workload(wid, device="cpu"):
+    """Workload `wid` (0..4) with its lengths drawn (for the random-length mix)."""
+    if wid == 0:
+        return Workload("single sequence L=128, n=2, H=2, K=V=64, fp32", [128], 2, 2, 2, 64, 64,
+                        torch.float32, False, scale=1.0 / 8.0, seed=1000)
+    if wid == 1:
+        return Workload("varlen lengths {37,64,200,511}, n=2, H=4, K=V=128, bf16", [37, 64, 200, 511], 2, 4, 4,
+                        128, 128, torch.bfloat16, False, init_std=0.1, seed=1001)
+    if wid == 2:
+        return Workload("single sequence L=32768, n=1, H=16, K=V=128, bf16, in-kernel L2 norm", [32768], 1, 16, 16,
+                        128, 128, torch.bfloat16, True, g_shift=2.0, output_final_state=False, seed=1002)
+    if wid == 3:
+        gen = torch.Generator(device="cpu").manual_seed(1003)
+        lens = _lens_c3(gen)
+        return Workload("serving mix: 64 sequences L~U[1,4096] + 4 padding, n=3, H=32, K=V=128, bf16, "
+                        "state cache + chunk states", lens, 3, 32, 32, 128, 128, torch.bfloat16, False,
+                        output_final_state=False, state_cache_slots=128, pad_sequences=4,
+                        return_chunk_states=True, seed=1003)
+    if wid == 4:
+        return Workload("long-context prefill: 8 x 65536 tokens, n=2, Hqk=16 / Hv=32, K=V=128, bf16, "
+                        "in-kernel L2 norm", [65536] * 8, 2, 16, 32, 128, 128, torch.bfloat16, True, g_shift=3.0,
+                        init_std=0.1, seed=1004)
+    raise ValueError(wid)
+
+
+def custom(lens, n, Hqk, Hv, K, V, dtype=torch.bfloat16, l2norm_in_kernel=False, g_shift=0.0, init_std=0.1,
+           seed=7, **kw):
+    return Workload("custom", list(lens), n, Hqk, Hv, K, V, dtype, l2norm_in_kernel, g_shift=g_shift,
+                    init_std=init_std, seed=seed, **kw)
+
+
+def _unit_rows(x):
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def generate(w: Workload, device="cpu"):
+    """Draw the inputs of workload `w` on `device`.  Returns a dict of tensors
+    and flags ready for the library's chunk_prefill front end."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    lens = list(w.lens) + [0] * w.pad_sequences
+    cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0).tolist()), dtype=torch.int32, device=dev)
+    N = len(lens)
+    slots = None
+    if w.state_cache_slots:
+        perm = torch.randperm(w.state_cache_slots, generator=torch.Generator().manual_seed(w.seed))
+        slots = torch.cat([perm[:N - w.pad_sequences], torch.full((w.pad_sequences,), -1)]).to(torch.int32).to(dev)
+    T, n = w.T, w.n
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    q = randn(T, w.Hqk, w.K)
+    k = randn(T * n, w.Hqk, w.K)
+    if not w.l2norm_in_kernel:
+        q = _unit_rows(q)
+        k = _unit_rows(k)
+    q = q.to(w.dtype)
+    k = k.to(w.dtype)
+    v = randn(T * n, w.Hv, w.V).to(w.dtype)
+    g = -torch.nn.functional.softplus(randn(T, w.Hv) - w.g_shift)
+    beta = torch.sigmoid(randn(T * n, w.Hv))
+    s0 = (w.init_std * randn(N, w.Hv, w.K, w.V)) if w.init_std > 0 else None
+    cache = randn(w.state_cache_slots, w.Hv, w.K, w.V) if w.state_cache_slots else None
+    return dict(q=q, k=k, v=v, g_log=g, beta=beta, num_householder=n, cu_seqlens=cu, scale=w.scale,
+                initial_state=s0, output_final_state=w.output_final_state, use_qk_l2norm=w.l2norm_in_kernel,
+                state_cache=cache, state_indices=slots, return_chunk_states=w.return_chunk_states)

@@ -1,0 +1,210 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gdp.h declares, and rejects bad arguments on the host (shapes, dtypes,
+strides, aliasing, workspace) before any launch.  Device pointers here are
+fake, well-aligned addresses that are never dereferenced: every case below
+fails validation, which reads shapes and pointer ranges only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdp.h")
+
+
+@pytest.fixture(scope="module")
+def b():
+    from gated_deltaproduct_recurrence_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdp_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(b):
+    names = declared_functions()
+    assert set(names) == set(b.EXPORTED), names
+    for name in names:
+        assert hasattr(b.LIB, name), f"{name} not exported"
+    assert "gfx950" in b.gdp_version()
+
+
+def test_capacity_and_workspace(b):
+    assert b.gdp_descriptor_capacity(812, 4, 2) == (16, 29)
+    assert b.gdp_descriptor_capacity(524288, 8, 2) == (8199, 16391)
+    assert b.gdp_workspace_bytes(812, 4, 2, 4, 4, 128, 128) >= (16 + 29) * 8 + 2 * 5 * 4
+    with pytest.raises(b.GdpError):
+        b.gdp_descriptor_capacity(10, 1, 0)
+
+
+class Fake:
+    """Allocates fake 4 KiB-aligned, non-overlapping "device" ranges."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def tensor(self, b, dtype, shape, strides=None, data=None):
+        t = b.gdp_tensor()
+        es = {b.GDP_F32: 4, b.GDP_BF16: 2, b.GDP_I32: 4, b.GDP_I64: 8}[dtype]
+        if strides is None:
+            strides, acc = [], 1
+            for d in reversed(shape):
+                strides.insert(0, acc)
+                acc *= d
+        size = es
+        for d, s in zip(shape, strides):
+            size += (d - 1) * s * es if d > 0 else 0
+        if data is None:
+            data = self.next
+            self.next += (size + 4095) // 4096 * 4096 + 4096
+        t.data = data
+        t.dtype = dtype
+        t.ndim = len(shape)
+        for i, (d, s) in enumerate(zip(shape, strides)):
+            t.shape[i] = d
+            t.stride[i] = s
+        return t
+
+
+def base_args(b, T=100, N=2, n=2, Hqk=2, Hv=4, K=128, V=128, dt=None):
+    f = Fake()
+    dt = b.GDP_BF16 if dt is None else dt
+    a = dict(
+        q=f.tensor(b, dt, [T, Hqk, K]), k=f.tensor(b, dt, [T * n, Hqk, K]), v=f.tensor(b, dt, [T * n, Hv, V]),
+        g_log=f.tensor(b, b.GDP_F32, [T, Hv]), beta=f.tensor(b, b.GDP_F32, [T * n, Hv]), n=n,
+        cu=f.tensor(b, b.GDP_I32, [N + 1]), scale=0.0, s0=f.tensor(b, b.GDP_F32, [N, Hv, K, V]), ofs=1, l2=0,
+        cache=b.gdp_tensor(), slots=b.gdp_tensor(), rcs=0, o=f.tensor(b, dt, [T, Hv, V]),
+        fs=f.tensor(b, b.GDP_F32, [N, Hv, K, V]), cs=b.gdp_tensor(), desc=None, ws=f.next, wsb=1 << 20)
+    a["fake"] = f
+    return a
+
+
+def call(b, a):
+    r = ctypes.byref
+    return b.LIB.gdp_chunk_prefill(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g_log"]), r(a["beta"]), a["n"], r(a["cu"]),
+                                   a["scale"], r(a["s0"]), a["ofs"], a["l2"], r(a["cache"]), r(a["slots"]),
+                                   a["rcs"], r(a["o"]), r(a["fs"]), r(a["cs"]), a["desc"], a["ws"], a["wsb"], None)
+
+
+def expect(b, a, code, fragment):
+    rc = call(b, a)
+    assert rc == code, (rc, b.gdp_last_error())
+    assert fragment in b.gdp_last_error(), b.gdp_last_error()
+
+
+def test_missing_required(b):
+    a = base_args(b)
+    a["cu"] = b.gdp_tensor()
+    expect(b, a, b.GDP_EINVAL, "cu_seqlens is required")
+    a = base_args(b)
+    a["q"] = b.gdp_tensor()
+    expect(b, a, b.GDP_EINVAL, "required")
+
+
+def test_householder_count(b):
+    a = base_args(b)
+    a["n"] = 0
+    expect(b, a, b.GDP_EINVAL, "num_householder")
+
+
+def test_head_grouping(b):
+    a = base_args(b, Hqk=3, Hv=4)
+    expect(b, a, b.GDP_EINVAL, "multiple of Hqk")
+
+
+def test_shape_mismatch(b):
+    a = base_args(b)
+    a["k"] = a["fake"].tensor(b, b.GDP_BF16, [150, 2, 128])
+    expect(b, a, b.GDP_EINVAL, "k: dim 0")
+    a = base_args(b)
+    a["beta"] = a["fake"].tensor(b, b.GDP_F32, [100, 4])
+    expect(b, a, b.GDP_EINVAL, "beta: dim 0")
+
+
+def test_dtype_rules(b):
+    a = base_args(b)
+    a["k"] = a["fake"].tensor(b, b.GDP_F32, [200, 2, 128])
+    expect(b, a, b.GDP_EUNSUPPORTED, "share one dtype")
+    a = base_args(b)
+    a["beta"] = a["fake"].tensor(b, b.GDP_BF16, [200, 4])
+    expect(b, a, b.GDP_EUNSUPPORTED, "float32")
+
+
+def test_unsupported_head_dims(b):
+    a = base_args(b, K=96, V=96)
+    expect(b, a, b.GDP_EUNSUPPORTED, "K=96")
+    a = base_args(b, K=128, V=128, dt=b.GDP_F32)
+    expect(b, a, b.GDP_EUNSUPPORTED, "f32")
+
+
+def test_inner_stride(b):
+    a = base_args(b)
+    a["q"] = a["fake"].tensor(b, b.GDP_BF16, [100, 2, 128], strides=[512, 256, 2])
+    expect(b, a, b.GDP_EINVAL, "innermost")
+
+
+def test_misaligned_row_stride(b):
+    a = base_args(b)
+    a["q"] = a["fake"].tensor(b, b.GDP_BF16, [100, 2, 128], strides=[260, 130, 1])
+    expect(b, a, b.GDP_EUNSUPPORTED, "16-byte")
+
+
+def test_final_state_aliasing_initial_state(b):
+    a = base_args(b)
+    a["fs"] = a["fake"].tensor(b, b.GDP_F32, [2, 4, 128, 128], data=a["s0"].data)
+    expect(b, a, b.GDP_EALIAS, "final_state overlaps input initial_state")
+
+
+def test_output_overlaps_input(b):
+    a = base_args(b)
+    a["o"] = a["fake"].tensor(b, b.GDP_BF16, [100, 4, 128], data=a["v"].data + 64)
+    expect(b, a, b.GDP_EALIAS, "o overlaps input v")
+
+
+def test_outputs_overlap_each_other(b):
+    a = base_args(b)
+    a["cache"] = a["fake"].tensor(b, b.GDP_F32, [4, 4, 128, 128], data=a["fs"].data)
+    a["slots"] = a["fake"].tensor(b, b.GDP_I32, [2])
+    expect(b, a, b.GDP_EALIAS, "overlaps")
+
+
+def test_cache_needs_indices(b):
+    a = base_args(b)
+    a["cache"] = a["fake"].tensor(b, b.GDP_F32, [4, 4, 128, 128])
+    expect(b, a, b.GDP_EINVAL, "go together")
+
+
+def test_final_state_buffer_required(b):
+    a = base_args(b)
+    a["fs"] = b.gdp_tensor()
+    expect(b, a, b.GDP_EINVAL, "final_state buffer")
+
+
+def test_chunk_states_capacity(b):
+    a = base_args(b)
+    a["rcs"] = 1
+    a["cs"] = a["fake"].tensor(b, b.GDP_F32, [2, 4, 128, 128])
+    expect(b, a, b.GDP_EINVAL, "rows")
+
+
+def test_workspace_too_small(b):
+    a = base_args(b)
+    a["wsb"] = 8
+    expect(b, a, b.GDP_EWORKSPACE, "workspace")
+    a = base_args(b)
+    a["ws"] = None
+    expect(b, a, b.GDP_EWORKSPACE, "workspace")
+
+
+def test_build_descriptors_capacity_check(b):
+    f = Fake()
+    cu = f.tensor(b, b.GDP_I32, [5])
+    d = b.gdp_descriptors()
+    d.chunk_indices = d.chunk_indices_dp = d.chunk_offsets = d.chunk_offsets_dp = f.next
+    d.nt_cap, d.ntdp_cap = 15, 29
+    rc = b.LIB.gdp_build_descriptors(ctypes.byref(cu), 2, 812, ctypes.byref(d), None)
+    assert rc == b.GDP_EINVAL and "below the bound" in b.gdp_last_error()
