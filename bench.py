@@ -128,6 +128,7 @@ def main():
             "chunk_offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
             "chunk_offsets_dp": torch.empty(N + 1, dtype=torch.int32, device=dev)}
     d = gdp._descs(desc, nt_cap, ntdp_cap)
+    ws = torch.empty(gdp.gdp_workspace_bytes(T, N, n, Hqk, Hv, K, V, w.dtype), dtype=torch.uint8, device=dev)
     cu_t = gdp.as_gdp_tensor(inp["cu_seqlens"])
     import ctypes
     stream = torch.cuda.current_stream(dev)
@@ -141,7 +142,7 @@ def main():
         gdp.gdp_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, inp["cu_seqlens"],
                               inp["scale"] or 0.0, inp["initial_state"], w.output_final_state,
                               w.l2norm_in_kernel, cache, inp["state_indices"], w.return_chunk_states, o, fs, cs,
-                              desc, None, stream=stream.cuda_stream)
+                              desc, ws, stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
         build_desc()

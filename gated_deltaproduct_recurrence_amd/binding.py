@@ -52,7 +52,7 @@ def _load(path=LIB_PATH):
     lib.gdp_build_descriptors.argtypes = [T, ctypes.c_int32, ctypes.c_int64, D, ctypes.c_void_p]
     lib.gdp_workspace_bytes.restype = ctypes.c_size_t
     lib.gdp_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.gdp_chunk_prefill.restype = ctypes.c_int
     lib.gdp_chunk_prefill.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
                                       ctypes.c_int32, T, T, ctypes.c_int32, T, T, T, D, ctypes.c_void_p,
@@ -115,8 +115,8 @@ def gdp_descriptor_capacity(T, N, num_householder):
     return a.value, b.value
 
 
-def gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V):
-    return int(LIB.gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V))
+def gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, dtype=torch.bfloat16):
+    return int(LIB.gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, _DT[dtype]))
 
 
 def gdp_build_descriptors(cu_seqlens, num_householder, T, nt_cap=None, ntdp_cap=None):
@@ -155,9 +155,9 @@ def gdp_chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=0
                       descriptors=None, workspace=None, stream=None):
     """Direct call of the C entry point with caller-allocated outputs (all torch tensors).
 
-    ``descriptors`` is a dict as returned by gdp_build_descriptors (or None, in
-    which case ``workspace`` must be a uint8 device tensor of at least
-    gdp_workspace_bytes(...) bytes)."""
+    ``descriptors`` is a dict as returned by gdp_build_descriptors or None;
+    ``workspace`` is a uint8 device tensor of at least gdp_workspace_bytes(...)
+    bytes."""
     args = [as_gdp_tensor(x) for x in (q, k, v, g_log, beta)]
     cu = as_gdp_tensor(cu_seqlens)
     s0 = as_gdp_tensor(initial_state)
@@ -201,12 +201,10 @@ def chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None,
     o = out if out is not None else torch.empty((T, Hv, V), dtype=q.dtype, device=dev)
     fs = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
     cs = None
-    ws = None
     if return_chunk_states and descriptors is None:
         descriptors = gdp_build_descriptors(cu_seqlens, num_householder, T)
-    if descriptors is None:
-        ws = torch.empty(max(gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V), 256),
-                         dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, q.dtype), 256),
+                     dtype=torch.uint8, device=dev)
     if return_chunk_states:
         nt_cap, _ = gdp_descriptor_capacity(T, N, num_householder)
         cs = torch.empty((max(nt_cap, 1), Hv, K, V), dtype=torch.float32, device=dev)

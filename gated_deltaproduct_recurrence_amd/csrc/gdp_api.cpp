@@ -106,11 +106,14 @@ int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t n, int64_t *nt_cap, in
   return GDP_OK;
 }
 
-size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V) {
-  (void)Hqk; (void)Hv; (void)K; (void)V;
+size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V,
+                           int32_t dtype) {
+  (void)Hqk; (void)K; (void)V;
   int64_t ct, cd;
+  if (Hv < 1 || (dtype != GDP_F32 && dtype != GDP_BF16)) return 0;
   if (gdp_descriptor_capacity(T, N, n, &ct, &cd) != GDP_OK) return 0;
-  return desc_bytes(N, ct, cd);
+  return align256(gdp::wy_buffer_bytes(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, cd, Hv)) +
+         desc_bytes(N, ct, cd);
 }
 
 int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t n, int64_t T, const gdp_descriptors *out,
@@ -224,15 +227,21 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
       return fail(GDP_EINVAL, "chunk_states has %lld rows; %lld needed", (long long)chunk_states->shape[0],
                   (long long)nt_cap);
   }
-  if (!gdp::fused_supported(dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V))
+  if (!gdp::prefill_supported(dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V))
     return fail(GDP_EUNSUPPORTED, "head dims K=%lld V=%lld with %s inputs are not served", (long long)K,
                 (long long)V, dt == GDP_BF16 ? "bf16" : "f32");
 
-  // 16-byte vector loads of q/k/v rows need aligned bases and row strides.
+  // 16-byte vector loads of q/k/v rows need aligned bases and row strides;
+  // the kernels address the 64 rows of a chunk with 32-bit byte offsets.
   const int es = elem_size(dt), eps = 16 / es;
   for (const gdp_tensor *t : {q, k, v})
     if (((uintptr_t)t->data & 15) || (t->stride[0] % eps) || (t->stride[1] % eps))
       return fail(GDP_EUNSUPPORTED, "q/k/v need 16-byte aligned data and row/head strides");
+  if (((uintptr_t)o->data & 7) || (o->stride[0] % 4) || (o->stride[1] % 4))
+    return fail(GDP_EUNSUPPORTED, "o needs 8-byte aligned data and row/head strides that are multiples of 4");
+  for (const gdp_tensor *t : {q, k, v, o, g_log, beta})
+    if (t->stride[0] * 64 * elem_size(t->dtype) >= ((int64_t)1 << 31))
+      return fail(GDP_EUNSUPPORTED, "row strides above 2^31 / 64 bytes are not served");
 
   // aliasing: outputs must not overlap inputs or each other
   Range ins[] = {range_of(q, "q"), range_of(k, "k"), range_of(v, "v"), range_of(g_log, "g_log"),
@@ -249,15 +258,17 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return fail(GDP_EALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
 
-  // descriptors: caller-built, or built into the workspace
+  // workspace: the WY matrices, then (when the caller passes none) the descriptors
+  const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
+  const size_t wy_bytes = align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv));
+  const size_t need = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap));
+  if (!workspace || workspace_bytes < need)
+    return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
   gdp_descriptors local;
   const gdp_descriptors *d = desc;
   if (!d) {
-    const size_t need = desc_bytes(N, nt_cap, ntdp_cap);
-    if (!workspace || workspace_bytes < need)
-      return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-    if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
-    char *p = (char *)workspace;
+    char *p = (char *)workspace + wy_bytes;
     local.chunk_indices = (int32_t *)p;
     p += align256((size_t)nt_cap * 8);
     local.chunk_indices_dp = (int32_t *)p;
@@ -270,11 +281,13 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
     gdp_tensor cu = *cu_seqlens;
     if ((rc = gdp_build_descriptors(&cu, n, T, &local, stream)) != GDP_OK) return rc;
     d = &local;
-  } else if (return_chunk_states && !d->chunk_offsets) {
-    return fail(GDP_EINVAL, "caller descriptors lack chunk_offsets");
+  } else {
+    if (!d->chunk_indices_dp || !d->chunk_offsets || !d->chunk_offsets_dp)
+      return fail(GDP_EINVAL, "caller descriptors need chunk_indices_dp, chunk_offsets and chunk_offsets_dp");
+    if (d->ntdp_cap < 0) return fail(GDP_EINVAL, "caller descriptors: negative capacity");
   }
 
-  gdp::FusedArgs a;
+  gdp::PrefillArgs a;
   std::memset(&a, 0, sizeof a);
   a.q = q->data; a.q_st = q->stride[0]; a.q_sh = q->stride[1];
   a.k = k->data; a.k_st = k->stride[0]; a.k_sh = k->stride[1];
@@ -296,11 +309,15 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   if (return_chunk_states) {
     a.chunk_states = (float *)chunk_states->data;
     a.cs_rows = chunk_states->shape[0];
-    a.chunk_offsets = d->chunk_offsets;
   }
+  a.chunk_offsets = d->chunk_offsets;
+  a.chunk_indices_dp = d->chunk_indices_dp;
+  a.chunk_offsets_dp = d->chunk_offsets_dp;
+  a.ntdp_rows = d->ntdp_cap;
+  a.tws = workspace;
+  a.tws_rows = ntdp_cap;
   a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
-  hipError_t e = gdp::launch_fused(a, dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V,
-                                   (hipStream_t)stream);
+  hipError_t e = gdp::launch_prefill(a, idt, (int)K, (int)V, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDP_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return GDP_OK;
 }

@@ -4,26 +4,31 @@
 // recurrence display; Megatron Core API docs, core.ssm.ops.gdp.chunk, stage list):
 // per token the K x V state S decays by alpha_t, then takes n beta-gated
 // Householder updates from the sub-token rows t*n..t*n+n-1, then is read out.
-// The chunked form used here works on 64-row chunks of the Householder-expanded
-// stream.  For an expanded chunk with start state S0, rows r, base-2 cumulative
-// log decay G_r (decays sit on the first sub-row of each token, Megatron stage 1),
+// The chunked form works on 64-row chunks of the Householder-expanded stream.
+// For an expanded chunk with start state S0, rows r, base-2 cumulative log
+// decay G_r (decays sit on the first sub-row of each token: Megatron stage 1)
 // and A[r,i] = beta_r 2^(G_r - G_i) k_r.k_i for i < r:
 //     T = (I + A)^-1                                  (WY step, Megatron stage 2)
-//     E = T (diag(beta) V - diag(beta 2^G) K S0)      (= U - W S0, the v_new rows)
+//     E = T (diag(beta) V - diag(beta 2^G) K S0)      (= U - W S0: the v_new rows)
 //     S_end = 2^G_last S0 + K^T diag(2^(G_last - G)) E  (state sweep, stage 3)
-// and for the token chunk c (n expanded chunks) with start state h_c,
+// and for token chunk c (n expanded chunks) with start state h_c,
 //     o_t = scale (2^Gt_t q_t^T h_c + sum_{r: tok(r) <= t} 2^(Gt_t - Gt_tok(r)) (q_t.k_r) e_r)
 // (output combine, stage 4), Gt being the token-stream cumulative decay.
 //
-// Design for CDNA4: one workgroup (4 waves) owns one (sequence, state head,
-// V-tile) chain and walks its chunks in order, so S never leaves the CU.  S is
-// held fp32 in MFMA accumulators; wave w owns a 16*NB-column slab of S, so the
-// S-dependent products (K S, Q S) take S straight from registers as the B
-// operand and the sweep needs no cross-wave exchange.  Chunk-local operands
-// (K, K^T, Q, V, T, P) are staged in LDS and read as A operands.  All
-// contractions run on v_mfma_f32_16x16x32_bf16 (bf16 inputs) or
-// v_mfma_f32_16x16x4_f32 (f32 inputs) with fp32 accumulation; the 64 x 64
-// triangular inverse is solved in fp32.
+// Kernels, in launch order on one stream:
+//   gdp_descriptor_kernel  both chunkings' descriptors (one workgroup)
+//   gdp_wy_kernel          one workgroup per (expanded chunk, q/k head): the Gram
+//                          matrix once, then per state head of the group the
+//                          64 x 64 inverse T in fp32 (LDS), stored in bf16/f32 in
+//                          MFMA-fragment order
+//   gdp_scan_kernel        one workgroup per (sequence, state head, V-tile): walks
+//                          the chunks in order with S in fp32 MFMA accumulators
+//                          (wave w owns a 16*NB-column slab), computing E = T R,
+//                          the state update and the outputs; the next chunk's
+//                          k/v/q rows are prefetched into registers and LDS is
+//                          double-buffered, so each chunk costs two barriers.
+// Every contraction is an MFMA: v_mfma_f32_16x16x32_bf16 for bf16 inputs,
+// v_mfma_f32_16x16x4_f32 for f32 inputs and for the fp32 triangular inverse.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -103,32 +108,27 @@ __device__ __forceinline__ void from_acc(Frag<float> &f, f32x4 lo, f32x4 hi) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { f.v[i] = lo[i]; f.v[4 + i] = hi[i]; }
 }
+// a fragment stored contiguously (8 elements per lane) in global memory
+__device__ __forceinline__ void load_frag(Frag<bf16> &f, const bf16 *p) { f.v = *(const bf16x8 *)p; }
+__device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
+  f32x4 lo = *(const f32x4 *)p, hi = *(const f32x4 *)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f.v[i] = lo[i]; f.v[4 + i] = hi[i]; }
+}
+__device__ __forceinline__ void store_frag(bf16 *p, const Frag<float> &f) {
+  bf16x8 x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (bf16)f.v[i];
+  *(bf16x8 *)p = x;
+}
+__device__ __forceinline__ void store_frag(float *p, const Frag<float> &f) {
+  *(f32x4 *)p = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+  *(f32x4 *)(p + 4) = f32x4{f.v[4], f.v[5], f.v[6], f.v[7]};
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
-
-// ---------------------------------------------------------------- shared memory
-
-template <typename T, int K, int NB> struct Smem {
-  static constexpr int EPS = 16 / (int)sizeof(T);  // elements per 16-byte segment
-  static constexpr int BV = 64 * NB;                // state columns per workgroup
-  static constexpr int LDK = K + EPS;               // k, q rows
-  static constexpr int LDKT = CH + EPS;             // k^T rows
-  static constexpr int LDV = BV + EPS;              // v rows
-  static constexpr int LDC = CH + EPS;              // T, P rows (type T)
-  static constexpr int LDA = CH + 4;                // A and fp32 T rows
-  static constexpr bool kTinF32 = sizeof(T) == 4;   // fp32 inputs: T is read from tf
-  T k[CH * LDK];
-  T kt[K * LDKT];
-  T q[CH * LDK];
-  T v[CH * LDV];
-  float a[CH * LDA];
-  float tf[CH * LDA];
-  T t[kTinF32 ? 4 : CH * LDC];
-  T p[CH * LDC];
-  float gtok[CH], gdp[CH], beta[CH], rk[CH], rq[CH];
-};
 
 // ---------------------------------------------------------------- small helpers
 
@@ -136,11 +136,57 @@ __device__ __forceinline__ int64_t load_index(const void *p, int is64, int64_t i
   return is64 ? ((const int64_t *)p)[i] : (int64_t)((const int32_t *)p)[i];
 }
 
-union Seg16 {
-  uint4 u;
-  bf16 h[8];
-  float f[4];
-};
+__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &s, int i) {
+  return i == 0 ? s.x : (i == 1 ? s.y : (i == 2 ? s.z : s.w));
+}
+
+// sum of squares of a 16-byte segment of T values (kept as raw words so that
+// the compiler does not split a prefetched segment at its load)
+template <typename T> __device__ __forceinline__ float seg_sumsq(const uint4 &s) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = word_of(s, i);
+    if constexpr (sizeof(T) == 2) {
+      const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+      a = fmaf(lo, lo, a);
+      a = fmaf(hi, hi, a);
+    } else {
+      const float x = __uint_as_float(w);
+      a = fmaf(x, x, a);
+    }
+  }
+  return a;
+}
+
+// Element e of four row segments r[0..3], stored as the 4-element run
+// d[0..3] of a transposed tile.
+template <typename T> __device__ __forceinline__ void store_col4(T *d, const uint4 (&r)[4], int e) {
+  if constexpr (sizeof(T) == 2) {
+    const int wi = e >> 1;
+    const uint32_t w0 = word_of(r[0], wi), w1 = word_of(r[1], wi), w2 = word_of(r[2], wi), w3 = word_of(r[3], wi);
+    uint2 x;
+    if (e & 1) {
+      x.x = (w0 >> 16) | (w1 & 0xffff0000u);
+      x.y = (w2 >> 16) | (w3 & 0xffff0000u);
+    } else {
+      x.x = (w0 & 0xffffu) | (w1 << 16);
+      x.y = (w2 & 0xffffu) | (w3 << 16);
+    }
+    *(uint2 *)d = x;
+  } else {
+    *(uint4 *)d = uint4{word_of(r[0], e), word_of(r[1], e), word_of(r[2], e), word_of(r[3], e)};
+  }
+}
 
 // rows [0, 64) x D columns of a strided global matrix into LDS (row stride ld);
 // rows >= nvalid are zero.  One 16-byte segment per thread per step.
@@ -153,37 +199,6 @@ __device__ __forceinline__ void load_rows(T *dst, const T *src, int64_t rs, int 
     uint4 x = {0u, 0u, 0u, 0u};
     if (r < nvalid) x = *(const uint4 *)(src + (int64_t)r * rs + s * EPS);
     *(uint4 *)(dst + r * LD + s * EPS) = x;
-  }
-}
-
-// k rows into LDS twice: row-major (sk) and transposed (skt, row = key dim).
-// Each work unit is 4 rows x one 16-byte segment, so the transposed copy is
-// written as 4-element runs.
-template <typename T, int K, int LDK, int LDKT>
-__device__ __forceinline__ void load_k_both(T *sk, T *skt, const T *src, int64_t rs, int nvalid,
-                                            int tid) {
-  constexpr int EPS = 16 / (int)sizeof(T), CB = K / EPS;
-  for (int u = tid; u < (CH / 4) * CB; u += NTHR) {
-    const int rb = u / CB, cb = u % CB;
-    Seg16 x[4];
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int r = 4 * rb + qd;
-      x[qd].u = uint4{0u, 0u, 0u, 0u};
-      if (r < nvalid) x[qd].u = *(const uint4 *)(src + (int64_t)r * rs + cb * EPS);
-      *(uint4 *)(sk + r * LDK + cb * EPS) = x[qd].u;
-    }
-#pragma unroll
-    for (int e = 0; e < EPS; ++e) {
-      T *d = skt + (cb * EPS + e) * LDKT + 4 * rb;
-      if constexpr (sizeof(T) == 2) {
-        bf16x4 w = {x[0].h[e], x[1].h[e], x[2].h[e], x[3].h[e]};
-        *(bf16x4 *)d = w;
-      } else {
-        f32x4 w = {x[0].f[e], x[1].f[e], x[2].f[e], x[3].f[e]};
-        *(f32x4 *)d = w;
-      }
-    }
   }
 }
 
@@ -204,38 +219,37 @@ __device__ __forceinline__ void rows_rstd(const T *base, int ld, float *out, int
 
 // ---------------------------------------------------------------- WY inverse
 //
-// T = (I + A)^-1 for the strictly lower-triangular 64 x 64 A in sm.a, in fp32.
-// Diagonal 16 x 16 blocks by forward substitution (wave 0, one lane per
-// column of each block), then the off-diagonal blocks by
-//     T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb,
-// one sweep per block distance a - b, on fp32 MFMA.  The result (zeros above
-// the diagonal blocks) goes to sm.t (bf16) or stays in sm.tf (f32).
-template <typename T, int K, int NB>
-__device__ __forceinline__ void wy_inverse(Smem<T, K, NB> &sm, int tid) {
-  using S = Smem<T, K, NB>;
-  constexpr int LDA = S::LDA;
+// T = (I + A)^-1 for the strictly lower-triangular 64 x 64 A (fp32, LDS), into
+// Tf (fp32, LDS, zeros above the diagonal blocks).  Wave w inverts diagonal
+// 16 x 16 block w by forward substitution, one lane per column, carrying the
+// partial sums of all later rows so that each row needs one dependent step.
+// The off-diagonal blocks follow from T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb,
+// one sweep per block distance a - b, on fp32 MFMA.
+template <int LDA>
+__device__ __forceinline__ void wy_inverse(const float *A, float *Tf, int tid) {
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  if (w == 0) {
-    const int bk = lg, j = lr;
-    const float *A = sm.a + (16 * bk) * LDA + 16 * bk;
-    float x[16];
+  for (int idx = tid; idx < 6 * 256; idx += NTHR) {  // blocks strictly above the diagonal
+    const int blk = idx >> 8, e = idx & 255;
+    const int a = (blk < 3) ? 0 : (blk < 5 ? 1 : 2);
+    const int b = (blk < 3) ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+    Tf[(16 * a + (e >> 4)) * LDA + 16 * b + (e & 15)] = 0.f;
+  }
+  {
+    const int j = lr;
+    const float *Ab = A + (16 * w) * LDA + 16 * w;
+    float acc[16], x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = 0.f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s = fmaf(A[r * LDA + i], x[i], s);
-      x[r] = (r == j ? 1.f : 0.f) - s;
+    for (int i = 0; i < 16; ++i) {
+      x[i] = (i == j ? 1.f : 0.f) - acc[i];
+#pragma unroll
+      for (int r = i + 1; r < 16; ++r) acc[r] = fmaf(Ab[r * LDA + i], x[i], acc[r]);
     }
-    float *Td = sm.tf + (16 * bk) * LDA + 16 * bk + j;
+    if (lg == 0) {
+      float *Td = Tf + (16 * w) * LDA + 16 * w + j;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Td[r * LDA] = x[r];
-  } else {
-    // zero the blocks strictly above the diagonal (rows 16a.., cols 16b.., b > a)
-    for (int idx = tid - 64; idx < 6 * 256; idx += NTHR - 64) {
-      const int blk = idx >> 8, e = idx & 255;
-      const int a = (blk < 3) ? 0 : (blk < 5 ? 1 : 2);
-      const int b = (blk < 3) ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-      sm.tf[(16 * a + (e >> 4)) * LDA + 16 * b + (e & 15)] = 0.f;
+      for (int r = 0; r < 16; ++r) Td[r * LDA] = x[r];
     }
   }
   __syncthreads();
@@ -247,37 +261,190 @@ __device__ __forceinline__ void wy_inverse(Smem<T, K, NB> &sm, int tid) {
       for (int c = bb; c < ba; ++c) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const float av = sm.a[(16 * ba + lr) * LDA + 16 * c + 4 * kk + lg];
-          const float bv = sm.tf[(16 * c + 4 * kk + lg) * LDA + 16 * bb + lr];
+          const float av = A[(16 * ba + lr) * LDA + 16 * c + 4 * kk + lg];
+          const float bv = Tf[(16 * c + 4 * kk + lg) * LDA + 16 * bb + lr];
           y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, y, 0, 0, 0);
         }
       }
       f32x4 z = zero4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float av = sm.tf[(16 * ba + lr) * LDA + 16 * ba + 4 * lg + i];
+        const float av = Tf[(16 * ba + lr) * LDA + 16 * ba + 4 * lg + i];
         z = __builtin_amdgcn_mfma_f32_16x16x4f32(av, y[i], z, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.tf[(16 * ba + 4 * lg + i) * LDA + 16 * bb + lr] = -z[i];
+      for (int i = 0; i < 4; ++i) Tf[(16 * ba + 4 * lg + i) * LDA + 16 * bb + lr] = -z[i];
     }
     __syncthreads();
   }
-  if constexpr (!S::kTinF32) {
-    for (int idx = tid; idx < CH * CH; idx += NTHR) {
-      const int r = idx >> 6, c = idx & 63;
-      sm.t[r * S::LDC + c] = (bf16)sm.tf[r * LDA + c];
+}
+
+// ---------------------------------------------------------------- WY kernel
+
+template <typename T, int K> struct WySmem {
+  static constexpr int EPS = 16 / (int)sizeof(T);
+  static constexpr int LDK = K + EPS;
+  static constexpr int LDA = CH + 4;
+  union {
+    T k[CH * LDK];      // k rows of the chunk (live until the Gram is formed)
+    float tf[CH * LDA];  // then the fp32 inverse
+  } u;
+  float a[CH * LDA];
+  float gdp[CH], beta[CH], rk[CH];
+};
+
+// the 10 lower-triangular 16 x 16 tiles of a 64 x 64 matrix
+__device__ __forceinline__ void lower_tile(int idx, int &ra, int &rb) {
+  ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
+  rb = idx - ra * (ra + 1) / 2;
+}
+
+template <typename T, int K>
+__global__ void __launch_bounds__(NTHR) gdp_wy_kernel(PrefillArgs a) {
+  using S = WySmem<T, K>;
+  constexpr int LDK = S::LDK, LDA = S::LDA, KS = K / 32;
+  __shared__ S sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+
+  const int64_t p = blockIdx.x / a.Hqk;
+  const int hq = (int)(blockIdx.x % a.Hqk);
+  if (p >= a.ntdp_rows || p >= a.tws_rows) return;
+  const int seq = a.chunk_indices_dp[2 * p], cc = a.chunk_indices_dp[2 * p + 1];
+  if (seq < 0 || seq >= a.N || cc < 0) return;  // padding row
+  const int n = a.n;
+  int64_t t0 = load_index(a.cu, a.cu_is64, seq), t1 = load_index(a.cu, a.cu_is64, seq + 1);
+  t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+  t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+  const int64_t nsub = (t1 - t0) * n, s0 = (int64_t)CH * cc;
+  if (s0 >= nsub) return;
+  const int nrow = (int)((nsub - s0) < CH ? (nsub - s0) : CH);
+  const int64_t row0 = t0 * n + s0;  // first sub-token row of the chunk
+
+  load_rows<T, K, LDK>(sm.u.k, (const T *)a.k + hq * a.k_sh + row0 * a.k_st, a.k_st, nrow, tid);
+  __syncthreads();
+  if (a.l2norm) rows_rstd<T, K>(sm.u.k, LDK, sm.rk, tid);
+  else if (tid < CH) sm.rk[tid] = 1.f;
+  __syncthreads();
+
+  // Gram tiles (k_r.k_i rk_r rk_i), kept in registers for every state head of the group
+  f32x4 gram[3];
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const int idx = w + 4 * it;
+    gram[it] = zero4();
+    if (idx < 10) {
+      int ra, rb;
+      lower_tile(idx, ra, rb);
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        gram[it] = mma(lds_contig(sm.u.k, LDK, 16 * ra + lr, 32 * s, lg),
+                       lds_contig(sm.u.k, LDK, 16 * rb + lr, 32 * s, lg), gram[it]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gram[it][i] *= sm.rk[16 * ra + 4 * lg + i] * sm.rk[16 * rb + lr];
     }
+  }
+  __syncthreads();  // k rows are dead; sm.u.tf reuses them
+
+  const int grp = a.Hv / a.Hqk;
+  for (int hh = 0; hh < grp; ++hh) {
+    const int h = hq * grp + hh;
+    if (w == 0) {
+      const int r = lane;
+      const int64_t s = s0 + r;
+      float gam = 0.f, bt = 0.f;
+      if (r < nrow) {
+        bt = a.beta[(row0 + r) * a.b_st + h * a.b_sh];
+        if (s % n == 0) gam = a.g[(t0 + s / n) * a.g_st + h * a.g_sh] * LOG2E;
+      }
+      sm.gdp[r] = wave_inclusive_sum(gam, lane);
+      sm.beta[r] = bt;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const int idx = w + 4 * it;
+      if (idx < 10) {
+        int ra, rb;
+        lower_tile(idx, ra, rb);
+        const int c = 16 * rb + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ra + 4 * lg + i;
+          sm.a[r * LDA + c] = (c < r) ? sm.beta[r] * exp2f(sm.gdp[r] - sm.gdp[c]) * gram[it][i] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+    wy_inverse<LDA>(sm.a, sm.u.tf, tid);
+    // T in fragment order: fragment f = (row tile f/2, reduction half f%2), lane-major
+    T *dst = (T *)a.tws + ((size_t)p * a.Hv + h) * (CH * CH);
+#pragma unroll
+    for (int f = 2 * w; f < 2 * w + 2; ++f) {
+      const Frag<float> fr = lds_perm(sm.u.tf, LDA, 16 * (f >> 1) + lr, 32 * (f & 1), lg);
+      store_frag(dst + (f * 64 + lane) * 8, fr);
+    }
+    __syncthreads();  // before the next head reuses sm.a / sm.gdp / sm.u.tf
   }
 }
 
-// ---------------------------------------------------------------- fused kernel
+// ---------------------------------------------------------------- scan kernel
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
+__device__ __forceinline__ float frsq(float x) { return __builtin_amdgcn_rsqf(x); }    // v_rsq_f32
+
+template <typename T, int K, int NB> struct ScanSmem {
+  static constexpr int EPS = 16 / (int)sizeof(T);  // elements per 16-byte segment
+  static constexpr int BV = 64 * NB;                // state columns per workgroup
+  static constexpr int LDK = K + EPS;               // k, q rows
+  static constexpr int LDKT = CH + EPS;             // k^T rows (one per key dim)
+  static constexpr int LDVT = CH + EPS;             // v^T rows (one per state column)
+  static constexpr int LDC = CH + EPS;              // P rows
+  static constexpr bool kTinLds = sizeof(T) == 2;   // bf16 WY blocks are staged in LDS
+  T k[2][CH * LDK];
+  T kt[2][K * LDKT];
+  T vt[2][BV * LDVT];
+  T q[CH * LDK];
+  T p[CH * LDC];
+  T t[kTinLds ? 2 : 1][kTinLds ? CH * CH : 8];
+  float gdp[2][CH], beta[2][CH], rk[2][CH];
+  float gtok[CH], rq[CH];
+};
+
+// Registers holding the next chunk's rows between their global load and their
+// LDS store.  k, q and v use 4-row units (rows 4rb..4rb+3 x one 16-byte
+// segment): one thread then holds what a transposed copy needs, and the CB
+// threads of a row group hold whole rows for the L2 norm.  Loads are never
+// predicated (rows past the end are clamped to the last valid row and zeroed
+// at commit), so issuing them never waits.
+template <typename T, int K, int BV> struct Prefetch {
+  static constexpr int EPS = 16 / (int)sizeof(T);
+  static constexpr int KCB = K / EPS, KUNITS = (CH / 4) * KCB;
+  static constexpr int VCB = BV / EPS, VUNITS = (CH / 4) * VCB;
+  static_assert(KUNITS <= NTHR && VUNITS <= NTHR, "one 4-row unit per thread");
+  uint4 k[4], q[4], v[4];
+  uint4 tw[2];
+  float beta, gam, gtk;
+};
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *(const f32x4 *)p; }
+
+// 16-byte load at a wave-uniform base plus a 32-bit per-lane byte offset
+__device__ __forceinline__ uint4 ldg16(const void *base, uint32_t off) {
+  return *(const uint4 *)((const char *)base + off);
+}
+
+// The state is kept as S = lam * Sst with a wave-uniform lam, so that the
+// per-chunk decay 2^G_last multiplies lam instead of the 64 accumulators of
+// each lane; Sst is rescaled only when lam * 2^G_last would drop below this.
+constexpr float LAM_MIN = 8.673617e-19f;  // 2^-60
 
 template <typename T, int K, int V, int NB>
-__global__ void __launch_bounds__(NTHR, 1) gdp_fused_kernel(FusedArgs a) {
-  using S = Smem<T, K, NB>;
-  constexpr int BV = S::BV, NVT = V / BV, KT16 = K / 16, KS = K / 32;
-  constexpr int LDK = S::LDK, LDKT = S::LDKT, LDV = S::LDV, LDC = S::LDC;
+__global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
+  using S = ScanSmem<T, K, NB>;
+  using P = Prefetch<T, K, S::BV>;
+  constexpr int BV = S::BV, NVT = V / BV, KT16 = K / 16, KS = K / 32, EPS = S::EPS;
+  constexpr int LDK = S::LDK, LDKT = S::LDKT, LDVT = S::LDVT, LDC = S::LDC;
+  constexpr uint32_t ES = sizeof(T);
   __shared__ S sm;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -297,16 +464,156 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_fused_kernel(FusedArgs a) {
   t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
   t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
   const int64_t L = t1 - t0, nsub = L * n;
-  const int wcol = w * 16 * NB;        // first column of this wave inside the tile
-  const int gcol = vt * BV + wcol;     // ... and inside the head
+  const int nexp = (int)((nsub + CH - 1) / CH);
+  const int wcol = w * 16 * NB;     // first column of this wave inside the tile
+  const int gcol = vt * BV + wcol;  // ... and inside the head
 
   const T *qg = (const T *)a.q + hq * a.q_sh;
   const T *kg = (const T *)a.k + hq * a.k_sh;
   const T *vg = (const T *)a.v + h * a.v_sh + vt * BV;
+  const float *gg = a.g + h * a.g_sh;
+  const float *bg = a.beta + h * a.b_sh;
   const size_t KV = (size_t)K * V;
   const size_t state_off = ((size_t)seq * a.Hv + h) * KV;
+  const int64_t tws_row0 = a.chunk_offsets_dp[seq];
+  auto wy_block = [&](int e) {  // WY block of expanded chunk e (clamped to the buffer)
+    int64_t r = tws_row0 + e;
+    r = r < 0 ? 0 : (r >= a.tws_rows ? a.tws_rows - 1 : r);
+    return (const T *)a.tws + ((size_t)r * a.Hv + h) * (CH * CH);
+  };
+  // byte strides of one row (the host guarantees 64 rows stay below 2^31 bytes)
+  const uint32_t kst = (uint32_t)a.k_st * ES, vst = (uint32_t)a.v_st * ES, qst = (uint32_t)a.q_st * ES;
+  const uint32_t gst = (uint32_t)a.g_st * 4u, bst = (uint32_t)a.b_st * 4u;
+  const int krb = tid / P::KCB, kcb = tid % P::KCB;  // k / q unit of this thread
+  const int vrb = tid / P::VCB, vcb = tid % P::VCB;  // v unit of this thread
 
-  // ---- state S (K x BV slab of this wave): fp32 accumulators
+  // ---- prefetch: issue the global loads of expanded chunk e (and, when it
+  // starts a token chunk, of that token chunk's q rows and decays)
+  P pf;
+  auto issue = [&](int e) {
+    const int64_t s0 = (int64_t)CH * e;
+    const int nrow = (int)((nsub - s0) < CH ? (nsub - s0) : CH);
+    const int64_t row0 = t0 * n + s0;
+    if (tid < P::KUNITS) {
+      const T *kb = kg + row0 * a.k_st;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        pf.k[qd] = ldg16(kb, (uint32_t)min(4 * krb + qd, nrow - 1) * kst + (uint32_t)kcb * 16u);
+    }
+    if (tid < P::VUNITS) {
+      const T *vb = vg + row0 * a.v_st;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        pf.v[qd] = ldg16(vb, (uint32_t)min(4 * vrb + qd, nrow - 1) * vst + (uint32_t)vcb * 16u);
+    }
+    if constexpr (S::kTinLds) {
+      const T *tb = wy_block(e);
+      pf.tw[0] = ldg16(tb, (uint32_t)tid * 32u);
+      pf.tw[1] = ldg16(tb, (uint32_t)tid * 32u + 16u);
+    }
+    if (tid < CH) {
+      const int r = min(tid, nrow - 1);
+      pf.beta = *(const float *)((const char *)(bg + row0 * a.b_st) + (uint32_t)r * bst);
+      // token of sub-row s0 + r relative to the first token of this chunk's rows
+      const int64_t tokf = s0 / n;
+      const int rel = (int)(s0 - tokf * n) + r;
+      pf.gam = *(const float *)((const char *)(gg + (t0 + tokf) * a.g_st) + (uint32_t)(rel / n) * gst);
+    }
+    if (e % n == 0) {
+      const int c = e / n;
+      const int64_t tokbase = t0 + (int64_t)CH * c;
+      const int ntok = (int)((L - (int64_t)CH * c) < CH ? (L - (int64_t)CH * c) : CH);
+      if (tid < P::KUNITS) {
+        const T *qb = qg + tokbase * a.q_st;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          pf.q[qd] = ldg16(qb, (uint32_t)min(4 * krb + qd, ntok - 1) * qst + (uint32_t)kcb * 16u);
+      }
+      if (tid < CH)
+        pf.gtk = *(const float *)((const char *)(gg + tokbase * a.g_st) + (uint32_t)min(tid, ntok - 1) * gst);
+    }
+  };
+  // ---- commit: wait for the prefetched rows, zero the rows past the end, and
+  // store them (with the transposed copies, L2 norms and decay cumsums) to LDS slot sl
+  auto commit = [&](int e, int sl) {
+    const int64_t s0 = (int64_t)CH * e;
+    const int nrow = (int)((nsub - s0) < CH ? (nsub - s0) : CH);
+    if (tid < P::KUNITS) {
+      if (nrow < CH) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          if (4 * krb + qd >= nrow) pf.k[qd] = uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) *(uint4 *)(sm.k[sl] + (4 * krb + qd) * LDK + kcb * EPS) = pf.k[qd];
+#pragma unroll
+      for (int e2 = 0; e2 < EPS; ++e2) store_col4<T>(sm.kt[sl] + (kcb * EPS + e2) * LDKT + 4 * krb, pf.k, e2);
+      if (a.l2norm) {
+        float ss[4];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) ss[qd] = seg_sumsq<T>(pf.k[qd]);
+#pragma unroll
+        for (int off = 1; off < P::KCB; off <<= 1)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) ss[qd] += __shfl_xor(ss[qd], off);
+        if (kcb == 0)
+          *(f32x4 *)(sm.rk[sl] + 4 * krb) =
+              f32x4{frsq(ss[0] + 1e-6f), frsq(ss[1] + 1e-6f), frsq(ss[2] + 1e-6f), frsq(ss[3] + 1e-6f)};
+      } else if (kcb == 0) {
+        *(f32x4 *)(sm.rk[sl] + 4 * krb) = f32x4{1.f, 1.f, 1.f, 1.f};
+      }
+    }
+    if (tid < P::VUNITS) {
+      if (nrow < CH) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          if (4 * vrb + qd >= nrow) pf.v[qd] = uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < EPS; ++e2) store_col4<T>(sm.vt[sl] + (vcb * EPS + e2) * LDVT + 4 * vrb, pf.v, e2);
+    }
+    if constexpr (S::kTinLds) {
+      *(uint4 *)(sm.t[sl] + tid * 16) = pf.tw[0];
+      *(uint4 *)(sm.t[sl] + tid * 16 + 8) = pf.tw[1];
+    }
+    if (tid < CH) {
+      const int rem = (int)(s0 % n);
+      const bool valid = tid < nrow;
+      const bool decay = valid && ((rem + tid) % n == 0);  // first sub-row of its token
+      sm.gdp[sl][tid] = wave_inclusive_sum(decay ? pf.gam * LOG2E : 0.f, lane);
+      sm.beta[sl][tid] = valid ? pf.beta : 0.f;
+    }
+    if (e % n == 0) {
+      const int c = e / n;
+      const int ntok = (int)((L - (int64_t)CH * c) < CH ? (L - (int64_t)CH * c) : CH);
+      if (tid < P::KUNITS) {
+        if (ntok < CH) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            if (4 * krb + qd >= ntok) pf.q[qd] = uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) *(uint4 *)(sm.q + (4 * krb + qd) * LDK + kcb * EPS) = pf.q[qd];
+        if (a.l2norm) {
+          float ss[4];
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) ss[qd] = seg_sumsq<T>(pf.q[qd]);
+#pragma unroll
+          for (int off = 1; off < P::KCB; off <<= 1)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) ss[qd] += __shfl_xor(ss[qd], off);
+          if (kcb == 0)
+            *(f32x4 *)(sm.rq + 4 * krb) =
+                f32x4{frsq(ss[0] + 1e-6f), frsq(ss[1] + 1e-6f), frsq(ss[2] + 1e-6f), frsq(ss[3] + 1e-6f)};
+        } else if (kcb == 0) {
+          *(f32x4 *)(sm.rq + 4 * krb) = f32x4{1.f, 1.f, 1.f, 1.f};
+        }
+      }
+      if (tid < CH) sm.gtok[tid] = wave_inclusive_sum(tid < ntok ? pf.gtk * LOG2E : 0.f, lane);
+    }
+  };
+
+  // ---- state S = lam * Sst (K x BV slab of this wave): fp32 accumulators
   f32x4 Sacc[KT16][NB];
 #pragma unroll
   for (int at = 0; at < KT16; ++at)
@@ -320,232 +627,236 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_fused_kernel(FusedArgs a) {
         Sacc[at][b] = zero4();
       }
     }
-  Frag<T> Sb[KS][NB];
-#pragma unroll
-  for (int s = 0; s < KS; ++s)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) from_acc(Sb[s][b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+  float lam = 1.f;
 
-  const int64_t nchunks = (L + CH - 1) / CH;
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int ntok = (int)((L - CH * c) < CH ? (L - CH * c) : CH);
-    const int64_t tokbase = t0 + CH * c;
+  if (nexp > 0) {
+    issue(0);
+    commit(0, 0);
+  }
+  __syncthreads();
 
-    // state entering token chunk c
-    if (a.chunk_states) {
-      const int64_t row = (int64_t)a.chunk_offsets[seq] + c;
-      if (row >= 0 && row < a.cs_rows) {
-        float *dst = a.chunk_states + ((size_t)row * a.Hv + h) * KV;
+  // O^T (this wave's 16*NB state columns x the 64 tokens of the chunk): the
+  // outputs are accumulated transposed, O^T = lam Sst^T Q^T diag(.) + E^T P^T,
+  // so that the state and E accumulators serve directly as A operands and each
+  // lane ends up holding 4 consecutive output columns of one token.
+  f32x4 O[NB][4];
+  for (int e = 0; e < nexp; ++e) {
+    const int sl = e & 1;
+    const int c = e / n;
+    const int j = e - c * n;
+    const int ntok = (int)((L - (int64_t)CH * c) < CH ? (L - (int64_t)CH * c) : CH);
+
+    Frag<T> Sb[KS][NB];
 #pragma unroll
-        for (int at = 0; at < KT16; ++at)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b) from_acc(Sb[s][b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+
+    if (j == 0) {
+      // state entering token chunk c
+      if (a.chunk_states) {
+        const int64_t row = (int64_t)a.chunk_offsets[seq] + c;
+        if (row >= 0 && row < a.cs_rows) {
+          float *dst = a.chunk_states + ((size_t)row * a.Hv + h) * KV;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              dst[(size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr] = Sacc[at][b][i];
+          for (int at = 0; at < KT16; ++at)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                dst[(size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr] = lam * Sacc[at][b][i];
+        }
+      }
+      // O^T = (Sst^T Q^T) diag(lam 2^Gt rq)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int t = 16 * a4 + lr;
+        const float f = lam * fexp2(sm.gtok[t]) * sm.rq[t];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mma(Sb[s][b], lds_perm(sm.q, LDK, t, 32 * s, lg), acc);
+          O[b][a4] = acc * f;
+        }
       }
     }
 
-    __syncthreads();  // previous chunk is done with sm.q / sm.gtok
-    load_rows<T, K, LDK>(sm.q, qg + tokbase * a.q_st, a.q_st, ntok, tid);
-    if (w == 0) {
-      float x = (lane < ntok) ? a.g[(tokbase + lane) * a.g_st + h * a.g_sh] * LOG2E : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      sm.gtok[lane] = x;
-    }
-    __syncthreads();
-    if (a.l2norm) rows_rstd<T, K>(sm.q, LDK, sm.rq, tid);
-    else if (tid < CH) sm.rq[tid] = 1.f;
-    __syncthreads();
+    if (e + 1 < nexp) issue(e + 1);
 
-    // O = diag(2^Gt * rq) Q h_c
-    f32x4 O[4][NB];
+    // scores P[t][r] = rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r for tok(r) <= t, tok(r) = (64j + r)/n
+    const int64_t s0 = (int64_t)CH * e;
+    const int nrow = (int)((nsub - s0) < CH ? (nsub - s0) : CH);
+    const T *kq = sm.k[sl];
+    const float *rk = sm.rk[sl];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int tt = w + 4 * it, ta = tt >> 2, tb = tt & 3;
+      const bool live = (CH * j + 16 * tb) / n <= 16 * ta + 15;
+      f32x4 acc = zero4();
+      if (live) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = mma(lds_contig(sm.q, LDK, 16 * ta + lr, 32 * s, lg), lds_contig(kq, LDK, 16 * tb + lr, 32 * s, lg),
+                    acc);
+      }
+      const int r = 16 * tb + lr;
+      const int tk = (CH * j + r) / n;
+      const float colf = (r < nrow) ? rk[r] : 0.f;
+      const float gk = sm.gtok[tk];
+      const f32x4 gt = ld4(sm.gtok + 16 * ta + 4 * lg), rq = ld4(sm.rq + 16 * ta + 4 * lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * ta + 4 * lg + i;
+        const float val = (live && tk <= t) ? rq[i] * colf * fexp2(gt[i] - gk) * acc[i] : 0.f;
+        sm.p[t * LDC + r] = (T)val;
+      }
+    }
+
+    // R = diag(beta) V - diag(beta 2^G rk lam) K Sst   (this wave's columns)
+    const float *gd = sm.gdp[sl];
+    const float *bt = sm.beta[sl];
+    const T *vtl = sm.vt[sl];
+    f32x4 R[4][NB];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int r0 = 16 * a4 + 4 * lg;
+      const f32x4 btv = ld4(bt + r0), gdv = ld4(gd + r0), rkv = ld4(rk + r0);
+      f32x4 coef;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) coef[i] = btv[i] * fexp2(gdv[i]) * rkv[i] * lam;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) x = mma(lds_perm(kq, LDK, 16 * a4 + lr, 32 * s, lg), Sb[s][b], x);
+        const T *vp = vtl + (wcol + 16 * b + lr) * LDVT + r0;
+        f32x4 vv;
+        if constexpr (sizeof(T) == 2) {
+          const bf16x4 v4 = *(const bf16x4 *)vp;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vv[i] = (float)v4[i];
+        } else {
+          vv = *(const f32x4 *)vp;
+        }
+        R[a4][b] = btv * vv - coef * x;
+      }
+    }
+    __syncthreads();  // P complete
+
+    // WY fragments of this chunk: fragment f = 2 * (row tile) + (reduction half),
+    // lane-major; the (0,1) and (1,1) halves are zero (T is lower triangular)
+    Frag<T> tfr[6];
+    {
+      const T *tl;
+      if constexpr (S::kTinLds) tl = sm.t[sl] + lane * 8;
+      else tl = wy_block(e) + lane * 8;
+      load_frag(tfr[0], tl + 0 * 512);
+      load_frag(tfr[1], tl + 2 * 512);
+      load_frag(tfr[2], tl + 4 * 512);
+      load_frag(tfr[3], tl + 5 * 512);
+      load_frag(tfr[4], tl + 6 * 512);
+      load_frag(tfr[5], tl + 7 * 512);
+    }
+
+    // E = T R
+    Frag<T> Rb[2][NB];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) from_acc(Rb[s][b], R[2 * s][b], R[2 * s + 1][b]);
+    f32x4 E[4][NB];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mma(lds_perm(sm.q, LDK, 16 * a4 + lr, 32 * s, lg), Sb[s][b], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * a4 + 4 * lg + i;
-          acc[i] *= exp2f(sm.gtok[r]) * sm.rq[r];
-        }
-        O[a4][b] = acc;
+        acc = mma(tfr[a4 < 2 ? a4 : 2 * a4 - 2], Rb[0][b], acc);
+        if (a4 >= 2) acc = mma(tfr[2 * a4 - 1], Rb[1][b], acc);
+        E[a4][b] = acc;
       }
 
-    for (int j = 0; j < n; ++j) {
-      const int64_t s0 = (int64_t)CH * (c * n + j);  // sub-token offset inside the sequence
-      if (s0 >= nsub) break;
-      const int nrow = (int)((nsub - s0) < CH ? (nsub - s0) : CH);
-      // first token of the sequence whose decay lies in this expanded chunk, minus one,
-      // relative to the token chunk: G of the rows before this expanded chunk
-      const int64_t prev_tok = (s0 + n - 1) / n - 1 - CH * c;
-
-      __syncthreads();  // previous expanded chunk is done with k / v / t / p
-      const int64_t krow0 = t0 * n + s0;
-      load_k_both<T, K, LDK, LDKT>(sm.k, sm.kt, kg + krow0 * a.k_st, a.k_st, nrow, tid);
-      load_rows<T, BV, LDV>(sm.v, vg + krow0 * a.v_st, a.v_st, nrow, tid);
-      if (tid < CH) {
-        const int r = tid;
-        const int rr = r < nrow ? r : nrow - 1;
-        const int tk = (int)((s0 + rr) / n - CH * c);
-        const float gp = prev_tok >= 0 ? sm.gtok[prev_tok] : 0.f;
-        sm.gdp[r] = sm.gtok[tk] - gp;
-        sm.beta[r] = (r < nrow) ? a.beta[(krow0 + r) * a.b_st + h * a.b_sh] : 0.f;
-      }
-      __syncthreads();
-      if (a.l2norm) rows_rstd<T, K>(sm.k, LDK, sm.rk, tid);
-      else if (tid < CH) sm.rk[tid] = 1.f;
-      __syncthreads();
-
-      // Gram K K^T -> A (strictly lower, scaled), and scores Q K^T -> P (masked, scaled)
-      for (int tt = w; tt < 32; tt += 4) {
-        if (tt < 16) {
-          const int ra = tt >> 2, rb = tt & 3;
-          if (rb > ra) continue;
-          f32x4 acc = zero4();
+    // O^T += E^T P^T  (k-steps whose P block is entirely masked are skipped)
+    Frag<T> Eb[2][NB];
 #pragma unroll
-          for (int s = 0; s < KS; ++s)
-            acc = mma(lds_contig(sm.k, LDK, 16 * ra + lr, 32 * s, lg),
-                      lds_contig(sm.k, LDK, 16 * rb + lr, 32 * s, lg), acc);
-          const int col = 16 * rb + lr;
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * ra + 4 * lg + i;
-            float val = 0.f;
-            if (col < r)
-              val = sm.beta[r] * sm.rk[r] * sm.rk[col] * exp2f(sm.gdp[r] - sm.gdp[col]) * acc[i];
-            sm.a[r * S::LDA + col] = val;
-          }
-        } else {
-          const int ta = (tt - 16) >> 2, tb = (tt - 16) & 3;
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int s = 0; s < KS; ++s)
-            acc = mma(lds_contig(sm.q, LDK, 16 * ta + lr, 32 * s, lg),
-                      lds_contig(sm.k, LDK, 16 * tb + lr, 32 * s, lg), acc);
-          const int r = 16 * tb + lr;
-          const int rr = r < nrow ? r : nrow - 1;
-          const int tk = (int)((s0 + rr) / n - CH * c);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * ta + 4 * lg + i;
-            float val = 0.f;
-            if (r < nrow && tk <= t)
-              val = sm.rq[t] * sm.rk[r] * exp2f(sm.gtok[t] - sm.gtok[tk]) * acc[i];
-            sm.p[t * LDC + r] = (T)val;
-          }
-        }
-      }
-
-      // R = diag(beta) V - diag(beta 2^G rk) K S0   (this wave's columns)
-      f32x4 R[4][NB];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          f32x4 x = zero4();
-#pragma unroll
-          for (int s = 0; s < KS; ++s) x = mma(lds_perm(sm.k, LDK, 16 * a4 + lr, 32 * s, lg), Sb[s][b], x);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * a4 + 4 * lg + i;
-            const float bt = sm.beta[r];
-            const float vv = to_f(sm.v[r * LDV + wcol + 16 * b + lr]);
-            x[i] = bt * vv - bt * exp2f(sm.gdp[r]) * sm.rk[r] * x[i];
-          }
-          R[a4][b] = x;
-        }
-      __syncthreads();  // A complete
-
-      wy_inverse<T, K, NB>(sm, tid);
-      __syncthreads();  // T complete
-      const T *Tm = S::kTinF32 ? (const T *)sm.tf : sm.t;
-      constexpr int LDT = S::kTinF32 ? S::LDA : LDC;
-
-      // E = T R
-      Frag<T> Rb[2][NB];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Rb[s][b], R[2 * s][b], R[2 * s + 1][b]);
-      f32x4 E[4][NB];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          f32x4 e = zero4();
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if (s == 1 && a4 < 2) continue;  // T is lower triangular
-            e = mma(lds_perm(Tm, LDT, 16 * a4 + lr, 32 * s, lg), Rb[s][b], e);
-          }
-          E[a4][b] = e;
-        }
-
-      // O += P E
-      Frag<T> Eb[2][NB];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            O[a4][b] = mma(lds_perm(sm.p, LDC, 16 * a4 + lr, 32 * s, lg), Eb[s][b], O[a4][b]);
-
-      // S = 2^G_last S + K^T diag(2^(G_last - G) rk) E
-      const float glast = sm.gdp[CH - 1];
-      const float dlast = exp2f(glast);
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * a4 + 4 * lg + i;
-            E[a4][b][i] *= exp2f(glast - sm.gdp[r]) * sm.rk[r];
-          }
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
-#pragma unroll
-      for (int at = 0; at < KT16; ++at)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          f32x4 acc = Sacc[at][b] * dlast;
-#pragma unroll
-          for (int s = 0; s < 2; ++s) acc = mma(lds_perm(sm.kt, LDKT, 16 * at + lr, 32 * s, lg), Eb[s][b], acc);
-          Sacc[at][b] = acc;
-        }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Sb[s][b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
-    }
-
-    // o rows of this token chunk
-    T *og = (T *)a.o + h * a.o_sh + gcol;
+      for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * a4 + 4 * lg + i;
+      for (int s = 0; s < 2; ++s) {
+        if ((CH * j + 32 * s) / n > 16 * a4 + 15) continue;
+        const Frag<T> pb = lds_perm(sm.p, LDC, 16 * a4 + lr, 32 * s, lg);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pb, O[b][a4]);
+      }
+
+    // state update.  True form: S = 2^G_last S + K^T diag(2^(G_last - G) rk) E.
+    // Kept lazily: Sst += K^T diag(2^-G rk / lam) E and lam *= 2^G_last, unless
+    // lam would fall below LAM_MIN, in which case Sst is rescaled to lam = 1.
+    const float glast = gd[CH - 1];
+    const float dl = lam * fexp2(glast);
+    const bool lazy = dl >= LAM_MIN;
+    const float base = lazy ? 0.f : glast;  // exponent offset of the E scaling
+    const float rl = lazy ? 1.f / lam : 1.f;
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int r0 = 16 * a4 + 4 * lg;
+      const f32x4 gdv = ld4(gd + r0), rkv = ld4(rk + r0);
+      f32x4 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = fexp2(base - gdv[i]) * rkv[i] * rl;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) E[a4][b] *= f;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
+    if (!lazy) {
+#pragma unroll
+      for (int at = 0; at < KT16; ++at)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Sacc[at][b] *= dl;
+    }
+#pragma unroll
+    for (int at = 0; at < KT16; ++at) {
+      const Frag<T> k0 = lds_perm(sm.kt[sl], LDKT, 16 * at + lr, 0, lg);
+      const Frag<T> k1 = lds_perm(sm.kt[sl], LDKT, 16 * at + lr, 32, lg);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        Sacc[at][b] = mma(k0, Eb[0][b], Sacc[at][b]);
+        Sacc[at][b] = mma(k1, Eb[1][b], Sacc[at][b]);
+      }
+    }
+    lam = lazy ? dl : 1.f;
+
+    if (e + 1 < nexp) commit(e + 1, sl ^ 1);
+
+    // outputs of token chunk c once its last expanded chunk is in: lane holds
+    // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns
+    if (j == n - 1 || e == nexp - 1) {
+      T *ob = (T *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol;
+      const uint32_t ost = (uint32_t)a.o_st * ES;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int t = 16 * a4 + lr;
         if (t < ntok) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) og[(tokbase + t) * a.o_st + 16 * b + lr] = (T)(O[a4][b][i] * a.scale);
+          for (int b = 0; b < NB; ++b) {
+            const f32x4 x = O[b][a4] * a.scale;
+            const uint32_t off = (uint32_t)t * ost + (uint32_t)(16 * b + 4 * lg) * ES;
+            if constexpr (sizeof(T) == 2) {
+              *(bf16x4 *)((char *)ob + off) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+            } else {
+              *(f32x4 *)((char *)ob + off) = x;
+            }
+          }
         }
       }
+    }
+    __syncthreads();
   }
 
   // final state and cache slot
@@ -562,8 +873,9 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_fused_kernel(FusedArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const size_t off = (size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr;
-        if (fdst) fdst[off] = Sacc[at][b][i];
-        if (cdst) cdst[off] = Sacc[at][b][i];
+        const float x = lam * Sacc[at][b][i];
+        if (fdst) fdst[off] = x;
+        if (cdst) cdst[off] = x;
       }
 }
 
@@ -656,41 +968,51 @@ __global__ void __launch_bounds__(1024) gdp_descriptor_kernel(DescArgs a) {
 
 namespace {
 template <typename T, int K, int V, int NB>
-hipError_t launch_one(const FusedArgs &a, hipStream_t stream) {
+hipError_t launch_scan(const PrefillArgs &a, hipStream_t stream) {
   constexpr int NVT = V / (64 * NB);
   const int64_t blocks = (int64_t)a.N * a.Hv * NVT;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdp_fused_kernel<T, K, V, NB>), dim3((unsigned)blocks), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL((gdp_scan_kernel<T, K, V, NB>), dim3((unsigned)blocks), dim3(NTHR), 0, stream, a);
   return hipGetLastError();
 }
 
-// Wider V-tiles when there are enough chains to fill the chip; narrower ones
-// otherwise, so that few long chains still spread over more CUs.
 template <typename T, int K, int V>
-hipError_t launch_v(const FusedArgs &a, hipStream_t stream) {
-  if constexpr (V == 128 && sizeof(T) == 2) {
-    if ((int64_t)a.N * a.Hv * 2 > 256) return launch_one<T, K, V, 2>(a, stream);
+hipError_t launch_all(const PrefillArgs &a, hipStream_t stream) {
+  const int64_t wy_blocks = a.ntdp_rows * a.Hqk;
+  if (wy_blocks > 0) {
+    hipLaunchKernelGGL((gdp_wy_kernel<T, K>), dim3((unsigned)wy_blocks), dim3(NTHR), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return launch_one<T, K, V, 1>(a, stream);
+  // Wider V-tiles when there are enough chains to fill the chip; narrower
+  // ones otherwise, so that few long chains still spread over more CUs.
+  if constexpr (V == 128 && sizeof(T) == 2) {
+    if ((int64_t)a.N * a.Hv * 2 > 256) return launch_scan<T, K, V, 2>(a, stream);
+  }
+  return launch_scan<T, K, V, 1>(a, stream);
 }
 }  // namespace
 
-bool fused_supported(int dtype, int K, int V) {
+bool prefill_supported(int dtype, int K, int V) {
   const bool kv = (K == 64 || K == 128) && (V == 64 || V == 128);
   if (dtype == IN_BF16) return kv;
   if (dtype == IN_F32) return kv && K == 64;
   return false;
 }
 
-hipError_t launch_fused(const FusedArgs &a, int dtype, int K, int V, hipStream_t stream) {
+size_t wy_buffer_bytes(int dtype, int64_t rows, int64_t Hv) {
+  return (size_t)rows * (size_t)Hv * CH * CH * (dtype == IN_BF16 ? 2 : 4);
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, hipStream_t stream) {
   if (dtype == IN_BF16) {
-    if (K == 128 && V == 128) return launch_v<bf16, 128, 128>(a, stream);
-    if (K == 128 && V == 64) return launch_v<bf16, 128, 64>(a, stream);
-    if (K == 64 && V == 128) return launch_v<bf16, 64, 128>(a, stream);
-    if (K == 64 && V == 64) return launch_v<bf16, 64, 64>(a, stream);
+    if (K == 128 && V == 128) return launch_all<bf16, 128, 128>(a, stream);
+    if (K == 128 && V == 64) return launch_all<bf16, 128, 64>(a, stream);
+    if (K == 64 && V == 128) return launch_all<bf16, 64, 128>(a, stream);
+    if (K == 64 && V == 64) return launch_all<bf16, 64, 64>(a, stream);
   } else if (dtype == IN_F32) {
-    if (K == 64 && V == 64) return launch_v<float, 64, 64>(a, stream);
-    if (K == 64 && V == 128) return launch_v<float, 64, 128>(a, stream);
+    if (K == 64 && V == 64) return launch_all<float, 64, 64>(a, stream);
+    if (K == 64 && V == 128) return launch_all<float, 64, 128>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -17,8 +17,9 @@ struct DescArgs {
   int32_t *chunk_indices, *chunk_indices_dp, *chunk_offsets, *chunk_offsets_dp;
 };
 
-// Arguments of the fused prefill kernel.  Strides are in elements.
-struct FusedArgs {
+// Arguments shared by the WY kernel and the scan/output kernel.  Strides are
+// in elements.
+struct PrefillArgs {
   const void *q; int64_t q_st, q_sh;
   const void *k; int64_t k_st, k_sh;
   const void *v; int64_t v_st, v_sh;
@@ -35,15 +36,21 @@ struct FusedArgs {
   const void *slots; int slots_is64; int64_t num_slots;
   float *chunk_states;   // [cs_rows, Hv, K, V] or null
   int64_t cs_rows;
-  const int32_t *chunk_offsets;  // [N+1], needed with chunk_states
+  const int32_t *chunk_offsets;     // [N+1]
+  const int32_t *chunk_indices_dp;  // [ntdp_rows, 2]
+  const int32_t *chunk_offsets_dp;  // [N+1]
+  int64_t ntdp_rows;                // rows of chunk_indices_dp (WY grid)
+  void *tws;                        // WY matrices: [tws_rows, Hv, 64*64] input dtype, fragment order
+  int64_t tws_rows;
   void *o; int64_t o_st, o_sh;
 };
 
 enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
 
-// Returns hipErrorInvalidValue for an instantiation this build does not have.
-bool fused_supported(int dtype, int K, int V);
-hipError_t launch_fused(const FusedArgs &a, int dtype, int K, int V, hipStream_t stream);
+bool prefill_supported(int dtype, int K, int V);
+// Bytes of the WY-matrix buffer for `rows` expanded chunks and Hv heads.
+size_t wy_buffer_bytes(int dtype, int64_t rows, int64_t Hv);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, hipStream_t stream);
 hipError_t launch_descriptors(const DescArgs &a, hipStream_t stream);
 
 }  // namespace gdp

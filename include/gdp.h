@@ -98,12 +98,14 @@ int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t num_householder,
 int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t num_householder, int64_t T,
                           const gdp_descriptors *out, void *stream);
 
-/* Host-only.  Workspace bytes gdp_chunk_prefill needs when it builds the
- * descriptors itself (desc == NULL) for T real tokens and N sequences.  The
- * other arguments are accepted for forward compatibility; the value depends
- * on (T, N, n) today.  Returns 0 for invalid sizes. */
+/* Host-only.  Workspace bytes gdp_chunk_prefill needs for T real tokens, N
+ * sequences, n Householder rows per token, Hv state heads and input dtype
+ * (GDP_BF16 or GDP_F32): the per-chunk WY matrices (64 x 64 per expanded
+ * chunk and state head, at the input precision) plus room for the descriptors
+ * when the caller passes none.  Hqk, K and V are accepted for forward
+ * compatibility.  Returns 0 for invalid sizes or dtypes. */
 size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk,
-                           int32_t Hv, int32_t K, int32_t V);
+                           int32_t Hv, int32_t K, int32_t V, int32_t dtype);
 
 /* Device.  The chunked GDP prefill forward pass.
  *
@@ -136,8 +138,9 @@ size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_
  *                                 are left untouched.
  *   desc         caller-built descriptors (gdp_build_descriptors) or NULL; when
  *                NULL they are built into the workspace on `stream`
- *   workspace    device scratch of workspace_bytes >= gdp_workspace_bytes(...)
- *                when desc == NULL (may be NULL otherwise)
+ *   workspace    device scratch, 256-byte aligned, of workspace_bytes >=
+ *                gdp_workspace_bytes(...) (required: it holds the per-chunk WY
+ *                matrices between the two kernels of the call)
  * Ownership/aliasing: no output may overlap an input or another output; in
  * particular final_state must not alias initial_state, because one sequence's
  * state is split over several workgroups (FlashInfer page, output_state).

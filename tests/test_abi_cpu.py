@@ -36,7 +36,9 @@ def test_every_declared_symbol_is_exported(b):
 def test_capacity_and_workspace(b):
     assert b.gdp_descriptor_capacity(812, 4, 2) == (16, 29)
     assert b.gdp_descriptor_capacity(524288, 8, 2) == (8199, 16391)
-    assert b.gdp_workspace_bytes(812, 4, 2, 4, 4, 128, 128) >= (16 + 29) * 8 + 2 * 5 * 4
+    assert b.gdp_workspace_bytes(812, 4, 2, 4, 4, 128, 128) >= 29 * 4 * 64 * 64 * 2 + (16 + 29) * 8 + 2 * 5 * 4
+    import torch
+    assert b.gdp_workspace_bytes(812, 4, 2, 4, 4, 64, 64, torch.float32) >= 29 * 4 * 64 * 64 * 4
     with pytest.raises(b.GdpError):
         b.gdp_descriptor_capacity(10, 1, 0)
 
@@ -78,7 +80,7 @@ def base_args(b, T=100, N=2, n=2, Hqk=2, Hv=4, K=128, V=128, dt=None):
         g_log=f.tensor(b, b.GDP_F32, [T, Hv]), beta=f.tensor(b, b.GDP_F32, [T * n, Hv]), n=n,
         cu=f.tensor(b, b.GDP_I32, [N + 1]), scale=0.0, s0=f.tensor(b, b.GDP_F32, [N, Hv, K, V]), ofs=1, l2=0,
         cache=b.gdp_tensor(), slots=b.gdp_tensor(), rcs=0, o=f.tensor(b, dt, [T, Hv, V]),
-        fs=f.tensor(b, b.GDP_F32, [N, Hv, K, V]), cs=b.gdp_tensor(), desc=None, ws=f.next, wsb=1 << 20)
+        fs=f.tensor(b, b.GDP_F32, [N, Hv, K, V]), cs=b.gdp_tensor(), desc=None, ws=f.next, wsb=1 << 30)
     a["fake"] = f
     return a
 

@@ -88,8 +88,9 @@ def test_workload_serving_mix_parity(gdp):
     desc = gdp.gdp_build_descriptors(inp["cu_seqlens"], n, T)
     args = dict(inp)
     args["state_cache"] = cache2
+    ws = torch.empty(gdp.gdp_workspace_bytes(T, N, n, w.Hqk, w.Hv, w.K, w.V), dtype=torch.uint8, device="cuda")
     gdp.gdp_chunk_prefill(args["q"], args["k"], args["v"], args["g_log"], args["beta"], n, args["cu_seqlens"],
-                          0.0, None, False, False, cache2, args["state_indices"], True, o2, None, cs2, desc, None)
+                          0.0, None, False, False, cache2, args["state_indices"], True, o2, None, cs2, desc, ws)
     torch.cuda.synchronize()
     assert torch.equal(o2, o), "two runs differ"
     NT = int(offs[-1].item())
@@ -225,7 +226,8 @@ def test_graph_capture_replay(gdp):
     w = workloads.custom([100, 60, 40], 2, 2, 2, 128, 128, dtype=torch.bfloat16)
     inp = to_device(workloads.generate(w, "cpu"))
     T, N = w.T, w.N
-    ws = torch.empty(gdp.gdp_workspace_bytes(T, N, 2, 2, 2, 128, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gdp.gdp_workspace_bytes(T, N, 2, 2, 2, 128, 128, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
     o = torch.empty((T, 2, 128), dtype=torch.bfloat16, device="cuda")
     fs = torch.empty((N, 2, 128, 128), dtype=torch.float32, device="cuda")
     cu = inp["cu_seqlens"].clone()
