@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_long_context_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_long_context_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "gated_deltaproduct_recurrence_amd", "csrc", "gdp_kernels.hip")
 
 
@@ -96,8 +96,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 = long-context prefill)")
-    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample: tokens per sequence")
+    ap.add_argument("--cpu-tokens", type=int, default=65536, help="oracle sample: tokens per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (three times); used to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -106,6 +109,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": src.numel() * 4, "launches": 3}))
+        return
 
     from gated_deltaproduct_recurrence_amd import binding as gdp
     from gated_deltaproduct_recurrence_amd import workloads
@@ -181,7 +193,7 @@ def main():
                    "output_final_state": w.output_final_state},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdp_fused_kernel", "kernel_ms": float(np.mean(fused_ms)),
+                     "kernel": "gdp_chunk_prefill (gdp_wy_kernel + gdp_scan_kernel)", "kernel_ms": float(np.mean(fused_ms)),
                      "algorithmic_bytes_per_launch": alg},
         "timing_detail": {"event_step_ms_median": float(np.median(step_ms)),
                           "descriptor_kernel_ms": float(np.mean(desc_ms))},
