@@ -7,7 +7,7 @@ kernel, random initial state, final state returned.  Inputs are seeded
 synthetic tensors resident in HBM before timing starts.
 
 One step = one whole forward pass over the batch: the descriptor build and
-the fused prefill kernel (both C-ABI calls, on torch's current stream).
+the prefill (both C-ABI calls, on torch's current stream).
 Prints one JSON line (metric, throughput in real tokens/s, roofline of the
 dominant kernel measured with HIP events on its stream, and the CPU oracle's
 rate on a bounded sample).
@@ -53,6 +53,16 @@ def measured_traffic():
     if rec.get("kernel_source_sha256_16") != source_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_label(w):
+    """Kernel(s) the library runs for this workload: the fused single kernel for
+    bf16 inputs with at least 256 (sequence, state head) chains, else the WY +
+    scan pair; GDP_PREFILL_PATH=fused|split forces one (bf16 only)."""
+    import torch
+    forced = os.environ.get("GDP_PREFILL_PATH")
+    fused = w.dtype == torch.bfloat16 and (forced == "fused" or (forced != "split" and w.N * w.Hv >= 256))
+    return "gdp_fused_kernel" if fused else "gdp_wy_kernel + gdp_scan_kernel"
 
 
 def cpu_baseline(inp, w, tokens_per_seq, threads):
@@ -193,7 +203,7 @@ def main():
                    "output_final_state": w.output_final_state},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdp_chunk_prefill (gdp_wy_kernel + gdp_scan_kernel)", "kernel_ms": float(np.mean(fused_ms)),
+                     "kernel": f"gdp_chunk_prefill ({kernel_label(w)})", "kernel_ms": float(np.mean(fused_ms)),
                      "algorithmic_bytes_per_launch": alg},
         "timing_detail": {"event_step_ms_median": float(np.median(step_ms)),
                           "descriptor_kernel_ms": float(np.mean(desc_ms))},

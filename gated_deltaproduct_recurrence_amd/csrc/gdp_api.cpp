@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -317,7 +318,14 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   a.tws = workspace;
   a.tws_rows = ntdp_cap;
   a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
-  hipError_t e = gdp::launch_prefill(a, idt, (int)K, (int)V, (hipStream_t)stream);
+  // GDP_PREFILL_PATH=fused|split overrides the automatic kernel choice (tests use it
+  // to run both paths on the same inputs); anything else means automatic.
+  int path = gdp::PATH_AUTO;
+  if (const char *env = std::getenv("GDP_PREFILL_PATH")) {
+    if (std::strcmp(env, "fused") == 0) path = gdp::PATH_FUSED;
+    else if (std::strcmp(env, "split") == 0) path = gdp::PATH_SPLIT;
+  }
+  hipError_t e = gdp::launch_prefill(a, idt, (int)K, (int)V, path, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDP_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return GDP_OK;
 }

@@ -879,6 +879,589 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
       }
 }
 
+// ---------------------------------------------------------------- fused kernel
+//
+// One workgroup of 8 waves per (sequence, state head, V-tile) does the whole
+// chunked pass, WY step included, so the per-chunk WY matrix never leaves the CU:
+//   waves 0-3  consumers: the state S (fp32 accumulators, one 16*NB-column slab
+//              per wave), scores, R = beta V - ..., E = T R, the outputs and the
+//              state update of expanded chunk e;
+//   wave  4    WY wave: row scalars, the Gram matrix, A and T = (I + A)^-1 of
+//              chunk e+1, entirely wave-local (a private fp32 LDS tile holds A
+//              below the diagonal and T^T on and above it);
+//   waves 5-7  loaders: direct global->LDS loads of the k rows of chunk e+2
+//              (3-slot ring), the v rows of chunk e+1, the betas and decays of
+//              chunk e+2 and the q rows of the next token chunk (2-slot rings),
+//              plus the q-row norms and the token-stream decay cumsum.
+// Two workgroup barriers per chunk separate the phases; between two barriers
+// each role only touches LDS slots no other role uses in that span.  Tiles of
+// 64 rows are stored unpadded with an XOR swizzle of their 16-byte segments;
+// k^T and v fragments come from the transposing LDS read of gfx950.
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte reads of lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12.
+__device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Byte offset of (row, byte) in a swizzled tile of rows of W bytes: segment g
+// of row r sits at slot g ^ (r mod W/16), so that 16 consecutive rows spread
+// one logical segment over all bank groups.
+template <int W> __device__ __forceinline__ int sw_off(int row, int byte) {
+  constexpr int NS = W / 16;
+  return row * W + ((((byte >> 4) ^ row) & (NS - 1)) << 4) + (byte & 15);
+}
+// bf16 fragments from swizzled tiles (k0, c0 in elements)
+template <int W> __device__ __forceinline__ Frag<bf16> sw_contig(const char *t, int row, int k0, int lg) {
+  Frag<bf16> f;
+  f.v = *(const bf16x8 *)(t + sw_off<W>(row, 2 * (k0 + 8 * lg)));
+  return f;
+}
+template <int W> __device__ __forceinline__ Frag<bf16> sw_perm(const char *t, int row, int k0, int lg) {
+  const bf16x4 lo = *(const bf16x4 *)(t + sw_off<W>(row, 2 * (k0 + 4 * lg)));
+  const bf16x4 hi = *(const bf16x4 *)(t + sw_off<W>(row, 2 * (k0 + 16 + 4 * lg)));
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+// reduction index down the rows: lane (lr, lg) gets t[k0 + 4lg + j][c0 + lr] and t[k0 + 16 + 4lg + j][c0 + lr]
+template <int W> __device__ __forceinline__ Frag<bf16> sw_colfrag(const char *t, int c0, int k0, int lr, int lg) {
+  const int row = k0 + 4 * lg + (lr >> 2), byte = 2 * (c0 + 4 * (lr & 3));
+  const bf16x4 lo = lds_tr4(t + sw_off<W>(row, byte)), hi = lds_tr4(t + sw_off<W>(row + 16, byte));
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+// rows r0..r0+3 of column c0 + lr (r0 uniform in each 16-lane group)
+template <int W> __device__ __forceinline__ f32x4 sw_col4(const char *t, int r0, int c0, int lr) {
+  const bf16x4 x = lds_tr4(t + sw_off<W>(r0 + (lr >> 2), 2 * (c0 + 4 * (lr & 3))));
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// Direct global->LDS load of a 64-row tile (rows past nrows repeat the last
+// row; they are never used unmasked).  Each wave-wide load fills 1 KiB of LDS,
+// 16 bytes per lane in lane order, so the swizzle is applied to the source.
+template <int W>
+__device__ __forceinline__ void tile_load(char *tile, const char *g, uint32_t rstride, int nrows, int lane) {
+  constexpr int NS = W / 16, RPI = 64 / NS;
+#pragma unroll
+  for (int i = 0; i < 64 / RPI; ++i) {
+    const int r = i * RPI + lane / NS, slot = lane % NS;
+    const char *src = g + (uint32_t)min(r, nrows - 1) * rstride + (uint32_t)((slot ^ (r & (NS - 1))) << 4);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)(tile + i * 1024), 16, 0, 0);
+  }
+}
+__device__ __forceinline__ void scalar_load(float *dst, const float *src) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+template <int K, int NB> struct FusedSmem {
+  static constexpr int KW = 2 * K;        // bytes per k / q row
+  static constexpr int VW = 2 * 64 * NB;  // bytes per v row of the tile
+  static constexpr int LDC = CH + 8;      // P rows (bf16, padded)
+  static constexpr int LDA = CH + 4;      // WY tile (fp32)
+  char k[3][CH * KW];
+  char v[2][CH * VW];
+  char q[2][CH * KW];
+  bf16 t[2][6 * 64 * 8];
+  bf16 p[CH * LDC];
+  float wa[CH * LDA];
+  float rawb[3][CH], rawg[3][CH], beta[3][CH], gdp[3][CH], rk[3][CH];
+  float rawt[2][CH], gtok[2][CH], rq[2][CH];
+};
+
+// WY fragment fi = 0..5 <-> (row tile, reduction half): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+__device__ __forceinline__ int frag_row(int fi) { return fi < 2 ? fi : (fi < 4 ? 2 : 3); }
+__device__ __forceinline__ int frag_half(int fi) { return (fi == 3 || fi == 5) ? 1 : 0; }
+
+// WY wave, first half: the chunk's row scalars (masked beta, base-2 decay
+// cumsum, k-row rstd from the Gram diagonal), A below the diagonal, and the
+// inverses of the four diagonal 16 x 16 blocks (stored transposed in place).
+template <int K, int LDA>
+__device__ __forceinline__ void wy_wave_a(const char *k, const float *rawb, const float *rawg, float *beta,
+                                          float *gdp, float *rk, float *wa, int nrow, int rem, int n, int l2norm,
+                                          int lane) {
+  constexpr int KS = K / 32, KW = 2 * K;
+  const int lr = lane & 15, lg = lane >> 4;
+  {
+    const bool valid = lane < nrow;
+    const bool decay = valid && ((rem + lane) % n == 0);  // first sub-row of its token
+    gdp[lane] = wave_inclusive_sum(decay ? rawg[lane] * LOG2E : 0.f, lane);
+    beta[lane] = valid ? rawb[lane] : 0.f;
+  }
+  f32x4 gram[10];
+#pragma unroll
+  for (int idx = 0; idx < 10; ++idx) {
+    int ra, rb;
+    lower_tile(idx, ra, rb);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      acc = mma(sw_contig<KW>(k, 16 * ra + lr, 32 * s, lg), sw_contig<KW>(k, 16 * rb + lr, 32 * s, lg), acc);
+    gram[idx] = acc;
+    if (ra == rb) {  // diagonal tile: lane (lg, lr) holds G[16ra + 4lg + i][16ra + lr]
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * lg + i == lr) rk[16 * ra + lr] = l2norm ? frsq(acc[i] + 1e-6f) : 1.f;
+    }
+  }
+#pragma unroll
+  for (int idx = 0; idx < 10; ++idx) {
+    int ra, rb;
+    lower_tile(idx, ra, rb);
+    const int c = 16 * rb + lr, r0 = 16 * ra + 4 * lg;
+    const f32x4 bt = ld4(beta + r0), gd = ld4(gdp + r0), rr = ld4(rk + r0);
+    const float gc = gdp[c], rc = rk[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float val = (c < r0 + i) ? bt[i] * rr[i] * rc * fexp2(gd[i] - gc) * gram[idx][i] : 0.f;
+      wa[(r0 + i) * LDA + c] = val;
+    }
+  }
+  // diagonal blocks: lane (block lg, column lr) by forward substitution, carrying
+  // the partial sums of the later rows; column lr of T_bb goes to row lr of the block
+  const float *Ab = wa + (16 * lg) * LDA + 16 * lg;
+  float acc[16], x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = (i == lr ? 1.f : 0.f) - acc[i];
+#pragma unroll
+    for (int r = i + 1; r < 16; ++r) acc[r] = fmaf(Ab[r * LDA + i], x[i], acc[r]);
+  }
+  float *d = wa + (16 * lg + lr) * LDA + 16 * lg;
+#pragma unroll
+  for (int r = 0; r < 16; r += 4) *(f32x4 *)(d + r) = f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]};
+}
+
+// WY wave, second half: the off-diagonal blocks T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
+// (stored transposed at block (b, a)) and the bf16 fragments of T.
+template <int LDA> __device__ __forceinline__ void wy_wave_b(float *wa, bf16 *tout, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int dd = 1; dd < 4; ++dd) {
+#pragma unroll
+    for (int ba = dd; ba < 4; ++ba) {
+      const int bb = ba - dd;
+      f32x4 y = zero4();
+#pragma unroll
+      for (int c = bb; c < ba; ++c)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[(16 * ba + lr) * LDA + 16 * c + 4 * kk + lg],
+                                                    wa[(16 * bb + lr) * LDA + 16 * c + 4 * kk + lg], y, 0, 0, 0);
+      f32x4 z = zero4();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[(16 * ba + 4 * lg + i) * LDA + 16 * ba + lr], y[i], z, 0, 0, 0);
+      *(f32x4 *)(wa + (16 * bb + lr) * LDA + 16 * ba + 4 * lg) = -z;
+    }
+  }
+  // lane (lr, lg) of fragment (a4, s) holds T[16 a4 + lr][32 s + 4 lg + i] and
+  // T[16 a4 + lr][32 s + 16 + 4 lg + i]; blocks right of the diagonal are zero
+#pragma unroll
+  for (int fi = 0; fi < 6; ++fi) {
+    const int a4 = frag_row(fi), s = frag_half(fi);
+    Frag<float> f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int cb = 2 * s + hh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f.v[4 * hh + i] = (cb <= a4) ? wa[(16 * cb + 4 * lg + i) * LDA + 16 * a4 + lr] : 0.f;
+    }
+    store_frag(tout + (fi * 64 + lane) * 8, f);
+  }
+}
+
+template <int K, int V, int NB>
+__global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
+  using S = FusedSmem<K, NB>;
+  constexpr int BV = 64 * NB, NVT = V / BV, KT16 = K / 16, KS = K / 32;
+  constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDA = S::LDA;
+  __shared__ S sm;
+
+  // the wave index is uniform per wave: role branches below contain barriers
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Workgroups are dealt to the 8 XCDs round-robin; remap so that each XCD
+  // walks a contiguous range of chains (the heads sharing a q/k head, and the
+  // V-tiles of one head, then read the same k/q rows through one L2).
+  const int64_t G = gridDim.x, bid = blockIdx.x;
+  const int64_t chain = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int vt = (int)(chain % NVT);
+  const int h = (int)((chain / NVT) % a.Hv);
+  const int seq = (int)(chain / ((int64_t)NVT * a.Hv));
+  const int hq = h / (a.Hv / a.Hqk);
+  const int n = a.n;
+
+  int64_t t0 = load_index(a.cu, a.cu_is64, seq), t1 = load_index(a.cu, a.cu_is64, seq + 1);
+  t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+  t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+  const int64_t L = t1 - t0, nsub = L * n;
+  const int nexp = (int)((nsub + CH - 1) / CH);
+  const int ntc = (int)((L + CH - 1) / CH);  // token chunks
+  const size_t KV = (size_t)K * V;
+  const size_t state_off = ((size_t)seq * a.Hv + h) * KV;
+  auto rows_of = [&](int e) { return (int)((nsub - (int64_t)CH * e) < CH ? (nsub - (int64_t)CH * e) : CH); };
+  auto toks_of = [&](int c) { return (int)((L - (int64_t)CH * c) < CH ? (L - (int64_t)CH * c) : CH); };
+
+  // ------------------------------------------------------------ loaders
+  const bf16 *qg = (const bf16 *)a.q + hq * a.q_sh;
+  const bf16 *kg = (const bf16 *)a.k + hq * a.k_sh;
+  const bf16 *vg = (const bf16 *)a.v + h * a.v_sh + vt * BV;
+  const float *gg = a.g + h * a.g_sh;
+  const float *bg = a.beta + h * a.b_sh;
+  const uint32_t kst = (uint32_t)a.k_st * 2u, vst = (uint32_t)a.v_st * 2u, qst = (uint32_t)a.q_st * 2u;
+  auto load_k = [&](int e) {
+    tile_load<KW>(sm.k[e % 3], (const char *)(kg + (t0 * n + (int64_t)CH * e) * a.k_st), kst, rows_of(e), lane);
+  };
+  auto load_v = [&](int e) {
+    tile_load<VW>(sm.v[e & 1], (const char *)(vg + (t0 * n + (int64_t)CH * e) * a.v_st), vst, rows_of(e), lane);
+  };
+  auto load_scalars = [&](int e) {  // raw beta and decay of each sub-row of chunk e
+    const int64_t s0 = (int64_t)CH * e;
+    const int r = min(lane, rows_of(e) - 1);
+    const int64_t tok = (s0 + r) / n;
+    scalar_load(sm.rawb[e % 3], bg + (t0 * n + s0 + r) * a.b_st);
+    scalar_load(sm.rawg[e % 3], gg + (t0 + tok) * a.g_st);
+  };
+  auto load_q = [&](int c) {  // q rows and token decays of token chunk c
+    const int64_t tokbase = t0 + (int64_t)CH * c;
+    tile_load<KW>(sm.q[c & 1], (const char *)(qg + tokbase * a.q_st), qst, toks_of(c), lane);
+    scalar_load(sm.rawt[c & 1], gg + (tokbase + min(lane, toks_of(c) - 1)) * a.g_st);
+  };
+  auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
+    const int sl = c & 1, ntok = toks_of(c);
+    float ss = 0.f;
+    if (a.l2norm) {
+#pragma unroll
+      for (int sg = 0; sg < KW / 16; ++sg) ss += seg_sumsq<bf16>(*(const uint4 *)(sm.q[sl] + sw_off<KW>(lane, 16 * sg)));
+    }
+    sm.rq[sl][lane] = a.l2norm ? frsq(ss + 1e-6f) : 1.f;
+    sm.gtok[sl][lane] = wave_inclusive_sum(lane < ntok ? sm.rawt[sl][lane] * LOG2E : 0.f, lane);
+  };
+
+  // ------------------------------------------------------------ roles
+  // Each role runs its own loop with the same barrier sequence (two in the
+  // prologue when there is work, two per expanded chunk), so that the
+  // registers live in one role never count against another.
+  if (w < 4) {
+    const int wcol = w * 16 * NB;     // first column of this wave inside the tile
+    const int gcol = vt * BV + wcol;  // ... and inside the head
+    f32x4 Sacc[KT16][NB];
+    f32x4 O[NB][4];
+    float lam = 1.f;
+#pragma unroll
+    for (int at = 0; at < KT16; ++at)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (a.s0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Sacc[at][b][i] = a.s0[state_off + (size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr];
+        } else {
+          Sacc[at][b] = zero4();
+        }
+      }
+    if (nexp > 0) {
+      __syncthreads();
+      __syncthreads();
+    }
+    for (int e = 0; e < nexp; ++e) {
+      const int ks = e % 3, ts = e & 1;
+      const int c = e / n;
+      const int j = e - c * n;
+      const int qs = c & 1;
+      // lane-derived LDS and global offsets are re-formed every chunk (an opaque
+      // copy of the lane index) instead of being hoisted into long-lived registers
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int lr = ln & 15, lg = ln >> 4;
+        // ---- phase A: X = K Sst (and at a token-chunk start O^T = Sst^T Q^T), scores, R
+        const int nrow = rows_of(e);
+        const char *kt = sm.k[ks];
+        const char *qt = sm.q[qs];
+        const float *rk = sm.rk[ks], *gd = sm.gdp[ks], *bt = sm.beta[ks];
+        const float *gtok = sm.gtok[qs], *rqv = sm.rq[qs];
+        if (j == 0 && a.chunk_states) {  // state entering token chunk c
+          const int64_t row = (int64_t)a.chunk_offsets[seq] + c;
+          if (row >= 0 && row < a.cs_rows) {
+            // the lane offset is made opaque so that the 16*NB*4 store addresses are
+            // formed here rather than hoisted out of the loop into live registers
+            uint32_t lo = (uint32_t)(4 * lg * V + gcol + lr);
+            asm volatile("" : "+v"(lo));
+            float *dst = a.chunk_states + ((size_t)row * a.Hv + h) * KV + lo;
+#pragma unroll
+            for (int at = 0; at < KT16; ++at)
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(16 * at + i) * V + 16 * b] = lam * Sacc[at][b][i];
+          }
+        }
+        f32x4 X[4][NB];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            X[a4][b] = zero4();
+            if (j == 0) O[b][a4] = zero4();
+          }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          Frag<bf16> Sb[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const Frag<bf16> kf = sw_perm<KW>(kt, 16 * a4 + lr, 32 * s, lg);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf, Sb[b], X[a4][b]);
+          }
+          if (j == 0) {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const Frag<bf16> qf = sw_perm<KW>(qt, 16 * a4 + lr, 32 * s, lg);
+#pragma unroll
+              for (int b = 0; b < NB; ++b) O[b][a4] = mma(Sb[b], qf, O[b][a4]);
+            }
+          }
+        }
+        if (j == 0) {
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int t = 16 * a4 + lr;
+            const float f = lam * fexp2(gtok[t]) * rqv[t];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) O[b][a4] *= f;
+          }
+        }
+        // scores P[t][r] = rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r for tok(r) <= t, tok(r) = (64j + r)/n
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int tt = w + 4 * it, ta = tt >> 2, tb = tt & 3;
+          const bool live = (CH * j + 16 * tb) / n <= 16 * ta + 15;
+          f32x4 acc = zero4();
+          if (live) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+              acc = mma(sw_contig<KW>(qt, 16 * ta + lr, 32 * s, lg), sw_contig<KW>(kt, 16 * tb + lr, 32 * s, lg), acc);
+          }
+          const int r = 16 * tb + lr;
+          const int tk = (CH * j + r) / n;
+          const float colf = (r < nrow) ? rk[r] : 0.f;
+          const float gk = gtok[tk];
+          const f32x4 gt = ld4(gtok + 16 * ta + 4 * lg), rq = ld4(rqv + 16 * ta + 4 * lg);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * ta + 4 * lg + i;
+            const float val = (live && tk <= t) ? rq[i] * colf * fexp2(gt[i] - gk) * acc[i] : 0.f;
+            sm.p[t * LDC + r] = (bf16)val;
+          }
+        }
+        // R = diag(beta) V - diag(beta 2^G rk lam) X, kept in X
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int r0 = 16 * a4 + 4 * lg;
+          const f32x4 btv = ld4(bt + r0), gdv = ld4(gd + r0), rkv = ld4(rk + r0);
+          f32x4 coef;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) coef[i] = btv[i] * fexp2(gdv[i]) * rkv[i] * lam;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) X[a4][b] = btv * sw_col4<VW>(sm.v[ts], r0, wcol + 16 * b, lr) - coef * X[a4][b];
+        }
+        __syncthreads();  // P complete
+        // ---- phase B: E = T R, O^T += E^T P^T, state update, outputs
+        Frag<bf16> tfr[6];
+#pragma unroll
+        for (int fi = 0; fi < 6; ++fi) load_frag(tfr[fi], sm.t[ts] + (fi * 64 + lane) * 8);
+        Frag<bf16> Rb[2][NB];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Rb[s][b], X[2 * s][b], X[2 * s + 1][b]);
+        f32x4 E[4][NB];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            f32x4 acc = mma(tfr[a4 < 2 ? a4 : 2 * a4 - 2], Rb[0][b], zero4());
+            if (a4 >= 2) acc = mma(tfr[2 * a4 - 1], Rb[1][b], acc);
+            E[a4][b] = acc;
+          }
+        Frag<bf16> Eb[2][NB];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            if ((CH * j + 32 * s) / n > 16 * a4 + 15) continue;  // P block entirely masked
+            const Frag<bf16> pf = lds_perm(sm.p, LDC, 16 * a4 + lr, 32 * s, lg);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pf, O[b][a4]);
+          }
+        // Sst += K^T diag(2^-G rk / lam) E and lam *= 2^G_last, unless lam would fall
+        // below LAM_MIN (then Sst is rescaled to lam = 1)
+        const float glast = gd[CH - 1];
+        const float dl = lam * fexp2(glast);
+        const bool lazy = dl >= LAM_MIN;
+        const float base = lazy ? 0.f : glast;
+        const float rl = lazy ? 1.f / lam : 1.f;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int r0 = 16 * a4 + 4 * lg;
+          const f32x4 gdv = ld4(gd + r0), rkv = ld4(rk + r0);
+          f32x4 f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[i] = fexp2(base - gdv[i]) * rkv[i] * rl;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) E[a4][b] *= f;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
+        if (!lazy) {
+#pragma unroll
+          for (int at = 0; at < KT16; ++at)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) Sacc[at][b] *= dl;
+        }
+#pragma unroll
+        for (int at = 0; at < KT16; ++at) {
+          const Frag<bf16> k0 = sw_colfrag<KW>(kt, 16 * at, 0, lr, lg);
+          const Frag<bf16> k1 = sw_colfrag<KW>(kt, 16 * at, 32, lr, lg);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            Sacc[at][b] = mma(k0, Eb[0][b], Sacc[at][b]);
+            Sacc[at][b] = mma(k1, Eb[1][b], Sacc[at][b]);
+          }
+        }
+        lam = lazy ? dl : 1.f;
+        // outputs of token chunk c once its last expanded chunk is in: lane holds
+        // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns
+        if (j == n - 1 || e == nexp - 1) {
+          const int ntok = toks_of(c);
+          const uint32_t ost = (uint32_t)a.o_st * 2u;
+          uint32_t lo = (uint32_t)lr * ost + (uint32_t)(8 * lg);
+          asm volatile("" : "+v"(lo));
+          char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol) + lo;
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            if (16 * a4 + lr < ntok) {
+#pragma unroll
+              for (int b = 0; b < NB; ++b) {
+                const f32x4 x = O[b][a4] * a.scale;
+                *(bf16x4 *)(ob + (uint32_t)(16 * a4) * ost + 32 * b) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+              }
+            }
+          }
+        }
+      __syncthreads();
+    }
+    float *fdst = a.final_state ? a.final_state + state_off : nullptr;
+    float *cdst = nullptr;
+    if (a.cache) {
+      const int64_t slot = load_index(a.slots, a.slots_is64, seq);
+      if (slot >= 0 && slot < a.num_slots) cdst = a.cache + ((size_t)slot * a.Hv + h) * KV;
+    }
+#pragma unroll
+    for (int at = 0; at < KT16; ++at)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t off = (size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr;
+          const float x = lam * Sacc[at][b][i];
+          if (fdst) fdst[off] = x;
+          if (cdst) cdst[off] = x;
+        }
+  } else if (w == 4) {
+    // WY wave: T of chunk 0 in the prologue, then T of chunk e+1 during chunk e
+    // (its k rows and raw scalars landed before the barrier that opened chunk e)
+    if (nexp > 0) {
+      __syncthreads();
+      wy_wave_a<K, LDA>(sm.k[0], sm.rawb[0], sm.rawg[0], sm.beta[0], sm.gdp[0], sm.rk[0], sm.wa, rows_of(0), 0, n,
+                        a.l2norm, lane);
+      wy_wave_b<LDA>(sm.wa, sm.t[0], lane);
+      __syncthreads();
+    }
+    for (int e = 0; e < nexp; ++e) {
+      const bool has = e + 1 < nexp;
+      const int k1 = (e + 1) % 3;
+      if (has)
+        wy_wave_a<K, LDA>(sm.k[k1], sm.rawb[k1], sm.rawg[k1], sm.beta[k1], sm.gdp[k1], sm.rk[k1], sm.wa,
+                          rows_of(e + 1), (int)(((int64_t)CH * (e + 1)) % n), n, a.l2norm, lane);
+      __syncthreads();
+      if (has) wy_wave_b<LDA>(sm.wa, sm.t[(e + 1) & 1], lane);
+      __syncthreads();
+    }
+  } else if (w == 5) {
+    // k rows: chunks 0 and 1 in the prologue, chunk e+2 during chunk e
+    if (nexp > 0) {
+      load_k(0);
+      if (nexp > 1) load_k(1);
+      wait_vm();
+      __syncthreads();
+      __syncthreads();
+    }
+    for (int e = 0; e < nexp; ++e) {
+      if (e + 2 < nexp) load_k(e + 2);
+      __syncthreads();
+      wait_vm();
+      __syncthreads();
+    }
+  } else if (w == 6) {
+    // v rows: chunk 0 in the prologue, chunk e+1 during chunk e
+    if (nexp > 0) {
+      load_v(0);
+      wait_vm();
+      __syncthreads();
+      __syncthreads();
+    }
+    for (int e = 0; e < nexp; ++e) {
+      if (e + 1 < nexp) load_v(e + 1);
+      __syncthreads();
+      wait_vm();
+      __syncthreads();
+    }
+  } else {
+    // betas and decays of chunk e+2, q rows of token chunk c+1 from the start of
+    // token chunk c, and their norms and decay cumsum once they have landed
+    if (nexp > 0) {
+      load_scalars(0);
+      if (nexp > 1) load_scalars(1);
+      load_q(0);
+      wait_vm();
+      finish_q(0);
+      __syncthreads();
+      __syncthreads();
+    }
+    for (int e = 0; e < nexp; ++e) {
+      const int c = e / n;
+      const int j = e - c * n;
+      if (e + 2 < nexp) load_scalars(e + 2);
+      if (j == 0 && c + 1 < ntc) load_q(c + 1);
+      __syncthreads();
+      wait_vm();
+      if ((e + 1) % n == 0 && c + 1 < ntc) finish_q(c + 1);
+      __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- descriptors
 //
 // Megatron Core page, chunk_indices / chunk_indices_dp / chunk_offsets: one
@@ -977,7 +1560,7 @@ hipError_t launch_scan(const PrefillArgs &a, hipStream_t stream) {
 }
 
 template <typename T, int K, int V>
-hipError_t launch_all(const PrefillArgs &a, hipStream_t stream) {
+hipError_t launch_split(const PrefillArgs &a, hipStream_t stream) {
   const int64_t wy_blocks = a.ntdp_rows * a.Hqk;
   if (wy_blocks > 0) {
     hipLaunchKernelGGL((gdp_wy_kernel<T, K>), dim3((unsigned)wy_blocks), dim3(NTHR), 0, stream, a);
@@ -990,6 +1573,27 @@ hipError_t launch_all(const PrefillArgs &a, hipStream_t stream) {
     if ((int64_t)a.N * a.Hv * 2 > 256) return launch_scan<T, K, V, 2>(a, stream);
   }
   return launch_scan<T, K, V, 1>(a, stream);
+}
+
+template <int K, int V>
+hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.N * a.Hv;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((gdp_fused_kernel<K, V, V / 64>), dim3((unsigned)blocks), dim3(2 * NTHR), 0, stream, a);
+  return hipGetLastError();
+}
+
+// The fused kernel keeps one chain per CU busy for its whole length; it is
+// chosen when there are enough chains to give every CU one.  Otherwise the
+// split pair (parallel WY kernel, then the scan) spreads the WY work of few
+// long chains over the whole chip.
+template <typename T, int K, int V>
+hipError_t launch_all(const PrefillArgs &a, int path, hipStream_t stream) {
+  if constexpr (sizeof(T) == 2) {
+    const bool fused = path == PATH_FUSED || (path == PATH_AUTO && (int64_t)a.N * a.Hv >= 256);
+    if (fused) return launch_fused<K, V>(a, stream);
+  }
+  return launch_split<T, K, V>(a, stream);
 }
 }  // namespace
 
@@ -1004,15 +1608,15 @@ size_t wy_buffer_bytes(int dtype, int64_t rows, int64_t Hv) {
   return (size_t)rows * (size_t)Hv * CH * CH * (dtype == IN_BF16 ? 2 : 4);
 }
 
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, int path, hipStream_t stream) {
   if (dtype == IN_BF16) {
-    if (K == 128 && V == 128) return launch_all<bf16, 128, 128>(a, stream);
-    if (K == 128 && V == 64) return launch_all<bf16, 128, 64>(a, stream);
-    if (K == 64 && V == 128) return launch_all<bf16, 64, 128>(a, stream);
-    if (K == 64 && V == 64) return launch_all<bf16, 64, 64>(a, stream);
+    if (K == 128 && V == 128) return launch_all<bf16, 128, 128>(a, path, stream);
+    if (K == 128 && V == 64) return launch_all<bf16, 128, 64>(a, path, stream);
+    if (K == 64 && V == 128) return launch_all<bf16, 64, 128>(a, path, stream);
+    if (K == 64 && V == 64) return launch_all<bf16, 64, 64>(a, path, stream);
   } else if (dtype == IN_F32) {
-    if (K == 64 && V == 64) return launch_all<float, 64, 64>(a, stream);
-    if (K == 64 && V == 128) return launch_all<float, 64, 128>(a, stream);
+    if (K == 64 && V == 64) return launch_all<float, 64, 64>(a, path, stream);
+    if (K == 64 && V == 128) return launch_all<float, 64, 128>(a, path, stream);
   }
   return hipErrorInvalidValue;
 }

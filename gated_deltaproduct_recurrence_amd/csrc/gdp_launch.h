@@ -47,10 +47,14 @@ struct PrefillArgs {
 
 enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
 
+// Kernel path: AUTO picks the fused single kernel for bf16 when there are at
+// least 256 (sequence, state head) chains, else the WY kernel + scan kernel pair.
+enum Path { PATH_AUTO = 0, PATH_FUSED = 1, PATH_SPLIT = 2 };
+
 bool prefill_supported(int dtype, int K, int V);
 // Bytes of the WY-matrix buffer for `rows` expanded chunks and Hv heads.
 size_t wy_buffer_bytes(int dtype, int64_t rows, int64_t Hv);
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, int path, hipStream_t stream);
 hipError_t launch_descriptors(const DescArgs &a, hipStream_t stream);
 
 }  // namespace gdp

@@ -17,6 +17,17 @@ def gdp():
     return binding
 
 
+# bf16 inputs have two kernel paths: the fused single kernel and the WY + scan
+# pair.  Tests over bf16 inputs run each path forced through GDP_PREFILL_PATH.
+PATHS = ["fused", "split"]
+
+
+@pytest.fixture(params=PATHS)
+def path(request, monkeypatch):
+    monkeypatch.setenv("GDP_PREFILL_PATH", request.param)
+    return request.param
+
+
 def run_gpu(gdp, inp):
     args = dict(inp)
     res = gdp.chunk_prefill(**args)
@@ -60,8 +71,16 @@ def test_descriptors_larger_capacity_padding(gdp):
 
 # ---------------------------------------------------------------- the five workloads
 
-@pytest.mark.parametrize("wid", [0, 1, 2])
-def test_workload_full_parity(gdp, wid):
+def test_workload0_fp32_full_parity(gdp):
+    w = workloads.workload(0)
+    inp = workloads.generate(w, "cpu")
+    ref = oracle_run(inp)
+    res = run_gpu(gdp, to_device(inp))
+    check_all(inp, res, ref, TOL[w.dtype], what=w.name)
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_workload_full_parity(gdp, wid, path):
     w = workloads.workload(wid)
     inp = workloads.generate(w, "cpu")
     ref = oracle_run(inp)
@@ -69,7 +88,7 @@ def test_workload_full_parity(gdp, wid):
     check_all(inp, res, ref, TOL[w.dtype], what=w.name)
 
 
-def test_workload_serving_mix_parity(gdp):
+def test_workload_serving_mix_parity(gdp, path):
     """Random-length mix with cache slots and chunk states; heads 0..3 against the oracle,
     the untouched slots and the padding chunk-state rows bit-exact."""
     w = workloads.workload(3)
@@ -150,9 +169,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
-def test_ragged_parity(gdp, case):
-    lens, n, Hqk, Hv, K, V, dtype, l2 = case
+CASE_PATHS = [(i, p) for i, c in enumerate(CASES) for p in (PATHS if c[6] == torch.bfloat16 else ["auto"])]
+
+
+@pytest.mark.parametrize("ci,kpath", CASE_PATHS, ids=[f"case{i}-{p}" for i, p in CASE_PATHS])
+def test_ragged_parity(gdp, ci, kpath, monkeypatch):
+    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    lens, n, Hqk, Hv, K, V, dtype, l2 = CASES[ci]
     w = workloads.custom(lens, n, Hqk, Hv, K, V, dtype=dtype, l2norm_in_kernel=l2, init_std=0.2)
     inp = workloads.generate(w, "cpu")
     inp["return_chunk_states"] = True
@@ -167,7 +190,7 @@ def test_ragged_parity(gdp, case):
     assert rel_err(to_np(cs[:NT]), ref["chunk_states"]) <= tol
 
 
-def test_all_sequences_empty(gdp):
+def test_all_sequences_empty(gdp, path):
     w = workloads.custom([0, 0, 0], 2, 1, 2, 64, 64, dtype=torch.bfloat16, init_std=0.3)
     inp = to_device(workloads.generate(w, "cpu"))
     o, fs = gdp.chunk_prefill(**inp)
@@ -176,7 +199,7 @@ def test_all_sequences_empty(gdp):
     assert torch.equal(fs, inp["initial_state"])
 
 
-def test_strided_q_and_o(gdp):
+def test_strided_q_and_o(gdp, path):
     w = workloads.custom([100, 29], 2, 2, 2, 128, 128, dtype=torch.bfloat16)
     inp = to_device(workloads.generate(w, "cpu"))
     ref_o, ref_s = gdp.chunk_prefill(**inp)
@@ -190,7 +213,7 @@ def test_strided_q_and_o(gdp):
     assert torch.all(obig[:, :, :64] == 0) and torch.all(obig[:, :, 192:] == 0)
 
 
-def test_determinism_and_caller_descriptors(gdp):
+def test_determinism_and_caller_descriptors(gdp, path):
     w = workloads.workload(1)
     inp = to_device(workloads.generate(w, "cpu"))
     a = gdp.chunk_prefill(**inp)
@@ -202,8 +225,8 @@ def test_determinism_and_caller_descriptors(gdp):
         assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1])
 
 
-def test_split_and_resume_on_gpu(gdp):
-    w = workloads.custom([333], 2, 1, 2, 128, 128, dtype=torch.float32 if False else torch.bfloat16)
+def test_split_and_resume_on_gpu(gdp, path):
+    w = workloads.custom([333], 2, 1, 2, 128, 128, dtype=torch.bfloat16)
     inp = to_device(workloads.generate(w, "cpu"))
     full_o, full_s = gdp.chunk_prefill(**inp)
     L1, n = 190, 2
@@ -220,7 +243,7 @@ def test_split_and_resume_on_gpu(gdp):
     assert rel_err(to_np(sb), to_np(full_s)) <= 1.5e-2
 
 
-def test_graph_capture_replay(gdp):
+def test_graph_capture_replay(gdp, path):
     """Descriptors at capacity keep the grid fixed for (T, N): a captured call
     replays correctly with new cu_seqlens contents of the same T and N."""
     w = workloads.custom([100, 60, 40], 2, 2, 2, 128, 128, dtype=torch.bfloat16)
@@ -254,3 +277,19 @@ def test_graph_capture_replay(gdp):
         call()
         torch.cuda.synchronize()
         assert torch.equal(go, o) and torch.equal(gs, fs), f"replay differs from eager for {lens}"
+
+
+def test_fused_and_split_agree(gdp, monkeypatch):
+    """Both bf16 paths on the varlen workload: each within tolerance of the
+    oracle, and of each other."""
+    w = workloads.workload(1)
+    inp = workloads.generate(w, "cpu")
+    ref = oracle_run(inp)
+    dev = to_device(inp)
+    out = {}
+    for p in PATHS:
+        monkeypatch.setenv("GDP_PREFILL_PATH", p)
+        out[p] = run_gpu(gdp, dev)
+        check_all(inp, out[p], ref, TOL[w.dtype], what=p)
+    assert rel_err(to_np(out["fused"][0]), to_np(out["split"][0])) <= TOL[w.dtype]
+    assert rel_err(to_np(out["fused"][1]), to_np(out["split"][1])) <= TOL[w.dtype]
