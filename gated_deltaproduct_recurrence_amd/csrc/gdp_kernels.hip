@@ -881,22 +881,29 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------- fused kernel
 //
-// One workgroup of 8 waves per (sequence, state head, V-tile) does the whole
-// chunked pass, WY step included, so the per-chunk WY matrix never leaves the CU:
+// One workgroup of 8 waves per (sequence, state head) does the whole chunked
+// pass, WY step included, so the per-chunk WY matrix never leaves the CU:
 //   waves 0-3  consumers: the state S (fp32 accumulators, one 16*NB-column slab
-//              per wave), scores, R = beta V - ..., E = T R, the outputs and the
+//              per wave), X = K S, the scores, R, E = T R, the outputs and the
 //              state update of expanded chunk e;
-//   wave  4    WY wave: row scalars, the Gram matrix, A and T = (I + A)^-1 of
-//              chunk e+1, entirely wave-local (a private fp32 LDS tile holds A
-//              below the diagonal and T^T on and above it);
+//   wave  4    WY wave: the Gram matrix, k-row norms, A and T = (I + A)^-1 of
+//              chunk e+1, plus the per-row coefficients the consumers use;
 //   waves 5-7  loaders: direct global->LDS loads of the k rows of chunk e+2
 //              (3-slot ring), the v rows of chunk e+1, the betas and decays of
-//              chunk e+2 and the q rows of the next token chunk (2-slot rings),
-//              plus the q-row norms and the token-stream decay cumsum.
+//              chunk e+2 and the q rows of the next token chunk (2-slot rings);
+//              wave 7 also forms the masked betas, the decay cumsums, the q-row
+//              norms and the per-row token tables.
 // Two workgroup barriers per chunk separate the phases; between two barriers
 // each role only touches LDS slots no other role uses in that span.  Tiles of
 // 64 rows are stored unpadded with an XOR swizzle of their 16-byte segments;
-// k^T and v fragments come from the transposing LDS read of gfx950.
+// k^T, v and T fragments come from the transposing LDS read of gfx950.
+//
+// WY step on one wave: the Gram tiles are formed with the k rows of the later
+// block as the B operand, so each lane ends up holding a row of A (the A-operand
+// layout of a 16 x 16 x 16 product).  The four diagonal 16 x 16 blocks are
+// inverted by row substitution, all four at once, with the rows already solved
+// broadcast across each 16-lane row by DPP (row_newbcast); the blocks below the
+// diagonal then follow from T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb on bf16 MFMA.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -907,38 +914,91 @@ __device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Byte offset of (row, byte) in a swizzled tile of rows of W bytes: segment g
-// of row r sits at slot g ^ (r mod W/16), so that 16 consecutive rows spread
-// one logical segment over all bank groups.
+// Tiles of 64 rows of W bytes are stored with their 16-byte segments permuted
+// per row: segment g of row r sits at slot g ^ swz(r).  The LDS serves 8-byte
+// reads (plain and transposing) 32 lanes at a time over 64 four-byte banks, and
+// 16-byte reads 8 lanes at a time over 128 bytes.  For 256-byte rows swz maps
+// row r = 8m + t (t < 8) to 2t + (t / 4 xor m): it is a bijection on 16 rows;
+// for each m its 8 values differ in bits 1-3, so the 8 rows x 2 adjacent
+// segments of a 32-lane transposing read meet 16 distinct slots; and they
+// differ in bits 0-2, so 8 lanes reading one segment of 8 consecutive rows meet
+// 8 distinct slots modulo 128 bytes.  For 128-byte rows no row permutation does
+// both; those tiles keep the identity.
+template <int NS> __device__ __forceinline__ int swz(int r) {
+  static_assert(NS == 16 || NS == 8, "rows of 128 or 256 bytes");
+  if constexpr (NS == 16) return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1);
+  return r & 7;
+}
 template <int W> __device__ __forceinline__ int sw_off(int row, int byte) {
   constexpr int NS = W / 16;
-  return row * W + ((((byte >> 4) ^ row) & (NS - 1)) << 4) + (byte & 15);
+  return row * W + ((((byte >> 4) ^ swz<NS>(row)) & (NS - 1)) << 4) + (byte & 15);
 }
-// bf16 fragments from swizzled tiles (k0, c0 in elements)
+// bf16 fragment from a swizzled tile: row `row`, reduction slots k0 + 8lg .. +7
 template <int W> __device__ __forceinline__ Frag<bf16> sw_contig(const char *t, int row, int k0, int lg) {
   Frag<bf16> f;
   f.v = *(const bf16x8 *)(t + sw_off<W>(row, 2 * (k0 + 8 * lg)));
   return f;
 }
-template <int W> __device__ __forceinline__ Frag<bf16> sw_perm(const char *t, int row, int k0, int lg) {
-  const bf16x4 lo = *(const bf16x4 *)(t + sw_off<W>(row, 2 * (k0 + 4 * lg)));
-  const bf16x4 hi = *(const bf16x4 *)(t + sw_off<W>(row, 2 * (k0 + 16 + 4 * lg)));
-  Frag<bf16> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
+// the same from an unswizzled bf16 tile with a row stride of ld elements
+__device__ __forceinline__ bf16x4 tr_col4(const bf16 *t, int ld, int r0, int c0, int lr) {
+  return lds_tr4((const char *)(t + (r0 + (lr >> 2)) * ld + c0 + 4 * (lr & 3)));
 }
-// reduction index down the rows: lane (lr, lg) gets t[k0 + 4lg + j][c0 + lr] and t[k0 + 16 + 4lg + j][c0 + lr]
-template <int W> __device__ __forceinline__ Frag<bf16> sw_colfrag(const char *t, int c0, int k0, int lr, int lg) {
-  const int row = k0 + 4 * lg + (lr >> 2), byte = 2 * (c0 + 4 * (lr & 3));
-  const bf16x4 lo = lds_tr4(t + sw_off<W>(row, byte)), hi = lds_tr4(t + sw_off<W>(row + 16, byte));
-  Frag<bf16> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
+
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-// rows r0..r0+3 of column c0 + lr (r0 uniform in each 16-lane group)
-template <int W> __device__ __forceinline__ f32x4 sw_col4(const char *t, int r0, int c0, int lr) {
-  const bf16x4 x = lds_tr4(t + sw_off<W>(r0 + (lr >> 2), 2 * (c0 + 4 * (lr & 3))));
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+__device__ __forceinline__ bf16x4 bf4(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+
+// Per-lane part of a family of accesses to a swizzled tile of rows of W bytes:
+// the lane's row r (taken mod W/16) and byte b inside its row.  The access at
+// row R + r (R a multiple of W/16) and byte B + b (B a multiple of 16 below W
+// whose segment bits do not overlap those of b) sits at
+// R * W + l + (B ^ x) with l = r * W + (b mod 16), x = 16 ((b / 16) ^ swz(r)).
+struct SwLane {
+  uint32_t l, x;
+};
+template <int N> struct IC {
+  static constexpr int value = N;
+};
+template <int W> __device__ __forceinline__ SwLane sw_lane(int r, int b) {
+  constexpr int NS = W / 16;
+  return SwLane{(uint32_t)(r * W + (b & 15)), (uint32_t)((((b >> 4) ^ swz<NS>(r)) & (NS - 1)) << 4)};
+}
+
+// DPP move of x (row mask ROWS; lanes of disabled rows and lanes whose source
+// lies outside their row read 0)
+template <int CTRL, int ROWS = 0xF> __device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, true));
+}
+// inclusive prefix sum over the 64 lanes: shifts inside each 16-lane row, then
+// row 0's total into row 1 (and row 2's into row 3), then lane 31 into rows 2, 3
+__device__ __forceinline__ float wave_scan(float x) {
+  x += dpp<0x111>(x);       // row_shr:1
+  x += dpp<0x112>(x);       // row_shr:2
+  x += dpp<0x114>(x);       // row_shr:4
+  x += dpp<0x118>(x);       // row_shr:8
+  x += dpp<0x142, 0xA>(x);  // row_bcast:15
+  x += dpp<0x143, 0xC>(x);  // row_bcast:31
+  return x;
+}
+
+// Row substitution for a unit-lower-triangular 16 x 16 system (I + L) T = I:
+// lane (lg, lr) holds row lr of -L (nl) and the entries T[lr][4lg + i]; step m
+// adds -L[lr][m] times row m, which lane (lg, m) of the same 16-lane row holds:
+// v_fmac_f32 with its first source read through DPP row_newbcast:m.  Each step
+// is one block of inline assembly (the compiler does not fold a DPP move into
+// an fmac).  A register written by step m-1 is read through DPP 3 instructions
+// later, and each block starts with 2 wait states for whatever the compiler
+// placed right before it: the VALU-write -> DPP-read hazard needs 2.
+template <int M> __device__ __forceinline__ void subst(float (&t)[4], const float (&nl)[16]) {
+  asm volatile("s_nop 1\n"
+               "v_fmac_f32_dpp %0, %0, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n"
+               "v_fmac_f32_dpp %1, %1, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n"
+               "v_fmac_f32_dpp %2, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n"
+               "v_fmac_f32_dpp %3, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
+               : "v"(nl[M]), "i"(M));
+  if constexpr (M < 14) subst<M + 1>(t, nl);
 }
 
 // Direct global->LDS load of a 64-row tile (rows past nrows repeat the last
@@ -950,7 +1010,7 @@ __device__ __forceinline__ void tile_load(char *tile, const char *g, uint32_t rs
 #pragma unroll
   for (int i = 0; i < 64 / RPI; ++i) {
     const int r = i * RPI + lane / NS, slot = lane % NS;
-    const char *src = g + (uint32_t)min(r, nrows - 1) * rstride + (uint32_t)((slot ^ (r & (NS - 1))) << 4);
+    const char *src = g + (uint32_t)min(r, nrows - 1) * rstride + (uint32_t)((slot ^ swz<NS>(r)) << 4);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                      (__attribute__((address_space(3))) void *)(tile + i * 1024), 16, 0, 0);
   }
@@ -965,127 +1025,31 @@ template <int K, int NB> struct FusedSmem {
   static constexpr int KW = 2 * K;        // bytes per k / q row
   static constexpr int VW = 2 * 64 * NB;  // bytes per v row of the tile
   static constexpr int LDC = CH + 8;      // P rows (bf16, padded)
-  static constexpr int LDA = CH + 4;      // WY tile (fp32)
+  static constexpr int LDT = CH + 16;     // rows of T^T (bf16, padded)
   char k[3][CH * KW];
   char v[2][CH * VW];
   char q[2][CH * KW];
-  bf16 t[2][6 * 64 * 8];
+  bf16 t[CH * LDT];         // T^T of the chunk being consumed: entry (r, c) of T at [c * LDT + r]
   bf16 p[CH * LDC];
-  float wa[CH * LDA];
-  float rawb[3][CH], rawg[3][CH], beta[3][CH], gdp[3][CH], rk[3][CH];
-  float rawt[2][CH], gtok[2][CH], rq[2][CH];
+  float gram[10][64 * 4];   // Gram tiles of the next chunk, lane order; the diagonal
+                            // ones are then reused for the rows of -L
+  bf16 alow[6][64 * 4];     // A below the diagonal blocks (A-operand layout, lane order)
+  bf16 tdiag[4][64 * 4];    // diagonal blocks of T (A-operand layout, lane order)
+  bf16 tdrow[4][256];       // diagonal blocks of T, row-major
+  float rawb[2][CH], rawg[2][CH];          // raw betas / decays
+  float beta[3][CH], gdp[3][CH];           // masked betas, base-2 decay cumsum
+  float rk[2][CH], c1[2][CH], wgt[2][CH];  // k-row rstd and the R / state-update weights
+  float rawt[2][CH], gtok[2][CH], rq[2][CH], qfac[2][CH];  // rq and qfac carry the output scale
+  float gkr[2][CH], rkg[2][CH];  // rkg = rk 2^(-Gt_tok(r)) (used when qsafe)
+  int tokr[2][CH];
+  int qsafe[2];                   // the token chunk's decay cumsum stays above -100 (base 2)
 };
-
-// WY fragment fi = 0..5 <-> (row tile, reduction half): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-__device__ __forceinline__ int frag_row(int fi) { return fi < 2 ? fi : (fi < 4 ? 2 : 3); }
-__device__ __forceinline__ int frag_half(int fi) { return (fi == 3 || fi == 5) ? 1 : 0; }
-
-// WY wave, first half: the chunk's row scalars (masked beta, base-2 decay
-// cumsum, k-row rstd from the Gram diagonal), A below the diagonal, and the
-// inverses of the four diagonal 16 x 16 blocks (stored transposed in place).
-template <int K, int LDA>
-__device__ __forceinline__ void wy_wave_a(const char *k, const float *rawb, const float *rawg, float *beta,
-                                          float *gdp, float *rk, float *wa, int nrow, int rem, int n, int l2norm,
-                                          int lane) {
-  constexpr int KS = K / 32, KW = 2 * K;
-  const int lr = lane & 15, lg = lane >> 4;
-  {
-    const bool valid = lane < nrow;
-    const bool decay = valid && ((rem + lane) % n == 0);  // first sub-row of its token
-    gdp[lane] = wave_inclusive_sum(decay ? rawg[lane] * LOG2E : 0.f, lane);
-    beta[lane] = valid ? rawb[lane] : 0.f;
-  }
-  f32x4 gram[10];
-#pragma unroll
-  for (int idx = 0; idx < 10; ++idx) {
-    int ra, rb;
-    lower_tile(idx, ra, rb);
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      acc = mma(sw_contig<KW>(k, 16 * ra + lr, 32 * s, lg), sw_contig<KW>(k, 16 * rb + lr, 32 * s, lg), acc);
-    gram[idx] = acc;
-    if (ra == rb) {  // diagonal tile: lane (lg, lr) holds G[16ra + 4lg + i][16ra + lr]
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * lg + i == lr) rk[16 * ra + lr] = l2norm ? frsq(acc[i] + 1e-6f) : 1.f;
-    }
-  }
-#pragma unroll
-  for (int idx = 0; idx < 10; ++idx) {
-    int ra, rb;
-    lower_tile(idx, ra, rb);
-    const int c = 16 * rb + lr, r0 = 16 * ra + 4 * lg;
-    const f32x4 bt = ld4(beta + r0), gd = ld4(gdp + r0), rr = ld4(rk + r0);
-    const float gc = gdp[c], rc = rk[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float val = (c < r0 + i) ? bt[i] * rr[i] * rc * fexp2(gd[i] - gc) * gram[idx][i] : 0.f;
-      wa[(r0 + i) * LDA + c] = val;
-    }
-  }
-  // diagonal blocks: lane (block lg, column lr) by forward substitution, carrying
-  // the partial sums of the later rows; column lr of T_bb goes to row lr of the block
-  const float *Ab = wa + (16 * lg) * LDA + 16 * lg;
-  float acc[16], x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = (i == lr ? 1.f : 0.f) - acc[i];
-#pragma unroll
-    for (int r = i + 1; r < 16; ++r) acc[r] = fmaf(Ab[r * LDA + i], x[i], acc[r]);
-  }
-  float *d = wa + (16 * lg + lr) * LDA + 16 * lg;
-#pragma unroll
-  for (int r = 0; r < 16; r += 4) *(f32x4 *)(d + r) = f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]};
-}
-
-// WY wave, second half: the off-diagonal blocks T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
-// (stored transposed at block (b, a)) and the bf16 fragments of T.
-template <int LDA> __device__ __forceinline__ void wy_wave_b(float *wa, bf16 *tout, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int dd = 1; dd < 4; ++dd) {
-#pragma unroll
-    for (int ba = dd; ba < 4; ++ba) {
-      const int bb = ba - dd;
-      f32x4 y = zero4();
-#pragma unroll
-      for (int c = bb; c < ba; ++c)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[(16 * ba + lr) * LDA + 16 * c + 4 * kk + lg],
-                                                    wa[(16 * bb + lr) * LDA + 16 * c + 4 * kk + lg], y, 0, 0, 0);
-      f32x4 z = zero4();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        z = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[(16 * ba + 4 * lg + i) * LDA + 16 * ba + lr], y[i], z, 0, 0, 0);
-      *(f32x4 *)(wa + (16 * bb + lr) * LDA + 16 * ba + 4 * lg) = -z;
-    }
-  }
-  // lane (lr, lg) of fragment (a4, s) holds T[16 a4 + lr][32 s + 4 lg + i] and
-  // T[16 a4 + lr][32 s + 16 + 4 lg + i]; blocks right of the diagonal are zero
-#pragma unroll
-  for (int fi = 0; fi < 6; ++fi) {
-    const int a4 = frag_row(fi), s = frag_half(fi);
-    Frag<float> f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int cb = 2 * s + hh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f.v[4 * hh + i] = (cb <= a4) ? wa[(16 * cb + 4 * lg + i) * LDA + 16 * a4 + lr] : 0.f;
-    }
-    store_frag(tout + (fi * 64 + lane) * 8, f);
-  }
-}
 
 template <int K, int V, int NB>
 __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
   using S = FusedSmem<K, NB>;
   constexpr int BV = 64 * NB, NVT = V / BV, KT16 = K / 16, KS = K / 32;
-  constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDA = S::LDA;
+  constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDT = S::LDT;
   __shared__ S sm;
 
   // the wave index is uniform per wave: role branches below contain barriers
@@ -1114,49 +1078,28 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
   auto rows_of = [&](int e) { return (int)((nsub - (int64_t)CH * e) < CH ? (nsub - (int64_t)CH * e) : CH); };
   auto toks_of = [&](int c) { return (int)((L - (int64_t)CH * c) < CH ? (L - (int64_t)CH * c) : CH); };
 
-  // ------------------------------------------------------------ loaders
-  const bf16 *qg = (const bf16 *)a.q + hq * a.q_sh;
-  const bf16 *kg = (const bf16 *)a.k + hq * a.k_sh;
-  const bf16 *vg = (const bf16 *)a.v + h * a.v_sh + vt * BV;
-  const float *gg = a.g + h * a.g_sh;
-  const float *bg = a.beta + h * a.b_sh;
-  const uint32_t kst = (uint32_t)a.k_st * 2u, vst = (uint32_t)a.v_st * 2u, qst = (uint32_t)a.q_st * 2u;
-  auto load_k = [&](int e) {
-    tile_load<KW>(sm.k[e % 3], (const char *)(kg + (t0 * n + (int64_t)CH * e) * a.k_st), kst, rows_of(e), lane);
-  };
-  auto load_v = [&](int e) {
-    tile_load<VW>(sm.v[e & 1], (const char *)(vg + (t0 * n + (int64_t)CH * e) * a.v_st), vst, rows_of(e), lane);
-  };
-  auto load_scalars = [&](int e) {  // raw beta and decay of each sub-row of chunk e
-    const int64_t s0 = (int64_t)CH * e;
-    const int r = min(lane, rows_of(e) - 1);
-    const int64_t tok = (s0 + r) / n;
-    scalar_load(sm.rawb[e % 3], bg + (t0 * n + s0 + r) * a.b_st);
-    scalar_load(sm.rawg[e % 3], gg + (t0 + tok) * a.g_st);
-  };
-  auto load_q = [&](int c) {  // q rows and token decays of token chunk c
-    const int64_t tokbase = t0 + (int64_t)CH * c;
-    tile_load<KW>(sm.q[c & 1], (const char *)(qg + tokbase * a.q_st), qst, toks_of(c), lane);
-    scalar_load(sm.rawt[c & 1], gg + (tokbase + min(lane, toks_of(c) - 1)) * a.g_st);
-  };
-  auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
-    const int sl = c & 1, ntok = toks_of(c);
-    float ss = 0.f;
-    if (a.l2norm) {
-#pragma unroll
-      for (int sg = 0; sg < KW / 16; ++sg) ss += seg_sumsq<bf16>(*(const uint4 *)(sm.q[sl] + sw_off<KW>(lane, 16 * sg)));
-    }
-    sm.rq[sl][lane] = a.l2norm ? frsq(ss + 1e-6f) : 1.f;
-    sm.gtok[sl][lane] = wave_inclusive_sum(lane < ntok ? sm.rawt[sl][lane] * LOG2E : 0.f, lane);
-  };
-
-  // ------------------------------------------------------------ roles
-  // Each role runs its own loop with the same barrier sequence (two in the
-  // prologue when there is work, two per expanded chunk), so that the
-  // registers live in one role never count against another.
   if (w < 4) {
+    // ---------------------------------------------------------------- consumers
     const int wcol = w * 16 * NB;     // first column of this wave inside the tile
     const int gcol = vt * BV + wcol;  // ... and inside the head
+    const char *smb = (const char *)&sm;
+    auto off_of = [&](const void *p) { return (uint32_t)((const char *)p - smb); };
+    auto rd8 = [&](uint32_t at) { return *(const bf16x4 *)(smb + at); };
+    auto rd16 = [&](uint32_t at) { return *(const bf16x8 *)(smb + at); };
+    auto tr8 = [&](uint32_t at) { return lds_tr4(smb + at); };
+    // per-lane parts of the LDS addresses; each access below is one xor-add of a
+    // compile-time segment offset plus an immediate row offset
+    const int rl0 = 4 * lg + (lr >> 2);  // row of a transposing read inside its 16-row group
+    const SwLane Lcont = sw_lane<KW>(lr, 16 * lg);         // k / q rows, reduction slots 8lg..
+    const SwLane Lcolk = sw_lane<KW>(rl0, 16 * (lr & 3));  // k^T fragments (state-row order)
+    const SwLane Lcolv = sw_lane<VW>(rl0, 8 * (lr & 3));   // v columns
+    const uint32_t LT = (uint32_t)((rl0 * LDT + 4 * (lr & 3)) * 2);  // T^T columns
+    const uint32_t LP = (uint32_t)((lr * LDC + 4 * lg) * 2);         // P rows
+    // The state rows are kept in a permuted key order: accumulator row 4g + i of
+    // tile at holds key kap(at, g, i) = 32 (at / 2) + 8 g + 4 (at % 2) + i, so that
+    // the two tiles of one 32-deep reduction step form the B operand whose slots
+    // pair with contiguous 16-byte k (or q) fragments.
+    auto kap = [](int at, int g, int i) { return 32 * (at >> 1) + 8 * g + 4 * (at & 1) + i; };
     f32x4 Sacc[KT16][NB];
     f32x4 O[NB][4];
     float lam = 1.f;
@@ -1167,12 +1110,17 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
         if (a.s0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            Sacc[at][b][i] = a.s0[state_off + (size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr];
+            Sacc[at][b][i] = a.s0[state_off + (size_t)kap(at, lg, i) * V + gcol + 16 * b + lr];
         } else {
           Sacc[at][b] = zero4();
         }
       }
-    if (nexp > 0) {
+    const int64_t cs_row0 = a.chunk_states ? (int64_t)a.chunk_offsets[seq] : 0;
+    // wait for the start state here: a wait placed by the compiler at its first
+    // use inside the loop would also wait, every chunk, for the output stores
+    wait_vm();
+    if (nexp > 0) {  // the helpers' prologue
+      __syncthreads();
       __syncthreads();
       __syncthreads();
     }
@@ -1181,194 +1129,260 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       const int c = e / n;
       const int j = e - c * n;
       const int qs = c & 1;
-      // lane-derived LDS and global offsets are re-formed every chunk (an opaque
-      // copy of the lane index) instead of being hoisted into long-lived registers
+      // the lane constants are made opaque every chunk so that the compiler forms
+      // each address where it is used instead of hoisting dozens of them
+      SwLane lcont = Lcont, lcolk = Lcolk, lcolv = Lcolv;
+      uint32_t lt = LT, lp = LP;
       int ln = lane;
-      asm volatile("" : "+v"(ln));
+      asm volatile("" : "+v"(lcont.l), "+v"(lcont.x), "+v"(lcolk.l), "+v"(lcolk.x), "+v"(lcolv.l), "+v"(lcolv.x),
+                   "+v"(lt), "+v"(lp), "+v"(ln));
       const int lr = ln & 15, lg = ln >> 4;
-        // ---- phase A: X = K Sst (and at a token-chunk start O^T = Sst^T Q^T), scores, R
-        const int nrow = rows_of(e);
-        const char *kt = sm.k[ks];
-        const char *qt = sm.q[qs];
-        const float *rk = sm.rk[ks], *gd = sm.gdp[ks], *bt = sm.beta[ks];
-        const float *gtok = sm.gtok[qs], *rqv = sm.rq[qs];
-        if (j == 0 && a.chunk_states) {  // state entering token chunk c
-          const int64_t row = (int64_t)a.chunk_offsets[seq] + c;
-          if (row >= 0 && row < a.cs_rows) {
-            // the lane offset is made opaque so that the 16*NB*4 store addresses are
-            // formed here rather than hoisted out of the loop into live registers
-            uint32_t lo = (uint32_t)(4 * lg * V + gcol + lr);
-            asm volatile("" : "+v"(lo));
-            float *dst = a.chunk_states + ((size_t)row * a.Hv + h) * KV + lo;
-#pragma unroll
-            for (int at = 0; at < KT16; ++at)
-#pragma unroll
-              for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(16 * at + i) * V + 16 * b] = lam * Sacc[at][b][i];
-          }
-        }
-        f32x4 X[4][NB];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            X[a4][b] = zero4();
-            if (j == 0) O[b][a4] = zero4();
-          }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          Frag<bf16> Sb[NB];
-#pragma unroll
-          for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const Frag<bf16> kf = sw_perm<KW>(kt, 16 * a4 + lr, 32 * s, lg);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf, Sb[b], X[a4][b]);
-          }
-          if (j == 0) {
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-              const Frag<bf16> qf = sw_perm<KW>(qt, 16 * a4 + lr, 32 * s, lg);
-#pragma unroll
-              for (int b = 0; b < NB; ++b) O[b][a4] = mma(Sb[b], qf, O[b][a4]);
-            }
-          }
-        }
-        if (j == 0) {
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int t = 16 * a4 + lr;
-            const float f = lam * fexp2(gtok[t]) * rqv[t];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) O[b][a4] *= f;
-          }
-        }
-        // scores P[t][r] = rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r for tok(r) <= t, tok(r) = (64j + r)/n
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int tt = w + 4 * it, ta = tt >> 2, tb = tt & 3;
-          const bool live = (CH * j + 16 * tb) / n <= 16 * ta + 15;
-          f32x4 acc = zero4();
-          if (live) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-              acc = mma(sw_contig<KW>(qt, 16 * ta + lr, 32 * s, lg), sw_contig<KW>(kt, 16 * tb + lr, 32 * s, lg), acc);
-          }
-          const int r = 16 * tb + lr;
-          const int tk = (CH * j + r) / n;
-          const float colf = (r < nrow) ? rk[r] : 0.f;
-          const float gk = gtok[tk];
-          const f32x4 gt = ld4(gtok + 16 * ta + 4 * lg), rq = ld4(rqv + 16 * ta + 4 * lg);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * ta + 4 * lg + i;
-            const float val = (live && tk <= t) ? rq[i] * colf * fexp2(gt[i] - gk) * acc[i] : 0.f;
-            sm.p[t * LDC + r] = (bf16)val;
-          }
-        }
-        // R = diag(beta) V - diag(beta 2^G rk lam) X, kept in X
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int r0 = 16 * a4 + 4 * lg;
-          const f32x4 btv = ld4(bt + r0), gdv = ld4(gd + r0), rkv = ld4(rk + r0);
-          f32x4 coef;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) coef[i] = btv[i] * fexp2(gdv[i]) * rkv[i] * lam;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) X[a4][b] = btv * sw_col4<VW>(sm.v[ts], r0, wcol + 16 * b, lr) - coef * X[a4][b];
-        }
-        __syncthreads();  // P complete
-        // ---- phase B: E = T R, O^T += E^T P^T, state update, outputs
-        Frag<bf16> tfr[6];
-#pragma unroll
-        for (int fi = 0; fi < 6; ++fi) load_frag(tfr[fi], sm.t[ts] + (fi * 64 + lane) * 8);
-        Frag<bf16> Rb[2][NB];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) from_acc(Rb[s][b], X[2 * s][b], X[2 * s + 1][b]);
-        f32x4 E[4][NB];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            f32x4 acc = mma(tfr[a4 < 2 ? a4 : 2 * a4 - 2], Rb[0][b], zero4());
-            if (a4 >= 2) acc = mma(tfr[2 * a4 - 1], Rb[1][b], acc);
-            E[a4][b] = acc;
-          }
-        Frag<bf16> Eb[2][NB];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if ((CH * j + 32 * s) / n > 16 * a4 + 15) continue;  // P block entirely masked
-            const Frag<bf16> pf = lds_perm(sm.p, LDC, 16 * a4 + lr, 32 * s, lg);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pf, O[b][a4]);
-          }
-        // Sst += K^T diag(2^-G rk / lam) E and lam *= 2^G_last, unless lam would fall
-        // below LAM_MIN (then Sst is rescaled to lam = 1)
-        const float glast = gd[CH - 1];
-        const float dl = lam * fexp2(glast);
-        const bool lazy = dl >= LAM_MIN;
-        const float base = lazy ? 0.f : glast;
-        const float rl = lazy ? 1.f / lam : 1.f;
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int r0 = 16 * a4 + 4 * lg;
-          const f32x4 gdv = ld4(gd + r0), rkv = ld4(rk + r0);
-          f32x4 f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) f[i] = fexp2(base - gdv[i]) * rkv[i] * rl;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) E[a4][b] *= f;
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
-        if (!lazy) {
+      const uint32_t kt = off_of(sm.k[ks]), qt = off_of(sm.q[qs]);
+      const float *gtok = sm.gtok[qs], *qfac = sm.qfac[qs], *rqv = sm.rq[qs];
+      const float *rk = sm.rk[ts], *gkr = sm.gkr[ts];
+      const int *tokr = sm.tokr[ts];
+      // ---- phase A: X = K Sst (and at a token-chunk start O^T = Sst^T Q^T), scores, R
+      if (j == 0 && a.chunk_states) {  // state entering token chunk c
+        const int64_t row = cs_row0 + c;
+        if (row >= 0 && row < a.cs_rows) {
+          uint32_t lo = (uint32_t)(8 * lg * V + gcol + lr);
+          asm volatile("" : "+v"(lo));
+          float *dst = a.chunk_states + ((size_t)row * a.Hv + h) * KV + lo;
 #pragma unroll
           for (int at = 0; at < KT16; ++at)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) Sacc[at][b] *= dl;
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) dst[kap(at, 0, i) * V + 16 * b] = lam * Sacc[at][b][i];
         }
+      }
+      f32x4 X[4][NB];
+      // k (and q) fragments of reduction step s+1 are read while step s multiplies
+      Frag<bf16> kf[2][4], qf[2][4];
+      auto load_kq = [&](int s, int buf) {  // reduction slots 32s + 8lg .. +7
+        const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
+        const uint32_t ka = xs + (kt + lcont.l);
 #pragma unroll
-        for (int at = 0; at < KT16; ++at) {
-          const Frag<bf16> k0 = sw_colfrag<KW>(kt, 16 * at, 0, lr, lg);
-          const Frag<bf16> k1 = sw_colfrag<KW>(kt, 16 * at, 32, lr, lg);
+        for (int a4 = 0; a4 < 4; ++a4) kf[buf][a4].v = rd16(ka + 16 * a4 * KW);
+        if (j == 0) {
+          const uint32_t qa = xs + (qt + lcont.l);
 #pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            Sacc[at][b] = mma(k0, Eb[0][b], Sacc[at][b]);
-            Sacc[at][b] = mma(k1, Eb[1][b], Sacc[at][b]);
-          }
+          for (int a4 = 0; a4 < 4; ++a4) qf[buf][a4].v = rd16(qa + 16 * a4 * KW);
         }
-        lam = lazy ? dl : 1.f;
-        // outputs of token chunk c once its last expanded chunk is in: lane holds
-        // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns
-        if (j == n - 1 || e == nexp - 1) {
-          const int ntok = toks_of(c);
-          const uint32_t ost = (uint32_t)a.o_st * 2u;
-          uint32_t lo = (uint32_t)lr * ost + (uint32_t)(8 * lg);
-          asm volatile("" : "+v"(lo));
-          char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol) + lo;
+      };
+      load_kq(0, 0);
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            if (16 * a4 + lr < ntok) {
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load_kq(s + 1, (s + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        Frag<bf16> Sb[NB];
 #pragma unroll
-              for (int b = 0; b < NB; ++b) {
-                const f32x4 x = O[b][a4] * a.scale;
-                *(bf16x4 *)(ob + (uint32_t)(16 * a4) * ost + 32 * b) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[s & 1][a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
+        if (j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) O[b][a4] = mma(Sb[b], qf[s & 1][a4], s == 0 ? zero4() : O[b][a4]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {  // O^T columns t times lam scale rq_t 2^Gt_t
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float f = lam * qfac[16 * a4 + lr];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) O[b][a4] *= f;
+        }
+      }
+      // scores, transposed: lane (lg, lr) of tile (ta, w) holds
+      // P[t = 16 ta + lr][r = 16 w + 4 lg + i] = scale rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r  (tok(r) <= t);
+      // the k fragments of the wave's row block serve all four tiles
+      {
+        const int r0 = 16 * w + 4 * lg;
+        const uint32_t kb0 = kt + lcont.l + (uint32_t)(16 * w * KW), qb0 = qt + lcont.l;
+        Frag<bf16> kb[KS], qb[2][KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kb[s].v = rd16((lcont.x ^ (uint32_t)(64 * s)) + kb0);
+        const int tok0 = tokr[16 * w];  // tok(r) is non-decreasing in r
+        auto load_q = [&](int ta, int buf) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qb[buf][s].v = rd16((lcont.x ^ (uint32_t)(64 * s)) + qb0 + 16 * ta * KW);
+        };
+        // when the token chunk's decay cumsum stays above -100, 2^(Gt_t - Gt_tok(r)) is
+        // formed as the product qfac_t rkg_r of per-token and per-row factors (both
+        // finite and normal); otherwise per entry
+        const bool fact = sm.qsafe[qs] != 0;
+        const f32x4 rk4 = ld4((fact ? sm.rkg[ts] : rk) + r0), gk4 = ld4(gkr + r0);
+        const int4 tk4 = *(const int4 *)(tokr + r0);
+        const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * w);
+        load_q(0, 0);
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+          if (ta + 1 < 4) load_q(ta + 1, (ta + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const int t = 16 * ta + lr;
+          f32x4 val = zero4();
+          if (tok0 <= 16 * ta + 15) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc = mma(kb[s], qb[ta & 1][s], acc);
+            if (fact) {
+              const float qv = qfac[t];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int tki = i == 0 ? tk4.x : (i == 1 ? tk4.y : (i == 2 ? tk4.z : tk4.w));
+                val[i] = tki <= t ? qv * rk4[i] * acc[i] : 0.f;
+              }
+            } else {
+              const float gt = gtok[t], rq = rqv[t];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int tki = i == 0 ? tk4.x : (i == 1 ? tk4.y : (i == 2 ? tk4.z : tk4.w));
+                val[i] = tki <= t ? rq * rk4[i] * fexp2(gt - gk4[i]) * acc[i] : 0.f;
               }
             }
           }
+          *(bf16x4 *)((char *)&sm + pw + 32 * ta * LDC) = bf4(val);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      // R = diag(beta) V - lam diag(beta 2^G rk) X, kept in X
+      {
+        const float *bt = sm.beta[ks], *cf = sm.c1[ts];
+        const uint32_t vb = off_of(sm.v[ts]) + lcolv.l;
+        uint32_t va[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) va[b] = (lcolv.x ^ (uint32_t)(2 * wcol + 32 * b)) + vb;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int r0 = 16 * a4 + 4 * lg;
+          const f32x4 btv = ld4(bt + r0), coef = ld4(cf + r0) * lam;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const bf16x4 vv = tr8(va[b] + 16 * a4 * VW);
+            const f32x4 vf = f32x4{(float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]};
+            X[a4][b] = btv * vf - coef * X[a4][b];
+          }
+        }
+      }
+      __syncthreads();  // P complete
+      // ---- phase B: E = T R, O^T += E^T P^T, state update, outputs
+      // T fragments (A operand, from T^T through the transposing read)
+      Frag<bf16> tfr[6];
+      {
+        const uint32_t tb = off_of(sm.t) + lt;
+#pragma unroll
+        for (int fi = 0; fi < 6; ++fi) {
+          const int a4 = fi < 2 ? fi : (fi < 4 ? 2 : 3), s = (fi == 3 || fi == 5) ? 1 : 0;
+          tfr[fi].v = __builtin_shufflevector(tr8(tb + (32 * s * LDT + 16 * a4) * 2), tr8(tb + ((32 * s + 16) * LDT + 16 * a4) * 2),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      Frag<bf16> Rb[2][NB];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) from_acc(Rb[s][b], X[2 * s][b], X[2 * s + 1][b]);
+      f32x4 E[4][NB];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          f32x4 acc = mma(tfr[a4 < 2 ? a4 : 2 * a4 - 2], Rb[0][b], zero4());
+          if (a4 >= 2) acc = mma(tfr[2 * a4 - 1], Rb[1][b], acc);
+          E[a4][b] = acc;
+        }
+      // while E forms: the P fragments and the k^T fragments of the first state row block
+      const int tokb0 = tokr[0], tokb1 = tokr[32];
+      Frag<bf16> pf[4][2];
+      {
+        const uint32_t pr = off_of(sm.p) + lp;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            pf[a4][s].v = __builtin_shufflevector(rd8(pr + (16 * a4 * LDC + 32 * s) * 2), rd8(pr + (16 * a4 * LDC + 32 * s + 16) * 2),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const uint32_t kcb = kt + lcolk.l;
+      Frag<bf16> kc[2][2];
+      auto load_kc = [&](int at, int buf) {  // lane lr of tile at: key kap(at, lr / 4, lr % 4)
+        const uint32_t x = (lcolk.x ^ (uint32_t)(64 * (at >> 1))) + kcb + 8 * (at & 1);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          kc[buf][h2].v = __builtin_shufflevector(tr8(x + 32 * h2 * KW), tr8(x + (32 * h2 + 16) * KW), 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      load_kc(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      Frag<bf16> Eb[2][NB];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if ((s ? tokb1 : tokb0) > 16 * a4 + 15) continue;  // P block entirely masked
+#pragma unroll
+          for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pf[a4][s], O[b][a4]);
+        }
+      // Sst += K^T diag(2^(G_last - G) rk / (lam 2^G_last)) E and lam *= 2^G_last, unless
+      // lam would fall below LAM_MIN (then Sst is rescaled to lam = 1)
+      const float glast = sm.gdp[ks][CH - 1];
+      const float dl = lam * fexp2(glast);
+      const bool lazy = dl >= LAM_MIN;
+      const float rl = lazy ? 1.f / dl : 1.f;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 f = ld4(sm.wgt[ts] + 16 * a4 + 4 * lg) * rl;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) E[a4][b] *= f;
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
+      if (!lazy) {
+#pragma unroll
+        for (int at = 0; at < KT16; ++at)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) Sacc[at][b] *= dl;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int at = 0; at < KT16; ++at) {
+        if (at + 1 < KT16) load_kc(at + 1, (at + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          Sacc[at][b] = mma(kc[at & 1][0], Eb[0][b], Sacc[at][b]);
+          Sacc[at][b] = mma(kc[at & 1][1], Eb[1][b], Sacc[at][b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lam = lazy ? dl : 1.f;
+      // outputs of token chunk c once its last expanded chunk is in: lane holds
+      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in rq)
+      if (j == n - 1 || e == nexp - 1) {
+        const int ntok = toks_of(c);
+        const uint32_t ost = (uint32_t)a.o_st * 2u;
+        uint32_t lo = (uint32_t)lr * ost + (uint32_t)(8 * lg);
+        asm volatile("" : "+v"(lo));
+        char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol) + lo;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          if (16 * a4 + lr < ntok) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) *(bf16x4 *)(ob + (uint32_t)(16 * a4) * ost + 32 * b) = bf4(O[b][a4]);
+          }
+        }
+      }
       __syncthreads();
     }
     float *fdst = a.final_state ? a.final_state + state_off : nullptr;
@@ -1383,80 +1397,269 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const size_t off = (size_t)(16 * at + 4 * lg + i) * V + gcol + 16 * b + lr;
+          const size_t off = (size_t)kap(at, lg, i) * V + gcol + 16 * b + lr;
           const float x = lam * Sacc[at][b][i];
           if (fdst) fdst[off] = x;
           if (cdst) cdst[off] = x;
         }
-  } else if (w == 4) {
-    // WY wave: T of chunk 0 in the prologue, then T of chunk e+1 during chunk e
-    // (its k rows and raw scalars landed before the barrier that opened chunk e)
-    if (nexp > 0) {
-      __syncthreads();
-      wy_wave_a<K, LDA>(sm.k[0], sm.rawb[0], sm.rawg[0], sm.beta[0], sm.gdp[0], sm.rk[0], sm.wa, rows_of(0), 0, n,
-                        a.l2norm, lane);
-      wy_wave_b<LDA>(sm.wa, sm.t[0], lane);
-      __syncthreads();
-    }
-    for (int e = 0; e < nexp; ++e) {
-      const bool has = e + 1 < nexp;
-      const int k1 = (e + 1) % 3;
-      if (has)
-        wy_wave_a<K, LDA>(sm.k[k1], sm.rawb[k1], sm.rawg[k1], sm.beta[k1], sm.gdp[k1], sm.rk[k1], sm.wa,
-                          rows_of(e + 1), (int)(((int64_t)CH * (e + 1)) % n), n, a.l2norm, lane);
-      __syncthreads();
-      if (has) wy_wave_b<LDA>(sm.wa, sm.t[(e + 1) & 1], lane);
-      __syncthreads();
-    }
-  } else if (w == 5) {
-    // k rows: chunks 0 and 1 in the prologue, chunk e+2 during chunk e
-    if (nexp > 0) {
-      load_k(0);
-      if (nexp > 1) load_k(1);
-      wait_vm();
-      __syncthreads();
-      __syncthreads();
-    }
-    for (int e = 0; e < nexp; ++e) {
-      if (e + 2 < nexp) load_k(e + 2);
-      __syncthreads();
-      wait_vm();
-      __syncthreads();
-    }
-  } else if (w == 6) {
-    // v rows: chunk 0 in the prologue, chunk e+1 during chunk e
-    if (nexp > 0) {
-      load_v(0);
-      wait_vm();
-      __syncthreads();
-      __syncthreads();
-    }
-    for (int e = 0; e < nexp; ++e) {
-      if (e + 1 < nexp) load_v(e + 1);
-      __syncthreads();
-      wait_vm();
-      __syncthreads();
-    }
   } else {
-    // betas and decays of chunk e+2, q rows of token chunk c+1 from the start of
-    // token chunk c, and their norms and decay cumsum once they have landed
+    // ---------------------------------------------------------------- helpers
+    // Four helper waves share the loads and the WY step.  For chunk x the WY
+    // step runs as a three-stage pipeline:
+    //   Gram stage   (iteration x-1, before the mid-chunk barrier): helpers 1-3
+    //                form the 10 Gram tiles (row blocks 0-1, 2, 3) and the k-row
+    //                rstd from the diagonal tiles;
+    //   block stage  (iteration x-1, after it): helper h builds row block h of
+    //                A and inverts its diagonal block by DPP row substitution;
+    //   merge stage  (iteration x, before the mid-chunk barrier): helper 0 forms
+    //                the blocks of T below the diagonal and writes T^T, which the
+    //                consumers read after that barrier.
+    // The loads are spread over the four helpers as well.
+    const int hw = w - 4;
+    const bf16 *qg = (const bf16 *)a.q + hq * a.q_sh;
+    const bf16 *kg = (const bf16 *)a.k + hq * a.k_sh;
+    const bf16 *vg = (const bf16 *)a.v + h * a.v_sh + vt * BV;
+    const float *gg = a.g + h * a.g_sh;
+    const float *bg = a.beta + h * a.b_sh;
+    const uint32_t kst = (uint32_t)a.k_st * 2u, vst = (uint32_t)a.v_st * 2u, qst = (uint32_t)a.q_st * 2u;
+    auto load_k = [&](int e) {
+      tile_load<KW>(sm.k[e % 3], (const char *)(kg + (t0 * n + (int64_t)CH * e) * a.k_st), kst, rows_of(e), lane);
+    };
+    auto load_v = [&](int e) {
+      tile_load<VW>(sm.v[e & 1], (const char *)(vg + (t0 * n + (int64_t)CH * e) * a.v_st), vst, rows_of(e), lane);
+    };
+    auto load_scalars = [&](int e) {  // raw beta and decay of each sub-row of chunk e
+      const int64_t s0 = (int64_t)CH * e;
+      const int r = min(lane, rows_of(e) - 1);
+      const int64_t tok = (s0 + r) / n;
+      scalar_load(sm.rawb[e & 1], bg + (t0 * n + s0 + r) * a.b_st);
+      scalar_load(sm.rawg[e & 1], gg + (t0 + tok) * a.g_st);
+    };
+    auto prep_scalars = [&](int e) {  // masked betas and the base-2 decay cumsum of chunk e
+      const bool valid = lane < rows_of(e);
+      const int rem = (int)(((int64_t)CH * e) % n);
+      const bool first = valid && (rem + lane) % n == 0;  // the decay sits on a token's first sub-row
+      sm.gdp[e % 3][lane] = wave_scan(first ? sm.rawg[e & 1][lane] * LOG2E : 0.f);
+      sm.beta[e % 3][lane] = valid ? sm.rawb[e & 1][lane] : 0.f;
+    };
+    auto load_q = [&](int c) {  // q rows and token decays of token chunk c
+      const int64_t tokbase = t0 + (int64_t)CH * c;
+      tile_load<KW>(sm.q[c & 1], (const char *)(qg + tokbase * a.q_st), qst, toks_of(c), lane);
+      scalar_load(sm.rawt[c & 1], gg + (tokbase + min(lane, toks_of(c) - 1)) * a.g_st);
+    };
+    auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
+      const int sl = c & 1, ntok = toks_of(c);
+      float ss = 0.f;
+      if (a.l2norm) {
+#pragma unroll
+        for (int sg = 0; sg < KW / 16; ++sg) ss += seg_sumsq<bf16>(*(const uint4 *)(sm.q[sl] + sw_off<KW>(lane, 16 * sg)));
+      }
+      const float rq = a.scale * (a.l2norm ? frsq(ss + 1e-6f) : 1.f);
+      const float gt = wave_scan(lane < ntok ? sm.rawt[sl][lane] * LOG2E : 0.f);
+      sm.rq[sl][lane] = rq;
+      sm.gtok[sl][lane] = gt;
+      sm.qfac[sl][lane] = rq * fexp2(gt);
+      // the cumsum is non-increasing, so its last valid entry is its minimum
+      const float gmin = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gt), ntok - 1));
+      if (lane == 0) sm.qsafe[sl] = gmin > -100.f;
+    };
+    auto tables = [&](int e) {  // token of each row of chunk e inside its token chunk, and its decay cumsum
+      const int c = e / n, j = e - c * n;
+      const int tk = (CH * j + lane) / n;
+      const float gk = sm.gtok[c & 1][tk];
+      sm.tokr[e & 1][lane] = tk;
+      sm.gkr[e & 1][lane] = gk;
+      sm.rkg[e & 1][lane] = sm.rk[e & 1][lane] * fexp2(-gk);  // overflow-free when qsafe
+    };
+    // Gram stage of chunk x: tiles [i0, i1) of the lower triangle, with the k rows
+    // of the later block as the B operand so that lane (lg, lr) of tile (ra, rb)
+    // holds G[16 ra + lr][16 rb + 4 lg + i]; rstd of the rows of its diagonal tiles
+    auto gram = [&](int x, int i0, int i1, int nblk) {
+      const char *k = sm.k[x % 3];
+      float *rk = sm.rk[x & 1];
+      const int nrow = rows_of(x);
+      Frag<bf16> kf[4][KS];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        if (rt < nblk) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) kf[rt][s] = sw_contig<KW>(k, 16 * rt + lr, 32 * s, lg);
+        }
+#pragma unroll
+      for (int idx = 0; idx < 10; ++idx) {
+        if (idx < i0 || idx >= i1) continue;
+        int ra, rb;
+        lower_tile(idx, ra, rb);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mma(kf[rb][s], kf[ra][s], acc);
+        *(f32x4 *)(sm.gram[idx] + 4 * lane) = acc;
+        if (ra == rb) {  // lane with 4 lg + i == lr holds the squared norm of row 16 ra + lr
+          const int i = lr & 3;
+          const float dv = i == 0 ? acc[0] : (i == 1 ? acc[1] : (i == 2 ? acc[2] : acc[3]));
+          if ((lr >> 2) == lg) rk[16 * ra + lr] = (16 * ra + lr < nrow) ? (a.l2norm ? frsq(dv + 1e-6f) : 1.f) : 0.f;
+        }
+      }
+    };
+    // block stage of chunk x, row block hb: A[r][c] = beta_r rk_r rk_c 2^(G_r - G_c) G[r][c]
+    // for c < r, the inverse of the diagonal block, and the consumers' row weights
+    auto block = [&](int x, auto hbc) {
+      constexpr int hb = decltype(hbc)::value;
+      const float *bt = sm.beta[x % 3], *gd = sm.gdp[x % 3], *rk = sm.rk[x & 1];
+      const int r = 16 * hb + lr;
+      const float fr = bt[r] * rk[r], gr = gd[r];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b > hb) continue;
+        const int idx = hb * (hb + 1) / 2 + b, c0 = 16 * b + 4 * lg;
+        const f32x4 g = *(const f32x4 *)(sm.gram[idx] + 4 * lane);
+        const f32x4 rc = ld4(rk + c0), gc = ld4(gd + c0);
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = fr * rc[i] * fexp2(gr - gc[i]) * g[i];
+        if (b < hb) {
+          *(bf16x4 *)(sm.alow[idx - hb] + 4 * lane) = bf4(v);  // idx - hb enumerates (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+        } else {  // rows of -L of the diagonal block over the Gram tile just read: the
+                  // 16-byte piece q of row lr at lr * 64 + 16 (q ^ (lr / 4 mod 4)), so that
+                  // 16 lanes writing one piece of 16 rows meet distinct banks
+          float *dg = sm.gram[idx];
+          const int sx = (lr >> 2) & 3;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (c0 + i < r) ? -v[i] : 0.f;
+          *(f32x4 *)(dg + lr * 16 + 4 * (lg ^ sx)) = v;
+          float nl[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 u = ld4(dg + lr * 16 + 4 * (q4 ^ sx));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nl[4 * q4 + i] = u[i];
+          }
+          float tdg[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tdg[i] = (lr == 4 * lg + i) ? 1.f : 0.f;
+          subst<0>(tdg, nl);
+          const bf16x4 tb = bf16x4{(bf16)tdg[0], (bf16)tdg[1], (bf16)tdg[2], (bf16)tdg[3]};
+          *(bf16x4 *)(sm.tdiag[hb] + 4 * lane) = tb;
+          *(bf16x4 *)(sm.tdrow[hb] + lr * 16 + 4 * lg) = tb;
+        }
+      }
+      if (lg == 0) {  // per-row weights of the consumers' R and state update
+        const float glast = gd[CH - 1];
+        sm.c1[x & 1][r] = bt[r] * fexp2(gr) * rk[r];
+        sm.wgt[x & 1][r] = fexp2(glast - gr) * rk[r];
+      }
+    };
+    // merge stage: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb below the diagonal, and
+    // T^T into the consumers' buffer (entry (r, c) of T at [c * LDT + r])
+    auto merge = [&]() {
+      bf16 *tt = sm.t;
+      bf16x4 tc[4], tn[4], al[6];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        tc[b] = tr_col4(sm.tdrow[b], 16, 4 * lg, 0, lr);  // T_b[4lg + i][lr]
+        tn[b] = -*(const bf16x4 *)(sm.tdiag[b] + 4 * lane);
+        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + 4 * lg) = tc[b];
+      }
+#pragma unroll
+      for (int i = 0; i < 6; ++i) al[i] = *(const bf16x4 *)(sm.alow[i] + 4 * lane);
+      auto put = [&](int ra, int rb, f32x4 v) {  // v: T[16 ra + 4 lg + i][16 rb + lr]
+        const bf16x4 x4 = bf4(v);
+        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + 4 * lg) = x4;
+        return x4;
+      };
+      // distance 1
+      const bf16x4 t10 = put(1, 0, mma16(tn[1], bf4(mma16(al[0], tc[0], zero4())), zero4()));
+      const bf16x4 t21 = put(2, 1, mma16(tn[2], bf4(mma16(al[2], tc[1], zero4())), zero4()));
+      put(3, 2, mma16(tn[3], bf4(mma16(al[5], tc[2], zero4())), zero4()));
+      // distance 2
+      const bf16x4 t20 = put(2, 0, mma16(tn[2], bf4(mma16(al[2], t10, mma16(al[1], tc[0], zero4()))), zero4()));
+      put(3, 1, mma16(tn[3], bf4(mma16(al[5], t21, mma16(al[4], tc[1], zero4()))), zero4()));
+      // distance 3
+      put(3, 0, mma16(tn[3], bf4(mma16(al[5], t20, mma16(al[4], t10, mma16(al[3], tc[0], zero4())))), zero4()));
+    };
+    if (hw == 0) {
+      // the two T^T blocks above the diagonal that the consumers' fragments cover
+      // ((0,1) and (2,3) of T) stay zero; nothing else writes them
+      for (int u = lane; u < 2 * 16 * 2; u += 64) {
+        const int blk = u >> 5, row = (u >> 1) & 15, half = u & 1;
+        *(uint4 *)(sm.t + (16 + 32 * blk + row) * LDT + 32 * blk + 8 * half) = uint4{0u, 0u, 0u, 0u};
+      }
+    }
+    // Work per helper and chunk e (WY stages for chunk e+1):
+    //   helper 0: betas/decays of chunk e+2 | merge stage   || row block 0 | their tables
+    //   helper 1: k rows of chunk e+2      | Gram tiles 0-2 || row block 1
+    //   helper 2: v rows of chunk e+1      | Gram tiles 3-5 || row block 2
+    //   helper 3: q rows of token chunk c+1 | Gram tiles 6-9 || row block 3 | q norms, row tables
     if (nexp > 0) {
-      load_scalars(0);
-      if (nexp > 1) load_scalars(1);
-      load_q(0);
-      wait_vm();
-      finish_q(0);
+      // prologue: rows of chunks 0 and 1, the tables of chunk 0, and the first two
+      // WY stages of chunk 0
+      if (hw == 0) {
+        load_scalars(0);
+        if (nexp > 1) load_scalars(1);
+        wait_vm();
+        prep_scalars(0);
+        if (nexp > 1) prep_scalars(1);
+      } else if (hw == 1) {
+        load_k(0);
+        if (nexp > 1) load_k(1);
+        wait_vm();
+      } else if (hw == 2) {
+        load_v(0);
+        wait_vm();
+      } else {
+        load_q(0);
+        wait_vm();
+        finish_q(0);
+      }
       __syncthreads();
+      if (hw == 1) gram(0, 0, 3, 2);
+      else if (hw == 2) gram(0, 3, 6, 3);
+      else if (hw == 3) gram(0, 6, 10, 4);
+      __syncthreads();
+      if (hw == 0) block(0, IC<0>{});
+      else if (hw == 1) block(0, IC<1>{});
+      else if (hw == 2) block(0, IC<2>{});
+      else {
+        block(0, IC<3>{});
+        tables(0);
+      }
       __syncthreads();
     }
     for (int e = 0; e < nexp; ++e) {
       const int c = e / n;
       const int j = e - c * n;
-      if (e + 2 < nexp) load_scalars(e + 2);
-      if (j == 0 && c + 1 < ntc) load_q(c + 1);
+      const bool next = e + 1 < nexp;
+      if (hw == 0) {
+        if (e + 2 < nexp) load_scalars(e + 2);
+        merge();
+      } else if (hw == 1) {
+        if (e + 2 < nexp) load_k(e + 2);
+        if (next) gram(e + 1, 0, 3, 2);
+      } else if (hw == 2) {
+        if (next) load_v(e + 1);
+        if (next) gram(e + 1, 3, 6, 3);
+      } else {
+        if (j == 0 && c + 1 < ntc) load_q(c + 1);
+        if (next) gram(e + 1, 6, 10, 4);
+      }
       __syncthreads();
-      wait_vm();
-      if ((e + 1) % n == 0 && c + 1 < ntc) finish_q(c + 1);
+      // the block stage needs none of this chunk's loads: they land meanwhile
+      if (hw == 0) {
+        if (next) block(e + 1, IC<0>{});
+        wait_vm();
+        if (e + 2 < nexp) prep_scalars(e + 2);
+      } else if (hw == 1) {
+        if (next) block(e + 1, IC<1>{});
+        wait_vm();
+      } else if (hw == 2) {
+        if (next) block(e + 1, IC<2>{});
+        wait_vm();
+      } else {
+        if (next) block(e + 1, IC<3>{});
+        wait_vm();
+        if ((e + 1) % n == 0 && c + 1 < ntc) finish_q(c + 1);
+        if (next) tables(e + 1);
+      }
       __syncthreads();
     }
   }
