@@ -1015,6 +1015,38 @@ __device__ __forceinline__ void tile_load(char *tile, const char *g, uint32_t rs
                                      (__attribute__((address_space(3))) void *)(tile + i * 1024), 16, 0, 0);
   }
 }
+// The same for a full tile, with the per-lane source offsets of its 64*W/1024
+// loads computed once (they depend only on the row stride): the loads then take
+// a uniform base plus a 32-bit lane offset and need no address arithmetic.
+// Lane offsets of a full 64-row tile load.  Row r = RPI i + lane / NS of load i
+// has the swizzle of r mod 16 (256-byte rows) or r mod 8 (128-byte rows), so
+// only PER distinct lane offsets exist; the row offset RPI i rs is uniform.
+template <int W> struct TileOffs {
+  static constexpr int NS = W / 16, RPI = 64 / NS, PER = (NS == 16 ? 16 : 8) / RPI;
+  uint32_t o[PER];
+  uint32_t rs;  // row stride in bytes
+};
+template <int W> __device__ __forceinline__ TileOffs<W> tile_offs(uint32_t rstride, int lane) {
+  using TO = TileOffs<W>;
+  TO t;
+  t.rs = rstride;
+#pragma unroll
+  for (int p = 0; p < TO::PER; ++p) {
+    const int r = p * TO::RPI + lane / TO::NS, slot = lane % TO::NS;
+    t.o[p] = (uint32_t)(lane / TO::NS) * rstride + (uint32_t)((slot ^ swz<TO::NS>(r)) << 4);
+  }
+  return t;
+}
+template <int W>
+__device__ __forceinline__ void tile_load_full(char *tile, const char *g, const TileOffs<W> &t) {
+  using TO = TileOffs<W>;
+#pragma unroll
+  for (int i = 0; i < 64 / TO::RPI; ++i) {
+    const char *gr = g + (uint32_t)(i * TO::RPI) * t.rs;  // uniform
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(gr + t.o[i % TO::PER]),
+                                     (__attribute__((address_space(3))) void *)(tile + i * 1024), 16, 0, 0);
+  }
+}
 __device__ __forceinline__ void scalar_load(float *dst, const float *src) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                    (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
@@ -1157,38 +1189,57 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
         }
       }
       f32x4 X[4][NB];
+      // Scores, transposed, of the wave's token block w against all rows: lane
+      // (lg, lr) of tile a4 holds Sc[r = 16 a4 + 4 lg + i][t = 16 w + lr] = k_r.q_t.
+      // They reuse the k fragments of X = K Sst as the A operand.
+      f32x4 Pacc[4];
       // k (and q) fragments of reduction step s+1 are read while step s multiplies
-      Frag<bf16> kf[2][4], qf[2][4];
-      auto load_kq = [&](int s, int buf) {  // reduction slots 32s + 8lg .. +7
-        const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
-        const uint32_t ka = xs + (kt + lcont.l);
+      {
+        Frag<bf16> kf[2][4], qw[2];
+        auto load_k = [&](int s, int buf) {  // reduction slots 32s + 8lg .. +7
+          const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) kf[buf][a4].v = rd16(ka + 16 * a4 * KW);
-        if (j == 0) {
-          const uint32_t qa = xs + (qt + lcont.l);
+          for (int a4 = 0; a4 < 4; ++a4) kf[buf][a4].v = rd16(xs + (kt + lcont.l) + 16 * a4 * KW);
+          qw[buf].v = rd16(xs + (qt + lcont.l) + 16 * w * KW);
+        };
+        load_k(0, 0);
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) qf[buf][a4].v = rd16(qa + 16 * a4 * KW);
+        for (int s = 0; s < KS; ++s) {
+          if (s + 1 < KS) load_k(s + 1, (s + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          Frag<bf16> Sb[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[s & 1][a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) Pacc[a4] = mma(kf[s & 1][a4], qw[s & 1], s == 0 ? zero4() : Pacc[a4]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      load_kq(0, 0);
+      }
+      if (j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
+        Frag<bf16> qf[2][4];
+        auto load_q = [&](int s, int buf) {
+          const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) load_kq(s + 1, (s + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        Frag<bf16> Sb[NB];
+          for (int a4 = 0; a4 < 4; ++a4) qf[buf][a4].v = rd16(xs + (qt + lcont.l) + 16 * a4 * KW);
+        };
+        load_q(0, 0);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+        for (int s = 0; s < KS; ++s) {
+          if (s + 1 < KS) load_q(s + 1, (s + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          Frag<bf16> Sb[NB];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[s & 1][a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
-        if (j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
+          for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
             for (int b = 0; b < NB; ++b) O[b][a4] = mma(Sb[b], qf[s & 1][a4], s == 0 ? zero4() : O[b][a4]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       if (j == 0) {  // O^T columns t times lam scale rq_t 2^Gt_t
 #pragma unroll
@@ -1198,56 +1249,39 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           for (int b = 0; b < NB; ++b) O[b][a4] *= f;
         }
       }
-      // scores, transposed: lane (lg, lr) of tile (ta, w) holds
-      // P[t = 16 ta + lr][r = 16 w + 4 lg + i] = scale rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r  (tok(r) <= t);
-      // the k fragments of the wave's row block serve all four tiles
+      // P[t][r] = scale rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r for tok(r) <= t, i.e. for
+      // r below n (t + 1) - 64 j; written to the P tile as rows t of contiguous r.
+      // When the token chunk's decay cumsum stays above -100 the decay factor is
+      // the product qfac_t rkg_r of per-token and per-row factors (both finite and
+      // normal); otherwise it is formed per entry.
       {
-        const int r0 = 16 * w + 4 * lg;
-        const uint32_t kb0 = kt + lcont.l + (uint32_t)(16 * w * KW), qb0 = qt + lcont.l;
-        Frag<bf16> kb[KS], qb[2][KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kb[s].v = rd16((lcont.x ^ (uint32_t)(64 * s)) + kb0);
-        const int tok0 = tokr[16 * w];  // tok(r) is non-decreasing in r
-        auto load_q = [&](int ta, int buf) {
-#pragma unroll
-          for (int s = 0; s < KS; ++s) qb[buf][s].v = rd16((lcont.x ^ (uint32_t)(64 * s)) + qb0 + 16 * ta * KW);
-        };
-        // when the token chunk's decay cumsum stays above -100, 2^(Gt_t - Gt_tok(r)) is
-        // formed as the product qfac_t rkg_r of per-token and per-row factors (both
-        // finite and normal); otherwise per entry
+        const int t = 16 * w + lr;
+        const int rlim = n * (t + 1) - CH * j;
         const bool fact = sm.qsafe[qs] != 0;
-        const f32x4 rk4 = ld4((fact ? sm.rkg[ts] : rk) + r0), gk4 = ld4(gkr + r0);
-        const int4 tk4 = *(const int4 *)(tokr + r0);
-        const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * w);
-        load_q(0, 0);
+        const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * w * LDC);
+        if (fact) {
+          const float qv = qfac[t];
+          const float *rkg = sm.rkg[ts];
 #pragma unroll
-        for (int ta = 0; ta < 4; ++ta) {
-          if (ta + 1 < 4) load_q(ta + 1, (ta + 1) & 1);
-          __builtin_amdgcn_sched_barrier(0);
-          const int t = 16 * ta + lr;
-          f32x4 val = zero4();
-          if (tok0 <= 16 * ta + 15) {
-            f32x4 acc = zero4();
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int r0 = 16 * a4 + 4 * lg;
+            const f32x4 f4 = ld4(rkg + r0) * qv;
+            f32x4 val;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mma(kb[s], qb[ta & 1][s], acc);
-            if (fact) {
-              const float qv = qfac[t];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int tki = i == 0 ? tk4.x : (i == 1 ? tk4.y : (i == 2 ? tk4.z : tk4.w));
-                val[i] = tki <= t ? qv * rk4[i] * acc[i] : 0.f;
-              }
-            } else {
-              const float gt = gtok[t], rq = rqv[t];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int tki = i == 0 ? tk4.x : (i == 1 ? tk4.y : (i == 2 ? tk4.z : tk4.w));
-                val[i] = tki <= t ? rq * rk4[i] * fexp2(gt - gk4[i]) * acc[i] : 0.f;
-              }
-            }
+            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? f4[i] * Pacc[a4][i] : 0.f;
+            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
           }
-          *(bf16x4 *)((char *)&sm + pw + 32 * ta * LDC) = bf4(val);
-          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          const float gt = gtok[t], rq = rqv[t];
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int r0 = 16 * a4 + 4 * lg;
+            const f32x4 rk4 = ld4(rk + r0), gk4 = ld4(gkr + r0);
+            f32x4 val;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? rq * rk4[i] * fexp2(gt - gk4[i]) * Pacc[a4][i] : 0.f;
+            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+          }
         }
       }
       // R = diag(beta) V - lam diag(beta 2^G rk) X, kept in X
@@ -1310,7 +1344,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
                                                   0, 1, 2, 3, 4, 5, 6, 7);
       }
       const uint32_t kcb = kt + lcolk.l;
-      Frag<bf16> kc[2][2];
+      Frag<bf16> kc[3][2];
       auto load_kc = [&](int at, int buf) {  // lane lr of tile at: key kap(at, lr / 4, lr % 4)
         const uint32_t x = (lcolk.x ^ (uint32_t)(64 * (at >> 1))) + kcb + 8 * (at & 1);
 #pragma unroll
@@ -1318,6 +1352,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           kc[buf][h2].v = __builtin_shufflevector(tr8(x + 32 * h2 * KW), tr8(x + (32 * h2 + 16) * KW), 0, 1, 2, 3, 4, 5, 6, 7);
       };
       load_kc(0, 0);
+      load_kc(1, 1);
       __builtin_amdgcn_sched_barrier(0);
       Frag<bf16> Eb[2][NB];
 #pragma unroll
@@ -1356,32 +1391,28 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int at = 0; at < KT16; ++at) {
-        if (at + 1 < KT16) load_kc(at + 1, (at + 1) & 1);
+      for (int at = 0; at < KT16; ++at) {  // k^T fragments two steps ahead
+        if (at + 2 < KT16) load_kc(at + 2, (at + 2) % 3);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          Sacc[at][b] = mma(kc[at & 1][0], Eb[0][b], Sacc[at][b]);
-          Sacc[at][b] = mma(kc[at & 1][1], Eb[1][b], Sacc[at][b]);
+          Sacc[at][b] = mma(kc[at % 3][0], Eb[0][b], Sacc[at][b]);
+          Sacc[at][b] = mma(kc[at % 3][1], Eb[1][b], Sacc[at][b]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       lam = lazy ? dl : 1.f;
       // outputs of token chunk c once its last expanded chunk is in: lane holds
-      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in rq)
+      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in rq).
+      // They are staged in bf16 in this chunk's v tile (unused after the R step)
+      // and helper 2 stores whole rows from there at the start of the next chunk.
       if (j == n - 1 || e == nexp - 1) {
-        const int ntok = toks_of(c);
-        const uint32_t ost = (uint32_t)a.o_st * 2u;
-        uint32_t lo = (uint32_t)lr * ost + (uint32_t)(8 * lg);
-        asm volatile("" : "+v"(lo));
-        char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol) + lo;
+        char *stg = sm.v[ts];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          if (16 * a4 + lr < ntok) {
+        for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) *(bf16x4 *)(ob + (uint32_t)(16 * a4) * ost + 32 * b) = bf4(O[b][a4]);
-          }
-        }
+          for (int b = 0; b < NB; ++b)
+            *(bf16x4 *)(stg + sw_off<VW>(16 * a4 + lr, 2 * (wcol + 16 * b + 4 * lg))) = bf4(O[b][a4]);
       }
       __syncthreads();
     }
@@ -1422,11 +1453,15 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     const float *gg = a.g + h * a.g_sh;
     const float *bg = a.beta + h * a.b_sh;
     const uint32_t kst = (uint32_t)a.k_st * 2u, vst = (uint32_t)a.v_st * 2u, qst = (uint32_t)a.q_st * 2u;
-    auto load_k = [&](int e) {
-      tile_load<KW>(sm.k[e % 3], (const char *)(kg + (t0 * n + (int64_t)CH * e) * a.k_st), kst, rows_of(e), lane);
+    auto load_k = [&](int e, const TileOffs<KW> &offs) {
+      const char *g = (const char *)(kg + (t0 * n + (int64_t)CH * e) * a.k_st);
+      if (rows_of(e) == CH) tile_load_full<KW>(sm.k[e % 3], g, offs);
+      else tile_load<KW>(sm.k[e % 3], g, kst, rows_of(e), lane);
     };
-    auto load_v = [&](int e) {
-      tile_load<VW>(sm.v[e & 1], (const char *)(vg + (t0 * n + (int64_t)CH * e) * a.v_st), vst, rows_of(e), lane);
+    auto load_v = [&](int e, const TileOffs<VW> &offs) {
+      const char *g = (const char *)(vg + (t0 * n + (int64_t)CH * e) * a.v_st);
+      if (rows_of(e) == CH) tile_load_full<VW>(sm.v[e & 1], g, offs);
+      else tile_load<VW>(sm.v[e & 1], g, vst, rows_of(e), lane);
     };
     auto load_scalars = [&](int e) {  // raw beta and decay of each sub-row of chunk e
       const int64_t s0 = (int64_t)CH * e;
@@ -1442,9 +1477,11 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       sm.gdp[e % 3][lane] = wave_scan(first ? sm.rawg[e & 1][lane] * LOG2E : 0.f);
       sm.beta[e % 3][lane] = valid ? sm.rawb[e & 1][lane] : 0.f;
     };
-    auto load_q = [&](int c) {  // q rows and token decays of token chunk c
+    auto load_q = [&](int c, const TileOffs<KW> &offs) {  // q rows and token decays of token chunk c
       const int64_t tokbase = t0 + (int64_t)CH * c;
-      tile_load<KW>(sm.q[c & 1], (const char *)(qg + tokbase * a.q_st), qst, toks_of(c), lane);
+      const char *g = (const char *)(qg + tokbase * a.q_st);
+      if (toks_of(c) == CH) tile_load_full<KW>(sm.q[c & 1], g, offs);
+      else tile_load<KW>(sm.q[c & 1], g, qst, toks_of(c), lane);
       scalar_load(sm.rawt[c & 1], gg + (tokbase + min(lane, toks_of(c) - 1)) * a.g_st);
     };
     auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
@@ -1585,82 +1622,132 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
         *(uint4 *)(sm.t + (16 + 32 * blk + row) * LDT + 32 * blk + 8 * half) = uint4{0u, 0u, 0u, 0u};
       }
     }
-    // Work per helper and chunk e (WY stages for chunk e+1):
-    //   helper 0: betas/decays of chunk e+2 | merge stage   || row block 0 | their tables
-    //   helper 1: k rows of chunk e+2      | Gram tiles 0-2 || row block 1
-    //   helper 2: v rows of chunk e+1      | Gram tiles 3-5 || row block 2
-    //   helper 3: q rows of token chunk c+1 | Gram tiles 6-9 || row block 3 | q norms, row tables
-    if (nexp > 0) {
-      // prologue: rows of chunks 0 and 1, the tables of chunk 0, and the first two
-      // WY stages of chunk 0
-      if (hw == 0) {
+    // output rows of the chunk eo, staged by the consumers in its v tile: whole
+    // 16-byte pieces of rows (8-byte pieces when o is not 16-byte aligned)
+    const bool o16 = (((uintptr_t)a.o & 15) == 0) && (a.o_st % 8 == 0) && (a.o_sh % 8 == 0);
+    auto store_o = [&](int eo) {
+      constexpr int NS = VW / 16, RPI = 1024 / VW, NI = CH / RPI;
+      const int c = eo / n, ntok = toks_of(c);
+      const char *stg = sm.v[eo & 1];
+      char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + vt * BV);
+      const uint32_t ost = (uint32_t)a.o_st * 2u;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {  // two batches of reads, then stores
+        uint4 x[NI / 2];
+#pragma unroll
+        for (int i = 0; i < NI / 2; ++i)
+          x[i] = *(const uint4 *)(stg + sw_off<VW>((hf * NI / 2 + i) * RPI + lane / NS, 16 * (lane % NS)));
+#pragma unroll
+        for (int i = 0; i < NI / 2; ++i) {
+          const int r = (hf * NI / 2 + i) * RPI + lane / NS;
+          if (r < ntok) {
+            char *dst = ob + (uint32_t)r * ost + 16 * (lane % NS);
+            if (o16) {
+              *(uint4 *)dst = x[i];
+            } else {
+              *(uint2 *)dst = uint2{x[i].x, x[i].y};
+              *(uint2 *)(dst + 8) = uint2{x[i].z, x[i].w};
+            }
+          }
+        }
+      }
+    };
+    // Work per helper and chunk e (WY stages for chunk e+1), before || after the
+    // mid-chunk barrier:
+    //   helper 0: k rows and betas/decays of chunk e+2,  || v rows of chunk e+1,
+    //             q rows of token chunk c+1                 masked betas and decay
+    //                                                       cumsum, q norms, row tables
+    //   helper 1: merge stage                               || row block 3
+    //   helper 2: Gram tiles 0-4                            || row blocks 0, 1
+    //   helper 3: outputs of chunk e-1, Gram tiles 5-9      || row block 2
+    // Helper 0 issues every direct-to-LDS load and touches LDS only where none
+    // of its loads is in flight: the compiler makes any LDS access that follows
+    // such a load in the same wave wait for it, which would otherwise stall the
+    // WY stages on HBM latency.
+    // Each helper runs its own loop (the same barrier sequence as the consumers:
+    // three in the prologue, two per chunk) so that its registers are its own.
+    if (hw == 0) {
+      const TileOffs<KW> koffs = tile_offs<KW>(kst, lane), qoffs = tile_offs<KW>(qst, lane);
+      const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
+      if (nexp > 0) {
+        load_k(0, koffs);
+        if (nexp > 1) load_k(1, koffs);
+        load_v(0, voffs);
         load_scalars(0);
         if (nexp > 1) load_scalars(1);
+        load_q(0, qoffs);
         wait_vm();
         prep_scalars(0);
         if (nexp > 1) prep_scalars(1);
-      } else if (hw == 1) {
-        load_k(0);
-        if (nexp > 1) load_k(1);
-        wait_vm();
-      } else if (hw == 2) {
-        load_v(0);
-        wait_vm();
-      } else {
-        load_q(0);
-        wait_vm();
         finish_q(0);
-      }
-      __syncthreads();
-      if (hw == 1) gram(0, 0, 3, 2);
-      else if (hw == 2) gram(0, 3, 6, 3);
-      else if (hw == 3) gram(0, 6, 10, 4);
-      __syncthreads();
-      if (hw == 0) block(0, IC<0>{});
-      else if (hw == 1) block(0, IC<1>{});
-      else if (hw == 2) block(0, IC<2>{});
-      else {
-        block(0, IC<3>{});
+        __syncthreads();
+        __syncthreads();
         tables(0);
+        __syncthreads();
       }
-      __syncthreads();
-    }
-    for (int e = 0; e < nexp; ++e) {
-      const int c = e / n;
-      const int j = e - c * n;
-      const bool next = e + 1 < nexp;
-      if (hw == 0) {
-        if (e + 2 < nexp) load_scalars(e + 2);
-        merge();
-      } else if (hw == 1) {
-        if (e + 2 < nexp) load_k(e + 2);
-        if (next) gram(e + 1, 0, 3, 2);
-      } else if (hw == 2) {
-        if (next) load_v(e + 1);
-        if (next) gram(e + 1, 3, 6, 3);
-      } else {
-        if (j == 0 && c + 1 < ntc) load_q(c + 1);
-        if (next) gram(e + 1, 6, 10, 4);
-      }
-      __syncthreads();
-      // the block stage needs none of this chunk's loads: they land meanwhile
-      if (hw == 0) {
-        if (next) block(e + 1, IC<0>{});
+      for (int e = 0; e < nexp; ++e) {
+        const int c = e / n;
+        const int j = e - c * n;
+        if (e + 2 < nexp) {
+          load_k(e + 2, koffs);
+          load_scalars(e + 2);
+        }
+        if (j == 0 && c + 1 < ntc) load_q(c + 1, qoffs);
+        __syncthreads();
+        if (e + 1 < nexp) load_v(e + 1, voffs);  // its tile is free once the R step is done
         wait_vm();
         if (e + 2 < nexp) prep_scalars(e + 2);
-      } else if (hw == 1) {
-        if (next) block(e + 1, IC<1>{});
-        wait_vm();
-      } else if (hw == 2) {
-        if (next) block(e + 1, IC<2>{});
-        wait_vm();
-      } else {
-        if (next) block(e + 1, IC<3>{});
-        wait_vm();
         if ((e + 1) % n == 0 && c + 1 < ntc) finish_q(c + 1);
-        if (next) tables(e + 1);
+        if (e + 1 < nexp) tables(e + 1);
+        __syncthreads();
       }
-      __syncthreads();
+    } else if (hw == 1) {
+      if (nexp > 0) {
+        __syncthreads();
+        __syncthreads();
+        block(0, IC<3>{});
+        __syncthreads();
+      }
+      for (int e = 0; e < nexp; ++e) {
+        merge();
+        __syncthreads();
+        if (e + 1 < nexp) block(e + 1, IC<3>{});
+        __syncthreads();
+      }
+    } else if (hw == 2) {
+      if (nexp > 0) {
+        __syncthreads();
+        gram(0, 0, 5, 3);
+        __syncthreads();
+        block(0, IC<0>{});
+        block(0, IC<1>{});
+        __syncthreads();
+      }
+      for (int e = 0; e < nexp; ++e) {
+        if (e + 1 < nexp) gram(e + 1, 0, 5, 3);
+        __syncthreads();
+        if (e + 1 < nexp) {
+          block(e + 1, IC<0>{});
+          block(e + 1, IC<1>{});
+        }
+        __syncthreads();
+      }
+    } else {
+      if (nexp > 0) {
+        __syncthreads();
+        gram(0, 5, 10, 4);
+        __syncthreads();
+        block(0, IC<2>{});
+        __syncthreads();
+      }
+      for (int e = 0; e < nexp; ++e) {
+        if (e >= 1 && e % n == 0) store_o(e - 1);
+        if (e + 1 < nexp) gram(e + 1, 5, 10, 4);
+        __syncthreads();
+        if (e + 1 < nexp) block(e + 1, IC<2>{});
+        __syncthreads();
+      }
+      if (nexp > 0) store_o(nexp - 1);
     }
   }
 }
