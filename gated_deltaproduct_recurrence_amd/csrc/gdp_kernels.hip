@@ -156,10 +156,10 @@ template <typename T> __device__ __forceinline__ float seg_sumsq(const uint4 &s)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t w = word_of(s, i);
-    if constexpr (sizeof(T) == 2) {
-      const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
-      a = fmaf(lo, lo, a);
-      a = fmaf(hi, hi, a);
+    if constexpr (sizeof(T) == 2) {  // both bf16 squares of the word in one v_dot2c_f32_bf16
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+      a = __builtin_amdgcn_fdot2_f32_bf16(v, v, a, false);
     } else {
       const float x = __uint_as_float(w);
       a = fmaf(x, x, a);
@@ -884,15 +884,16 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
 // One workgroup of 8 waves per (sequence, state head) does the whole chunked
 // pass, WY step included, so the per-chunk WY matrix never leaves the CU:
 //   waves 0-3  consumers: the state S (fp32 accumulators, one 16*NB-column slab
-//              per wave), X = K S, the scores, R, E = T R, the outputs and the
-//              state update of expanded chunk e;
-//   wave  4    WY wave: the Gram matrix, k-row norms, A and T = (I + A)^-1 of
-//              chunk e+1, plus the per-row coefficients the consumers use;
-//   waves 5-7  loaders: direct global->LDS loads of the k rows of chunk e+2
-//              (3-slot ring), the v rows of chunk e+1, the betas and decays of
-//              chunk e+2 and the q rows of the next token chunk (2-slot rings);
-//              wave 7 also forms the masked betas, the decay cumsums, the q-row
-//              norms and the per-row token tables.
+//              per wave), X = K S, the scores, R, E = T R, the state update of
+//              expanded chunk e, and the outputs, staged in LDS;
+//   waves 4-7  helpers: wave 4 issues every direct global->LDS load (the k rows
+//              and the betas and decays of chunk e+2 in 3-slot rings, the v
+//              rows of chunk e+1 and the q rows of token chunk c+2 in 2-slot
+//              rings) and forms the masked betas, the decay cumsums, the
+//              q-row norms and the per-row token tables; waves 5-7 run the WY
+//              step of chunk e+1 (Gram matrix, k-row norms, A, T = (I + A)^-1)
+//              and the per-row coefficients the consumers use, and wave 7
+//              stores the staged outputs.
 // Two workgroup barriers per chunk separate the phases; between two barriers
 // each role only touches LDS slots no other role uses in that span.  Tiles of
 // 64 rows are stored unpadded with an XOR swizzle of their 16-byte segments;
@@ -1052,6 +1053,18 @@ __device__ __forceinline__ void scalar_load(float *dst, const float *src) {
                                    (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
 }
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations (the
+// most recently issued ones; loads complete in issue order) still in flight
+template <int N> __device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are complete
+// (lgkmcnt(0)) and no memory access moves across it, but outstanding global
+// loads and stores stay in flight (__syncthreads would wait for them, which
+// turns every prefetch and output store into a stall).  A wave whose
+// direct-to-LDS loads feed the next phase waits for them itself before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int K, int NB> struct FusedSmem {
   static constexpr int KW = 2 * K;        // bytes per k / q row
@@ -1070,7 +1083,7 @@ template <int K, int NB> struct FusedSmem {
   bf16 tdrow[4][256];       // diagonal blocks of T, row-major
   float rawb[2][CH], rawg[2][CH];          // raw betas / decays
   float beta[3][CH], gdp[3][CH];           // masked betas, base-2 decay cumsum
-  float rk[2][CH], c1[2][CH], wgt[2][CH];  // k-row rstd and the R / state-update weights
+  float rk[2][CH], c1[2][CH], wgt[2][CH];  // k-row rstd, 2^G rk (the X weights of R) and the state-update weights
   float rawt[2][CH], gtok[2][CH], rq[2][CH], qfac[2][CH];  // rq and qfac carry the output scale
   float gkr[2][CH], rkg[2][CH];  // rkg = rk 2^(-Gt_tok(r)) (used when qsafe)
   int tokr[2][CH];
@@ -1124,9 +1137,9 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     const int rl0 = 4 * lg + (lr >> 2);  // row of a transposing read inside its 16-row group
     const SwLane Lcont = sw_lane<KW>(lr, 16 * lg);         // k / q rows, reduction slots 8lg..
     const SwLane Lcolk = sw_lane<KW>(rl0, 16 * (lr & 3));  // k^T fragments (state-row order)
-    const SwLane Lcolv = sw_lane<VW>(rl0, 8 * (lr & 3));   // v columns
-    const uint32_t LT = (uint32_t)((rl0 * LDT + 4 * (lr & 3)) * 2);  // T^T columns
-    const uint32_t LP = (uint32_t)((lr * LDC + 4 * lg) * 2);         // P rows
+    // (the v-column, T^T-column and P-row parts are re-derived every chunk
+    // from the lane index, which keeps them out of the registers live across
+    // the chunk loop)
     // The state rows are kept in a permuted key order: accumulator row 4g + i of
     // tile at holds key kap(at, g, i) = 32 (at / 2) + 8 g + 4 (at % 2) + i, so that
     // the two tiles of one 32-deep reduction step form the B operand whose slots
@@ -1152,9 +1165,9 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     // use inside the loop would also wait, every chunk, for the output stores
     wait_vm();
     if (nexp > 0) {  // the helpers' prologue
-      __syncthreads();
-      __syncthreads();
-      __syncthreads();
+      lds_barrier();
+      lds_barrier();
+      lds_barrier();
     }
     for (int e = 0; e < nexp; ++e) {
       const int ks = e % 3, ts = e & 1;
@@ -1163,12 +1176,14 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       const int qs = c & 1;
       // the lane constants are made opaque every chunk so that the compiler forms
       // each address where it is used instead of hoisting dozens of them
-      SwLane lcont = Lcont, lcolk = Lcolk, lcolv = Lcolv;
-      uint32_t lt = LT, lp = LP;
+      SwLane lcont = Lcont, lcolk = Lcolk;
       int ln = lane;
-      asm volatile("" : "+v"(lcont.l), "+v"(lcont.x), "+v"(lcolk.l), "+v"(lcolk.x), "+v"(lcolv.l), "+v"(lcolv.x),
-                   "+v"(lt), "+v"(lp), "+v"(ln));
+      asm volatile("" : "+v"(lcont.l), "+v"(lcont.x), "+v"(lcolk.l), "+v"(lcolk.x), "+v"(ln));
       const int lr = ln & 15, lg = ln >> 4;
+      const int rt = 4 * lg + (lr >> 2);  // row of a transposing read inside its 16-row group
+      const SwLane lcolv = sw_lane<VW>(rt, 8 * (lr & 3));                // v columns
+      const uint32_t lt = (uint32_t)((rt * LDT + 4 * (lr & 3)) * 2);  // T^T columns
+      const uint32_t lp = (uint32_t)((lr * LDC + 4 * lg) * 2);        // P rows
       const uint32_t kt = off_of(sm.k[ks]), qt = off_of(sm.q[qs]);
       const float *gtok = sm.gtok[qs], *qfac = sm.qfac[qs], *rqv = sm.rq[qs];
       const float *rk = sm.rk[ts], *gkr = sm.gkr[ts];
@@ -1284,29 +1299,28 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           }
         }
       }
-      // R = diag(beta) V - lam diag(beta 2^G rk) X, kept in X
+      // R = diag(beta) (V + Y) with Y = -lam diag(2^G rk) X; the beta sits in the
+      // WY matrix (T diag(beta)) and V enters the E product as it is, so only Y
+      // is formed here, in bf16
+      Frag<bf16> Yb[2][NB];
       {
-        const float *bt = sm.beta[ks], *cf = sm.c1[ts];
-        const uint32_t vb = off_of(sm.v[ts]) + lcolv.l;
-        uint32_t va[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) va[b] = (lcolv.x ^ (uint32_t)(2 * wcol + 32 * b)) + vb;
+        const float *cf = sm.c1[ts];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int r0 = 16 * a4 + 4 * lg;
-          const f32x4 btv = ld4(bt + r0), coef = ld4(cf + r0) * lam;
+          const f32x4 coef = ld4(cf + 16 * a4 + 4 * lg) * (-lam);
 #pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const bf16x4 vv = tr8(va[b] + 16 * a4 * VW);
-            const f32x4 vf = f32x4{(float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]};
-            X[a4][b] = btv * vf - coef * X[a4][b];
-          }
+          for (int b = 0; b < NB; ++b) X[a4][b] *= coef;
         }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Yb[s][b], X[2 * s][b], X[2 * s + 1][b]);
       }
-      __syncthreads();  // P complete
+      lds_barrier();  // P complete
       // ---- phase B: E = T R, O^T += E^T P^T, state update, outputs
-      // T fragments (A operand, from T^T through the transposing read)
-      Frag<bf16> tfr[6];
+      // fragments of T diag(beta) (A operand, from its transpose through the
+      // transposing read) and of V (B operand, rows in the order of Y's slots)
+      Frag<bf16> tfr[6], vfr[2][NB];
       {
         const uint32_t tb = off_of(sm.t) + lt;
 #pragma unroll
@@ -1315,20 +1329,28 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           tfr[fi].v = __builtin_shufflevector(tr8(tb + (32 * s * LDT + 16 * a4) * 2), tr8(tb + ((32 * s + 16) * LDT + 16 * a4) * 2),
                                               0, 1, 2, 3, 4, 5, 6, 7);
         }
+        const uint32_t vb = off_of(sm.v[ts]) + lcolv.l;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const uint32_t va = (lcolv.x ^ (uint32_t)(2 * wcol + 32 * b)) + vb;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            vfr[s][b].v = __builtin_shufflevector(tr8(va + 32 * s * VW), tr8(va + (32 * s + 16) * VW), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      Frag<bf16> Rb[2][NB];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Rb[s][b], X[2 * s][b], X[2 * s + 1][b]);
       f32x4 E[4][NB];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          f32x4 acc = mma(tfr[a4 < 2 ? a4 : 2 * a4 - 2], Rb[0][b], zero4());
-          if (a4 >= 2) acc = mma(tfr[2 * a4 - 1], Rb[1][b], acc);
+          const Frag<bf16> &t0f = tfr[a4 < 2 ? a4 : 2 * a4 - 2];
+          f32x4 acc = mma(t0f, vfr[0][b], zero4());
+          acc = mma(t0f, Yb[0][b], acc);
+          if (a4 >= 2) {
+            acc = mma(tfr[2 * a4 - 1], vfr[1][b], acc);
+            acc = mma(tfr[2 * a4 - 1], Yb[1][b], acc);
+          }
           E[a4][b] = acc;
         }
       // while E forms: the P fragments and the k^T fragments of the first state row block
@@ -1405,7 +1427,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       // outputs of token chunk c once its last expanded chunk is in: lane holds
       // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in rq).
       // They are staged in bf16 in this chunk's v tile (unused after the R step)
-      // and helper 2 stores whole rows from there at the start of the next chunk.
+      // and helper 3 stores whole rows from there in the next chunk.
       if (j == n - 1 || e == nexp - 1) {
         char *stg = sm.v[ts];
 #pragma unroll
@@ -1414,7 +1436,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           for (int b = 0; b < NB; ++b)
             *(bf16x4 *)(stg + sw_off<VW>(16 * a4 + lr, 2 * (wcol + 16 * b + 4 * lg))) = bf4(O[b][a4]);
       }
-      __syncthreads();
+      lds_barrier();
     }
     float *fdst = a.final_state ? a.final_state + state_off : nullptr;
     float *cdst = nullptr;
@@ -1484,6 +1506,14 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       else tile_load<KW>(sm.q[c & 1], g, qst, toks_of(c), lane);
       scalar_load(sm.rawt[c & 1], gg + (tokbase + min(lane, toks_of(c) - 1)) * a.g_st);
     };
+    auto tables = [&](int e) {  // token of each row of chunk e inside its token chunk, and its decay cumsum
+      const int c = e / n, j = e - c * n;
+      const int tk = (CH * j + lane) / n;
+      const float gk = sm.gtok[c & 1][tk];
+      sm.tokr[e & 1][lane] = tk;
+      sm.gkr[e & 1][lane] = gk;
+      sm.rkg[e & 1][lane] = sm.rk[e & 1][lane] * fexp2(-gk);  // overflow-free when qsafe
+    };
     auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
       const int sl = c & 1, ntok = toks_of(c);
       float ss = 0.f;
@@ -1499,14 +1529,6 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       // the cumsum is non-increasing, so its last valid entry is its minimum
       const float gmin = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gt), ntok - 1));
       if (lane == 0) sm.qsafe[sl] = gmin > -100.f;
-    };
-    auto tables = [&](int e) {  // token of each row of chunk e inside its token chunk, and its decay cumsum
-      const int c = e / n, j = e - c * n;
-      const int tk = (CH * j + lane) / n;
-      const float gk = sm.gtok[c & 1][tk];
-      sm.tokr[e & 1][lane] = tk;
-      sm.gkr[e & 1][lane] = gk;
-      sm.rkg[e & 1][lane] = sm.rk[e & 1][lane] * fexp2(-gk);  // overflow-free when qsafe
     };
     // Gram stage of chunk x: tiles [i0, i1) of the lower triangle, with the k rows
     // of the later block as the B operand so that lane (lg, lr) of tile (ra, rb)
@@ -1582,27 +1604,31 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       }
       if (lg == 0) {  // per-row weights of the consumers' R and state update
         const float glast = gd[CH - 1];
-        sm.c1[x & 1][r] = bt[r] * fexp2(gr) * rk[r];
+        sm.c1[x & 1][r] = fexp2(gr) * rk[r];
         sm.wgt[x & 1][r] = fexp2(glast - gr) * rk[r];
       }
     };
-    // merge stage: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb below the diagonal, and
-    // T^T into the consumers' buffer (entry (r, c) of T at [c * LDT + r])
-    auto merge = [&]() {
+    // merge stage of chunk x: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb below the
+    // diagonal, and (T diag(beta))^T into the consumers' buffer (entry (r, c) of
+    // T diag(beta) at [c * LDT + r])
+    auto merge = [&](int x) {
       bf16 *tt = sm.t;
       bf16x4 tc[4], tn[4], al[6];
+      float bcol[4];  // beta of the column this lane writes in each column block
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bcol[b] = sm.beta[x % 3][16 * b + lr];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         tc[b] = tr_col4(sm.tdrow[b], 16, 4 * lg, 0, lr);  // T_b[4lg + i][lr]
         tn[b] = -*(const bf16x4 *)(sm.tdiag[b] + 4 * lane);
-        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + 4 * lg) = tc[b];
+        const f32x4 d = f32x4{(float)tc[b][0], (float)tc[b][1], (float)tc[b][2], (float)tc[b][3]} * bcol[b];
+        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + 4 * lg) = bf4(d);
       }
 #pragma unroll
       for (int i = 0; i < 6; ++i) al[i] = *(const bf16x4 *)(sm.alow[i] + 4 * lane);
-      auto put = [&](int ra, int rb, f32x4 v) {  // v: T[16 ra + 4 lg + i][16 rb + lr]
-        const bf16x4 x4 = bf4(v);
-        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + 4 * lg) = x4;
-        return x4;
+      auto put = [&](int ra, int rb, f32x4 v) {  // v: T[16 ra + 4 lg + i][16 rb + lr]; writes it times beta
+        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + 4 * lg) = bf4(v * bcol[rb]);
+        return bf4(v);
       };
       // distance 1
       const bf16x4 t10 = put(1, 0, mma16(tn[1], bf4(mma16(al[0], tc[0], zero4())), zero4()));
@@ -1654,9 +1680,10 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     };
     // Work per helper and chunk e (WY stages for chunk e+1), before || after the
     // mid-chunk barrier:
-    //   helper 0: k rows and betas/decays of chunk e+2,  || v rows of chunk e+1,
-    //             q rows of token chunk c+1                 masked betas and decay
-    //                                                       cumsum, q norms, row tables
+    //   helper 0: masked betas and decay cumsum of chunk || row tables of chunk e+1;
+    //             e+1, q norms and token decay cumsum       then v rows of chunk e+1,
+    //             of token chunk c+1; then k rows and       q rows of token chunk c+2
+    //             betas/decays of chunk e+2
     //   helper 1: merge stage                               || row block 3
     //   helper 2: Gram tiles 0-4                            || row blocks 0, 1
     //   helper 3: outputs of chunk e-1, Gram tiles 5-9      || row block 2
@@ -1667,6 +1694,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     // Each helper runs its own loop (the same barrier sequence as the consumers:
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
+      constexpr int NLQ = KW / 16 + 1;  // loads per q tile and its token decays
       const TileOffs<KW> koffs = tile_offs<KW>(kst, lane), qoffs = tile_offs<KW>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
       if (nexp > 0) {
@@ -1676,76 +1704,91 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
         load_scalars(0);
         if (nexp > 1) load_scalars(1);
         load_q(0, qoffs);
+        if (ntc > 1) load_q(1, qoffs);
         wait_vm();
         prep_scalars(0);
-        if (nexp > 1) prep_scalars(1);
         finish_q(0);
-        __syncthreads();
-        __syncthreads();
+        lds_barrier();
+        lds_barrier();
         tables(0);
-        __syncthreads();
+        lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
         const int c = e / n;
         const int j = e - c * n;
+        // phase A.  All that can be in flight are the q rows of token chunk c+1,
+        // issued one phase ago.
+        wait_vm();
+        if (e + 1 < nexp) prep_scalars(e + 1);
+        if (j == 0 && c + 1 < ntc) finish_q(c + 1);
+        // this wave touches LDS no more until the next phase A: the loads below
+        // never hold up an LDS access of its own
         if (e + 2 < nexp) {
           load_k(e + 2, koffs);
           load_scalars(e + 2);
         }
-        if (j == 0 && c + 1 < ntc) load_q(c + 1, qoffs);
-        __syncthreads();
-        if (e + 1 < nexp) load_v(e + 1, voffs);  // its tile is free once the R step is done
-        wait_vm();
-        if (e + 2 < nexp) prep_scalars(e + 2);
-        if ((e + 1) % n == 0 && c + 1 < ntc) finish_q(c + 1);
-        if (e + 1 < nexp) tables(e + 1);
-        __syncthreads();
+        lds_barrier();
+        // phase B.  The v tile of chunk e-1 (its outputs are stored) and, after
+        // the last expanded chunk of token chunk c, its q tile are free: refill
+        // them with chunk e+1 and token chunk c+2, then wait for everything but
+        // the q rows: the consumers read the v rows after the next barrier and
+        // the Gram stage the k rows of chunk e+2.
+        const bool lq = j == n - 1 && c + 2 < ntc;
+        if (e + 1 < nexp) tables(e + 1);  // needs the k-row norms from the Gram stage
+        if (e + 1 < nexp) load_v(e + 1, voffs);
+        if (lq) {
+          load_q(c + 2, qoffs);
+          wait_vm_keep<NLQ>();
+        } else {
+          wait_vm();
+        }
+        lds_barrier();
       }
     } else if (hw == 1) {
       if (nexp > 0) {
-        __syncthreads();
-        __syncthreads();
+        lds_barrier();
+        lds_barrier();
         block(0, IC<3>{});
-        __syncthreads();
+        lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
-        merge();
-        __syncthreads();
+        merge(e);
+        lds_barrier();
         if (e + 1 < nexp) block(e + 1, IC<3>{});
-        __syncthreads();
+        lds_barrier();
       }
     } else if (hw == 2) {
       if (nexp > 0) {
-        __syncthreads();
+        lds_barrier();
         gram(0, 0, 5, 3);
-        __syncthreads();
+        lds_barrier();
         block(0, IC<0>{});
         block(0, IC<1>{});
-        __syncthreads();
+        lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
         if (e + 1 < nexp) gram(e + 1, 0, 5, 3);
-        __syncthreads();
+        lds_barrier();
         if (e + 1 < nexp) {
           block(e + 1, IC<0>{});
           block(e + 1, IC<1>{});
         }
-        __syncthreads();
+        lds_barrier();
       }
     } else {
       if (nexp > 0) {
-        __syncthreads();
+        lds_barrier();
         gram(0, 5, 10, 4);
-        __syncthreads();
+        lds_barrier();
         block(0, IC<2>{});
-        __syncthreads();
+        lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
         if (e >= 1 && e % n == 0) store_o(e - 1);
         if (e + 1 < nexp) gram(e + 1, 5, 10, 4);
-        __syncthreads();
+        lds_barrier();
         if (e + 1 < nexp) block(e + 1, IC<2>{});
-        __syncthreads();
+        lds_barrier();
       }
       if (nexp > 0) store_o(nexp - 1);
     }
