@@ -916,28 +916,32 @@ __device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
 }
 
 // Tiles of 64 rows of W bytes are stored with their 16-byte segments permuted
-// per row: segment g of row r sits at slot g ^ swz(r).  The LDS serves 8-byte
-// reads (plain and transposing) 32 lanes at a time over 64 four-byte banks, and
-// 16-byte reads 8 lanes at a time over 128 bytes.  For 256-byte rows swz maps
-// row r = 8m + t (t < 8) to 2t + (t / 4 xor m): it is a bijection on 16 rows;
-// for each m its 8 values differ in bits 1-3, so the 8 rows x 2 adjacent
-// segments of a 32-lane transposing read meet 16 distinct slots; and they
-// differ in bits 0-2, so 8 lanes reading one segment of 8 consecutive rows meet
-// 8 distinct slots modulo 128 bytes.  For 128-byte rows no row permutation does
-// both; those tiles keep the identity.
-template <int NS> __device__ __forceinline__ int swz(int r) {
+// per row: segment g of row r sits at slot g ^ swz(r).  The permutation depends
+// on how the tile is read (measured on gfx950, where 16-byte reads are served
+// 16 lanes at a time and 8-byte reads, plain or transposing, 32 at a time):
+//   TK = 1, k and q tiles (256-byte rows): swz(r) = 2 (r mod 8).  16 lanes
+//     reading one segment of 16 consecutive rows (the k/q fragments) meet two
+//     segments' worth of distinct slots; the transposing k^T reads (8 rows x 4
+//     segments per 32 lanes) are served at the same rate as with any other
+//     row permutation tried.
+//   TK = 0, v tiles (256-byte rows): r = 8m + t (t < 8) maps to 2t + (t / 4 xor m),
+//     a bijection on 16 rows, which keeps the 8-byte output staging writes and
+//     the transposing v reads at the conflict-free rate.
+// Tiles of 128-byte rows keep swz(r) = r mod 8.
+template <int NS, int TK = 0> __device__ __forceinline__ int swz(int r) {
   static_assert(NS == 16 || NS == 8, "rows of 128 or 256 bytes");
+  if constexpr (NS == 16 && TK == 1) return (r & 7) << 1;
   if constexpr (NS == 16) return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1);
   return r & 7;
 }
-template <int W> __device__ __forceinline__ int sw_off(int row, int byte) {
+template <int W, int TK = 0> __device__ __forceinline__ int sw_off(int row, int byte) {
   constexpr int NS = W / 16;
-  return row * W + ((((byte >> 4) ^ swz<NS>(row)) & (NS - 1)) << 4) + (byte & 15);
+  return row * W + ((((byte >> 4) ^ swz<NS, TK>(row)) & (NS - 1)) << 4) + (byte & 15);
 }
 // bf16 fragment from a swizzled tile: row `row`, reduction slots k0 + 8lg .. +7
-template <int W> __device__ __forceinline__ Frag<bf16> sw_contig(const char *t, int row, int k0, int lg) {
+template <int W, int TK = 0> __device__ __forceinline__ Frag<bf16> sw_contig(const char *t, int row, int k0, int lg) {
   Frag<bf16> f;
-  f.v = *(const bf16x8 *)(t + sw_off<W>(row, 2 * (k0 + 8 * lg)));
+  f.v = *(const bf16x8 *)(t + sw_off<W, TK>(row, 2 * (k0 + 8 * lg)));
   return f;
 }
 // the same from an unswizzled bf16 tile with a row stride of ld elements
@@ -961,9 +965,9 @@ struct SwLane {
 template <int N> struct IC {
   static constexpr int value = N;
 };
-template <int W> __device__ __forceinline__ SwLane sw_lane(int r, int b) {
+template <int W, int TK = 0> __device__ __forceinline__ SwLane sw_lane(int r, int b) {
   constexpr int NS = W / 16;
-  return SwLane{(uint32_t)(r * W + (b & 15)), (uint32_t)((((b >> 4) ^ swz<NS>(r)) & (NS - 1)) << 4)};
+  return SwLane{(uint32_t)(r * W + (b & 15)), (uint32_t)((((b >> 4) ^ swz<NS, TK>(r)) & (NS - 1)) << 4)};
 }
 
 // DPP move of x (row mask ROWS; lanes of disabled rows and lanes whose source
@@ -1005,13 +1009,13 @@ template <int M> __device__ __forceinline__ void subst(float (&t)[4], const floa
 // Direct global->LDS load of a 64-row tile (rows past nrows repeat the last
 // row; they are never used unmasked).  Each wave-wide load fills 1 KiB of LDS,
 // 16 bytes per lane in lane order, so the swizzle is applied to the source.
-template <int W>
+template <int W, int TK = 0>
 __device__ __forceinline__ void tile_load(char *tile, const char *g, uint32_t rstride, int nrows, int lane) {
   constexpr int NS = W / 16, RPI = 64 / NS;
 #pragma unroll
   for (int i = 0; i < 64 / RPI; ++i) {
     const int r = i * RPI + lane / NS, slot = lane % NS;
-    const char *src = g + (uint32_t)min(r, nrows - 1) * rstride + (uint32_t)((slot ^ swz<NS>(r)) << 4);
+    const char *src = g + (uint32_t)min(r, nrows - 1) * rstride + (uint32_t)((slot ^ swz<NS, TK>(r)) << 4);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                      (__attribute__((address_space(3))) void *)(tile + i * 1024), 16, 0, 0);
   }
@@ -1022,25 +1026,25 @@ __device__ __forceinline__ void tile_load(char *tile, const char *g, uint32_t rs
 // Lane offsets of a full 64-row tile load.  Row r = RPI i + lane / NS of load i
 // has the swizzle of r mod 16 (256-byte rows) or r mod 8 (128-byte rows), so
 // only PER distinct lane offsets exist; the row offset RPI i rs is uniform.
-template <int W> struct TileOffs {
+template <int W, int TK = 0> struct TileOffs {
   static constexpr int NS = W / 16, RPI = 64 / NS, PER = (NS == 16 ? 16 : 8) / RPI;
   uint32_t o[PER];
   uint32_t rs;  // row stride in bytes
 };
-template <int W> __device__ __forceinline__ TileOffs<W> tile_offs(uint32_t rstride, int lane) {
-  using TO = TileOffs<W>;
+template <int W, int TK = 0> __device__ __forceinline__ TileOffs<W, TK> tile_offs(uint32_t rstride, int lane) {
+  using TO = TileOffs<W, TK>;
   TO t;
   t.rs = rstride;
 #pragma unroll
   for (int p = 0; p < TO::PER; ++p) {
     const int r = p * TO::RPI + lane / TO::NS, slot = lane % TO::NS;
-    t.o[p] = (uint32_t)(lane / TO::NS) * rstride + (uint32_t)((slot ^ swz<TO::NS>(r)) << 4);
+    t.o[p] = (uint32_t)(lane / TO::NS) * rstride + (uint32_t)((slot ^ swz<TO::NS, TK>(r)) << 4);
   }
   return t;
 }
-template <int W>
-__device__ __forceinline__ void tile_load_full(char *tile, const char *g, const TileOffs<W> &t) {
-  using TO = TileOffs<W>;
+template <int W, int TK = 0>
+__device__ __forceinline__ void tile_load_full(char *tile, const char *g, const TileOffs<W, TK> &t) {
+  using TO = TileOffs<W, TK>;
 #pragma unroll
   for (int i = 0; i < 64 / TO::RPI; ++i) {
     const char *gr = g + (uint32_t)(i * TO::RPI) * t.rs;  // uniform
@@ -1066,9 +1070,9 @@ template <int N> __device__ __forceinline__ void wait_vm_keep() {
 // direct-to-LDS loads feed the next phase waits for them itself before it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int K, int NB> struct FusedSmem {
+template <int K, int V> struct FusedSmem {
   static constexpr int KW = 2 * K;        // bytes per k / q row
-  static constexpr int VW = 2 * 64 * NB;  // bytes per v row of the tile
+  static constexpr int VW = 2 * V;       // bytes per v row
   static constexpr int LDC = CH + 8;      // P rows (bf16, padded)
   static constexpr int LDT = CH + 16;     // rows of T^T (bf16, padded)
   char k[3][CH * KW];
@@ -1090,10 +1094,14 @@ template <int K, int NB> struct FusedSmem {
   int qsafe[2];                   // the token chunk's decay cumsum stays above -100 (base 2)
 };
 
-template <int K, int V, int NB>
-__global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
-  using S = FusedSmem<K, NB>;
-  constexpr int BV = 64 * NB, NVT = V / BV, KT16 = K / 16, KS = K / 32;
+template <int K, int V, int NCW>
+__global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArgs a) {
+  using S = FusedSmem<K, V>;
+  // NCW consumer waves of 16 NB state columns each cover all V columns; the
+  // 16 score tiles (4 token blocks x 4 row blocks) are shared out RBW per wave
+  constexpr int NB = V / (16 * NCW), BV = V, NVT = 1, KT16 = K / 16, KS = K / 32;
+  constexpr int RBW = 16 / NCW;
+  static_assert(NB >= 1 && 16 * NB * NCW == V && RBW * NCW == 16, "consumer waves must tile V and the scores");
   constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDT = S::LDT;
   __shared__ S sm;
 
@@ -1123,9 +1131,13 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
   auto rows_of = [&](int e) { return (int)((nsub - (int64_t)CH * e) < CH ? (nsub - (int64_t)CH * e) : CH); };
   auto toks_of = [&](int c) { return (int)((L - (int64_t)CH * c) < CH ? (L - (int64_t)CH * c) : CH); };
 
-  if (w < 4) {
+  // the consumer body, instantiated per half of the score row blocks so that
+  // every register array index is a compile-time constant
+  auto consumer = [&](auto halfc) {
+    constexpr int rb0 = decltype(halfc)::value * RBW;
     // ---------------------------------------------------------------- consumers
     const int wcol = w * 16 * NB;     // first column of this wave inside the tile
+    const int tb = w & 3;  // the wave's score tiles: token block tb, row blocks rb0 .. rb0 + RBW - 1
     const int gcol = vt * BV + wcol;  // ... and inside the head
     const char *smb = (const char *)&sm;
     auto off_of = [&](const void *p) { return (uint32_t)((const char *)p - smb); };
@@ -1135,8 +1147,8 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     // per-lane parts of the LDS addresses; each access below is one xor-add of a
     // compile-time segment offset plus an immediate row offset
     const int rl0 = 4 * lg + (lr >> 2);  // row of a transposing read inside its 16-row group
-    const SwLane Lcont = sw_lane<KW>(lr, 16 * lg);         // k / q rows, reduction slots 8lg..
-    const SwLane Lcolk = sw_lane<KW>(rl0, 16 * (lr & 3));  // k^T fragments (state-row order)
+    const SwLane Lcont = sw_lane<KW, 1>(lr, 16 * lg);         // k / q rows, reduction slots 8lg..
+    const SwLane Lcolk = sw_lane<KW, 1>(rl0, 16 * (lr & 3));  // k^T fragments (state-row order)
     // (the v-column, T^T-column and P-row parts are re-derived every chunk
     // from the lane index, which keeps them out of the registers live across
     // the chunk loop)
@@ -1204,33 +1216,41 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
         }
       }
       f32x4 X[4][NB];
-      // Scores, transposed, of the wave's token block w against all rows: lane
-      // (lg, lr) of tile a4 holds Sc[r = 16 a4 + 4 lg + i][t = 16 w + lr] = k_r.q_t.
-      // They reuse the k fragments of X = K Sst as the A operand.
-      f32x4 Pacc[4];
+      // Scores, transposed, of the wave's token block tb against its row blocks:
+      // lane (lg, lr) of tile pa holds Sc[r = 16 (rb0 + pa) + 4 lg + i][t = 16 tb + lr]
+      // = k_r.q_t.  They reuse the k fragments of X = K Sst as the A operand.
+      f32x4 Pacc[RBW];
       // k (and q) fragments of reduction step s+1 are read while step s multiplies
       {
-        Frag<bf16> kf[2][4], qw[2];
-        auto load_k = [&](int s, int buf) {  // reduction slots 32s + 8lg .. +7
+        // rolling single buffer: fragment a4 of step s+1 is read right after the
+        // last product of step s that uses it
+        Frag<bf16> kf[4], qw[2];
+        auto load_kf = [&](int s, int a4) {  // reduction slots 32s + 8lg .. +7 of row block a4
           const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) kf[buf][a4].v = rd16(xs + (kt + lcont.l) + 16 * a4 * KW);
-          qw[buf].v = rd16(xs + (qt + lcont.l) + 16 * w * KW);
+          kf[a4].v = rd16(xs + (kt + lcont.l) + 16 * a4 * KW);
         };
-        load_k(0, 0);
+        auto load_qw = [&](int s, int buf) {
+          const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
+          qw[buf].v = rd16(xs + (qt + lcont.l) + 16 * tb * KW);
+        };
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) load_kf(0, a4);
+        load_qw(0, 0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          if (s + 1 < KS) load_k(s + 1, (s + 1) & 1);
+          if (s + 1 < KS) load_qw(s + 1, (s + 1) & 1);
           __builtin_amdgcn_sched_barrier(0);
           Frag<bf16> Sb[NB];
 #pragma unroll
           for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
+          for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[s & 1][a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) Pacc[a4] = mma(kf[s & 1][a4], qw[s & 1], s == 0 ? zero4() : Pacc[a4]);
+            for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
+            if (a4 >= rb0 && a4 < rb0 + RBW)
+              Pacc[a4 - rb0] = mma(kf[a4], qw[s & 1], s == 0 ? zero4() : Pacc[a4 - rb0]);
+            if (s + 1 < KS) load_kf(s + 1, a4);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1270,31 +1290,31 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       // the product qfac_t rkg_r of per-token and per-row factors (both finite and
       // normal); otherwise it is formed per entry.
       {
-        const int t = 16 * w + lr;
+        const int t = 16 * tb + lr;
         const int rlim = n * (t + 1) - CH * j;
         const bool fact = sm.qsafe[qs] != 0;
-        const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * w * LDC);
+        const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * tb * LDC);
         if (fact) {
           const float qv = qfac[t];
           const float *rkg = sm.rkg[ts];
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int r0 = 16 * a4 + 4 * lg;
+          for (int pa = 0; pa < RBW; ++pa) {
+            const int a4 = rb0 + pa, r0 = 16 * a4 + 4 * lg;
             const f32x4 f4 = ld4(rkg + r0) * qv;
             f32x4 val;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? f4[i] * Pacc[a4][i] : 0.f;
+            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? f4[i] * Pacc[pa][i] : 0.f;
             *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
           }
         } else {
           const float gt = gtok[t], rq = rqv[t];
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int r0 = 16 * a4 + 4 * lg;
+          for (int pa = 0; pa < RBW; ++pa) {
+            const int a4 = rb0 + pa, r0 = 16 * a4 + 4 * lg;
             const f32x4 rk4 = ld4(rk + r0), gk4 = ld4(gkr + r0);
             f32x4 val;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? rq * rk4[i] * fexp2(gt - gk4[i]) * Pacc[a4][i] : 0.f;
+            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? rq * rk4[i] * fexp2(gt - gk4[i]) * Pacc[pa][i] : 0.f;
             *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
           }
         }
@@ -1353,20 +1373,20 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           }
           E[a4][b] = acc;
         }
-      // while E forms: the P fragments and the k^T fragments of the first state row block
+      // while E forms: the P fragments of the first token block and the k^T
+      // fragments of the first state row block
       const int tokb0 = tokr[0], tokb1 = tokr[32];
-      Frag<bf16> pf[4][2];
-      {
-        const uint32_t pr = off_of(sm.p) + lp;
+      Frag<bf16> pf[2][2];
+      const uint32_t pr = off_of(sm.p) + lp;
+      auto load_pf = [&](int a4, int buf) {  // P rows of token block a4
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            pf[a4][s].v = __builtin_shufflevector(rd8(pr + (16 * a4 * LDC + 32 * s) * 2), rd8(pr + (16 * a4 * LDC + 32 * s + 16) * 2),
-                                                  0, 1, 2, 3, 4, 5, 6, 7);
-      }
+        for (int s = 0; s < 2; ++s)
+          pf[buf][s].v = __builtin_shufflevector(rd8(pr + (16 * a4 * LDC + 32 * s) * 2), rd8(pr + (16 * a4 * LDC + 32 * s + 16) * 2),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      load_pf(0, 0);
       const uint32_t kcb = kt + lcolk.l;
-      Frag<bf16> kc[3][2];
+      Frag<bf16> kc[2][2];
       auto load_kc = [&](int at, int buf) {  // lane lr of tile at: key kap(at, lr / 4, lr % 4)
         const uint32_t x = (lcolk.x ^ (uint32_t)(64 * (at >> 1))) + kcb + 8 * (at & 1);
 #pragma unroll
@@ -1374,7 +1394,6 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           kc[buf][h2].v = __builtin_shufflevector(tr8(x + 32 * h2 * KW), tr8(x + (32 * h2 + 16) * KW), 0, 1, 2, 3, 4, 5, 6, 7);
       };
       load_kc(0, 0);
-      load_kc(1, 1);
       __builtin_amdgcn_sched_barrier(0);
       Frag<bf16> Eb[2][NB];
 #pragma unroll
@@ -1382,13 +1401,17 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
+      for (int a4 = 0; a4 < 4; ++a4) {
+        if (a4 + 1 < 4) load_pf(a4 + 1, (a4 + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           if ((s ? tokb1 : tokb0) > 16 * a4 + 15) continue;  // P block entirely masked
 #pragma unroll
-          for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pf[a4][s], O[b][a4]);
+          for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pf[a4 & 1][s], O[b][a4]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // Sst += K^T diag(2^(G_last - G) rk / (lam 2^G_last)) E and lam *= 2^G_last, unless
       // lam would fall below LAM_MIN (then Sst is rescaled to lam = 1)
       const float glast = sm.gdp[ks][CH - 1];
@@ -1413,13 +1436,13 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int at = 0; at < KT16; ++at) {  // k^T fragments two steps ahead
-        if (at + 2 < KT16) load_kc(at + 2, (at + 2) % 3);
+      for (int at = 0; at < KT16; ++at) {  // k^T fragments one step ahead
+        if (at + 1 < KT16) load_kc(at + 1, (at + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          Sacc[at][b] = mma(kc[at % 3][0], Eb[0][b], Sacc[at][b]);
-          Sacc[at][b] = mma(kc[at % 3][1], Eb[1][b], Sacc[at][b]);
+          Sacc[at][b] = mma(kc[at & 1][0], Eb[0][b], Sacc[at][b]);
+          Sacc[at][b] = mma(kc[at & 1][1], Eb[1][b], Sacc[at][b]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1455,6 +1478,10 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
           if (fdst) fdst[off] = x;
           if (cdst) cdst[off] = x;
         }
+  };
+  if (w < NCW) {
+    if (NCW > 4 && w >= 4) consumer(IC<1>{});
+    else consumer(IC<0>{});
   } else {
     // ---------------------------------------------------------------- helpers
     // Four helper waves share the loads and the WY step.  For chunk x the WY
@@ -1468,67 +1495,72 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     //                the blocks of T below the diagonal and writes T^T, which the
     //                consumers read after that barrier.
     // The loads are spread over the four helpers as well.
-    const int hw = w - 4;
+    const int hw = w - NCW;
     const bf16 *qg = (const bf16 *)a.q + hq * a.q_sh;
     const bf16 *kg = (const bf16 *)a.k + hq * a.k_sh;
     const bf16 *vg = (const bf16 *)a.v + h * a.v_sh + vt * BV;
     const float *gg = a.g + h * a.g_sh;
     const float *bg = a.beta + h * a.b_sh;
     const uint32_t kst = (uint32_t)a.k_st * 2u, vst = (uint32_t)a.v_st * 2u, qst = (uint32_t)a.q_st * 2u;
-    auto load_k = [&](int e, const TileOffs<KW> &offs) {
+    // lane index of the loader's address and table arithmetic; the loader loop
+    // makes it opaque every chunk so that nothing derived from it is hoisted
+    // out of the loop and held in registers (a spilled value reloaded between
+    // direct-to-LDS loads would wait for them)
+    int hl = lane;
+    auto load_k = [&](int e, const TileOffs<KW, 1> &offs) {
       const char *g = (const char *)(kg + (t0 * n + (int64_t)CH * e) * a.k_st);
-      if (rows_of(e) == CH) tile_load_full<KW>(sm.k[e % 3], g, offs);
-      else tile_load<KW>(sm.k[e % 3], g, kst, rows_of(e), lane);
+      if (rows_of(e) == CH) tile_load_full<KW, 1>(sm.k[e % 3], g, offs);
+      else tile_load<KW, 1>(sm.k[e % 3], g, kst, rows_of(e), hl);
     };
     auto load_v = [&](int e, const TileOffs<VW> &offs) {
       const char *g = (const char *)(vg + (t0 * n + (int64_t)CH * e) * a.v_st);
       if (rows_of(e) == CH) tile_load_full<VW>(sm.v[e & 1], g, offs);
-      else tile_load<VW>(sm.v[e & 1], g, vst, rows_of(e), lane);
+      else tile_load<VW>(sm.v[e & 1], g, vst, rows_of(e), hl);
     };
     auto load_scalars = [&](int e) {  // raw beta and decay of each sub-row of chunk e
       const int64_t s0 = (int64_t)CH * e;
-      const int r = min(lane, rows_of(e) - 1);
+      const int r = min(hl, rows_of(e) - 1);
       const int64_t tok = (s0 + r) / n;
       scalar_load(sm.rawb[e & 1], bg + (t0 * n + s0 + r) * a.b_st);
       scalar_load(sm.rawg[e & 1], gg + (t0 + tok) * a.g_st);
     };
     auto prep_scalars = [&](int e) {  // masked betas and the base-2 decay cumsum of chunk e
-      const bool valid = lane < rows_of(e);
+      const bool valid = hl < rows_of(e);
       const int rem = (int)(((int64_t)CH * e) % n);
-      const bool first = valid && (rem + lane) % n == 0;  // the decay sits on a token's first sub-row
-      sm.gdp[e % 3][lane] = wave_scan(first ? sm.rawg[e & 1][lane] * LOG2E : 0.f);
-      sm.beta[e % 3][lane] = valid ? sm.rawb[e & 1][lane] : 0.f;
+      const bool first = valid && (rem + hl) % n == 0;  // the decay sits on a token's first sub-row
+      sm.gdp[e % 3][hl] = wave_scan(first ? sm.rawg[e & 1][hl] * LOG2E : 0.f);
+      sm.beta[e % 3][hl] = valid ? sm.rawb[e & 1][hl] : 0.f;
     };
-    auto load_q = [&](int c, const TileOffs<KW> &offs) {  // q rows and token decays of token chunk c
+    auto load_q = [&](int c, const TileOffs<KW, 1> &offs) {  // q rows and token decays of token chunk c
       const int64_t tokbase = t0 + (int64_t)CH * c;
       const char *g = (const char *)(qg + tokbase * a.q_st);
-      if (toks_of(c) == CH) tile_load_full<KW>(sm.q[c & 1], g, offs);
-      else tile_load<KW>(sm.q[c & 1], g, qst, toks_of(c), lane);
-      scalar_load(sm.rawt[c & 1], gg + (tokbase + min(lane, toks_of(c) - 1)) * a.g_st);
+      if (toks_of(c) == CH) tile_load_full<KW, 1>(sm.q[c & 1], g, offs);
+      else tile_load<KW, 1>(sm.q[c & 1], g, qst, toks_of(c), hl);
+      scalar_load(sm.rawt[c & 1], gg + (tokbase + min(hl, toks_of(c) - 1)) * a.g_st);
     };
     auto tables = [&](int e) {  // token of each row of chunk e inside its token chunk, and its decay cumsum
       const int c = e / n, j = e - c * n;
-      const int tk = (CH * j + lane) / n;
+      const int tk = (CH * j + hl) / n;
       const float gk = sm.gtok[c & 1][tk];
-      sm.tokr[e & 1][lane] = tk;
-      sm.gkr[e & 1][lane] = gk;
-      sm.rkg[e & 1][lane] = sm.rk[e & 1][lane] * fexp2(-gk);  // overflow-free when qsafe
+      sm.tokr[e & 1][hl] = tk;
+      sm.gkr[e & 1][hl] = gk;
+      sm.rkg[e & 1][hl] = sm.rk[e & 1][hl] * fexp2(-gk);  // overflow-free when qsafe
     };
     auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
       const int sl = c & 1, ntok = toks_of(c);
       float ss = 0.f;
       if (a.l2norm) {
 #pragma unroll
-        for (int sg = 0; sg < KW / 16; ++sg) ss += seg_sumsq<bf16>(*(const uint4 *)(sm.q[sl] + sw_off<KW>(lane, 16 * sg)));
+        for (int sg = 0; sg < KW / 16; ++sg) ss += seg_sumsq<bf16>(*(const uint4 *)(sm.q[sl] + sw_off<KW, 1>(hl, 16 * sg)));
       }
       const float rq = a.scale * (a.l2norm ? frsq(ss + 1e-6f) : 1.f);
-      const float gt = wave_scan(lane < ntok ? sm.rawt[sl][lane] * LOG2E : 0.f);
-      sm.rq[sl][lane] = rq;
-      sm.gtok[sl][lane] = gt;
-      sm.qfac[sl][lane] = rq * fexp2(gt);
+      const float gt = wave_scan(hl < ntok ? sm.rawt[sl][hl] * LOG2E : 0.f);
+      sm.rq[sl][hl] = rq;
+      sm.gtok[sl][hl] = gt;
+      sm.qfac[sl][hl] = rq * fexp2(gt);
       // the cumsum is non-increasing, so its last valid entry is its minimum
       const float gmin = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gt), ntok - 1));
-      if (lane == 0) sm.qsafe[sl] = gmin > -100.f;
+      if (hl == 0) sm.qsafe[sl] = gmin > -100.f;
     };
     // Gram stage of chunk x: tiles [i0, i1) of the lower triangle, with the k rows
     // of the later block as the B operand so that lane (lg, lr) of tile (ra, rb)
@@ -1542,7 +1574,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       for (int rt = 0; rt < 4; ++rt)
         if (rt < nblk) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) kf[rt][s] = sw_contig<KW>(k, 16 * rt + lr, 32 * s, lg);
+          for (int s = 0; s < KS; ++s) kf[rt][s] = sw_contig<KW, 1>(k, 16 * rt + lr, 32 * s, lg);
         }
 #pragma unroll
       for (int idx = 0; idx < 10; ++idx) {
@@ -1695,7 +1727,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
       constexpr int NLQ = KW / 16 + 1;  // loads per q tile and its token decays
-      const TileOffs<KW> koffs = tile_offs<KW>(kst, lane), qoffs = tile_offs<KW>(qst, lane);
+      const TileOffs<KW, 1> koffs = tile_offs<KW, 1>(kst, lane), qoffs = tile_offs<KW, 1>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
       if (nexp > 0) {
         load_k(0, koffs);
@@ -1716,6 +1748,7 @@ __global__ void __launch_bounds__(2 * NTHR, 1) gdp_fused_kernel(PrefillArgs a) {
       for (int e = 0; e < nexp; ++e) {
         const int c = e / n;
         const int j = e - c * n;
+        asm volatile("" : "+v"(hl));
         // phase A.  All that can be in flight are the q rows of token chunk c+1,
         // issued one phase ago.
         wait_vm();
@@ -1910,9 +1943,13 @@ hipError_t launch_split(const PrefillArgs &a, hipStream_t stream) {
 
 template <int K, int V>
 hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
+  // 4 consumer waves of V/4 state columns and 4 helper waves.  8 consumer waves
+  // of 16 columns (the kernel supports it) hide more latency but read every k,
+  // k^T, T and P fragment twice as often, which costs more LDS time than it hides.
+  constexpr int NCW = 4;
   const int64_t blocks = (int64_t)a.N * a.Hv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdp_fused_kernel<K, V, V / 64>), dim3((unsigned)blocks), dim3(2 * NTHR), 0, stream, a);
+  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
   return hipGetLastError();
 }
 
