@@ -6,7 +6,9 @@ package, and this package imports nothing from the library.
 
 The arithmetic lives in ``gdp_oracle.c`` (a plain token-by-token recurrence,
 FlashInfer docs "flashinfer.gdp_prefill.chunk_gated_delta_product", the
-recurrence display); this module only marshals numpy arrays into it.
+recurrence display); this module only marshals numpy arrays into it.  The
+single-token decode step is that same recurrence on one-token sequences whose
+states come from, and go back to, the state cache.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 brute-force Householder products, closed forms and invariants.
@@ -154,3 +156,43 @@ def prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None,
     if vn is not None:
         out["vnew"] = vn
     return out
+
+
+def decode(q, k, v, g_log, beta, num_householder, state_cache, state_indices, scale=None,
+           use_qk_l2norm=False, threads=None, lib=None):
+    """One recurrent step per sequence on the state cache, in place.
+
+    The recurrent decode step of the blog page's GDN section (Sbar = lambda S,
+    vhat = Sbar^T k, e = beta (v - vhat), S = Sbar + k e^T, r = q^T S), with the
+    n Householder rows of the FlashInfer recurrence display, reading the state
+    of sequence i from state_cache[state_indices[i]] and writing it back there
+    (Megatron Core page, state / state_indices).  It is the prefill token loop
+    run on one-token sequences whose initial states are the cache rows.
+    A negative index marks a padding entry: its output row is zero and the
+    cache is not touched.  Two entries may not name the same slot.
+
+    Shapes: q [N, Hqk, K], k [N*n, Hqk, K], v [N*n, Hv, V], g_log [N, Hv],
+    beta [N*n, Hv], state_cache [S, Hv, K, V], state_indices [N].
+    Returns {"o": [N, Hv, V], "state_cache": the updated copy}.
+    """
+    n = int(num_householder)
+    q = _f64(q); k = _f64(k); v = _f64(v); g = _f64(g_log); b = _f64(beta)
+    cache = _f64(state_cache).copy()
+    slots = np.asarray(state_indices, dtype=np.int64)
+    N, Hqk, K = q.shape
+    Hv, V = v.shape[1], v.shape[2]
+    if k.shape != (N * n, Hqk, K) or v.shape != (N * n, Hv, V) or g.shape != (N, Hv) or b.shape != (N * n, Hv):
+        raise ValueError("decode: shapes do not match q and num_householder")
+    if slots.shape != (N,) or cache.shape[1:] != (Hv, K, V):
+        raise ValueError("decode: state_indices / state_cache shapes")
+    sel = np.nonzero((slots >= 0) & (slots < cache.shape[0]))[0]
+    if len(set(slots[sel].tolist())) != len(sel):
+        raise ValueError("decode: two entries name the same cache slot")
+    o = np.zeros((N, Hv, V), np.float64)
+    if sel.size:
+        rows = (sel[:, None] * n + np.arange(n)[None, :]).reshape(-1)
+        res = prefill(q[sel], k[rows], v[rows], g[sel], b[rows], n, np.arange(sel.size + 1), scale=scale,
+                      initial_state=cache[slots[sel]], use_qk_l2norm=use_qk_l2norm, threads=threads, lib=lib)
+        o[sel] = res["o"]
+        cache[slots[sel]] = res["final_state"]
+    return {"o": o, "state_cache": cache}

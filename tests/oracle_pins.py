@@ -20,7 +20,9 @@ oracle disagrees with what the pages and the mathematics fix:
     the run cut after 64*c tokens (Megatron Core page, return_chunk_states);
     cache slots receive final states and -1 writes nothing (Megatron Core
     page, state / state_indices); the in-kernel L2 norm is invariant to
-    positive row scaling; scale None/0 means K^-1/2 (FlashInfer page, scale).
+    positive row scaling; scale None/0 means K^-1/2 (FlashInfer page, scale);
+  * the single-token decode step on the state cache: brute force per entry
+    (padding entries untouched), and T decode steps equal a T-token prefill.
 """
 import numpy as np
 
@@ -376,3 +378,59 @@ ALL_PINS = [
     pin_gqa_repeat_interleave, pin_linearity, pin_default_scale, pin_chunk_states,
     pin_state_cache, pin_l2norm_scale_invariance, pin_decay_before_update,
 ]
+
+
+def _decode_problem(rng, N, n, Hqk, Hv, K, V, S):
+    q = _unit_rows(rng.standard_normal((N, Hqk, K)))
+    k = _unit_rows(rng.standard_normal((N * n, Hqk, K)))
+    v = rng.standard_normal((N * n, Hv, V))
+    g = -np.log1p(np.exp(rng.standard_normal((N, Hv))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((N * n, Hv))))
+    cache = 0.3 * rng.standard_normal((S, Hv, K, V))
+    return q, k, v, g, beta, cache
+
+
+def pin_decode_brute_force(lib):
+    """Each entry's step is the explicit Householder product applied to its cache row;
+    padding entries (-1) leave o zero and the cache untouched."""
+    rng = np.random.default_rng(RNG_SEED + 40)
+    N, n, Hqk, Hv, K, V, S = 5, 3, 1, 2, 4, 3, 7
+    q, k, v, g, beta, cache = _decode_problem(rng, N, n, Hqk, Hv, K, V, S)
+    slots = np.array([4, -1, 0, 6, -1])
+    res = oracle.decode(q, k, v, g, beta, n, cache, slots, lib=lib)
+    want_cache = cache.copy()
+    for i in range(N):
+        if slots[i] < 0:
+            _close(res["o"][i], np.zeros((Hv, V)), what="padding output")
+            continue
+        rows = np.arange(i * n, (i + 1) * n)
+        bo, bfin = brute_force(q[i:i + 1], k[rows], v[rows], g[i:i + 1], beta[rows], n, np.array([0, 1]),
+                               initial_state=cache[slots[i]][None])
+        _close(res["o"][i], bo[0], what=f"decode o[{i}]")
+        want_cache[slots[i]] = bfin[0]
+    _close(res["state_cache"], want_cache, what="decode cache")
+
+
+def pin_decode_steps_equal_prefill(lib):
+    """T decode steps of N sequences, each on its own slot, equal the prefill of the
+    T-token sequences started from those slots."""
+    rng = np.random.default_rng(RNG_SEED + 41)
+    N, T, n, Hqk, Hv, K, V, S = 3, 5, 2, 1, 2, 4, 3, 4
+    prob = make_problem(rng, [T] * N, n, Hqk, Hv, K, V, init=False)
+    cache = 0.3 * rng.standard_normal((S, Hv, K, V))
+    slots = np.array([2, 0, 3])
+    ref = oracle.prefill(prob["q"], prob["k"], prob["v"], prob["g_log"], prob["beta"], n, prob["cu_seqlens"],
+                         initial_state=cache[slots], lib=lib)
+    cur = cache.copy()
+    for t in range(T):
+        tok = np.arange(N) * T + t  # token t of every sequence
+        rows = (tok[:, None] * n + np.arange(n)[None, :]).reshape(-1)
+        step = oracle.decode(prob["q"][tok], prob["k"][rows], prob["v"][rows], prob["g_log"][tok],
+                             prob["beta"][rows], n, cur, slots, lib=lib)
+        _close(step["o"], ref["o"][tok], what=f"decode step {t}")
+        cur = step["state_cache"]
+    _close(cur[slots], ref["final_state"], what="decode final states")
+    untouched = [s for s in range(S) if s not in slots]
+    _close(cur[untouched], cache[untouched], what="untouched slots")
+
+ALL_PINS += [pin_decode_brute_force, pin_decode_steps_equal_prefill]
