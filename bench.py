@@ -100,6 +100,50 @@ def cpu_baseline(inp, w, tokens_per_seq, threads):
     return rec, ref, it
 
 
+def bench_decode(args, gdp, workloads):
+    """One decode step per timed step on the serving batch; HBM-bound (each live
+    entry reads and writes its Hv K x V fp32 states once)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N, n, Hqk, Hv, K, V, S, pad = 256, 2, 16, 32, 128, 128, 1024, 8
+    inp = workloads.decode_batch(N, n, Hqk, Hv, K, V, S, pad=pad, dtype=torch.bfloat16, l2norm_in_kernel=True,
+                                 g_shift=3.0, seed=2024, device="cuda")
+    o = torch.empty((N, Hv, V), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdp.gdp_recurrent_decode(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, 0.0, True,
+                                 inp["state_cache"], inp["state_indices"], o, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    live = N - pad
+    alg = live * Hv * (2 * K * V * 4 + 4 + 4 * n) + live * (2 * K * Hqk * (1 + n)) + live * Hv * 2 * V * (n + 1)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    line = {"metric": "decode entries/s, single-token GDP decode step on the state cache (bf16, d=128) + % of HBM roofline",
+            "value": live / (wall / args.steps), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "serving decode step: 256 entries (8 padding), n=2, Hqk=16 / Hv=32, K=V=128, "
+                                   "bf16, in-kernel L2 norm, 1024 cache slots", "entries": N, "padding": pad},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gdp_decode_kernel",
+                         "kernel_ms": kern_ms, "algorithmic_bytes_per_launch": alg},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +152,10 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 = long-context prefill)")
     ap.add_argument("--cpu-tokens", type=int, default=65536, help="oracle sample: tokens per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure the single-token decode step on the state cache instead of the prefill "
+                         "(serving batch: 256 entries with 8 padding, n=2, Hqk=16 / Hv=32, K=V=128, bf16, "
+                         "1024 cache slots)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (three times); used to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -131,6 +179,10 @@ def main():
 
     from gated_deltaproduct_recurrence_amd import binding as gdp
     from gated_deltaproduct_recurrence_amd import workloads
+
+    if args.decode:
+        bench_decode(args, gdp, workloads)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

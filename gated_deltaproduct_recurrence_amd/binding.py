@@ -18,7 +18,7 @@ STATUS_NAMES = {GDP_EINVAL: "GDP_EINVAL", GDP_EUNSUPPORTED: "GDP_EUNSUPPORTED", 
                 GDP_EWORKSPACE: "GDP_EWORKSPACE", GDP_EHIP: "GDP_EHIP"}
 
 EXPORTED = ("gdp_descriptor_capacity", "gdp_build_descriptors", "gdp_workspace_bytes",
-            "gdp_chunk_prefill", "gdp_last_error", "gdp_version")
+            "gdp_chunk_prefill", "gdp_recurrent_decode", "gdp_last_error", "gdp_version")
 
 
 class gdp_tensor(ctypes.Structure):
@@ -57,6 +57,9 @@ def _load(path=LIB_PATH):
     lib.gdp_chunk_prefill.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
                                       ctypes.c_int32, T, T, ctypes.c_int32, T, T, T, D, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]
+    lib.gdp_recurrent_decode.restype = ctypes.c_int
+    lib.gdp_recurrent_decode.argtypes = [T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, T, T, T,
+                                         ctypes.c_void_p]
     lib.gdp_last_error.restype = ctypes.c_char_p
     lib.gdp_last_error.argtypes = []
     lib.gdp_version.restype = ctypes.c_char_p
@@ -179,6 +182,17 @@ def gdp_chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=0
     _check(rc)
 
 
+def gdp_recurrent_decode(q, k, v, g_log, beta, num_householder, scale, use_qk_l2norm, state_cache,
+                         state_indices, o, stream=None):
+    """Direct call of the C entry point; o is caller-allocated, state_cache is updated in place."""
+    args = [as_gdp_tensor(x) for x in (q, k, v, g_log, beta)]
+    cache, slots, ot = as_gdp_tensor(state_cache), as_gdp_tensor(state_indices), as_gdp_tensor(o)
+    st = _stream(q.device) if stream is None else stream
+    _check(LIB.gdp_recurrent_decode(*[ctypes.byref(a) for a in args], int(num_householder), float(scale or 0.0),
+                                    int(bool(use_qk_l2norm)), ctypes.byref(cache), ctypes.byref(slots),
+                                    ctypes.byref(ot), st))
+
+
 # ---------------------------------------------------------------- convenience wrapper
 
 def chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None, initial_state=None,
@@ -216,3 +230,15 @@ def chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None,
     if return_chunk_states:
         return o, fs, cs, descriptors["chunk_offsets"]
     return o, fs
+
+
+def recurrent_decode(q, k, v, g_log, beta, num_householder, state_cache, state_indices, scale=None,
+                     use_qk_l2norm=False, out=None):
+    """Allocating front end of the decode step: returns o [N, Hv, V]; the state
+    cache is updated in place."""
+    N = q.shape[0]
+    Hv, V = v.shape[1], v.shape[2]
+    o = out if out is not None else torch.empty((N, Hv, V), dtype=q.dtype, device=q.device)
+    gdp_recurrent_decode(q, k, v, g_log, beta, num_householder, scale or 0.0, use_qk_l2norm, state_cache,
+                         state_indices, o)
+    return o

@@ -8,7 +8,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdp.so")
-SOURCES = [os.path.join(CSRC, "gdp_kernels.hip"), os.path.join(CSRC, "gdp_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gdp_kernels.hip"), os.path.join(CSRC, "gdp_decode.hip"),
+           os.path.join(CSRC, "gdp_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are disabled for every gfx950 compile.

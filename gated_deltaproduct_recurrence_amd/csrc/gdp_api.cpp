@@ -330,4 +330,72 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   return GDP_OK;
 }
 
+int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
+                         const gdp_tensor *beta, int32_t n, float scale, int32_t use_qk_l2norm,
+                         const gdp_tensor *state_cache, const gdp_tensor *state_indices, const gdp_tensor *o,
+                         void *stream) {
+  g_last_error.clear();
+  if (!present(q) || !present(k) || !present(v) || !present(g_log) || !present(beta) || !present(o))
+    return fail(GDP_EINVAL, "q, k, v, g_log, beta and o are required");
+  if (!present(state_cache) || !present(state_indices))
+    return fail(GDP_EINVAL, "state_cache and state_indices are required");
+  if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1, got %d", n);
+  if (q->ndim != 3 || v->ndim != 3) return fail(GDP_EINVAL, "q must be [N, Hqk, K] and v [N*n, Hv, V]");
+  const int64_t N = q->shape[0], Hqk = q->shape[1], K = q->shape[2];
+  const int64_t Hv = v->shape[1], V = v->shape[2];
+  if (Hqk < 1 || Hv < 1 || K < 1 || V < 1) return fail(GDP_EINVAL, "head counts and dims must be positive");
+  if (Hv % Hqk != 0) return fail(GDP_EINVAL, "Hv (%lld) must be a multiple of Hqk (%lld)", (long long)Hv, (long long)Hqk);
+  if (N > INT32_MAX || Hv > 65535) return fail(GDP_EINVAL, "too many sequences or heads");
+  const int32_t dt = q->dtype;
+  if (dt != GDP_F32 && dt != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q must be float32 or bfloat16");
+  if (k->dtype != dt || v->dtype != dt || o->dtype != dt)
+    return fail(GDP_EUNSUPPORTED, "q, k, v and o must share one dtype");
+  if (g_log->dtype != GDP_F32 || beta->dtype != GDP_F32 || state_cache->dtype != GDP_F32)
+    return fail(GDP_EUNSUPPORTED, "g_log, beta and state_cache must be float32");
+  if (state_indices->dtype != GDP_I32 && state_indices->dtype != GDP_I64)
+    return fail(GDP_EINVAL, "state_indices must be int32 or int64");
+  int rc;
+  const int64_t sq[3] = {N, Hqk, K}, sk[3] = {N * n, Hqk, K}, sv[3] = {N * n, Hv, V};
+  const int64_t sg[2] = {N, Hv}, sb[2] = {N * n, Hv}, so[3] = {N, Hv, V}, si[1] = {N};
+  const int64_t sc[4] = {-1, Hv, K, V};
+  if ((rc = check_shape(q, "q", 3, sq)) || (rc = check_shape(k, "k", 3, sk)) || (rc = check_shape(v, "v", 3, sv)) ||
+      (rc = check_shape(g_log, "g_log", 2, sg)) || (rc = check_shape(beta, "beta", 2, sb)) ||
+      (rc = check_shape(o, "o", 3, so)) || (rc = check_shape(state_indices, "state_indices", 1, si)) ||
+      (rc = check_shape(state_cache, "state_cache", 4, sc)))
+    return rc;
+  for (const gdp_tensor *t : {q, k, v, g_log, beta, o})
+    if (!nonneg_strides(t)) return fail(GDP_EINVAL, "negative strides are not supported");
+  if (!contiguous(state_cache)) return fail(GDP_EINVAL, "state_cache must be contiguous");
+  if (!gdp::decode_supported((int)K, (int)V))
+    return fail(GDP_EUNSUPPORTED, "head dims K=%lld V=%lld are not served", (long long)K, (long long)V);
+  // the state cache is read and written; o is written: neither may overlap an input or the other
+  Range ins[] = {range_of(q, "q"), range_of(k, "k"), range_of(v, "v"), range_of(g_log, "g_log"),
+                 range_of(beta, "beta"), range_of(state_indices, "state_indices")};
+  Range outs[] = {range_of(o, "o"), range_of(state_cache, "state_cache")};
+  for (const Range &ro : outs)
+    for (const Range &ri : ins)
+      if (overlap(ro, ri)) return fail(GDP_EALIAS, "%s overlaps input %s", ro.name, ri.name);
+  if (overlap(outs[0], outs[1])) return fail(GDP_EALIAS, "o overlaps state_cache");
+
+  gdp::DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q->data; a.q_st = q->stride[0]; a.q_sh = q->stride[1];
+  a.k = k->data; a.k_st = k->stride[0]; a.k_sh = k->stride[1];
+  a.v = v->data; a.v_st = v->stride[0]; a.v_sh = v->stride[1];
+  a.g = (const float *)g_log->data; a.g_st = g_log->stride[0]; a.g_sh = g_log->stride[1];
+  a.beta = (const float *)beta->data; a.b_st = beta->stride[0]; a.b_sh = beta->stride[1];
+  a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv;
+  a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
+  a.l2norm = use_qk_l2norm ? 1 : 0;
+  a.cache = (float *)state_cache->data;
+  a.num_slots = state_cache->shape[0];
+  a.slots = state_indices->data;
+  a.slots_is64 = state_indices->dtype == GDP_I64;
+  a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
+  hipError_t e = gdp::launch_decode(a, dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDP_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return GDP_OK;
+}
+
 }  // extern "C"

@@ -47,6 +47,21 @@ struct PrefillArgs {
 
 enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
 
+// Arguments of the single-token decode step (strides in elements).
+struct DecodeArgs {
+  const void *q; int64_t q_st, q_sh;      // [N, Hqk, K]
+  const void *k; int64_t k_st, k_sh;      // [N*n, Hqk, K]
+  const void *v; int64_t v_st, v_sh;      // [N*n, Hv, V]
+  const float *g; int64_t g_st, g_sh;     // [N, Hv]
+  const float *beta; int64_t b_st, b_sh;  // [N*n, Hv]
+  int N, n, Hqk, Hv;
+  float scale;
+  int l2norm;
+  float *cache; int64_t num_slots;        // [num_slots, Hv, K, V], read and written in place
+  const void *slots; int slots_is64;      // [N]
+  void *o; int64_t o_st, o_sh;            // [N, Hv, V]
+};
+
 // Kernel path: AUTO picks the fused single kernel for bf16 when there are at
 // least 256 (sequence, state head) chains, else the WY kernel + scan kernel pair.
 enum Path { PATH_AUTO = 0, PATH_FUSED = 1, PATH_SPLIT = 2 };
@@ -56,5 +71,7 @@ bool prefill_supported(int dtype, int K, int V);
 size_t wy_buffer_bytes(int dtype, int64_t rows, int64_t Hv);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, int path, hipStream_t stream);
 hipError_t launch_descriptors(const DescArgs &a, hipStream_t stream);
+bool decode_supported(int K, int V);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int K, int V, hipStream_t stream);
 
 }  // namespace gdp

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for chunked GDP prefill.
+"""Seeded synthetic inputs for chunked GDP prefill and the decode step.
 
 Input generation only -- this module holds none of the method's arithmetic.
 It serves both the GPU path's tests and benchmark and the oracle-side checks
@@ -119,3 +119,33 @@ def generate(w: Workload, device="cpu"):
     return dict(q=q, k=k, v=v, g_log=g, beta=beta, num_householder=n, cu_seqlens=cu, scale=w.scale,
                 initial_state=s0, output_final_state=w.output_final_state, use_qk_l2norm=w.l2norm_in_kernel,
                 state_cache=cache, state_indices=slots, return_chunk_states=w.return_chunk_states)
+
+
+def decode_batch(N, n, Hqk, Hv, K, V, slots, pad=0, dtype=torch.bfloat16, l2norm_in_kernel=False, g_shift=0.0,
+                 cache_std=0.3, seed=11, device="cpu"):
+    """Inputs of one decode step for N entries: one token (n sub-rows) each, a
+    state cache of `slots` rows ~ N(0, cache_std^2), and state indices that are a
+    seeded permutation of the slots with `pad` entries set to -1 at seeded
+    positions.  Distributions as for the prefill workloads."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    cpu_gen = torch.Generator().manual_seed(seed)
+    idx = torch.randperm(slots, generator=cpu_gen)[:N].to(torch.int32)
+    if pad:
+        idx[torch.randperm(N, generator=cpu_gen)[:pad]] = -1
+    idx = idx.to(dev)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    q = randn(N, Hqk, K)
+    k = randn(N * n, Hqk, K)
+    if not l2norm_in_kernel:
+        q = _unit_rows(q)
+        k = _unit_rows(k)
+    v = randn(N * n, Hv, V)
+    g = -torch.nn.functional.softplus(randn(N, Hv) - g_shift)
+    beta = torch.sigmoid(randn(N * n, Hv))
+    cache = cache_std * randn(slots, Hv, K, V)
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), g_log=g, beta=beta, num_householder=n,
+                state_cache=cache, state_indices=idx, use_qk_l2norm=l2norm_in_kernel)

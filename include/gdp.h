@@ -157,6 +157,35 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
                       const gdp_tensor *chunk_states, const gdp_descriptors *desc,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Device.  The single-token recurrent decode step on the state cache, in place.
+ *
+ * The decode step of the blog page "Attention Cache and Sequence Parallelism"
+ * (section "GDN: fixed state instead of a per-token cache": Sbar = lambda S,
+ * vhat = Sbar^T k, e = beta (v - vhat), S = Sbar + k e^T, r = q^T S), with the
+ * n Householder rows per token of the FlashInfer recurrence display and the
+ * slot convention of the Megatron Core page (state / state_indices).  For
+ * every entry i and state head h with slot = state_indices[i] in [0, S):
+ *     S = state_cache[slot, h];  S *= exp(g_log[i, h]);
+ *     for j = 0..n-1, r = i*n + j:  e = beta[r,h] (v[r,h] - S^T k[r]);  S += k[r] e^T;
+ *     o[i, h] = scale * S^T q[i];  state_cache[slot, h] = S.
+ * Entries whose index is negative (padding, -1) or past the cache get a zero
+ * output row and leave the cache untouched.
+ *   q [N, Hqk, K], k [N*n, Hqk, K], v [N*n, Hv, V]   bf16 or f32 (one dtype); rows may be strided
+ *   g_log [N, Hv], beta [N*n, Hv]                    f32 (log decays; alpha = exp(g_log))
+ *   scale                                            0 means K^-1/2
+ *   use_qk_l2norm                                    as for gdp_chunk_prefill
+ *   state_cache [S, Hv, K, V]                        f32 contiguous, K-major states, read and written
+ *   state_indices [N]                                int32 or int64
+ *   o [N, Hv, V]                                     q's dtype, written
+ * Two entries naming the same slot race (caller error; not checked: that needs
+ * a device read).  o and the cache may not overlap the inputs or each other
+ * (GDP_EALIAS).  K, V in {64, 128}.  One kernel launch on `stream`; nothing is
+ * allocated, so the call is capturable. */
+int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                         const gdp_tensor *g_log, const gdp_tensor *beta, int32_t num_householder,
+                         float scale, int32_t use_qk_l2norm, const gdp_tensor *state_cache,
+                         const gdp_tensor *state_indices, const gdp_tensor *o, void *stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *gdp_last_error(void);
 

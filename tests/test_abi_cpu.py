@@ -210,3 +210,64 @@ def test_build_descriptors_capacity_check(b):
     d.nt_cap, d.ntdp_cap = 15, 29
     rc = b.LIB.gdp_build_descriptors(ctypes.byref(cu), 2, 812, ctypes.byref(d), None)
     assert rc == b.GDP_EINVAL and "below the bound" in b.gdp_last_error()
+
+
+# ---------------------------------------------------------------- decode step
+
+def decode_args(b, N=8, n=2, Hqk=2, Hv=4, K=128, V=128, S=16, dt=None):
+    f = Fake()
+    dt = b.GDP_BF16 if dt is None else dt
+    a = dict(q=f.tensor(b, dt, [N, Hqk, K]), k=f.tensor(b, dt, [N * n, Hqk, K]), v=f.tensor(b, dt, [N * n, Hv, V]),
+             g_log=f.tensor(b, b.GDP_F32, [N, Hv]), beta=f.tensor(b, b.GDP_F32, [N * n, Hv]), n=n, scale=0.0, l2=0,
+             cache=f.tensor(b, b.GDP_F32, [S, Hv, K, V]), slots=f.tensor(b, b.GDP_I32, [N]),
+             o=f.tensor(b, dt, [N, Hv, V]))
+    a["fake"] = f
+    return a
+
+
+def decode_expect(b, a, code, fragment):
+    r = ctypes.byref
+    rc = b.LIB.gdp_recurrent_decode(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g_log"]), r(a["beta"]), a["n"],
+                                    a["scale"], a["l2"], r(a["cache"]), r(a["slots"]), r(a["o"]), None)
+    assert rc == code, (rc, b.gdp_last_error())
+    assert fragment in b.gdp_last_error(), b.gdp_last_error()
+
+
+def test_decode_requires_cache(b):
+    a = decode_args(b)
+    a["cache"] = b.gdp_tensor()
+    decode_expect(b, a, b.GDP_EINVAL, "state_cache and state_indices are required")
+
+
+def test_decode_shapes_and_dtypes(b):
+    a = decode_args(b)
+    a["k"] = a["fake"].tensor(b, b.GDP_BF16, [8, 2, 128])
+    decode_expect(b, a, b.GDP_EINVAL, "k: dim 0")
+    a = decode_args(b)
+    a["cache"] = a["fake"].tensor(b, b.GDP_F32, [16, 4, 128, 64])
+    decode_expect(b, a, b.GDP_EINVAL, "state_cache: dim 3")
+    a = decode_args(b)
+    a["cache"] = a["fake"].tensor(b, b.GDP_BF16, [16, 4, 128, 128])
+    decode_expect(b, a, b.GDP_EUNSUPPORTED, "float32")
+    a = decode_args(b)
+    a["slots"] = a["fake"].tensor(b, b.GDP_F32, [8])
+    decode_expect(b, a, b.GDP_EINVAL, "int32 or int64")
+    a = decode_args(b, K=96, V=96)
+    decode_expect(b, a, b.GDP_EUNSUPPORTED, "K=96")
+    a = decode_args(b, Hqk=3, Hv=4)
+    decode_expect(b, a, b.GDP_EINVAL, "multiple of Hqk")
+    a = decode_args(b)
+    a["n"] = 0
+    decode_expect(b, a, b.GDP_EINVAL, "num_householder")
+
+
+def test_decode_aliasing(b):
+    a = decode_args(b)
+    a["o"] = a["fake"].tensor(b, b.GDP_BF16, [8, 4, 128], data=a["v"].data)
+    decode_expect(b, a, b.GDP_EALIAS, "o overlaps input v")
+    a = decode_args(b)
+    a["cache"] = a["fake"].tensor(b, b.GDP_F32, [16, 4, 128, 128], data=a["k"].data)
+    decode_expect(b, a, b.GDP_EALIAS, "state_cache overlaps input k")
+    a = decode_args(b)
+    a["o"] = a["fake"].tensor(b, b.GDP_BF16, [8, 4, 128], data=a["cache"].data + 4096)
+    decode_expect(b, a, b.GDP_EALIAS, "o overlaps state_cache")
