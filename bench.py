@@ -56,12 +56,22 @@ def measured_traffic():
 
 
 def kernel_label(w):
-    """Kernel(s) the library runs for this workload: the fused single kernel for
-    bf16 inputs with at least 256 (sequence, state head) chains, else the WY +
-    scan pair; GDP_PREFILL_PATH=fused|split forces one (bf16 only)."""
+    """Kernel(s) the library runs for this workload (the same rule as the
+    library's path choice; GDP_PREFILL_PATH=fused|split|segmented forces one):
+    the fused single kernel for bf16 inputs with at least 256 (sequence, state
+    head) chains; for fewer chains of long sequences (bf16, K == V) the fused
+    kernel on segments plus the segment combine; otherwise the WY + scan pair."""
     import torch
     forced = os.environ.get("GDP_PREFILL_PATH")
-    fused = w.dtype == torch.bfloat16 and (forced == "fused" or (forced != "split" and w.N * w.Hv >= 256))
+    bf16 = w.dtype == torch.bfloat16
+    chains = w.N * w.Hv
+    if bf16 and w.K == w.V and w.K in (64, 128) and forced not in ("fused", "split"):
+        avg = -(-w.T // max(w.N, 1))
+        target = max(2, 256 // max(chains, 1))
+        L = max(256, (-(-avg // target) + 63) // 64 * 64)
+        if forced == "segmented" or (chains < 256 and avg >= 2 * L):
+            return "gdp_fused_kernel on segments + gdp_combine_kernel"
+    fused = bf16 and (forced == "fused" or (forced != "split" and chains >= 256))
     return "gdp_fused_kernel" if fused else "gdp_wy_kernel + gdp_scan_kernel"
 
 

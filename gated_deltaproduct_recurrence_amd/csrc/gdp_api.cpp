@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -92,6 +93,48 @@ size_t desc_bytes(int64_t N, int64_t nt_cap, int64_t ntdp_cap) {
   return align256((size_t)nt_cap * 8) + align256((size_t)ntdp_cap * 8) + 2 * align256((size_t)(N + 1) * 4);
 }
 
+// Segmented prefill plan (host-known sizes only, so the call stays capturable):
+// bf16 inputs, K == V, fewer than 256 (sequence, state head) chains and
+// sequences long enough to cut into segments of whole 64-token chunks such that
+// the segment chains fill the 256 compute units.
+struct SegPlan {
+  bool use = false;
+  int64_t Lseg = 0, ns_cap = 0;
+};
+
+SegPlan seg_plan(int64_t T, int64_t N, int64_t Hv, int64_t K, int64_t V, int32_t dtype, int path) {
+  SegPlan p;
+  if (dtype != GDP_BF16 || K != V || !(K == 64 || K == 128) || N < 1 || T < 0) return p;
+  if (path == gdp::PATH_FUSED || path == gdp::PATH_SPLIT) return p;
+  if (path != gdp::PATH_SEGMENTED && N * Hv >= 256) return p;
+  const int64_t avg = (T + N - 1) / N;
+  const int64_t target = std::max<int64_t>(2, 256 / (N * Hv));  // segments per sequence
+  int64_t L = (avg + target - 1) / target;
+  L = std::max<int64_t>(256, (L + 63) / 64 * 64);
+  if (path != gdp::PATH_SEGMENTED && avg < 2 * L) return p;
+  p.use = true;
+  p.Lseg = L;
+  p.ns_cap = (T + (L - 1) * N) / L;
+  return p;
+}
+
+size_t seg_bytes(const SegPlan &p, int64_t N, int64_t Hv, int64_t K, int64_t V) {
+  if (!p.use) return 0;
+  return align256((size_t)(p.ns_cap + 1) * 4) + align256((size_t)(N + 1) * 4) + align256((size_t)p.ns_cap * 4) +
+         align256((size_t)p.ns_cap * Hv * K * K * 4) + 2 * align256((size_t)p.ns_cap * Hv * K * V * 4);
+}
+
+int env_path() {
+  // GDP_PREFILL_PATH=fused|split|segmented overrides the automatic kernel
+  // choice (tests use it to run every path on the same inputs)
+  if (const char *env = std::getenv("GDP_PREFILL_PATH")) {
+    if (std::strcmp(env, "fused") == 0) return gdp::PATH_FUSED;
+    if (std::strcmp(env, "split") == 0) return gdp::PATH_SPLIT;
+    if (std::strcmp(env, "segmented") == 0) return gdp::PATH_SEGMENTED;
+  }
+  return gdp::PATH_AUTO;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,12 +152,14 @@ int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t n, int64_t *nt_cap, in
 
 size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V,
                            int32_t dtype) {
-  (void)Hqk; (void)K; (void)V;
+  (void)Hqk;
   int64_t ct, cd;
   if (Hv < 1 || (dtype != GDP_F32 && dtype != GDP_BF16)) return 0;
   if (gdp_descriptor_capacity(T, N, n, &ct, &cd) != GDP_OK) return 0;
-  return align256(gdp::wy_buffer_bytes(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, cd, Hv)) +
-         desc_bytes(N, ct, cd);
+  const size_t wy = align256(gdp::wy_buffer_bytes(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, cd, Hv));
+  // the segmented path (forced or automatic) needs its own buffers instead of the WY matrices
+  const SegPlan forced = seg_plan(T, N, Hv, K, V, dtype, gdp::PATH_SEGMENTED);
+  return std::max(wy, seg_bytes(forced, N, Hv, K, V)) + desc_bytes(N, ct, cd);
 }
 
 int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t n, int64_t T, const gdp_descriptors *out,
@@ -259,9 +304,14 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return fail(GDP_EALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
 
-  // workspace: the WY matrices, then (when the caller passes none) the descriptors
+  // workspace: the WY matrices (or, on the segmented path, the segment buffers),
+  // then (when the caller passes none) the descriptors
   const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
-  const size_t wy_bytes = align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv));
+  const int path = env_path();
+  const SegPlan plan = seg_plan(T, N, Hv, K, V, dt, path);
+  if (path == gdp::PATH_SEGMENTED && !plan.use)
+    return fail(GDP_EUNSUPPORTED, "the segmented path needs bf16 inputs with K == V in {64, 128}");
+  const size_t wy_bytes = std::max(align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv)), seg_bytes(plan, N, Hv, K, V));
   const size_t need = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap));
   if (!workspace || workspace_bytes < need)
     return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
@@ -318,14 +368,43 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   a.tws = workspace;
   a.tws_rows = ntdp_cap;
   a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
-  // GDP_PREFILL_PATH=fused|split overrides the automatic kernel choice (tests use it
-  // to run both paths on the same inputs); anything else means automatic.
-  int path = gdp::PATH_AUTO;
-  if (const char *env = std::getenv("GDP_PREFILL_PATH")) {
-    if (std::strcmp(env, "fused") == 0) path = gdp::PATH_FUSED;
-    else if (std::strcmp(env, "split") == 0) path = gdp::PATH_SPLIT;
+  hipError_t e;
+  if (plan.use) {
+    // segmented: segment boundaries, summaries (M, B) of every segment, their
+    // in-order combination per chain, then every segment from its start state
+    char *p = (char *)workspace;
+    int32_t *cu_seg = (int32_t *)p; p += align256((size_t)(plan.ns_cap + 1) * 4);
+    int32_t *seg_first = (int32_t *)p; p += align256((size_t)(N + 1) * 4);
+    int32_t *seg_cs_off = (int32_t *)p; p += align256((size_t)plan.ns_cap * 4);
+    float *msum = (float *)p; p += align256((size_t)plan.ns_cap * Hv * K * K * 4);
+    float *bsum = (float *)p; p += align256((size_t)plan.ns_cap * Hv * K * V * 4);
+    float *seg_init = (float *)p;
+    gdp::SegArgs sa;
+    sa.cu = cu_seqlens->data; sa.cu_is64 = a.cu_is64; sa.N = N; sa.T = T; sa.Lseg = plan.Lseg;
+    sa.ns_cap = plan.ns_cap; sa.chunk_offsets = d->chunk_offsets;
+    sa.cu_seg = cu_seg; sa.seg_first = seg_first; sa.seg_cs_off = seg_cs_off;
+    if ((e = gdp::launch_segments(sa, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "segment launch: %s", hipGetErrorString(e));
+    gdp::PrefillArgs s1 = a;
+    s1.cu = cu_seg; s1.cu_is64 = 0; s1.N = (int)plan.ns_cap;
+    s1.s0 = nullptr; s1.final_state = bsum; s1.msum = msum; s1.summary = 1; s1.o = nullptr;
+    s1.cache = nullptr; s1.chunk_states = nullptr;
+    if ((e = gdp::launch_fused_prefill(s1, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "segment summary launch: %s", hipGetErrorString(e));
+    gdp::CombineArgs ca;
+    ca.N = (int)N; ca.Hv = (int)Hv; ca.seg_first = seg_first; ca.msum = msum; ca.bsum = bsum;
+    ca.seg_init = seg_init; ca.s0 = a.s0; ca.final_state = a.final_state;
+    ca.cache = a.cache; ca.slots = a.slots; ca.slots_is64 = a.slots_is64; ca.num_slots = a.num_slots;
+    if ((e = gdp::launch_combine(ca, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "segment combine launch: %s", hipGetErrorString(e));
+    gdp::PrefillArgs s3 = a;
+    s3.cu = cu_seg; s3.cu_is64 = 0; s3.N = (int)plan.ns_cap;
+    s3.s0 = seg_init; s3.final_state = nullptr; s3.cache = nullptr; s3.chunk_offsets = seg_cs_off;
+    if ((e = gdp::launch_fused_prefill(s3, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "segment prefill launch: %s", hipGetErrorString(e));
+    return GDP_OK;
   }
-  hipError_t e = gdp::launch_prefill(a, idt, (int)K, (int)V, path, (hipStream_t)stream);
+  e = gdp::launch_prefill(a, idt, (int)K, (int)V, path, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDP_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return GDP_OK;
 }

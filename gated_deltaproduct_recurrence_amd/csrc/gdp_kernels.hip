@@ -1113,7 +1113,12 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   // walks a contiguous range of chains (the heads sharing a q/k head, and the
   // V-tiles of one head, then read the same k/q rows through one L2).
   const int64_t G = gridDim.x, bid = blockIdx.x;
-  const int64_t chain = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  int64_t chain = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  // segment summaries: the second half of the grid is part 1 (zero values,
+  // identity start state, final state to msum)
+  const int64_t nchain = (int64_t)a.N * a.Hv * NVT;
+  const bool part1 = a.summary && chain >= nchain;
+  if (part1) chain -= nchain;
   const int vt = (int)(chain % NVT);
   const int h = (int)((chain / NVT) % a.Hv);
   const int seq = (int)(chain / ((int64_t)NVT * a.Hv));
@@ -1164,7 +1169,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     for (int at = 0; at < KT16; ++at)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        if (a.s0) {
+        if (part1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Sacc[at][b][i] = kap(at, lg, i) == gcol + 16 * b + lr ? 1.f : 0.f;
+        } else if (a.s0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             Sacc[at][b][i] = a.s0[state_off + (size_t)kap(at, lg, i) * V + gcol + 16 * b + lr];
@@ -1451,7 +1459,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in rq).
       // They are staged in bf16 in this chunk's v tile (unused after the R step)
       // and helper 3 stores whole rows from there in the next chunk.
-      if (j == n - 1 || e == nexp - 1) {
+      if ((j == n - 1 || e == nexp - 1) && a.o) {
         char *stg = sm.v[ts];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4)
@@ -1461,7 +1469,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       }
       lds_barrier();
     }
-    float *fdst = a.final_state ? a.final_state + state_off : nullptr;
+    float *fdst = part1 ? a.msum + state_off : (a.final_state ? a.final_state + state_off : nullptr);
     float *cdst = nullptr;
     if (a.cache) {
       const int64_t slot = load_index(a.slots, a.slots_is64, seq);
@@ -1729,10 +1737,13 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       constexpr int NLQ = KW / 16 + 1;  // loads per q tile and its token decays
       const TileOffs<KW, 1> koffs = tile_offs<KW, 1>(kst, lane), qoffs = tile_offs<KW, 1>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
+      if (part1) {  // zero values: both v tiles stay zero (no outputs are staged in them)
+        for (int u = hl; u < 2 * CH * VW / 16; u += 64) *(uint4 *)(sm.v[0] + 16 * u) = uint4{0u, 0u, 0u, 0u};
+      }
       if (nexp > 0) {
         load_k(0, koffs);
         if (nexp > 1) load_k(1, koffs);
-        load_v(0, voffs);
+        if (!part1) load_v(0, voffs);
         load_scalars(0);
         if (nexp > 1) load_scalars(1);
         load_q(0, qoffs);
@@ -1768,7 +1779,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         // the Gram stage the k rows of chunk e+2.
         const bool lq = j == n - 1 && c + 2 < ntc;
         if (e + 1 < nexp) tables(e + 1);  // needs the k-row norms from the Gram stage
-        if (e + 1 < nexp) load_v(e + 1, voffs);
+        if (e + 1 < nexp && !part1) load_v(e + 1, voffs);
         if (lq) {
           load_q(c + 2, qoffs);
           wait_vm_keep<NLQ>();
@@ -1817,13 +1828,13 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
-        if (e >= 1 && e % n == 0) store_o(e - 1);
+        if (e >= 1 && e % n == 0 && a.o) store_o(e - 1);
         if (e + 1 < nexp) gram(e + 1, 5, 10, 4);
         lds_barrier();
         if (e + 1 < nexp) block(e + 1, IC<2>{});
         lds_barrier();
       }
-      if (nexp > 0) store_o(nexp - 1);
+      if (nexp > 0 && a.o) store_o(nexp - 1);
     }
   }
 }
@@ -1953,6 +1964,15 @@ hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int K, int V>
+hipError_t launch_fused_twice(const PrefillArgs &a, hipStream_t stream) {
+  constexpr int NCW = 4;
+  const int64_t blocks = 2 * (int64_t)a.N * a.Hv;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
+  return hipGetLastError();
+}
+
 // The fused kernel keeps one chain per CU busy for its whole length; it is
 // chosen when there are enough chains to give every CU one.  Otherwise the
 // split pair (parallel WY kernel, then the scan) spreads the WY work of few
@@ -1987,6 +2007,19 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, int pat
   } else if (dtype == IN_F32) {
     if (K == 64 && V == 64) return launch_all<float, 64, 64>(a, path, stream);
     if (K == 64 && V == 128) return launch_all<float, 64, 128>(a, path, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_prefill(const PrefillArgs &a, int K, int V, hipStream_t stream) {
+  // the summary grid holds every chain twice
+  if (K == 128 && V == 128) {
+    PrefillArgs b = a;
+    return a.summary ? launch_fused_twice<128, 128>(b, stream) : launch_fused<128, 128>(b, stream);
+  }
+  if (K == 64 && V == 64) {
+    PrefillArgs b = a;
+    return a.summary ? launch_fused_twice<64, 64>(b, stream) : launch_fused<64, 64>(b, stream);
   }
   return hipErrorInvalidValue;
 }

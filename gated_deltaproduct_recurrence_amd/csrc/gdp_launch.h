@@ -42,7 +42,14 @@ struct PrefillArgs {
   int64_t ntdp_rows;                // rows of chunk_indices_dp (WY grid)
   void *tws;                        // WY matrices: [tws_rows, Hv, 64*64] input dtype, fragment order
   int64_t tws_rows;
-  void *o; int64_t o_st, o_sh;
+  void *o; int64_t o_st, o_sh;      // null: no outputs (the segment summaries of the fused kernel)
+  // Segment summaries (fused kernel only, K == V): the grid holds each chain
+  // twice.  Part 0 runs from a zero state with the real values and writes its
+  // final state (B of the segment's map S -> M S + B) to final_state; part 1
+  // runs from the identity with zero values and writes its final state (M) to
+  // msum.
+  int summary;
+  float *msum;                      // [N, Hv, K, K]
 };
 
 enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
@@ -63,14 +70,41 @@ struct DecodeArgs {
 };
 
 // Kernel path: AUTO picks the fused single kernel for bf16 when there are at
-// least 256 (sequence, state head) chains, else the WY kernel + scan kernel pair.
-enum Path { PATH_AUTO = 0, PATH_FUSED = 1, PATH_SPLIT = 2 };
+// least 256 (sequence, state head) chains, the segmented path (fused kernel on
+// segments of long sequences) for bf16 with fewer chains and long sequences,
+// else the WY kernel + scan kernel pair.
+enum Path { PATH_AUTO = 0, PATH_FUSED = 1, PATH_SPLIT = 2, PATH_SEGMENTED = 3 };
 
 bool prefill_supported(int dtype, int K, int V);
 // Bytes of the WY-matrix buffer for `rows` expanded chunks and Hv heads.
 size_t wy_buffer_bytes(int dtype, int64_t rows, int64_t Hv);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, int path, hipStream_t stream);
 hipError_t launch_descriptors(const DescArgs &a, hipStream_t stream);
+// Segmented prefill: segment boundaries of every sequence (segments of Lseg
+// tokens, a multiple of 64), padded to ns_cap zero-length segments at T.
+struct SegArgs {
+  const void *cu; int cu_is64;
+  int64_t N, T, Lseg, ns_cap;
+  const int32_t *chunk_offsets;  // [N+1] token-chunk offsets of the sequences
+  int32_t *cu_seg;               // [ns_cap+1] segment boundaries (a cu_seqlens of segments)
+  int32_t *seg_first;            // [N+1] first segment of every sequence
+  int32_t *seg_cs_off;           // [ns_cap] chunk-state row of every segment's first chunk
+};
+// Segmented prefill: the in-order combination of the segment summaries.
+struct CombineArgs {
+  int N, Hv;
+  const int32_t *seg_first;      // [N+1]
+  const float *msum, *bsum;      // [ns, Hv, K, K] and [ns, Hv, K, V]
+  float *seg_init;               // [ns, Hv, K, V] start state of every segment (written)
+  const float *s0;               // [N, Hv, K, V] or null
+  float *final_state;            // [N, Hv, K, V] or null
+  float *cache; const void *slots; int slots_is64; int64_t num_slots;
+};
+hipError_t launch_segments(const SegArgs &a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);
+// launches the fused kernel regardless of the chain count (bf16 only)
+hipError_t launch_fused_prefill(const PrefillArgs &a, int K, int V, hipStream_t stream);
+
 bool decode_supported(int K, int V);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int K, int V, hipStream_t stream);
 

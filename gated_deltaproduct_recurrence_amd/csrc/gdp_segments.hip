@@ -1,0 +1,207 @@
+// gdp_segments.hip -- gfx950 kernels of the segmented (chunk-parallel) prefill
+// for workloads with few (sequence, state head) chains.
+//
+// A chain's state after a run of tokens is an affine map of the state before
+// it, S -> M S + B (blog page "Attention Cache and Sequence Parallelism",
+// section "GDN: pass the state, not the KV": each chunk forms an
+// input-state -> output-state transition summary, combined by a scan).  Long
+// sequences are cut into segments of whole 64-token chunks; the summaries
+// (M, B) of all segments are formed in parallel by the fused prefill kernel
+// (B from a zero state with the real values, M from the identity with zero
+// values), combined in order per chain here, and the segments are then run
+// again from their true start states.
+//
+//   gdp_segment_kernel   one workgroup: segment boundaries (as a cu_seqlens of
+//                        segments), the first segment of every sequence and
+//                        the chunk-state row offset of every segment
+//   gdp_combine_kernel   one workgroup per (sequence, state head, 16-column
+//                        tile): S = s0; per segment: record S as the segment's
+//                        start state, S = M S + B (fp32 MFMA); final state and
+//                        cache slot at the end
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdp_launch.h"
+
+namespace gdp {
+namespace {
+
+__device__ __forceinline__ int64_t seg_index_at(const void *p, int is64, int64_t i) {
+  return is64 ? ((const int64_t *)p)[i] : (int64_t)((const int32_t *)p)[i];
+}
+
+// exclusive block scan of one value per thread (1024 threads); returns the
+// prefix and writes the total to *total
+__device__ int64_t block_exclusive_scan(int64_t x, int64_t *ws, int64_t *total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int64_t v = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(v, d, 64);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) ws[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int64_t u = lane < 16 ? ws[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int64_t y = __shfl_up(u, d, 64);
+      if (lane >= d) u += y;
+    }
+    if (lane < 16) ws[16 + lane] = u;
+  }
+  __syncthreads();
+  const int64_t before = (w > 0 ? ws[16 + w - 1] : 0) + v - x;
+  *total = ws[16 + 15];
+  __syncthreads();
+  return before;
+}
+
+__global__ void __launch_bounds__(1024) gdp_segment_kernel(SegArgs a) {
+  __shared__ int64_t ws[32];
+  const int t = threadIdx.x;
+  // pass 1: first segment of every sequence (ceil(L / Lseg) segments each)
+  int64_t carry = 0;
+  for (int64_t base = 0; base < a.N; base += 1024) {
+    const int64_t i = base + t;
+    int64_t cnt = 0;
+    if (i < a.N) {
+      int64_t t0 = seg_index_at(a.cu, a.cu_is64, i), t1 = seg_index_at(a.cu, a.cu_is64, i + 1);
+      t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+      t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+      cnt = (t1 - t0 + a.Lseg - 1) / a.Lseg;
+    }
+    int64_t total;
+    const int64_t pre = block_exclusive_scan(cnt, ws, &total);
+    if (i < a.N) a.seg_first[i] = (int32_t)min(carry + pre, a.ns_cap);
+    carry += total;
+  }
+  if (t == 0) a.seg_first[a.N] = (int32_t)min(carry, a.ns_cap);
+  __syncthreads();
+  // pass 2: every segment row finds its sequence by binary search
+  const int64_t nreal = min(carry, a.ns_cap);
+  for (int64_t s = t; s <= a.ns_cap; s += 1024) {
+    if (s >= nreal) {  // the end of the last real segment, then zero-length padding
+      a.cu_seg[s] = (int32_t)a.T;
+      if (s < a.ns_cap) a.seg_cs_off[s] = 0;
+      continue;
+    }
+    int64_t lo = 0, hi = a.N - 1;  // last i with seg_first[i] <= s
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (a.seg_first[mid] <= s) lo = mid; else hi = mid - 1;
+    }
+    int64_t t0 = seg_index_at(a.cu, a.cu_is64, lo);
+    t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+    const int64_t k = s - a.seg_first[lo];
+    a.cu_seg[s] = (int32_t)min(t0 + k * a.Lseg, a.T);
+    a.seg_cs_off[s] = (a.chunk_offsets ? a.chunk_offsets[lo] : 0) + (int32_t)(k * (a.Lseg / 64));
+  }
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// S = M S + B per segment, on a 16-column tile of the state kept in LDS.  M of
+// the segment is staged in LDS with 16-byte loads (rows padded by one float so
+// that 16 lanes reading one column of 16 rows meet 16 banks), the next
+// segment's M is read into registers while this one multiplies.  Wave w
+// computes rows 16 RT w .. of the tile with v_mfma_f32_16x16x4_f32: lane
+// (lg, lr) supplies M[row lr][k = 4 kk + lg] and S[k = 4 kk + lg][col lr] and holds
+// C[4 lg + i][lr].
+template <int K, int V>
+__global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
+  static_assert(K == 128 || K == 64, "K of 64 or 128");
+  constexpr int CT = 16, NCT = V / CT, RT = K / 64, LDM = K + 1;
+  constexpr int NL = K * K / 4 / 256;  // 16-byte loads of M per thread
+  __shared__ float S[K][CT];
+  __shared__ float Ms[K * LDM];
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bid = blockIdx.x;
+  const int ct = (int)(bid % NCT);
+  const int h = (int)((bid / NCT) % a.Hv);
+  const int64_t i = bid / ((int64_t)NCT * a.Hv);
+  const size_t KV = (size_t)K * V, KK = (size_t)K * K;
+  const int c0 = ct * CT;
+  for (int x = tid; x < K * CT; x += 256) {
+    const int r = x / CT, c = x % CT;
+    S[r][c] = a.s0 ? a.s0[((size_t)i * a.Hv + h) * KV + (size_t)r * V + c0 + c] : 0.f;
+  }
+  const int64_t s_lo = a.seg_first[i], s_hi = a.seg_first[i + 1];
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  f4 mreg[NL];
+  auto load_m = [&](int64_t s) {
+    const f4 *M = (const f4 *)(a.msum + ((size_t)s * a.Hv + h) * KK);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) mreg[u] = M[tid + 256 * u];
+  };
+  if (s_lo < s_hi) load_m(s_lo);
+  __syncthreads();
+  for (int64_t s = s_lo; s < s_hi; ++s) {
+    // this segment's M into LDS (element x of the row-major M at row x / K, column x % K)
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = 4 * (tid + 256 * u), r = x / K, c = x % K;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ms[r * LDM + c + e] = mreg[u][e];
+    }
+    if (s + 1 < s_hi) load_m(s + 1);
+    float *init = a.seg_init + ((size_t)s * a.Hv + h) * KV + c0;
+    for (int x = tid; x < K * CT; x += 256) {
+      const int r = x / CT, c = x % CT;
+      init[(size_t)r * V + c] = S[r][c];
+    }
+    const float *B = a.bsum + ((size_t)s * a.Hv + h) * KV + c0;
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[rt][e] = B[(size_t)(w * 16 * RT + 16 * rt + 4 * lg + e) * V + lr];
+    __syncthreads();  // M in LDS
+#pragma unroll 8
+    for (int kk = 0; kk < K / 4; ++kk) {
+      const int kx = 4 * kk + lg;
+      const float bv = S[kx][lr];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ms[(w * 16 * RT + 16 * rt + lr) * LDM + kx], bv, acc[rt], 0, 0, 0);
+    }
+    __syncthreads();  // every wave has read S and M
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[w * 16 * RT + 16 * rt + 4 * lg + e][lr] = acc[rt][e];
+    __syncthreads();
+  }
+  float *fdst = a.final_state ? a.final_state + ((size_t)i * a.Hv + h) * KV + c0 : nullptr;
+  float *cdst = nullptr;
+  if (a.cache) {
+    const int64_t slot = seg_index_at(a.slots, a.slots_is64, i);
+    if (slot >= 0 && slot < a.num_slots) cdst = a.cache + ((size_t)slot * a.Hv + h) * KV + c0;
+  }
+  for (int x = tid; x < K * CT; x += 256) {
+    const int r = x / CT, c = x % CT;
+    if (fdst) fdst[(size_t)r * V + c] = S[r][c];
+    if (cdst) cdst[(size_t)r * V + c] = S[r][c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_segments(const SegArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(gdp_segment_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.N * a.Hv * (V / 16);
+  if (blocks == 0) return hipSuccess;
+  if (K == 128 && V == 128) hipLaunchKernelGGL((gdp_combine_kernel<128, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else if (K == 64 && V == 64) hipLaunchKernelGGL((gdp_combine_kernel<64, 64>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace gdp

@@ -17,9 +17,11 @@ def gdp():
     return binding
 
 
-# bf16 inputs have two kernel paths: the fused single kernel and the WY + scan
-# pair.  Tests over bf16 inputs run each path forced through GDP_PREFILL_PATH.
-PATHS = ["fused", "split"]
+# bf16 inputs have three kernel paths: the fused single kernel, the WY + scan
+# pair, and the segmented path (fused kernel on segments of long sequences,
+# K == V only).  Tests over bf16 inputs run each path forced through
+# GDP_PREFILL_PATH.
+PATHS = ["fused", "split", "segmented"]
 
 
 @pytest.fixture(params=PATHS)
@@ -169,7 +171,8 @@ CASES = [
 ]
 
 
-CASE_PATHS = [(i, p) for i, c in enumerate(CASES) for p in (PATHS if c[6] == torch.bfloat16 else ["auto"])]
+CASE_PATHS = [(i, p) for i, c in enumerate(CASES)
+              for p in (PATHS if c[6] == torch.bfloat16 else ["auto"]) if p != "segmented" or c[4] == c[5]]
 
 
 @pytest.mark.parametrize("ci,kpath", CASE_PATHS, ids=[f"case{i}-{p}" for i, p in CASE_PATHS])
@@ -277,6 +280,36 @@ def test_graph_capture_replay(gdp, path):
         call()
         torch.cuda.synchronize()
         assert torch.equal(go, o) and torch.equal(gs, fs), f"replay differs from eager for {lens}"
+
+
+def test_segmented_long_sequence(gdp, monkeypatch):
+    """A sequence long enough for several segments, with GQA, chunk states and a
+    cache slot: the automatic choice is the segmented path (4 chains); every
+    output, the final state, the chunk-state rows and the cache slot match the
+    oracle, and the fused path on the same inputs."""
+    monkeypatch.delenv("GDP_PREFILL_PATH", raising=False)
+    w = workloads.custom([3000, 1500], 2, 1, 2, 128, 128, dtype=torch.bfloat16, l2norm_in_kernel=True, init_std=0.2,
+                         seed=31, state_cache_slots=3)
+    inp = workloads.generate(w, "cpu")
+    inp["state_indices"] = torch.tensor([2, 0], dtype=torch.int32)
+    inp["return_chunk_states"] = True
+    ref = oracle_run(inp)
+    dev = to_device(inp)
+    cache0 = dev["state_cache"].clone()
+    o, fs, cs, offs = gdp.chunk_prefill(**dev)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    assert rel_err(to_np(o), ref["o"]) <= tol
+    assert rel_err(to_np(fs), ref["final_state"]) <= tol
+    NT = int(offs[-1].item())
+    assert rel_err(to_np(cs[:NT]), ref["chunk_states"]) <= tol
+    assert rel_err(to_np(dev["state_cache"][[2, 0]]), ref["state_cache"][[2, 0]]) <= tol
+    assert torch.equal(dev["state_cache"][1], cache0[1])
+    monkeypatch.setenv("GDP_PREFILL_PATH", "fused")
+    dev2 = to_device(inp)
+    o2, fs2, _, _ = gdp.chunk_prefill(**dev2)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(o), to_np(o2)) <= tol and rel_err(to_np(fs), to_np(fs2)) <= tol
 
 
 def test_fused_and_split_agree(gdp, monkeypatch):
