@@ -124,6 +124,13 @@ size_t seg_bytes(const SegPlan &p, int64_t N, int64_t Hv, int64_t K, int64_t V) 
          align256((size_t)p.ns_cap * Hv * K * K * 4) + 2 * align256((size_t)p.ns_cap * Hv * K * V * 4);
 }
 
+// the fused kernel's longest-first chain order: for grids of more than one round
+// of workgroups (one per CU) and at most ORDER_MAX_SEQ sequences; the workspace
+// reserves it whenever the grid qualifies, the call builds it only when the
+// fused kernel runs
+bool order_grid(int64_t N, int64_t Hv) { return N * Hv > 256 && N <= gdp::ORDER_MAX_SEQ; }
+size_t order_bytes(int64_t N, int64_t Hv) { return order_grid(N, Hv) ? align256((size_t)N * Hv * 4) : 0; }
+
 int env_path() {
   // GDP_PREFILL_PATH=fused|split|segmented overrides the automatic kernel
   // choice (tests use it to run every path on the same inputs)
@@ -159,7 +166,7 @@ size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t
   const size_t wy = align256(gdp::wy_buffer_bytes(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, cd, Hv));
   // the segmented path (forced or automatic) needs its own buffers instead of the WY matrices
   const SegPlan forced = seg_plan(T, N, Hv, K, V, dtype, gdp::PATH_SEGMENTED);
-  return std::max(wy, seg_bytes(forced, N, Hv, K, V)) + desc_bytes(N, ct, cd);
+  return std::max(wy, seg_bytes(forced, N, Hv, K, V)) + desc_bytes(N, ct, cd) + order_bytes(N, Hv);
 }
 
 int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t n, int64_t T, const gdp_descriptors *out,
@@ -312,7 +319,7 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   if (path == gdp::PATH_SEGMENTED && !plan.use)
     return fail(GDP_EUNSUPPORTED, "the segmented path needs bf16 inputs with K == V in {64, 128}");
   const size_t wy_bytes = std::max(align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv)), seg_bytes(plan, N, Hv, K, V));
-  const size_t need = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap));
+  const size_t need = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap)) + order_bytes(N, Hv);
   if (!workspace || workspace_bytes < need)
     return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -403,6 +410,15 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
     if ((e = gdp::launch_fused_prefill(s3, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
       return fail(GDP_EHIP, "segment prefill launch: %s", hipGetErrorString(e));
     return GDP_OK;
+  }
+  if (order_grid(N, Hv) && gdp::fused_chosen(idt, N, Hv, path)) {  // at the end of the workspace
+    int32_t *order = (int32_t *)((char *)workspace + wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap)));
+    gdp::OrderArgs oa;
+    oa.cu = cu_seqlens->data; oa.cu_is64 = a.cu_is64; oa.N = N; oa.T = T; oa.Hqk = (int)Hqk; oa.Hv = (int)Hv;
+    oa.order = order;
+    if ((e = gdp::launch_order(oa, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "order launch: %s", hipGetErrorString(e));
+    a.order = order;
   }
   e = gdp::launch_prefill(a, idt, (int)K, (int)V, path, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDP_EHIP, "prefill launch: %s", hipGetErrorString(e));

@@ -1113,7 +1113,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   // walks a contiguous range of chains (the heads sharing a q/k head, and the
   // V-tiles of one head, then read the same k/q rows through one L2).
   const int64_t G = gridDim.x, bid = blockIdx.x;
-  int64_t chain = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  int64_t chain = a.order ? (int64_t)a.order[bid] : ((G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid);
   // segment summaries: the second half of the grid is part 1 (zero values,
   // identity start state, final state to msum)
   const int64_t nchain = (int64_t)a.N * a.Hv * NVT;
@@ -1979,13 +1979,16 @@ hipError_t launch_fused_twice(const PrefillArgs &a, hipStream_t stream) {
 // long chains over the whole chip.
 template <typename T, int K, int V>
 hipError_t launch_all(const PrefillArgs &a, int path, hipStream_t stream) {
-  if constexpr (sizeof(T) == 2) {
-    const bool fused = path == PATH_FUSED || (path == PATH_AUTO && (int64_t)a.N * a.Hv >= 256);
-    if (fused) return launch_fused<K, V>(a, stream);
+  if (fused_chosen(sizeof(T) == 2 ? IN_BF16 : IN_F32, a.N, a.Hv, path)) {
+    if constexpr (sizeof(T) == 2) return launch_fused<K, V>(a, stream);
   }
   return launch_split<T, K, V>(a, stream);
 }
 }  // namespace
+
+bool fused_chosen(int dtype, int64_t N, int64_t Hv, int path) {
+  return dtype == IN_BF16 && (path == PATH_FUSED || (path == PATH_AUTO && N * Hv >= 256));
+}
 
 bool prefill_supported(int dtype, int K, int V) {
   const bool kv = (K == 64 || K == 128) && (V == 64 || V == 128);

@@ -50,6 +50,17 @@ struct PrefillArgs {
   // msum.
   int summary;
   float *msum;                      // [N, Hv, K, K]
+  // fused kernel: chain run by workgroup b (longest sequences first, spread over
+  // the XCDs), or null for the plain XCD-grouped order
+  const int32_t *order;             // [N * Hv]
+};
+
+// Longest-first order of the fused kernel's chains (one workgroup).
+struct OrderArgs {
+  const void *cu; int cu_is64;
+  int64_t N, T;
+  int Hqk, Hv;
+  int32_t *order;                   // [N * Hv]
 };
 
 enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
@@ -100,7 +111,13 @@ struct CombineArgs {
   float *final_state;            // [N, Hv, K, V] or null
   float *cache; const void *slots; int slots_is64; int64_t num_slots;
 };
+// whether launch_prefill runs the fused kernel (else the split pair) for this
+// input dtype, grid and path
+bool fused_chosen(int dtype, int64_t N, int64_t Hv, int path);
 hipError_t launch_segments(const SegArgs &a, hipStream_t stream);
+// sequences the ordering kernel can rank (LDS-resident lengths)
+constexpr int64_t ORDER_MAX_SEQ = 4096;
+hipError_t launch_order(const OrderArgs &a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);
 // launches the fused kernel regardless of the chain count (bf16 only)
 hipError_t launch_fused_prefill(const PrefillArgs &a, int K, int V, hipStream_t stream);

@@ -101,6 +101,45 @@ __global__ void __launch_bounds__(1024) gdp_segment_kernel(SegArgs a) {
   }
 }
 
+// Longest-first order of the fused kernel's chains.  The dispatcher deals
+// workgroup b to XCD b mod 8 as that XCD's (b / 8)-th workgroup, and a CU runs
+// one fused workgroup at a time, so starting the longest chains first (longest
+// processing time first) shortens the tail of mixed-length batches.  Units are
+// the groups of grp state heads sharing a q/k head (grp = Hv / Hqk, when the
+// grid splits evenly into 8 XCD lists of whole groups; else single heads) in
+// decreasing sequence length (ties by index); XCD x takes units x, x + 8, ...
+// so that each XCD gets an even mix and a unit's heads share that XCD's L2.
+__global__ void __launch_bounds__(1024) gdp_order_kernel(OrderArgs a) {
+  __shared__ int32_t len[ORDER_MAX_SEQ];
+  __shared__ int32_t by_rank[ORDER_MAX_SEQ];
+  const int t = threadIdx.x;
+  for (int64_t i = t; i < a.N; i += 1024) {
+    int64_t t0 = seg_index_at(a.cu, a.cu_is64, i), t1 = seg_index_at(a.cu, a.cu_is64, i + 1);
+    t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+    t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+    len[i] = (int32_t)(t1 - t0);
+  }
+  __syncthreads();
+  for (int64_t i = t; i < a.N; i += 1024) {
+    int32_t r = 0;
+    const int32_t li = len[i];
+    for (int64_t j = 0; j < a.N; ++j) r += (len[j] > li) || (len[j] == li && j < i);
+    by_rank[r] = (int32_t)i;
+  }
+  __syncthreads();
+  const int64_t G = a.N * a.Hv;
+  int grp = a.Hv / a.Hqk;
+  if (G % (8 * grp) != 0) grp = 1;
+  const int64_t units_per_seq = a.Hv / grp;
+  for (int64_t b = t; b < G; b += 1024) {
+    const int64_t x = b % 8, slot = b / 8;
+    const int64_t u = x + 8 * (slot / grp), c = slot % grp;  // unit and head within it
+    const int64_t seq = by_rank[u / units_per_seq];
+    const int64_t h = (u % units_per_seq) * grp + c;
+    a.order[b] = (int32_t)(seq * a.Hv + h);
+  }
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // S = M S + B per segment, on a 16-column tile of the state kept in LDS.  M of
@@ -192,6 +231,12 @@ __global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
 
 hipError_t launch_segments(const SegArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(gdp_segment_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_order(const OrderArgs &a, hipStream_t stream) {
+  if (a.N < 1 || a.N > ORDER_MAX_SEQ) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gdp_order_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -101,9 +101,13 @@ int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t num_householder,
 /* Host-only.  Workspace bytes gdp_chunk_prefill needs for T real tokens, N
  * sequences, n Householder rows per token, Hv state heads and input dtype
  * (GDP_BF16 or GDP_F32): the per-chunk WY matrices (64 x 64 per expanded
- * chunk and state head, at the input precision) plus room for the descriptors
- * when the caller passes none.  Hqk, K and V are accepted for forward
- * compatibility.  Returns 0 for invalid sizes or dtypes. */
+ * chunk and state head, at the input precision) or the buffers of the
+ * segmented (chunk-parallel) path for few long sequences (bf16, K == V: per
+ * segment of at least 256 tokens an f32 K x K map and two K x V states per
+ * head), whichever is larger; plus room for the descriptors when the caller
+ * passes none; plus an int32 work order of N x Hv entries when N x Hv > 256 and
+ * N <= 4096.  Hqk is accepted for forward compatibility.  Returns 0 for invalid
+ * sizes or dtypes. */
 size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk,
                            int32_t Hv, int32_t K, int32_t V, int32_t dtype);
 

@@ -326,3 +326,29 @@ def test_fused_and_split_agree(gdp, monkeypatch):
         check_all(inp, out[p], ref, TOL[w.dtype], what=p)
     assert rel_err(to_np(out["fused"][0]), to_np(out["split"][0])) <= TOL[w.dtype]
     assert rel_err(to_np(out["fused"][1]), to_np(out["split"][1])) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("N,Hqk,Hv", [(40, 4, 8), (90, 1, 3)], ids=["grouped-heads", "odd-grid"])
+def test_longest_first_order_every_chain(gdp, N, Hqk, Hv, monkeypatch):
+    """More chains than CUs with mixed lengths: the fused kernel runs its chains
+    longest sequence first.  Every head of every sequence (outputs, final states,
+    cache slots) matches the oracle, so the order visits each chain exactly once,
+    for a grid of whole q/k head groups (N*Hv = 320) and one that does not split
+    into 8 XCD lists (N*Hv = 270)."""
+    monkeypatch.delenv("GDP_PREFILL_PATH", raising=False)
+    gen = torch.Generator().manual_seed(N)
+    lens = torch.randint(0, 200, (N,), generator=gen).tolist()
+    w = workloads.custom(lens, 2, Hqk, Hv, 64, 64, dtype=torch.bfloat16, init_std=0.2, seed=41,
+                         state_cache_slots=N + 3)
+    inp = workloads.generate(w, "cpu")
+    ref = oracle_run(inp)
+    dev = to_device(inp)
+    cache0 = dev["state_cache"].clone()
+    o, fs = gdp.chunk_prefill(**dev)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    check_all(inp, (o, fs), ref, tol, what="ordered")
+    slots = inp["state_indices"].numpy()
+    assert rel_err(to_np(dev["state_cache"][slots]), ref["state_cache"][slots]) <= tol
+    untouched = sorted(set(range(N + 3)) - set(slots.tolist()))
+    assert torch.equal(dev["state_cache"][untouched], cache0[untouched])
