@@ -1088,7 +1088,7 @@ template <int K, int V> struct FusedSmem {
   float rawb[2][CH], rawg[2][CH];          // raw betas / decays
   float beta[3][CH], gdp[3][CH];           // masked betas, base-2 decay cumsum
   float rk[2][CH], c1[2][CH], wgt[2][CH];  // k-row rstd, 2^G rk (the X weights of R) and the state-update weights
-  float rawt[2][CH], gtok[2][CH], rq[2][CH], qfac[2][CH];  // rq and qfac carry the output scale
+  float rawt[2][CH], gtok[2][CH], rq[2][CH], qfac[2][CH];  // rq: q-row rstd; qfac carries the output scale
   float gkr[2][CH], rkg[2][CH];  // rkg = rk 2^(-Gt_tok(r)) (used when qsafe)
   int tokr[2][CH];
   int qsafe[2];                   // the token chunk's decay cumsum stays above -100 (base 2)
@@ -1205,7 +1205,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       const uint32_t lt = (uint32_t)((rt * LDT + 4 * (lr & 3)) * 2);  // T^T columns
       const uint32_t lp = (uint32_t)((lr * LDC + 4 * lg) * 2);        // P rows
       const uint32_t kt = off_of(sm.k[ks]), qt = off_of(sm.q[qs]);
-      const float *gtok = sm.gtok[qs], *qfac = sm.qfac[qs], *rqv = sm.rq[qs];
+      const float *gtok = sm.gtok[qs], *qfac = sm.qfac[qs];
       const float *rk = sm.rk[ts], *gkr = sm.gkr[ts];
       const int *tokr = sm.tokr[ts];
       // ---- phase A: X = K Sst (and at a token-chunk start O^T = Sst^T Q^T), scores, R
@@ -1228,6 +1228,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // lane (lg, lr) of tile pa holds Sc[r = 16 (rb0 + pa) + 4 lg + i][t = 16 tb + lr]
       // = k_r.q_t.  They reuse the k fragments of X = K Sst as the A operand.
       f32x4 Pacc[RBW];
+      // at a token-chunk start with the in-kernel norm: the sum of squares of q
+      // row 16 tb + lr over the 32 elements this lane reads
+      float qss = 0.f;
+      const bool qnorm = j == 0 && a.l2norm;
       // k (and q) fragments of reduction step s+1 are read while step s multiplies
       {
         // rolling single buffer: fragment a4 of step s+1 is read right after the
@@ -1259,8 +1263,16 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
               Pacc[a4 - rb0] = mma(kf[a4], qw[s & 1], s == 0 ? zero4() : Pacc[a4 - rb0]);
             if (s + 1 < KS) load_kf(s + 1, a4);
           }
+          if (qnorm) qss += seg_sumsq<bf16>(__builtin_bit_cast(uint4, qw[s & 1].v));
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      // q-row rstd of the wave's 16 tokens (the four lanes lg of a row hold a
+      // quarter each); the outputs of token chunk c take it when staged
+      if (qnorm) {
+        qss += __shfl_xor(qss, 16, 64);
+        qss += __shfl_xor(qss, 32, 64);
+        if (lg == 0) sm.rq[qs][16 * tb + lr] = frsq(qss + 1e-6f);
       }
       if (j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
         Frag<bf16> qf[2][4];
@@ -1284,7 +1296,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (j == 0) {  // O^T columns t times lam scale rq_t 2^Gt_t
+      if (j == 0) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const float f = lam * qfac[16 * a4 + lr];
@@ -1292,7 +1304,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           for (int b = 0; b < NB; ++b) O[b][a4] *= f;
         }
       }
-      // P[t][r] = scale rq_t rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r for tok(r) <= t, i.e. for
+      // P[t][r] = scale rk_r 2^(Gt_t - Gt_tok(r)) q_t.k_r for tok(r) <= t, i.e. for
       // r below n (t + 1) - 64 j; written to the P tile as rows t of contiguous r.
       // When the token chunk's decay cumsum stays above -100 the decay factor is
       // the product qfac_t rkg_r of per-token and per-row factors (both finite and
@@ -1315,7 +1327,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
           }
         } else {
-          const float gt = gtok[t], rq = rqv[t];
+          const float gt = gtok[t], rq = a.scale;
 #pragma unroll
           for (int pa = 0; pa < RBW; ++pa) {
             const int a4 = rb0 + pa, r0 = 16 * a4 + 4 * lg;
@@ -1456,16 +1468,23 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       }
       lam = lazy ? dl : 1.f;
       // outputs of token chunk c once its last expanded chunk is in: lane holds
-      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in rq).
+      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in qfac
+      // and P; the q-row rstd rq_t multiplies every term of row t and is applied here).
       // They are staged in bf16 in this chunk's v tile (unused after the R step)
       // and helper 3 stores whole rows from there in the next chunk.
       if ((j == n - 1 || e == nexp - 1) && a.o) {
         char *stg = sm.v[ts];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
+        for (int a4 = 0; a4 < 4; ++a4) {
+          if (a.l2norm) {
+            const float f = sm.rq[qs][16 * a4 + lr];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) O[b][a4] *= f;
+          }
 #pragma unroll
           for (int b = 0; b < NB; ++b)
             *(bf16x4 *)(stg + sw_off<VW>(16 * a4 + lr, 2 * (wcol + 16 * b + 4 * lg))) = bf4(O[b][a4]);
+        }
       }
       lds_barrier();
     }
@@ -1528,7 +1547,11 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     auto load_scalars = [&](int e) {  // raw beta and decay of each sub-row of chunk e
       const int64_t s0 = (int64_t)CH * e;
       const int r = min(hl, rows_of(e) - 1);
-      const int64_t tok = (s0 + r) / n;
+      // token of sub-row s0 + r: the 64-bit quotient of the chunk start once per
+      // wave, then a 32-bit one for the lane
+      const int64_t q0 = s0 / n;
+      const int r0 = (int)(s0 - q0 * n);
+      const int64_t tok = q0 + (int64_t)((uint32_t)(r0 + r) / (uint32_t)n);
       scalar_load(sm.rawb[e & 1], bg + (t0 * n + s0 + r) * a.b_st);
       scalar_load(sm.rawg[e & 1], gg + (t0 + tok) * a.g_st);
     };
@@ -1554,18 +1577,11 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       sm.gkr[e & 1][hl] = gk;
       sm.rkg[e & 1][hl] = sm.rk[e & 1][hl] * fexp2(-gk);  // overflow-free when qsafe
     };
-    auto finish_q = [&](int c) {  // after load_q(c) has landed: q-row rstd and token decay cumsum
+    auto finish_q = [&](int c) {  // after load_q(c) has landed: token decay cumsum of token chunk c
       const int sl = c & 1, ntok = toks_of(c);
-      float ss = 0.f;
-      if (a.l2norm) {
-#pragma unroll
-        for (int sg = 0; sg < KW / 16; ++sg) ss += seg_sumsq<bf16>(*(const uint4 *)(sm.q[sl] + sw_off<KW, 1>(hl, 16 * sg)));
-      }
-      const float rq = a.scale * (a.l2norm ? frsq(ss + 1e-6f) : 1.f);
       const float gt = wave_scan(hl < ntok ? sm.rawt[sl][hl] * LOG2E : 0.f);
-      sm.rq[sl][hl] = rq;
       sm.gtok[sl][hl] = gt;
-      sm.qfac[sl][hl] = rq * fexp2(gt);
+      sm.qfac[sl][hl] = a.scale * fexp2(gt);
       // the cumsum is non-increasing, so its last valid entry is its minimum
       const float gmin = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gt), ntok - 1));
       if (hl == 0) sm.qsafe[sl] = gmin > -100.f;
@@ -1718,19 +1734,23 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
       }
     };
-    // Work per helper and chunk e (WY stages for chunk e+1), before || after the
-    // mid-chunk barrier:
-    //   helper 0: masked betas and decay cumsum of chunk || row tables of chunk e+1;
-    //             e+1, q norms and token decay cumsum       then v rows of chunk e+1,
-    //             of token chunk c+1; then k rows and       q rows of token chunk c+2
-    //             betas/decays of chunk e+2
-    //   helper 1: merge stage                               || row block 3
-    //   helper 2: Gram tiles 0-4                            || row blocks 0, 1
-    //   helper 3: outputs of chunk e-1, Gram tiles 5-9      || row block 2
-    // Helper 0 issues every direct-to-LDS load and touches LDS only where none
-    // of its loads is in flight: the compiler makes any LDS access that follows
-    // such a load in the same wave wait for it, which would otherwise stall the
-    // WY stages on HBM latency.
+    // Work per helper and chunk e = (token chunk c, sub-chunk j) (WY stages for
+    // chunk e+1), before || after the mid-chunk barrier:
+    //   helper 0: k rows and betas/decays of chunk e+2   || v rows of chunk e+1,
+    //                                                       q rows of token chunk c+2
+    //   helper 1: merge stage                            || row block 3
+    //   helper 2: Gram tiles 0-4, masked betas and decay || row blocks 0, 1
+    //             cumsum of chunk e+1, and at j = n-1 the
+    //             q norms and token decay cumsum of token
+    //             chunk c+1
+    //   helper 3: outputs of chunk e-1, Gram tiles 5-9   || row block 2, row tables
+    //                                                       of chunk e+1
+    // Helper 0 issues every direct-to-LDS load and never touches LDS: the
+    // compiler makes any LDS access that follows such a load in the same wave
+    // wait for it, which would stall that wave on HBM latency.  The q rows of
+    // token chunk c+1 are issued at the end of token chunk c-1 and read at its
+    // sub-chunk n-1: for n >= 2 they are waited for only with the next chunk's
+    // loads.
     // Each helper runs its own loop (the same barrier sequence as the consumers:
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
@@ -1749,24 +1769,16 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         load_q(0, qoffs);
         if (ntc > 1) load_q(1, qoffs);
         wait_vm();
-        prep_scalars(0);
-        finish_q(0);
         lds_barrier();
         lds_barrier();
-        tables(0);
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
         const int c = e / n;
         const int j = e - c * n;
         asm volatile("" : "+v"(hl));
-        // phase A.  All that can be in flight are the q rows of token chunk c+1,
-        // issued one phase ago.
-        wait_vm();
-        if (e + 1 < nexp) prep_scalars(e + 1);
-        if (j == 0 && c + 1 < ntc) finish_q(c + 1);
-        // this wave touches LDS no more until the next phase A: the loads below
-        // never hold up an LDS access of its own
+        // phase A: k rows and scalars of chunk e+2 (the Gram stage reads them in
+        // chunk e+1)
         if (e + 2 < nexp) {
           load_k(e + 2, koffs);
           load_scalars(e + 2);
@@ -1775,17 +1787,14 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         // phase B.  The v tile of chunk e-1 (its outputs are stored) and, after
         // the last expanded chunk of token chunk c, its q tile are free: refill
         // them with chunk e+1 and token chunk c+2, then wait for everything but
-        // the q rows: the consumers read the v rows after the next barrier and
-        // the Gram stage the k rows of chunk e+2.
+        // the q rows when n >= 2 (they are read at the end of token chunk c+1; a
+        // later wait for newer loads covers them): the consumers read the v rows
+        // after the next barrier and the Gram stage the k rows of chunk e+2.
         const bool lq = j == n - 1 && c + 2 < ntc;
-        if (e + 1 < nexp) tables(e + 1);  // needs the k-row norms from the Gram stage
         if (e + 1 < nexp && !part1) load_v(e + 1, voffs);
-        if (lq) {
-          load_q(c + 2, qoffs);
-          wait_vm_keep<NLQ>();
-        } else {
-          wait_vm();
-        }
+        if (lq) load_q(c + 2, qoffs);
+        if (lq && n >= 2) wait_vm_keep<NLQ>();
+        else wait_vm();
         lds_barrier();
       }
     } else if (hw == 1) {
@@ -1804,6 +1813,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     } else if (hw == 2) {
       if (nexp > 0) {
         lds_barrier();
+        prep_scalars(0);
+        finish_q(0);
         gram(0, 0, 5, 3);
         lds_barrier();
         block(0, IC<0>{});
@@ -1811,7 +1822,16 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
-        if (e + 1 < nexp) gram(e + 1, 0, 5, 3);
+        const int c = e / n;
+        const int j = e - c * n;
+        asm volatile("" : "+v"(hl));
+        if (e + 1 < nexp) {
+          gram(e + 1, 0, 5, 3);
+          prep_scalars(e + 1);
+        }
+        // token chunk c+1: its q rows landed with the loads of a chunk before
+        // (n >= 2) or before the last barrier (n = 1)
+        if (j == n - 1 && c + 1 < ntc) finish_q(c + 1);
         lds_barrier();
         if (e + 1 < nexp) {
           block(e + 1, IC<0>{});
@@ -1825,13 +1845,18 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         gram(0, 5, 10, 4);
         lds_barrier();
         block(0, IC<2>{});
+        tables(0);
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
+        asm volatile("" : "+v"(hl));
         if (e >= 1 && e % n == 0 && a.o) store_o(e - 1);
         if (e + 1 < nexp) gram(e + 1, 5, 10, 4);
         lds_barrier();
-        if (e + 1 < nexp) block(e + 1, IC<2>{});
+        if (e + 1 < nexp) {
+          block(e + 1, IC<2>{});
+          tables(e + 1);  // needs the k-row norms from the Gram stage
+        }
         lds_barrier();
       }
       if (nexp > 0 && a.o) store_o(nexp - 1);
