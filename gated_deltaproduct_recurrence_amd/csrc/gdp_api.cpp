@@ -130,6 +130,9 @@ size_t seg_bytes(const SegPlan &p, int64_t N, int64_t Hv, int64_t K, int64_t V) 
 // fused kernel runs
 bool order_grid(int64_t N, int64_t Hv) { return N * Hv > 256 && N <= gdp::ORDER_MAX_SEQ; }
 size_t order_bytes(int64_t N, int64_t Hv) { return order_grid(N, Hv) ? align256((size_t)N * Hv * 4) : 0; }
+// the fused kernel's chunk progress per chain (pacing of state heads that share
+// a q/k head)
+size_t progress_bytes(int64_t N, int64_t Hv, int64_t Hqk) { return Hv > Hqk ? align256((size_t)N * Hv * 4) : 0; }
 
 int env_path() {
   // GDP_PREFILL_PATH=fused|split|segmented overrides the automatic kernel
@@ -159,14 +162,14 @@ int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t n, int64_t *nt_cap, in
 
 size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V,
                            int32_t dtype) {
-  (void)Hqk;
   int64_t ct, cd;
   if (Hv < 1 || (dtype != GDP_F32 && dtype != GDP_BF16)) return 0;
   if (gdp_descriptor_capacity(T, N, n, &ct, &cd) != GDP_OK) return 0;
   const size_t wy = align256(gdp::wy_buffer_bytes(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, cd, Hv));
   // the segmented path (forced or automatic) needs its own buffers instead of the WY matrices
   const SegPlan forced = seg_plan(T, N, Hv, K, V, dtype, gdp::PATH_SEGMENTED);
-  return std::max(wy, seg_bytes(forced, N, Hv, K, V)) + desc_bytes(N, ct, cd) + order_bytes(N, Hv);
+  return std::max(wy, seg_bytes(forced, N, Hv, K, V)) + desc_bytes(N, ct, cd) + order_bytes(N, Hv) +
+         progress_bytes(N, Hv, Hqk);
 }
 
 int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t n, int64_t T, const gdp_descriptors *out,
@@ -319,7 +322,8 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   if (path == gdp::PATH_SEGMENTED && !plan.use)
     return fail(GDP_EUNSUPPORTED, "the segmented path needs bf16 inputs with K == V in {64, 128}");
   const size_t wy_bytes = std::max(align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv)), seg_bytes(plan, N, Hv, K, V));
-  const size_t need = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap)) + order_bytes(N, Hv);
+  const size_t tail0 = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap));
+  const size_t need = tail0 + order_bytes(N, Hv) + progress_bytes(N, Hv, Hqk);
   if (!workspace || workspace_bytes < need)
     return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -411,8 +415,13 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
       return fail(GDP_EHIP, "segment prefill launch: %s", hipGetErrorString(e));
     return GDP_OK;
   }
-  if (order_grid(N, Hv) && gdp::fused_chosen(idt, N, Hv, path)) {  // at the end of the workspace
-    int32_t *order = (int32_t *)((char *)workspace + wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap)));
+  if (progress_bytes(N, Hv, Hqk) > 0 && gdp::fused_chosen(idt, N, Hv, path)) {  // after the work order
+    a.progress = (int32_t *)((char *)workspace + tail0 + order_bytes(N, Hv));
+    if ((e = gdp::launch_fill(a.progress, N * Hv, INT32_MAX, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "progress fill launch: %s", hipGetErrorString(e));
+  }
+  if (order_grid(N, Hv) && gdp::fused_chosen(idt, N, Hv, path)) {  // after the WY region and the descriptors
+    int32_t *order = (int32_t *)((char *)workspace + tail0);
     gdp::OrderArgs oa;
     oa.cu = cu_seqlens->data; oa.cu_is64 = a.cu_is64; oa.N = N; oa.T = T; oa.Hqk = (int)Hqk; oa.Hv = (int)Hv;
     oa.order = order;

@@ -1070,6 +1070,14 @@ template <int N> __device__ __forceinline__ void wait_vm_keep() {
 // direct-to-LDS loads feed the next phase waits for them itself before it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// pacing of the chains that share a q/k head (fused kernel): checked every
+// PACE_EVERY chunks, a chain may lead the others of its group by PACE_AHEAD
+// chunks, and a check polls at most PACE_SPIN times.  Measured on the
+// long-context workload (pairs of state heads per q/k head): without pacing
+// the pairs drift apart and HBM fetch grows from 15.3 to 17-20 GB per call;
+// with these values it stays at 15.3 GB at no measurable cost in time.
+constexpr int PACE_EVERY = 8, PACE_AHEAD = 4, PACE_SPIN = 500;
+
 template <int K, int V> struct FusedSmem {
   static constexpr int KW = 2 * K;        // bytes per k / q row
   static constexpr int VW = 2 * V;       // bytes per v row
@@ -1755,6 +1763,26 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
       constexpr int NLQ = KW / 16 + 1;  // loads per q tile and its token decays
+      // Pacing inside the group of state heads sharing q/k head hq (the group
+      // shares one sequence, hence one chunk count).  Every PACE_EVERY chunks,
+      // at the end of a chunk whose loads have all completed (the loader waits
+      // there for the consumers anyway), a chain publishes its chunk index and
+      // polls the others' counters until none is more than PACE_AHEAD chunks
+      // behind, at most PACE_SPIN times, so that no chain ever waits for good.
+      // The counters start at INT32_MAX (set before the launch): a chain that
+      // has not started yet is never waited for.
+      const int grp = a.Hv / a.Hqk, gi = h - hq * grp;
+      int32_t *prog = (a.progress && grp > 1 && !a.summary) ? a.progress + (size_t)seq * a.Hv + (size_t)hq * grp : nullptr;
+      auto pace = [&](int e) {
+        if (lane == 0) __hip_atomic_store(prog + gi, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < grp; ++i) {
+          if (i == gi) continue;
+          for (int it = 0; it < PACE_SPIN; ++it) {
+            if (__hip_atomic_load(prog + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= e - PACE_AHEAD) break;
+            __builtin_amdgcn_s_sleep(4);
+          }
+        }
+      };
       const TileOffs<KW, 1> koffs = tile_offs<KW, 1>(kst, lane), qoffs = tile_offs<KW, 1>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
       if (part1) {  // zero values: both v tiles stay zero (no outputs are staged in them)
@@ -1793,8 +1821,13 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         const bool lq = j == n - 1 && c + 2 < ntc;
         if (e + 1 < nexp && !part1) load_v(e + 1, voffs);
         if (lq) load_q(c + 2, qoffs);
-        if (lq && n >= 2) wait_vm_keep<NLQ>();
-        else wait_vm();
+        if (lq && n >= 2) {
+          wait_vm_keep<NLQ>();
+        } else {
+          wait_vm();
+          // nothing of this wave is in flight: the polls wait for themselves only
+          if (prog && e % PACE_EVERY == 0) pace(e);
+        }
         lds_barrier();
       }
     } else if (hw == 1) {

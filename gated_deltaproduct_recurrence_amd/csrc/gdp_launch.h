@@ -53,6 +53,11 @@ struct PrefillArgs {
   // fused kernel: chain run by workgroup b (longest sequences first, spread over
   // the XCDs), or null for the plain XCD-grouped order
   const int32_t *order;             // [N * Hv]
+  // fused kernel: chunk progress of every chain, or null.  The state heads of
+  // one q/k head read the same k/q rows; a chain more than a few chunks ahead of
+  // another of its group waits (bounded) so that the group shares those rows
+  // through its XCD's L2 instead of fetching them once per head.
+  int32_t *progress;                // [N * Hv]
 };
 
 // Longest-first order of the fused kernel's chains (one workgroup).
@@ -118,6 +123,7 @@ hipError_t launch_segments(const SegArgs &a, hipStream_t stream);
 // sequences the ordering kernel can rank (LDS-resident lengths)
 constexpr int64_t ORDER_MAX_SEQ = 4096;
 hipError_t launch_order(const OrderArgs &a, hipStream_t stream);
+hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);
 // launches the fused kernel regardless of the chain count (bf16 only)
 hipError_t launch_fused_prefill(const PrefillArgs &a, int K, int V, hipStream_t stream);

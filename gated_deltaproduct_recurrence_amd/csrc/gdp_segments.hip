@@ -234,6 +234,19 @@ hipError_t launch_segments(const SegArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// every entry of p[0 .. n) set to v (a kernel, not a memset, so that the call
+// stays safe to capture in a graph)
+__global__ void __launch_bounds__(256) gdp_fill_kernel(int32_t *p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(gdp_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_order(const OrderArgs &a, hipStream_t stream) {
   if (a.N < 1 || a.N > ORDER_MAX_SEQ) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gdp_order_kernel, dim3(1), dim3(1024), 0, stream, a);

@@ -106,8 +106,9 @@ int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t num_householder,
  * segment of at least 256 tokens an f32 K x K map and two K x V states per
  * head), whichever is larger; plus room for the descriptors when the caller
  * passes none; plus an int32 work order of N x Hv entries when N x Hv > 256 and
- * N <= 4096.  Hqk is accepted for forward compatibility.  Returns 0 for invalid
- * sizes or dtypes. */
+ * N <= 4096; plus an int32 chunk counter per (sequence, state head) when
+ * Hv > Hqk (the fused kernel paces the state heads that share a q/k head).
+ * Returns 0 for invalid sizes or dtypes. */
 size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk,
                            int32_t Hv, int32_t K, int32_t V, int32_t dtype);
 
