@@ -12,13 +12,14 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdp.so")
 
-GDP_F32, GDP_BF16, GDP_I32, GDP_I64 = 0, 1, 2, 3
+GDP_F32, GDP_BF16, GDP_I32, GDP_I64, GDP_F16 = 0, 1, 2, 3, 4
 GDP_OK, GDP_EINVAL, GDP_EUNSUPPORTED, GDP_EALIAS, GDP_EWORKSPACE, GDP_EHIP = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {GDP_EINVAL: "GDP_EINVAL", GDP_EUNSUPPORTED: "GDP_EUNSUPPORTED", GDP_EALIAS: "GDP_EALIAS",
                 GDP_EWORKSPACE: "GDP_EWORKSPACE", GDP_EHIP: "GDP_EHIP"}
 
 EXPORTED = ("gdp_descriptor_capacity", "gdp_build_descriptors", "gdp_workspace_bytes",
-            "gdp_chunk_prefill", "gdp_recurrent_decode", "gdp_last_error", "gdp_version")
+            "gdp_chunk_prefill", "gdp_recurrent_decode", "gdp_fi_workspace_bytes",
+            "gdp_chunk_gated_delta_product", "gdp_last_error", "gdp_version")
 
 
 class gdp_tensor(ctypes.Structure):
@@ -60,6 +61,14 @@ def _load(path=LIB_PATH):
     lib.gdp_recurrent_decode.restype = ctypes.c_int
     lib.gdp_recurrent_decode.argtypes = [T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, T, T, T,
                                          ctypes.c_void_p]
+    lib.gdp_fi_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdp_fi_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32]
+    lib.gdp_chunk_gated_delta_product.restype = ctypes.c_int
+    lib.gdp_chunk_gated_delta_product.argtypes = [T, T, T, T, T, ctypes.c_int32, ctypes.c_float, T,
+                                                  ctypes.c_int32, T, ctypes.c_int32, T, T, ctypes.c_void_p,
+                                                  ctypes.c_size_t, ctypes.c_void_p]
     lib.gdp_last_error.restype = ctypes.c_char_p
     lib.gdp_last_error.argtypes = []
     lib.gdp_version.restype = ctypes.c_char_p
@@ -69,7 +78,8 @@ def _load(path=LIB_PATH):
 
 LIB = _load()
 
-_DT = {torch.float32: GDP_F32, torch.bfloat16: GDP_BF16, torch.int32: GDP_I32, torch.int64: GDP_I64}
+_DT = {torch.float32: GDP_F32, torch.bfloat16: GDP_BF16, torch.int32: GDP_I32, torch.int64: GDP_I64,
+       torch.float16: GDP_F16}
 
 
 def as_gdp_tensor(t):
@@ -193,6 +203,29 @@ def gdp_recurrent_decode(q, k, v, g_log, beta, num_householder, scale, use_qk_l2
                                     ctypes.byref(ot), st))
 
 
+def gdp_fi_workspace_bytes(T, N, num_householder, Hq, Hv, head_size, dtype=torch.bfloat16,
+                           with_initial_state=False, output_final_state=False):
+    return int(LIB.gdp_fi_workspace_bytes(T, N, num_householder, Hq, Hv, head_size, _DT[dtype],
+                                          int(bool(with_initial_state)), int(bool(output_final_state))))
+
+
+def gdp_chunk_gated_delta_product(q, k, v, g, beta, num_householder, scale, initial_state, output_final_state,
+                                  cu_seqlens, use_qk_l2norm_in_kernel, output, output_state, workspace,
+                                  stream=None):
+    """Direct call of the FlashInfer-convention C entry point (caller-allocated
+    output, output_state and workspace)."""
+    ts = [as_gdp_tensor(x) for x in (q, k, v, g, beta)]
+    s0, cu = as_gdp_tensor(initial_state), as_gdp_tensor(cu_seqlens)
+    ot, st_out = as_gdp_tensor(output), as_gdp_tensor(output_state)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _stream(q.device) if stream is None else stream
+    _check(LIB.gdp_chunk_gated_delta_product(*[ctypes.byref(a) for a in ts], int(num_householder),
+                                             float(scale or 0.0), ctypes.byref(s0), int(bool(output_final_state)),
+                                             ctypes.byref(cu), int(bool(use_qk_l2norm_in_kernel)),
+                                             ctypes.byref(ot), ctypes.byref(st_out), ws_ptr, ws_bytes, st))
+
+
 # ---------------------------------------------------------------- convenience wrapper
 
 def chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None, initial_state=None,
@@ -242,3 +275,28 @@ def recurrent_decode(q, k, v, g_log, beta, num_householder, state_cache, state_i
     gdp_recurrent_decode(q, k, v, g_log, beta, num_householder, scale or 0.0, use_qk_l2norm, state_cache,
                          state_indices, o)
     return o
+
+
+def chunk_gated_delta_product(q, k, v, g=None, beta=None, num_householder=1, scale=None, initial_state=None,
+                              output_final_state=False, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
+                              output=None, output_state=None):
+    """Allocating front end in the FlashInfer convention (FlashInfer docs,
+    "flashinfer.gdp_prefill.chunk_gated_delta_product", parameter list): linear
+    decays g (None: no decay), beta (None: ones), V-major states.  Returns
+    output, or (output, final_state) when output_final_state."""
+    if cu_seqlens is None:
+        raise ValueError("cu_seqlens is required (varlen input only)")
+    T, Hq, d = q.shape
+    Hv = v.shape[1]
+    N = cu_seqlens.shape[0] - 1
+    dev = q.device
+    out = output if output is not None else torch.empty((T, Hv, d), dtype=q.dtype, device=dev)
+    fs = None
+    if output_final_state:
+        fs = output_state if output_state is not None else torch.empty(
+            (N, Hv, d, d), dtype=initial_state.dtype if initial_state is not None else torch.float32, device=dev)
+    ws = torch.empty(max(gdp_fi_workspace_bytes(T, N, num_householder, Hq, Hv, d, q.dtype, initial_state is not None,
+                                                output_final_state), 256), dtype=torch.uint8, device=dev)
+    gdp_chunk_gated_delta_product(q, k, v, g, beta, num_householder, scale, initial_state, output_final_state,
+                                  cu_seqlens, use_qk_l2norm_in_kernel, out, fs, ws)
+    return (out, fs) if output_final_state else out

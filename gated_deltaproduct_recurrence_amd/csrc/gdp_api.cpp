@@ -38,6 +38,7 @@ int elem_size(int32_t dt) {
     case GDP_BF16: return 2;
     case GDP_I32: return 4;
     case GDP_I64: return 8;
+    case GDP_F16: return 2;
     default: return 0;
   }
 }
@@ -151,6 +152,146 @@ extern "C" {
 
 const char *gdp_last_error(void) { return g_last_error.c_str(); }
 
+namespace {
+int el_type(int32_t dt) { return dt == GDP_F32 ? gdp::EL_F32 : (dt == GDP_BF16 ? gdp::EL_BF16 : gdp::EL_F16); }
+
+// Workspace of the FlashInfer-convention front end, in order: the gates in the
+// prefill kernels' form, the K-major initial and final states, then the
+// prefill's own workspace.
+struct FiLayout {
+  size_t glog = 0, beta = 0, s0 = 0, fin = 0, inner = 0, total = 0;
+};
+FiLayout fi_layout(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int32_t d, int32_t dtype,
+                   bool with_initial, bool with_final) {
+  FiLayout L;
+  const size_t st = align256((size_t)N * Hv * d * d * 4);
+  L.glog = 0;
+  L.beta = L.glog + align256((size_t)T * Hv * 4);
+  L.s0 = L.beta + align256((size_t)T * n * Hv * 4);
+  L.fin = L.s0 + (with_initial ? st : 0);
+  L.inner = L.fin + (with_final ? st : 0);
+  const size_t ws = gdp_workspace_bytes(T, N, n, Hq, Hv, d, d, dtype);
+  L.total = ws ? L.inner + ws : 0;
+  return L;
+}
+}  // namespace
+
+size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int32_t d, int32_t dtype,
+                              int32_t with_initial_state, int32_t output_final_state) {
+  if (T < 0 || N < 0 || n < 1 || Hq < 1 || Hv < 1 || d < 1) return 0;
+  if (dtype != GDP_BF16) return 0;
+  return fi_layout(T, N, n, Hq, Hv, d, dtype, with_initial_state != 0, output_final_state != 0).total;
+}
+
+int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                                  const gdp_tensor *g, const gdp_tensor *beta, int32_t n, float scale,
+                                  const gdp_tensor *initial_state, int32_t output_final_state,
+                                  const gdp_tensor *cu_seqlens, int32_t use_qk_l2norm_in_kernel,
+                                  const gdp_tensor *output, const gdp_tensor *output_state, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  if (!present(q) || !present(k) || !present(v) || !present(output))
+    return fail(GDP_EINVAL, "q, k, v and output are required");
+  if (!present(cu_seqlens)) return fail(GDP_EINVAL, "cu_seqlens is required (varlen input only)");
+  if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1, got %d", n);
+  if (q->ndim != 3 || k->ndim != 3 || v->ndim != 3 || cu_seqlens->ndim != 1)
+    return fail(GDP_EINVAL, "q, k, v must be 3-d and cu_seqlens 1-d");
+  const int64_t T = q->shape[0], Hq = q->shape[1], d = q->shape[2], Hv = v->shape[1];
+  const int64_t N = cu_seqlens->shape[0] - 1;
+  if (N < 0) return fail(GDP_EINVAL, "cu_seqlens must have N+1 >= 1 entries");
+  if (Hq < 1 || Hv < 1) return fail(GDP_EINVAL, "head counts must be positive");
+  if (Hq > Hv) return fail(GDP_EUNSUPPORTED, "more q heads than v heads is not served (Hq %lld, Hv %lld)",
+                           (long long)Hq, (long long)Hv);
+  if (v->shape[2] != d) return fail(GDP_EINVAL, "q, k and v share one head size");
+  if (q->dtype == GDP_F16) return fail(GDP_EUNSUPPORTED, "float16 q/k/v are not served yet (bfloat16 only)");
+  if (q->dtype != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q, k and v must be bfloat16");
+  if (d != 64 && d != 128) return fail(GDP_EUNSUPPORTED, "head size must be 64 or 128");
+  int rc;
+  const int64_t Hk = k->shape[1];
+  if (Hk != Hq && Hk != Hv) return fail(GDP_EINVAL, "k must have Hq or Hv heads, got %lld", (long long)Hk);
+  if (Hv % Hq != 0) return fail(GDP_EINVAL, "Hv (%lld) must be a multiple of Hq (%lld)", (long long)Hv, (long long)Hq);
+  if (k->dtype != q->dtype || v->dtype != q->dtype || output->dtype != q->dtype)
+    return fail(GDP_EUNSUPPORTED, "q, k, v and output must share one dtype");
+  const int64_t sk[3] = {T * n, Hk, d}, sv[3] = {T * n, Hv, d}, so[3] = {T, Hv, d};
+  if ((rc = check_shape(k, "k", 3, sk)) || (rc = check_shape(v, "v", 3, sv)) || (rc = check_shape(output, "output", 3, so)))
+    return rc;
+  const int64_t sg[2] = {T, Hv}, sb[2] = {T * n, Hv}, sst[4] = {N, Hv, d, d};
+  if (present(g)) {
+    if ((rc = check_shape(g, "g", 2, sg))) return rc;
+    if (g->dtype != GDP_F32 && g->dtype != GDP_BF16 && g->dtype != GDP_F16)
+      return fail(GDP_EUNSUPPORTED, "g must be float32, bfloat16 or float16");
+    if (!nonneg_strides(g)) return fail(GDP_EINVAL, "negative strides are not supported");
+  }
+  if (present(beta)) {
+    if ((rc = check_shape(beta, "beta", 2, sb))) return rc;
+    if (beta->dtype != GDP_F32 && beta->dtype != q->dtype) return fail(GDP_EUNSUPPORTED, "beta must be float32 or q's dtype");
+    if (!nonneg_strides(beta)) return fail(GDP_EINVAL, "negative strides are not supported");
+  }
+  if (present(initial_state)) {
+    if ((rc = check_shape(initial_state, "initial_state", 4, sst))) return rc;
+    if (!contiguous(initial_state)) return fail(GDP_EINVAL, "initial_state must be contiguous");
+    if (initial_state->dtype != GDP_F32 && initial_state->dtype != GDP_BF16)
+      return fail(GDP_EUNSUPPORTED, "initial_state must be float32 or bfloat16");
+  }
+  if (output_final_state) {
+    if (!present(output_state)) return fail(GDP_EINVAL, "output_state is required when output_final_state is set");
+    if ((rc = check_shape(output_state, "output_state", 4, sst))) return rc;
+    if (!contiguous(output_state)) return fail(GDP_EINVAL, "output_state must be contiguous");
+    if (output_state->dtype != GDP_F32 && output_state->dtype != GDP_BF16)
+      return fail(GDP_EUNSUPPORTED, "output_state must be float32 or bfloat16");
+    // the page's ownership rule (FlashInfer docs, output_state)
+    if (overlap(range_of(output_state, "output_state"), range_of(initial_state, "initial_state")))
+      return fail(GDP_EALIAS, "output_state overlaps initial_state");
+    for (const Range &ri : {range_of(q, "q"), range_of(k, "k"), range_of(v, "v"), range_of(g, "g"),
+                            range_of(beta, "beta"), range_of(cu_seqlens, "cu_seqlens"), range_of(output, "output")})
+      if (overlap(range_of(output_state, "output_state"), ri)) return fail(GDP_EALIAS, "output_state overlaps %s", ri.name);
+  }
+  const FiLayout L = fi_layout(T, N, n, (int32_t)Hq, (int32_t)Hv, (int32_t)d, q->dtype, present(initial_state),
+                               output_final_state != 0);
+  if (L.total == 0) return fail(GDP_EINVAL, "bad sizes");
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
+  char *ws = (char *)workspace;
+
+  hipError_t e;
+  gdp::GateArgs ga;
+  ga.alpha = present(g) ? g->data : nullptr;
+  ga.alpha_dtype = present(g) ? el_type(g->dtype) : 0;
+  ga.a_st = present(g) ? g->stride[0] : 0; ga.a_sh = present(g) ? g->stride[1] : 0;
+  ga.beta = present(beta) ? beta->data : nullptr;
+  ga.beta_dtype = present(beta) ? el_type(beta->dtype) : 0;
+  ga.b_st = present(beta) ? beta->stride[0] : 0; ga.b_sh = present(beta) ? beta->stride[1] : 0;
+  ga.T = T; ga.n = n; ga.Hv = (int)Hv;
+  ga.g_log = (float *)(ws + L.glog); ga.beta32 = (float *)(ws + L.beta);
+  if ((e = gdp::launch_gates(ga, (hipStream_t)stream)) != hipSuccess)
+    return fail(GDP_EHIP, "gate launch: %s", hipGetErrorString(e));
+  if (present(initial_state)) {
+    gdp::StateArgs sa;
+    sa.src = initial_state->data; sa.dst = ws + L.s0; sa.mats = N * Hv; sa.K = (int)d; sa.V = (int)d;
+    sa.state_dtype = el_type(initial_state->dtype);
+    if ((e = gdp::launch_state_transpose(sa, true, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "state launch: %s", hipGetErrorString(e));
+  }
+  // the prefill in the Megatron Core convention on the restated operands
+  gdp_tensor tg{ws + L.glog, GDP_F32, 2, {T, Hv}, {Hv, 1}};
+  gdp_tensor tb{ws + L.beta, GDP_F32, 2, {T * n, Hv}, {Hv, 1}};
+  gdp_tensor ts0{present(initial_state) ? ws + L.s0 : nullptr, GDP_F32, 4, {N, Hv, d, d}, {Hv * d * d, d * d, d, 1}};
+  gdp_tensor tfin{output_final_state ? ws + L.fin : nullptr, GDP_F32, 4, {N, Hv, d, d}, {Hv * d * d, d * d, d, 1}};
+  if ((rc = gdp_chunk_prefill(q, k, v, &tg, &tb, n, cu_seqlens, scale, &ts0, output_final_state,
+                              use_qk_l2norm_in_kernel, nullptr, nullptr, 0, output, &tfin, nullptr, nullptr,
+                              ws + L.inner, workspace_bytes - L.inner, stream)) != GDP_OK)
+    return rc;
+  if (output_final_state) {
+    gdp::StateArgs sa;
+    sa.src = ws + L.fin; sa.dst = output_state->data; sa.mats = N * Hv; sa.K = (int)d; sa.V = (int)d;
+    sa.state_dtype = el_type(output_state->dtype);
+    if ((e = gdp::launch_state_transpose(sa, false, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "state launch: %s", hipGetErrorString(e));
+  }
+  return GDP_OK;
+}
+
 const char *gdp_version(void) { return "gdp-mi355x 0.1.0 (gfx950)"; }
 
 int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t n, int64_t *nt_cap, int64_t *ntdp_cap) {
@@ -216,9 +357,10 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   if (!present(cu_seqlens)) return fail(GDP_EINVAL, "cu_seqlens is required (varlen input only)");
   if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1, got %d", n);
   if (q->ndim != 3) return fail(GDP_EINVAL, "q must be [T, Hqk, K]");
+  if (k->ndim != 3) return fail(GDP_EINVAL, "k must be [T*n, Hk, K]");
   if (v->ndim != 3) return fail(GDP_EINVAL, "v must be [T*n, Hv, V]");
   const int64_t T = q->shape[0], Hqk = q->shape[1], K = q->shape[2];
-  const int64_t Hv = v->shape[1], V = v->shape[2];
+  const int64_t Hv = v->shape[1], V = v->shape[2], Hk = k->shape[1];
   if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1 || cu_seqlens->stride[0] != 1)
     return fail(GDP_EINVAL, "cu_seqlens must be a contiguous [N+1] vector");
   if (cu_seqlens->dtype != GDP_I32 && cu_seqlens->dtype != GDP_I64)
@@ -226,6 +368,7 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   const int64_t N = cu_seqlens->shape[0] - 1;
   if (Hqk < 1 || Hv < 1 || K < 1 || V < 1) return fail(GDP_EINVAL, "head counts and dims must be positive");
   if (Hv % Hqk != 0) return fail(GDP_EINVAL, "Hv (%lld) must be a multiple of Hqk (%lld)", (long long)Hv, (long long)Hqk);
+  if (Hk != Hqk && Hk != Hv) return fail(GDP_EINVAL, "k must have Hqk or Hv heads, got %lld", (long long)Hk);
   if (N > INT32_MAX || Hv > 65535) return fail(GDP_EINVAL, "too many sequences or heads");
 
   const int32_t dt = q->dtype;
@@ -236,7 +379,7 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
     return fail(GDP_EUNSUPPORTED, "g_log and beta must be float32");
 
   int rc;
-  const int64_t sq[3] = {T, Hqk, K}, sk[3] = {T * n, Hqk, K}, sv[3] = {T * n, Hv, V};
+  const int64_t sq[3] = {T, Hqk, K}, sk[3] = {T * n, Hk, K}, sv[3] = {T * n, Hv, V};
   const int64_t sg[2] = {T, Hv}, sb[2] = {T * n, Hv}, so[3] = {T, Hv, V};
   if ((rc = check_shape(q, "q", 3, sq)) || (rc = check_shape(k, "k", 3, sk)) || (rc = check_shape(v, "v", 3, sv)) ||
       (rc = check_shape(g_log, "g_log", 2, sg)) || (rc = check_shape(beta, "beta", 2, sb)) ||
@@ -357,7 +500,7 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   a.g = (const float *)g_log->data; a.g_st = g_log->stride[0]; a.g_sh = g_log->stride[1];
   a.beta = (const float *)beta->data; a.b_st = beta->stride[0]; a.b_sh = beta->stride[1];
   a.cu = cu_seqlens->data; a.cu_is64 = cu_seqlens->dtype == GDP_I64;
-  a.T = T; a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv;
+  a.T = T; a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv; a.Hk = (int)Hk;
   a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
   a.l2norm = use_qk_l2norm ? 1 : 0;
   a.s0 = present(initial_state) ? (const float *)initial_state->data : nullptr;
@@ -444,11 +587,13 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
   if (!present(state_cache) || !present(state_indices))
     return fail(GDP_EINVAL, "state_cache and state_indices are required");
   if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1, got %d", n);
-  if (q->ndim != 3 || v->ndim != 3) return fail(GDP_EINVAL, "q must be [N, Hqk, K] and v [N*n, Hv, V]");
+  if (q->ndim != 3 || k->ndim != 3 || v->ndim != 3)
+    return fail(GDP_EINVAL, "q must be [N, Hqk, K], k [N*n, Hk, K] and v [N*n, Hv, V]");
   const int64_t N = q->shape[0], Hqk = q->shape[1], K = q->shape[2];
-  const int64_t Hv = v->shape[1], V = v->shape[2];
+  const int64_t Hv = v->shape[1], V = v->shape[2], Hk = k->shape[1];
   if (Hqk < 1 || Hv < 1 || K < 1 || V < 1) return fail(GDP_EINVAL, "head counts and dims must be positive");
   if (Hv % Hqk != 0) return fail(GDP_EINVAL, "Hv (%lld) must be a multiple of Hqk (%lld)", (long long)Hv, (long long)Hqk);
+  if (Hk != Hqk && Hk != Hv) return fail(GDP_EINVAL, "k must have Hqk or Hv heads, got %lld", (long long)Hk);
   if (N > INT32_MAX || Hv > 65535) return fail(GDP_EINVAL, "too many sequences or heads");
   const int32_t dt = q->dtype;
   if (dt != GDP_F32 && dt != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q must be float32 or bfloat16");
@@ -459,7 +604,7 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
   if (state_indices->dtype != GDP_I32 && state_indices->dtype != GDP_I64)
     return fail(GDP_EINVAL, "state_indices must be int32 or int64");
   int rc;
-  const int64_t sq[3] = {N, Hqk, K}, sk[3] = {N * n, Hqk, K}, sv[3] = {N * n, Hv, V};
+  const int64_t sq[3] = {N, Hqk, K}, sk[3] = {N * n, Hk, K}, sv[3] = {N * n, Hv, V};
   const int64_t sg[2] = {N, Hv}, sb[2] = {N * n, Hv}, so[3] = {N, Hv, V}, si[1] = {N};
   const int64_t sc[4] = {-1, Hv, K, V};
   if ((rc = check_shape(q, "q", 3, sq)) || (rc = check_shape(k, "k", 3, sk)) || (rc = check_shape(v, "v", 3, sv)) ||
@@ -488,7 +633,7 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
   a.v = v->data; a.v_st = v->stride[0]; a.v_sh = v->stride[1];
   a.g = (const float *)g_log->data; a.g_st = g_log->stride[0]; a.g_sh = g_log->stride[1];
   a.beta = (const float *)beta->data; a.b_st = beta->stride[0]; a.b_sh = beta->stride[1];
-  a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv;
+  a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv; a.Hk = (int)Hk;
   a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
   a.l2norm = use_qk_l2norm ? 1 : 0;
   a.cache = (float *)state_cache->data;

@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(256) gdp_decode_kernel(DecodeArgs a) {
   const int vt = (int)(bid % NVT);
   const int h = (int)((bid / NVT) % a.Hv);
   const int64_t i = bid / ((int64_t)NVT * a.Hv);
-  const int hq = h / (a.Hv / a.Hqk);
+  const int hq = h / (a.Hv / a.Hqk), hk = h / (a.Hv / a.Hk);
   const int col = vt * 64 + lane;
   T *orow = (T *)a.o + i * a.o_st + (int64_t)h * a.o_sh;
   const int64_t slot = index_at(a.slots, a.slots_is64, i);
@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) gdp_decode_kernel(DecodeArgs a) {
   __shared__ float red[2][4][64];
   for (int j = 0; j < a.n; ++j) {
     const int64_t row = i * a.n + j;
-    const T *kr = (const T *)a.k + row * a.k_st + (int64_t)hq * a.k_sh;
+    const T *kr = (const T *)a.k + row * a.k_st + (int64_t)hk * a.k_sh;
     const float rk = a.l2norm ? row_rstd<T, K>(kr, lane) : 1.f;
     float kap[RW];
 #pragma unroll

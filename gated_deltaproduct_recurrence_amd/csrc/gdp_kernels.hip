@@ -306,8 +306,8 @@ __global__ void __launch_bounds__(NTHR) gdp_wy_kernel(PrefillArgs a) {
   __shared__ S sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
 
-  const int64_t p = blockIdx.x / a.Hqk;
-  const int hq = (int)(blockIdx.x % a.Hqk);
+  const int64_t p = blockIdx.x / a.Hk;
+  const int hk = (int)(blockIdx.x % a.Hk);  // k head; its state heads share the Gram tiles
   if (p >= a.ntdp_rows || p >= a.tws_rows) return;
   const int seq = a.chunk_indices_dp[2 * p], cc = a.chunk_indices_dp[2 * p + 1];
   if (seq < 0 || seq >= a.N || cc < 0) return;  // padding row
@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(NTHR) gdp_wy_kernel(PrefillArgs a) {
   const int nrow = (int)((nsub - s0) < CH ? (nsub - s0) : CH);
   const int64_t row0 = t0 * n + s0;  // first sub-token row of the chunk
 
-  load_rows<T, K, LDK>(sm.u.k, (const T *)a.k + hq * a.k_sh + row0 * a.k_st, a.k_st, nrow, tid);
+  load_rows<T, K, LDK>(sm.u.k, (const T *)a.k + hk * a.k_sh + row0 * a.k_st, a.k_st, nrow, tid);
   __syncthreads();
   if (a.l2norm) rows_rstd<T, K>(sm.u.k, LDK, sm.rk, tid);
   else if (tid < CH) sm.rk[tid] = 1.f;
@@ -345,9 +345,9 @@ __global__ void __launch_bounds__(NTHR) gdp_wy_kernel(PrefillArgs a) {
   }
   __syncthreads();  // k rows are dead; sm.u.tf reuses them
 
-  const int grp = a.Hv / a.Hqk;
+  const int grp = a.Hv / a.Hk;
   for (int hh = 0; hh < grp; ++hh) {
-    const int h = hq * grp + hh;
+    const int h = hk * grp + hh;
     if (w == 0) {
       const int r = lane;
       const int64_t s = s0 + r;
@@ -457,7 +457,7 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
   const int vt = (int)(chain % NVT);
   const int h = (int)((chain / NVT) % a.Hv);
   const int seq = (int)(chain / ((int64_t)NVT * a.Hv));
-  const int hq = h / (a.Hv / a.Hqk);
+  const int hq = h / (a.Hv / a.Hqk), hk = h / (a.Hv / a.Hk);
   const int n = a.n;
 
   int64_t t0 = load_index(a.cu, a.cu_is64, seq), t1 = load_index(a.cu, a.cu_is64, seq + 1);
@@ -469,7 +469,7 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
   const int gcol = vt * BV + wcol;  // ... and inside the head
 
   const T *qg = (const T *)a.q + hq * a.q_sh;
-  const T *kg = (const T *)a.k + hq * a.k_sh;
+  const T *kg = (const T *)a.k + hk * a.k_sh;
   const T *vg = (const T *)a.v + h * a.v_sh + vt * BV;
   const float *gg = a.g + h * a.g_sh;
   const float *bg = a.beta + h * a.b_sh;
@@ -1130,7 +1130,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   const int vt = (int)(chain % NVT);
   const int h = (int)((chain / NVT) % a.Hv);
   const int seq = (int)(chain / ((int64_t)NVT * a.Hv));
-  const int hq = h / (a.Hv / a.Hqk);
+  const int hq = h / (a.Hv / a.Hqk), hk = h / (a.Hv / a.Hk);
   const int n = a.n;
 
   int64_t t0 = load_index(a.cu, a.cu_is64, seq), t1 = load_index(a.cu, a.cu_is64, seq + 1);
@@ -1532,7 +1532,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // The loads are spread over the four helpers as well.
     const int hw = w - NCW;
     const bf16 *qg = (const bf16 *)a.q + hq * a.q_sh;
-    const bf16 *kg = (const bf16 *)a.k + hq * a.k_sh;
+    const bf16 *kg = (const bf16 *)a.k + hk * a.k_sh;
     const bf16 *vg = (const bf16 *)a.v + h * a.v_sh + vt * BV;
     const float *gg = a.g + h * a.g_sh;
     const float *bg = a.beta + h * a.b_sh;
@@ -1996,7 +1996,7 @@ hipError_t launch_scan(const PrefillArgs &a, hipStream_t stream) {
 
 template <typename T, int K, int V>
 hipError_t launch_split(const PrefillArgs &a, hipStream_t stream) {
-  const int64_t wy_blocks = a.ntdp_rows * a.Hqk;
+  const int64_t wy_blocks = a.ntdp_rows * a.Hk;
   if (wy_blocks > 0) {
     hipLaunchKernelGGL((gdp_wy_kernel<T, K>), dim3((unsigned)wy_blocks), dim3(NTHR), 0, stream, a);
     hipError_t e = hipGetLastError();

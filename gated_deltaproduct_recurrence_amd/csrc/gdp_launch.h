@@ -28,6 +28,7 @@ struct PrefillArgs {
   const void *cu; int cu_is64;
   int64_t T;
   int N, n, Hqk, Hv;
+  int Hk;                // k heads: Hqk or Hv (state head h reads k head h / (Hv / Hk))
   float scale;
   int l2norm;
   const float *s0;       // [N, Hv, K, V] or null
@@ -73,11 +74,12 @@ enum InDtype { IN_F32 = 0, IN_BF16 = 1 };
 // Arguments of the single-token decode step (strides in elements).
 struct DecodeArgs {
   const void *q; int64_t q_st, q_sh;      // [N, Hqk, K]
-  const void *k; int64_t k_st, k_sh;      // [N*n, Hqk, K]
+  const void *k; int64_t k_st, k_sh;      // [N*n, Hk, K]
   const void *v; int64_t v_st, v_sh;      // [N*n, Hv, V]
   const float *g; int64_t g_st, g_sh;     // [N, Hv]
   const float *beta; int64_t b_st, b_sh;  // [N*n, Hv]
   int N, n, Hqk, Hv;
+  int Hk;                                 // k heads: Hqk or Hv
   float scale;
   int l2norm;
   float *cache; int64_t num_slots;        // [num_slots, Hv, K, V], read and written in place
@@ -123,6 +125,29 @@ hipError_t launch_segments(const SegArgs &a, hipStream_t stream);
 // sequences the ordering kernel can rank (LDS-resident lengths)
 constexpr int64_t ORDER_MAX_SEQ = 4096;
 hipError_t launch_order(const OrderArgs &a, hipStream_t stream);
+
+// Element types of the front end's conversion kernels.
+enum ElType { EL_F32 = 0, EL_BF16 = 1, EL_F16 = 2 };
+
+// Gates in the prefill kernels' form: g_log [T, Hv] = ln(alpha) (0 without
+// alpha), beta32 [T*n, Hv] (1 without beta); both contiguous float32.
+struct GateArgs {
+  const void *alpha; int alpha_dtype; int64_t a_st, a_sh;  // [T, Hv] or null
+  const void *beta; int beta_dtype; int64_t b_st, b_sh;    // [T*n, Hv] or null
+  int64_t T; int n, Hv;
+  float *g_log, *beta32;
+};
+hipError_t launch_gates(const GateArgs &a, hipStream_t stream);
+
+// State layout change of `mats` contiguous K x V states: V-major (state_dtype)
+// to K-major float32, or K-major float32 to V-major (state_dtype).  K and V
+// multiples of 64.
+struct StateArgs {
+  const void *src; void *dst;
+  int64_t mats; int K, V;
+  int state_dtype;
+};
+hipError_t launch_state_transpose(const StateArgs &a, bool to_k_major, hipStream_t stream);
 hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);
 // launches the fused kernel regardless of the chain count (bf16 only)

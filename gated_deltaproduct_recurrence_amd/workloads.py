@@ -149,3 +149,33 @@ def decode_batch(N, n, Hqk, Hv, K, V, slots, pad=0, dtype=torch.bfloat16, l2norm
     cache = cache_std * randn(slots, Hv, K, V)
     return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), g_log=g, beta=beta, num_householder=n,
                 state_cache=cache, state_indices=idx, use_qk_l2norm=l2norm_in_kernel)
+
+
+def flashinfer_batch(lens, n, Hq, Hk, Hv, d, dtype=torch.bfloat16, l2norm_in_kernel=False, g_shift=0.0,
+                     g_dtype=torch.float32, beta_dtype=torch.float32, init_std=0.0, state_dtype=torch.float32,
+                     seed=17, device="cpu"):
+    """Inputs in the FlashInfer convention: q [T, Hq, d], k [T*n, Hk, d],
+    v [T*n, Hv, d], g = alpha = exp(-softplus(N(0,1) - shift)) in (0, 1)
+    (g_dtype None: absent), beta = sigmoid(N(0,1)) (beta_dtype None: absent),
+    V-major initial states ~ N(0, init_std^2) (init_std 0: absent).  Same
+    distributions as the prefill workloads."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    cu = torch.tensor([0] + list(torch.tensor(list(lens)).cumsum(0).tolist()), dtype=torch.int32, device=dev)
+    T, N = int(sum(lens)), len(lens)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    q = randn(T, Hq, d)
+    k = randn(T * n, Hk, d)
+    if not l2norm_in_kernel:
+        q = _unit_rows(q)
+        k = _unit_rows(k)
+    v = randn(T * n, Hv, d)
+    alpha = torch.exp(-torch.nn.functional.softplus(randn(T, Hv) - g_shift))
+    beta = torch.sigmoid(randn(T * n, Hv))
+    s0 = init_std * randn(N, Hv, d, d) if init_std > 0 else None
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), g=None if g_dtype is None else alpha.to(g_dtype),
+                beta=None if beta_dtype is None else beta.to(beta_dtype), num_householder=n, cu_seqlens=cu,
+                initial_state=None if s0 is None else s0.to(state_dtype), use_qk_l2norm_in_kernel=l2norm_in_kernel)

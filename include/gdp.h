@@ -40,7 +40,7 @@ extern "C" {
 #endif
 
 /* Element types of gdp_tensor. */
-enum gdp_dtype { GDP_F32 = 0, GDP_BF16 = 1, GDP_I32 = 2, GDP_I64 = 3 };
+enum gdp_dtype { GDP_F32 = 0, GDP_BF16 = 1, GDP_I32 = 2, GDP_I64 = 3, GDP_F16 = 4 };
 
 /* Return codes. */
 enum gdp_status {
@@ -117,7 +117,11 @@ size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_
  * Inputs (T real tokens, N sequences, n = num_householder, Hqk q/k heads,
  * Hv state heads = v/g/beta/output heads, head dims K and V):
  *   q            [T, Hqk, K]      bf16 or f32; rows may be strided
- *   k            [T*n, Hqk, K]    same dtype as q; rows t*n..t*n+n-1 belong to token t
+ *   k            [T*n, Hk, K]     same dtype as q; rows t*n..t*n+n-1 belong to token t;
+ *                                 Hk = Hqk, or Hk = Hv (one k head per state head;
+ *                                 FlashInfer page, k: num_k_heads equals the q or the
+ *                                 v head count).  State head h reads q head
+ *                                 h / (Hv / Hqk) and k head h / (Hv / Hk)
  *   v            [T*n, Hv, V]     same dtype as q
  *   g_log        [T, Hv]          f32 log decays (alpha_t = exp(g_log_t))
  *   beta         [T*n, Hv]        f32
@@ -175,7 +179,8 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
  *     o[i, h] = scale * S^T q[i];  state_cache[slot, h] = S.
  * Entries whose index is negative (padding, -1) or past the cache get a zero
  * output row and leave the cache untouched.
- *   q [N, Hqk, K], k [N*n, Hqk, K], v [N*n, Hv, V]   bf16 or f32 (one dtype); rows may be strided
+ *   q [N, Hqk, K], k [N*n, Hk, K], v [N*n, Hv, V]    bf16 or f32 (one dtype); rows may be strided;
+ *                                                    Hk = Hqk or Hv, as for gdp_chunk_prefill
  *   g_log [N, Hv], beta [N*n, Hv]                    f32 (log decays; alpha = exp(g_log))
  *   scale                                            0 means K^-1/2
  *   use_qk_l2norm                                    as for gdp_chunk_prefill
@@ -190,6 +195,49 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
                          const gdp_tensor *g_log, const gdp_tensor *beta, int32_t num_householder,
                          float scale, int32_t use_qk_l2norm, const gdp_tensor *state_cache,
                          const gdp_tensor *state_indices, const gdp_tensor *o, void *stream);
+
+/* Host-only.  Workspace bytes gdp_chunk_gated_delta_product needs: the gates
+ * restated as float32 log decays and betas (4 (1 + n) T Hv bytes), a float32
+ * K-major copy of each state it converts (4 N Hv d^2 bytes each, when an
+ * initial state is given and when the final state is requested), and the
+ * workspace of the prefill it runs (gdp_workspace_bytes).  dtype is q's
+ * (GDP_BF16).  Returns 0 for invalid sizes or dtypes. */
+size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hq, int32_t Hv,
+                              int32_t head_size, int32_t dtype, int32_t with_initial_state,
+                              int32_t output_final_state);
+
+/* Device.  The chunked GDP prefill in the FlashInfer convention (FlashInfer docs,
+ * "flashinfer.gdp_prefill.chunk_gated_delta_product": its recurrence display and
+ * parameter list, in the same order, with workspace and stream appended).
+ * It computes what gdp_chunk_prefill computes; only the operands are stated
+ * differently:
+ *   q  [T, Hq, d], k [T*n, Hk, d] (Hk = Hq or Hv), v [T*n, Hv, d]   bfloat16, rows may
+ *                  be strided; Hv a multiple of Hq (more q than v heads is
+ *                  GDP_EUNSUPPORTED), d in {64, 128}
+ *   g    [T, Hv]   the decay alpha itself (in (0, 1]), float32, bfloat16 or float16,
+ *                  or data == NULL for no decay (alpha = 1)
+ *   beta [T*n, Hv] float32 or q's dtype, or data == NULL for all ones
+ *   scale          0 means d^-1/2
+ *   initial_state  [N, Hv, d, d] V-major (entry [v][k]), float32 or bfloat16,
+ *                  contiguous, or data == NULL for zero states
+ *   output_final_state  write output_state when nonzero
+ *   cu_seqlens     [N+1] int32 or int64, required
+ *   use_qk_l2norm_in_kernel   as gdp_chunk_prefill's use_qk_l2norm
+ *   output         [T, Hv, d] q's dtype, written
+ *   output_state   [N, Hv, d, d] V-major, float32 or bfloat16, contiguous; required
+ *                  iff output_final_state; it may not overlap initial_state or any
+ *                  input (GDP_EALIAS; FlashInfer page, output_state)
+ *   workspace      device scratch of at least gdp_fi_workspace_bytes(...), 256-byte
+ *                  aligned
+ * Everything runs on `stream` (conversion kernels, then the prefill), with no
+ * host read of device memory and no allocation, so the call is capturable.
+ * float16 q/k/v are GDP_EUNSUPPORTED in this version. */
+int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                                  const gdp_tensor *g, const gdp_tensor *beta, int32_t num_householder,
+                                  float scale, const gdp_tensor *initial_state, int32_t output_final_state,
+                                  const gdp_tensor *cu_seqlens, int32_t use_qk_l2norm_in_kernel,
+                                  const gdp_tensor *output, const gdp_tensor *output_state, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *gdp_last_error(void);

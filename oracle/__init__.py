@@ -196,3 +196,36 @@ def decode(q, k, v, g_log, beta, num_householder, state_cache, state_indices, sc
         o[sel] = res["o"]
         cache[slots[sel]] = res["final_state"]
     return {"o": o, "state_cache": cache}
+
+
+def prefill_flashinfer(q, k, v, g=None, beta=None, num_householder=1, scale=None, initial_state=None,
+                       output_final_state=False, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
+                       threads=None, lib=None):
+    """The prefill in the FlashInfer convention (FlashInfer docs,
+    "flashinfer.gdp_prefill.chunk_gated_delta_product": recurrence display and
+    parameter list), restated for the token loop above:
+      - g is the decay alpha itself; the loop multiplies S by exp(g_log), so
+        g_log = ln(alpha); g None means alpha = 1 (g_log = 0);
+      - beta None means all ones;
+      - k may carry one head per q head or one per v (state) head; with
+        Hk = Hv != Hq the loop, which reads q and k through one head index, gets
+        q with each head repeated for the Hv / Hq state heads that read it;
+      - states are V-major [N, H, V, K] (entry [v][k] = S[k][v] of the loop).
+    Shapes: q [T, Hq, d], k [T*n, Hk, d], v [T*n, Hv, d], g [T, Hv],
+    beta [T*n, Hv], initial_state [N, Hv, d, d].  Returns {"o", "final_state"}
+    with final_state V-major (None unless output_final_state)."""
+    n = int(num_householder)
+    q = _f64(q); k = _f64(k); v = _f64(v)
+    T, Hq, d = q.shape
+    Hk, Hv = k.shape[1], v.shape[1]
+    if Hk not in (Hq, Hv) or Hv % Hq != 0:
+        raise ValueError("k must have Hq or Hv heads, and Hv must be a multiple of Hq")
+    if Hk == Hv and Hq != Hv:
+        q = np.repeat(q, Hv // Hq, axis=1)
+    g_log = np.zeros((T, Hv)) if g is None else np.log(_f64(g))
+    b = np.ones((T * n, Hv)) if beta is None else _f64(beta)
+    s0 = None if initial_state is None else np.ascontiguousarray(np.swapaxes(_f64(initial_state), 2, 3))
+    res = prefill(q, k, v, g_log, b, n, cu_seqlens, scale=scale, initial_state=s0,
+                  use_qk_l2norm=use_qk_l2norm_in_kernel, threads=threads, lib=lib)
+    fin = np.ascontiguousarray(np.swapaxes(res["final_state"], 2, 3)) if output_final_state else None
+    return {"o": res["o"], "final_state": fin}

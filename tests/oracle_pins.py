@@ -434,3 +434,61 @@ def pin_decode_steps_equal_prefill(lib):
     _close(cur[untouched], cache[untouched], what="untouched slots")
 
 ALL_PINS += [pin_decode_brute_force, pin_decode_steps_equal_prefill]
+
+
+def flashinfer_literal(q, k, v, alpha, beta, n, cu, scale=None, init=None, l2norm=False):
+    """The FlashInfer recurrence display taken literally, per (sequence, head), on a
+    V-major state S [V, K]: S *= alpha_t; for each j, v_new = beta (v - S k),
+    S += v_new (x) k; o_t = scale S q_t.  k has Hq or Hv heads; alpha/beta None
+    mean ones."""
+    T, Hq, d = q.shape
+    Hk, Hv = k.shape[1], v.shape[1]
+    sc = 1.0 / np.sqrt(d) if not scale else scale
+    o = np.zeros((T, Hv, d))
+    fin = np.zeros((len(cu) - 1, Hv, d, d))
+    for i in range(len(cu) - 1):
+        for h in range(Hv):
+            hq, hk = h // (Hv // Hq), h // (Hv // Hk)
+            S = np.zeros((d, d)) if init is None else init[i, h].copy()
+            for t in range(cu[i], cu[i + 1]):
+                S = (1.0 if alpha is None else alpha[t, h]) * S
+                for j in range(n):
+                    kv = k[t * n + j, hk].copy()
+                    if l2norm:
+                        kv = kv / np.sqrt(kv @ kv + 1e-6)
+                    b = 1.0 if beta is None else beta[t * n + j, h]
+                    vnew = b * (v[t * n + j, h] - S @ kv)
+                    S = S + np.outer(vnew, kv)
+                qt = q[t, hq].copy()
+                if l2norm:
+                    qt = qt / np.sqrt(qt @ qt + 1e-6)
+                o[t, h] = sc * (S @ qt)
+            fin[i, h] = S
+    return o, fin
+
+
+def pin_flashinfer_literal(lib):
+    """The FlashInfer-convention front end (linear alpha, V-major states, None
+    gates, k with one head per state head) against the page's recurrence display
+    written out literally."""
+    rng = np.random.default_rng(23)
+    cu = [0, 3, 5]
+    for (Hq, Hk, Hv, n, with_gates, l2) in [(1, 2, 2, 2, True, False), (2, 2, 4, 3, False, True),
+                                            (2, 4, 4, 1, True, True)]:
+        T, d = cu[-1], 4
+        q = rng.standard_normal((T, Hq, d)); k = rng.standard_normal((T * n, Hk, d))
+        if not l2:
+            k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((T * n, Hv, d))
+        alpha = rng.uniform(0.3, 1.0, (T, Hv)) if with_gates else None
+        beta = rng.uniform(0.1, 0.9, (T * n, Hv)) if with_gates else None
+        init = rng.standard_normal((2, Hv, d, d)) * 0.3 if with_gates else None
+        ro, rf = flashinfer_literal(q, k, v, alpha, beta, n, cu, scale=0.7, init=init, l2norm=l2)
+        res = oracle.prefill_flashinfer(q, k, v, alpha, beta, n, scale=0.7, initial_state=init,
+                                        output_final_state=True, cu_seqlens=np.array(cu), use_qk_l2norm_in_kernel=l2,
+                                        lib=lib)
+        _close(res["o"], ro, what=f"o Hq={Hq} Hk={Hk} Hv={Hv}")
+        _close(res["final_state"], rf, what=f"S Hq={Hq} Hk={Hk} Hv={Hv}")
+
+
+ALL_PINS += [pin_flashinfer_literal]

@@ -51,7 +51,7 @@ class Fake:
 
     def tensor(self, b, dtype, shape, strides=None, data=None):
         t = b.gdp_tensor()
-        es = {b.GDP_F32: 4, b.GDP_BF16: 2, b.GDP_I32: 4, b.GDP_I64: 8}[dtype]
+        es = {b.GDP_F32: 4, b.GDP_BF16: 2, b.GDP_I32: 4, b.GDP_I64: 8, b.GDP_F16: 2}[dtype]
         if strides is None:
             strides, acc = [], 1
             for d in reversed(shape):
@@ -271,3 +271,62 @@ def test_decode_aliasing(b):
     a = decode_args(b)
     a["o"] = a["fake"].tensor(b, b.GDP_BF16, [8, 4, 128], data=a["cache"].data + 4096)
     decode_expect(b, a, b.GDP_EALIAS, "o overlaps state_cache")
+
+
+# ---------------------------------------------------------------- FlashInfer-convention entry point
+
+def fi_args(b, T=100, N=2, n=2, Hq=2, Hk=2, Hv=4, d=128, dt=None):
+    f = Fake()
+    dt = b.GDP_BF16 if dt is None else dt
+    a = dict(q=f.tensor(b, dt, [T, Hq, d]), k=f.tensor(b, dt, [T * n, Hk, d]), v=f.tensor(b, dt, [T * n, Hv, d]),
+             g=f.tensor(b, b.GDP_F32, [T, Hv]), beta=f.tensor(b, b.GDP_F32, [T * n, Hv]), n=n, scale=0.0,
+             s0=f.tensor(b, b.GDP_F32, [N, Hv, d, d]), ofs=1, cu=f.tensor(b, b.GDP_I32, [N + 1]), l2=0,
+             o=f.tensor(b, dt, [T, Hv, d]), fs=f.tensor(b, b.GDP_F32, [N, Hv, d, d]), ws=None, wsb=0)
+    a["fake"] = f
+    return a
+
+
+def fi_expect(b, a, code, fragment):
+    r = ctypes.byref
+    rc = b.LIB.gdp_chunk_gated_delta_product(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["beta"]), a["n"],
+                                             a["scale"], r(a["s0"]), a["ofs"], r(a["cu"]), a["l2"], r(a["o"]),
+                                             r(a["fs"]), a["ws"], a["wsb"], None)
+    assert rc == code, (rc, b.gdp_last_error())
+    assert fragment in b.gdp_last_error(), b.gdp_last_error()
+
+
+def test_fi_validation(b):
+    fi_expect(b, fi_args(b), b.GDP_EWORKSPACE, "workspace")
+    a = fi_args(b)
+    a["fs"] = a["fake"].tensor(b, b.GDP_F32, [2, 4, 128, 128], data=a["s0"].data)
+    fi_expect(b, a, b.GDP_EALIAS, "output_state overlaps initial_state")
+    fi_expect(b, fi_args(b, dt=b.GDP_F16), b.GDP_EUNSUPPORTED, "float16")
+    fi_expect(b, fi_args(b, Hk=3), b.GDP_EINVAL, "Hq or Hv heads")
+    fi_expect(b, fi_args(b, Hq=4, Hk=4, Hv=2), b.GDP_EUNSUPPORTED, "more q heads")
+    fi_expect(b, fi_args(b, d=96), b.GDP_EUNSUPPORTED, "head size")
+    a = fi_args(b)
+    a["g"] = a["fake"].tensor(b, b.GDP_I32, [100, 4])
+    fi_expect(b, a, b.GDP_EUNSUPPORTED, "g must be")
+    a = fi_args(b)
+    a["beta"] = a["fake"].tensor(b, b.GDP_F16, [200, 4])
+    fi_expect(b, a, b.GDP_EUNSUPPORTED, "beta must be")
+    a = fi_args(b)
+    a["fs"] = b.gdp_tensor()
+    fi_expect(b, a, b.GDP_EINVAL, "output_state is required")
+    a = fi_args(b)
+    a["o"] = a["fake"].tensor(b, b.GDP_BF16, [100, 2, 128])
+    fi_expect(b, a, b.GDP_EINVAL, "output: dim 1")
+
+
+def test_fi_workspace_bytes(b):
+    import torch
+    base = b.gdp_workspace_bytes(100, 2, 2, 2, 4, 128, 128)
+    ws = b.gdp_fi_workspace_bytes(100, 2, 2, 2, 4, 128, torch.bfloat16, True, True)
+    assert ws >= base + 4 * 3 * 100 * 4 + 2 * 2 * 4 * 128 * 128 * 4
+    assert b.gdp_fi_workspace_bytes(100, 2, 2, 2, 4, 128, torch.float16) == 0
+
+
+def test_prefill_accepts_k_per_state_head(b):
+    a = base_args(b)
+    a["k"] = a["fake"].tensor(b, b.GDP_BF16, [200, 3, 128])
+    expect(b, a, b.GDP_EINVAL, "Hqk or Hv heads")
