@@ -492,3 +492,58 @@ def pin_flashinfer_literal(lib):
 
 
 ALL_PINS += [pin_flashinfer_literal]
+
+
+# ---------------------------------------------------------------- backward oracle
+
+def pin_backward_forward_matches_c_oracle(lib):
+    """The autograd token loop's forward equals the C oracle (GQA, l2norm, n=3)."""
+    from oracle import backward as ob
+    import torch
+    rng = np.random.default_rng(31)
+    for l2 in (False, True):
+        prob = make_problem(rng, (3, 1, 4), 3, 1, 2, 5, 3, unit_qk=not l2)
+        o, fin = ob.forward_torch(*[torch.tensor(prob[x]) for x in ("q", "k", "v", "g_log", "beta")], 3,
+                                  prob["cu_seqlens"], scale=0.7,
+                                  initial_state=torch.tensor(prob["initial_state"]), use_qk_l2norm=l2)
+        out = _run(lib, prob, scale=0.7, use_qk_l2norm=l2)
+        _close(o.numpy(), out["o"], what=f"o l2={l2}")
+        _close(fin.numpy(), out["final_state"], what=f"S l2={l2}")
+
+
+def pin_backward_finite_differences(lib):
+    """Every gradient of the backward oracle against central differences of the
+    C oracle's forward on a tiny problem (k with one head per state head)."""
+    from oracle import backward as ob
+    rng = np.random.default_rng(37)
+    lens, n, Hq, Hk, Hv, K, V = (2, 3), 2, 1, 2, 2, 3, 2
+    T, N = sum(lens), len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((T, Hq, K)); k = rng.standard_normal((T * n, Hk, K))
+    v = rng.standard_normal((T * n, Hv, V)); g = -rng.uniform(0.05, 0.7, (T, Hv))
+    b = rng.uniform(0.2, 0.9, (T * n, Hv)); s0 = 0.5 * rng.standard_normal((N, Hv, K, V))
+    do = rng.standard_normal((T, Hv, V)); dfin = rng.standard_normal((N, Hv, K, V))
+    for l2 in (False, True):
+        grads = ob.backward(q, k, v, g, b, n, cu, do, dfin, scale=0.6, initial_state=s0, use_qk_l2norm=l2)
+
+        def loss(q_, k_, v_, g_, b_, s0_):
+            # the C oracle reads q and k through one head index: give it q per k head
+            out = oracle.prefill(np.repeat(q_, Hk // Hq, axis=1), k_, v_, g_, b_, n, cu, scale=0.6,
+                                 initial_state=s0_, use_qk_l2norm=l2, lib=lib)
+            return float(np.sum(out["o"] * do) + np.sum(out["final_state"] * dfin))
+
+        base = [q, k, v, g, b, s0]
+        for idx, name in enumerate(["dq", "dk", "dv", "dg_log", "dbeta", "dinitial_state"]):
+            x = base[idx]
+            num = np.zeros_like(x)
+            h = 1e-6
+            for pos in np.ndindex(*x.shape):
+                xp = x.copy(); xp[pos] += h
+                xm = x.copy(); xm[pos] -= h
+                args_p = list(base); args_p[idx] = xp
+                args_m = list(base); args_m[idx] = xm
+                num[pos] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(grads[name], num, tol=1e-6, what=f"{name} l2={l2}")
+
+
+ALL_PINS += [pin_backward_forward_matches_c_oracle, pin_backward_finite_differences]
