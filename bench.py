@@ -154,6 +154,62 @@ def bench_decode(args, gdp, workloads):
     print(json.dumps(line), flush=True)
 
 
+def bench_backward(args, gdp, workloads):
+    """Gradients of the long-context prefill (its shape and inputs, one call per
+    step, including the forward rerun that leaves the chunk states).  The
+    recurrent reverse pass is bound by its per-token vector arithmetic; the line
+    reports its HBM bytes (inputs read once, float32 gradients written once) so
+    that the fraction shows how far it is from the bandwidth bound."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.workload(4)
+    inp = workloads.generate(w, dev)
+    T, N, n, Hqk, Hv, K, V = w.T, w.N, w.n, w.Hqk, w.Hv, w.K, w.V
+    gen = torch.Generator(device=dev).manual_seed(4242)
+    d_o = torch.randn(T, Hv, V, generator=gen, device=dev).to(torch.bfloat16)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk = torch.empty((T, Hqk, K), **f32), torch.empty((T * n, Hqk, K), **f32)
+    dv, dg, db = torch.empty((T * n, Hv, V), **f32), torch.empty((T, Hv), **f32), torch.empty((T * n, Hv), **f32)
+    ds0 = torch.empty((N, Hv, K, V), **f32)
+    ws = torch.empty(gdp.gdp_backward_workspace_bytes(T, N, n, Hqk, Hv, K, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdp.gdp_chunk_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, inp["cu_seqlens"],
+                                       0.0, inp["initial_state"], True, d_o, None, dq, dk, dv, dg, db, ds0, ws,
+                                       stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    # read: q, k, v, do (bf16), g, beta, s0; written: dq, dk, dv, dg, dbeta, ds0 (float32)
+    alg = (T * (2 * K * Hqk * (1 + n) + 2 * V * Hv * (1 + n) + 4 * Hv * (1 + n)) + 4 * N * Hv * K * V +
+           T * 4 * (K * Hqk * (1 + n) + V * Hv * n + Hv * (1 + n)) + 4 * N * Hv * K * V)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    line = {"metric": "real tokens/s, gradients of the chunked GDP prefill (bf16 inputs, float32 gradients) + % of HBM roofline",
+            "value": T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "backward of the long-context prefill: 8 x 65536 tokens, n=2, Hqk=16 / Hv=32, "
+                                   "K=V=128, bf16, in-kernel L2 norm", "real_tokens": T},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gdp_chunk_prefill_backward (forward rerun + gdp_backward_kernel)",
+                         "kernel_ms": kern_ms, "algorithmic_bytes_per_launch": alg},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +222,8 @@ def main():
                     help="measure the single-token decode step on the state cache instead of the prefill "
                          "(serving batch: 256 entries with 8 padding, n=2, Hqk=16 / Hv=32, K=V=128, bf16, "
                          "1024 cache slots)")
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the gradients of the long-context prefill instead of the forward pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (three times); used to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -192,6 +250,9 @@ def main():
 
     if args.decode:
         bench_decode(args, gdp, workloads)
+        return
+    if args.backward:
+        bench_backward(args, gdp, workloads)
         return
 
     dev = torch.device("cuda:0")

@@ -19,7 +19,8 @@ STATUS_NAMES = {GDP_EINVAL: "GDP_EINVAL", GDP_EUNSUPPORTED: "GDP_EUNSUPPORTED", 
 
 EXPORTED = ("gdp_descriptor_capacity", "gdp_build_descriptors", "gdp_workspace_bytes",
             "gdp_chunk_prefill", "gdp_recurrent_decode", "gdp_fi_workspace_bytes",
-            "gdp_chunk_gated_delta_product", "gdp_last_error", "gdp_version")
+            "gdp_chunk_gated_delta_product", "gdp_backward_workspace_bytes", "gdp_chunk_prefill_backward",
+            "gdp_last_error", "gdp_version")
 
 
 class gdp_tensor(ctypes.Structure):
@@ -69,6 +70,13 @@ def _load(path=LIB_PATH):
     lib.gdp_chunk_gated_delta_product.argtypes = [T, T, T, T, T, ctypes.c_int32, ctypes.c_float, T,
                                                   ctypes.c_int32, T, ctypes.c_int32, T, T, ctypes.c_void_p,
                                                   ctypes.c_size_t, ctypes.c_void_p]
+    lib.gdp_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdp_backward_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.gdp_chunk_prefill_backward.restype = ctypes.c_int
+    lib.gdp_chunk_prefill_backward.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
+                                               T, T, T, T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t,
+                                               ctypes.c_void_p]
     lib.gdp_last_error.restype = ctypes.c_char_p
     lib.gdp_last_error.argtypes = []
     lib.gdp_version.restype = ctypes.c_char_p
@@ -226,6 +234,25 @@ def gdp_chunk_gated_delta_product(q, k, v, g, beta, num_householder, scale, init
                                              ctypes.byref(ot), ctypes.byref(st_out), ws_ptr, ws_bytes, st))
 
 
+def gdp_backward_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, dtype=torch.bfloat16):
+    return int(LIB.gdp_backward_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, _DT[dtype]))
+
+
+def gdp_chunk_prefill_backward(q, k, v, g_log, beta, num_householder, cu_seqlens, scale, initial_state,
+                               use_qk_l2norm, d_o, d_final_state, dq, dk, dv, dg_log, dbeta, d_initial_state,
+                               workspace, stream=None):
+    """Direct call of the backward C entry point (caller-allocated gradients and workspace)."""
+    ts = [as_gdp_tensor(x) for x in (q, k, v, g_log, beta)]
+    cu, s0 = as_gdp_tensor(cu_seqlens), as_gdp_tensor(initial_state)
+    dts = [as_gdp_tensor(x) for x in (d_o, d_final_state, dq, dk, dv, dg_log, dbeta, d_initial_state)]
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _stream(q.device) if stream is None else stream
+    _check(LIB.gdp_chunk_prefill_backward(*[ctypes.byref(a) for a in ts], int(num_householder), ctypes.byref(cu),
+                                          float(scale or 0.0), ctypes.byref(s0), int(bool(use_qk_l2norm)),
+                                          *[ctypes.byref(a) for a in dts], ws_ptr, ws_bytes, st))
+
+
 # ---------------------------------------------------------------- convenience wrapper
 
 def chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=None, initial_state=None,
@@ -300,3 +327,24 @@ def chunk_gated_delta_product(q, k, v, g=None, beta=None, num_householder=1, sca
     gdp_chunk_gated_delta_product(q, k, v, g, beta, num_householder, scale, initial_state, output_final_state,
                                   cu_seqlens, use_qk_l2norm_in_kernel, out, fs, ws)
     return (out, fs) if output_final_state else out
+
+
+def chunk_prefill_backward(q, k, v, g_log, beta, num_householder, cu_seqlens, d_o, d_final_state=None, scale=None,
+                           initial_state=None, use_qk_l2norm=False):
+    """Allocating front end of the gradients: returns a dict of float32 tensors
+    dq, dk, dv, dg_log, dbeta and d_initial_state (None without an initial state)."""
+    T, Hqk, K = q.shape
+    Hk, Hv, V = k.shape[1], v.shape[1], v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    n = int(num_householder)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk = torch.empty((T, Hqk, K), **f32), torch.empty((T * n, Hk, K), **f32)
+    dv, dg = torch.empty((T * n, Hv, V), **f32), torch.empty((T, Hv), **f32)
+    db = torch.empty((T * n, Hv), **f32)
+    ds0 = torch.empty((N, Hv, K, V), **f32) if initial_state is not None else None
+    ws = torch.empty(max(gdp_backward_workspace_bytes(T, N, n, Hqk, Hv, K, V, q.dtype), 256), dtype=torch.uint8,
+                     device=dev)
+    gdp_chunk_prefill_backward(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, use_qk_l2norm, d_o,
+                               d_final_state, dq, dk, dv, dg, db, ds0, ws)
+    return {"dq": dq, "dk": dk, "dv": dv, "dg_log": dg, "dbeta": db, "d_initial_state": ds0}

@@ -577,6 +577,163 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   return GDP_OK;
 }
 
+namespace {
+struct BwdLayout {
+  size_t desc = 0, cs = 0, o = 0, fwd = 0, total = 0;
+  int64_t nt_cap = 0, ntdp_cap = 0;
+};
+BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V, int32_t dtype) {
+  BwdLayout L;
+  if (gdp_descriptor_capacity(T, N, n, &L.nt_cap, &L.ntdp_cap) != GDP_OK) return L;
+  const size_t fwd = gdp_workspace_bytes(T, N, n, Hqk, Hv, K, V, dtype);
+  if (!fwd) return L;
+  L.desc = 0;
+  L.cs = L.desc + desc_bytes(N, L.nt_cap, L.ntdp_cap);
+  L.o = L.cs + align256((size_t)(L.nt_cap > 0 ? L.nt_cap : 1) * Hv * K * V * 4);
+  L.fwd = L.o + align256((size_t)T * Hv * V * elem_size(dtype));
+  L.total = L.fwd + fwd;
+  return L;
+}
+}  // namespace
+
+size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V,
+                                    int32_t dtype) {
+  if (T < 0 || N < 0 || n < 1 || Hqk < 1 || Hv < 1 || K < 1 || V < 1) return 0;
+  if (dtype != GDP_F32 && dtype != GDP_BF16) return 0;
+  return bwd_layout(T, N, n, Hqk, Hv, K, V, dtype).total;
+}
+
+int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
+                               const gdp_tensor *beta, int32_t n, const gdp_tensor *cu_seqlens, float scale,
+                               const gdp_tensor *initial_state, int32_t use_qk_l2norm, const gdp_tensor *d_o,
+                               const gdp_tensor *d_final_state, const gdp_tensor *dq, const gdp_tensor *dk,
+                               const gdp_tensor *dv, const gdp_tensor *dg_log, const gdp_tensor *dbeta,
+                               const gdp_tensor *d_initial_state, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  g_last_error.clear();
+  if (!present(q) || !present(k) || !present(v) || !present(g_log) || !present(beta) || !present(d_o))
+    return fail(GDP_EINVAL, "q, k, v, g_log, beta and d_o are required");
+  if (!present(dq) || !present(dk) || !present(dv) || !present(dg_log) || !present(dbeta))
+    return fail(GDP_EINVAL, "dq, dk, dv, dg_log and dbeta are required");
+  if (!present(cu_seqlens)) return fail(GDP_EINVAL, "cu_seqlens is required (varlen input only)");
+  if (n < 1) return fail(GDP_EINVAL, "num_householder must be >= 1, got %d", n);
+  if (q->ndim != 3 || k->ndim != 3 || v->ndim != 3 || cu_seqlens->ndim != 1)
+    return fail(GDP_EINVAL, "q, k, v must be 3-d and cu_seqlens 1-d");
+  const int64_t T = q->shape[0], Hqk = q->shape[1], K = q->shape[2];
+  const int64_t Hk = k->shape[1], Hv = v->shape[1], V = v->shape[2];
+  const int64_t N = cu_seqlens->shape[0] - 1;
+  if (N < 0 || Hqk < 1 || Hv < 1 || Hk < 1) return fail(GDP_EINVAL, "bad sizes");
+  if (Hv % Hqk != 0 || (Hk != Hqk && Hk != Hv)) return fail(GDP_EINVAL, "head counts: Hv a multiple of Hqk, Hk = Hqk or Hv");
+  if (!gdp::backward_supported((int)K, (int)V, n))
+    return fail(GDP_EUNSUPPORTED, "backward needs K, V in {64, 128} and num_householder <= 4");
+  const int32_t dt = q->dtype;
+  if (dt != GDP_F32 && dt != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q must be float32 or bfloat16");
+  if (d_o->dtype != dt) return fail(GDP_EUNSUPPORTED, "d_o must have q's dtype");
+  int rc;
+  const int64_t sdo[3] = {T, Hv, V}, sq[3] = {T, Hqk, K}, sk[3] = {T * n, Hk, K}, sv[3] = {T * n, Hv, V};
+  const int64_t sg[2] = {T, Hv}, sb[2] = {T * n, Hv}, sst[4] = {N, Hv, K, V};
+  if ((rc = check_shape(d_o, "d_o", 3, sdo)) || (rc = check_shape(dq, "dq", 3, sq)) || (rc = check_shape(dk, "dk", 3, sk)) ||
+      (rc = check_shape(dv, "dv", 3, sv)) || (rc = check_shape(dg_log, "dg_log", 2, sg)) ||
+      (rc = check_shape(dbeta, "dbeta", 2, sb)))
+    return rc;
+  for (const gdp_tensor *t : {dq, dk, dv, dg_log, dbeta})
+    if (t->dtype != GDP_F32) return fail(GDP_EUNSUPPORTED, "gradients are float32");
+  for (const gdp_tensor *t : {dq, dk, dg_log, dbeta})
+    if (!contiguous(t)) return fail(GDP_EINVAL, "dq, dk, dg_log and dbeta must be contiguous (they are accumulated)");
+  if (!nonneg_strides(d_o) || !nonneg_strides(dv)) return fail(GDP_EINVAL, "negative strides are not supported");
+  if (present(d_final_state)) {
+    if ((rc = check_shape(d_final_state, "d_final_state", 4, sst))) return rc;
+    if (d_final_state->dtype != GDP_F32 || !contiguous(d_final_state))
+      return fail(GDP_EUNSUPPORTED, "d_final_state must be contiguous float32");
+  }
+  if (present(d_initial_state)) {
+    if ((rc = check_shape(d_initial_state, "d_initial_state", 4, sst))) return rc;
+    if (d_initial_state->dtype != GDP_F32 || !contiguous(d_initial_state))
+      return fail(GDP_EUNSUPPORTED, "d_initial_state must be contiguous float32");
+  }
+  // gradients may not overlap inputs or each other
+  Range ins[] = {range_of(q, "q"), range_of(k, "k"), range_of(v, "v"), range_of(g_log, "g_log"),
+                 range_of(beta, "beta"), range_of(cu_seqlens, "cu_seqlens"), range_of(initial_state, "initial_state"),
+                 range_of(d_o, "d_o"), range_of(d_final_state, "d_final_state")};
+  Range outs[] = {range_of(dq, "dq"), range_of(dk, "dk"), range_of(dv, "dv"), range_of(dg_log, "dg_log"),
+                  range_of(dbeta, "dbeta"), range_of(d_initial_state, "d_initial_state")};
+  for (const Range &ro : outs)
+    for (const Range &ri : ins)
+      if (overlap(ro, ri)) return fail(GDP_EALIAS, "%s overlaps input %s", ro.name, ri.name);
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDP_EALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  const BwdLayout L = bwd_layout(T, N, n, (int32_t)Hqk, (int32_t)Hv, (int32_t)K, (int32_t)V, dt);
+  if (!L.total) return fail(GDP_EINVAL, "bad sizes");
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
+  char *ws = (char *)workspace;
+
+  // descriptors, then the forward pass leaving the state entering every token chunk
+  gdp_descriptors d;
+  char *p = ws + L.desc;
+  d.chunk_indices = (int32_t *)p; p += align256((size_t)L.nt_cap * 8);
+  d.chunk_indices_dp = (int32_t *)p; p += align256((size_t)L.ntdp_cap * 8);
+  d.chunk_offsets = (int32_t *)p; p += align256((size_t)(N + 1) * 4);
+  d.chunk_offsets_dp = (int32_t *)p;
+  d.nt_cap = L.nt_cap; d.ntdp_cap = L.ntdp_cap;
+  gdp_tensor cu = *cu_seqlens;
+  if ((rc = gdp_build_descriptors(&cu, n, T, &d, stream)) != GDP_OK) return rc;
+  const int64_t csr = L.nt_cap > 0 ? L.nt_cap : 1;
+  gdp_tensor tcs{ws + L.cs, GDP_F32, 4, {csr, Hv, K, V}, {Hv * K * V, K * V, V, 1}};
+  gdp_tensor to{ws + L.o, dt, 3, {T, Hv, V}, {Hv * V, V, 1}};
+  gdp_tensor none{};
+  if ((rc = gdp_chunk_prefill(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, 0, use_qk_l2norm, &none,
+                              &none, 1, &to, &none, &tcs, &d, ws + L.fwd, workspace_bytes - L.fwd, stream)) != GDP_OK)
+    return rc;
+  hipError_t e;
+  for (const gdp_tensor *t : {dq, dk, dg_log, dbeta}) {
+    int64_t cnt = 1;
+    for (int i = 0; i < t->ndim; ++i) cnt *= t->shape[i];
+    if ((e = gdp::launch_fill((int32_t *)t->data, cnt, 0, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
+  }
+  gdp::BwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q->data; a.q_st = q->stride[0]; a.q_sh = q->stride[1];
+  a.k = k->data; a.k_st = k->stride[0]; a.k_sh = k->stride[1];
+  a.v = v->data; a.v_st = v->stride[0]; a.v_sh = v->stride[1];
+  a.g = (const float *)g_log->data; a.g_st = g_log->stride[0]; a.g_sh = g_log->stride[1];
+  a.beta = (const float *)beta->data; a.b_st = beta->stride[0]; a.b_sh = beta->stride[1];
+  a.cu = cu_seqlens->data; a.cu_is64 = cu_seqlens->dtype == GDP_I64;
+  a.T = T; a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv; a.Hk = (int)Hk;
+  a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
+  a.l2norm = use_qk_l2norm ? 1 : 0;
+  a.chunk_states = (const float *)(ws + L.cs);
+  a.chunk_offsets = d.chunk_offsets;
+  a.dout = d_o->data; a.do_st = d_o->stride[0]; a.do_sh = d_o->stride[1];
+  a.dfinal = present(d_final_state) ? (const float *)d_final_state->data : nullptr;
+  a.dq = (float *)dq->data; a.dq_st = dq->stride[0]; a.dq_sh = dq->stride[1];
+  a.dk = (float *)dk->data; a.dk_st = dk->stride[0]; a.dk_sh = dk->stride[1];
+  a.dv = (float *)dv->data; a.dv_st = dv->stride[0]; a.dv_sh = dv->stride[1];
+  a.dg = (float *)dg_log->data; a.dg_st = dg_log->stride[0]; a.dg_sh = dg_log->stride[1];
+  a.dbeta = (float *)dbeta->data; a.db_st = dbeta->stride[0]; a.db_sh = dbeta->stride[1];
+  a.ds0 = present(d_initial_state) ? (float *)d_initial_state->data : nullptr;
+  const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
+  if ((e = gdp::launch_backward(a, idt, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
+    return fail(GDP_EHIP, "backward launch: %s", hipGetErrorString(e));
+  if (use_qk_l2norm) {
+    gdp::NormGradArgs na;
+    na.x = q->data; na.x_st = q->stride[0]; na.x_sh = q->stride[1];
+    na.g = (float *)dq->data; na.g_st = dq->stride[0]; na.g_sh = dq->stride[1];
+    na.rows = T * Hqk; na.heads = (int)Hqk;
+    if ((e = gdp::launch_l2norm_grad(na, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "norm gradient launch: %s", hipGetErrorString(e));
+    na.x = k->data; na.x_st = k->stride[0]; na.x_sh = k->stride[1];
+    na.g = (float *)dk->data; na.g_st = dk->stride[0]; na.g_sh = dk->stride[1];
+    na.rows = T * n * Hk; na.heads = (int)Hk;
+    if ((e = gdp::launch_l2norm_grad(na, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "norm gradient launch: %s", hipGetErrorString(e));
+  }
+  return GDP_OK;
+}
+
 int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
                          const gdp_tensor *beta, int32_t n, float scale, int32_t use_qk_l2norm,
                          const gdp_tensor *state_cache, const gdp_tensor *state_indices, const gdp_tensor *o,

@@ -126,6 +126,42 @@ hipError_t launch_segments(const SegArgs &a, hipStream_t stream);
 constexpr int64_t ORDER_MAX_SEQ = 4096;
 hipError_t launch_order(const OrderArgs &a, hipStream_t stream);
 
+// Gradients of the prefill (recurrent reverse pass; gdp_backward.hip).
+struct BwdArgs {
+  const void *q; int64_t q_st, q_sh;        // [T, Hqk, K]
+  const void *k; int64_t k_st, k_sh;        // [T*n, Hk, K]
+  const void *v; int64_t v_st, v_sh;        // [T*n, Hv, V]
+  const float *g; int64_t g_st, g_sh;       // [T, Hv] log decays
+  const float *beta; int64_t b_st, b_sh;    // [T*n, Hv]
+  const void *cu; int cu_is64;
+  int64_t T;
+  int N, n, Hqk, Hv, Hk;
+  float scale;
+  int l2norm;
+  const float *chunk_states;                // [NT, Hv, K, V]: state entering each token chunk
+  const int32_t *chunk_offsets;             // [N+1]
+  const void *dout; int64_t do_st, do_sh;   // [T, Hv, V], the inputs' dtype
+  const float *dfinal;                      // [N, Hv, K, V] or null
+  // outputs (float32): dq, dk, dbeta, dg accumulate into zeroed buffers
+  float *dq; int64_t dq_st, dq_sh;
+  float *dk; int64_t dk_st, dk_sh;
+  float *dv; int64_t dv_st, dv_sh;
+  float *dg; int64_t dg_st, dg_sh;
+  float *dbeta; int64_t db_st, db_sh;
+  float *ds0;                               // [N, Hv, K, V] or null
+};
+bool backward_supported(int K, int V, int n);
+hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_t stream);
+
+// Gradient with respect to raw rows from the one with respect to their L2-normalised
+// versions, in place (rows = R * heads rows of a [R, heads, K] tensor).
+struct NormGradArgs {
+  const void *x; int64_t x_st, x_sh;
+  float *g; int64_t g_st, g_sh;
+  int64_t rows; int heads;
+};
+hipError_t launch_l2norm_grad(const NormGradArgs &a, int dtype, int K, hipStream_t stream);
+
 // Element types of the front end's conversion kernels.
 enum ElType { EL_F32 = 0, EL_BF16 = 1, EL_F16 = 2 };
 

@@ -196,6 +196,45 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
                          float scale, int32_t use_qk_l2norm, const gdp_tensor *state_cache,
                          const gdp_tensor *state_indices, const gdp_tensor *o, void *stream);
 
+/* Host-only.  Workspace bytes gdp_chunk_prefill_backward needs: the
+ * descriptors, the float32 state entering every token chunk (nt_cap x Hv x K x V),
+ * an output buffer of the forward pass it reruns, and that pass's workspace
+ * (gdp_workspace_bytes).  Returns 0 for invalid sizes or dtypes. */
+size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk, int32_t Hv,
+                                    int32_t K, int32_t V, int32_t dtype);
+
+/* Device.  Gradients of the prefill: with L = <o, d_o> + <final_state,
+ * d_final_state>, writes dL/dq, dL/dk, dL/dv, dL/dg_log, dL/dbeta and (when
+ * d_initial_state is given) dL/dinitial_state, for the same inputs and
+ * conventions as gdp_chunk_prefill (no state cache, no chunk states).
+ *
+ * The pages give no backward formulas (the blog page "Attention Cache and
+ * Sequence Parallelism", section "GDN: pass the state, not the KV", notes only
+ * that the dependencies run in reverse); these are the gradients of the
+ * recurrence itself, by reverse-mode differentiation token by token.  The call
+ * reruns the forward pass to obtain the state entering every 64-token chunk,
+ * then walks each chain backwards, recomputing the states in between.
+ *   d_o            [T, Hv, V]      q's dtype, rows may be strided
+ *   d_final_state  [N, Hv, K, V]   float32 contiguous, or data == NULL (zero)
+ *   dq [T, Hqk, K], dk [T*n, Hk, K], dg_log [T, Hv], dbeta [T*n, Hv]
+ *                                  float32, contiguous: they are accumulated with
+ *                                  float atomics over state heads and V tiles, so
+ *                                  their last bits depend on the order of the adds
+ *   dv [T*n, Hv, V]                float32, rows may be strided
+ *   d_initial_state [N, Hv, K, V]  float32 contiguous, or data == NULL
+ *   workspace      at least gdp_backward_workspace_bytes(...), 256-byte aligned
+ * No gradient may overlap an input or another gradient (GDP_EALIAS).  K, V in
+ * {64, 128}, num_householder <= 4 (GDP_EUNSUPPORTED otherwise).  Everything
+ * runs on `stream` with no allocation and no host read of device memory. */
+int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                               const gdp_tensor *g_log, const gdp_tensor *beta, int32_t num_householder,
+                               const gdp_tensor *cu_seqlens, float scale, const gdp_tensor *initial_state,
+                               int32_t use_qk_l2norm, const gdp_tensor *d_o, const gdp_tensor *d_final_state,
+                               const gdp_tensor *dq, const gdp_tensor *dk, const gdp_tensor *dv,
+                               const gdp_tensor *dg_log, const gdp_tensor *dbeta,
+                               const gdp_tensor *d_initial_state, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* Host-only.  Workspace bytes gdp_chunk_gated_delta_product needs: the gates
  * restated as float32 log decays and betas (4 (1 + n) T Hv bytes), a float32
  * K-major copy of each state it converts (4 N Hv d^2 bytes each, when an

@@ -1,0 +1,73 @@
+"""Gradients of the prefill (gdp_chunk_prefill_backward) against the fp64
+autograd oracle, element by element, through the C ABI (needs a gfx950 GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltaproduct_recurrence_amd import workloads
+from oracle import backward as obwd
+from tests.parity import TOL, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdp():
+    from gated_deltaproduct_recurrence_amd import binding
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return binding
+
+
+CASES = [
+    # lens, n, Hqk, Hk, Hv, K, V, dtype, l2norm, init, dfinal
+    ([37, 64, 130], 2, 2, 2, 4, 128, 128, torch.bfloat16, False, True, True),
+    ([70, 1, 0, 9], 3, 1, 1, 2, 64, 64, torch.float32, True, True, False),
+    ([100, 29], 1, 1, 2, 2, 64, 128, torch.bfloat16, True, False, True),
+    ([65, 63], 4, 2, 2, 2, 128, 64, torch.bfloat16, False, False, False),
+]
+
+
+def run_case(gdp, ci, seed=0):
+    lens, n, Hqk, Hk, Hv, K, V, dt, l2, init, dfin = CASES[ci]
+    w = workloads.custom(lens, n, Hqk, Hv, K, V, dtype=dt, l2norm_in_kernel=l2, init_std=0.2 if init else 0.0,
+                         seed=100 + ci)
+    inp = workloads.generate(w, "cpu")
+    gen = torch.Generator().manual_seed(200 + ci)
+    T, N = w.T, w.N
+    if Hk != Hqk:  # one k head per state head
+        k = torch.randn(T * n, Hk, K, generator=gen)
+        inp["k"] = (k if l2 else k / k.norm(dim=-1, keepdim=True)).to(dt)
+    d_o = torch.randn(T, Hv, V, generator=gen).to(dt)
+    d_fin = torch.randn(N, Hv, K, V, generator=gen) if dfin else None
+    ref = obwd.backward(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(inp["g_log"]), to_np(inp["beta"]),
+                        n, inp["cu_seqlens"].numpy(), to_np(d_o), None if d_fin is None else d_fin.numpy(),
+                        initial_state=to_np(inp["initial_state"]), use_qk_l2norm=l2)
+    dev = lambda x: None if x is None else x.cuda()
+    res = gdp.chunk_prefill_backward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g_log"]),
+                                     dev(inp["beta"]), n, dev(inp["cu_seqlens"]), dev(d_o), dev(d_fin),
+                                     initial_state=dev(inp["initial_state"]), use_qk_l2norm=l2)
+    torch.cuda.synchronize()
+    return res, ref, TOL[dt]
+
+
+@pytest.mark.parametrize("kpath", ["fused", "split"])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_backward_parity(gdp, ci, kpath, monkeypatch):
+    if CASES[ci][7] == torch.float32 and kpath == "fused":
+        pytest.skip("float32 inputs run the split forward only")
+    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    res, ref, tol = run_case(gdp, ci)
+    names = ["dq", "dk", "dv", "dg_log", "dbeta"] + (["d_initial_state"] if res["d_initial_state"] is not None else [])
+    for name in names:
+        key = "dinitial_state" if name == "d_initial_state" else name
+        e = rel_err(to_np(res[name]), ref[key])
+        assert e <= tol, f"case {ci} {kpath}: {name} err {e:.3e}"
+
+
+def test_backward_zero_length_and_padding_rows(gdp):
+    """A zero-length sequence contributes nothing, and its initial-state gradient
+    is d_final_state passed straight through."""
+    res, ref, tol = run_case(gdp, 1)
+    lens = CASES[1][0]
+    assert lens[2] == 0
+    assert rel_err(to_np(res["d_initial_state"][2]), ref["dinitial_state"][2]) <= tol
