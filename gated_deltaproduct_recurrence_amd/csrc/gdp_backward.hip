@@ -21,12 +21,15 @@
 // recurrence once to keep the state entering every 8th token in LDS, and once
 // per 8-token block to hold the 8 token states in registers, then walks the
 // block backwards.  One wave owns one (sequence, state head, 8-column V tile):
-// lane (rg, c) = (lane / 8, lane % 8) holds rows 16 rg .. 16 rg + 15 (K = 128;
-// 8 rows for K = 64) of column c, so a column dot over K is a sum over the 8
-// lanes of equal c and a row sum over the tile's columns one over the 8 lanes of
-// equal rg, both by lane exchanges.  Gradients shared by several waves (dq, dk:
+// lane (c, rg) = (lane / 8, lane % 8) holds rows 16 rg .. 16 rg + 15 (K = 128;
+// 8 rows for K = 64) of column c, so a column dot over K (on the recurrence's
+// critical path) is a sum over 8 adjacent lanes, done with DPP moves, and a row
+// sum over the tile's columns one over the 8 lanes of equal rg, by lane
+// exchanges.  Gradients shared by several waves (dq, dk:
 // all V tiles and the state heads of a q/k head; dbeta, dg_log: all V tiles)
-// are accumulated with float atomics into zeroed buffers.
+// are accumulated with float atomics into zeroed buffers, after the four waves
+// of a workgroup (four adjacent V tiles of one chain, in lockstep token by
+// token) have summed theirs in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,7 +42,7 @@ namespace {
 constexpr int CH = 64;     // token chunk of the forward pass's chunk states
 constexpr int VT = 8;      // columns per wave
 constexpr int BLK = 8;     // tokens per register block (checkpoint spacing)
-constexpr int NMAX = 4;    // Householder rows per token served
+constexpr int NMAX = 3;    // Householder rows per token served
 constexpr float LOG2E_B = 1.4426950408889634f;
 
 __device__ __forceinline__ int64_t idx_at(const void *p, int is64, int64_t i) {
@@ -51,54 +54,92 @@ template <int LO, int HI> __device__ __forceinline__ float xsum(float x) {
   for (int m = LO; m <= HI; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
 }
-__device__ __forceinline__ float col_sum(float x) { return xsum<8, 32>(x); }  // over rg (rows)
-__device__ __forceinline__ float row_sum(float x) { return xsum<1, 4>(x); }   // over c (columns)
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// sum over the 8 lanes of an aligned group (the lane's row groups of one column),
+// with DPP only: swap neighbours, swap pairs, then the two quads of the half row
+__device__ __forceinline__ float col_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  return x;
+}
+__device__ __forceinline__ float row_sum(float x) { return xsum<8, 32>(x); }  // over the 8 columns
 
 template <typename T, int K, int V> struct Bwd {
-  static constexpr int RK = K / 8;  // rows per lane
+  static constexpr int RK = K / 8;                     // rows per lane
+  static constexpr int RW = RK * (int)sizeof(T) / 16;  // 16-byte words holding them
+  static_assert(RW >= 1, "at least one 16-byte word per lane");
+  // the inputs of one token (loaded a token ahead of their use): the lane's RK
+  // entries of the token's k rows (and q row) as loaded, its v, beta, decay and
+  // output gradient
+  struct In {
+    uint4 k[NMAX][RW];
+    uint4 q[RW];
+    float v[NMAX], b[NMAX], al, dov;
+  };
   const BwdArgs &a;
-  int seq, h, hq, hk, vt, lane, rg, c;
-  int64_t t0, L;
+  int seq, h, hq, hk, vt, lane, rg, c, col;
   __device__ Bwd(const BwdArgs &args) : a(args) {}
 
-  // the lane's RK entries of row `row` of a [., H, K] tensor (normalised when asked)
-  __device__ __forceinline__ void load_row(float (&x)[RK], const T *base, int64_t row, int64_t st, int64_t sh, int head,
-                                           float &rstd) const {
-    const T *p = base + row * st + (int64_t)head * sh + RK * rg;
+  __device__ __forceinline__ void load(In &x, int64_t t, bool with_q) const {
+    x.al = __builtin_amdgcn_exp2f(a.g[t * a.g_st + (int64_t)h * a.g_sh] * LOG2E_B);
 #pragma unroll
-    for (int i = 0; i < RK; ++i) x[i] = (float)p[i];
-    rstd = 1.f;
+    for (int j = 0; j < NMAX; ++j) {
+      if (j < a.n) {
+        const int64_t r = t * a.n + j;
+        const uint4 *p = (const uint4 *)((const T *)a.k + r * a.k_st + (int64_t)hk * a.k_sh + RK * rg);
+#pragma unroll
+        for (int i = 0; i < RW; ++i) x.k[j][i] = p[i];
+        x.b[j] = a.beta[r * a.b_st + (int64_t)h * a.b_sh];
+        x.v[j] = (float)((const T *)a.v)[r * a.v_st + (int64_t)h * a.v_sh + col];
+      }
+    }
+    if (with_q) {
+      const uint4 *p = (const uint4 *)((const T *)a.q + t * a.q_st + (int64_t)hq * a.q_sh + RK * rg);
+#pragma unroll
+      for (int i = 0; i < RW; ++i) x.q[i] = p[i];
+      x.dov = (float)((const T *)a.dout)[t * a.do_st + (int64_t)h * a.do_sh + col] * a.scale;
+    }
+  }
+  // a row in float, L2-normalised over all K entries when asked
+  __device__ __forceinline__ void row(float (&o)[RK], const uint4 (&x)[RW]) const {
+#pragma unroll
+    for (int i = 0; i < RK; ++i) {
+      constexpr int PER = 16 / (int)sizeof(T);  // elements per word
+      const uint4 wd = x[i / PER];
+      const int e = i % PER;
+      const uint32_t u32 = (sizeof(T) == 4) ? (e == 0 ? wd.x : e == 1 ? wd.y : e == 2 ? wd.z : wd.w)
+                                            : (e / 2 == 0 ? wd.x : e / 2 == 1 ? wd.y : e / 2 == 2 ? wd.z : wd.w);
+      o[i] = (sizeof(T) == 4) ? __builtin_bit_cast(float, u32)
+                              : __builtin_bit_cast(float, (e & 1) ? (u32 & 0xFFFF0000u) : (u32 << 16));
+    }
     if (a.l2norm) {
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < RK; ++i) ss = fmaf(x[i], x[i], ss);
-      rstd = __builtin_amdgcn_rsqf(col_sum(ss) + 1e-6f);
+      for (int i = 0; i < RK; ++i) ss = fmaf(o[i], o[i], ss);
+      const float rs = __builtin_amdgcn_rsqf(col_sum(ss) + 1e-6f);
 #pragma unroll
-      for (int i = 0; i < RK; ++i) x[i] *= rstd;
+      for (int i = 0; i < RK; ++i) o[i] *= rs;
     }
   }
-  __device__ __forceinline__ float alpha_of(int64_t t) const {
-    return __builtin_amdgcn_exp2f(a.g[t * a.g_st + (int64_t)h * a.g_sh] * LOG2E_B);
-  }
-  __device__ __forceinline__ float beta_of(int64_t r) const { return a.beta[r * a.b_st + (int64_t)h * a.b_sh]; }
-  __device__ __forceinline__ float v_of(int64_t r) const {
-    return (float)((const T *)a.v)[r * a.v_st + (int64_t)h * a.v_sh + VT * vt + c];
-  }
-  // one token forward on S (the lane's part)
-  __device__ __forceinline__ void step(float (&S)[RK], int64_t t) const {
-    const float al = alpha_of(t);
+  // one token forward on the lane's part of S
+  __device__ __forceinline__ void step(float (&S)[RK], const In &x) const {
 #pragma unroll
-    for (int i = 0; i < RK; ++i) S[i] *= al;
-    for (int j = 0; j < a.n; ++j) {
-      const int64_t r = t * a.n + j;
-      float kv[RK], rk;
-      load_row(kv, (const T *)a.k, r, a.k_st, a.k_sh, hk, rk);
-      float part = 0.f;
+    for (int i = 0; i < RK; ++i) S[i] *= x.al;
 #pragma unroll
-      for (int i = 0; i < RK; ++i) part = fmaf(S[i], kv[i], part);
-      const float e = beta_of(r) * (v_of(r) - col_sum(part));
+    for (int j = 0; j < NMAX; ++j) {
+      if (j < a.n) {
+        float kv[RK];
+        row(kv, x.k[j]);
+        float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < RK; ++i) S[i] = fmaf(kv[i], e, S[i]);
+        for (int i = 0; i < RK; ++i) part = fmaf(S[i], kv[i], part);
+        const float e = x.b[j] * (x.v[j] - col_sum(part));
+#pragma unroll
+        for (int i = 0; i < RK; ++i) S[i] = fmaf(kv[i], e, S[i]);
+      }
     }
   }
 };
@@ -106,126 +147,147 @@ template <typename T, int K, int V> struct Bwd {
 template <typename T, int K, int V>
 __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   using B = Bwd<T, K, V>;
+  using In = typename B::In;
   constexpr int RK = B::RK, NVT = V / VT;
   // per wave: the state entering each 8-token block of the chunk (64 tokens)
   __shared__ float ck[4][CH / BLK][RK * 64];
+  // per token, double-buffered by token parity: the four waves' partial dq and
+  // dk rows (slot 0: dq, 1 + j: dk of row j) and, in column K, their partial
+  // dg_log (slot 0) and dbeta (slot 1 + j); summed after one barrier, then one
+  // atomic per element
+  __shared__ float red[2][NMAX + 1][4][K + 4];
   B s(a);
   const int w = threadIdx.x >> 6;
   s.lane = threadIdx.x & 63;
-  s.rg = s.lane >> 3;
-  s.c = s.lane & 7;
+  s.rg = s.lane & 7;
+  s.c = s.lane >> 3;
   const int64_t wid = (int64_t)blockIdx.x * 4 + w;
   const int64_t nw = (int64_t)a.N * a.Hv * NVT;
-  if (wid >= nw) return;
+  if (wid >= nw) return;  // never taken: the grid holds exactly nw waves (V / 8 is a multiple of 4)
   s.vt = (int)(wid % NVT);
   s.h = (int)((wid / NVT) % a.Hv);
   s.seq = (int)(wid / ((int64_t)NVT * a.Hv));
   s.hq = s.h / (a.Hv / a.Hqk);
   s.hk = s.h / (a.Hv / a.Hk);
+  s.col = VT * s.vt + s.c;
   int64_t t0 = idx_at(a.cu, a.cu_is64, s.seq), t1 = idx_at(a.cu, a.cu_is64, s.seq + 1);
   t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
   t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
-  s.t0 = t0;
-  s.L = t1 - t0;
-  const int ntc = (int)((s.L + CH - 1) / CH);
-  const int col = VT * s.vt + s.c;
+  const int ntc = (int)((t1 - t0 + CH - 1) / CH);
   const size_t KV = (size_t)K * V;
-  const size_t soff = ((size_t)s.seq * a.Hv + s.h) * KV + (size_t)(RK * s.rg) * V + col;  // + i * V
+  const size_t hoff = (size_t)s.h * KV + (size_t)(RK * s.rg) * V + s.col;  // within one [Hv, K, V] state; + i * V
+  const size_t soff = (size_t)s.seq * a.Hv * KV + hoff;
   float *my_ck = &ck[w][0][0];
 
   float dS[RK];
 #pragma unroll
   for (int i = 0; i < RK; ++i) dS[i] = a.dfinal ? a.dfinal[soff + (size_t)i * V] : 0.f;
 
+  // token inputs, double-buffered: the next token's are loaded while the
+  // current one is used (the buffer index is a compile-time constant below)
+  In buf[2];
   for (int cc = ntc - 1; cc >= 0; --cc) {
     const int64_t tb = t0 + (int64_t)CH * cc;
     const int ntok = (int)((t1 - tb) < CH ? (t1 - tb) : CH);
-    // the state entering the chunk, then the states entering every 8th token
+    const int nblk = (ntok + BLK - 1) / BLK;
+    // the state entering the chunk, then the state entering every 8th token
     float S[RK];
-    const int64_t csrow = (int64_t)a.chunk_offsets[s.seq] + cc;
-    const float *src = a.chunk_states + (size_t)csrow * a.Hv * KV + (soff - (size_t)s.seq * a.Hv * KV);
+    const float *src = a.chunk_states + (size_t)((int64_t)a.chunk_offsets[s.seq] + cc) * a.Hv * KV + hoff;
 #pragma unroll
     for (int i = 0; i < RK; ++i) S[i] = src[(size_t)i * V];
-    const int nblk = (ntok + BLK - 1) / BLK;
-    for (int b = 0; b < nblk; ++b) {
+    const int nstep = BLK * (nblk - 1);  // tokens before the last block's start (a multiple of 8)
+    if (nstep > 0) s.load(buf[0], tb, false);
+    for (int m = 0; m < nstep; m += 2) {
+      if (m % BLK == 0) {
 #pragma unroll
-      for (int i = 0; i < RK; ++i) my_ck[(b * RK + i) * 64 + s.lane] = S[i];
-      if (b + 1 < nblk)
-        for (int m = 0; m < BLK; ++m) s.step(S, tb + BLK * b + m);
+        for (int i = 0; i < RK; ++i) my_ck[((m / BLK) * RK + i) * 64 + s.lane] = S[i];
+      }
+      s.load(buf[1], tb + m + 1, false);
+      s.step(S, buf[0]);
+      if (m + 2 < nstep) s.load(buf[0], tb + m + 2, false);
+      s.step(S, buf[1]);
     }
+#pragma unroll
+    for (int i = 0; i < RK; ++i) my_ck[((nblk - 1) * RK + i) * 64 + s.lane] = S[i];
     // blocks backwards
     for (int b = nblk - 1; b >= 0; --b) {
       const int nb = (ntok - BLK * b) < BLK ? (ntok - BLK * b) : BLK;
+      const int64_t tbb = tb + BLK * b;
       float ST[BLK][RK];  // state entering token m of the block
 #pragma unroll
       for (int i = 0; i < RK; ++i) ST[0][i] = my_ck[(b * RK + i) * 64 + s.lane];
-#pragma unroll
+      // token m - 1 of the block moves ST[m-1] to ST[m]; its inputs sit in buf[(m - 1) & 1]
+      if (nb > 1) s.load(buf[0], tbb, false);
+#pragma clang loop unroll(full)
       for (int m = 1; m < BLK; ++m) {
         if (m < nb) {
+          if (m + 1 < nb) s.load(buf[m & 1], tbb + m, false);
 #pragma unroll
           for (int i = 0; i < RK; ++i) ST[m][i] = ST[m - 1][i];
-          s.step(ST[m], tb + BLK * b + m - 1);
+          s.step(ST[m], buf[(m - 1) & 1]);
         }
       }
-#pragma unroll
+      // backwards over the block: token m's inputs (with q and the output
+      // gradient) in buf[m & 1], token m - 1's loaded meanwhile
+      if ((nb - 1) & 1) s.load(buf[1], tbb + nb - 1, true);  // constant indices keep buf in registers
+      else s.load(buf[0], tbb + nb - 1, true);
+#pragma clang loop unroll(full)
       for (int m = BLK - 1; m >= 0; --m) {
         if (m >= nb) continue;
-        const int64_t t = tb + BLK * b + m;
-        const float al = s.alpha_of(t);
+        const int64_t t = tbb + m;
+        In &cur = buf[m & 1];
+        if (m > 0) s.load(buf[(m - 1) & 1], t - 1, true);
         // recompute the token's sub-states S^j and u_j, e_j
-        float Sj[NMAX][RK], u[NMAX], e[NMAX], bt[NMAX];
-        float cur[RK];
+        float Sj[NMAX][RK], u[NMAX], e[NMAX];
+        float st[RK];
 #pragma unroll
-        for (int i = 0; i < RK; ++i) cur[i] = al * ST[m][i];
+        for (int i = 0; i < RK; ++i) st[i] = cur.al * ST[m][i];
 #pragma unroll
         for (int j = 0; j < NMAX; ++j) {
           if (j < a.n) {
-            const int64_t r = t * a.n + j;
-            float kv[RK], rk;
-            s.load_row(kv, (const T *)a.k, r, a.k_st, a.k_sh, s.hk, rk);
+            float kv[RK];
+            s.row(kv, cur.k[j]);
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
-              Sj[j][i] = cur[i];
-              part = fmaf(cur[i], kv[i], part);
+              Sj[j][i] = st[i];
+              part = fmaf(st[i], kv[i], part);
             }
-            bt[j] = s.beta_of(r);
-            u[j] = s.v_of(r) - col_sum(part);
-            e[j] = bt[j] * u[j];
+            u[j] = cur.v[j] - col_sum(part);
+            e[j] = cur.b[j] * u[j];
 #pragma unroll
-            for (int i = 0; i < RK; ++i) cur[i] = fmaf(kv[i], e[j], cur[i]);
+            for (int i = 0; i < RK; ++i) st[i] = fmaf(kv[i], e[j], st[i]);
           }
         }
         // readout: o_t = scale S_t^T q_t
         {
-          float qv[RK], rq;
-          s.load_row(qv, (const T *)a.q, t, a.q_st, a.q_sh, s.hq, rq);
-          const float dov = (float)((const T *)a.dout)[t * a.do_st + (int64_t)s.h * a.do_sh + col] * a.scale;
+          float qv[RK];
+          s.row(qv, cur.q);
 #pragma unroll
           for (int i = 0; i < RK; ++i) {
-            const float dq = row_sum(cur[i] * dov);
-            if (s.c == 0) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + RK * s.rg + i, dq);
-            dS[i] = fmaf(qv[i], dov, dS[i]);
+            const float dq = row_sum(st[i] * cur.dov);
+            if (s.c == 0) red[t & 1][0][w][RK * s.rg + i] = dq;
+            dS[i] = fmaf(qv[i], cur.dov, dS[i]);
           }
         }
 #pragma unroll
         for (int j = NMAX - 1; j >= 0; --j) {
           if (j < a.n) {
             const int64_t r = t * a.n + j;
-            float kv[RK], rk;
-            s.load_row(kv, (const T *)a.k, r, a.k_st, a.k_sh, s.hk, rk);
+            float kv[RK];
+            s.row(kv, cur.k[j]);
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < RK; ++i) part = fmaf(dS[i], kv[i], part);
             const float de = col_sum(part);
-            const float du = bt[j] * de;
-            if (s.rg == 0) a.dv[r * a.dv_st + (int64_t)s.h * a.dv_sh + col] = du;
+            const float du = cur.b[j] * de;
+            if (s.rg == 0) a.dv[r * a.dv_st + (int64_t)s.h * a.dv_sh + s.col] = du;
             const float db = row_sum(de * u[j]);
-            if (s.lane == 0) atomicAdd(a.dbeta + r * a.db_st + (int64_t)s.h * a.db_sh, db);
+            if (s.lane == 0) red[t & 1][1 + j][w][K] = db;
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
               const float dk = row_sum(dS[i] * e[j] - Sj[j][i] * du);
-              if (s.c == 0) atomicAdd(a.dk + r * a.dk_st + (int64_t)s.hk * a.dk_sh + RK * s.rg + i, dk);
+              if (s.c == 0) red[t & 1][1 + j][w][RK * s.rg + i] = dk;
               dS[i] = fmaf(-kv[i], du, dS[i]);
             }
           }
@@ -235,9 +297,26 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(dS[i], ST[m][i], part);
         const float dal = xsum<1, 32>(part);
-        if (s.lane == 0) atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, dal * al);
+        if (s.lane == 0) red[t & 1][0][w][K] = dal * cur.al;
 #pragma unroll
-        for (int i = 0; i < RK; ++i) dS[i] *= al;
+        for (int i = 0; i < RK; ++i) dS[i] *= cur.al;
+        // the four V tiles' partials of this token, then one atomic per element
+        // (the other contributions: the state heads sharing a q/k head, and the
+        // other workgroups of this chain's V tiles)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int x = threadIdx.x; x < (1 + a.n) * (K + 1); x += 256) {
+          const int slot = x / (K + 1), el = x - slot * (K + 1);
+          const float sum = (red[t & 1][slot][0][el] + red[t & 1][slot][1][el]) +
+                            (red[t & 1][slot][2][el] + red[t & 1][slot][3][el]);
+          if (slot == 0) {
+            if (el < K) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sum);
+            else atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
+          } else {
+            const int64_t r = t * a.n + slot - 1;
+            if (el < K) atomicAdd(a.dk + r * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sum);
+            else atomicAdd(a.dbeta + r * a.db_st + (int64_t)s.h * a.db_sh, sum);
+          }
+        }
       }
     }
   }
@@ -276,6 +355,7 @@ __global__ void __launch_bounds__(256) gdp_l2norm_grad_kernel(NormGradArgs a) {
 }
 
 template <typename T, int K, int V> hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
+  static_assert((V / VT) % 4 == 0, "a workgroup holds four V tiles of one chain");
   const int64_t waves = (int64_t)a.N * a.Hv * (V / VT);
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL((gdp_backward_kernel<T, K, V>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
@@ -294,9 +374,7 @@ hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_
     if (K == 128 && V == 64) return launch_bwd<__bf16, 128, 64>(a, stream);
     if (K == 64 && V == 128) return launch_bwd<__bf16, 64, 128>(a, stream);
     if (K == 64 && V == 64) return launch_bwd<__bf16, 64, 64>(a, stream);
-  } else if (dtype == IN_F32) {
-    if (K == 128 && V == 128) return launch_bwd<float, 128, 128>(a, stream);
-    if (K == 128 && V == 64) return launch_bwd<float, 128, 64>(a, stream);
+  } else if (dtype == IN_F32) {  // the float32 forward serves K = 64
     if (K == 64 && V == 128) return launch_bwd<float, 64, 128>(a, stream);
     if (K == 64 && V == 64) return launch_bwd<float, 64, 64>(a, stream);
   }
