@@ -159,18 +159,24 @@ int el_type(int32_t dt) { return dt == GDP_F32 ? gdp::EL_F32 : (dt == GDP_BF16 ?
 // prefill kernels' form, the K-major initial and final states, then the
 // prefill's own workspace.
 struct FiLayout {
-  size_t glog = 0, beta = 0, s0 = 0, fin = 0, inner = 0, total = 0;
+  size_t glog = 0, beta = 0, s0 = 0, fin = 0, q = 0, k = 0, v = 0, o = 0, inner = 0, total = 0;
 };
+// float16 inputs add bfloat16 copies of q, k, v and the output (k sized for Hk = Hv)
 FiLayout fi_layout(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int32_t d, int32_t dtype,
                    bool with_initial, bool with_final) {
   FiLayout L;
   const size_t st = align256((size_t)N * Hv * d * d * 4);
+  const bool half = dtype == GDP_F16;
   L.glog = 0;
   L.beta = L.glog + align256((size_t)T * Hv * 4);
   L.s0 = L.beta + align256((size_t)T * n * Hv * 4);
   L.fin = L.s0 + (with_initial ? st : 0);
-  L.inner = L.fin + (with_final ? st : 0);
-  const size_t ws = gdp_workspace_bytes(T, N, n, Hq, Hv, d, d, dtype);
+  L.q = L.fin + (with_final ? st : 0);
+  L.k = L.q + (half ? align256((size_t)T * Hq * d * 2) : 0);
+  L.v = L.k + (half ? align256((size_t)T * n * Hv * d * 2) : 0);
+  L.o = L.v + (half ? align256((size_t)T * n * Hv * d * 2) : 0);
+  L.inner = L.o + (half ? align256((size_t)T * Hv * d * 2) : 0);
+  const size_t ws = gdp_workspace_bytes(T, N, n, Hq, Hv, d, d, GDP_BF16);
   L.total = ws ? L.inner + ws : 0;
   return L;
 }
@@ -179,7 +185,7 @@ FiLayout fi_layout(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int3
 size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int32_t d, int32_t dtype,
                               int32_t with_initial_state, int32_t output_final_state) {
   if (T < 0 || N < 0 || n < 1 || Hq < 1 || Hv < 1 || d < 1) return 0;
-  if (dtype != GDP_BF16) return 0;
+  if (dtype != GDP_BF16 && dtype != GDP_F16) return 0;
   return fi_layout(T, N, n, Hq, Hv, d, dtype, with_initial_state != 0, output_final_state != 0).total;
 }
 
@@ -203,8 +209,7 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
   if (Hq > Hv) return fail(GDP_EUNSUPPORTED, "more q heads than v heads is not served (Hq %lld, Hv %lld)",
                            (long long)Hq, (long long)Hv);
   if (v->shape[2] != d) return fail(GDP_EINVAL, "q, k and v share one head size");
-  if (q->dtype == GDP_F16) return fail(GDP_EUNSUPPORTED, "float16 q/k/v are not served yet (bfloat16 only)");
-  if (q->dtype != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q, k and v must be bfloat16");
+  if (q->dtype != GDP_BF16 && q->dtype != GDP_F16) return fail(GDP_EUNSUPPORTED, "q, k and v must be bfloat16 or float16");
   if (d != 64 && d != 128) return fail(GDP_EUNSUPPORTED, "head size must be 64 or 128");
   int rc;
   const int64_t Hk = k->shape[1];
@@ -215,6 +220,10 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
   const int64_t sk[3] = {T * n, Hk, d}, sv[3] = {T * n, Hv, d}, so[3] = {T, Hv, d};
   if ((rc = check_shape(k, "k", 3, sk)) || (rc = check_shape(v, "v", 3, sv)) || (rc = check_shape(output, "output", 3, so)))
     return rc;
+  if (q->dtype == GDP_F16 &&
+      ((q->stride[0] | q->stride[1] | k->stride[0] | k->stride[1] | v->stride[0] | v->stride[1] | output->stride[0] |
+        output->stride[1]) & 7))
+    return fail(GDP_EUNSUPPORTED, "float16 q/k/v/output need row and head strides that are multiples of 8");
   const int64_t sg[2] = {T, Hv}, sb[2] = {T * n, Hv}, sst[4] = {N, Hv, d, d};
   if (present(g)) {
     if ((rc = check_shape(g, "g", 2, sg))) return rc;
@@ -273,15 +282,36 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
     if ((e = gdp::launch_state_transpose(sa, true, (hipStream_t)stream)) != hipSuccess)
       return fail(GDP_EHIP, "state launch: %s", hipGetErrorString(e));
   }
+  // float16 inputs: bfloat16 copies of q, k, v (and an output buffer)
+  const bool half = q->dtype == GDP_F16;
+  gdp_tensor hq_t, hk_t, hv_t, ho_t;
+  const gdp_tensor *pq = q, *pk = k, *pv = v, *po = output;
+  if (half) {
+    struct { const gdp_tensor *t; size_t off; int64_t R, H; gdp_tensor *dst; } cp[3] = {
+        {q, L.q, T, Hq, &hq_t}, {k, L.k, T * n, Hk, &hk_t}, {v, L.v, T * n, Hv, &hv_t}};
+    for (auto &c : cp) {
+      gdp::HalfCopyArgs ha{c.t->data, ws + c.off, c.R, (int)c.H, (int)d, c.t->stride[0], c.t->stride[1]};
+      if ((e = gdp::launch_half_copy(ha, true, (hipStream_t)stream)) != hipSuccess)
+        return fail(GDP_EHIP, "input copy launch: %s", hipGetErrorString(e));
+      *c.dst = gdp_tensor{ws + c.off, GDP_BF16, 3, {c.R, c.H, d}, {c.H * d, d, 1}};
+    }
+    ho_t = gdp_tensor{ws + L.o, GDP_BF16, 3, {T, Hv, d}, {Hv * d, d, 1}};
+    pq = &hq_t; pk = &hk_t; pv = &hv_t; po = &ho_t;
+  }
   // the prefill in the Megatron Core convention on the restated operands
   gdp_tensor tg{ws + L.glog, GDP_F32, 2, {T, Hv}, {Hv, 1}};
   gdp_tensor tb{ws + L.beta, GDP_F32, 2, {T * n, Hv}, {Hv, 1}};
   gdp_tensor ts0{present(initial_state) ? ws + L.s0 : nullptr, GDP_F32, 4, {N, Hv, d, d}, {Hv * d * d, d * d, d, 1}};
   gdp_tensor tfin{output_final_state ? ws + L.fin : nullptr, GDP_F32, 4, {N, Hv, d, d}, {Hv * d * d, d * d, d, 1}};
-  if ((rc = gdp_chunk_prefill(q, k, v, &tg, &tb, n, cu_seqlens, scale, &ts0, output_final_state,
-                              use_qk_l2norm_in_kernel, nullptr, nullptr, 0, output, &tfin, nullptr, nullptr,
+  if ((rc = gdp_chunk_prefill(pq, pk, pv, &tg, &tb, n, cu_seqlens, scale, &ts0, output_final_state,
+                              use_qk_l2norm_in_kernel, nullptr, nullptr, 0, po, &tfin, nullptr, nullptr,
                               ws + L.inner, workspace_bytes - L.inner, stream)) != GDP_OK)
     return rc;
+  if (half) {
+    gdp::HalfCopyArgs ha{ws + L.o, output->data, T, (int)Hv, (int)d, output->stride[0], output->stride[1]};
+    if ((e = gdp::launch_half_copy(ha, false, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "output copy launch: %s", hipGetErrorString(e));
+  }
   if (output_final_state) {
     gdp::StateArgs sa;
     sa.src = ws + L.fin; sa.dst = output_state->data; sa.mats = N * Hv; sa.K = (int)d; sa.V = (int)d;

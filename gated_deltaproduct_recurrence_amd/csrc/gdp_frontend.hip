@@ -12,6 +12,10 @@
 //     kernels keep K-major [N, H, K, V] float32 states.
 // These kernels restate the operands in the prefill kernels' form (in the
 // caller's workspace) and write the final state back in the caller's layout.
+// float16 q/k/v are restated as bfloat16: the prefill kernels' products with the
+// state (kept with a lazy scale far outside float16's range) need bfloat16
+// operands, and one matrix-core product takes one operand type; the output is
+// formed in bfloat16 and converted to float16.
 // The recurrence itself runs in the prefill kernels.
 
 #include <hip/hip_runtime.h>
@@ -69,7 +73,34 @@ __global__ void __launch_bounds__(256) gdp_state_transpose_kernel(StateArgs a) {
   }
 }
 
+// Row-strided [R, H, D] copy between float16 and bfloat16 (TO_BF16: float16
+// source, contiguous bfloat16 destination; else contiguous bfloat16 source,
+// strided float16 destination).  D a multiple of 8: each thread moves 8 elements.
+template <bool TO_BF16>
+__global__ void __launch_bounds__(256) gdp_half_copy_kernel(HalfCopyArgs a) {
+  const int64_t per_row = (int64_t)a.H * a.D / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.R * per_row; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row, rem = i - r * per_row, hh = rem / (a.D / 8), d8 = rem - hh * (a.D / 8);
+    const int64_t strided = r * a.st + hh * a.sh + 8 * d8, dense = (r * a.H + hh) * a.D + 8 * d8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (TO_BF16) ((__bf16 *)a.dst)[dense + e] = (__bf16)(float)((const _Float16 *)a.src)[strided + e];
+      else ((_Float16 *)a.dst)[strided + e] = (_Float16)(float)((const __bf16 *)a.src)[dense + e];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_half_copy(const HalfCopyArgs &a, bool to_bf16, hipStream_t stream) {
+  if (a.D % 8) return hipErrorInvalidValue;
+  const int64_t total = a.R * a.H * a.D / 8;
+  if (total <= 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
+  if (to_bf16) hipLaunchKernelGGL(gdp_half_copy_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(gdp_half_copy_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gates(const GateArgs &a, hipStream_t stream) {
   const int64_t total = a.T * a.Hv * (1 + a.n);

@@ -184,6 +184,15 @@ struct StateArgs {
   int state_dtype;
 };
 hipError_t launch_state_transpose(const StateArgs &a, bool to_k_major, hipStream_t stream);
+
+// float16 <-> bfloat16 copy of a [R, H, D] tensor whose rows (st) and heads (sh)
+// may be strided on the float16 side; the bfloat16 side is contiguous.
+struct HalfCopyArgs {
+  const void *src; void *dst;
+  int64_t R; int H, D;
+  int64_t st, sh;
+};
+hipError_t launch_half_copy(const HalfCopyArgs &a, bool to_bf16, hipStream_t stream);
 hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);
 // launches the fused kernel regardless of the chain count (bf16 only)

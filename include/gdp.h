@@ -239,8 +239,9 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
  * restated as float32 log decays and betas (4 (1 + n) T Hv bytes), a float32
  * K-major copy of each state it converts (4 N Hv d^2 bytes each, when an
  * initial state is given and when the final state is requested), and the
- * workspace of the prefill it runs (gdp_workspace_bytes).  dtype is q's
- * (GDP_BF16).  Returns 0 for invalid sizes or dtypes. */
+ * workspace of the prefill it runs (gdp_workspace_bytes); with float16 inputs
+ * also bfloat16 copies of q, k, v and the output.  dtype is q's (GDP_BF16 or
+ * GDP_F16).  Returns 0 for invalid sizes or dtypes. */
 size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hq, int32_t Hv,
                               int32_t head_size, int32_t dtype, int32_t with_initial_state,
                               int32_t output_final_state);
@@ -250,9 +251,12 @@ size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int
  * parameter list, in the same order, with workspace and stream appended).
  * It computes what gdp_chunk_prefill computes; only the operands are stated
  * differently:
- *   q  [T, Hq, d], k [T*n, Hk, d] (Hk = Hq or Hv), v [T*n, Hv, d]   bfloat16, rows may
- *                  be strided; Hv a multiple of Hq (more q than v heads is
- *                  GDP_EUNSUPPORTED), d in {64, 128}
+ *   q  [T, Hq, d], k [T*n, Hk, d] (Hk = Hq or Hv), v [T*n, Hv, d]   bfloat16 or
+ *                  float16, rows may be strided; Hv a multiple of Hq (more q than v
+ *                  heads is GDP_EUNSUPPORTED), d in {64, 128}.  float16 inputs
+ *                  are copied to bfloat16 operands in the workspace (row and head
+ *                  strides must be multiples of 8) and the output, formed in
+ *                  bfloat16, is converted to float16
  *   g    [T, Hv]   the decay alpha itself (in (0, 1]), float32, bfloat16 or float16,
  *                  or data == NULL for no decay (alpha = 1)
  *   beta [T*n, Hv] float32 or q's dtype, or data == NULL for all ones
@@ -269,8 +273,7 @@ size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int
  *   workspace      device scratch of at least gdp_fi_workspace_bytes(...), 256-byte
  *                  aligned
  * Everything runs on `stream` (conversion kernels, then the prefill), with no
- * host read of device memory and no allocation, so the call is capturable.
- * float16 q/k/v are GDP_EUNSUPPORTED in this version. */
+ * host read of device memory and no allocation, so the call is capturable. */
 int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
                                   const gdp_tensor *g, const gdp_tensor *beta, int32_t num_householder,
                                   float scale, const gdp_tensor *initial_state, int32_t output_final_state,

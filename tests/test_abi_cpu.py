@@ -300,7 +300,11 @@ def test_fi_validation(b):
     a = fi_args(b)
     a["fs"] = a["fake"].tensor(b, b.GDP_F32, [2, 4, 128, 128], data=a["s0"].data)
     fi_expect(b, a, b.GDP_EALIAS, "output_state overlaps initial_state")
-    fi_expect(b, fi_args(b, dt=b.GDP_F16), b.GDP_EUNSUPPORTED, "float16")
+    fi_expect(b, fi_args(b, dt=b.GDP_F32), b.GDP_EUNSUPPORTED, "bfloat16 or float16")
+    a = fi_args(b, dt=b.GDP_F16)
+    a["q"] = a["fake"].tensor(b, b.GDP_F16, [100, 2, 128], strides=[260, 130, 1])
+    a["ws"], a["wsb"] = a["fake"].next, 1 << 34
+    fi_expect(b, a, b.GDP_EUNSUPPORTED, "multiples of 8")
     fi_expect(b, fi_args(b, Hk=3), b.GDP_EINVAL, "Hq or Hv heads")
     fi_expect(b, fi_args(b, Hq=4, Hk=4, Hv=2), b.GDP_EUNSUPPORTED, "more q heads")
     fi_expect(b, fi_args(b, d=96), b.GDP_EUNSUPPORTED, "head size")
@@ -323,7 +327,9 @@ def test_fi_workspace_bytes(b):
     base = b.gdp_workspace_bytes(100, 2, 2, 2, 4, 128, 128)
     ws = b.gdp_fi_workspace_bytes(100, 2, 2, 2, 4, 128, torch.bfloat16, True, True)
     assert ws >= base + 4 * 3 * 100 * 4 + 2 * 2 * 4 * 128 * 128 * 4
-    assert b.gdp_fi_workspace_bytes(100, 2, 2, 2, 4, 128, torch.float16) == 0
+    assert b.gdp_fi_workspace_bytes(100, 2, 2, 2, 4, 128, torch.float16) >= b.gdp_fi_workspace_bytes(
+        100, 2, 2, 2, 4, 128, torch.bfloat16) + 2 * (100 * 2 + 2 * 2 * 100 * 4 + 100 * 4) * 128
+    assert b.gdp_fi_workspace_bytes(100, 2, 2, 2, 4, 128, torch.float32) == 0
 
 
 def test_prefill_accepts_k_per_state_head(b):

@@ -50,6 +50,11 @@ CASES = [
     ([130, 65], 1, 1, 2, 2, 64, torch.float16, None, (0.0, None), False),
     ([33, 0, 200], 2, 1, 1, 2, 64, None, torch.float32, (0.2, torch.float32), True),
 ]
+# float16 q/k/v (restated as bfloat16 operands; beta in q's dtype)
+HALF_CASES = [
+    ([37, 64, 200, 511], 2, 2, 2, 4, 128, torch.float16, torch.float16, (0.1, torch.float32), True),
+    ([150, 3, 97], 3, 2, 4, 4, 64, torch.float32, None, (0.0, None), False),
+]
 PATHS = ["fused", "split", "segmented"]
 
 
@@ -63,6 +68,18 @@ def test_flashinfer_parity(gdp, ci, kpath, monkeypatch):
     o, f, ref = run_both(gdp, inp, state_dtype=sdt or torch.float32)
     e1, e2 = rel_err(to_np(o), ref["o"]), rel_err(to_np(f), ref["final_state"])
     assert e1 <= TOL and e2 <= TOL, f"case {ci} {kpath}: o {e1:.3e} final state {e2:.3e}"
+
+
+@pytest.mark.parametrize("ci", range(len(HALF_CASES)))
+def test_flashinfer_float16_inputs(gdp, ci):
+    lens, n, Hq, Hk, Hv, d, gdt, bdt, (istd, sdt), l2 = HALF_CASES[ci]
+    inp = workloads.flashinfer_batch(lens, n, Hq, Hk, Hv, d, dtype=torch.float16, g_dtype=gdt, beta_dtype=bdt,
+                                     init_std=istd, state_dtype=sdt or torch.float32, l2norm_in_kernel=l2,
+                                     g_shift=1.0, seed=50 + ci)
+    o, f, ref = run_both(gdp, inp, state_dtype=sdt or torch.float32)
+    assert o.dtype == torch.float16
+    e1, e2 = rel_err(to_np(o), ref["o"]), rel_err(to_np(f), ref["final_state"])
+    assert e1 <= TOL and e2 <= TOL, f"half case {ci}: o {e1:.3e} final state {e2:.3e}"
 
 
 def test_flashinfer_no_final_state_and_scale(gdp):
