@@ -1102,7 +1102,9 @@ template <int K, int V> struct FusedSmem {
   int qsafe[2];                   // the token chunk's decay cumsum stays above -100 (base 2)
 };
 
-template <int K, int V, int NCW>
+// SUM: segment summaries only (the states of the segmented path): no outputs,
+// so the scores, P, O^T, the q rows and the per-row token tables are skipped.
+template <int K, int V, int NCW, bool SUM>
 __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArgs a) {
   using S = FusedSmem<K, V>;
   // NCW consumer waves of 16 NB state columns each cover all V columns; the
@@ -1255,10 +1257,12 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         };
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) load_kf(0, a4);
-        load_qw(0, 0);
+        if constexpr (!SUM) load_qw(0, 0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          if (s + 1 < KS) load_qw(s + 1, (s + 1) & 1);
+          if constexpr (!SUM) {
+            if (s + 1 < KS) load_qw(s + 1, (s + 1) & 1);
+          }
           __builtin_amdgcn_sched_barrier(0);
           Frag<bf16> Sb[NB];
 #pragma unroll
@@ -1267,22 +1271,26 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
-            if (a4 >= rb0 && a4 < rb0 + RBW)
-              Pacc[a4 - rb0] = mma(kf[a4], qw[s & 1], s == 0 ? zero4() : Pacc[a4 - rb0]);
+            if constexpr (!SUM) {
+              if (a4 >= rb0 && a4 < rb0 + RBW)
+                Pacc[a4 - rb0] = mma(kf[a4], qw[s & 1], s == 0 ? zero4() : Pacc[a4 - rb0]);
+            }
             if (s + 1 < KS) load_kf(s + 1, a4);
           }
-          if (qnorm) qss += seg_sumsq<bf16>(__builtin_bit_cast(uint4, qw[s & 1].v));
+          if constexpr (!SUM) {
+            if (qnorm) qss += seg_sumsq<bf16>(__builtin_bit_cast(uint4, qw[s & 1].v));
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       // q-row rstd of the wave's 16 tokens (the four lanes lg of a row hold a
       // quarter each); the outputs of token chunk c take it when staged
-      if (qnorm) {
+      if (!SUM && qnorm) {
         qss += __shfl_xor(qss, 16, 64);
         qss += __shfl_xor(qss, 32, 64);
         if (lg == 0) sm.rq[qs][16 * tb + lr] = frsq(qss + 1e-6f);
       }
-      if (j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
+      if (!SUM && j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
         Frag<bf16> qf[2][4];
         auto load_q = [&](int s, int buf) {
           const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
@@ -1304,7 +1312,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (j == 0) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
+      if (!SUM && j == 0) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const float f = lam * qfac[16 * a4 + lr];
@@ -1317,7 +1325,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // When the token chunk's decay cumsum stays above -100 the decay factor is
       // the product qfac_t rkg_r of per-token and per-row factors (both finite and
       // normal); otherwise it is formed per entry.
-      {
+      if constexpr (!SUM) {
         const int t = 16 * tb + lr;
         const int rlim = n * (t + 1) - CH * j;
         const bool fact = sm.qsafe[qs] != 0;
@@ -1403,7 +1411,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
       // while E forms: the P fragments of the first token block and the k^T
       // fragments of the first state row block
-      const int tokb0 = tokr[0], tokb1 = tokr[32];
+      const int tokb0 = SUM ? 0 : tokr[0], tokb1 = SUM ? 0 : tokr[32];
       Frag<bf16> pf[2][2];
       const uint32_t pr = off_of(sm.p) + lp;
       auto load_pf = [&](int a4, int buf) {  // P rows of token block a4
@@ -1412,7 +1420,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           pf[buf][s].v = __builtin_shufflevector(rd8(pr + (16 * a4 * LDC + 32 * s) * 2), rd8(pr + (16 * a4 * LDC + 32 * s + 16) * 2),
                                                  0, 1, 2, 3, 4, 5, 6, 7);
       };
-      load_pf(0, 0);
+      if constexpr (!SUM) load_pf(0, 0);
       const uint32_t kcb = kt + lcolk.l;
       Frag<bf16> kc[2][2];
       auto load_kc = [&](int at, int buf) {  // lane lr of tile at: key kap(at, lr / 4, lr % 4)
@@ -1424,6 +1432,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       load_kc(0, 0);
       __builtin_amdgcn_sched_barrier(0);
       Frag<bf16> Eb[2][NB];
+      if constexpr (!SUM) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1439,6 +1448,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           for (int b = 0; b < NB; ++b) O[b][a4] = mma(Eb[s][b], pf[a4 & 1][s], O[b][a4]);
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
       }
       // Sst += K^T diag(2^(G_last - G) rk / (lam 2^G_last)) E and lam *= 2^G_last, unless
       // lam would fall below LAM_MIN (then Sst is rescaled to lam = 1)
@@ -1480,7 +1490,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // and P; the q-row rstd rq_t multiplies every term of row t and is applied here).
       // They are staged in bf16 in this chunk's v tile (unused after the R step)
       // and helper 3 stores whole rows from there in the next chunk.
-      if ((j == n - 1 || e == nexp - 1) && a.o) {
+      if (!SUM && (j == n - 1 || e == nexp - 1) && a.o) {
         char *stg = sm.v[ts];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
@@ -1794,8 +1804,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         if (!part1) load_v(0, voffs);
         load_scalars(0);
         if (nexp > 1) load_scalars(1);
-        load_q(0, qoffs);
-        if (ntc > 1) load_q(1, qoffs);
+        if constexpr (!SUM) {
+          load_q(0, qoffs);
+          if (ntc > 1) load_q(1, qoffs);
+        }
         wait_vm();
         lds_barrier();
         lds_barrier();
@@ -1818,7 +1830,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         // the q rows when n >= 2 (they are read at the end of token chunk c+1; a
         // later wait for newer loads covers them): the consumers read the v rows
         // after the next barrier and the Gram stage the k rows of chunk e+2.
-        const bool lq = j == n - 1 && c + 2 < ntc;
+        const bool lq = !SUM && j == n - 1 && c + 2 < ntc;
         if (e + 1 < nexp && !part1) load_v(e + 1, voffs);
         if (lq) load_q(c + 2, qoffs);
         if (lq && n >= 2) {
@@ -1847,7 +1859,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       if (nexp > 0) {
         lds_barrier();
         prep_scalars(0);
-        finish_q(0);
+        if constexpr (!SUM) finish_q(0);
         gram(0, 0, 5, 3);
         lds_barrier();
         block(0, IC<0>{});
@@ -1864,7 +1876,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
         // token chunk c+1: its q rows landed with the loads of a chunk before
         // (n >= 2) or before the last barrier (n = 1)
-        if (j == n - 1 && c + 1 < ntc) finish_q(c + 1);
+        if (!SUM && j == n - 1 && c + 1 < ntc) finish_q(c + 1);
         lds_barrier();
         if (e + 1 < nexp) {
           block(e + 1, IC<0>{});
@@ -1878,7 +1890,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         gram(0, 5, 10, 4);
         lds_barrier();
         block(0, IC<2>{});
-        tables(0);
+        if constexpr (!SUM) tables(0);
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
@@ -1888,7 +1900,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         lds_barrier();
         if (e + 1 < nexp) {
           block(e + 1, IC<2>{});
-          tables(e + 1);  // needs the k-row norms from the Gram stage
+          if constexpr (!SUM) tables(e + 1);  // needs the k-row norms from the Gram stage
         }
         lds_barrier();
       }
@@ -2018,7 +2030,7 @@ hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
   constexpr int NCW = 4;
   const int64_t blocks = (int64_t)a.N * a.Hv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
+  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW, false>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -2027,7 +2039,7 @@ hipError_t launch_fused_twice(const PrefillArgs &a, hipStream_t stream) {
   constexpr int NCW = 4;
   const int64_t blocks = 2 * (int64_t)a.N * a.Hv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
+  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW, true>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
   return hipGetLastError();
 }
 
