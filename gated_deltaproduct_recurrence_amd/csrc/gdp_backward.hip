@@ -23,13 +23,15 @@
 // block backwards.  One wave owns one (sequence, state head, 8-column V tile):
 // lane (c, rg) = (lane / 8, lane % 8) holds rows 16 rg .. 16 rg + 15 (K = 128;
 // 8 rows for K = 64) of column c, so a column dot over K (on the recurrence's
-// critical path) is a sum over 8 adjacent lanes, done with DPP moves, and a row
-// sum over the tile's columns one over the 8 lanes of equal rg, by lane
-// exchanges.  Gradients shared by several waves (dq, dk:
-// all V tiles and the state heads of a q/k head; dbeta, dg_log: all V tiles)
-// are accumulated with float atomics into zeroed buffers, after the four waves
-// of a workgroup (four adjacent V tiles of one chain, in lockstep token by
-// token) have summed theirs in LDS.
+// critical path) is a sum over 8 adjacent lanes, done with DPP moves.  Sums over
+// the tile's 8 columns (lane bits 3 .. 5) stay in the VALU too: the 16 row
+// entries of a dq or dk partial are reduce-scattered over those lanes with the
+// gfx950 half-wave and row swaps and a DPP row rotation, so that each lane ends
+// with two finished entries.  Gradients shared by several waves (dq, dk: all V
+// tiles and the state heads of a q/k head; dbeta, dg_log: all V tiles) are
+// summed over the four waves of a workgroup (four adjacent V tiles of one chain)
+// with LDS float atomics, for a whole 8-token block, and then added to the zeroed
+// output buffers with one float atomic per element and block.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -65,26 +67,66 @@ __device__ __forceinline__ float col_sum(float x) {
   x += dpp_mov<0x141>(x);  // row_half_mirror
   return x;
 }
-__device__ __forceinline__ float row_sum(float x) { return xsum<8, 32>(x); }  // over the 8 columns
+// x + the value of the lane whose index differs in bit 5 (W32) or bit 4, for
+// the pair (x, y): the half-wave (row) swap leaves (own x, partner's x) in the
+// lanes with the bit clear and (partner's y, own y) in the others
+template <bool W32> __device__ __forceinline__ float swap_add(float x, float y) {
+  const uint32_t ux = __builtin_bit_cast(uint32_t, x), uy = __builtin_bit_cast(uint32_t, y);
+  uint32_t r0, r1;
+  if constexpr (W32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(ux, uy, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(ux, uy, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+// sum over the 8 columns of the tile (lane bits 3 .. 5), in every lane
+__device__ __forceinline__ float row_all(float x) {
+  x = swap_add<true>(x, x);
+  x = swap_add<false>(x, x);
+  return x + dpp_mov<0x128>(x);  // row_ror:8, i.e. the lane with bit 3 flipped
+}
+// Reduce-scatter over the 8 columns: v holds the lane's R row entries of one
+// column; afterwards out[p] is, in lane (c, rg), the sum over the columns of
+// entry (R / 8) c + p.  Each stage halves the entries: the lanes with the stage's
+// lane bit clear keep the lower half, the others the upper half.
+template <int R> __device__ __forceinline__ void row_scatter(const float (&v)[R], float (&out)[R / 8], bool bit3) {
+  float a[R / 2], b[R / 4];
+#pragma unroll
+  for (int p = 0; p < R / 2; ++p) a[p] = swap_add<true>(v[p], v[p + R / 2]);
+#pragma unroll
+  for (int p = 0; p < R / 4; ++p) b[p] = swap_add<false>(a[p], a[p + R / 4]);
+#pragma unroll
+  for (int p = 0; p < R / 8; ++p) {
+    const float keep = bit3 ? b[p + R / 8] : b[p], send = bit3 ? b[p] : b[p + R / 8];
+    out[p] = keep + dpp_mov<0x128>(send);
+  }
+}
 
 template <typename T, int K, int V> struct Bwd {
   static constexpr int RK = K / 8;                     // rows per lane
   static constexpr int RW = RK * (int)sizeof(T) / 16;  // 16-byte words holding them
   static_assert(RW >= 1, "at least one 16-byte word per lane");
-  // the inputs of one token (loaded a token ahead of their use): the lane's RK
-  // entries of the token's k rows (and q row) as loaded, its v, beta, decay and
-  // output gradient
+  // the inputs of one token (loaded a token ahead of their use), all as loaded
+  // (converted where used, so that the loads stay in flight): the lane's RK
+  // entries of the token's k rows (and q row), its beta, log decay, v and output
+  // gradient
   struct In {
     uint4 k[NMAX][RW];
     uint4 q[RW];
-    float v[NMAX], b[NMAX], al, dov;
+    float b[NMAX], g;
+    T v[NMAX], dov;
   };
   const BwdArgs &a;
   int seq, h, hq, hk, vt, lane, rg, c, col;
   __device__ Bwd(const BwdArgs &args) : a(args) {}
 
   __device__ __forceinline__ void load(In &x, int64_t t, bool with_q) const {
-    x.al = __builtin_amdgcn_exp2f(a.g[t * a.g_st + (int64_t)h * a.g_sh] * LOG2E_B);
+    x.g = a.g[t * a.g_st + (int64_t)h * a.g_sh];
 #pragma unroll
     for (int j = 0; j < NMAX; ++j) {
       if (j < a.n) {
@@ -93,14 +135,14 @@ template <typename T, int K, int V> struct Bwd {
 #pragma unroll
         for (int i = 0; i < RW; ++i) x.k[j][i] = p[i];
         x.b[j] = a.beta[r * a.b_st + (int64_t)h * a.b_sh];
-        x.v[j] = (float)((const T *)a.v)[r * a.v_st + (int64_t)h * a.v_sh + col];
+        x.v[j] = ((const T *)a.v)[r * a.v_st + (int64_t)h * a.v_sh + col];
       }
     }
     if (with_q) {
       const uint4 *p = (const uint4 *)((const T *)a.q + t * a.q_st + (int64_t)hq * a.q_sh + RK * rg);
 #pragma unroll
       for (int i = 0; i < RW; ++i) x.q[i] = p[i];
-      x.dov = (float)((const T *)a.dout)[t * a.do_st + (int64_t)h * a.do_sh + col] * a.scale;
+      x.dov = ((const T *)a.dout)[t * a.do_st + (int64_t)h * a.do_sh + col];
     }
   }
   // a row in float, L2-normalised over all K entries when asked
@@ -125,9 +167,11 @@ template <typename T, int K, int V> struct Bwd {
     }
   }
   // one token forward on the lane's part of S
+  __device__ __forceinline__ static float decay(const In &x) { return __builtin_amdgcn_exp2f(x.g * LOG2E_B); }
   __device__ __forceinline__ void step(float (&S)[RK], const In &x) const {
+    const float al = decay(x);
 #pragma unroll
-    for (int i = 0; i < RK; ++i) S[i] *= x.al;
+    for (int i = 0; i < RK; ++i) S[i] *= al;
 #pragma unroll
     for (int j = 0; j < NMAX; ++j) {
       if (j < a.n) {
@@ -136,7 +180,7 @@ template <typename T, int K, int V> struct Bwd {
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(S[i], kv[i], part);
-        const float e = x.b[j] * (x.v[j] - col_sum(part));
+        const float e = x.b[j] * ((float)x.v[j] - col_sum(part));
 #pragma unroll
         for (int i = 0; i < RK; ++i) S[i] = fmaf(kv[i], e, S[i]);
       }
@@ -151,11 +195,10 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   constexpr int RK = B::RK, NVT = V / VT;
   // per wave: the state entering each 8-token block of the chunk (64 tokens)
   __shared__ float ck[4][CH / BLK][RK * 64];
-  // per token, double-buffered by token parity: the four waves' partial dq and
-  // dk rows (slot 0: dq, 1 + j: dk of row j) and, in column K, their partial
-  // dg_log (slot 0) and dbeta (slot 1 + j); summed after one barrier, then one
-  // atomic per element
-  __shared__ float red[2][NMAX + 1][4][K + 4];
+  // per token of the current 8-token block, the sums over the four waves of the
+  // dq row (slot 0) and the dk rows (slot 1 + j) and, in column K, of dg_log
+  // (slot 0) and dbeta (slot 1 + j); zero between blocks
+  __shared__ float acc[BLK][NMAX + 1][K + 1];
   B s(a);
   const int w = threadIdx.x >> 6;
   s.lane = threadIdx.x & 63;
@@ -178,6 +221,9 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   const size_t hoff = (size_t)s.h * KV + (size_t)(RK * s.rg) * V + s.col;  // within one [Hv, K, V] state; + i * V
   const size_t soff = (size_t)s.seq * a.Hv * KV + hoff;
   float *my_ck = &ck[w][0][0];
+  const bool bit3 = (s.lane >> 3) & 1;
+  for (int x = threadIdx.x; x < BLK * (NMAX + 1) * (K + 1); x += 256) (&acc[0][0][0])[x] = 0.f;
+  __syncthreads();
 
   float dS[RK];
 #pragma unroll
@@ -238,10 +284,11 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
         In &cur = buf[m & 1];
         if (m > 0) s.load(buf[(m - 1) & 1], t - 1, true);
         // recompute the token's sub-states S^j and u_j, e_j
+        const float al = B::decay(cur);
         float Sj[NMAX][RK], u[NMAX], e[NMAX];
         float st[RK];
 #pragma unroll
-        for (int i = 0; i < RK; ++i) st[i] = cur.al * ST[m][i];
+        for (int i = 0; i < RK; ++i) st[i] = al * ST[m][i];
 #pragma unroll
         for (int j = 0; j < NMAX; ++j) {
           if (j < a.n) {
@@ -253,22 +300,27 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
               Sj[j][i] = st[i];
               part = fmaf(st[i], kv[i], part);
             }
-            u[j] = cur.v[j] - col_sum(part);
+            u[j] = (float)cur.v[j] - col_sum(part);
             e[j] = cur.b[j] * u[j];
 #pragma unroll
             for (int i = 0; i < RK; ++i) st[i] = fmaf(kv[i], e[j], st[i]);
           }
         }
         // readout: o_t = scale S_t^T q_t
+        float *acc_m = &acc[m][0][0];
+        const int el0 = RK * s.rg + (RK / 8) * s.c;  // the row entries this lane finishes
         {
-          float qv[RK];
+          const float dov = (float)cur.dov * a.scale;
+          float qv[RK], pq[RK], oq[RK / 8];
           s.row(qv, cur.q);
 #pragma unroll
           for (int i = 0; i < RK; ++i) {
-            const float dq = row_sum(st[i] * cur.dov);
-            if (s.c == 0) red[t & 1][0][w][RK * s.rg + i] = dq;
-            dS[i] = fmaf(qv[i], cur.dov, dS[i]);
+            pq[i] = st[i] * dov;
+            dS[i] = fmaf(qv[i], dov, dS[i]);
           }
+          row_scatter<RK>(pq, oq, bit3);
+#pragma unroll
+          for (int p = 0; p < RK / 8; ++p) atomicAdd(acc_m + el0 + p, oq[p]);
         }
 #pragma unroll
         for (int j = NMAX - 1; j >= 0; --j) {
@@ -279,45 +331,52 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < RK; ++i) part = fmaf(dS[i], kv[i], part);
-            const float de = col_sum(part);
+            const float de = col_sum(part);  // equal in the column's 8 lanes
             const float du = cur.b[j] * de;
-            if (s.rg == 0) a.dv[r * a.dv_st + (int64_t)s.h * a.dv_sh + s.col] = du;
-            const float db = row_sum(de * u[j]);
-            if (s.lane == 0) red[t & 1][1 + j][w][K] = db;
+            a.dv[r * a.dv_st + (int64_t)s.h * a.dv_sh + s.col] = du;
+            const float db = row_all(de * u[j]);
+            if (s.lane == 0) atomicAdd(acc_m + (1 + j) * (K + 1) + K, db);
+            float pk[RK], ok[RK / 8];
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
-              const float dk = row_sum(dS[i] * e[j] - Sj[j][i] * du);
-              if (s.c == 0) red[t & 1][1 + j][w][RK * s.rg + i] = dk;
+              pk[i] = fmaf(dS[i], e[j], -Sj[j][i] * du);
               dS[i] = fmaf(-kv[i], du, dS[i]);
             }
+            row_scatter<RK>(pk, ok, bit3);
+#pragma unroll
+            for (int p = 0; p < RK / 8; ++p) atomicAdd(acc_m + (1 + j) * (K + 1) + el0 + p, ok[p]);
           }
         }
         // decay
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(dS[i], ST[m][i], part);
-        const float dal = xsum<1, 32>(part);
-        if (s.lane == 0) red[t & 1][0][w][K] = dal * cur.al;
+        const float dal = row_all(col_sum(part));
+        if (s.lane == 0) atomicAdd(acc_m + K, dal * al);
 #pragma unroll
-        for (int i = 0; i < RK; ++i) dS[i] *= cur.al;
-        // the four V tiles' partials of this token, then one atomic per element
-        // (the other contributions: the state heads sharing a q/k head, and the
-        // other workgroups of this chain's V tiles)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        for (int x = threadIdx.x; x < (1 + a.n) * (K + 1); x += 256) {
-          const int slot = x / (K + 1), el = x - slot * (K + 1);
-          const float sum = (red[t & 1][slot][0][el] + red[t & 1][slot][1][el]) +
-                            (red[t & 1][slot][2][el] + red[t & 1][slot][3][el]);
-          if (slot == 0) {
-            if (el < K) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sum);
-            else atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
-          } else {
-            const int64_t r = t * a.n + slot - 1;
-            if (el < K) atomicAdd(a.dk + r * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sum);
-            else atomicAdd(a.dbeta + r * a.db_st + (int64_t)s.h * a.db_sh, sum);
-          }
+        for (int i = 0; i < RK; ++i) dS[i] *= al;
+      }
+      // the block's sums over the four waves, then one atomic per element (the
+      // other contributions: the state heads sharing a q/k head, and the other
+      // workgroups of this chain's V tiles); acc is left zero
+      __syncthreads();
+      const int per_tok = (1 + a.n) * (K + 1);
+      for (int x = threadIdx.x; x < nb * per_tok; x += 256) {
+        const int m = x / per_tok, rem = x - m * per_tok, slot = rem / (K + 1), el = rem - slot * (K + 1);
+        float *cell = &acc[m][slot][el];
+        const float sum = *cell;
+        *cell = 0.f;
+        const int64_t t = tbb + m;
+        if (slot == 0) {
+          if (el < K) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sum);
+          else atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
+        } else {
+          const int64_t r = t * a.n + slot - 1;
+          if (el < K) atomicAdd(a.dk + r * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sum);
+          else atomicAdd(a.dbeta + r * a.db_st + (int64_t)s.h * a.db_sh, sum);
         }
       }
+      __syncthreads();
     }
   }
   if (a.ds0) {
