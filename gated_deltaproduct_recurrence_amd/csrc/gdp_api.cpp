@@ -609,7 +609,7 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
 
 namespace {
 struct BwdLayout {
-  size_t desc = 0, cs = 0, o = 0, fwd = 0, total = 0;
+  size_t desc = 0, cs = 0, o = 0, rn = 0, fwd = 0, total = 0;
   int64_t nt_cap = 0, ntdp_cap = 0;
 };
 BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V, int32_t dtype) {
@@ -620,7 +620,9 @@ BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, i
   L.desc = 0;
   L.cs = L.desc + desc_bytes(N, L.nt_cap, L.ntdp_cap);
   L.o = L.cs + align256((size_t)(L.nt_cap > 0 ? L.nt_cap : 1) * Hv * K * V * 4);
-  L.fwd = L.o + align256((size_t)T * Hv * V * elem_size(dtype));
+  L.rn = L.o + align256((size_t)T * Hv * V * elem_size(dtype));
+  // the rows' norm factors: q [T, Hqk], k [T*n, Hk <= Hv], then one float 1
+  L.fwd = L.rn + align256((size_t)T * Hqk * 4) + align256((size_t)T * n * Hv * 4) + 256;
   L.total = L.fwd + fwd;
   return L;
 }
@@ -724,8 +726,31 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
     if ((e = gdp::launch_fill((int32_t *)t->data, cnt, 0, (hipStream_t)stream)) != hipSuccess)
       return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
   }
+  // the rows' L2-norm factors (or a single 1 read with zero strides)
+  float *rq = (float *)(ws + L.rn), *rk = (float *)(ws + L.rn + align256((size_t)T * Hqk * 4));
+  float *one = (float *)(ws + L.fwd - 256);
+  const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
+  if (use_qk_l2norm) {
+    gdp::NormGradArgs ra;
+    ra.x = q->data; ra.x_st = q->stride[0]; ra.x_sh = q->stride[1];
+    ra.g = rq; ra.g_st = Hqk; ra.g_sh = 1; ra.rows = T * Hqk; ra.heads = (int)Hqk;
+    if ((e = gdp::launch_row_norm(ra, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "row norm launch: %s", hipGetErrorString(e));
+    ra.x = k->data; ra.x_st = k->stride[0]; ra.x_sh = k->stride[1];
+    ra.g = rk; ra.g_st = Hk; ra.rows = T * n * Hk; ra.heads = (int)Hk;
+    if ((e = gdp::launch_row_norm(ra, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "row norm launch: %s", hipGetErrorString(e));
+  } else if ((e = gdp::launch_fill((int32_t *)one, 1, 0x3f800000, (hipStream_t)stream)) != hipSuccess) {
+    return fail(GDP_EHIP, "fill launch: %s", hipGetErrorString(e));
+  }
   gdp::BwdArgs a;
   std::memset(&a, 0, sizeof a);
+  if (use_qk_l2norm) {
+    a.rq = rq; a.rq_st = Hqk; a.rq_sh = 1;
+    a.rk = rk; a.rk_st = Hk; a.rk_sh = 1;
+  } else {
+    a.rq = one; a.rk = one;  // zero strides
+  }
   a.q = q->data; a.q_st = q->stride[0]; a.q_sh = q->stride[1];
   a.k = k->data; a.k_st = k->stride[0]; a.k_sh = k->stride[1];
   a.v = v->data; a.v_st = v->stride[0]; a.v_sh = v->stride[1];
@@ -734,7 +759,6 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   a.cu = cu_seqlens->data; a.cu_is64 = cu_seqlens->dtype == GDP_I64;
   a.T = T; a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv; a.Hk = (int)Hk;
   a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
-  a.l2norm = use_qk_l2norm ? 1 : 0;
   a.chunk_states = (const float *)(ws + L.cs);
   a.chunk_offsets = d.chunk_offsets;
   a.dout = d_o->data; a.do_st = d_o->stride[0]; a.do_sh = d_o->stride[1];
@@ -745,7 +769,6 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   a.dg = (float *)dg_log->data; a.dg_st = dg_log->stride[0]; a.dg_sh = dg_log->stride[1];
   a.dbeta = (float *)dbeta->data; a.db_st = dbeta->stride[0]; a.db_sh = dbeta->stride[1];
   a.ds0 = present(d_initial_state) ? (float *)d_initial_state->data : nullptr;
-  const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
   if ((e = gdp::launch_backward(a, idt, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
     return fail(GDP_EHIP, "backward launch: %s", hipGetErrorString(e));
   if (use_qk_l2norm) {

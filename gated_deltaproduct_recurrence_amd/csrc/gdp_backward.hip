@@ -13,8 +13,9 @@
 //     for j = n-1 .. 0:  de = dS^T k_j;  du = beta_j de;  dv_j = du;
 //                        dbeta_j = de . u_j;  dk_j = dS e_j - S^j du;  dS -= k_j du^T
 //     dalpha_t = <dS, S_{t-1}>,  dg_log_t = alpha_t dalpha_t;  dS <- alpha_t dS.
-// (k and q here are the L2-normalised rows when the in-kernel norm is on; the
-// finalize kernel maps their gradients back to the raw rows.)
+// (k and q here are the L2-normalised rows when the in-kernel norm is on: a
+// pre-pass stores each row's norm factor, which scales the products with the
+// stored row; a last kernel maps the q and k gradients back to the raw rows.)
 //
 // The states S_{t-1} are recomputed: the forward pass leaves the state entering
 // every 64-token chunk (return_chunk_states); per chunk this kernel re-runs the
@@ -107,34 +108,42 @@ template <int R> __device__ __forceinline__ void row_scatter(const float (&v)[R]
   }
 }
 
-template <typename T, int K, int V> struct Bwd {
+template <typename T, int K, int V, int NH> struct Bwd {
   static constexpr int RK = K / 8;                     // rows per lane
   static constexpr int RW = RK * (int)sizeof(T) / 16;  // 16-byte words holding them
   static_assert(RW >= 1, "at least one 16-byte word per lane");
   // the inputs of one token (loaded a token ahead of their use), all as loaded
   // (converted where used, so that the loads stay in flight): the lane's RK
-  // entries of the token's k rows (and q row), its beta, log decay, v and output
-  // gradient
+  // entries of the token's k rows (and q row), the rows' L2-norm factors (1
+  // without the norm), its beta, log decay, v and output gradient
   struct In {
-    uint4 k[NMAX][RW];
+    uint4 k[NH][RW];
     uint4 q[RW];
-    float b[NMAX], g;
-    T v[NMAX], dov;
+    float rk[NH], rq, b[NH], g;
+    T v[NH], dov;
   };
   const BwdArgs &a;
   int seq, h, hq, hk, vt, lane, rg, c, col;
   __device__ Bwd(const BwdArgs &args) : a(args) {}
 
+  // the loads of one token, issued where called: the scheduling barrier keeps
+  // the compiler from sinking them towards their use, which would undo the
+  // prefetch
   __device__ __forceinline__ void load(In &x, int64_t t, bool with_q) const {
+    load_(x, t, with_q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void load_(In &x, int64_t t, bool with_q) const {
     x.g = a.g[t * a.g_st + (int64_t)h * a.g_sh];
 #pragma unroll
-    for (int j = 0; j < NMAX; ++j) {
-      if (j < a.n) {
-        const int64_t r = t * a.n + j;
+    for (int j = 0; j < NH; ++j) {
+      if (j < NH) {
+        const int64_t r = t * NH + j;
         const uint4 *p = (const uint4 *)((const T *)a.k + r * a.k_st + (int64_t)hk * a.k_sh + RK * rg);
 #pragma unroll
         for (int i = 0; i < RW; ++i) x.k[j][i] = p[i];
         x.b[j] = a.beta[r * a.b_st + (int64_t)h * a.b_sh];
+        x.rk[j] = a.rk[r * a.rk_st + (int64_t)hk * a.rk_sh];
         x.v[j] = ((const T *)a.v)[r * a.v_st + (int64_t)h * a.v_sh + col];
       }
     }
@@ -143,9 +152,11 @@ template <typename T, int K, int V> struct Bwd {
 #pragma unroll
       for (int i = 0; i < RW; ++i) x.q[i] = p[i];
       x.dov = ((const T *)a.dout)[t * a.do_st + (int64_t)h * a.do_sh + col];
+      x.rq = a.rq[t * a.rq_st + (int64_t)hq * a.rq_sh];
     }
   }
-  // a row in float, L2-normalised over all K entries when asked
+  // the lane's entries of a row in float, as stored (the norm factor is
+  // applied to the products with the row)
   __device__ __forceinline__ void row(float (&o)[RK], const uint4 (&x)[RW]) const {
 #pragma unroll
     for (int i = 0; i < RK; ++i) {
@@ -157,14 +168,6 @@ template <typename T, int K, int V> struct Bwd {
       o[i] = (sizeof(T) == 4) ? __builtin_bit_cast(float, u32)
                               : __builtin_bit_cast(float, (e & 1) ? (u32 & 0xFFFF0000u) : (u32 << 16));
     }
-    if (a.l2norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < RK; ++i) ss = fmaf(o[i], o[i], ss);
-      const float rs = __builtin_amdgcn_rsqf(col_sum(ss) + 1e-6f);
-#pragma unroll
-      for (int i = 0; i < RK; ++i) o[i] *= rs;
-    }
   }
   // one token forward on the lane's part of S
   __device__ __forceinline__ static float decay(const In &x) { return __builtin_amdgcn_exp2f(x.g * LOG2E_B); }
@@ -173,32 +176,42 @@ template <typename T, int K, int V> struct Bwd {
 #pragma unroll
     for (int i = 0; i < RK; ++i) S[i] *= al;
 #pragma unroll
-    for (int j = 0; j < NMAX; ++j) {
-      if (j < a.n) {
+    for (int j = 0; j < NH; ++j) {
+      if (j < NH) {
         float kv[RK];
         row(kv, x.k[j]);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(S[i], kv[i], part);
-        const float e = x.b[j] * ((float)x.v[j] - col_sum(part));
+        const float e = x.b[j] * ((float)x.v[j] - x.rk[j] * col_sum(part));
+        const float ek = e * x.rk[j];
 #pragma unroll
-        for (int i = 0; i < RK; ++i) S[i] = fmaf(kv[i], e, S[i]);
+        for (int i = 0; i < RK; ++i) S[i] = fmaf(kv[i], ek, S[i]);
       }
     }
   }
 };
 
-template <typename T, int K, int V>
+template <typename T, int K, int V, int NH>
 __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
-  using B = Bwd<T, K, V>;
+  using B = Bwd<T, K, V, NH>;
   using In = typename B::In;
   constexpr int RK = B::RK, NVT = V / VT;
+  // tokens in flight in the forward passes (two where the rows take more registers)
+  constexpr int PF = RK * NH > 32 ? 2 : 4;
   // per wave: the state entering each 8-token block of the chunk (64 tokens)
   __shared__ float ck[4][CH / BLK][RK * 64];
-  // per token of the current 8-token block, the sums over the four waves of the
-  // dq row (slot 0) and the dk rows (slot 1 + j) and, in column K, of dg_log
-  // (slot 0) and dbeta (slot 1 + j); zero between blocks
-  __shared__ float acc[BLK][NMAX + 1][K + 1];
+  // per token of the current group of F tokens: each wave's finished entries of
+  // the dq row (slot 0) and the dk rows (slot 1 + j), summed over the four waves
+  // when the group is flushed (sized so that the checkpoints and these fit in LDS)
+  constexpr int F = K == 64 ? 8 : (NH <= 2 ? 4 : 2);
+  __shared__ float wsl[F][NH + 1][4][K];
+  // per token of the block and wave, the wave's dg_log (slot 0) and dbeta
+  // (slot 1 + j) partials, summed over the waves at the flush
+  __shared__ float scal[BLK][NH + 1][4];
+  // per token of the block, dv of the workgroup's 4 x 8 columns (written by
+  // the wave owning the column, stored with the block's flush)
+  __shared__ float dvs[BLK][NH][4 * VT];
   B s(a);
   const int w = threadIdx.x >> 6;
   s.lane = threadIdx.x & 63;
@@ -222,15 +235,13 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   const size_t soff = (size_t)s.seq * a.Hv * KV + hoff;
   float *my_ck = &ck[w][0][0];
   const bool bit3 = (s.lane >> 3) & 1;
-  for (int x = threadIdx.x; x < BLK * (NMAX + 1) * (K + 1); x += 256) (&acc[0][0][0])[x] = 0.f;
-  __syncthreads();
 
   float dS[RK];
 #pragma unroll
   for (int i = 0; i < RK; ++i) dS[i] = a.dfinal ? a.dfinal[soff + (size_t)i * V] : 0.f;
 
-  // token inputs, double-buffered: the next token's are loaded while the
-  // current one is used (the buffer index is a compile-time constant below)
+  // the backward walk's token inputs, double-buffered: the next token's are
+  // loaded while the current one is used (compile-time buffer indices)
   In buf[2];
   for (int cc = ntc - 1; cc >= 0; --cc) {
     const int64_t tb = t0 + (int64_t)CH * cc;
@@ -242,56 +253,75 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < RK; ++i) S[i] = src[(size_t)i * V];
     const int nstep = BLK * (nblk - 1);  // tokens before the last block's start (a multiple of 8)
-    if (nstep > 0) s.load(buf[0], tb, false);
-    for (int m = 0; m < nstep; m += 2) {
-      if (m % BLK == 0) {
+    // (block 0's entry is stored before the loop, so that the loop waits for no
+    // state load)
 #pragma unroll
-        for (int i = 0; i < RK; ++i) my_ck[((m / BLK) * RK + i) * 64 + s.lane] = S[i];
+    for (int i = 0; i < RK; ++i) my_ck[i * 64 + s.lane] = S[i];
+    // One forward token is shorter than a load's latency: the forward passes
+    // keep the inputs of the next PF tokens in flight, in a ring of registers
+    // indexed by compile-time constants.  Every load is issued (past the end of
+    // the range, the sequence's or the block's last token is loaded again and not
+    // used) and only the arithmetic depends on run-time counts: with no load under
+    // a run-time condition the compiler can count the loads in flight exactly.
+    const int64_t tseq = t1 - 1;
+    In fb[PF];
+#pragma unroll
+    for (int d = 0; d < PF; ++d) s.load(fb[d], tb + d < tseq ? tb + d : tseq, false);
+    for (int m0 = 0; m0 < nstep; m0 += BLK) {
+      if (m0 > 0) {
+#pragma unroll
+        for (int i = 0; i < RK; ++i) my_ck[((m0 / BLK) * RK + i) * 64 + s.lane] = S[i];
       }
-      s.load(buf[1], tb + m + 1, false);
-      s.step(S, buf[0]);
-      if (m + 2 < nstep) s.load(buf[0], tb + m + 2, false);
-      s.step(S, buf[1]);
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) {
+        s.step(S, fb[i % PF]);
+        const int64_t tn = tb + m0 + i + PF;
+        s.load(fb[i % PF], tn < tseq ? tn : tseq, false);
+      }
     }
 #pragma unroll
     for (int i = 0; i < RK; ++i) my_ck[((nblk - 1) * RK + i) * 64 + s.lane] = S[i];
     // blocks backwards
     for (int b = nblk - 1; b >= 0; --b) {
       const int nb = (ntok - BLK * b) < BLK ? (ntok - BLK * b) : BLK;
-      const int64_t tbb = tb + BLK * b;
+      const int64_t tbb = tb + BLK * b, tlast = tbb + nb - 1;
+      // the backward walk's first token (with q and the output gradient), in buf[1]
+      s.load(buf[1], tbb + BLK - 1 < tlast ? tbb + BLK - 1 : tlast, true);
       float ST[BLK][RK];  // state entering token m of the block
 #pragma unroll
       for (int i = 0; i < RK; ++i) ST[0][i] = my_ck[(b * RK + i) * 64 + s.lane];
-      // token m - 1 of the block moves ST[m-1] to ST[m]; its inputs sit in buf[(m - 1) & 1]
-      if (nb > 1) s.load(buf[0], tbb, false);
+      // token m - 1 of the block moves ST[m-1] to ST[m]; its inputs sit in fb[(m - 1) % PF]
+#pragma unroll
+      for (int d = 0; d < PF; ++d) s.load(fb[d], tbb + d < tlast ? tbb + d : tlast, false);
 #pragma clang loop unroll(full)
       for (int m = 1; m < BLK; ++m) {
         if (m < nb) {
-          if (m + 1 < nb) s.load(buf[m & 1], tbb + m, false);
 #pragma unroll
           for (int i = 0; i < RK; ++i) ST[m][i] = ST[m - 1][i];
-          s.step(ST[m], buf[(m - 1) & 1]);
+          s.step(ST[m], fb[(m - 1) % PF]);
+        }
+        if (m - 1 + PF < BLK - 1) {  // token m - 1 + PF is one of the tokens stepped (0 .. BLK - 2)
+          const int64_t tn = tbb + m - 1 + PF;
+          s.load(fb[(m - 1) % PF], tn < tlast ? tn : tlast, false);
         }
       }
       // backwards over the block: token m's inputs (with q and the output
       // gradient) in buf[m & 1], token m - 1's loaded meanwhile
-      if ((nb - 1) & 1) s.load(buf[1], tbb + nb - 1, true);  // constant indices keep buf in registers
-      else s.load(buf[0], tbb + nb - 1, true);
 #pragma clang loop unroll(full)
       for (int m = BLK - 1; m >= 0; --m) {
-        if (m >= nb) continue;
         const int64_t t = tbb + m;
         In &cur = buf[m & 1];
-        if (m > 0) s.load(buf[(m - 1) & 1], t - 1, true);
+        if (m > 0) s.load(buf[(m - 1) & 1], t - 1 < tlast ? t - 1 : tlast, true);
+        if (m >= nb) continue;
         // recompute the token's sub-states S^j and u_j, e_j
         const float al = B::decay(cur);
-        float Sj[NMAX][RK], u[NMAX], e[NMAX];
+        float Sj[NH][RK], u[NH], e[NH];
         float st[RK];
 #pragma unroll
         for (int i = 0; i < RK; ++i) st[i] = al * ST[m][i];
 #pragma unroll
-        for (int j = 0; j < NMAX; ++j) {
-          if (j < a.n) {
+        for (int j = 0; j < NH; ++j) {
+          if (j < NH) {
             float kv[RK];
             s.row(kv, cur.k[j]);
             float part = 0.f;
@@ -300,51 +330,51 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
               Sj[j][i] = st[i];
               part = fmaf(st[i], kv[i], part);
             }
-            u[j] = (float)cur.v[j] - col_sum(part);
+            u[j] = (float)cur.v[j] - cur.rk[j] * col_sum(part);
             e[j] = cur.b[j] * u[j];
+            const float ek = e[j] * cur.rk[j];
 #pragma unroll
-            for (int i = 0; i < RK; ++i) st[i] = fmaf(kv[i], e[j], st[i]);
+            for (int i = 0; i < RK; ++i) st[i] = fmaf(kv[i], ek, st[i]);
           }
         }
         // readout: o_t = scale S_t^T q_t
-        float *acc_m = &acc[m][0][0];
+        float(*wm)[4][K] = wsl[m % F];
         const int el0 = RK * s.rg + (RK / 8) * s.c;  // the row entries this lane finishes
         {
-          const float dov = (float)cur.dov * a.scale;
+          const float dov = (float)cur.dov * a.scale, dovq = dov * cur.rq;
           float qv[RK], pq[RK], oq[RK / 8];
           s.row(qv, cur.q);
 #pragma unroll
           for (int i = 0; i < RK; ++i) {
             pq[i] = st[i] * dov;
-            dS[i] = fmaf(qv[i], dov, dS[i]);
+            dS[i] = fmaf(qv[i], dovq, dS[i]);
           }
           row_scatter<RK>(pq, oq, bit3);
 #pragma unroll
-          for (int p = 0; p < RK / 8; ++p) atomicAdd(acc_m + el0 + p, oq[p]);
+          for (int p = 0; p < RK / 8; ++p) wm[0][w][el0 + p] = oq[p];
         }
 #pragma unroll
-        for (int j = NMAX - 1; j >= 0; --j) {
-          if (j < a.n) {
-            const int64_t r = t * a.n + j;
+        for (int j = NH - 1; j >= 0; --j) {
+          if (j < NH) {
             float kv[RK];
             s.row(kv, cur.k[j]);
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < RK; ++i) part = fmaf(dS[i], kv[i], part);
-            const float de = col_sum(part);  // equal in the column's 8 lanes
-            const float du = cur.b[j] * de;
-            a.dv[r * a.dv_st + (int64_t)s.h * a.dv_sh + s.col] = du;
+            const float de = cur.rk[j] * col_sum(part);  // equal in the column's 8 lanes
+            const float du = cur.b[j] * de, duk = du * cur.rk[j];
+            dvs[m][j][VT * w + s.c] = du;
             const float db = row_all(de * u[j]);
-            if (s.lane == 0) atomicAdd(acc_m + (1 + j) * (K + 1) + K, db);
+            if (s.lane == 0) scal[m][1 + j][w] = db;
             float pk[RK], ok[RK / 8];
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
               pk[i] = fmaf(dS[i], e[j], -Sj[j][i] * du);
-              dS[i] = fmaf(-kv[i], du, dS[i]);
+              dS[i] = fmaf(-kv[i], duk, dS[i]);
             }
             row_scatter<RK>(pk, ok, bit3);
 #pragma unroll
-            for (int p = 0; p < RK / 8; ++p) atomicAdd(acc_m + (1 + j) * (K + 1) + el0 + p, ok[p]);
+            for (int p = 0; p < RK / 8; ++p) wm[1 + j][w][el0 + p] = ok[p];
           }
         }
         // decay
@@ -352,31 +382,38 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(dS[i], ST[m][i], part);
         const float dal = row_all(col_sum(part));
-        if (s.lane == 0) atomicAdd(acc_m + K, dal * al);
+        if (s.lane == 0) scal[m][0][w] = dal * al;
 #pragma unroll
         for (int i = 0; i < RK; ++i) dS[i] *= al;
-      }
-      // the block's sums over the four waves, then one atomic per element (the
-      // other contributions: the state heads sharing a q/k head, and the other
-      // workgroups of this chain's V tiles); acc is left zero
-      __syncthreads();
-      const int per_tok = (1 + a.n) * (K + 1);
-      for (int x = threadIdx.x; x < nb * per_tok; x += 256) {
-        const int m = x / per_tok, rem = x - m * per_tok, slot = rem / (K + 1), el = rem - slot * (K + 1);
-        float *cell = &acc[m][slot][el];
-        const float sum = *cell;
-        *cell = 0.f;
-        const int64_t t = tbb + m;
-        if (slot == 0) {
-          if (el < K) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sum);
-          else atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
-        } else {
-          const int64_t r = t * a.n + slot - 1;
-          if (el < K) atomicAdd(a.dk + r * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sum);
-          else atomicAdd(a.dbeta + r * a.db_st + (int64_t)s.h * a.db_sh, sum);
+        // the group of tokens m .. m + F - 1 is done: the sums over the four waves,
+        // then one float atomic per element (the other contributions: the state
+        // heads sharing a q/k head, and the other workgroups of this chain's V tiles)
+        if (m % F == 0 && m < nb) {
+          __syncthreads();
+          const int ng = (nb - m) < F ? (nb - m) : F;  // tokens m .. m + ng - 1 of the block
+          const int per_tok = (1 + NH) * (K + 1);
+          for (int x = threadIdx.x; x < ng * per_tok; x += 256) {
+            const int mm = x / per_tok, rem = x - mm * per_tok, slot = rem / (K + 1), el = rem - slot * (K + 1);
+            const int64_t t = tbb + m + mm;
+            if (el < K) {
+              const float sum = (wsl[mm][slot][0][el] + wsl[mm][slot][1][el]) + (wsl[mm][slot][2][el] + wsl[mm][slot][3][el]);
+              if (slot == 0) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sum);
+              else atomicAdd(a.dk + (t * NH + slot - 1) * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sum);
+            } else {
+              const float *sc = scal[m + mm][slot];
+              const float sum = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+              if (slot == 0) atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
+              else atomicAdd(a.dbeta + (t * NH + slot - 1) * a.db_st + (int64_t)s.h * a.db_sh, sum);
+            }
+          }
+          const int64_t col0 = (int64_t)VT * (s.vt - w);  // the workgroup's first column
+          for (int x = threadIdx.x; x < ng * NH * 4 * VT; x += 256) {
+            const int mm = x / (NH * 4 * VT), rem = x - mm * (NH * 4 * VT), j = rem / (4 * VT), cc = rem - j * (4 * VT);
+            a.dv[((tbb + m + mm) * NH + j) * a.dv_st + (int64_t)s.h * a.dv_sh + col0 + cc] = dvs[m + mm][j][cc];
+          }
+          __syncthreads();  // before the next group's partials overwrite the slots
         }
       }
-      __syncthreads();
     }
   }
   if (a.ds0) {
@@ -413,12 +450,41 @@ __global__ void __launch_bounds__(256) gdp_l2norm_grad_kernel(NormGradArgs a) {
   for (int i = 0; i < PL; ++i) g[lane + 64 * i] = rs * (gv[i] - xv[i] * rs * dot);
 }
 
-template <typename T, int K, int V> hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
+// The L2-norm factor (|x|^2 + 1e-6)^(-1/2) of each [rows, heads, K] row, into
+// a dense [rows, heads] float32 array (g, g_st = heads, g_sh = 1).  One wave per row.
+template <typename T, int K>
+__global__ void __launch_bounds__(256) gdp_row_norm_kernel(NormGradArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const int64_t r = row / a.heads, hh = row % a.heads;
+  const T *x = (const T *)a.x + r * a.x_st + hh * a.x_sh;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < K / 64; ++i) {
+    const float xv = (float)x[lane + 64 * i];
+    ss = fmaf(xv, xv, ss);
+  }
+  ss = xsum<1, 32>(ss);
+  if (lane == 0) a.g[r * a.g_st + hh * a.g_sh] = __builtin_amdgcn_rsqf(ss + 1e-6f);
+}
+
+template <typename T, int K, int V, int NH> hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream) {
   static_assert((V / VT) % 4 == 0, "a workgroup holds four V tiles of one chain");
   const int64_t waves = (int64_t)a.N * a.Hv * (V / VT);
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdp_backward_kernel<T, K, V>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gdp_backward_kernel<T, K, V, NH>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+// the number of Householder rows is a template parameter: the per-token loads
+// are then unconditional and stay in flight across the token they are hidden by
+template <typename T, int K, int V> hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
+  switch (a.n) {
+    case 1: return launch_bwd_n<T, K, V, 1>(a, stream);
+    case 2: return launch_bwd_n<T, K, V, 2>(a, stream);
+    case 3: return launch_bwd_n<T, K, V, 3>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -438,6 +504,17 @@ hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_
     if (K == 64 && V == 64) return launch_bwd<float, 64, 64>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_row_norm(const NormGradArgs &a, int dtype, int K, hipStream_t stream) {
+  if (a.rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.rows + 3) / 4));
+  if (dtype == IN_BF16 && K == 128) hipLaunchKernelGGL((gdp_row_norm_kernel<__bf16, 128>), grid, dim3(256), 0, stream, a);
+  else if (dtype == IN_BF16 && K == 64) hipLaunchKernelGGL((gdp_row_norm_kernel<__bf16, 64>), grid, dim3(256), 0, stream, a);
+  else if (dtype == IN_F32 && K == 128) hipLaunchKernelGGL((gdp_row_norm_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+  else if (dtype == IN_F32 && K == 64) hipLaunchKernelGGL((gdp_row_norm_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_l2norm_grad(const NormGradArgs &a, int dtype, int K, hipStream_t stream) {

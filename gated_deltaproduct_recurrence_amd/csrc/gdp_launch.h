@@ -137,7 +137,10 @@ struct BwdArgs {
   int64_t T;
   int N, n, Hqk, Hv, Hk;
   float scale;
-  int l2norm;
+  // the rows' L2-norm factors, [T, Hqk] and [T*n, Hk] float32; without the norm
+  // a single 1 with zero strides
+  const float *rq; int64_t rq_st, rq_sh;
+  const float *rk; int64_t rk_st, rk_sh;
   const float *chunk_states;                // [NT, Hv, K, V]: state entering each token chunk
   const int32_t *chunk_offsets;             // [N+1]
   const void *dout; int64_t do_st, do_sh;   // [T, Hv, V], the inputs' dtype
@@ -161,6 +164,8 @@ struct NormGradArgs {
   int64_t rows; int heads;
 };
 hipError_t launch_l2norm_grad(const NormGradArgs &a, int dtype, int K, hipStream_t stream);
+// the norm factors of the rows of x into g (dense [rows, heads]: g_st = heads, g_sh = 1)
+hipError_t launch_row_norm(const NormGradArgs &a, int dtype, int K, hipStream_t stream);
 
 // Element types of the front end's conversion kernels.
 enum ElType { EL_F32 = 0, EL_BF16 = 1, EL_F16 = 2 };
