@@ -198,7 +198,8 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
 
 /* Host-only.  Workspace bytes gdp_chunk_prefill_backward needs: the
  * descriptors, the float32 state entering every token chunk (nt_cap x Hv x K x V),
- * an output buffer of the forward pass it reruns, and that pass's workspace
+ * an output buffer of the forward pass it reruns, the float32 L2-norm factors of
+ * the q and k rows (T x Hqk and T*n x Hv at most), and that pass's workspace
  * (gdp_workspace_bytes).  Returns 0 for invalid sizes or dtypes. */
 size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk, int32_t Hv,
                                     int32_t K, int32_t V, int32_t dtype);
