@@ -14,13 +14,14 @@ LIB_PATH = os.path.join(_HERE, "libgdp.so")
 
 GDP_F32, GDP_BF16, GDP_I32, GDP_I64, GDP_F16 = 0, 1, 2, 3, 4
 GDP_OK, GDP_EINVAL, GDP_EUNSUPPORTED, GDP_EALIAS, GDP_EWORKSPACE, GDP_EHIP = 0, -1, -2, -3, -4, -5
+GDP_DBG_CU, GDP_DBG_SLOT, GDP_DBG_DUP = 1, 2, 4
 STATUS_NAMES = {GDP_EINVAL: "GDP_EINVAL", GDP_EUNSUPPORTED: "GDP_EUNSUPPORTED", GDP_EALIAS: "GDP_EALIAS",
                 GDP_EWORKSPACE: "GDP_EWORKSPACE", GDP_EHIP: "GDP_EHIP"}
 
 EXPORTED = ("gdp_descriptor_capacity", "gdp_build_descriptors", "gdp_workspace_bytes",
             "gdp_chunk_prefill", "gdp_recurrent_decode", "gdp_fi_workspace_bytes",
             "gdp_chunk_gated_delta_product", "gdp_backward_workspace_bytes", "gdp_chunk_prefill_backward",
-            "gdp_last_error", "gdp_version")
+            "gdp_debug_status", "gdp_last_error", "gdp_version")
 
 
 class gdp_tensor(ctypes.Structure):
@@ -77,6 +78,8 @@ def _load(path=LIB_PATH):
     lib.gdp_chunk_prefill_backward.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
                                                T, T, T, T, T, T, T, T, ctypes.c_void_p, ctypes.c_size_t,
                                                ctypes.c_void_p]
+    lib.gdp_debug_status.restype = ctypes.c_int
+    lib.gdp_debug_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32, ctypes.c_void_p]
     lib.gdp_last_error.restype = ctypes.c_char_p
     lib.gdp_last_error.argtypes = []
     lib.gdp_version.restype = ctypes.c_char_p
@@ -128,6 +131,15 @@ def gdp_version():
 
 def gdp_last_error():
     return LIB.gdp_last_error().decode()
+
+
+def gdp_debug_status(clear=True, device=None):
+    """The current device's debug-validation word (GDP_DBG_* bits) after the work
+    queued on the current stream; cleared afterwards when `clear`.  The checks run
+    only with GDP_DEBUG_VALIDATE=1 in the environment."""
+    word = ctypes.c_uint32(0)
+    _check(LIB.gdp_debug_status(ctypes.byref(word), 1 if clear else 0, _stream(device)))
+    return int(word.value)
 
 
 def gdp_descriptor_capacity(T, N, num_householder):

@@ -32,6 +32,12 @@ int fail(int code, const char *fmt, ...) {
 
 bool present(const gdp_tensor *t) { return t != nullptr && t->data != nullptr; }
 
+// GDP_DEBUG_VALIDATE=1: launch the device checks of cu_seqlens and the state indices
+bool debug_validate() {
+  const char *s = std::getenv("GDP_DEBUG_VALIDATE");
+  return s != nullptr && s[0] == '1' && s[1] == '\0';
+}
+
 int elem_size(int32_t dt) {
   switch (dt) {
     case GDP_F32: return 4;
@@ -322,6 +328,18 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
   return GDP_OK;
 }
 
+int gdp_debug_status(uint32_t *word, int32_t clear, void *stream) {
+  g_last_error.clear();
+  if (!word) return fail(GDP_EINVAL, "word is required");
+  uint32_t *p = nullptr;
+  hipError_t e = gdp::debug_word_ptr(&p);
+  if (e == hipSuccess) e = hipMemcpyAsync(word, p, sizeof(uint32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess && clear) e = gdp::launch_fill((int32_t *)p, 1, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDP_EHIP, "debug status: %s", hipGetErrorString(e));
+  return GDP_OK;
+}
+
 const char *gdp_version(void) { return "gdp-mi355x 0.1.0 (gfx950)"; }
 
 int gdp_descriptor_capacity(int64_t T, int64_t N, int32_t n, int64_t *nt_cap, int64_t *ntdp_cap) {
@@ -553,6 +571,16 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   a.tws_rows = ntdp_cap;
   a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
   hipError_t e;
+  if (debug_validate()) {
+    gdp::ValidateArgs va;
+    std::memset(&va, 0, sizeof va);
+    va.cu = cu_seqlens->data; va.cu_is64 = a.cu_is64; va.N = N; va.T = T;
+    if (a.cache) {
+      va.slots = a.slots; va.slots_is64 = a.slots_is64; va.nslots_given = N; va.num_slots = a.num_slots;
+    }
+    if ((e = gdp::launch_validate(va, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "validation launch: %s", hipGetErrorString(e));
+  }
   if (plan.use) {
     // segmented: segment boundaries, summaries (M, B) of every segment, their
     // in-order combination per chain, then every segment from its start state
@@ -851,8 +879,15 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
   a.slots = state_indices->data;
   a.slots_is64 = state_indices->dtype == GDP_I64;
   a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
-  hipError_t e = gdp::launch_decode(a, dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V,
-                                    (hipStream_t)stream);
+  hipError_t e;
+  if (debug_validate()) {
+    gdp::ValidateArgs va;
+    std::memset(&va, 0, sizeof va);
+    va.slots = a.slots; va.slots_is64 = a.slots_is64; va.nslots_given = N; va.num_slots = a.num_slots;
+    if ((e = gdp::launch_validate(va, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "validation launch: %s", hipGetErrorString(e));
+  }
+  e = gdp::launch_decode(a, dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, (int)K, (int)V, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDP_EHIP, "decode launch: %s", hipGetErrorString(e));
   return GDP_OK;
 }

@@ -199,6 +199,17 @@ struct HalfCopyArgs {
 };
 hipError_t launch_half_copy(const HalfCopyArgs &a, bool to_bf16, hipStream_t stream);
 hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
+
+// Opt-in checks of the data-dependent arguments (GDP_DEBUG_VALIDATE=1): the
+// bits GDP_DBG_* of include/gdp.h are ORed into one device-global word per device.
+struct ValidateArgs {
+  const void *cu; int cu_is64; int64_t N, T;                    // cu_seqlens [N+1], or null
+  const void *slots; int slots_is64; int64_t nslots_given, num_slots;  // state indices, or null
+  uint32_t *word;                                               // set by launch_validate
+};
+hipError_t launch_validate(ValidateArgs a, hipStream_t stream);
+// device address of the current device's word
+hipError_t debug_word_ptr(uint32_t **out);
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);
 // launches the fused kernel regardless of the chain count (bf16 only)
 hipError_t launch_fused_prefill(const PrefillArgs &a, int K, int V, hipStream_t stream);

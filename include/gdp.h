@@ -282,6 +282,29 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
                                   const gdp_tensor *output, const gdp_tensor *output_state, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* Debug validation of the data-dependent arguments.  These are not checked by
+ * default, because checking them needs a read of device data.  A bad value stays
+ * in bounds (every kernel clamps sequence ranges to [0, T] and skips slots
+ * outside the cache), but the results are then undefined.  With the environment
+ * variable GDP_DEBUG_VALIDATE=1, gdp_chunk_prefill (and the entries built on it)
+ * and gdp_recurrent_decode first launch a check on their stream.  The check ORs
+ * these bits into a word kept per device:
+ *   GDP_DBG_CU    cu_seqlens decreases somewhere, or an entry lies outside [0, T]
+ *                 (Megatron Core page, chunk_gated_delta_product_varlen: the
+ *                 cumulative sequence boundaries)
+ *   GDP_DBG_SLOT  a state index below -1 or not below the number of cache slots
+ *   GDP_DBG_DUP   two sequences (decode entries) share a non-negative state
+ *                 index (same page, the state-cache arguments: -1 means no write)
+ * The duplicate check is quadratic in the number of sequences: it is a
+ * debugging aid, not for production steps. */
+enum gdp_debug_bits { GDP_DBG_CU = 1, GDP_DBG_SLOT = 2, GDP_DBG_DUP = 4 };
+
+/* Host-side: reads the current device's debug word into *word (host memory)
+ * after the work queued on `stream` so far, then, if clear != 0, queues its
+ * reset to 0 on `stream`.  Synchronises `stream`.  GDP_EINVAL if word is NULL,
+ * GDP_EHIP on a runtime failure. */
+int gdp_debug_status(uint32_t *word, int32_t clear, void *stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *gdp_last_error(void);
 
