@@ -43,9 +43,12 @@ def source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(wid):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current kernel source and on this workload
+    (the counters were taken on the long-context prefill, workload 4); else None."""
+    if wid != 4:
+        return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -218,6 +221,9 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 = long-context prefill)")
     ap.add_argument("--cpu-tokens", type=int, default=65536, help="oracle sample: tokens per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step (descriptor build + prefill) in a HIP graph and time its "
+                         "replays; the replayed output is checked against the eager one bit for bit")
     ap.add_argument("--decode", action="store_true",
                     help="measure the single-token decode step on the state cache instead of the prefill "
                          "(serving batch: 256 entries with 8 padding, n=2, Hqk=16 / Hv=32, K=V=128, bf16, "
@@ -278,16 +284,16 @@ def main():
     import ctypes
     stream = torch.cuda.current_stream(dev)
 
-    def build_desc():
-        rc = gdp.LIB.gdp_build_descriptors(ctypes.byref(cu_t), n, T, ctypes.byref(d), stream.cuda_stream)
+    def build_desc(st=stream):
+        rc = gdp.LIB.gdp_build_descriptors(ctypes.byref(cu_t), n, T, ctypes.byref(d), st.cuda_stream)
         if rc != 0:
             raise gdp.GdpError(rc, gdp.gdp_last_error())
 
-    def prefill():
+    def prefill(st=stream):
         gdp.gdp_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, inp["cu_seqlens"],
                               inp["scale"] or 0.0, inp["initial_state"], w.output_final_state,
                               w.l2norm_in_kernel, cache, inp["state_indices"], w.return_chunk_states, o, fs, cs,
-                              desc, ws, stream=stream.cuda_stream)
+                              desc, ws, stream=st.cuda_stream)
 
     for _ in range(args.warmup):
         build_desc()
@@ -310,10 +316,46 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = T / (ms_per_step * 1e-3)
 
+    graph_detail = None
+    if args.graph:
+        # one step captured (every grid depends only on host-known sizes), then
+        # replayed; the outputs must equal the eager step's
+        o_eager = o.clone()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            build_desc(side)
+            prefill(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream(dev)
+            build_desc(cap)
+            prefill(cap)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_g = time.perf_counter()
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        wall_g = time.perf_counter() - t_g
+        same = bool(torch.equal(o, o_eager))
+        if not same:
+            print("bench: graph replay output differs from the eager output", file=sys.stderr)
+        graph_detail = {"graph_replay_ms_per_step": wall_g * 1e3 / args.steps,
+                        "graph_replay_event_ms": g0.elapsed_time(g1) / args.steps,
+                        "graph_replay_equals_eager": same}
+
     alg = algorithmic_bytes(w)
     fused_avg_s = float(np.mean(fused_ms)) * 1e-3
     achieved = alg / fused_avg_s / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.workload)
 
     line = {
         "metric": "real tokens/s, chunked GDP prefill (bf16, d=128) + % of MFMA/HBM roofline",
@@ -331,6 +373,8 @@ def main():
         "timing_detail": {"event_step_ms_median": float(np.median(step_ms)),
                           "descriptor_kernel_ms": float(np.mean(desc_ms))},
     }
+    if graph_detail is not None:
+        line["timing_detail"].update(graph_detail)
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         rec, ref, it = cpu_baseline(inp, w, args.cpu_tokens, threads)
