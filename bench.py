@@ -78,6 +78,27 @@ def kernel_label(w):
     return "gdp_fused_kernel" if fused else "gdp_wy_kernel + gdp_scan_kernel"
 
 
+def copy_bandwidth(dev, reps=5):
+    """Read + write bytes per second of a plain 1 GiB device-to-device copy on
+    this GPU (torch's copy kernel), timed with HIP events: a practical ceiling
+    next to the 8 TB/s peak."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def cpu_baseline(inp, w, tokens_per_seq, threads):
     """The fp64 oracle on the first `tokens_per_seq` tokens of every sequence
     (all heads), timed on the host cores; returns (record, oracle outputs)."""
@@ -221,6 +242,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 = long-context prefill)")
     ap.add_argument("--cpu-tokens", type=int, default=65536, help="oracle sample: tokens per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the oracle baseline (default: the cores, at most 16)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step (descriptor build + prefill) in a HIP graph and time its "
                          "replays; the replayed output is checked against the eager one bit for bit")
@@ -375,8 +398,11 @@ def main():
     }
     if graph_detail is not None:
         line["timing_detail"].update(graph_detail)
+    copy_gbs = copy_bandwidth(dev)
+    line["copy_bound"] = {"copy_GBs": copy_gbs, "achieved_GBs": achieved, "frac": achieved / copy_gbs,
+                          "what": "1 GiB device-to-device copy on this GPU, read + write bytes per second"}
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
         rec, ref, it = cpu_baseline(inp, w, args.cpu_tokens, threads)
         line["cpu_baseline"] = rec
         got = o.index_select(0, it).to("cpu", torch.float64).numpy()
