@@ -29,10 +29,11 @@
 // entries of a dq or dk partial are reduce-scattered over those lanes with the
 // gfx950 half-wave and row swaps and a DPP row rotation, so that each lane ends
 // with two finished entries.  Gradients shared by several waves (dq, dk: all V
-// tiles and the state heads of a q/k head; dbeta, dg_log: all V tiles) are
-// summed over the four waves of a workgroup (four adjacent V tiles of one chain)
-// with LDS float atomics, for a whole 8-token block, and then added to the zeroed
-// output buffers with one float atomic per element and block.
+// tiles and the state heads of a q/k head; dbeta, dg_log: all V tiles) go to
+// per-wave LDS slots; every few tokens the workgroup (four adjacent V tiles of
+// one chain) sums the four waves' slots after a barrier and adds the sums to the
+// zeroed output buffers with one float atomic per element.  dv is stored there
+// too, coalesced over the workgroup's columns.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   // (slot 1 + j) partials, summed over the waves at the flush
   __shared__ float scal[BLK][NH + 1][4];
   // per token of the block, dv of the workgroup's 4 x 8 columns (written by
-  // the wave owning the column, stored with the block's flush)
+  // the wave owning the column, stored with its group's flush)
   __shared__ float dvs[BLK][NH][4 * VT];
   B s(a);
   const int w = threadIdx.x >> 6;
