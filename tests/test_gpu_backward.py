@@ -6,7 +6,7 @@ import torch
 
 from gated_deltaproduct_recurrence_amd import workloads
 from oracle import backward as obwd
-from tests.parity import TOL, rel_err, to_np
+from tests.parity import TOL, oracle_run, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +72,45 @@ def test_backward_zero_length_and_padding_rows(gdp):
     lens = CASES[1][0]
     assert lens[2] == 0
     assert rel_err(to_np(res["d_initial_state"][2]), ref["dinitial_state"][2]) <= tol
+
+
+def test_backward_long_context_sampled(gdp):
+    """Full-size long-context gradients (8 x 65536 tokens, n=2, Hqk=16 / Hv=32,
+    in-kernel norm), as the benchmark runs them.  A token's gradients depend only
+    on the inputs from that token on and on the state entering it, so the oracle
+    checks the last M tokens of sampled (sequence, q/k head) groups: the fp64
+    forward oracle gives the state entering the suffix from the prefix, and the
+    autograd oracle differentiates the suffix alone.  The two state heads of the
+    group are both in the sample, so dq and dk (summed over them) compare too."""
+    w = workloads.workload(4)
+    inp = workloads.generate(w, "cuda")
+    gen = torch.Generator(device="cuda").manual_seed(404)
+    d_o = torch.randn(w.T, w.Hv, w.V, generator=gen, device="cuda").to(w.dtype)
+    res = gdp.chunk_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], w.n,
+                                     inp["cu_seqlens"], d_o, None, initial_state=inp["initial_state"],
+                                     use_qk_l2norm=True)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg_log", "dbeta"):
+        assert torch.isfinite(res[name]).all(), name
+    cu = inp["cu_seqlens"].cpu().numpy()
+    n, M = w.n, 160
+    for seq, hq in ((7, 5), (2, 12)):
+        t0, t1 = int(cu[seq]), int(cu[seq + 1])
+        ts = t1 - M
+        heads = [2 * hq, 2 * hq + 1]
+        prefix = dict(q=inp["q"][t0:ts, hq:hq + 1], k=inp["k"][t0 * n:ts * n, hq:hq + 1],
+                      v=inp["v"][t0 * n:ts * n, heads], g_log=inp["g_log"][t0:ts, heads],
+                      beta=inp["beta"][t0 * n:ts * n, heads], num_householder=n,
+                      cu_seqlens=torch.tensor([0, ts - t0]), scale=None,
+                      initial_state=inp["initial_state"][seq:seq + 1, heads], use_qk_l2norm=True)
+        s_mid = oracle_run(prefix, threads=2)["final_state"]
+        ref = obwd.backward(to_np(inp["q"][ts:t1, hq:hq + 1]), to_np(inp["k"][ts * n:t1 * n, hq:hq + 1]),
+                            to_np(inp["v"][ts * n:t1 * n, heads]), to_np(inp["g_log"][ts:t1, heads]),
+                            to_np(inp["beta"][ts * n:t1 * n, heads]), n, np.array([0, M]),
+                            to_np(d_o[ts:t1, heads]), None, initial_state=s_mid, use_qk_l2norm=True)
+        got = {"dq": res["dq"][ts:t1, hq:hq + 1], "dk": res["dk"][ts * n:t1 * n, hq:hq + 1],
+               "dv": res["dv"][ts * n:t1 * n, heads], "dg_log": res["dg_log"][ts:t1, heads],
+               "dbeta": res["dbeta"][ts * n:t1 * n, heads]}
+        for name, x in got.items():
+            e = rel_err(to_np(x), ref[name])
+            assert e <= TOL[w.dtype], f"seq {seq} q/k head {hq}: {name} err {e:.3e}"
