@@ -150,6 +150,34 @@ def bench_decode(args, gdp, workloads):
         gdp.gdp_recurrent_decode(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, 0.0, True,
                                  inp["state_cache"], inp["state_indices"], o, stream=stream.cuda_stream)
 
+    rec = None
+    if not args.no_cpu_baseline:
+        # the oracle on every live entry of the step, with the cache cut down to
+        # their slots; the GPU output of the same step (from the same cache) is
+        # checked against it before the timed steps change the cache
+        import oracle
+        idx = inp["state_indices"]
+        sel = torch.nonzero(idx >= 0).flatten()
+        rows = (sel[:, None] * n + torch.arange(n, device=dev)).flatten()
+        f64 = lambda x: x.to("cpu", torch.float64).numpy()
+        args_o = (f64(inp["q"][sel]), f64(inp["k"][rows]), f64(inp["v"][rows]), f64(inp["g_log"][sel]),
+                  f64(inp["beta"][rows]), n, f64(inp["state_cache"][idx[sel].long()]),
+                  np.arange(sel.numel(), dtype=np.int32))
+        step()
+        torch.cuda.synchronize()
+        got = o.index_select(0, sel).to("cpu", torch.float64).numpy()
+        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
+        reps = 10  # the step is small: repeated for a stable rate
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            ref = oracle.decode(*args_o, use_qk_l2norm=True, threads=threads)
+        dt = (time.perf_counter() - t0) / reps
+        err = float(np.max(np.abs(got - ref["o"]))) / max(1.0, float(np.sqrt(np.mean(ref["o"] ** 2))))
+        print(f"bench: decode outputs vs oracle err {err:.3e}", file=sys.stderr)
+        rec = {"value": sel.numel() / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
+               "sample": f"all {sel.numel()} live entries of one step, all {Hv} heads, fp64 "
+                         f"(cache cut to their slots), {reps} runs of {dt:.2f} s"}
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -174,8 +202,50 @@ def bench_decode(args, gdp, workloads):
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gdp_decode_kernel",
                          "kernel_ms": kern_ms, "algorithmic_bytes_per_launch": alg},
-            "cpu_baseline": None}
+            "cpu_baseline": rec}
     print(json.dumps(line), flush=True)
+
+
+def backward_cpu_baseline(args, inp, w, d_o, grads, M=2048, seq=7, hq=5):
+    """The fp64 autograd oracle on the last M tokens of sequence `seq` for the
+    two state heads of q/k head `hq` (given the state entering the suffix, from
+    the forward oracle over the prefix, which is not timed), scaled to all
+    heads; also checks the GPU gradients of that sample."""
+    import torch
+
+    import oracle
+    from oracle import backward as obwd
+    n, grp = w.n, w.Hv // w.Hqk
+    cu = inp["cu_seqlens"].cpu().numpy()
+    t0, t1 = int(cu[seq]), int(cu[seq + 1])
+    ts = t1 - M
+    heads = list(range(grp * hq, grp * hq + grp))
+    f64 = lambda x: x.to("cpu", torch.float64).numpy()
+    pre = oracle.prefill(f64(inp["q"][t0:ts, hq:hq + 1]), f64(inp["k"][t0 * n:ts * n, hq:hq + 1]),
+                         f64(inp["v"][t0 * n:ts * n, heads]), f64(inp["g_log"][t0:ts, heads]),
+                         f64(inp["beta"][t0 * n:ts * n, heads]), n, np.array([0, ts - t0]),
+                         initial_state=f64(inp["initial_state"][seq:seq + 1, heads]), use_qk_l2norm=True)
+    sub = (f64(inp["q"][ts:t1, hq:hq + 1]), f64(inp["k"][ts * n:t1 * n, hq:hq + 1]), f64(inp["v"][ts * n:t1 * n, heads]),
+           f64(inp["g_log"][ts:t1, heads]), f64(inp["beta"][ts * n:t1 * n, heads]), n, np.array([0, M]),
+           f64(d_o[ts:t1, heads]), None)
+    if args.cpu_threads:
+        torch.set_num_threads(args.cpu_threads)
+    threads = torch.get_num_threads()
+    t_start = time.perf_counter()
+    ref = obwd.backward(*sub, initial_state=pre["final_state"], use_qk_l2norm=True)
+    dt = time.perf_counter() - t_start
+    got = {"dq": grads["dq"][ts:t1, hq:hq + 1], "dk": grads["dk"][ts * n:t1 * n, hq:hq + 1],
+           "dv": grads["dv"][ts * n:t1 * n, heads], "dg_log": grads["dg_log"][ts:t1, heads],
+           "dbeta": grads["dbeta"][ts * n:t1 * n, heads]}
+    for name, x in got.items():
+        r = ref[name]
+        e = float(np.max(np.abs(f64(x) - r))) / max(1.0, float(np.sqrt(np.mean(r ** 2))))
+        print(f"bench: {name} vs oracle err {e:.3e}", file=sys.stderr)
+    groups = w.Hqk
+    return {"value": M / (dt * groups), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"last {M} tokens of sequence {seq}, the {grp} state heads of q/k head {hq} (one of {groups} "
+                      f"groups; the rate is scaled to all {w.Hv} heads), fp64 autograd token loop given the state "
+                      f"entering the suffix, {dt:.2f} s"}
 
 
 def bench_backward(args, gdp, workloads):
@@ -231,6 +301,9 @@ def bench_backward(args, gdp, workloads):
                          "kernel": "gdp_chunk_prefill_backward (forward rerun + gdp_backward_kernel)",
                          "kernel_ms": kern_ms, "algorithmic_bytes_per_launch": alg},
             "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        grads = {"dq": dq, "dk": dk, "dv": dv, "dg_log": dg, "dbeta": db}
+        line["cpu_baseline"] = backward_cpu_baseline(args, inp, w, d_o, grads)
     print(json.dumps(line), flush=True)
 
 
