@@ -248,6 +248,82 @@ def backward_cpu_baseline(args, inp, w, d_o, grads, M=2048, seq=7, hq=5):
                       f"entering the suffix, {dt:.2f} s"}
 
 
+def bench_flashinfer(args, gdp, workloads):
+    """The long-context prefill through the FlashInfer-convention entry point:
+    linear decays alpha, float32 betas, V-major float32 initial and final states
+    (restated by the front end's small kernels around the prefill kernels)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lens, n, Hq, Hv, d = [65536] * 8, 2, 16, 32, 128
+    inp = workloads.flashinfer_batch(lens, n, Hq, Hq, Hv, d, dtype=torch.bfloat16, l2norm_in_kernel=True,
+                                     g_shift=3.0, init_std=0.1, seed=1004, device=dev)
+    T, N = sum(lens), len(lens)
+    out = torch.empty((T, Hv, d), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((N, Hv, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdp.gdp_fi_workspace_bytes(T, N, n, Hq, Hv, d, torch.bfloat16, True, True), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdp.gdp_chunk_gated_delta_product(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], n, None,
+                                          inp["initial_state"], True, inp["cu_seqlens"], True, out, fs, ws,
+                                          stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    # the op's own bytes: q, k, v, o (bf16), alpha, beta (float32), initial and final states (float32)
+    alg = T * (2 * d * Hq * (1 + n) + 2 * d * Hv * (1 + n) + 4 * Hv * (1 + n)) + 2 * 4 * N * Hv * d * d
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    line = {"metric": "real tokens/s, chunked GDP prefill in the FlashInfer convention (bf16, d=128) + % of HBM roofline",
+            "value": T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "long-context prefill in the FlashInfer convention: 8 x 65536 tokens, n=2, "
+                                   "Hq=Hk=16 / Hv=32, d=128, bf16, linear alpha, V-major float32 states, "
+                                   "in-kernel L2 norm", "real_tokens": T},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gdp_chunk_gated_delta_product (gate and state kernels + gdp_fused_kernel)",
+                         "kernel_ms": kern_ms, "algorithmic_bytes_per_launch": alg},
+            "cpu_baseline": None}
+    copy_gbs = copy_bandwidth(dev)
+    line["copy_bound"] = {"copy_GBs": copy_gbs, "achieved_GBs": achieved, "frac": achieved / copy_gbs,
+                          "what": "1 GiB device-to-device copy on this GPU, read + write bytes per second"}
+    if not args.no_cpu_baseline:
+        # the FlashInfer-convention oracle on the first L tokens of every sequence
+        # (outputs depend only on the tokens before them), all heads
+        import oracle
+        L = min(args.cpu_tokens, 32768)
+        it = torch.cat([torch.arange(i * lens[0], i * lens[0] + L, device=dev) for i in range(N)])
+        isub = torch.cat([torch.arange(i * lens[0] * n, (i * lens[0] + L) * n, device=dev) for i in range(N)])
+        host = lambda x, rows: x.index_select(0, rows).to("cpu", torch.float64).numpy()
+        sub = (host(inp["q"], it), host(inp["k"], isub), host(inp["v"], isub), host(inp["g"], it),
+               host(inp["beta"], isub))
+        threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
+        t0 = time.perf_counter()
+        ref = oracle.prefill_flashinfer(*sub, num_householder=n, initial_state=inp["initial_state"].cpu().double().numpy(),
+                                        cu_seqlens=np.arange(N + 1) * L, use_qk_l2norm_in_kernel=True, threads=threads)
+        dt = time.perf_counter() - t0
+        got = out.index_select(0, it).to("cpu", torch.float64).numpy()
+        err = float(np.max(np.abs(got - ref["o"]))) / max(1.0, float(np.sqrt(np.mean(ref["o"] ** 2))))
+        print(f"bench: sampled outputs vs oracle err {err:.3e}", file=sys.stderr)
+        line["cpu_baseline"] = {"value": N * L / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                "sample": f"first {L} tokens of each of the {N} sequences, all {Hv} heads, fp64 "
+                                          f"token loop (FlashInfer convention), {dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def bench_backward(args, gdp, workloads):
     """Gradients of the long-context prefill (its shape and inputs, one call per
     step, including the forward rerun that leaves the chunk states).  The
@@ -324,6 +400,8 @@ def main():
                     help="measure the single-token decode step on the state cache instead of the prefill "
                          "(serving batch: 256 entries with 8 padding, n=2, Hqk=16 / Hv=32, K=V=128, bf16, "
                          "1024 cache slots)")
+    ap.add_argument("--flashinfer", action="store_true",
+                    help="time the FlashInfer-convention entry point on the long-context shape instead")
     ap.add_argument("--backward", action="store_true",
                     help="measure the gradients of the long-context prefill instead of the forward pass")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -355,6 +433,9 @@ def main():
         return
     if args.backward:
         bench_backward(args, gdp, workloads)
+        return
+    if args.flashinfer:
+        bench_flashinfer(args, gdp, workloads)
         return
 
     dev = torch.device("cuda:0")

@@ -278,7 +278,9 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
   ga.beta_dtype = present(beta) ? el_type(beta->dtype) : 0;
   ga.b_st = present(beta) ? beta->stride[0] : 0; ga.b_sh = present(beta) ? beta->stride[1] : 0;
   ga.T = T; ga.n = n; ga.Hv = (int)Hv;
-  ga.g_log = (float *)(ws + L.glog); ga.beta32 = (float *)(ws + L.beta);
+  // a float32 beta is read in place by the prefill; otherwise it is restated
+  const bool beta_direct = present(beta) && beta->dtype == GDP_F32;
+  ga.g_log = (float *)(ws + L.glog); ga.beta32 = beta_direct ? nullptr : (float *)(ws + L.beta);
   if ((e = gdp::launch_gates(ga, (hipStream_t)stream)) != hipSuccess)
     return fail(GDP_EHIP, "gate launch: %s", hipGetErrorString(e));
   if (present(initial_state)) {
@@ -306,7 +308,7 @@ int gdp_chunk_gated_delta_product(const gdp_tensor *q, const gdp_tensor *k, cons
   }
   // the prefill in the Megatron Core convention on the restated operands
   gdp_tensor tg{ws + L.glog, GDP_F32, 2, {T, Hv}, {Hv, 1}};
-  gdp_tensor tb{ws + L.beta, GDP_F32, 2, {T * n, Hv}, {Hv, 1}};
+  const gdp_tensor tb = beta_direct ? *beta : gdp_tensor{ws + L.beta, GDP_F32, 2, {T * n, Hv}, {Hv, 1}};
   gdp_tensor ts0{present(initial_state) ? ws + L.s0 : nullptr, GDP_F32, 4, {N, Hv, d, d}, {Hv * d * d, d * d, d, 1}};
   gdp_tensor tfin{output_final_state ? ws + L.fin : nullptr, GDP_F32, 4, {N, Hv, d, d}, {Hv * d * d, d * d, d, 1}};
   if ((rc = gdp_chunk_prefill(pq, pk, pv, &tg, &tb, n, cu_seqlens, scale, &ts0, output_final_state,

@@ -33,9 +33,10 @@ __device__ __forceinline__ float load_as_f32(const void *p, int64_t i, int dtype
 }
 
 // g_log[t, h] = ln(alpha[t, h]) (0 when alpha is absent); beta32[r, h] = beta[r, h]
-// (1 when absent).  Both outputs are contiguous float32.
+// (1 when absent), unless beta32 is null (a float32 beta is read in place).  Both
+// outputs are contiguous float32.
 __global__ void __launch_bounds__(256) gdp_gate_kernel(GateArgs a) {
-  const int64_t ng = a.T * a.Hv, nb = a.T * a.n * a.Hv;
+  const int64_t ng = a.T * a.Hv, nb = a.beta32 ? a.T * a.n * a.Hv : 0;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < ng + nb; i += (int64_t)gridDim.x * 256) {
     if (i < ng) {
       const int64_t t = i / a.Hv, h = i - t * a.Hv;
@@ -103,7 +104,7 @@ hipError_t launch_half_copy(const HalfCopyArgs &a, bool to_bf16, hipStream_t str
 }
 
 hipError_t launch_gates(const GateArgs &a, hipStream_t stream) {
-  const int64_t total = a.T * a.Hv * (1 + a.n);
+  const int64_t total = a.T * a.Hv * (1 + (a.beta32 ? a.n : 0));
   if (total <= 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096;
   hipLaunchKernelGGL(gdp_gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
