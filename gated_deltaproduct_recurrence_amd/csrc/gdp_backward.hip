@@ -392,20 +392,35 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
         if (m % F == 0 && m < nb) {
           __syncthreads();
           const int ng = (nb - m) < F ? (nb - m) : F;  // tokens m .. m + ng - 1 of the block
-          const int per_tok = (1 + NH) * (K + 1);
-          for (int x = threadIdx.x; x < ng * per_tok; x += 256) {
-            const int mm = x / per_tok, rem = x - mm * per_tok, slot = rem / (K + 1), el = rem - slot * (K + 1);
-            const int64_t t = tbb + m + mm;
-            if (el < K) {
-              const float sum = (wsl[mm][slot][0][el] + wsl[mm][slot][1][el]) + (wsl[mm][slot][2][el] + wsl[mm][slot][3][el]);
-              if (slot == 0) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sum);
-              else atomicAdd(a.dk + (t * NH + slot - 1) * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sum);
-            } else {
-              const float *sc = scal[m + mm][slot];
-              const float sum = (sc[0] + sc[1]) + (sc[2] + sc[3]);
-              if (slot == 0) atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
-              else atomicAdd(a.dbeta + (t * NH + slot - 1) * a.db_st + (int64_t)s.h * a.db_sh, sum);
+          // rows (token mm, slot) of the group, EPT at a time over the 256 threads;
+          // a wave's 64 threads share one row, so every branch is wave-uniform.
+          // All LDS reads are issued before the first atomic.
+          constexpr int EPT = 256 / K, NP = F * (NH + 1), IT = (NP + EPT - 1) / EPT;
+          const int el = threadIdx.x % K;
+          const int sub = __builtin_amdgcn_readfirstlane((int)threadIdx.x / K);  // uniform per wave (K >= 64)
+          float sums[IT];
+#pragma unroll
+          for (int it = 0; it < IT; ++it) {
+            const int p = it * EPT + sub, mm = p / (NH + 1), slot = p - mm * (NH + 1);
+            sums[it] = p < NP ? (wsl[mm][slot][0][el] + wsl[mm][slot][1][el]) + (wsl[mm][slot][2][el] + wsl[mm][slot][3][el])
+                              : 0.f;
+          }
+#pragma unroll
+          for (int it = 0; it < IT; ++it) {
+            const int p = it * EPT + sub, mm = p / (NH + 1), slot = p - mm * (NH + 1);
+            if (p < NP && mm < ng) {
+              const int64_t t = tbb + m + mm;
+              if (slot == 0) atomicAdd(a.dq + t * a.dq_st + (int64_t)s.hq * a.dq_sh + el, sums[it]);
+              else atomicAdd(a.dk + (t * NH + slot - 1) * a.dk_st + (int64_t)s.hk * a.dk_sh + el, sums[it]);
             }
+          }
+          if ((int)threadIdx.x < ng * (NH + 1)) {  // dg_log (slot 0) and dbeta (slot 1 + j)
+            const int mm = threadIdx.x / (NH + 1), slot = threadIdx.x - mm * (NH + 1);
+            const float *sc = scal[m + mm][slot];
+            const float sum = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+            const int64_t t = tbb + m + mm;
+            if (slot == 0) atomicAdd(a.dg + t * a.dg_st + (int64_t)s.h * a.dg_sh, sum);
+            else atomicAdd(a.dbeta + (t * NH + slot - 1) * a.db_st + (int64_t)s.h * a.db_sh, sum);
           }
           const int64_t col0 = (int64_t)VT * (s.vt - w);  // the workgroup's first column
           for (int x = threadIdx.x; x < ng * NH * 4 * VT; x += 256) {
