@@ -142,20 +142,31 @@ __global__ void __launch_bounds__(1024) gdp_order_kernel(OrderArgs a) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroup barrier for LDS only: this wave's LDS accesses are complete, but
+// its global loads and stores may still be in flight (__syncthreads waits for
+// them too, which would stall every step on the next segment's prefetch).  The
+// combine's barriers order LDS traffic only; a register loaded from global
+// memory is waited for where it is used.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // S = M S + B per segment, on a 16-column tile of the state kept in LDS.  M of
-// the segment is staged in LDS with 16-byte loads (rows padded by one float so
-// that 16 lanes reading one column of 16 rows meet 16 banks), the next
-// segment's M is read into registers while this one multiplies.  Wave w
-// computes rows 16 RT w .. of the tile with v_mfma_f32_16x16x4_f32: lane
+// the segment is staged in LDS with 16-byte stores (rows padded by four floats,
+// so that the 64 lanes reading 16 rows x 4 columns meet 64 banks); the next
+// segment's M and B are read into registers while this one multiplies.  Wave w
+// computes rows 16 w .. 16 w + 15 of the tile with v_mfma_f32_16x16x4_f32: lane
 // (lg, lr) supplies M[row lr][k = 4 kk + lg] and S[k = 4 kk + lg][col lr] and holds
 // C[4 lg + i][lr].
 template <int K, int V>
-__global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
+__global__ void __launch_bounds__(4 * K) gdp_combine_kernel(CombineArgs a) {
   static_assert(K == 128 || K == 64, "K of 64 or 128");
-  constexpr int CT = 16, NCT = V / CT, RT = K / 64, LDM = K + 1;
-  constexpr int NL = K * K / 4 / 256;  // 16-byte loads of M per thread
+  // M rows padded by 4 floats: the fragment reads below (16 rows x 4 columns
+  // per instruction) then meet 64 distinct banks, and rows stay 16-byte aligned
+  // one wave per 16 state rows (K / 16 waves): each step's chain of dependent
+  // products is then K / 4 long
+  constexpr int NT = 4 * K, CT = 16, NCT = V / CT, RT = 1, LDM = K + 4;
+  constexpr int NL = K * K / 4 / NT;  // 16-byte loads of M per thread
   __shared__ float S[K][CT];
-  __shared__ float Ms[K * LDM];
+  __shared__ __attribute__((aligned(16))) float Ms[K * LDM];
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bid = blockIdx.x;
@@ -164,7 +175,7 @@ __global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
   const int64_t i = bid / ((int64_t)NCT * a.Hv);
   const size_t KV = (size_t)K * V, KK = (size_t)K * K;
   const int c0 = ct * CT;
-  for (int x = tid; x < K * CT; x += 256) {
+  for (int x = tid; x < K * CT; x += NT) {
     const int r = x / CT, c = x % CT;
     S[r][c] = a.s0 ? a.s0[((size_t)i * a.Hv + h) * KV + (size_t)r * V + c0 + c] : 0.f;
   }
@@ -174,31 +185,42 @@ __global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
   auto load_m = [&](int64_t s) {
     const f4 *M = (const f4 *)(a.msum + ((size_t)s * a.Hv + h) * KK);
 #pragma unroll
-    for (int u = 0; u < NL; ++u) mreg[u] = M[tid + 256 * u];
+    for (int u = 0; u < NL; ++u) mreg[u] = M[tid + NT * u];
   };
-  if (s_lo < s_hi) load_m(s_lo);
+  // this wave's rows of the segment's B tile, also loaded a segment ahead
+  f32x4 breg[RT];
+  auto load_b = [&](int64_t s) {
+    const float *B = a.bsum + ((size_t)s * a.Hv + h) * KV + c0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) breg[rt][e] = B[(size_t)(w * 16 * RT + 16 * rt + 4 * lg + e) * V + lr];
+  };
+  if (s_lo < s_hi) {
+    load_m(s_lo);
+    load_b(s_lo);
+  }
   __syncthreads();
   for (int64_t s = s_lo; s < s_hi; ++s) {
     // this segment's M into LDS (element x of the row-major M at row x / K, column x % K)
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int x = 4 * (tid + 256 * u), r = x / K, c = x % K;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Ms[r * LDM + c + e] = mreg[u][e];
+      const int x = 4 * (tid + NT * u), r = x / K, c = x % K;
+      *(f4 *)&Ms[r * LDM + c] = mreg[u];
     }
-    if (s + 1 < s_hi) load_m(s + 1);
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = breg[rt];
+    if (s + 1 < s_hi) {
+      load_m(s + 1);
+      load_b(s + 1);
+    }
     float *init = a.seg_init + ((size_t)s * a.Hv + h) * KV + c0;
-    for (int x = tid; x < K * CT; x += 256) {
+    for (int x = tid; x < K * CT; x += NT) {
       const int r = x / CT, c = x % CT;
       init[(size_t)r * V + c] = S[r][c];
     }
-    const float *B = a.bsum + ((size_t)s * a.Hv + h) * KV + c0;
-    f32x4 acc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[rt][e] = B[(size_t)(w * 16 * RT + 16 * rt + 4 * lg + e) * V + lr];
-    __syncthreads();  // M in LDS
+    lds_sync();  // M in LDS
 #pragma unroll 8
     for (int kk = 0; kk < K / 4; ++kk) {
       const int kx = 4 * kk + lg;
@@ -207,12 +229,12 @@ __global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
       for (int rt = 0; rt < RT; ++rt)
         acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ms[(w * 16 * RT + 16 * rt + lr) * LDM + kx], bv, acc[rt], 0, 0, 0);
     }
-    __syncthreads();  // every wave has read S and M
+    lds_sync();  // every wave has read S and M
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[w * 16 * RT + 16 * rt + 4 * lg + e][lr] = acc[rt][e];
-    __syncthreads();
+    lds_sync();
   }
   float *fdst = a.final_state ? a.final_state + ((size_t)i * a.Hv + h) * KV + c0 : nullptr;
   float *cdst = nullptr;
@@ -220,7 +242,7 @@ __global__ void __launch_bounds__(256) gdp_combine_kernel(CombineArgs a) {
     const int64_t slot = seg_index_at(a.slots, a.slots_is64, i);
     if (slot >= 0 && slot < a.num_slots) cdst = a.cache + ((size_t)slot * a.Hv + h) * KV + c0;
   }
-  for (int x = tid; x < K * CT; x += 256) {
+  for (int x = tid; x < K * CT; x += NT) {
     const int r = x / CT, c = x % CT;
     if (fdst) fdst[(size_t)r * V + c] = S[r][c];
     if (cdst) cdst[(size_t)r * V + c] = S[r][c];
@@ -256,7 +278,7 @@ hipError_t launch_order(const OrderArgs &a, hipStream_t stream) {
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.N * a.Hv * (V / 16);
   if (blocks == 0) return hipSuccess;
-  if (K == 128 && V == 128) hipLaunchKernelGGL((gdp_combine_kernel<128, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (K == 128 && V == 128) hipLaunchKernelGGL((gdp_combine_kernel<128, 128>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
   else if (K == 64 && V == 64) hipLaunchKernelGGL((gdp_combine_kernel<64, 64>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
