@@ -336,3 +336,15 @@ def test_prefill_accepts_k_per_state_head(b):
     a = base_args(b)
     a["k"] = a["fake"].tensor(b, b.GDP_BF16, [200, 3, 128])
     expect(b, a, b.GDP_EINVAL, "Hqk or Hv heads")
+
+
+def test_debug_status_requires_a_word(b):
+    """The word pointer is checked before any runtime call."""
+    assert b.LIB.gdp_debug_status(None, 0, None) == b.GDP_EINVAL
+    assert "word" in b.gdp_last_error()
+
+
+def test_debug_bits_match_the_header(b):
+    text = open(HEADER).read()
+    for name, val in (("GDP_DBG_CU", b.GDP_DBG_CU), ("GDP_DBG_SLOT", b.GDP_DBG_SLOT), ("GDP_DBG_DUP", b.GDP_DBG_DUP)):
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
