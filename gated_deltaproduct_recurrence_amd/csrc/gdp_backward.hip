@@ -21,19 +21,22 @@
 // every 64-token chunk (return_chunk_states); per chunk this kernel re-runs the
 // recurrence once to keep the state entering every 8th token in LDS, and once
 // per 8-token block to hold the 8 token states in registers, then walks the
-// block backwards.  One wave owns one (sequence, state head, 8-column V tile):
-// lane (c, rg) = (lane / 8, lane % 8) holds rows 16 rg .. 16 rg + 15 (K = 128;
-// 8 rows for K = 64) of column c, so a column dot over K (on the recurrence's
-// critical path) is a sum over 8 adjacent lanes, done with DPP moves.  Sums over
-// the tile's 8 columns (lane bits 3 .. 5) stay in the VALU too: the 16 row
-// entries of a dq or dk partial are reduce-scattered over those lanes with the
-// gfx950 half-wave and row swaps and a DPP row rotation, so that each lane ends
-// with two finished entries.  Gradients shared by several waves (dq, dk: all V
-// tiles and the state heads of a q/k head; dbeta, dg_log: all V tiles) go to
-// per-wave LDS slots; every few tokens the workgroup (four adjacent V tiles of
-// one chain) sums the four waves' slots after a barrier and adds the sums to the
-// zeroed output buffers with one float atomic per element.  dv is stored there
-// too, coalesced over the workgroup's columns.
+// block backwards.  One wave owns one (sequence, state head, V tile of VT
+// columns): VT = 4 for K = 128 and 8 for K = 64, with 64 / VT row groups of 8
+// state rows; lane = (64 / VT) c + rg holds rows 8 rg .. 8 rg + 7 of column c.
+// A column dot over K (on the recurrence's critical path) is then a sum over
+// the adjacent lanes of one column, done with DPP moves.  Sums over the tile's
+// columns stay in the VALU too: the 8 row entries of a dq or dk partial are
+// reduce-scattered over the column lanes with the gfx950 half-wave and row
+// swaps (and, for 8 columns, a DPP row rotation), so that each lane ends with
+// finished entries.  Gradients shared by several waves (dq, dk: all V tiles and
+// the state heads of a q/k head; dbeta, dg_log: all V tiles) go to per-wave LDS
+// slots; every few tokens the workgroup (four adjacent V tiles of one chain)
+// sums the four waves' slots after a barrier and adds the sums to the zeroed
+// output buffers with one float atomic per element.  dv is stored there too,
+// coalesced over the workgroup's columns.  A workgroup stays within half the
+// CU's LDS and, for n <= 2 with bfloat16 inputs, 256 registers, so two run per
+// CU and each SIMD has a second wave to cover stalls.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,9 +47,9 @@ namespace gdp {
 namespace {
 
 constexpr int CH = 64;     // token chunk of the forward pass's chunk states
-constexpr int VT = 8;      // columns per wave
 constexpr int BLK = 8;     // tokens per register block (checkpoint spacing)
 constexpr int NMAX = 3;    // Householder rows per token served
+constexpr int RKL = 8;     // state rows per lane
 constexpr float LOG2E_B = 1.4426950408889634f;
 
 __device__ __forceinline__ int64_t idx_at(const void *p, int is64, int64_t i) {
@@ -61,12 +64,15 @@ template <int LO, int HI> __device__ __forceinline__ float xsum(float x) {
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
-// sum over the 8 lanes of an aligned group (the lane's row groups of one column),
-// with DPP only: swap neighbours, swap pairs, then the two quads of the half row
-__device__ __forceinline__ float col_sum(float x) {
+// sum over the RG lanes of an aligned group (the row groups of one column), in
+// every lane, with DPP only: swap neighbours, swap pairs, the two quads of the
+// half row, then (RG = 16) the two halves of the row
+template <int RG> __device__ __forceinline__ float col_sum(float x) {
+  static_assert(RG == 8 || RG == 16, "8 or 16 row groups");
   x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
   x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
   x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (RG == 16) x += dpp_mov<0x140>(x);  // row_mirror
   return x;
 }
 // x + the value of the lane whose index differs in bit 5 (W32) or bit 4, for
@@ -86,31 +92,42 @@ template <bool W32> __device__ __forceinline__ float swap_add(float x, float y) 
   }
   return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
-// sum over the 8 columns of the tile (lane bits 3 .. 5), in every lane
-__device__ __forceinline__ float row_all(float x) {
+// sum over the VT columns of the tile (lane bits 3 .. 5 for 8 columns, 4 .. 5
+// for 4), in every lane
+template <int VT> __device__ __forceinline__ float row_all(float x) {
   x = swap_add<true>(x, x);
   x = swap_add<false>(x, x);
-  return x + dpp_mov<0x128>(x);  // row_ror:8, i.e. the lane with bit 3 flipped
+  if constexpr (VT == 8) x += dpp_mov<0x128>(x);  // row_ror:8, i.e. the lane with bit 3 flipped
+  return x;
 }
-// Reduce-scatter over the 8 columns: v holds the lane's R row entries of one
+// Reduce-scatter over the VT columns: v holds the lane's R row entries of one
 // column; afterwards out[p] is, in lane (c, rg), the sum over the columns of
-// entry (R / 8) c + p.  Each stage halves the entries: the lanes with the stage's
-// lane bit clear keep the lower half, the others the upper half.
-template <int R> __device__ __forceinline__ void row_scatter(const float (&v)[R], float (&out)[R / 8], bool bit3) {
+// entry (R / VT) c + p.  Each stage halves the entries: the lanes with the
+// stage's lane bit clear keep the lower half, the others the upper half.
+template <int R, int VT> __device__ __forceinline__ void row_scatter(const float (&v)[R], float (&out)[R / VT], bool bit3) {
+  static_assert(VT == 4 || VT == 8, "4 or 8 columns");
   float a[R / 2], b[R / 4];
 #pragma unroll
   for (int p = 0; p < R / 2; ++p) a[p] = swap_add<true>(v[p], v[p + R / 2]);
 #pragma unroll
   for (int p = 0; p < R / 4; ++p) b[p] = swap_add<false>(a[p], a[p + R / 4]);
+  if constexpr (VT == 4) {
 #pragma unroll
-  for (int p = 0; p < R / 8; ++p) {
-    const float keep = bit3 ? b[p + R / 8] : b[p], send = bit3 ? b[p] : b[p + R / 8];
-    out[p] = keep + dpp_mov<0x128>(send);
+    for (int p = 0; p < R / 4; ++p) out[p] = b[p];
+  } else {
+#pragma unroll
+    for (int p = 0; p < R / 8; ++p) {
+      const float keep = bit3 ? b[p + R / 8] : b[p], send = bit3 ? b[p] : b[p + R / 8];
+      out[p] = keep + dpp_mov<0x128>(send);
+    }
   }
 }
 
 template <typename T, int K, int V, int NH> struct Bwd {
-  static constexpr int RK = K / 8;                     // rows per lane
+  // a wave owns VT columns (4 for K = 128, 8 for K = 64) with RG row groups of
+  // RK = 8 rows each: lane = RG c + rg
+  static constexpr int VT = K == 128 ? 4 : 8, RG = 64 / VT, RK = K / RG;
+  static_assert(RK == RKL, "eight state rows per lane");
   static constexpr int RW = RK * (int)sizeof(T) / 16;  // 16-byte words holding them
   static_assert(RW >= 1, "at least one 16-byte word per lane");
   // the inputs of one token (loaded a token ahead of their use), all as loaded
@@ -184,7 +201,7 @@ template <typename T, int K, int V, int NH> struct Bwd {
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(S[i], kv[i], part);
-        const float e = x.b[j] * ((float)x.v[j] - x.rk[j] * col_sum(part));
+        const float e = x.b[j] * ((float)x.v[j] - x.rk[j] * col_sum<RG>(part));
         const float ek = e * x.rk[j];
 #pragma unroll
         for (int i = 0; i < RK; ++i) S[i] = fmaf(kv[i], ek, S[i]);
@@ -194,10 +211,10 @@ template <typename T, int K, int V, int NH> struct Bwd {
 };
 
 template <typename T, int K, int V, int NH>
-__global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, (NH <= 2 && sizeof(T) == 2) ? 2 : 1) gdp_backward_kernel(BwdArgs a) {
   using B = Bwd<T, K, V, NH>;
   using In = typename B::In;
-  constexpr int RK = B::RK, NVT = V / VT;
+  constexpr int RK = B::RK, VT = B::VT, RG = B::RG, NVT = V / VT;
   // tokens in flight in the forward passes (two where the rows take more registers)
   constexpr int PF = RK * NH > 32 ? 2 : 4;
   // per wave: the state entering each 8-token block of the chunk (64 tokens)
@@ -205,7 +222,13 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   // per token of the current group of F tokens: each wave's finished entries of
   // the dq row (slot 0) and the dk rows (slot 1 + j), summed over the four waves
   // when the group is flushed (sized so that the checkpoints and these fit in LDS)
-  constexpr int F = K == 64 ? 8 : (NH <= 2 ? 4 : 2);
+  // F: the largest of 8, 4, 2, 1 tokens whose slots fit beside the other arrays
+  // in half the CU's LDS (two workgroups per CU)
+  constexpr int LDS_HALF = 80 * 1024;
+  constexpr int FIXED = 4 * (CH / BLK) * RK * 64 * 4 + BLK * (NH + 1) * 4 * 4 + BLK * NH * 4 * VT * 4;
+  constexpr int SLOT = (NH + 1) * 4 * K * 4;
+  constexpr int F = FIXED + 8 * SLOT <= LDS_HALF ? 8 : FIXED + 4 * SLOT <= LDS_HALF ? 4 : FIXED + 2 * SLOT <= LDS_HALF ? 2 : 1;
+  static_assert(FIXED + F * SLOT <= LDS_HALF, "two workgroups per CU");
   __shared__ float wsl[F][NH + 1][4][K];
   // per token of the block and wave, the wave's dg_log (slot 0) and dbeta
   // (slot 1 + j) partials, summed over the waves at the flush
@@ -214,10 +237,10 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   // the wave owning the column, stored with its group's flush)
   __shared__ float dvs[BLK][NH][4 * VT];
   B s(a);
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform per wave: the chain and its addresses stay scalar
   s.lane = threadIdx.x & 63;
-  s.rg = s.lane & 7;
-  s.c = s.lane >> 3;
+  s.rg = s.lane % RG;
+  s.c = s.lane / RG;
   const int64_t wid = (int64_t)blockIdx.x * 4 + w;
   const int64_t nw = (int64_t)a.N * a.Hv * NVT;
   if (wid >= nw) return;  // never taken: the grid holds exactly nw waves (V / 8 is a multiple of 4)
@@ -235,7 +258,7 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
   const size_t hoff = (size_t)s.h * KV + (size_t)(RK * s.rg) * V + s.col;  // within one [Hv, K, V] state; + i * V
   const size_t soff = (size_t)s.seq * a.Hv * KV + hoff;
   float *my_ck = &ck[w][0][0];
-  const bool bit3 = (s.lane >> 3) & 1;
+  const bool bit3 = (s.lane >> 3) & 1;  // (8 columns: the last reduce-scatter stage)
 
   float dS[RK];
 #pragma unroll
@@ -331,7 +354,7 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
               Sj[j][i] = st[i];
               part = fmaf(st[i], kv[i], part);
             }
-            u[j] = (float)cur.v[j] - cur.rk[j] * col_sum(part);
+            u[j] = (float)cur.v[j] - cur.rk[j] * col_sum<RG>(part);
             e[j] = cur.b[j] * u[j];
             const float ek = e[j] * cur.rk[j];
 #pragma unroll
@@ -340,19 +363,19 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
         }
         // readout: o_t = scale S_t^T q_t
         float(*wm)[4][K] = wsl[m % F];
-        const int el0 = RK * s.rg + (RK / 8) * s.c;  // the row entries this lane finishes
+        const int el0 = RK * s.rg + (RK / VT) * s.c;  // the row entries this lane finishes
         {
           const float dov = (float)cur.dov * a.scale, dovq = dov * cur.rq;
-          float qv[RK], pq[RK], oq[RK / 8];
+          float qv[RK], pq[RK], oq[RK / VT];
           s.row(qv, cur.q);
 #pragma unroll
           for (int i = 0; i < RK; ++i) {
             pq[i] = st[i] * dov;
             dS[i] = fmaf(qv[i], dovq, dS[i]);
           }
-          row_scatter<RK>(pq, oq, bit3);
+          row_scatter<RK, VT>(pq, oq, bit3);
 #pragma unroll
-          for (int p = 0; p < RK / 8; ++p) wm[0][w][el0 + p] = oq[p];
+          for (int p = 0; p < RK / VT; ++p) wm[0][w][el0 + p] = oq[p];
         }
 #pragma unroll
         for (int j = NH - 1; j >= 0; --j) {
@@ -362,27 +385,27 @@ __global__ void __launch_bounds__(256) gdp_backward_kernel(BwdArgs a) {
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < RK; ++i) part = fmaf(dS[i], kv[i], part);
-            const float de = cur.rk[j] * col_sum(part);  // equal in the column's 8 lanes
+            const float de = cur.rk[j] * col_sum<RG>(part);  // equal in the column's RG lanes
             const float du = cur.b[j] * de, duk = du * cur.rk[j];
             dvs[m][j][VT * w + s.c] = du;
-            const float db = row_all(de * u[j]);
+            const float db = row_all<VT>(de * u[j]);
             if (s.lane == 0) scal[m][1 + j][w] = db;
-            float pk[RK], ok[RK / 8];
+            float pk[RK], ok[RK / VT];
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
               pk[i] = fmaf(dS[i], e[j], -Sj[j][i] * du);
               dS[i] = fmaf(-kv[i], duk, dS[i]);
             }
-            row_scatter<RK>(pk, ok, bit3);
+            row_scatter<RK, VT>(pk, ok, bit3);
 #pragma unroll
-            for (int p = 0; p < RK / 8; ++p) wm[1 + j][w][el0 + p] = ok[p];
+            for (int p = 0; p < RK / VT; ++p) wm[1 + j][w][el0 + p] = ok[p];
           }
         }
         // decay
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < RK; ++i) part = fmaf(dS[i], ST[m][i], part);
-        const float dal = row_all(col_sum(part));
+        const float dal = row_all<VT>(col_sum<RG>(part));
         if (s.lane == 0) scal[m][0][w] = dal * al;
 #pragma unroll
         for (int i = 0; i < RK; ++i) dS[i] *= al;
@@ -486,6 +509,7 @@ __global__ void __launch_bounds__(256) gdp_row_norm_kernel(NormGradArgs a) {
 }
 
 template <typename T, int K, int V, int NH> hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream) {
+  constexpr int VT = Bwd<T, K, V, NH>::VT;
   static_assert((V / VT) % 4 == 0, "a workgroup holds four V tiles of one chain");
   const int64_t waves = (int64_t)a.N * a.Hv * (V / VT);
   if (waves == 0) return hipSuccess;
