@@ -352,3 +352,26 @@ def test_longest_first_order_every_chain(gdp, N, Hqk, Hv, monkeypatch):
     assert rel_err(to_np(dev["state_cache"][slots]), ref["state_cache"][slots]) <= tol
     untouched = sorted(set(range(N + 3)) - set(slots.tolist()))
     assert torch.equal(dev["state_cache"][untouched], cache0[untouched])
+
+
+@pytest.mark.parametrize("N", [1500, 5000], ids=["N1500-ordered", "N5000-unordered"])
+@pytest.mark.parametrize("kpath", ["fused", "split"])
+def test_many_short_sequences(gdp, N, kpath, monkeypatch):
+    """Thousands of sequences of 0..6 tokens: the descriptor scan over several
+    1024-sequence passes, the longest-first work order (up to 4096 sequences;
+    beyond that the grid runs in sequence order), zero-length sequences, and
+    chunk states, against the oracle."""
+    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    lens = np.random.default_rng(N).integers(0, 7, size=N).tolist()
+    w = workloads.custom(lens, 2, 1, 2, 64, 64, dtype=torch.bfloat16, init_std=0.2, seed=N)
+    inp = workloads.generate(w, "cpu")
+    inp["return_chunk_states"] = True
+    ref = oracle_run(inp)
+    o, fs, cs, offs = gdp.chunk_prefill(**to_device(inp))
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    assert rel_err(to_np(o), ref["o"]) <= tol
+    assert rel_err(to_np(fs), ref["final_state"]) <= tol
+    NT = int(offs[-1].item())
+    assert NT == ref["chunk_states"].shape[0] == sum(1 for L in lens if L > 0)
+    assert rel_err(to_np(cs[:NT]), ref["chunk_states"]) <= tol
