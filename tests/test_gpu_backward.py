@@ -146,3 +146,51 @@ def test_backward_strided_d_o_and_dv(gdp):
         e = rel_err(to_np(x), ref[name])
         assert e <= tol, f"{name} err {e:.3e}"
     assert torch.isnan(dv_wide[:, :2]).all(), "dv wrote outside its view"
+
+
+def test_backward_graph_capture_replay(gdp):
+    """The backward call (forward rerun, fills, backward and norm kernels) is
+    captured in a HIP graph and replayed three times, with eager work between
+    the replays: every replay matches the eager call (float atomics may reorder
+    the last bits) and the oracle."""
+    lens, n, Hqk, Hk, Hv, K, V, dt, l2, init, dfin = CASES[0]
+    w = workloads.custom(lens, n, Hqk, Hv, K, V, dtype=dt, l2norm_in_kernel=l2, init_std=0.2, seed=100)
+    inp = {k: (x.cuda() if isinstance(x, torch.Tensor) else x) for k, x in workloads.generate(w, "cpu").items()}
+    gen = torch.Generator().manual_seed(200)
+    T, N = w.T, w.N
+    d_o = torch.randn(T, Hv, V, generator=gen).to(dt).cuda()
+    f32 = dict(dtype=torch.float32, device="cuda")
+    outs = {"dq": torch.empty((T, Hqk, K), **f32), "dk": torch.empty((T * n, Hk, K), **f32),
+            "dv": torch.empty((T * n, Hv, V), **f32), "dg_log": torch.empty((T, Hv), **f32),
+            "dbeta": torch.empty((T * n, Hv), **f32), "dinitial_state": torch.empty((N, Hv, K, V), **f32)}
+    ws = torch.empty(gdp.gdp_backward_workspace_bytes(T, N, n, Hqk, Hv, K, V, dt), dtype=torch.uint8, device="cuda")
+
+    def call():
+        gdp.gdp_chunk_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, inp["cu_seqlens"],
+                                       0.0, inp["initial_state"], l2, d_o, None, outs["dq"], outs["dk"], outs["dv"],
+                                       outs["dg_log"], outs["dbeta"], outs["dinitial_state"], ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = {k: x.clone() for k, x in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    ref = obwd.backward(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(inp["g_log"]), to_np(inp["beta"]), n,
+                        inp["cu_seqlens"].cpu().numpy(), to_np(d_o), None, initial_state=to_np(inp["initial_state"]),
+                        use_qk_l2norm=l2)
+    for rep in range(3):
+        for x in outs.values():
+            x.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x in outs.items():
+            assert rel_err(to_np(x), to_np(eager[name])) <= 1e-5, f"replay {rep}: {name} differs from eager"
+            assert rel_err(to_np(x), ref[name]) <= TOL[dt], f"replay {rep}: {name} vs oracle"
+        call()  # eager work between the replays
+        torch.cuda.synchronize()
