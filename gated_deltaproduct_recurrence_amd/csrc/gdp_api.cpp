@@ -687,7 +687,7 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   if (N < 0 || Hqk < 1 || Hv < 1 || Hk < 1) return fail(GDP_EINVAL, "bad sizes");
   if (Hv % Hqk != 0 || (Hk != Hqk && Hk != Hv)) return fail(GDP_EINVAL, "head counts: Hv a multiple of Hqk, Hk = Hqk or Hv");
   if (!gdp::backward_supported((int)K, (int)V, n))
-    return fail(GDP_EUNSUPPORTED, "backward needs K, V in {64, 128} and num_householder <= 3");
+    return fail(GDP_EUNSUPPORTED, "backward needs K, V in {64, 128} and num_householder <= 5");
   const int32_t dt = q->dtype;
   if (dt != GDP_F32 && dt != GDP_BF16) return fail(GDP_EUNSUPPORTED, "q must be float32 or bfloat16");
   if (d_o->dtype != dt) return fail(GDP_EUNSUPPORTED, "d_o must have q's dtype");

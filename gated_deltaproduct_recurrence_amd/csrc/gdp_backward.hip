@@ -48,7 +48,7 @@ namespace {
 
 constexpr int CH = 64;     // token chunk of the forward pass's chunk states
 constexpr int BLK = 8;     // tokens per register block (checkpoint spacing)
-constexpr int NMAX = 3;    // Householder rows per token served
+constexpr int NMAX = 5;    // Householder rows per token served
 constexpr int RKL = 8;     // state rows per lane
 constexpr float LOG2E_B = 1.4426950408889634f;
 
@@ -523,6 +523,8 @@ template <typename T, int K, int V> hipError_t launch_bwd(const BwdArgs &a, hipS
     case 1: return launch_bwd_n<T, K, V, 1>(a, stream);
     case 2: return launch_bwd_n<T, K, V, 2>(a, stream);
     case 3: return launch_bwd_n<T, K, V, 3>(a, stream);
+    case 4: return launch_bwd_n<T, K, V, 4>(a, stream);
+    case 5: return launch_bwd_n<T, K, V, 5>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

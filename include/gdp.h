@@ -225,7 +225,7 @@ size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t num_householde
  *   d_initial_state [N, Hv, K, V]  float32 contiguous, or data == NULL
  *   workspace      at least gdp_backward_workspace_bytes(...), 256-byte aligned
  * No gradient may overlap an input or another gradient (GDP_EALIAS).  K, V in
- * {64, 128}, num_householder <= 3 (GDP_EUNSUPPORTED otherwise).  Everything
+ * {64, 128}, num_householder <= 5 (GDP_EUNSUPPORTED otherwise).  Everything
  * runs on `stream` with no allocation and no host read of device memory. */
 int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
                                const gdp_tensor *g_log, const gdp_tensor *beta, int32_t num_householder,

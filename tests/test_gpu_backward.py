@@ -25,6 +25,8 @@ CASES = [
     ([100, 29], 1, 1, 2, 2, 64, 128, torch.bfloat16, True, False, True),
     ([65, 63], 3, 2, 2, 2, 128, 64, torch.bfloat16, False, False, False),
     ([45, 80], 2, 2, 4, 4, 128, 128, torch.bfloat16, True, True, False),
+    ([30, 41], 4, 1, 2, 2, 128, 128, torch.bfloat16, True, True, True),
+    ([19, 0, 26], 5, 1, 1, 2, 64, 64, torch.bfloat16, False, True, False),
 ]
 
 
