@@ -237,7 +237,8 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
                                void *stream);
 
 /* Host-only.  Workspace bytes gdp_chunk_gated_delta_product needs: the gates
- * restated as float32 log decays and betas (4 (1 + n) T Hv bytes), a float32
+ * restated as float32 log decays and betas (4 (1 + n) T Hv bytes; the betas are
+ * used only when they are not float32 already), a float32
  * K-major copy of each state it converts (4 N Hv d^2 bytes each, when an
  * initial state is given and when the final state is requested), and the
  * workspace of the prefill it runs (gdp_workspace_bytes); with float16 inputs
@@ -260,7 +261,8 @@ size_t gdp_fi_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int
  *                  bfloat16, is converted to float16
  *   g    [T, Hv]   the decay alpha itself (in (0, 1]), float32, bfloat16 or float16,
  *                  or data == NULL for no decay (alpha = 1)
- *   beta [T*n, Hv] float32 or q's dtype, or data == NULL for all ones
+ *   beta [T*n, Hv] float32 (read in place, strides honoured) or q's dtype, or
+ *                  data == NULL for all ones
  *   scale          0 means d^-1/2
  *   initial_state  [N, Hv, d, d] V-major (entry [v][k]), float32 or bfloat16,
  *                  contiguous, or data == NULL for zero states
