@@ -168,7 +168,7 @@ struct FiLayout {
   size_t glog = 0, beta = 0, s0 = 0, fin = 0, q = 0, k = 0, v = 0, o = 0, inner = 0, total = 0;
 };
 // float16 inputs add bfloat16 copies of q, k, v and the output (k sized for Hk = Hv)
-FiLayout fi_layout(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int32_t d, int32_t dtype,
+static FiLayout fi_layout(int64_t T, int64_t N, int32_t n, int32_t Hq, int32_t Hv, int32_t d, int32_t dtype,
                    bool with_initial, bool with_final) {
   FiLayout L;
   const size_t st = align256((size_t)N * Hv * d * d * 4);
@@ -539,7 +539,9 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   } else {
     if (!d->chunk_indices_dp || !d->chunk_offsets || !d->chunk_offsets_dp)
       return fail(GDP_EINVAL, "caller descriptors need chunk_indices_dp, chunk_offsets and chunk_offsets_dp");
-    if (d->ntdp_cap < 0) return fail(GDP_EINVAL, "caller descriptors: negative capacity");
+    if (d->nt_cap < nt_cap || d->ntdp_cap < ntdp_cap)
+      return fail(GDP_EINVAL, "caller descriptors hold capacities %lld / %lld, below the bounds %lld / %lld for (T, N, n)",
+                  (long long)d->nt_cap, (long long)d->ntdp_cap, (long long)nt_cap, (long long)ntdp_cap);
   }
 
   gdp::PrefillArgs a;
@@ -642,7 +644,7 @@ struct BwdLayout {
   size_t desc = 0, cs = 0, o = 0, rn = 0, fwd = 0, total = 0;
   int64_t nt_cap = 0, ntdp_cap = 0;
 };
-BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V, int32_t dtype) {
+static BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V, int32_t dtype) {
   BwdLayout L;
   if (gdp_descriptor_capacity(T, N, n, &L.nt_cap, &L.ntdp_cap) != GDP_OK) return L;
   const size_t fwd = gdp_workspace_bytes(T, N, n, Hqk, Hv, K, V, dtype);
@@ -790,6 +792,7 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   a.T = T; a.N = (int)N; a.n = n; a.Hqk = (int)Hqk; a.Hv = (int)Hv; a.Hk = (int)Hk;
   a.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
   a.chunk_states = (const float *)(ws + L.cs);
+  a.cs_rows = csr;
   a.chunk_offsets = d.chunk_offsets;
   a.dout = d_o->data; a.do_st = d_o->stride[0]; a.do_sh = d_o->stride[1];
   a.dfinal = present(d_final_state) ? (const float *)d_final_state->data : nullptr;
@@ -801,6 +804,14 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   a.ds0 = present(d_initial_state) ? (float *)d_initial_state->data : nullptr;
   if ((e = gdp::launch_backward(a, idt, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
     return fail(GDP_EHIP, "backward launch: %s", hipGetErrorString(e));
+  {  // the rows of dv no sequence covers (before cu[0] or from cu[N] on) are zero
+    gdp::ZeroOutsideArgs z;
+    z.p = (float *)dv->data; z.st = dv->stride[0]; z.sh = dv->stride[1];
+    z.cu = cu_seqlens->data; z.cu_is64 = cu_seqlens->dtype == GDP_I64;
+    z.T = T; z.N = (int)N; z.n = n; z.heads = (int)Hv; z.D = (int)V;
+    if ((e = gdp::launch_zero_outside(z, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
+  }
   if (use_qk_l2norm) {
     gdp::NormGradArgs na;
     na.x = q->data; na.x_st = q->stride[0]; na.x_sh = q->stride[1];

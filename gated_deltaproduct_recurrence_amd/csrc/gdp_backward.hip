@@ -272,10 +272,14 @@ __global__ void __launch_bounds__(256, (NH <= 2 && sizeof(T) == 2) ? 2 : 1) gdp_
     const int ntok = (int)((t1 - tb) < CH ? (t1 - tb) : CH);
     const int nblk = (ntok + BLK - 1) / BLK;
     // the state entering the chunk, then the state entering every 8th token
+    // (the row comes from descriptors built on cu_seqlens; contents that are not
+    // monotone can place it outside the buffer, and then no state is read)
     float S[RK];
-    const float *src = a.chunk_states + (size_t)((int64_t)a.chunk_offsets[s.seq] + cc) * a.Hv * KV + hoff;
+    const int64_t csrow = (int64_t)a.chunk_offsets[s.seq] + cc;
+    const bool csok = csrow >= 0 && csrow < a.cs_rows;
+    const float *src = a.chunk_states + (size_t)(csok ? csrow : 0) * a.Hv * KV + hoff;
 #pragma unroll
-    for (int i = 0; i < RK; ++i) S[i] = src[(size_t)i * V];
+    for (int i = 0; i < RK; ++i) S[i] = csok ? src[(size_t)i * V] : 0.f;
     const int nstep = BLK * (nblk - 1);  // tokens before the last block's start (a multiple of 8)
     // (block 0's entry is stored before the loop, so that the loop waits for no
     // state load)
@@ -508,6 +512,27 @@ __global__ void __launch_bounds__(256) gdp_row_norm_kernel(NormGradArgs a) {
   if (lane == 0) a.g[r * a.g_st + hh * a.g_sh] = __builtin_amdgcn_rsqf(ss + 1e-6f);
 }
 
+// Zero the rows of a [T*n, heads, D] float32 tensor (row stride st, head stride
+// sh, elements contiguous) that no sequence covers: sub-rows before cu[0]*n and
+// from cu[N]*n on (bounds clamped to [0, T] as the other kernels clamp them).
+// The backward kernel writes every other row of dv.
+__global__ void __launch_bounds__(256) gdp_zero_outside_kernel(ZeroOutsideArgs a) {
+  int64_t lo = idx_at(a.cu, a.cu_is64, 0), hi = idx_at(a.cu, a.cu_is64, a.N);
+  lo = lo < 0 ? 0 : (lo > a.T ? a.T : lo);
+  hi = hi < lo ? lo : (hi > a.T ? a.T : hi);
+  lo *= a.n;
+  hi *= a.n;
+  const int64_t R = a.T * a.n, per_row = (int64_t)a.heads * a.D;
+  const int64_t total = (lo + (R - hi)) * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i / per_row;
+    const int64_t rem = i - r * per_row;
+    const int hh = (int)(rem / a.D), d = (int)(rem - (int64_t)hh * a.D);
+    if (r >= lo) r += hi - lo;
+    a.p[r * a.st + hh * a.sh + d] = 0.f;
+  }
+}
+
 template <typename T, int K, int V, int NH> hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream) {
   constexpr int VT = Bwd<T, K, V, NH>::VT;
   static_assert((V / VT) % 4 == 0, "a workgroup holds four V tiles of one chain");
@@ -546,6 +571,12 @@ hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_
     if (K == 64 && V == 64) return launch_bwd<float, 64, 64>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_outside(const ZeroOutsideArgs &a, hipStream_t stream) {
+  if (a.T * a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gdp_zero_outside_kernel, dim3(256), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_row_norm(const NormGradArgs &a, int dtype, int K, hipStream_t stream) {

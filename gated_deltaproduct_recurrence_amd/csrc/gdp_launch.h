@@ -141,7 +141,9 @@ struct BwdArgs {
   // a single 1 with zero strides
   const float *rq; int64_t rq_st, rq_sh;
   const float *rk; int64_t rk_st, rk_sh;
-  const float *chunk_states;                // [NT, Hv, K, V]: state entering each token chunk
+  const float *chunk_states;                // [cs_rows, Hv, K, V]: state entering each token chunk
+  int64_t cs_rows;                          // rows of chunk_states; a row index outside [0, cs_rows)
+                                            // (bad cu_seqlens contents) reads a zero state instead
   const int32_t *chunk_offsets;             // [N+1]
   const void *dout; int64_t do_st, do_sh;   // [T, Hv, V], the inputs' dtype
   const float *dfinal;                      // [N, Hv, K, V] or null
@@ -155,6 +157,15 @@ struct BwdArgs {
 };
 bool backward_supported(int K, int V, int n);
 hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_t stream);
+
+// Zero fill of the rows of a strided [T*n, heads, D] float32 tensor that lie
+// outside [cu[0]*n, cu[N]*n) (the rows no sequence covers).
+struct ZeroOutsideArgs {
+  float *p; int64_t st, sh;
+  const void *cu; int cu_is64;
+  int64_t T; int N, n, heads, D;
+};
+hipError_t launch_zero_outside(const ZeroOutsideArgs &a, hipStream_t stream);
 
 // Gradient with respect to raw rows from the one with respect to their L2-normalised
 // versions, in place (rows = R * heads rows of a [R, heads, K] tensor).

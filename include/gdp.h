@@ -146,7 +146,10 @@ size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_
  *                                 return_chunk_states).  Rows past the real count
  *                                 are left untouched.
  *   desc         caller-built descriptors (gdp_build_descriptors) or NULL; when
- *                NULL they are built into the workspace on `stream`
+ *                NULL they are built into the workspace on `stream`.  Their
+ *                capacities must be at least gdp_descriptor_capacity(T, N, n)
+ *                (GDP_EINVAL otherwise: descriptors built for a smaller T or a
+ *                different n would leave chunks out of the grids)
  *   workspace    device scratch, 256-byte aligned, of workspace_bytes >=
  *                gdp_workspace_bytes(...) (required: it holds the per-chunk WY
  *                matrices between the two kernels of the call)
@@ -221,7 +224,10 @@ size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t num_householde
  *                                  float32, contiguous: they are accumulated with
  *                                  float atomics over state heads and V tiles, so
  *                                  their last bits depend on the order of the adds
- *   dv [T*n, Hv, V]                float32, rows may be strided
+ *   dv [T*n, Hv, V]                float32, rows may be strided; the sub-rows no
+ *                                  sequence covers (before cu_seqlens[0]*n or from
+ *                                  cu_seqlens[N]*n on) are written as zeros, like
+ *                                  the other gradients' rows there
  *   d_initial_state [N, Hv, K, V]  float32 contiguous, or data == NULL
  *   workspace      at least gdp_backward_workspace_bytes(...), 256-byte aligned
  * No gradient may overlap an input or another gradient (GDP_EALIAS).  K, V in

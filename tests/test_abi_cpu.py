@@ -212,6 +212,21 @@ def test_build_descriptors_capacity_check(b):
     assert rc == b.GDP_EINVAL and "below the bound" in b.gdp_last_error()
 
 
+@pytest.mark.parametrize("caps", [(2, 5), (3, 4)], ids=["token-capacity", "expanded-capacity"])
+def test_caller_descriptors_below_the_bound(b, caps):
+    """Caller descriptors built for a smaller T (or another n) would leave
+    chunks out of the grids: their capacities are checked against the bound
+    of (T, N, n) = (100, 2, 2), which is (3, 5)."""
+    assert b.gdp_descriptor_capacity(100, 2, 2) == (3, 5)
+    a = base_args(b)
+    f = a["fake"]
+    d = b.gdp_descriptors()
+    d.chunk_indices = d.chunk_indices_dp = d.chunk_offsets = d.chunk_offsets_dp = f.next
+    d.nt_cap, d.ntdp_cap = caps
+    a["desc"] = ctypes.byref(d)
+    expect(b, a, b.GDP_EINVAL, "below the bounds")
+
+
 # ---------------------------------------------------------------- decode step
 
 def decode_args(b, N=8, n=2, Hqk=2, Hv=4, K=128, V=128, S=16, dt=None):

@@ -196,3 +196,64 @@ def test_backward_graph_capture_replay(gdp):
             assert rel_err(to_np(x), ref[name]) <= TOL[dt], f"replay {rep}: {name} vs oracle"
         call()  # eager work between the replays
         torch.cuda.synchronize()
+
+
+def _backward_into(gdp, inp, n, d_o, cu, fill=float("nan")):
+    """Low-level backward call into caller buffers pre-filled with `fill`."""
+    T, Hqk, K = inp["q"].shape
+    Hk, Hv, V = inp["k"].shape[1], inp["v"].shape[1], inp["v"].shape[2]
+    N = cu.shape[0] - 1
+    f32 = dict(dtype=torch.float32, device="cuda")
+    outs = {"dq": torch.full((T, Hqk, K), fill, **f32), "dk": torch.full((T * n, Hk, K), fill, **f32),
+            "dv": torch.full((T * n, Hv, V), fill, **f32), "dg_log": torch.full((T, Hv), fill, **f32),
+            "dbeta": torch.full((T * n, Hv), fill, **f32), "dinitial_state": torch.full((N, Hv, K, V), fill, **f32)}
+    ws = torch.empty(gdp.gdp_backward_workspace_bytes(T, N, n, Hqk, Hv, K, V, inp["q"].dtype), dtype=torch.uint8,
+                     device="cuda")
+    gdp.gdp_chunk_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, cu, 0.0,
+                                   inp["initial_state"], inp["use_qk_l2norm"], d_o, None, outs["dq"], outs["dk"],
+                                   outs["dv"], outs["dg_log"], outs["dbeta"], outs["dinitial_state"], ws)
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("cu_list", [[0, 50, 100], [7, 50, 100]], ids=["tail-padding", "head-and-tail-padding"])
+def test_backward_rows_outside_the_sequences_are_zero(gdp, cu_list):
+    """cu_seqlens covering only part of T (a fixed padded T under graph capture):
+    every gradient, dv included, is 0 on the sub-rows no sequence covers (the
+    buffers start as NaN), and the covered rows match the oracle run on them."""
+    n, T = 2, 120
+    w = workloads.custom([T // 2, T // 2], n, 1, 2, 128, 128, dtype=torch.bfloat16, init_std=0.2, seed=77)
+    inp = {k: (x.cuda() if isinstance(x, torch.Tensor) else x) for k, x in workloads.generate(w, "cpu").items()}
+    d_o = torch.randn(T, 2, 128, generator=torch.Generator().manual_seed(78)).to(torch.bfloat16).cuda()
+    cu = torch.tensor(cu_list, dtype=torch.int32, device="cuda")
+    outs = _backward_into(gdp, inp, n, d_o, cu)
+    lo, hi = cu_list[0], cu_list[-1]
+    for name, per in (("dq", 1), ("dk", n), ("dv", n), ("dg_log", 1), ("dbeta", n)):
+        x = outs[name]
+        assert torch.all(x[:lo * per] == 0) and torch.all(x[hi * per:] == 0), f"{name} padding rows not zero"
+    sub = np.array(cu_list) - lo
+    ref = obwd.backward(to_np(inp["q"][lo:hi]), to_np(inp["k"][lo * n:hi * n]), to_np(inp["v"][lo * n:hi * n]),
+                        to_np(inp["g_log"][lo:hi]), to_np(inp["beta"][lo * n:hi * n]), n, sub, to_np(d_o[lo:hi]), None,
+                        initial_state=to_np(inp["initial_state"]), use_qk_l2norm=False)
+    for name, per in (("dq", 1), ("dk", n), ("dv", n), ("dg_log", 1), ("dbeta", n)):
+        e = rel_err(to_np(outs[name][lo * per:hi * per]), ref[name])
+        assert e <= TOL[torch.bfloat16], f"{name} err {e:.3e}"
+    assert rel_err(to_np(outs["dinitial_state"]), ref["dinitial_state"]) <= TOL[torch.bfloat16]
+
+
+def test_backward_non_monotone_cu_seqlens_stays_in_bounds(gdp):
+    """cu_seqlens = [0, T, 0, T] (not monotone) makes the descriptors place the
+    last sequence's chunk-state rows past the buffer; the backward reads a zero
+    state there instead of reading out of bounds, and the call completes with
+    finite gradients."""
+    n, T = 2, 640
+    w = workloads.custom([T], n, 1, 2, 64, 64, dtype=torch.bfloat16, init_std=0.2, seed=79)
+    inp = workloads.generate(w, "cpu")
+    inp["initial_state"] = torch.cat([inp["initial_state"]] * 3)
+    inp = {k: (x.cuda() if isinstance(x, torch.Tensor) else x) for k, x in inp.items()}
+    d_o = torch.randn(T, 2, 64, generator=torch.Generator().manual_seed(80)).to(torch.bfloat16).cuda()
+    cu = torch.tensor([0, T, 0, T], dtype=torch.int32, device="cuda")
+    assert gdp.gdp_descriptor_capacity(T, 3, n)[0] < 20  # the last sequence's rows 10..19 lie past it
+    outs = _backward_into(gdp, inp, n, d_o, cu, fill=0.0)
+    for name, x in outs.items():
+        assert torch.isfinite(x).all(), name
