@@ -10,7 +10,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdp.so")
+# GDP_LIBRARY names another build of the library (the host-sanitized check
+# build of the CPU sanitizer run); by default the in-tree libgdp.so
+LIB_PATH = os.environ.get("GDP_LIBRARY") or os.path.join(_HERE, "libgdp.so")
 
 GDP_F32, GDP_BF16, GDP_I32, GDP_I64, GDP_F16 = 0, 1, 2, 3, 4
 GDP_OK, GDP_EINVAL, GDP_EUNSUPPORTED, GDP_EALIAS, GDP_EWORKSPACE, GDP_EHIP = 0, -1, -2, -3, -4, -5
@@ -152,17 +154,24 @@ def gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, dtype=torch.bfloat
     return int(LIB.gdp_workspace_bytes(T, N, num_householder, Hqk, Hv, K, V, _DT[dtype]))
 
 
-def gdp_build_descriptors(cu_seqlens, num_householder, T, nt_cap=None, ntdp_cap=None):
-    """Device-built descriptors of both chunkings (int32 tensors), padded to capacity."""
+def gdp_build_descriptors(cu_seqlens, num_householder, T, nt_cap=None, ntdp_cap=None, out=None):
+    """Device-built descriptors of both chunkings (int32 tensors), padded to capacity.
+
+    ``out``: a dict of caller-allocated buffers (as this function returns) to
+    build into, with the capacities their row counts give; nothing is then
+    allocated, so the call can be captured in a graph."""
     N = cu_seqlens.shape[0] - 1
-    ct, cd = gdp_descriptor_capacity(T, N, num_householder)
-    nt_cap = ct if nt_cap is None else nt_cap
-    ntdp_cap = cd if ntdp_cap is None else ntdp_cap
     dev = cu_seqlens.device
-    out = {"chunk_indices": torch.empty((max(nt_cap, 1), 2), dtype=torch.int32, device=dev),
-           "chunk_indices_dp": torch.empty((max(ntdp_cap, 1), 2), dtype=torch.int32, device=dev),
-           "chunk_offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
-           "chunk_offsets_dp": torch.empty(N + 1, dtype=torch.int32, device=dev)}
+    if out is None:
+        ct, cd = gdp_descriptor_capacity(T, N, num_householder)
+        nt_cap = ct if nt_cap is None else nt_cap
+        ntdp_cap = cd if ntdp_cap is None else ntdp_cap
+        out = {"chunk_indices": torch.empty((max(nt_cap, 1), 2), dtype=torch.int32, device=dev),
+               "chunk_indices_dp": torch.empty((max(ntdp_cap, 1), 2), dtype=torch.int32, device=dev),
+               "chunk_offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+               "chunk_offsets_dp": torch.empty(N + 1, dtype=torch.int32, device=dev)}
+    else:
+        nt_cap, ntdp_cap = out["chunk_indices"].shape[0], out["chunk_indices_dp"].shape[0]
     d = _descs(out, nt_cap, ntdp_cap)
     cu = as_gdp_tensor(cu_seqlens)
     _check(LIB.gdp_build_descriptors(ctypes.byref(cu), num_householder, T, ctypes.byref(d), _stream(dev)))

@@ -17,6 +17,29 @@ def rel_err(x, ref):
     return float(np.max(np.abs(x - ref))) / max(1.0, rms)
 
 
+class ErrAcc:
+    """rel_err over a tensor compared piece by piece: the max of |x - ref| and
+    the rms of ref are taken over every piece seen, as rel_err takes them over
+    the whole tensor."""
+
+    def __init__(self):
+        self.maxabs, self.ss, self.count = 0.0, 0.0, 0
+
+    def add(self, x, ref):
+        x = np.asarray(x, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        if ref.size == 0:
+            return
+        self.maxabs = max(self.maxabs, float(np.max(np.abs(x - ref))))
+        self.ss += float(np.sum(ref * ref))
+        self.count += ref.size
+
+    def err(self):
+        if self.count == 0:
+            return 0.0
+        return self.maxabs / max(1.0, float(np.sqrt(self.ss / self.count)))
+
+
 def to_np(t):
     return t.detach().to("cpu", torch.float64).numpy() if t is not None else None
 

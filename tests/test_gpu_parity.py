@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from gated_deltaproduct_recurrence_amd import workloads
-from tests.parity import TOL, oracle_run, rel_err, to_device, to_np
+from tests.parity import TOL, ErrAcc, oracle_run, rel_err, to_device, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -85,75 +85,245 @@ def test_workload0_fp32_full_parity(gdp):
 def test_workload_full_parity(gdp, wid, path):
     w = workloads.workload(wid)
     inp = workloads.generate(w, "cpu")
+    inp["output_final_state"] = True  # workload 2 is timed without it; parity checks it too
     ref = oracle_run(inp)
     res = run_gpu(gdp, to_device(inp))
     check_all(inp, res, ref, TOL[w.dtype], what=w.name)
 
 
-def test_workload_serving_mix_parity(gdp, path):
-    """Random-length mix with cache slots and chunk states; heads 0..3 against the oracle,
-    the untouched slots and the padding chunk-state rows bit-exact."""
-    w = workloads.workload(3)
-    inp = to_device(workloads.generate(w, "cpu"))
-    cache0 = inp["state_cache"].clone()
-    sentinel = 12345.0
-    o, fs, cs, offs = gdp.chunk_prefill(**inp)
-    torch.cuda.synchronize()
-    # chunk_states buffer was allocated by the wrapper; rows past NT are never written,
-    # so re-run into a sentinel-filled buffer to check that.
+def _serving_mix_run(gdp, inp, w, desc, cache0, sentinel):
+    """One low-level call on the serving mix into a sentinel-filled chunk-state
+    buffer and a fresh copy of the cache; returns (o, chunk_states, cache)."""
     T, N, n = w.T, w.N, w.n
     nt_cap, _ = gdp.gdp_descriptor_capacity(T, N, n)
-    cs2 = torch.full((nt_cap, w.Hv, w.K, w.V), sentinel, dtype=torch.float32, device="cuda")
-    cache2 = cache0.clone()
-    o2 = torch.empty_like(o)
-    desc = gdp.gdp_build_descriptors(inp["cu_seqlens"], n, T)
-    args = dict(inp)
-    args["state_cache"] = cache2
+    cs = torch.full((nt_cap, w.Hv, w.K, w.V), sentinel, dtype=torch.float32, device="cuda")
+    cache = cache0.clone()
+    o = torch.empty((T, w.Hv, w.V), dtype=w.dtype, device="cuda")
     ws = torch.empty(gdp.gdp_workspace_bytes(T, N, n, w.Hqk, w.Hv, w.K, w.V), dtype=torch.uint8, device="cuda")
-    gdp.gdp_chunk_prefill(args["q"], args["k"], args["v"], args["g_log"], args["beta"], n, args["cu_seqlens"],
-                          0.0, None, False, False, cache2, args["state_indices"], True, o2, None, cs2, desc, ws)
+    gdp.gdp_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, inp["cu_seqlens"], 0.0, None,
+                          False, False, cache, inp["state_indices"], True, o, None, cs, desc, ws)
     torch.cuda.synchronize()
-    assert torch.equal(o2, o), "two runs differ"
-    NT = int(offs[-1].item())
-    assert torch.all(cs2[NT:] == sentinel), "padding chunk-state rows were written"
-    heads = [0, 1, 2, 3]
-    ref = oracle_run(inp, heads=heads)
-    assert rel_err(to_np(o[:, heads]), ref["o"]) <= TOL[w.dtype]
-    assert np.array_equal(offs.cpu().numpy(), ref["chunk_offsets"])
-    e = rel_err(to_np(cs2[:NT, heads]), ref["chunk_states"])
-    assert e <= TOL[w.dtype], f"chunk states err {e:.3e}"
+    return o, cs, cache
+
+
+def test_workload_serving_mix_every_head(gdp, monkeypatch):
+    """Random-length mix (64 sequences + 4 zero-length padding sequences, n=3,
+    H=32) with cache slots and chunk states, on every kernel path.  Every state
+    head's o, chunk-state rows and written cache slots are compared with the
+    oracle, which runs four heads at a time (the error's max and rms are taken
+    over the whole tensor); the untouched slots and the padding chunk-state rows
+    are bit-exact, and the descriptors' offsets equal the oracle's."""
+    w = workloads.workload(3)
+    cpu_inp = workloads.generate(w, "cpu")
+    inp = to_device(cpu_inp)
+    T, N, n = w.T, w.N, w.n
+    desc = gdp.gdp_build_descriptors(inp["cu_seqlens"], n, T)
+    sentinel = 12345.0
+    cache0 = inp["state_cache"].clone()
+    runs = {}
+    for p in PATHS:
+        monkeypatch.setenv("GDP_PREFILL_PATH", p)
+        runs[p] = _serving_mix_run(gdp, inp, w, desc, cache0, sentinel)
+        print(f"serving mix: {p} path ran", flush=True)
+    offs = desc["chunk_offsets"].cpu().numpy()
+    NT = int(offs[-1])
     slots = inp["state_indices"].cpu().numpy()
-    written = [s for s in slots if s >= 0]
-    e = rel_err(to_np(cache2[written][:, heads]), ref["state_cache"][written])
-    assert e <= TOL[w.dtype], f"cache err {e:.3e}"
+    written = [int(s) for s in slots if s >= 0]
     untouched = sorted(set(range(cache0.shape[0])) - set(written))
-    assert torch.equal(cache2[untouched], cache0[untouched]), "untouched cache slots changed"
+    for p, (o, cs, cache) in runs.items():
+        assert torch.all(cs[NT:] == sentinel), f"{p}: padding chunk-state rows were written"
+        assert torch.equal(cache[untouched], cache0[untouched]), f"{p}: untouched cache slots changed"
+    acc = {(p, what): ErrAcc() for p in PATHS for what in ("o", "chunk_states", "cache")}
+    for h0 in range(0, w.Hv, 4):
+        heads = list(range(h0, h0 + 4))
+        ref = oracle_run(cpu_inp, heads=heads)
+        assert np.array_equal(offs, ref["chunk_offsets"])
+        for p, (o, cs, cache) in runs.items():
+            acc[p, "o"].add(to_np(o[:, heads]), ref["o"])
+            acc[p, "chunk_states"].add(to_np(cs[:NT, heads]), ref["chunk_states"])
+            acc[p, "cache"].add(to_np(cache[written][:, heads]), ref["state_cache"][written])
+        del ref
+        print(f"serving mix: heads {h0}..{h0 + 3} compared", flush=True)
+    for (p, what), a in acc.items():
+        assert a.err() <= TOL[w.dtype], f"{p}: {what} err {a.err():.3e}"
 
 
-def test_workload_long_context_sampled(gdp):
-    """Full-size long-context run in the benchmark's launch configuration; the
-    oracle checks sampled (sequence, head) chains one by one."""
+def test_workload_serving_mix_graph_replay(gdp):
+    """The serving mix at its full size (T, N) as a captured graph: descriptor
+    build plus prefill (cache slots, chunk states), captured once and replayed
+    for three seeded length sets of the same T and N.  Every replay's o, chunk
+    states and cache equal an eager call on the same lengths bit for bit."""
+    w = workloads.workload(3)
+    inp = workloads.generate(w, "cuda")
+    T, N, n = w.T, w.N, w.n
+    nt_cap, ntdp_cap = gdp.gdp_descriptor_capacity(T, N, n)
+    cu = inp["cu_seqlens"].clone()
+    desc = {"chunk_indices": torch.empty((nt_cap, 2), dtype=torch.int32, device="cuda"),
+            "chunk_indices_dp": torch.empty((ntdp_cap, 2), dtype=torch.int32, device="cuda"),
+            "chunk_offsets": torch.empty(N + 1, dtype=torch.int32, device="cuda"),
+            "chunk_offsets_dp": torch.empty(N + 1, dtype=torch.int32, device="cuda")}
+    o = torch.empty((T, w.Hv, w.V), dtype=w.dtype, device="cuda")
+    cs = torch.zeros((nt_cap, w.Hv, w.K, w.V), dtype=torch.float32, device="cuda")
+    cache = inp["state_cache"]
+    ws = torch.empty(gdp.gdp_workspace_bytes(T, N, n, w.Hqk, w.Hv, w.K, w.V), dtype=torch.uint8, device="cuda")
+
+    def call():
+        gdp.gdp_build_descriptors(cu, n, T, out=desc)
+        gdp.gdp_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g_log"], inp["beta"], n, cu, 0.0, None, False,
+                              False, cache, inp["state_indices"], True, o, None, cs, desc, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    lens0 = list(w.lens)
+    rng = np.random.default_rng(33)
+    lens1 = [lens0[i] for i in rng.permutation(len(lens0))]
+    lens2 = list(lens1)
+    for i in range(0, len(lens2) - 1, 2):  # move tokens between neighbours, T unchanged
+        m = int(rng.integers(0, lens2[i] + 1))
+        lens2[i] -= m
+        lens2[i + 1] += m
+    for lens in (lens0, lens1, lens2):
+        assert sum(lens) == T
+        full = lens + [0] * w.pad_sequences
+        cu.copy_(torch.tensor([0] + [int(x) for x in np.cumsum(full)], dtype=torch.int32, device="cuda"))
+        cs.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rcs, rcache = o.clone(), cs.clone(), cache.clone()
+        cs.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(ro, o), "replayed o differs from eager"
+        assert torch.equal(rcs, cs), "replayed chunk states differ from eager"
+        assert torch.equal(rcache, cache), "replayed cache differs from eager"
+        assert torch.isfinite(o.float()).all()
+
+
+def test_workload_long_context_every_chain(gdp):
+    """Full-size long-context run (8 x 65536 tokens, n=2, Hqk=16 / Hv=32) in the
+    benchmark's launch configuration.  The oracle runs one sequence and eight q/k
+    heads (sixteen state heads) at a time; every output and every chain's final
+    state is compared, with the error's max and rms over the whole tensor."""
     w = workloads.workload(4)
     inp = workloads.generate(w, "cuda")
     o, fs = gdp.chunk_prefill(**inp)
     torch.cuda.synchronize()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(fs).all()
     cu = inp["cu_seqlens"].cpu().numpy()
-    n = w.n
-    rng = np.random.default_rng(4)
-    picks = [(int(rng.integers(0, w.N)), int(rng.integers(0, w.Hqk))) for _ in range(4)]
-    for seq, hq in picks:
+    n, grp, half = w.n, w.Hv // w.Hqk, w.Hqk // 2
+    acc_o, acc_s = ErrAcc(), ErrAcc()
+    for seq in range(w.N):
         t0, t1 = int(cu[seq]), int(cu[seq + 1])
-        heads = [2 * hq, 2 * hq + 1]
-        sub = dict(q=inp["q"][t0:t1, hq:hq + 1], k=inp["k"][t0 * n:t1 * n, hq:hq + 1],
-                   v=inp["v"][t0 * n:t1 * n, heads], g_log=inp["g_log"][t0:t1, heads],
-                   beta=inp["beta"][t0 * n:t1 * n, heads], num_householder=n,
-                   cu_seqlens=torch.tensor([0, t1 - t0]), scale=None,
-                   initial_state=inp["initial_state"][seq:seq + 1, heads], use_qk_l2norm=True)
-        ref = oracle_run(sub)
-        e1 = rel_err(to_np(o[t0:t1, heads]), ref["o"])
-        e2 = rel_err(to_np(fs[seq:seq + 1, heads]), ref["final_state"])
-        assert e1 <= TOL[w.dtype] and e2 <= TOL[w.dtype], f"seq {seq} heads {heads}: o {e1:.3e} S {e2:.3e}"
+        for g0 in (0, half):
+            qk = slice(g0, g0 + half)
+            heads = slice(grp * g0, grp * (g0 + half))
+            sub = dict(q=inp["q"][t0:t1, qk], k=inp["k"][t0 * n:t1 * n, qk], v=inp["v"][t0 * n:t1 * n, heads],
+                       g_log=inp["g_log"][t0:t1, heads], beta=inp["beta"][t0 * n:t1 * n, heads], num_householder=n,
+                       cu_seqlens=torch.tensor([0, t1 - t0]), scale=None,
+                       initial_state=inp["initial_state"][seq:seq + 1, heads], use_qk_l2norm=True)
+            ref = oracle_run(sub)
+            acc_o.add(to_np(o[t0:t1, heads]), ref["o"])
+            acc_s.add(to_np(fs[seq:seq + 1, heads]), ref["final_state"])
+            del ref, sub
+        print(f"long context: sequence {seq} compared (o err so far {acc_o.err():.3e})", flush=True)
+    assert acc_o.err() <= TOL[w.dtype], f"o err {acc_o.err():.3e}"
+    assert acc_s.err() <= TOL[w.dtype], f"final_state err {acc_s.err():.3e}"
+
+
+# ---------------------------------------------------------------- strong decays and non-finite inputs
+
+STRONG = [
+    # lens, n, Hqk, Hv, K, V, dtype, l2norm
+    ([700, 300, 77], 2, 2, 4, 128, 128, torch.bfloat16, True),
+    ([400, 129], 3, 1, 2, 128, 128, torch.bfloat16, False),
+    ([130, 70], 2, 1, 2, 64, 64, torch.float32, False),
+]
+STRONG_PATHS = [(i, p) for i, c in enumerate(STRONG) for p in (PATHS if c[6] == torch.bfloat16 else ["auto"])]
+
+
+def strong_decay_inputs(ci):
+    """g_log = -softplus(N(0,1) + 2) (alpha about 0.12) with 2% of the (token,
+    head) entries at -40: the allowed range of the gate (alpha in (0, 1]) taken
+    to where a 64-token chunk's decay sum underflows exp2."""
+    lens, n, Hqk, Hv, K, V, dt, l2 = STRONG[ci]
+    w = workloads.custom(lens, n, Hqk, Hv, K, V, dtype=dt, l2norm_in_kernel=l2, g_shift=-2.0, init_std=0.2,
+                         seed=90 + ci)
+    inp = workloads.generate(w, "cpu")
+    hit = torch.rand(inp["g_log"].shape, generator=torch.Generator().manual_seed(190 + ci)) < 0.02
+    inp["g_log"][hit] = -40.0
+    inp["return_chunk_states"] = True
+    return w, inp
+
+
+def min_chunk_decay_sum_base2(g_log, cu):
+    """Smallest base-2 decay sum over the 64-token chunks of every sequence and head."""
+    g = g_log.double().numpy() * np.log2(np.e)
+    best = 0.0
+    for i in range(len(cu) - 1):
+        for c0 in range(int(cu[i]), int(cu[i + 1]), 64):
+            best = min(best, float(g[c0:min(c0 + 64, int(cu[i + 1]))].sum(0).min()))
+    return best
+
+
+@pytest.mark.parametrize("ci,kpath", STRONG_PATHS, ids=[f"strong{i}-{p}" for i, p in STRONG_PATHS])
+def test_strong_decay_parity(gdp, ci, kpath, monkeypatch):
+    """Strong decays against the oracle on every path: the chunks whose decay sum
+    falls below 2^-100 take the per-entry decay branch of the output scores, and
+    the state's lazy decay scale is renormalised, in every chunk."""
+    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    w, inp = strong_decay_inputs(ci)
+    assert min_chunk_decay_sum_base2(inp["g_log"], inp["cu_seqlens"].numpy()) < -100.0
+    ref = oracle_run(inp)
+    o, fs, cs, offs = gdp.chunk_prefill(**to_device(inp))
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    e = rel_err(to_np(o), ref["o"])
+    assert e <= tol, f"o err {e:.3e}"
+    e = rel_err(to_np(fs), ref["final_state"])
+    assert e <= tol, f"final state err {e:.3e}"
+    NT = int(offs[-1].item())
+    e = rel_err(to_np(cs[:NT]), ref["chunk_states"])
+    assert e <= tol, f"chunk states err {e:.3e}"
+
+
+def test_non_finite_input_stays_in_its_chain(gdp, path):
+    """A NaN in one v row of one chain (sequence, state head) and an infinite beta
+    in another reach only those chains, from the 64-token chunk of the bad token
+    on (inside a chunk the masked products multiply it by zero, which gives NaN):
+    every other chain's outputs and final state, and those chains' outputs before
+    that chunk, are bit-equal to the clean run."""
+    w = workloads.workload(1)
+    clean = to_device(workloads.generate(w, "cpu"))
+    n = w.n
+    cu = clean["cu_seqlens"].cpu().numpy()
+    bad = dict(clean)
+    bad["v"] = clean["v"].clone()
+    bad["beta"] = clean["beta"].clone()
+    # chain (sequence 3, head 1): NaN in v at token 300 of the sequence, sub-row 1
+    t_a = int(cu[3]) + 300
+    bad["v"][t_a * n + 1, 1, 5] = float("nan")
+    # chain (sequence 2, head 2): infinite beta at token 70 of the sequence, sub-row 0
+    t_b = int(cu[2]) + 70
+    bad["beta"][t_b * n, 2] = float("inf")
+    o0, s0 = gdp.chunk_prefill(**clean)
+    o1, s1 = gdp.chunk_prefill(**bad)
+    torch.cuda.synchronize()
+    for (seq, h, t) in ((3, 1, t_a), (2, 2, t_b)):
+        c0 = int(cu[seq]) + (t - int(cu[seq])) // 64 * 64
+        assert torch.equal(o1[int(cu[seq]):c0, h], o0[int(cu[seq]):c0, h]), "outputs before the bad chunk changed"
+        assert not torch.isfinite(o1[t, h].float()).all(), "the bad token's output is finite"
+        assert not torch.isfinite(s1[seq, h]).all(), "the chain's final state is finite"
+        o1[int(cu[seq]):int(cu[seq + 1]), h] = o0[int(cu[seq]):int(cu[seq + 1]), h]
+        s1[seq, h] = s0[seq, h]
+    assert torch.equal(o1, o0), "a non-finite input reached another chain's outputs"
+    assert torch.equal(s1, s0), "a non-finite input reached another chain's final state"
 
 
 # ---------------------------------------------------------------- ragged tails, dims, dtypes, edge cases
