@@ -29,13 +29,47 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_long_context_traffic.json
 KERNEL_SOURCE = os.path.join(ROOT, "gated_deltaproduct_recurrence_amd", "csrc", "gdp_kernels.hip")
 
 
-def algorithmic_bytes(w):
+def algorithmic_bytes(w, slots=None):
     """Each input read once, each output written once, no intermediates.
     Per real token: q, k (Hqk*K*(1+n) bf16), v, o (Hv*V*(1+n) bf16), g, beta
-    (Hv*(1+n) fp32); per sequence: initial and final state (Hv*K*V fp32 each)."""
-    per_tok = 2 * w.K * w.Hqk * (1 + w.n) + 2 * w.V * w.Hv * (1 + w.n) + 4 * w.Hv * (1 + w.n)
-    per_seq = 4 * w.Hv * w.K * w.V * ((1 if w.init_std > 0 else 0) + (1 if w.output_final_state else 0))
-    return per_tok * w.T + per_seq * w.N
+    (Hv*(1+n) fp32); per sequence: initial and final state (Hv*K*V fp32 each);
+    per 64-token chunk when chunk states are returned, and per cache slot
+    written (a state index >= 0), one more Hv*K*V fp32 state."""
+    es = 2 if str(w.dtype).endswith("bfloat16") else 4
+    state = 4 * w.Hv * w.K * w.V
+    per_tok = es * w.K * w.Hqk * (1 + w.n) + es * w.V * w.Hv * (1 + w.n) + 4 * w.Hv * (1 + w.n)
+    per_seq = state * ((1 if w.init_std > 0 else 0) + (1 if w.output_final_state else 0))
+    total = per_tok * w.T + per_seq * w.N
+    if w.return_chunk_states:
+        total += state * sum((L + 63) // 64 for L in w.lens)
+    if slots is not None:
+        total += state * int(sum(1 for s in slots if 0 <= s < w.state_cache_slots))
+    return total
+
+
+# parity bar of the oracle checks: max|x - ref| / max(1, rms(ref)) over the sample
+TOL = {"f32": 1e-4, "bf16": 1.5e-2}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def check_against_oracle(what, err, tol):
+    """A GPU result outside the parity bar fails the run (no JSON line is printed)."""
+    print(f"bench: {what} vs oracle err {err:.3e} (tolerance {tol:.1e})", file=sys.stderr)
+    if not err <= tol:
+        print(f"bench: {what} is outside the tolerance: the run fails", file=sys.stderr)
+        sys.exit(1)
 
 
 def source_hash():
@@ -128,7 +162,7 @@ def cpu_baseline(inp, w, tokens_per_seq, threads):
     ref = oracle.prefill(q, k, v, g, b, n, cus, initial_state=s0, use_qk_l2norm=w.l2norm_in_kernel,
                          threads=threads)
     dt = time.perf_counter() - t_start
-    rec = {"value": float(cus[-1] / dt), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    rec = {"value": float(cus[-1] / dt), "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
            "sample": f"first {tokens_per_seq} tokens of each of the {w.N} sequences, all {w.Hv} heads "
                      f"({int(cus[-1])} real tokens), fp64 token loop, {dt:.2f} s"}
     return rec, ref, it
@@ -173,8 +207,9 @@ def bench_decode(args, gdp, workloads):
             ref = oracle.decode(*args_o, use_qk_l2norm=True, threads=threads)
         dt = (time.perf_counter() - t0) / reps
         err = float(np.max(np.abs(got - ref["o"]))) / max(1.0, float(np.sqrt(np.mean(ref["o"] ** 2))))
-        print(f"bench: decode outputs vs oracle err {err:.3e}", file=sys.stderr)
-        rec = {"value": sel.numel() / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
+        check_against_oracle("decode outputs", err, TOL["bf16"])
+        rec = {"value": sel.numel() / dt, "unit": "entries/s", "cores": threads, "cpu_model": cpu_model(),
+               "kind": "oracle",
                "sample": f"all {sel.numel()} live entries of one step, all {Hv} heads, fp64 "
                          f"(cache cut to their slots), {reps} runs of {dt:.2f} s"}
 
@@ -240,9 +275,9 @@ def backward_cpu_baseline(args, inp, w, d_o, grads, M=2048, seq=7, hq=5):
     for name, x in got.items():
         r = ref[name]
         e = float(np.max(np.abs(f64(x) - r))) / max(1.0, float(np.sqrt(np.mean(r ** 2))))
-        print(f"bench: {name} vs oracle err {e:.3e}", file=sys.stderr)
+        check_against_oracle(name, e, TOL["bf16"])
     groups = w.Hqk
-    return {"value": M / (dt * groups), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": M / (dt * groups), "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"last {M} tokens of sequence {seq}, the {grp} state heads of q/k head {hq} (one of {groups} "
                       f"groups; the rate is scaled to all {w.Hv} heads), fp64 autograd token loop given the state "
                       f"entering the suffix, {dt:.2f} s"}
@@ -317,8 +352,9 @@ def bench_flashinfer(args, gdp, workloads):
         dt = time.perf_counter() - t0
         got = out.index_select(0, it).to("cpu", torch.float64).numpy()
         err = float(np.max(np.abs(got - ref["o"]))) / max(1.0, float(np.sqrt(np.mean(ref["o"] ** 2))))
-        print(f"bench: sampled outputs vs oracle err {err:.3e}", file=sys.stderr)
-        line["cpu_baseline"] = {"value": N * L / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        check_against_oracle("sampled outputs", err, TOL["bf16"])
+        line["cpu_baseline"] = {"value": N * L / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
+                                "kind": "oracle",
                                 "sample": f"first {L} tokens of each of the {N} sequences, all {Hv} heads, fp64 "
                                           f"token loop (FlashInfer convention), {dt:.2f} s"}
     print(json.dumps(line), flush=True)
@@ -524,12 +560,13 @@ def main():
         wall_g = time.perf_counter() - t_g
         same = bool(torch.equal(o, o_eager))
         if not same:
-            print("bench: graph replay output differs from the eager output", file=sys.stderr)
+            print("bench: graph replay output differs from the eager output: the run fails", file=sys.stderr)
+            sys.exit(1)
         graph_detail = {"graph_replay_ms_per_step": wall_g * 1e3 / args.steps,
                         "graph_replay_event_ms": g0.elapsed_time(g1) / args.steps,
                         "graph_replay_equals_eager": same}
 
-    alg = algorithmic_bytes(w)
+    alg = algorithmic_bytes(w, None if inp["state_indices"] is None else inp["state_indices"].cpu().tolist())
     fused_avg_s = float(np.mean(fused_ms)) * 1e-3
     achieved = alg / fused_avg_s / 1e9
     traffic = measured_traffic(args.workload)
@@ -561,7 +598,8 @@ def main():
         line["cpu_baseline"] = rec
         got = o.index_select(0, it).to("cpu", torch.float64).numpy()
         err = float(np.max(np.abs(got - ref["o"]))) / max(1.0, float(np.sqrt(np.mean(ref["o"] ** 2))))
-        print(f"bench: sampled outputs vs oracle err {err:.3e}", file=sys.stderr)
+        check_against_oracle("sampled outputs", err, TOL["bf16" if w.dtype == torch.bfloat16 else "f32"])
+        rec["oracle_check_err"] = err
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
