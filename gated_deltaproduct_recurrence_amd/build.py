@@ -18,10 +18,30 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build_library(out=LIB, verbose=False):
-    """Compile and link libgdp.so; raises CalledProcessError on failure."""
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the check build
+# (each -fsanitize applies to the host compile only; the device code is built
+# as usual).  Such a library needs the clang ASan runtime loaded first
+# (LD_PRELOAD) and is meant for the CPU test suite: it exercises the host-side
+# validation and never runs a kernel.
+HOST_SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-shared-libsan",
+                       "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all"]
+SANITIZED_LIB = os.path.join(ROOT, "_build", "sanitize", "libgdp_hostcheck.so")
+
+
+def asan_runtime():
+    """Path of the clang AddressSanitizer runtime that the sanitized builds link against."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_library(out=LIB, verbose=False, sanitize=False):
+    """Compile and link libgdp.so; raises CalledProcessError on failure.
+    sanitize=True builds the host-sanitized check library instead (to `out`)."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *DEVICE_FLAGS, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    opt = HOST_SANITIZE_FLAGS if sanitize else ["-O3"]
+    cmd = [HIPCC, *DEVICE_FLAGS, *opt, "-std=c++17", "-fPIC", "-shared", "-Wall",
            f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd))

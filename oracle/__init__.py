@@ -25,11 +25,16 @@ _LIB = None
 
 
 def _lib():
+    """The oracle library: GDP_ORACLE_LIBRARY names another build of it (the
+    sanitized one of the CPU sanitizer run); otherwise the in-tree build."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.compile_oracle()
-        _LIB = load(_build.LIB)
+        path = os.environ.get("GDP_ORACLE_LIBRARY")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.compile_oracle()
+        _LIB = load(path)
     return _LIB
 
 

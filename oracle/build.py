@@ -13,8 +13,21 @@ SRC = os.path.join(HERE, "gdp_oracle.c")
 LIB = os.path.join(HERE, "libgdp_oracle.so")
 
 
-def compile_oracle(src=SRC, out=LIB, extra_flags=()):
-    """Compile ``src`` to the shared library ``out``; raises on failure."""
+SANITIZED_LIB = os.path.join(os.path.dirname(HERE), "_build", "sanitize", "libgdp_oracle_sanitized.so")
+
+
+def compile_oracle(src=SRC, out=LIB, extra_flags=(), sanitize=False):
+    """Compile ``src`` to the shared library ``out``; raises on failure.
+    sanitize=True builds it with clang's AddressSanitizer and
+    UndefinedBehaviorSanitizer (the same runtime as the library's check build)."""
+    if sanitize:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer", "-march=x86-64-v3", "-fPIC",
+               "-shared", "-shared-libsan", "-pthread", "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+               *extra_flags, src, "-o", out + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(out + ".tmp", out)
+        return out
     cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fPIC", "-shared", "-pthread",
            "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter",
            *extra_flags, src, "-o", out + ".tmp", "-lm"]
