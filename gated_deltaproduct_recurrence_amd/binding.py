@@ -23,7 +23,7 @@ STATUS_NAMES = {GDP_EINVAL: "GDP_EINVAL", GDP_EUNSUPPORTED: "GDP_EUNSUPPORTED", 
 EXPORTED = ("gdp_descriptor_capacity", "gdp_build_descriptors", "gdp_workspace_bytes",
             "gdp_chunk_prefill", "gdp_recurrent_decode", "gdp_fi_workspace_bytes",
             "gdp_chunk_gated_delta_product", "gdp_backward_workspace_bytes", "gdp_chunk_prefill_backward",
-            "gdp_debug_status", "gdp_last_error", "gdp_version")
+            "gdp_debug_status", "gdp_last_error", "gdp_version", "gdp_chunk_prefill_noalloc")
 
 
 class gdp_tensor(ctypes.Structure):
@@ -62,6 +62,9 @@ def _load(path=LIB_PATH):
     lib.gdp_chunk_prefill.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
                                       ctypes.c_int32, T, T, ctypes.c_int32, T, T, T, D, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]
+    lib.gdp_chunk_prefill_noalloc.restype = ctypes.c_int
+    lib.gdp_chunk_prefill_noalloc.argtypes = [T, T, T, T, T, ctypes.c_int32, T, ctypes.c_float, T, ctypes.c_int32,
+                                              ctypes.c_int32, T, T, ctypes.c_int32, T, T, T, D, ctypes.c_void_p]
     lib.gdp_recurrent_decode.restype = ctypes.c_int
     lib.gdp_recurrent_decode.argtypes = [T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, T, T, T,
                                          ctypes.c_void_p]
@@ -218,6 +221,31 @@ def gdp_chunk_prefill(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=0
                                int(bool(use_qk_l2norm)), ctypes.byref(cache), ctypes.byref(slots),
                                int(bool(return_chunk_states)), ctypes.byref(ot), ctypes.byref(ft),
                                ctypes.byref(ct), dptr, ws_ptr, ws_bytes, st)
+    _check(rc)
+
+
+def gdp_chunk_prefill_noalloc(q, k, v, g_log, beta, num_householder, cu_seqlens, scale=0.0, initial_state=None,
+                              output_final_state=False, use_qk_l2norm=False, state_cache=None, state_indices=None,
+                              return_chunk_states=False, o=None, final_state=None, chunk_states=None,
+                              descriptors=None, stream=None):
+    """Direct call of the C entry point that takes no workspace (its scratch is
+    the library's static per-GPU array); outputs are caller-allocated."""
+    args = [as_gdp_tensor(x) for x in (q, k, v, g_log, beta)]
+    cu = as_gdp_tensor(cu_seqlens)
+    s0 = as_gdp_tensor(initial_state)
+    cache = as_gdp_tensor(state_cache)
+    slots = as_gdp_tensor(state_indices)
+    ot, ft, ct = as_gdp_tensor(o), as_gdp_tensor(final_state), as_gdp_tensor(chunk_states)
+    dptr = None
+    if descriptors is not None:
+        d = _descs(descriptors, descriptors["chunk_indices"].shape[0], descriptors["chunk_indices_dp"].shape[0])
+        dptr = ctypes.byref(d)
+    st = _stream(q.device) if stream is None else stream
+    rc = LIB.gdp_chunk_prefill_noalloc(*[ctypes.byref(a) for a in args], int(num_householder), ctypes.byref(cu),
+                                       float(scale or 0.0), ctypes.byref(s0), int(bool(output_final_state)),
+                                       int(bool(use_qk_l2norm)), ctypes.byref(cache), ctypes.byref(slots),
+                                       int(bool(return_chunk_states)), ctypes.byref(ot), ctypes.byref(ft),
+                                       ctypes.byref(ct), dptr, st)
     _check(rc)
 
 

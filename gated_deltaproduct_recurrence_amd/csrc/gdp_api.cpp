@@ -395,12 +395,16 @@ int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t n, int64_t T, co
   return GDP_OK;
 }
 
-int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
-                      const gdp_tensor *beta, int32_t n, const gdp_tensor *cu_seqlens, float scale,
-                      const gdp_tensor *initial_state, int32_t output_final_state, int32_t use_qk_l2norm,
-                      const gdp_tensor *state_cache, const gdp_tensor *state_indices, int32_t return_chunk_states,
-                      const gdp_tensor *o, const gdp_tensor *final_state, const gdp_tensor *chunk_states,
-                      const gdp_descriptors *desc, void *workspace, size_t workspace_bytes, void *stream) {
+// The prefill behind both entry points.  noalloc: the workspace is the static
+// scratch array of the current device (gdp_chunk_prefill_noalloc), after a
+// check that the call fits in it.
+static int prefill_impl(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
+                        const gdp_tensor *beta, int32_t n, const gdp_tensor *cu_seqlens, float scale,
+                        const gdp_tensor *initial_state, int32_t output_final_state, int32_t use_qk_l2norm,
+                        const gdp_tensor *state_cache, const gdp_tensor *state_indices, int32_t return_chunk_states,
+                        const gdp_tensor *o, const gdp_tensor *final_state, const gdp_tensor *chunk_states,
+                        const gdp_descriptors *desc, void *workspace, size_t workspace_bytes, void *stream,
+                        bool noalloc) {
   g_last_error.clear();
   if (!present(q) || !present(k) || !present(v) || !present(g_log) || !present(beta) || !present(o))
     return fail(GDP_EINVAL, "q, k, v, g_log, beta and o are required");
@@ -514,9 +518,24 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   const SegPlan plan = seg_plan(T, N, Hv, K, V, dt, path);
   if (path == gdp::PATH_SEGMENTED && !plan.use)
     return fail(GDP_EUNSUPPORTED, "the segmented path needs bf16 inputs with K == V in {64, 128}");
-  const size_t wy_bytes = std::max(align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv)), seg_bytes(plan, N, Hv, K, V));
+  // (the fused kernel keeps its WY matrices in LDS: the region is empty then)
+  const bool fused_run = !plan.use && gdp::fused_chosen(idt, N, Hv, path);
+  const size_t wy_bytes = plan.use ? seg_bytes(plan, N, Hv, K, V)
+                                   : (fused_run ? 0 : align256(gdp::wy_buffer_bytes(idt, ntdp_cap, Hv)));
   const size_t tail0 = wy_bytes + (desc ? 0 : desc_bytes(N, nt_cap, ntdp_cap));
   const size_t need = tail0 + order_bytes(N, Hv) + progress_bytes(N, Hv, Hqk);
+  if (noalloc) {
+    if (need > GDP_NOALLOC_SCRATCH_BYTES)
+      return fail(GDP_EWORKSPACE,
+                  "gdp_chunk_prefill_noalloc: this call needs %zu bytes of scratch, more than the %zu bytes of "
+                  "its static scratch array; call gdp_chunk_prefill with a workspace instead",
+                  need, (size_t)GDP_NOALLOC_SCRATCH_BYTES);
+    void *p = nullptr;
+    hipError_t e = gdp::noalloc_scratch(&p);
+    if (e != hipSuccess) return fail(GDP_EHIP, "scratch array address: %s", hipGetErrorString(e));
+    workspace = p;
+    workspace_bytes = GDP_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -637,6 +656,29 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
   e = gdp::launch_prefill(a, idt, (int)K, (int)V, path, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDP_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return GDP_OK;
+}
+
+int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
+                      const gdp_tensor *beta, int32_t n, const gdp_tensor *cu_seqlens, float scale,
+                      const gdp_tensor *initial_state, int32_t output_final_state, int32_t use_qk_l2norm,
+                      const gdp_tensor *state_cache, const gdp_tensor *state_indices, int32_t return_chunk_states,
+                      const gdp_tensor *o, const gdp_tensor *final_state, const gdp_tensor *chunk_states,
+                      const gdp_descriptors *desc, void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_impl(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, output_final_state, use_qk_l2norm,
+                      state_cache, state_indices, return_chunk_states, o, final_state, chunk_states, desc, workspace,
+                      workspace_bytes, stream, false);
+}
+
+int gdp_chunk_prefill_noalloc(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                              const gdp_tensor *g_log, const gdp_tensor *beta, int32_t n,
+                              const gdp_tensor *cu_seqlens, float scale, const gdp_tensor *initial_state,
+                              int32_t output_final_state, int32_t use_qk_l2norm, const gdp_tensor *state_cache,
+                              const gdp_tensor *state_indices, int32_t return_chunk_states, const gdp_tensor *o,
+                              const gdp_tensor *final_state, const gdp_tensor *chunk_states,
+                              const gdp_descriptors *desc, void *stream) {
+  return prefill_impl(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, output_final_state, use_qk_l2norm,
+                      state_cache, state_indices, return_chunk_states, o, final_state, chunk_states, desc, nullptr, 0,
+                      stream, true);
 }
 
 namespace {

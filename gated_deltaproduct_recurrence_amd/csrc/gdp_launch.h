@@ -219,6 +219,9 @@ struct ValidateArgs {
   uint32_t *word;                                               // set by launch_validate
 };
 hipError_t launch_validate(ValidateArgs a, hipStream_t stream);
+// device address of the static scratch array of the current device (the
+// workspace of gdp_chunk_prefill_noalloc), looked up once per device
+hipError_t noalloc_scratch(void **out);
 // device address of the current device's word
 hipError_t debug_word_ptr(uint32_t **out);
 hipError_t launch_combine(const CombineArgs &a, int K, int V, hipStream_t stream);

@@ -169,6 +169,33 @@ int gdp_chunk_prefill(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor
                       const gdp_tensor *chunk_states, const gdp_descriptors *desc,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the static scratch array of gdp_chunk_prefill_noalloc, per GPU. */
+#define GDP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Device.  gdp_chunk_prefill without a workspace argument, for callers that
+ * cannot allocate device memory: code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, results and errors are
+ * those of gdp_chunk_prefill; the workspace is a file-scope device array of
+ * GDP_NOALLOC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds
+ * until the process ends.  The call allocates nothing.  A call whose workspace
+ * need exceeds the array returns GDP_EWORKSPACE with the size it needs.  The
+ * fused path needs only the descriptors (when desc is NULL), the work order and
+ * the pacing counters: 16 bytes per chunk row plus 8 per (sequence, state
+ * head), under 1 MiB up to tens of millions of tokens; the split path's WY
+ * matrices take 8 KiB (bf16) or 16 KiB (f32) per expanded chunk and state head,
+ * and the segmented path 12 K V bytes per segment and state head.  All calls on one GPU share its array:
+ * calls that overlap on one GPU (for instance on two streams) race; calls on
+ * one stream are ordered.  No call depends on what an earlier one left in the
+ * array. */
+int gdp_chunk_prefill_noalloc(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v,
+                              const gdp_tensor *g_log, const gdp_tensor *beta, int32_t num_householder,
+                              const gdp_tensor *cu_seqlens, float scale, const gdp_tensor *initial_state,
+                              int32_t output_final_state, int32_t use_qk_l2norm,
+                              const gdp_tensor *state_cache, const gdp_tensor *state_indices,
+                              int32_t return_chunk_states, const gdp_tensor *o,
+                              const gdp_tensor *final_state, const gdp_tensor *chunk_states,
+                              const gdp_descriptors *desc, void *stream);
+
 /* Device.  The single-token recurrent decode step on the state cache, in place.
  *
  * The decode step of the blog page "Attention Cache and Sequence Parallelism"

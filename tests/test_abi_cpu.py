@@ -363,3 +363,36 @@ def test_debug_bits_match_the_header(b):
     text = open(HEADER).read()
     for name, val in (("GDP_DBG_CU", b.GDP_DBG_CU), ("GDP_DBG_SLOT", b.GDP_DBG_SLOT), ("GDP_DBG_DUP", b.GDP_DBG_DUP)):
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+
+
+# ---------------------------------------------------------------- entry point without a workspace
+
+def call_noalloc(b, a):
+    r = ctypes.byref
+    return b.LIB.gdp_chunk_prefill_noalloc(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g_log"]), r(a["beta"]), a["n"],
+                                           r(a["cu"]), a["scale"], r(a["s0"]), a["ofs"], a["l2"], r(a["cache"]),
+                                           r(a["slots"]), a["rcs"], r(a["o"]), r(a["fs"]), r(a["cs"]), a["desc"],
+                                           None)
+
+
+def test_noalloc_validates_like_the_workspace_entry(b):
+    """The entry point without a workspace runs the same host checks first."""
+    a = base_args(b)
+    a["n"] = 0
+    assert call_noalloc(b, a) == b.GDP_EINVAL and "num_householder" in b.gdp_last_error()
+    a = base_args(b)
+    a["fs"] = a["s0"]
+    assert call_noalloc(b, a) == b.GDP_EALIAS
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(b, monkeypatch):
+    """A call whose workspace need exceeds the static scratch array (here the
+    float32 split path's WY matrices, 16 KiB per expanded chunk and state head:
+    about 200 MB for 100,000 tokens, n=2, four heads) is refused before any
+    device call, with the size it needs."""
+    monkeypatch.delenv("GDP_PREFILL_PATH", raising=False)
+    a = base_args(b, T=100000, N=1, n=2, Hqk=1, Hv=4, K=64, V=64, dt=b.GDP_F32)
+    rc = call_noalloc(b, a)
+    assert rc == b.GDP_EWORKSPACE, (rc, b.gdp_last_error())
+    msg = b.gdp_last_error()
+    assert "noalloc" in msg and str(64 << 20) in msg, msg
