@@ -885,15 +885,15 @@ __global__ void __launch_bounds__(NTHR, 1) gdp_scan_kernel(PrefillArgs a) {
 // pass, WY step included, so the per-chunk WY matrix never leaves the CU:
 //   waves 0-3  consumers: the state S (fp32 accumulators, one 16*NB-column slab
 //              per wave), X = K S, the scores, R, E = T R, the state update of
-//              expanded chunk e, and the outputs, staged in LDS;
+//              expanded chunk e, and the outputs, which they store to o;
 //   waves 4-7  helpers: wave 4 issues every direct global->LDS load (the k rows
 //              and the betas and decays of chunk e+2 in 3-slot rings, the v
 //              rows of chunk e+1 and the q rows of token chunk c+2 in 2-slot
 //              rings) and forms the masked betas, the decay cumsums, the
 //              q-row norms and the per-row token tables; waves 5-7 run the WY
-//              step of chunk e+1 (Gram matrix, k-row norms, A, T = (I + A)^-1)
-//              and the per-row coefficients the consumers use, and wave 7
-//              stores the staged outputs.
+//              step of chunk e+1 (Gram matrix, k-row norms, A, T = (I + A)^-1),
+//              the per-row coefficients the consumers use and, on wave 5, the
+//              chunk's scale scalars.
 // Two workgroup barriers per chunk separate the phases; between two barriers
 // each role only touches LDS slots no other role uses in that span.  Tiles of
 // 64 rows are stored unpadded with an XOR swizzle of their 16-byte segments;
@@ -925,8 +925,8 @@ __device__ __forceinline__ bf16x4 lds_tr4(const char *p) {
 //     segments per 32 lanes) are served at the same rate as with any other
 //     row permutation tried.
 //   TK = 0, v tiles (256-byte rows): r = 8m + t (t < 8) maps to 2t + (t / 4 xor m),
-//     a bijection on 16 rows, which keeps the 8-byte output staging writes and
-//     the transposing v reads at the conflict-free rate.
+//     a bijection on 16 rows, which keeps the transposing v reads at the
+//     conflict-free rate.
 // Tiles of 128-byte rows keep swz(r) = r mod 8.
 template <int NS, int TK = 0> __device__ __forceinline__ int swz(int r) {
   static_assert(NS == 16 || NS == 8, "rows of 128 or 256 bytes");
@@ -1100,7 +1100,16 @@ template <int K, int V> struct FusedSmem {
   float gkr[2][CH], rkg[2][CH];  // rkg = rk 2^(-Gt_tok(r)) (used when qsafe)
   int tokr[2][CH];
   int qsafe[2];                   // the token chunk's decay cumsum stays above -100 (base 2)
+  float scal[2][4];               // per expanded chunk: lazy scale entering it, that scale times the
+                                  // chunk's decay, the reciprocal the state update uses, unused
+  int sflag[2];                   // per expanded chunk: SF_* bits
 };
+// Bits of FusedSmem::sflag.  A "fast" token chunk keeps the lazy scale above
+// LAM_MIN through all of its expanded chunks (a rescale, when needed, is done at
+// its start): its outputs are then formed from the raw masked scores and the
+// state-update rows E_w = diag(f) E, with every per-row and per-token factor
+// collected at staging.
+constexpr int SF_FAST = 1, SF_LAZY = 2, SF_RESCALE = 4, SF_TF = 8;
 
 // SUM: segment summaries only (the states of the segmented path): no outputs,
 // so the scores, P, O^T, the q rows and the per-row token tables are skipped.
@@ -1199,11 +1208,24 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       lds_barrier();
       lds_barrier();
     }
+    float lam_c = 1.f;  // the lazy scale at the start of the current token chunk
     for (int e = 0; e < nexp; ++e) {
       const int ks = e % 3, ts = e & 1;
       const int c = e / n;
       const int j = e - c * n;
       const int qs = c & 1;
+      // the chunk's scale scalars and flags (helper 2 wrote them a chunk ahead)
+      const int fl = __builtin_amdgcn_readfirstlane(sm.sflag[ts]);
+      const bool fast = !SUM && (fl & SF_FAST), lazy = fl & SF_LAZY, tfs = fl & SF_TF;
+      const float dl = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.scal[ts][1])));
+      if (fl & SF_RESCALE) {  // rescale at the token chunk's start: Sst *= lam, lam = 1
+#pragma unroll
+        for (int at = 0; at < KT16; ++at)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) Sacc[at][b] *= lam;
+        lam = 1.f;
+      }
+      if (j == 0) lam_c = lam;
       // the lane constants are made opaque every chunk so that the compiler forms
       // each address where it is used instead of hoisting dozens of them
       SwLane lcont = Lcont, lcolk = Lcolk;
@@ -1312,7 +1334,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (!SUM && j == 0) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
+      if (!SUM && j == 0 && !fast) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const float f = lam * qfac[16 * a4 + lr];
@@ -1330,7 +1352,16 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         const int rlim = n * (t + 1) - CH * j;
         const bool fact = sm.qsafe[qs] != 0;
         const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * tb * LDC);
-        if (fact) {
+        if (fast) {  // raw masked scores: the factors sit in E_w and at staging
+#pragma unroll
+          for (int pa = 0; pa < RBW; ++pa) {
+            const int a4 = rb0 + pa, r0 = 16 * a4 + 4 * lg;
+            f32x4 val;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? Pacc[pa][i] : 0.f;
+            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+          }
+        } else if (fact) {
           const float qv = qfac[t];
           const float *rkg = sm.rkg[ts];
 #pragma unroll
@@ -1431,12 +1462,14 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       };
       load_kc(0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      // E: the v_new rows, or (chunks whose WY matrix carries the state-update
+      // weights, SF_TF) E_w = diag(f) E, which both products below then use
       Frag<bf16> Eb[2][NB];
-      if constexpr (!SUM) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
+      if constexpr (!SUM) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         if (a4 + 1 < 4) load_pf(a4 + 1, (a4 + 1) & 1);
@@ -1450,27 +1483,40 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         __builtin_amdgcn_sched_barrier(0);
       }
       }
-      // Sst += K^T diag(2^(G_last - G) rk / (lam 2^G_last)) E and lam *= 2^G_last, unless
-      // lam would fall below LAM_MIN (then Sst is rescaled to lam = 1)
-      const float glast = sm.gdp[ks][CH - 1];
-      const float dl = lam * fexp2(glast);
-      const bool lazy = dl >= LAM_MIN;
-      const float rl = lazy ? 1.f / dl : 1.f;
+      // Sst += K^T diag(f) E with f = 2^(G_last - G) rk / (lam 2^G_last) and lam *= 2^G_last,
+      // unless lam would fall below LAM_MIN (then f = 2^(G_last - G) rk and Sst is
+      // rescaled to lam = 1); dl = lam 2^G_last and f come from the helpers' tables
+      if (!tfs) {
+        const float rl = sm.scal[ts][2];
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 f = ld4(sm.wgt[ts] + 16 * a4 + 4 * lg) * rl;
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 f = ld4(sm.wgt[ts] + 16 * a4 + 4 * lg) * rl;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) E[a4][b] *= f;
+          for (int b = 0; b < NB; ++b) E[a4][b] *= f;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
       }
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
       if (!lazy) {
 #pragma unroll
         for (int at = 0; at < KT16; ++at)
 #pragma unroll
           for (int b = 0; b < NB; ++b) Sacc[at][b] *= dl;
+      }
+      // row factors of the outputs (staged after the state update, read here so
+      // that their LDS reads overlap it): the q-row rstd rq_t and, on a fast token
+      // chunk, lam_c scale 2^Gt_t (lam_c 2^Gt_t stays above LAM_MIN there, so the
+      // product is a normal float)
+      const bool stage = !SUM && (j == n - 1 || e == nexp - 1) && a.o;
+      float sfac[4];
+      if (stage) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float qf = sm.qfac[qs][16 * a4 + lr], rq = sm.rq[qs][16 * a4 + lr];
+          sfac[a4] = (fast ? lam_c * qf : 1.f) * (a.l2norm ? rq : 1.f);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1486,22 +1532,39 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       }
       lam = lazy ? dl : 1.f;
       // outputs of token chunk c once its last expanded chunk is in: lane holds
-      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns (scale is in qfac
-      // and P; the q-row rstd rq_t multiplies every term of row t and is applied here).
-      // They are staged in bf16 in this chunk's v tile (unused after the R step)
-      // and helper 3 stores whole rows from there in the next chunk.
-      if (!SUM && (j == n - 1 || e == nexp - 1) && a.o) {
-        char *stg = sm.v[ts];
+      // O[t = 16 a4 + lr][16 b + 4 lg .. +3] of this wave's columns.  The q-row rstd
+      // rq_t (and on a fast token chunk lam_c scale 2^Gt_t) multiplies every term of
+      // row t and is applied here; the four bf16 values go straight to o (each
+      // store instruction writes 32 contiguous bytes of 16 rows, and the four
+      // consumer waves together cover whole rows).
+      if (stage) {
+        const int ntok = toks_of(c);
+        char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol);
+        const uint32_t ost = (uint32_t)a.o_st * 2u;
+        // every row is packed and addressed first and the stores follow back to
+        // back: a store reads its data and address registers only when the memory
+        // pipeline takes it, and rewriting them before that stalls the wave
+        uint2 pk[4][NB];
+        uint2 *dst[4];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          if (a.l2norm) {
-            const float f = sm.rq[qs][16 * a4 + lr];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) O[b][a4] *= f;
-          }
+          for (int b = 0; b < NB; ++b) pk[a4][b] = __builtin_bit_cast(uint2, bf4(O[b][a4] * sfac[a4]));
+          dst[a4] = (uint2 *)(ob + (uint32_t)(16 * a4 + lr) * ost + 8 * lg);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ntok == CH) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-            *(bf16x4 *)(stg + sw_off<VW>(16 * a4 + lr, 2 * (wcol + 16 * b + 4 * lg))) = bf4(O[b][a4]);
+          for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) dst[a4][4 * b] = pk[a4][b];
+        } else {
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            if (16 * a4 + lr < ntok) {
+#pragma unroll
+              for (int b = 0; b < NB; ++b) dst[a4][4 * b] = pk[a4][b];
+            }
         }
       }
       lds_barrier();
@@ -1604,6 +1667,39 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       const float gmin = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gt), ntok - 1));
       if (hl == 0) sm.qsafe[sl] = gmin > -100.f;
     };
+    // Scale scalars of chunk x (after its decay cumsum and, at a token chunk's
+    // start, its token decay cumsum are in), in the order the consumers apply
+    // them: lam is the lazy state scale (S = lam Sst) entering the chunk.  At a
+    // token chunk's start, when lam 2^Gt_end would fall below LAM_MIN inside it,
+    // the state is first rescaled to lam = 1; the token chunk is fast when lam
+    // 2^Gt_end then stays at or above LAM_MIN (so no rescale happens inside it).
+    // dl = lam 2^G_last; the chunk is lazy when dl >= LAM_MIN (always inside a fast
+    // token chunk), and the state update's weights then carry rl = 1 / dl.
+    // Summary mode has no outputs: every chunk uses the weighted WY matrix.
+    auto scalars = [&](int x, float &lam_h, bool &fast_h) {
+      const int cx = x / n, jx = x - cx * n;
+      int fl = 0;
+      if (jx == 0) {
+        if constexpr (SUM) {
+          fast_h = false;
+        } else {
+          const float gend = sm.gtok[cx & 1][CH - 1];
+          if (lam_h * fexp2(gend) < LAM_MIN && lam_h != 1.f) {
+            fl |= SF_RESCALE;
+            lam_h = 1.f;
+          }
+          fast_h = lam_h * fexp2(gend) >= LAM_MIN;
+        }
+      }
+      const float dl = lam_h * fexp2(sm.gdp[x % 3][CH - 1]);
+      const bool lazy = fast_h || dl >= LAM_MIN;
+      fl |= (fast_h ? SF_FAST | SF_TF : 0) | (SUM ? SF_TF : 0) | (lazy ? SF_LAZY : 0);
+      if (hl == 0) {
+        *(f32x4 *)sm.scal[x & 1] = f32x4{lam_h, dl, lazy ? 1.f / dl : 1.f, 0.f};
+        sm.sflag[x & 1] = fl;
+      }
+      lam_h = lazy ? dl : 1.f;
+    };
     // Gram stage of chunk x: tiles [i0, i1) of the lower triangle, with the k rows
     // of the later block as the B operand so that lane (lg, lr) of tile (ra, rb)
     // holds G[16 ra + lr][16 rb + 4 lg + i]; rstd of the rows of its diagonal tiles
@@ -1676,7 +1772,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           *(bf16x4 *)(sm.tdrow[hb] + lr * 16 + 4 * lg) = tb;
         }
       }
-      if (lg == 0) {  // per-row weights of the consumers' R and state update
+      if (lg == 0) {  // per-row weights of the consumers' R (2^G rk) and state update (2^(G_last - G) rk)
         const float glast = gd[CH - 1];
         sm.c1[x & 1][r] = fexp2(gr) * rk[r];
         sm.wgt[x & 1][r] = fexp2(glast - gr) * rk[r];
@@ -1687,21 +1783,37 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // T diag(beta) at [c * LDT + r])
     auto merge = [&](int x) {
       bf16 *tt = sm.t;
+      // every input is read first, so that the merge waits for one LDS round trip
       bf16x4 tc[4], tn[4], al[6];
       float bcol[4];  // beta of the column this lane writes in each column block
+      f32x4 w4[4];    // state-update weights of rows 16 ra + 4 lg + i
 #pragma unroll
       for (int b = 0; b < 4; ++b) bcol[b] = sm.beta[x % 3][16 * b + lr];
+#pragma unroll
+      for (int ra = 0; ra < 4; ++ra) w4[ra] = ld4(sm.wgt[x & 1] + 16 * ra + 4 * lg);
+      const float rl = sm.scal[x & 1][2];
+      const int fl = sm.sflag[x & 1];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         tc[b] = tr_col4(sm.tdrow[b], 16, 4 * lg, 0, lr);  // T_b[4lg + i][lr]
         tn[b] = -*(const bf16x4 *)(sm.tdiag[b] + 4 * lane);
-        const f32x4 d = f32x4{(float)tc[b][0], (float)tc[b][1], (float)tc[b][2], (float)tc[b][3]} * bcol[b];
-        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + 4 * lg) = bf4(d);
       }
 #pragma unroll
       for (int i = 0; i < 6; ++i) al[i] = *(const bf16x4 *)(sm.alow[i] + 4 * lane);
-      auto put = [&](int ra, int rb, f32x4 v) {  // v: T[16 ra + 4 lg + i][16 rb + lr]; writes it times beta
-        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + 4 * lg) = bf4(v * bcol[rb]);
+      // on SF_TF chunks the rows are scaled by the state-update weights f = w rl,
+      // which makes the consumers' product E_w = diag(f) E directly
+      const bool tf = __builtin_amdgcn_readfirstlane(fl) & SF_TF;
+      const float fm = tf ? rl : 0.f, fa = tf ? 0.f : 1.f;
+      f32x4 frow[4];
+#pragma unroll
+      for (int ra = 0; ra < 4; ++ra) frow[ra] = w4[ra] * fm + fa;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 d = f32x4{(float)tc[b][0], (float)tc[b][1], (float)tc[b][2], (float)tc[b][3]} * (frow[b] * bcol[b]);
+        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + 4 * lg) = bf4(d);
+      }
+      auto put = [&](int ra, int rb, f32x4 v) {  // v: T[16 ra + 4 lg + i][16 rb + lr]; writes it times f_row beta_col
+        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + 4 * lg) = bf4(v * (frow[ra] * bcol[rb]));
         return bf4(v);
       };
       // distance 1
@@ -1722,46 +1834,17 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         *(uint4 *)(sm.t + (16 + 32 * blk + row) * LDT + 32 * blk + 8 * half) = uint4{0u, 0u, 0u, 0u};
       }
     }
-    // output rows of the chunk eo, staged by the consumers in its v tile: whole
-    // 16-byte pieces of rows (8-byte pieces when o is not 16-byte aligned)
-    const bool o16 = (((uintptr_t)a.o & 15) == 0) && (a.o_st % 8 == 0) && (a.o_sh % 8 == 0);
-    auto store_o = [&](int eo) {
-      constexpr int NS = VW / 16, RPI = 1024 / VW, NI = CH / RPI;
-      const int c = eo / n, ntok = toks_of(c);
-      const char *stg = sm.v[eo & 1];
-      char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + vt * BV);
-      const uint32_t ost = (uint32_t)a.o_st * 2u;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {  // two batches of reads, then stores
-        uint4 x[NI / 2];
-#pragma unroll
-        for (int i = 0; i < NI / 2; ++i)
-          x[i] = *(const uint4 *)(stg + sw_off<VW>((hf * NI / 2 + i) * RPI + lane / NS, 16 * (lane % NS)));
-#pragma unroll
-        for (int i = 0; i < NI / 2; ++i) {
-          const int r = (hf * NI / 2 + i) * RPI + lane / NS;
-          if (r < ntok) {
-            char *dst = ob + (uint32_t)r * ost + 16 * (lane % NS);
-            if (o16) {
-              *(uint4 *)dst = x[i];
-            } else {
-              *(uint2 *)dst = uint2{x[i].x, x[i].y};
-              *(uint2 *)(dst + 8) = uint2{x[i].z, x[i].w};
-            }
-          }
-        }
-      }
-    };
     // Work per helper and chunk e = (token chunk c, sub-chunk j) (WY stages for
     // chunk e+1), before || after the mid-chunk barrier:
     //   helper 0: k rows and betas/decays of chunk e+2   || v rows of chunk e+1,
     //                                                       q rows of token chunk c+2
-    //   helper 1: merge stage                            || row block 3
+    //   helper 1: merge stage                            || scale scalars and row
+    //                                                       block 3 of chunk e+1
     //   helper 2: Gram tiles 0-4, masked betas and decay || row blocks 0, 1
     //             cumsum of chunk e+1, and at j = n-1 the
     //             q norms and token decay cumsum of token
     //             chunk c+1
-    //   helper 3: outputs of chunk e-1, Gram tiles 5-9   || row block 2, row tables
+    //   helper 3: Gram tiles 5-9                         || row block 2, row tables
     //                                                       of chunk e+1
     // Helper 0 issues every direct-to-LDS load and never touches LDS: the
     // compiler makes any LDS access that follows such a load in the same wave
@@ -1795,7 +1878,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       };
       const TileOffs<KW, 1> koffs = tile_offs<KW, 1>(kst, lane), qoffs = tile_offs<KW, 1>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
-      if (part1) {  // zero values: both v tiles stay zero (no outputs are staged in them)
+      if (part1) {  // zero values: both v tiles stay zero
         for (int u = hl; u < 2 * CH * VW / 16; u += 64) *(uint4 *)(sm.v[0] + 16 * u) = uint4{0u, 0u, 0u, 0u};
       }
       if (nexp > 0) {
@@ -1824,8 +1907,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           load_scalars(e + 2);
         }
         lds_barrier();
-        // phase B.  The v tile of chunk e-1 (its outputs are stored) and, after
-        // the last expanded chunk of token chunk c, its q tile are free: refill
+        // phase B.  The v tile of chunk e-1 and, after the last expanded chunk
+        // of token chunk c, its q tile are free: refill
         // them with chunk e+1 and token chunk c+2, then wait for everything but
         // the q rows when n >= 2 (they are read at the end of token chunk c+1; a
         // later wait for newer loads covers them): the consumers read the v rows
@@ -1843,16 +1926,22 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         lds_barrier();
       }
     } else if (hw == 1) {
+      float lam_h = 1.f;    // the lazy state scale, tracked as the consumers apply it
+      bool fast_h = false;  // the current token chunk is fast
       if (nexp > 0) {
         lds_barrier();
         lds_barrier();
+        scalars(0, lam_h, fast_h);
         block(0, IC<3>{});
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
         merge(e);
         lds_barrier();
-        if (e + 1 < nexp) block(e + 1, IC<3>{});
+        if (e + 1 < nexp) {
+          scalars(e + 1, lam_h, fast_h);
+          block(e + 1, IC<3>{});
+        }
         lds_barrier();
       }
     } else if (hw == 2) {
@@ -1895,7 +1984,6 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       }
       for (int e = 0; e < nexp; ++e) {
         asm volatile("" : "+v"(hl));
-        if (e >= 1 && e % n == 0 && a.o) store_o(e - 1);
         if (e + 1 < nexp) gram(e + 1, 5, 10, 4);
         lds_barrier();
         if (e + 1 < nexp) {
@@ -1904,7 +1992,6 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
         lds_barrier();
       }
-      if (nexp > 0 && a.o) store_o(nexp - 1);
     }
   }
 }
