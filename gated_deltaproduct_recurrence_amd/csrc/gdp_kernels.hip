@@ -1543,25 +1543,46 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         const uint32_t ost = (uint32_t)a.o_st * 2u;
         // every row is packed and addressed first and the stores follow back to
         // back: a store reads its data and address registers only when the memory
-        // pipeline takes it, and rewriting them before that stalls the wave
-        uint2 pk[4][NB];
-        uint2 *dst[4];
+        // pipeline takes it, and rewriting them before that stalls the wave.
+        // With 16-byte aligned rows, lanes 16 apart swap halves (row swap), so
+        // that each lane holds 8 consecutive columns and 4 lanes cover the wave's
+        // 64 bytes of a row; otherwise each lane stores its two 8-byte pieces.
+        const bool o16 = (((uintptr_t)a.o & 15) == 0) && (a.o_st % 8 == 0) && (a.o_sh % 8 == 0);
+        if constexpr (NB == 2) if (o16) {
+          uint4 pk[4];
+          uint4 *dst[4];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const uint2 p0 = __builtin_bit_cast(uint2, bf4(O[0][a4] * sfac[a4]));
+            const uint2 p1 = __builtin_bit_cast(uint2, bf4(O[1][a4] * sfac[a4]));
+            const auto rx = __builtin_amdgcn_permlane16_swap(p0.x, p1.x, false, false);
+            const auto ry = __builtin_amdgcn_permlane16_swap(p0.y, p1.y, false, false);
+            pk[a4] = uint4{(uint32_t)rx[0], (uint32_t)ry[0], (uint32_t)rx[1], (uint32_t)ry[1]};
+            dst[a4] = (uint4 *)(ob + (uint32_t)(16 * a4 + lr) * ost + 16 * (lg >> 1) + 32 * (lg & 1));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (ntok == CH) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) pk[a4][b] = __builtin_bit_cast(uint2, bf4(O[b][a4] * sfac[a4]));
-          dst[a4] = (uint2 *)(ob + (uint32_t)(16 * a4 + lr) * ost + 8 * lg);
+            for (int a4 = 0; a4 < 4; ++a4) *dst[a4] = pk[a4];
+          } else {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+              if (16 * a4 + lr < ntok) *dst[a4] = pk[a4];
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (ntok == CH) {
+        if (NB != 2 || !o16) {
+          uint2 pk[4][NB];
+          uint2 *dst[4];
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) pk[a4][b] = __builtin_bit_cast(uint2, bf4(O[b][a4] * sfac[a4]));
+            dst[a4] = (uint2 *)(ob + (uint32_t)(16 * a4 + lr) * ost + 8 * lg);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) dst[a4][4 * b] = pk[a4][b];
-        } else {
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
-            if (16 * a4 + lr < ntok) {
+            if (ntok == CH || 16 * a4 + lr < ntok) {
 #pragma unroll
               for (int b = 0; b < NB; ++b) dst[a4][4 * b] = pk[a4][b];
             }
