@@ -404,7 +404,7 @@ static int prefill_impl(const gdp_tensor *q, const gdp_tensor *k, const gdp_tens
                         const gdp_tensor *state_cache, const gdp_tensor *state_indices, int32_t return_chunk_states,
                         const gdp_tensor *o, const gdp_tensor *final_state, const gdp_tensor *chunk_states,
                         const gdp_descriptors *desc, void *workspace, size_t workspace_bytes, void *stream,
-                        bool noalloc) {
+                        bool noalloc, bool tc_outputs = false) {
   g_last_error.clear();
   if (!present(q) || !present(k) || !present(v) || !present(g_log) || !present(beta) || !present(o))
     return fail(GDP_EINVAL, "q, k, v, g_log, beta and o are required");
@@ -593,6 +593,7 @@ static int prefill_impl(const gdp_tensor *q, const gdp_tensor *k, const gdp_tens
   a.tws = workspace;
   a.tws_rows = ntdp_cap;
   a.o = o->data; a.o_st = o->stride[0]; a.o_sh = o->stride[1];
+  a.tc_outputs = tc_outputs ? 1 : 0;
   hipError_t e;
   if (debug_validate()) {
     gdp::ValidateArgs va;
@@ -790,8 +791,8 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   gdp_tensor tcs{ws + L.cs, GDP_F32, 4, {csr, Hv, K, V}, {Hv * K * V, K * V, V, 1}};
   gdp_tensor to{ws + L.o, dt, 3, {T, Hv, V}, {Hv * V, V, 1}};
   gdp_tensor none{};
-  if ((rc = gdp_chunk_prefill(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, 0, use_qk_l2norm, &none,
-                              &none, 1, &to, &none, &tcs, &d, ws + L.fwd, workspace_bytes - L.fwd, stream)) != GDP_OK)
+  if ((rc = prefill_impl(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, 0, use_qk_l2norm, &none, &none, 1,
+                         &to, &none, &tcs, &d, ws + L.fwd, workspace_bytes - L.fwd, stream, false, true)) != GDP_OK)
     return rc;
   hipError_t e;
   for (const gdp_tensor *t : {dq, dk, dg_log, dbeta}) {

@@ -33,6 +33,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "gdp_launch.h"
 
 namespace gdp {
@@ -1113,14 +1116,24 @@ constexpr int SF_FAST = 1, SF_LAZY = 2, SF_RESCALE = 4, SF_TF = 8;
 
 // SUM: segment summaries only (the states of the segmented path): no outputs,
 // so the scores, P, O^T, the q rows and the per-row token tables are skipped.
-template <int K, int V, int NCW, bool SUM>
+// LT = 2 (n = 2 only): outputs per expanded chunk.  With two Householder rows
+// per token an expanded chunk holds whole tokens (32 of them, token blocks 2j
+// and 2j+1 of its token chunk), so each token's output is the state entering
+// that expanded chunk read out with q_t, plus the masked scores against that
+// chunk's rows only: O^T (two token blocks), the scores (eight tiles) and the
+// O += E P^T product (half the rows) are spread evenly over the two expanded
+// chunks of a token chunk, and all the decay factors are those of the
+// expanded-stream cumsum.  LT = 0: outputs per token chunk (any n).
+template <int K, int V, int NCW, bool SUM, int LT = 0>
 __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArgs a) {
+  static_assert(LT == 0 || (LT == 2 && !SUM && NCW == 4), "per-expanded-chunk outputs: n = 2, four consumer waves");
   using S = FusedSmem<K, V>;
   // NCW consumer waves of 16 NB state columns each cover all V columns; the
   // 16 score tiles (4 token blocks x 4 row blocks) are shared out RBW per wave
   constexpr int NB = V / (16 * NCW), BV = V, NVT = 1, KT16 = K / 16, KS = K / 32;
-  constexpr int RBW = 16 / NCW;
-  static_assert(NB >= 1 && 16 * NB * NCW == V && RBW * NCW == 16, "consumer waves must tile V and the scores");
+  constexpr int RBW = LT ? 2 : 16 / NCW;   // score row blocks per wave
+  constexpr int OTB = LT ? LT : 4;          // token blocks of O per wave
+  static_assert(NB >= 1 && 16 * NB * NCW == V && (LT || RBW * NCW == 16), "consumer waves must tile V and the scores");
   constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDT = S::LDT;
   __shared__ S sm;
 
@@ -1161,7 +1174,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     constexpr int rb0 = decltype(halfc)::value * RBW;
     // ---------------------------------------------------------------- consumers
     const int wcol = w * 16 * NB;     // first column of this wave inside the tile
-    const int tb = w & 3;  // the wave's score tiles: token block tb, row blocks rb0 .. rb0 + RBW - 1
+    // the wave's score tiles: token block tb, row blocks rb0 .. rb0 + RBW - 1 (with
+    // LT, tb is the token block inside the expanded chunk's 32 tokens)
+    const int tb = LT ? (w >> 1) : (w & 3);
     const int gcol = vt * BV + wcol;  // ... and inside the head
     const char *smb = (const char *)&sm;
     auto off_of = [&](const void *p) { return (uint32_t)((const char *)p - smb); };
@@ -1182,7 +1197,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // pair with contiguous 16-byte k (or q) fragments.
     auto kap = [](int at, int g, int i) { return 32 * (at >> 1) + 8 * g + 4 * (at & 1) + i; };
     f32x4 Sacc[KT16][NB];
-    f32x4 O[NB][4];
+    f32x4 O[NB][OTB];
     float lam = 1.f;
 #pragma unroll
     for (int at = 0; at < KT16; ++at)
@@ -1225,7 +1240,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           for (int b = 0; b < NB; ++b) Sacc[at][b] *= lam;
         lam = 1.f;
       }
-      if (j == 0) lam_c = lam;
+      if (LT || j == 0) lam_c = lam;
       // the lane constants are made opaque every chunk so that the compiler forms
       // each address where it is used instead of hoisting dozens of them
       SwLane lcont = Lcont, lcolk = Lcolk;
@@ -1264,6 +1279,59 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // row 16 tb + lr over the 32 elements this lane reads
       float qss = 0.f;
       const bool qnorm = j == 0 && a.l2norm;
+      float rqv[LT ? OTB : 1];  // (LT) q-row rstd of the expanded chunk's token blocks, per lane row
+      if constexpr (LT) {
+        // X = K Sst, the wave's score tiles and O^T = Sst^T Q^T of the expanded
+        // chunk's two token blocks (rows 32 j + 16 a4 + lr of the q tile), all on
+        // the same Sst fragments; k and q fragments of step s+1 are read while
+        // step s multiplies
+        Frag<bf16> kf[4], qf[2][2];
+        float qs2[2] = {0.f, 0.f};
+        auto load_kf = [&](int s, int a4) {
+          const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
+          kf[a4].v = rd16(xs + (kt + lcont.l) + 16 * a4 * KW);
+        };
+        auto load_qf = [&](int s, int buf) {
+          const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
+#pragma unroll
+          for (int a4 = 0; a4 < 2; ++a4) qf[buf][a4].v = rd16(xs + (qt + lcont.l) + 16 * (2 * j + a4) * KW);
+        };
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) load_kf(0, a4);
+        load_qf(0, 0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          if (s + 1 < KS) load_qf(s + 1, (s + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          Frag<bf16> Sb[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) from_acc(Sb[b], Sacc[2 * s][b], Sacc[2 * s + 1][b]);
+          const Frag<bf16> &qw = tb ? qf[s & 1][1] : qf[s & 1][0];
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
+            if (a4 >= rb0 && a4 < rb0 + RBW) Pacc[a4 - rb0] = mma(kf[a4], qw, s == 0 ? zero4() : Pacc[a4 - rb0]);
+            if (s + 1 < KS) load_kf(s + 1, a4);
+          }
+#pragma unroll
+          for (int a4 = 0; a4 < 2; ++a4)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) O[b][a4] = mma(Sb[b], qf[s & 1][a4], s == 0 ? zero4() : O[b][a4]);
+          if (a.l2norm) {
+#pragma unroll
+            for (int a4 = 0; a4 < 2; ++a4) qs2[a4] += seg_sumsq<bf16>(__builtin_bit_cast(uint4, qf[s & 1][a4].v));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int a4 = 0; a4 < 2; ++a4) {
+          float x = qs2[a4];
+          x += __shfl_xor(x, 16, 64);
+          x += __shfl_xor(x, 32, 64);
+          rqv[a4] = a.l2norm ? frsq(x + 1e-6f) : 1.f;
+        }
+      } else
       // k (and q) fragments of reduction step s+1 are read while step s multiplies
       {
         // rolling single buffer: fragment a4 of step s+1 is read right after the
@@ -1307,12 +1375,12 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       }
       // q-row rstd of the wave's 16 tokens (the four lanes lg of a row hold a
       // quarter each); the outputs of token chunk c take it when staged
-      if (!SUM && qnorm) {
+      if (!SUM && !LT && qnorm) {
         qss += __shfl_xor(qss, 16, 64);
         qss += __shfl_xor(qss, 32, 64);
         if (lg == 0) sm.rq[qs][16 * tb + lr] = frsq(qss + 1e-6f);
       }
-      if (!SUM && j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
+      if (!SUM && !LT && j == 0) {  // a token chunk starts: O^T = Sst^T Q^T
         Frag<bf16> qf[2][4];
         auto load_q = [&](int s, int buf) {
           const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
@@ -1334,10 +1402,18 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (!SUM && j == 0 && !fast) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
+      if (!SUM && !LT && j == 0 && !fast) {  // O^T columns t times lam scale 2^Gt_t (the q-row rstd comes at staging)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const float f = lam * qfac[16 * a4 + lr];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) O[b][a4] *= f;
+        }
+      }
+      if (LT && !fast) {  // O^T columns t times lam scale 2^G(t), G(t) the expanded cumsum at t's rows
+#pragma unroll
+        for (int a4 = 0; a4 < 2; ++a4) {
+          const float f = lam * a.scale * fexp2(sm.gdp[ks][2 * (16 * a4 + lr)]);
 #pragma unroll
           for (int b = 0; b < NB; ++b) O[b][a4] *= f;
         }
@@ -1348,9 +1424,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // the product qfac_t rkg_r of per-token and per-row factors (both finite and
       // normal); otherwise it is formed per entry.
       if constexpr (!SUM) {
-        const int t = 16 * tb + lr;
-        const int rlim = n * (t + 1) - CH * j;
-        const bool fact = sm.qsafe[qs] != 0;
+        const int t = 16 * tb + lr;  // (with LT: the token inside the expanded chunk)
+        const int rlim = LT ? 2 * (t + 1) : n * (t + 1) - CH * j;
+        const bool fact = !LT && sm.qsafe[qs] != 0;
         const uint32_t pw = off_of(sm.p) + lp + (uint32_t)(32 * tb * LDC);
         if (fast) {  // raw masked scores: the factors sit in E_w and at staging
 #pragma unroll
@@ -1359,6 +1435,18 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? Pacc[pa][i] : 0.f;
+            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+          }
+        } else if (LT) {  // per entry: scale rk_r 2^(G(t) - G_r), both on the expanded cumsum
+          const float *gd = sm.gdp[ks];
+          const float gt = gd[2 * t], rq = a.scale;
+#pragma unroll
+          for (int pa = 0; pa < RBW; ++pa) {
+            const int a4 = rb0 + pa, r0 = 16 * a4 + 4 * lg;
+            const f32x4 rk4 = ld4(rk + r0), gk4 = ld4(gd + r0);
+            f32x4 val;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? rq * rk4[i] * fexp2(gt - gk4[i]) * Pacc[pa][i] : 0.f;
             *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
           }
         } else if (fact) {
@@ -1442,7 +1530,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
       // while E forms: the P fragments of the first token block and the k^T
       // fragments of the first state row block
-      const int tokb0 = SUM ? 0 : tokr[0], tokb1 = SUM ? 0 : tokr[32];
+      // first token of each 32-row half (with LT the rows 32 s.. hold tokens 16 s..)
+      const int tokb0 = (SUM || LT) ? 0 : tokr[0], tokb1 = SUM ? 0 : (LT ? 16 : tokr[32]);
       Frag<bf16> pf[2][2];
       const uint32_t pr = off_of(sm.p) + lp;
       auto load_pf = [&](int a4, int buf) {  // P rows of token block a4
@@ -1471,8 +1560,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         for (int b = 0; b < NB; ++b) from_acc(Eb[s][b], E[2 * s][b], E[2 * s + 1][b]);
       if constexpr (!SUM) {
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        if (a4 + 1 < 4) load_pf(a4 + 1, (a4 + 1) & 1);
+      for (int a4 = 0; a4 < OTB; ++a4) {
+        if (a4 + 1 < OTB) load_pf(a4 + 1, (a4 + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -1509,13 +1598,21 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // that their LDS reads overlap it): the q-row rstd rq_t and, on a fast token
       // chunk, lam_c scale 2^Gt_t (lam_c 2^Gt_t stays above LAM_MIN there, so the
       // product is a normal float)
-      const bool stage = !SUM && (j == n - 1 || e == nexp - 1) && a.o;
-      float sfac[4];
+      // (with LT every expanded chunk stages its own 32 tokens: rq_t and, on a fast
+      // chunk, lam scale 2^G(t), which stays above LAM_MIN)
+      const bool stage = !SUM && (LT || j == n - 1 || e == nexp - 1) && a.o;
+      float sfac[OTB];
       if (stage) {
+        if constexpr (LT) {
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const float qf = sm.qfac[qs][16 * a4 + lr], rq = sm.rq[qs][16 * a4 + lr];
-          sfac[a4] = (fast ? lam_c * qf : 1.f) * (a.l2norm ? rq : 1.f);
+          for (int a4 = 0; a4 < OTB; ++a4)
+            sfac[a4] = (fast ? lam_c * a.scale * fexp2(sm.gdp[ks][2 * (16 * a4 + lr)]) : 1.f) * rqv[a4];
+        } else {
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const float qf = sm.qfac[qs][16 * a4 + lr], rq = sm.rq[qs][16 * a4 + lr];
+            sfac[a4] = (fast ? lam_c * qf : 1.f) * (a.l2norm ? rq : 1.f);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1539,6 +1636,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // consumer waves together cover whole rows).
       if (stage) {
         const int ntok = toks_of(c);
+        const int row0 = LT ? 32 * j : 0;  // first staged row inside the token chunk
+        const bool full = row0 + 16 * OTB <= ntok;
         char *ob = (char *)((bf16 *)a.o + (t0 + (int64_t)CH * c) * a.o_st + h * a.o_sh + gcol);
         const uint32_t ost = (uint32_t)a.o_st * 2u;
         // every row is packed and addressed first and the stores follow back to
@@ -1549,40 +1648,40 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         // 64 bytes of a row; otherwise each lane stores its two 8-byte pieces.
         const bool o16 = (((uintptr_t)a.o & 15) == 0) && (a.o_st % 8 == 0) && (a.o_sh % 8 == 0);
         if constexpr (NB == 2) if (o16) {
-          uint4 pk[4];
-          uint4 *dst[4];
+          uint4 pk[OTB];
+          uint4 *dst[OTB];
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
+          for (int a4 = 0; a4 < OTB; ++a4) {
             const uint2 p0 = __builtin_bit_cast(uint2, bf4(O[0][a4] * sfac[a4]));
             const uint2 p1 = __builtin_bit_cast(uint2, bf4(O[1][a4] * sfac[a4]));
             const auto rx = __builtin_amdgcn_permlane16_swap(p0.x, p1.x, false, false);
             const auto ry = __builtin_amdgcn_permlane16_swap(p0.y, p1.y, false, false);
             pk[a4] = uint4{(uint32_t)rx[0], (uint32_t)ry[0], (uint32_t)rx[1], (uint32_t)ry[1]};
-            dst[a4] = (uint4 *)(ob + (uint32_t)(16 * a4 + lr) * ost + 16 * (lg >> 1) + 32 * (lg & 1));
+            dst[a4] = (uint4 *)(ob + (uint32_t)(row0 + 16 * a4 + lr) * ost + 16 * (lg >> 1) + 32 * (lg & 1));
           }
           __builtin_amdgcn_sched_barrier(0);
-          if (ntok == CH) {
+          if (full) {
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) *dst[a4] = pk[a4];
+            for (int a4 = 0; a4 < OTB; ++a4) *dst[a4] = pk[a4];
           } else {
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4)
-              if (16 * a4 + lr < ntok) *dst[a4] = pk[a4];
+            for (int a4 = 0; a4 < OTB; ++a4)
+              if (row0 + 16 * a4 + lr < ntok) *dst[a4] = pk[a4];
           }
         }
         if (NB != 2 || !o16) {
-          uint2 pk[4][NB];
-          uint2 *dst[4];
+          uint2 pk[OTB][NB];
+          uint2 *dst[OTB];
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
+          for (int a4 = 0; a4 < OTB; ++a4) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) pk[a4][b] = __builtin_bit_cast(uint2, bf4(O[b][a4] * sfac[a4]));
-            dst[a4] = (uint2 *)(ob + (uint32_t)(16 * a4 + lr) * ost + 8 * lg);
+            dst[a4] = (uint2 *)(ob + (uint32_t)(row0 + 16 * a4 + lr) * ost + 8 * lg);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
-            if (ntok == CH || 16 * a4 + lr < ntok) {
+          for (int a4 = 0; a4 < OTB; ++a4)
+            if (full || row0 + 16 * a4 + lr < ntok) {
 #pragma unroll
               for (int b = 0; b < NB; ++b) dst[a4][4 * b] = pk[a4][b];
             }
@@ -1609,7 +1708,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
   };
   if (w < NCW) {
-    if (NCW > 4 && w >= 4) consumer(IC<1>{});
+    if ((LT && (w & 1)) || (NCW > 4 && w >= 4)) consumer(IC<1>{});
     else consumer(IC<0>{});
   } else {
     // ---------------------------------------------------------------- helpers
@@ -1700,7 +1799,14 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     auto scalars = [&](int x, float &lam_h, bool &fast_h) {
       const int cx = x / n, jx = x - cx * n;
       int fl = 0;
-      if (jx == 0) {
+      if constexpr (LT) {  // per expanded chunk: its own decay decides
+        const float gl = sm.gdp[x % 3][CH - 1];
+        if (lam_h * fexp2(gl) < LAM_MIN && lam_h != 1.f) {
+          fl |= SF_RESCALE;
+          lam_h = 1.f;
+        }
+        fast_h = lam_h * fexp2(gl) >= LAM_MIN;
+      } else if (jx == 0) {
         if constexpr (SUM) {
           fast_h = false;
         } else {
@@ -1969,7 +2075,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       if (nexp > 0) {
         lds_barrier();
         prep_scalars(0);
-        if constexpr (!SUM) finish_q(0);
+        if constexpr (!SUM && !LT) finish_q(0);
         gram(0, 0, 5, 3);
         lds_barrier();
         block(0, IC<0>{});
@@ -1986,7 +2092,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
         // token chunk c+1: its q rows landed with the loads of a chunk before
         // (n >= 2) or before the last barrier (n = 1)
-        if (!SUM && j == n - 1 && c + 1 < ntc) finish_q(c + 1);
+        if (!SUM && !LT && j == n - 1 && c + 1 < ntc) finish_q(c + 1);
         lds_barrier();
         if (e + 1 < nexp) {
           block(e + 1, IC<0>{});
@@ -2000,7 +2106,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         gram(0, 5, 10, 4);
         lds_barrier();
         block(0, IC<2>{});
-        if constexpr (!SUM) tables(0);
+        if constexpr (!SUM && !LT) tables(0);
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
@@ -2009,7 +2115,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         lds_barrier();
         if (e + 1 < nexp) {
           block(e + 1, IC<2>{});
-          if constexpr (!SUM) tables(e + 1);  // needs the k-row norms from the Gram stage
+          if constexpr (!SUM && !LT) tables(e + 1);  // needs the k-row norms from the Gram stage
         }
         lds_barrier();
       }
@@ -2130,6 +2236,13 @@ hipError_t launch_split(const PrefillArgs &a, hipStream_t stream) {
   return launch_scan<T, K, V, 1>(a, stream);
 }
 
+// GDP_FUSED_OUTPUTS=token_chunk keeps the per-token-chunk output form for n = 2
+// too (the tests run both forms on the same inputs)
+bool fused_per_token_chunk() {
+  const char *env = std::getenv("GDP_FUSED_OUTPUTS");
+  return env && std::strcmp(env, "token_chunk") == 0;
+}
+
 template <int K, int V>
 hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
   // 4 consumer waves of V/4 state columns and 4 helper waves.  8 consumer waves
@@ -2138,7 +2251,10 @@ hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
   constexpr int NCW = 4;
   const int64_t blocks = (int64_t)a.N * a.Hv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW, false>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
+  if (a.n == 2 && !a.tc_outputs && !fused_per_token_chunk())
+    hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW, false, 2>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW, false>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
   return hipGetLastError();
 }
 

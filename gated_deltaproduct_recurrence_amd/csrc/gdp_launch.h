@@ -51,6 +51,11 @@ struct PrefillArgs {
   // msum.
   int summary;
   float *msum;                      // [N, Hv, K, K]
+  // fused kernel, n = 2: outputs per token chunk instead of per expanded chunk
+  // (the backward's forward pass asks for it: its chunk states then come from
+  // the per-token-chunk decay logic, whose rounding its decay gradients were
+  // checked against)
+  int tc_outputs;
   // fused kernel: chain run by workgroup b (longest sequences first, spread over
   // the XCDs), or null for the plain XCD-grouped order
   const int32_t *order;             // [N * Hv]

@@ -22,11 +22,23 @@ def gdp():
 # K == V only).  Tests over bf16 inputs run each path forced through
 # GDP_PREFILL_PATH.
 PATHS = ["fused", "split", "segmented"]
+# the fused kernel has two output forms for n = 2: per expanded chunk (the
+# default) and per token chunk (the form every other n uses); "fused_tc" runs
+# the second on the same inputs
+FUSED_FORMS = PATHS + ["fused_tc"]
 
 
-@pytest.fixture(params=PATHS)
+def set_path(monkeypatch, p):
+    monkeypatch.setenv("GDP_PREFILL_PATH", "fused" if p == "fused_tc" else p)
+    if p == "fused_tc":
+        monkeypatch.setenv("GDP_FUSED_OUTPUTS", "token_chunk")
+    else:
+        monkeypatch.delenv("GDP_FUSED_OUTPUTS", raising=False)
+
+
+@pytest.fixture(params=FUSED_FORMS)
 def path(request, monkeypatch):
-    monkeypatch.setenv("GDP_PREFILL_PATH", request.param)
+    set_path(monkeypatch, request.param)
     return request.param
 
 
@@ -245,7 +257,7 @@ STRONG = [
     ([400, 129], 3, 1, 2, 128, 128, torch.bfloat16, False),
     ([130, 70], 2, 1, 2, 64, 64, torch.float32, False),
 ]
-STRONG_PATHS = [(i, p) for i, c in enumerate(STRONG) for p in (PATHS if c[6] == torch.bfloat16 else ["auto"])]
+STRONG_PATHS = [(i, p) for i, c in enumerate(STRONG) for p in (FUSED_FORMS if c[6] == torch.bfloat16 else ["auto"])]
 
 
 def strong_decay_inputs(ci):
@@ -277,7 +289,7 @@ def test_strong_decay_parity(gdp, ci, kpath, monkeypatch):
     """Strong decays against the oracle on every path: the chunks whose decay sum
     falls below 2^-100 take the per-entry decay branch of the output scores, and
     the state's lazy decay scale is renormalised, in every chunk."""
-    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    set_path(monkeypatch, kpath)
     w, inp = strong_decay_inputs(ci)
     assert min_chunk_decay_sum_base2(inp["g_log"], inp["cu_seqlens"].numpy()) < -100.0
     ref = oracle_run(inp)
@@ -342,12 +354,12 @@ CASES = [
 
 
 CASE_PATHS = [(i, p) for i, c in enumerate(CASES)
-              for p in (PATHS if c[6] == torch.bfloat16 else ["auto"]) if p != "segmented" or c[4] == c[5]]
+              for p in (FUSED_FORMS if c[6] == torch.bfloat16 else ["auto"]) if p != "segmented" or c[4] == c[5]]
 
 
 @pytest.mark.parametrize("ci,kpath", CASE_PATHS, ids=[f"case{i}-{p}" for i, p in CASE_PATHS])
 def test_ragged_parity(gdp, ci, kpath, monkeypatch):
-    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    set_path(monkeypatch, kpath)
     lens, n, Hqk, Hv, K, V, dtype, l2 = CASES[ci]
     w = workloads.custom(lens, n, Hqk, Hv, K, V, dtype=dtype, l2norm_in_kernel=l2, init_std=0.2)
     inp = workloads.generate(w, "cpu")
@@ -483,19 +495,20 @@ def test_segmented_long_sequence(gdp, monkeypatch):
 
 
 def test_fused_and_split_agree(gdp, monkeypatch):
-    """Both bf16 paths on the varlen workload: each within tolerance of the
-    oracle, and of each other."""
+    """Every bf16 path and fused output form on the varlen workload: each within
+    tolerance of the oracle, and of the split pair."""
     w = workloads.workload(1)
     inp = workloads.generate(w, "cpu")
     ref = oracle_run(inp)
     dev = to_device(inp)
     out = {}
-    for p in PATHS:
-        monkeypatch.setenv("GDP_PREFILL_PATH", p)
+    for p in FUSED_FORMS:
+        set_path(monkeypatch, p)
         out[p] = run_gpu(gdp, dev)
         check_all(inp, out[p], ref, TOL[w.dtype], what=p)
-    assert rel_err(to_np(out["fused"][0]), to_np(out["split"][0])) <= TOL[w.dtype]
-    assert rel_err(to_np(out["fused"][1]), to_np(out["split"][1])) <= TOL[w.dtype]
+    for p in ("fused", "fused_tc", "segmented"):
+        assert rel_err(to_np(out[p][0]), to_np(out["split"][0])) <= TOL[w.dtype], p
+        assert rel_err(to_np(out[p][1]), to_np(out["split"][1])) <= TOL[w.dtype], p
 
 
 @pytest.mark.parametrize("N,Hqk,Hv", [(40, 4, 8), (90, 1, 3)], ids=["grouped-heads", "odd-grid"])
