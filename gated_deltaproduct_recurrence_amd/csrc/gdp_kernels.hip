@@ -1116,6 +1116,10 @@ constexpr int SF_FAST = 1, SF_LAZY = 2, SF_RESCALE = 4, SF_TF = 8;
 
 // SUM: segment summaries only (the states of the segmented path): no outputs,
 // so the scores, P, O^T, the q rows and the per-row token tables are skipped.
+// One workgroup forms both summaries of its segment, which share the k rows,
+// the decays and the WY matrix: NCW = 8 consumer waves, waves 0-3 holding B
+// (zero start state, the real values) and waves 4-7 holding M (identity start
+// state, zero values, so their E = T Y has no V term).
 // LT = 2 (n = 2 only): outputs per expanded chunk.  With two Householder rows
 // per token an expanded chunk holds whole tokens (32 of them, token blocks 2j
 // and 2j+1 of its token chunk), so each token's output is the state entering
@@ -1127,13 +1131,16 @@ constexpr int SF_FAST = 1, SF_LAZY = 2, SF_RESCALE = 4, SF_TF = 8;
 template <int K, int V, int NCW, bool SUM, int LT = 0>
 __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArgs a) {
   static_assert(LT == 0 || (LT == 2 && !SUM && NCW == 4), "per-expanded-chunk outputs: n = 2, four consumer waves");
+  static_assert(!SUM || (NCW == 8 && K == V), "summaries: four consumer waves each for B and M");
   using S = FusedSmem<K, V>;
-  // NCW consumer waves of 16 NB state columns each cover all V columns; the
-  // 16 score tiles (4 token blocks x 4 row blocks) are shared out RBW per wave
-  constexpr int NB = V / (16 * NCW), BV = V, NVT = 1, KT16 = K / 16, KS = K / 32;
+  // NCG consumer waves of 16 NB state columns each cover all V columns (in
+  // summary mode once for B and once for M); the 16 score tiles (4 token
+  // blocks x 4 row blocks) are shared out RBW per wave
+  constexpr int NCG = SUM ? NCW / 2 : NCW;
+  constexpr int NB = V / (16 * NCG), BV = V, NVT = 1, KT16 = K / 16, KS = K / 32;
   constexpr int RBW = LT ? 2 : 16 / NCW;   // score row blocks per wave
   constexpr int OTB = LT ? LT : 4;          // token blocks of O per wave
-  static_assert(NB >= 1 && 16 * NB * NCW == V && (LT || RBW * NCW == 16), "consumer waves must tile V and the scores");
+  static_assert(NB >= 1 && 16 * NB * NCG == V && (LT || SUM || RBW * NCW == 16), "consumer waves must tile V and the scores");
   constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDT = S::LDT;
   __shared__ S sm;
 
@@ -1145,12 +1152,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   // walks a contiguous range of chains (the heads sharing a q/k head, and the
   // V-tiles of one head, then read the same k/q rows through one L2).
   const int64_t G = gridDim.x, bid = blockIdx.x;
-  int64_t chain = a.order ? (int64_t)a.order[bid] : ((G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid);
-  // segment summaries: the second half of the grid is part 1 (zero values,
-  // identity start state, final state to msum)
-  const int64_t nchain = (int64_t)a.N * a.Hv * NVT;
-  const bool part1 = a.summary && chain >= nchain;
-  if (part1) chain -= nchain;
+  const int64_t chain = a.order ? (int64_t)a.order[bid] : ((G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid);
   const int vt = (int)(chain % NVT);
   const int h = (int)((chain / NVT) % a.Hv);
   const int seq = (int)(chain / ((int64_t)NVT * a.Hv));
@@ -1172,8 +1174,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   // every register array index is a compile-time constant
   auto consumer = [&](auto halfc) {
     constexpr int rb0 = decltype(halfc)::value * RBW;
+    constexpr bool MP = SUM && decltype(halfc)::value == 1;  // a wave of the M summary
     // ---------------------------------------------------------------- consumers
-    const int wcol = w * 16 * NB;     // first column of this wave inside the tile
+    const int wcol = (w % NCG) * 16 * NB;  // first column of this wave inside the tile
     // the wave's score tiles: token block tb, row blocks rb0 .. rb0 + RBW - 1 (with
     // LT, tb is the token block inside the expanded chunk's 32 tokens)
     const int tb = LT ? (w >> 1) : (w & 3);
@@ -1203,7 +1206,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     for (int at = 0; at < KT16; ++at)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        if (part1) {
+        if constexpr (MP) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) Sacc[at][b][i] = kap(at, lg, i) == gcol + 16 * b + lr ? 1.f : 0.f;
         } else if (a.s0) {
@@ -1507,6 +1510,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         const uint32_t vb = off_of(sm.v[ts]) + lcolv.l;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+          if constexpr (MP) continue;  // zero values
           const uint32_t va = (lcolv.x ^ (uint32_t)(2 * wcol + 32 * b)) + vb;
 #pragma unroll
           for (int s = 0; s < 2; ++s)
@@ -1520,10 +1524,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const Frag<bf16> &t0f = tfr[a4 < 2 ? a4 : 2 * a4 - 2];
-          f32x4 acc = mma(t0f, vfr[0][b], zero4());
+          f32x4 acc = MP ? zero4() : mma(t0f, vfr[0][b], zero4());
           acc = mma(t0f, Yb[0][b], acc);
           if (a4 >= 2) {
-            acc = mma(tfr[2 * a4 - 1], vfr[1][b], acc);
+            if constexpr (!MP) acc = mma(tfr[2 * a4 - 1], vfr[1][b], acc);
             acc = mma(tfr[2 * a4 - 1], Yb[1][b], acc);
           }
           E[a4][b] = acc;
@@ -1689,7 +1693,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       }
       lds_barrier();
     }
-    float *fdst = part1 ? a.msum + state_off : (a.final_state ? a.final_state + state_off : nullptr);
+    float *fdst = MP ? a.msum + state_off : (a.final_state ? a.final_state + state_off : nullptr);
     float *cdst = nullptr;
     if (a.cache) {
       const int64_t slot = load_index(a.slots, a.slots_is64, seq);
@@ -1701,7 +1705,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const size_t off = (size_t)kap(at, lg, i) * V + gcol + 16 * b + lr;
+          const int k = kap(at, lg, i), col = gcol + 16 * b + lr;
+          const size_t off = MP ? (size_t)msum_index<K>(k, col) : (size_t)k * V + col;
           const float x = lam * Sacc[at][b][i];
           if (fdst) fdst[off] = x;
           if (cdst) cdst[off] = x;
@@ -2005,13 +2010,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       };
       const TileOffs<KW, 1> koffs = tile_offs<KW, 1>(kst, lane), qoffs = tile_offs<KW, 1>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
-      if (part1) {  // zero values: both v tiles stay zero
-        for (int u = hl; u < 2 * CH * VW / 16; u += 64) *(uint4 *)(sm.v[0] + 16 * u) = uint4{0u, 0u, 0u, 0u};
-      }
       if (nexp > 0) {
         load_k(0, koffs);
         if (nexp > 1) load_k(1, koffs);
-        if (!part1) load_v(0, voffs);
+        load_v(0, voffs);
         load_scalars(0);
         if (nexp > 1) load_scalars(1);
         if constexpr (!SUM) {
@@ -2041,7 +2043,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         // later wait for newer loads covers them): the consumers read the v rows
         // after the next barrier and the Gram stage the k rows of chunk e+2.
         const bool lq = !SUM && j == n - 1 && c + 2 < ntc;
-        if (e + 1 < nexp && !part1) load_v(e + 1, voffs);
+        if (e + 1 < nexp) load_v(e + 1, voffs);
         if (lq) load_q(c + 2, qoffs);
         if (lq && n >= 2) {
           wait_vm_keep<NLQ>();
@@ -2259,9 +2261,9 @@ hipError_t launch_fused(const PrefillArgs &a, hipStream_t stream) {
 }
 
 template <int K, int V>
-hipError_t launch_fused_twice(const PrefillArgs &a, hipStream_t stream) {
-  constexpr int NCW = 4;
-  const int64_t blocks = 2 * (int64_t)a.N * a.Hv;
+hipError_t launch_fused_summary(const PrefillArgs &a, hipStream_t stream) {
+  constexpr int NCW = 8;
+  const int64_t blocks = (int64_t)a.N * a.Hv;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((gdp_fused_kernel<K, V, NCW, true>), dim3((unsigned)blocks), dim3(64 * (NCW + 4)), 0, stream, a);
   return hipGetLastError();
@@ -2309,14 +2311,13 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int K, int V, int pat
 }
 
 hipError_t launch_fused_prefill(const PrefillArgs &a, int K, int V, hipStream_t stream) {
-  // the summary grid holds every chain twice
   if (K == 128 && V == 128) {
     PrefillArgs b = a;
-    return a.summary ? launch_fused_twice<128, 128>(b, stream) : launch_fused<128, 128>(b, stream);
+    return a.summary ? launch_fused_summary<128, 128>(b, stream) : launch_fused<128, 128>(b, stream);
   }
   if (K == 64 && V == 64) {
     PrefillArgs b = a;
-    return a.summary ? launch_fused_twice<64, 64>(b, stream) : launch_fused<64, 64>(b, stream);
+    return a.summary ? launch_fused_summary<64, 64>(b, stream) : launch_fused<64, 64>(b, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -44,13 +44,13 @@ struct PrefillArgs {
   void *tws;                        // WY matrices: [tws_rows, Hv, 64*64] input dtype, fragment order
   int64_t tws_rows;
   void *o; int64_t o_st, o_sh;      // null: no outputs (the segment summaries of the fused kernel)
-  // Segment summaries (fused kernel only, K == V): the grid holds each chain
-  // twice.  Part 0 runs from a zero state with the real values and writes its
-  // final state (B of the segment's map S -> M S + B) to final_state; part 1
-  // runs from the identity with zero values and writes its final state (M) to
-  // msum.
+  // Segment summaries (fused kernel only, K == V): one workgroup per chain
+  // forms both maps.  Its B waves run from a zero state with the real values
+  // and write their final state (B of the segment's map S -> M S + B) to
+  // final_state; its M waves run from the identity with zero values and write
+  // their final state (M) to msum, in the msum_index order.
   int summary;
-  float *msum;                      // [N, Hv, K, K]
+  float *msum;                      // [N, Hv, K * K]
   // fused kernel, n = 2: outputs per token chunk instead of per expanded chunk
   // (the backward's forward pass asks for it: its chunk states then come from
   // the per-token-chunk decay logic, whose rounding its decay gradients were
@@ -113,6 +113,15 @@ struct SegArgs {
   int32_t *seg_first;            // [N+1] first segment of every sequence
   int32_t *seg_cs_off;           // [ns_cap] chunk-state row of every segment's first chunk
 };
+// Layout of one K x K summary M in the msum buffer: entry (k, c) (row k, column
+// c) sits where the combine kernel reads it, so that each of its loads is one
+// contiguous kilobyte per wave.  Wave w of the combine computes rows 16 w .. 16 w
+// + 15 and its lane (lg, lr) holds M[16 w + lr][(K / 4) lg + 4 u + i] as float i
+// of its u-th 16-byte load; the load u of wave w covers floats
+// 256 ((K / 16) w + u) .. + 255, lane-ordered.
+template <int K> __host__ __device__ constexpr int msum_index(int k, int c) {
+  return ((((k >> 4) * (K / 16) + ((c % (K / 4)) >> 2)) * 64 + 16 * (c / (K / 4)) + (k & 15)) << 2) + (c & 3);
+}
 // Segmented prefill: the in-order combination of the segment summaries.
 struct CombineArgs {
   int N, Hv;

@@ -7,17 +7,19 @@
 // input-state -> output-state transition summary, combined by a scan).  Long
 // sequences are cut into segments of whole 64-token chunks; the summaries
 // (M, B) of all segments are formed in parallel by the fused prefill kernel
-// (B from a zero state with the real values, M from the identity with zero
-// values), combined in order per chain here, and the segments are then run
-// again from their true start states.
+// (one workgroup per segment: B from a zero state with the real values, M from
+// the identity with zero values, on the same WY matrices), combined in order
+// per chain here, and the segments are then run again from their true start
+// states.
 //
 //   gdp_segment_kernel   one workgroup: segment boundaries (as a cu_seqlens of
 //                        segments), the first segment of every sequence and
 //                        the chunk-state row offset of every segment
 //   gdp_combine_kernel   one workgroup per (sequence, state head, 16-column
 //                        tile): S = s0; per segment: record S as the segment's
-//                        start state, S = M S + B (fp32 MFMA); final state and
-//                        cache slot at the end
+//                        start state, S = M S + B (fp32 MFMA, M read straight
+//                        into the operand registers); final state and cache
+//                        slot at the end
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -149,103 +151,103 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // memory is waited for where it is used.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// S = M S + B per segment, on a 16-column tile of the state kept in LDS.  M of
-// the segment is staged in LDS with 16-byte stores (rows padded by four floats,
-// so that the 64 lanes reading 16 rows x 4 columns meet 64 banks); the next
-// segment's M and B are read into registers while this one multiplies.  Wave w
-// computes rows 16 w .. 16 w + 15 of the tile with v_mfma_f32_16x16x4_f32: lane
-// (lg, lr) supplies M[row lr][k = 4 kk + lg] and S[k = 4 kk + lg][col lr] and holds
-// C[4 lg + i][lr].
+// S = M S + B per segment, on a 16-column tile of the state.  Wave w computes
+// rows 16 w .. 16 w + 15 of the new tile with v_mfma_f32_16x16x4_f32, taking the
+// reduction index in the order k = (K / 4) lg + kk: at product kk lane (lg, lr)
+// supplies M[16 w + lr][k] and S[k][lr] and holds C[4 lg + i][lr].  The summary
+// kernel stores M in the order these operands are read (msum_index), so they come
+// straight into registers, a kilobyte per wave and load, two segments ahead (no
+// workgroup ever stages M); only the tile of S goes through LDS,
+// transposed (St[c][k], rows padded by four floats so that the 16 lanes reading
+// 16-byte pieces of 16 rows meet distinct banks) and double buffered, so each
+// segment takes one barrier.  Four accumulators split the product chain.
 template <int K, int V>
 __global__ void __launch_bounds__(4 * K) gdp_combine_kernel(CombineArgs a) {
   static_assert(K == 128 || K == 64, "K of 64 or 128");
-  // M rows padded by 4 floats: the fragment reads below (16 rows x 4 columns
-  // per instruction) then meet 64 distinct banks, and rows stay 16-byte aligned
-  // one wave per 16 state rows (K / 16 waves): each step's chain of dependent
-  // products is then K / 4 long
-  constexpr int NT = 4 * K, CT = 16, NCT = V / CT, RT = 1, LDM = K + 4;
-  constexpr int NL = K * K / 4 / NT;  // 16-byte loads of M per thread
-  __shared__ float S[K][CT];
-  __shared__ __attribute__((aligned(16))) float Ms[K * LDM];
+  constexpr int CT = 16, NCT = V / CT, KL = K / 4, LDR = K + 4;
+  __shared__ __attribute__((aligned(16))) float St[2][CT * LDR];
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bid = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin; remap so that each XCD takes
+  // a contiguous range of tiles, which keeps the column tiles of one chain (all
+  // reading the same M) on one XCD's L2
+  const int64_t G = gridDim.x, b0 = blockIdx.x;
+  const int64_t bid = (G % 8 == 0) ? (b0 % 8) * (G / 8) + b0 / 8 : b0;
   const int ct = (int)(bid % NCT);
   const int h = (int)((bid / NCT) % a.Hv);
   const int64_t i = bid / ((int64_t)NCT * a.Hv);
   const size_t KV = (size_t)K * V, KK = (size_t)K * K;
-  const int c0 = ct * CT;
-  for (int x = tid; x < K * CT; x += NT) {
-    const int r = x / CT, c = x % CT;
-    S[r][c] = a.s0 ? a.s0[((size_t)i * a.Hv + h) * KV + (size_t)r * V + c0 + c] : 0.f;
-  }
+  const int c0 = ct * CT, row0 = 16 * w + 4 * lg;  // lane entries: rows row0 .. row0 + 3, column c0 + lr
+  f32x4 s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = a.s0 ? a.s0[((size_t)i * a.Hv + h) * KV + (size_t)(row0 + e) * V + c0 + lr] : 0.f;
   const int64_t s_lo = a.seg_first[i], s_hi = a.seg_first[i + 1];
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  f4 mreg[NL];
-  auto load_m = [&](int64_t s) {
-    const f4 *M = (const f4 *)(a.msum + ((size_t)s * a.Hv + h) * KK);
-#pragma unroll
-    for (int u = 0; u < NL; ++u) mreg[u] = M[tid + NT * u];
+  // M row pieces and B entries of three segments in flight: segment sg uses
+  // buffer sg mod 3 and issues the loads of segment sg + 2.  The loop runs whole
+  // rounds of three steps, and no global load or store in it is conditional, so
+  // that the compiler's waits count exactly and a step waits only for its own
+  // loads: a step past the last segment loads the last segment again, keeps the
+  // tile and stores the last segment's start state again (the same values).
+  struct Ops {
+    f32x4 m[KL / 4], b;
   };
-  // this wave's rows of the segment's B tile, also loaded a segment ahead
-  f32x4 breg[RT];
-  auto load_b = [&](int64_t s) {
-    const float *B = a.bsum + ((size_t)s * a.Hv + h) * KV + c0;
+  Ops o0, o1, o2;
+  auto load = [&](Ops &o, int64_t sg) {
+    // msum_index layout: load u of this wave is one contiguous kilobyte
+    const f32x4 *M = (const f32x4 *)(a.msum + ((size_t)sg * a.Hv + h) * KK) + (size_t)w * (KL / 4) * 64 + lane;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int u = 0; u < KL / 4; ++u) o.m[u] = M[64 * u];
+    const float *B = a.bsum + ((size_t)sg * a.Hv + h) * KV + c0 + lr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) breg[rt][e] = B[(size_t)(w * 16 * RT + 16 * rt + 4 * lg + e) * V + lr];
+    for (int e = 0; e < 4; ++e) o.b[e] = B[(size_t)(row0 + e) * V];
+  };
+  f32x4 sin = s;  // the tile entering the last segment stepped through
+  auto step = [&](const Ops &o, Ops &onext2, int64_t sg) {
+    const bool real = sg < s_hi;
+    load(onext2, min(sg + 2, s_hi - 1));  // into the buffer segment sg - 1 used
+    if (real) sin = s;
+    float *buf = St[sg & 1];
+    *(f32x4 *)&buf[lr * LDR + row0] = s;
+    float *init = a.seg_init + ((size_t)(real ? sg : s_hi - 1) * a.Hv + h) * KV + c0 + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) init[(size_t)(row0 + e) * V] = sin[e];
+    // every wave's rows are in; the barrier also orders this segment's writes of
+    // the other buffer after every wave's reads of it in the segment before
+    lds_sync();
+    f32x4 acc[4];
+    acc[0] = o.b;
+    acc[1] = acc[2] = acc[3] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *sr = &buf[lr * LDR + KL * lg];
+#pragma unroll
+    for (int u = 0; u < KL / 4; ++u) {
+      const f32x4 sv = *(const f32x4 *)(sr + 4 * u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.m[u][q], sv[q], acc[q], 0, 0, 0);
+    }
+    if (real) s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
   if (s_lo < s_hi) {
-    load_m(s_lo);
-    load_b(s_lo);
+    // the start tile has landed before the prefetches are issued (a wait for it
+    // inside the loop would cover every load in flight)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    load(o0, s_lo);
+    load(o1, min(s_lo + 1, s_hi - 1));
+    for (int64_t sg = s_lo; sg < s_hi; sg += 3) {
+      step(o0, o2, sg);
+      step(o1, o0, sg + 1);
+      step(o2, o1, sg + 2);
+    }
   }
-  __syncthreads();
-  for (int64_t s = s_lo; s < s_hi; ++s) {
-    // this segment's M into LDS (element x of the row-major M at row x / K, column x % K)
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int x = 4 * (tid + NT * u), r = x / K, c = x % K;
-      *(f4 *)&Ms[r * LDM + c] = mreg[u];
-    }
-    f32x4 acc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[rt] = breg[rt];
-    if (s + 1 < s_hi) {
-      load_m(s + 1);
-      load_b(s + 1);
-    }
-    float *init = a.seg_init + ((size_t)s * a.Hv + h) * KV + c0;
-    for (int x = tid; x < K * CT; x += NT) {
-      const int r = x / CT, c = x % CT;
-      init[(size_t)r * V + c] = S[r][c];
-    }
-    lds_sync();  // M in LDS
-#pragma unroll 8
-    for (int kk = 0; kk < K / 4; ++kk) {
-      const int kx = 4 * kk + lg;
-      const float bv = S[kx][lr];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ms[(w * 16 * RT + 16 * rt + lr) * LDM + kx], bv, acc[rt], 0, 0, 0);
-    }
-    lds_sync();  // every wave has read S and M
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[w * 16 * RT + 16 * rt + 4 * lg + e][lr] = acc[rt][e];
-    lds_sync();
-  }
-  float *fdst = a.final_state ? a.final_state + ((size_t)i * a.Hv + h) * KV + c0 : nullptr;
+  float *fdst = a.final_state ? a.final_state + ((size_t)i * a.Hv + h) * KV + c0 + lr : nullptr;
   float *cdst = nullptr;
   if (a.cache) {
     const int64_t slot = seg_index_at(a.slots, a.slots_is64, i);
-    if (slot >= 0 && slot < a.num_slots) cdst = a.cache + ((size_t)slot * a.Hv + h) * KV + c0;
+    if (slot >= 0 && slot < a.num_slots) cdst = a.cache + ((size_t)slot * a.Hv + h) * KV + c0 + lr;
   }
-  for (int x = tid; x < K * CT; x += NT) {
-    const int r = x / CT, c = x % CT;
-    if (fdst) fdst[(size_t)r * V + c] = S[r][c];
-    if (cdst) cdst[(size_t)r * V + c] = S[r][c];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (fdst) fdst[(size_t)(row0 + e) * V] = s[e];
+    if (cdst) cdst[(size_t)(row0 + e) * V] = s[e];
   }
 }
 
