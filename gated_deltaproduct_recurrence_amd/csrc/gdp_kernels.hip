@@ -1089,8 +1089,13 @@ template <int K, int V> struct FusedSmem {
   char k[3][CH * KW];
   char v[2][CH * VW];
   char q[2][CH * KW];
-  bf16 t[CH * LDT];         // T^T of the chunk being consumed: entry (r, c) of T at [c * LDT + r]
-  bf16 p[CH * LDC];
+  bf16 t[CH * LDT];         // T^T of the chunk being consumed: entry (r, c) of T at
+                            // [c * LDT + (r ^ (8 ((c / 8) mod 2)))], the xor halving the
+                            // bank conflicts of the 16-row stores without costing the
+                            // transposing reads any
+  bf16 p[CH * LDC];         // P: entry (t, r) with r = 32 s + 16 h + 4 g + i at
+                            // [t * LDC + 32 s + 8 g + 4 h + i], so that a lane's 8 values of
+                            // an MFMA operand are one 16-byte read
   float gram[10][64 * 4];   // Gram tiles of the next chunk, lane order; the diagonal
                             // ones are then reused for the rows of -L
   bf16 alow[6][64 * 4];     // A below the diagonal blocks (A-operand layout, lane order)
@@ -1142,7 +1147,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   constexpr int OTB = LT ? LT : 4;          // token blocks of O per wave
   static_assert(NB >= 1 && 16 * NB * NCG == V && (LT || SUM || RBW * NCW == 16), "consumer waves must tile V and the scores");
   constexpr int KW = S::KW, VW = S::VW, LDC = S::LDC, LDT = S::LDT;
-  __shared__ S sm;
+  // 16-byte alignment lets the 8- and 16-byte LDS accesses below compile to
+  // single b64 / b128 instructions (at 4-byte alignment an 8-byte store is split
+  // into a write2_b32 that takes twice the cycles)
+  __shared__ __attribute__((aligned(16))) S sm;
 
   // the wave index is uniform per wave: role branches below contain barriers
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -1252,8 +1260,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       const int lr = ln & 15, lg = ln >> 4;
       const int rt = 4 * lg + (lr >> 2);  // row of a transposing read inside its 16-row group
       const SwLane lcolv = sw_lane<VW>(rt, 8 * (lr & 3));                // v columns
-      const uint32_t lt = (uint32_t)((rt * LDT + 4 * (lr & 3)) * 2);  // T^T columns
-      const uint32_t lp = (uint32_t)((lr * LDC + 4 * lg) * 2);        // P rows
+      const uint32_t lt = (uint32_t)((rt * LDT + ((4 * (lr & 3)) ^ (8 * ((rt >> 3) & 1)))) * 2);  // T^T columns
+      const uint32_t lp = (uint32_t)((lr * LDC + 8 * lg) * 2);        // P rows
       const uint32_t kt = off_of(sm.k[ks]), qt = off_of(sm.q[qs]);
       const float *gtok = sm.gtok[qs], *qfac = sm.qfac[qs];
       const float *rk = sm.rk[ts], *gkr = sm.gkr[ts];
@@ -1438,7 +1446,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? Pacc[pa][i] : 0.f;
-            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+            *(bf16x4 *)((char *)&sm + pw + 64 * (a4 >> 1) + 8 * (a4 & 1)) = bf4(val);
           }
         } else if (LT) {  // per entry: scale rk_r 2^(G(t) - G_r), both on the expanded cumsum
           const float *gd = sm.gdp[ks];
@@ -1450,7 +1458,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? rq * rk4[i] * fexp2(gt - gk4[i]) * Pacc[pa][i] : 0.f;
-            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+            *(bf16x4 *)((char *)&sm + pw + 64 * (a4 >> 1) + 8 * (a4 & 1)) = bf4(val);
           }
         } else if (fact) {
           const float qv = qfac[t];
@@ -1462,7 +1470,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? f4[i] * Pacc[pa][i] : 0.f;
-            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+            *(bf16x4 *)((char *)&sm + pw + 64 * (a4 >> 1) + 8 * (a4 & 1)) = bf4(val);
           }
         } else {
           const float gt = gtok[t], rq = a.scale;
@@ -1473,7 +1481,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = r0 + i < rlim ? rq * rk4[i] * fexp2(gt - gk4[i]) * Pacc[pa][i] : 0.f;
-            *(bf16x4 *)((char *)&sm + pw + 32 * a4) = bf4(val);
+            *(bf16x4 *)((char *)&sm + pw + 64 * (a4 >> 1) + 8 * (a4 & 1)) = bf4(val);
           }
         }
       }
@@ -1541,8 +1549,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       auto load_pf = [&](int a4, int buf) {  // P rows of token block a4
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          pf[buf][s].v = __builtin_shufflevector(rd8(pr + (16 * a4 * LDC + 32 * s) * 2), rd8(pr + (16 * a4 * LDC + 32 * s + 16) * 2),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
+          pf[buf][s].v = rd16(pr + (16 * a4 * LDC + 32 * s) * 2);
       };
       if constexpr (!SUM) load_pf(0, 0);
       const uint32_t kcb = kt + lcolk.l;
@@ -1915,6 +1922,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // T diag(beta) at [c * LDT + r])
     auto merge = [&](int x) {
       bf16 *tt = sm.t;
+      const int tsw = 8 * ((lr >> 3) & 1);  // the T^T swizzle of this lane's rows
       // every input is read first, so that the merge waits for one LDS round trip
       bf16x4 tc[4], tn[4], al[6];
       float bcol[4];  // beta of the column this lane writes in each column block
@@ -1942,10 +1950,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const f32x4 d = f32x4{(float)tc[b][0], (float)tc[b][1], (float)tc[b][2], (float)tc[b][3]} * (frow[b] * bcol[b]);
-        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + 4 * lg) = bf4(d);
+        *(bf16x4 *)(tt + (16 * b + lr) * LDT + 16 * b + ((4 * lg) ^ tsw)) = bf4(d);
       }
       auto put = [&](int ra, int rb, f32x4 v) {  // v: T[16 ra + 4 lg + i][16 rb + lr]; writes it times f_row beta_col
-        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + 4 * lg) = bf4(v * (frow[ra] * bcol[rb]));
+        *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + ((4 * lg) ^ tsw)) = bf4(v * (frow[ra] * bcol[rb]));
         return bf4(v);
       };
       // distance 1
@@ -1960,7 +1968,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     };
     if (hw == 0) {
       // the two T^T blocks above the diagonal that the consumers' fragments cover
-      // ((0,1) and (2,3) of T) stay zero; nothing else writes them
+      // ((0,1) and (2,3) of T) stay zero; nothing else writes them (the T^T
+      // swizzle keeps every 16-column group of a row in place)
       for (int u = lane; u < 2 * 16 * 2; u += 64) {
         const int blk = u >> 5, row = (u >> 1) & 15, half = u & 1;
         *(uint4 *)(sm.t + (16 + 32 * blk + row) * LDT + 32 * blk + 8 * half) = uint4{0u, 0u, 0u, 0u};
