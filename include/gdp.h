@@ -108,7 +108,10 @@ int gdp_build_descriptors(const gdp_tensor *cu_seqlens, int32_t num_householder,
  * passes none; plus an int32 work order of N x Hv entries when N x Hv > 256 and
  * N <= 4096; plus an int32 chunk counter per (sequence, state head) when
  * Hv > Hqk (the fused kernel paces the state heads that share a q/k head).
- * Returns 0 for invalid sizes or dtypes. */
+ * The size depends on host-known shapes only, so one allocation serves every
+ * call of a captured batch shape, as the fixed-length descriptors do (Megatron
+ * Core page, core.ssm.ops.gdp.chunk, the note on the descriptor arguments and
+ * graph capture).  Returns 0 for invalid sizes or dtypes. */
 size_t gdp_workspace_bytes(int64_t T, int64_t N, int32_t num_householder, int32_t Hqk,
                            int32_t Hv, int32_t K, int32_t V, int32_t dtype);
 
@@ -340,10 +343,14 @@ enum gdp_debug_bits { GDP_DBG_CU = 1, GDP_DBG_SLOT = 2, GDP_DBG_DUP = 4 };
  * GDP_EHIP on a runtime failure. */
 int gdp_debug_status(uint32_t *word, int32_t clear, void *stream);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none).  A request the
+ * library does not serve is declined with GDP_EUNSUPPORTED and its reason left
+ * here rather than aborting the caller, the way the FlashInfer page
+ * (flashinfer.gdp_prefill.chunk_gated_delta_product, requirements note) has an
+ * engine decline a graph it cannot serve and log why. */
 const char *gdp_last_error(void);
 
-/* Library version string. */
+/* Library version string.  Informational; no passage of the pages defines it. */
 const char *gdp_version(void);
 
 #ifdef __cplusplus
