@@ -1290,7 +1290,6 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // row 16 tb + lr over the 32 elements this lane reads
       float qss = 0.f;
       const bool qnorm = j == 0 && a.l2norm;
-      float rqv[LT ? OTB : 1];  // (LT) q-row rstd of the expanded chunk's token blocks, per lane row
       if constexpr (LT) {
         // X = K Sst, the wave's score tiles and O^T = Sst^T Q^T of the expanded
         // chunk's two token blocks (rows 32 j + 16 a4 + lr of the q tile), all on
@@ -1329,18 +1328,16 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           for (int a4 = 0; a4 < 2; ++a4)
 #pragma unroll
             for (int b = 0; b < NB; ++b) O[b][a4] = mma(Sb[b], qf[s & 1][a4], s == 0 ? zero4() : O[b][a4]);
-          if (a.l2norm) {
-#pragma unroll
-            for (int a4 = 0; a4 < 2; ++a4) qs2[a4] += seg_sumsq<bf16>(__builtin_bit_cast(uint4, qf[s & 1][a4].v));
-          }
+          if (a.l2norm && w < 2) qs2[0] += seg_sumsq<bf16>(__builtin_bit_cast(uint4, qf[s & 1][decltype(halfc)::value].v));
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int a4 = 0; a4 < 2; ++a4) {
-          float x = qs2[a4];
+        // q-row rstd: waves 0 and 1 form it for token blocks 0 and 1 of the
+        // expanded chunk and leave it in LDS for every wave's staging
+        if (a.l2norm && w < 2) {
+          float x = qs2[0];
           x += __shfl_xor(x, 16, 64);
           x += __shfl_xor(x, 32, 64);
-          rqv[a4] = a.l2norm ? frsq(x + 1e-6f) : 1.f;
+          if (lg == 0) sm.rq[ts][16 * decltype(halfc)::value + lr] = frsq(x + 1e-6f);
         }
       } else
       // k (and q) fragments of reduction step s+1 are read while step s multiplies
@@ -1617,7 +1614,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         if constexpr (LT) {
 #pragma unroll
           for (int a4 = 0; a4 < OTB; ++a4)
-            sfac[a4] = (fast ? lam_c * a.scale * fexp2(sm.gdp[ks][2 * (16 * a4 + lr)]) : 1.f) * rqv[a4];
+            sfac[a4] = (fast ? lam_c * a.scale * fexp2(sm.gdp[ks][2 * (16 * a4 + lr)]) : 1.f) * (a.l2norm ? sm.rq[ts][16 * a4 + lr] : 1.f);
         } else {
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4) {
