@@ -1710,10 +1710,17 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int k = kap(at, lg, i), col = gcol + 16 * b + lr;
-          const size_t off = MP ? (size_t)msum_index<K>(k, col) : (size_t)k * V + col;
           const float x = lam * Sacc[at][b][i];
-          if (fdst) fdst[off] = x;
-          if (cdst) cdst[off] = x;
+          if constexpr (MP) {  // M as a bfloat16 hi/lo pair (msum_index)
+            bf16 *mb = (bf16 *)fdst;
+            const bf16 hi = (bf16)x;
+            mb[msum_index<K>(k, col, 0)] = hi;
+            mb[msum_index<K>(k, col, 1)] = (bf16)(x - (float)hi);
+          } else {
+            const size_t off = (size_t)k * V + col;
+            if (fdst) fdst[off] = x;
+            if (cdst) cdst[off] = x;
+          }
         }
   };
   if (w < NCW) {

@@ -48,7 +48,8 @@ struct PrefillArgs {
   // forms both maps.  Its B waves run from a zero state with the real values
   // and write their final state (B of the segment's map S -> M S + B) to
   // final_state; its M waves run from the identity with zero values and write
-  // their final state (M) to msum, in the msum_index order.
+  // their final state (M) to msum as a bfloat16 hi/lo pair, in the msum_index
+  // order.
   int summary;
   float *msum;                      // [N, Hv, K * K]
   // fused kernel, n = 2: outputs per token chunk instead of per expanded chunk
@@ -113,14 +114,15 @@ struct SegArgs {
   int32_t *seg_first;            // [N+1] first segment of every sequence
   int32_t *seg_cs_off;           // [ns_cap] chunk-state row of every segment's first chunk
 };
-// Layout of one K x K summary M in the msum buffer: entry (k, c) (row k, column
-// c) sits where the combine kernel reads it, so that each of its loads is one
-// contiguous kilobyte per wave.  Wave w of the combine computes rows 16 w .. 16 w
-// + 15 and its lane (lg, lr) holds M[16 w + lr][(K / 4) lg + 4 u + i] as float i
-// of its u-th 16-byte load; the load u of wave w covers floats
-// 256 ((K / 16) w + u) .. + 255, lane-ordered.
-template <int K> __host__ __device__ constexpr int msum_index(int k, int c) {
-  return ((((k >> 4) * (K / 16) + ((c % (K / 4)) >> 2)) * 64 + 16 * (c / (K / 4)) + (k & 15)) << 2) + (c & 3);
+// Layout of one K x K summary M in the msum buffer (K * K floats' room): M is
+// kept as a pair of bfloat16 matrices, M_hi = bf16(M) and M_lo = bf16(M - M_hi),
+// in the order the combine kernel reads its MFMA A operands, so that each of its
+// loads is one contiguous kilobyte per wave.  Wave w of the combine computes rows
+// 16 w .. 16 w + 15; for the 32-deep reduction block u its lane (lg, lr) holds
+// M[16 w + lr][32 u + 8 lg .. + 7] of part p (0: hi, 1: lo) as one 16-byte piece.
+// msum_index gives the bfloat16 element index of entry (k, c) of part p.
+template <int K> __host__ __device__ constexpr int msum_index(int k, int c, int p) {
+  return (((((k >> 4) * (K / 32) + (c >> 5)) * 2 + p) * 64 + 16 * ((c >> 3) & 3) + (k & 15)) << 3) + (c & 7);
 }
 // Segmented prefill: the in-order combination of the segment summaries.
 struct CombineArgs {

@@ -17,9 +17,9 @@
 //                        the chunk-state row offset of every segment
 //   gdp_combine_kernel   one workgroup per (sequence, state head, 16-column
 //                        tile): S = s0; per segment: record S as the segment's
-//                        start state, S = M S + B (fp32 MFMA, M read straight
-//                        into the operand registers); final state and cache
-//                        slot at the end
+//                        start state, S = M S + B (split-precision bf16 MFMA,
+//                        M read straight into the operand registers); final
+//                        state and cache slot at the end
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -151,20 +151,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // memory is waited for where it is used.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
 // S = M S + B per segment, on a 16-column tile of the state.  Wave w computes
-// rows 16 w .. 16 w + 15 of the new tile with v_mfma_f32_16x16x4_f32, taking the
-// reduction index in the order k = (K / 4) lg + kk: at product kk lane (lg, lr)
-// supplies M[16 w + lr][k] and S[k][lr] and holds C[4 lg + i][lr].  The summary
-// kernel stores M in the order these operands are read (msum_index), so they come
-// straight into registers, a kilobyte per wave and load, two segments ahead (no
-// workgroup ever stages M); only the tile of S goes through LDS,
-// transposed (St[c][k], rows padded by four floats so that the 16 lanes reading
-// 16-byte pieces of 16 rows meet distinct banks) and double buffered, so each
-// segment takes one barrier.  Four accumulators split the product chain.
+// rows 16 w .. 16 w + 15 of the new tile on bf16 16x16x32 MFMA in three products
+// per 32-deep block (split precision: with x_hi = bf16(x) and x_lo = bf16(x -
+// x_hi), M S = M_hi S_hi + M_hi S_lo + M_lo S_hi up to the M_lo S_lo term, about
+// 2^-16 relative, with fp32 accumulation).  The summary kernel stores M_hi and
+// M_lo in the order these A operands are read (msum_index), so they come straight
+// into registers, a kilobyte per wave and load, two segments ahead (no workgroup
+// ever stages M); only the tile of S goes through LDS, transposed (St[c][k], rows
+// padded by four floats so that 16 lanes reading 16-byte pieces of 16 rows meet
+// distinct banks) and double buffered, so each segment takes one barrier.  Each
+// lane splits its 8 S values of a block into the two bfloat16 parts itself.
 template <int K, int V>
 __global__ void __launch_bounds__(4 * K) gdp_combine_kernel(CombineArgs a) {
   static_assert(K == 128 || K == 64, "K of 64 or 128");
-  constexpr int CT = 16, NCT = V / CT, KL = K / 4, LDR = K + 4;
+  constexpr int CT = 16, NCT = V / CT, NU = K / 32, LDR = K + 4;
   __shared__ __attribute__((aligned(16))) float St[2][CT * LDR];
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,21 +185,23 @@ __global__ void __launch_bounds__(4 * K) gdp_combine_kernel(CombineArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) s[e] = a.s0 ? a.s0[((size_t)i * a.Hv + h) * KV + (size_t)(row0 + e) * V + c0 + lr] : 0.f;
   const int64_t s_lo = a.seg_first[i], s_hi = a.seg_first[i + 1];
-  // M row pieces and B entries of three segments in flight: segment sg uses
+  // M operands and B entries of three segments in flight: segment sg uses
   // buffer sg mod 3 and issues the loads of segment sg + 2.  The loop runs whole
   // rounds of three steps, and no global load or store in it is conditional, so
   // that the compiler's waits count exactly and a step waits only for its own
   // loads: a step past the last segment loads the last segment again, keeps the
   // tile and stores the last segment's start state again (the same values).
   struct Ops {
-    f32x4 m[KL / 4], b;
+    uint4 m[NU][2];  // [block][hi, lo]
+    f32x4 b;
   };
   Ops o0, o1, o2;
   auto load = [&](Ops &o, int64_t sg) {
-    // msum_index layout: load u of this wave is one contiguous kilobyte
-    const f32x4 *M = (const f32x4 *)(a.msum + ((size_t)sg * a.Hv + h) * KK) + (size_t)w * (KL / 4) * 64 + lane;
+    const uint4 *M = (const uint4 *)(a.msum + ((size_t)sg * a.Hv + h) * KK) + (size_t)w * NU * 2 * 64 + lane;
 #pragma unroll
-    for (int u = 0; u < KL / 4; ++u) o.m[u] = M[64 * u];
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) o.m[u][p] = M[(2 * u + p) * 64];
     const float *B = a.bsum + ((size_t)sg * a.Hv + h) * KV + c0 + lr;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o.b[e] = B[(size_t)(row0 + e) * V];
@@ -214,17 +219,27 @@ __global__ void __launch_bounds__(4 * K) gdp_combine_kernel(CombineArgs a) {
     // every wave's rows are in; the barrier also orders this segment's writes of
     // the other buffer after every wave's reads of it in the segment before
     lds_sync();
-    f32x4 acc[4];
+    f32x4 acc[3];
     acc[0] = o.b;
-    acc[1] = acc[2] = acc[3] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float *sr = &buf[lr * LDR + KL * lg];
+    acc[1] = acc[2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *sr = &buf[lr * LDR + 8 * lg];
 #pragma unroll
-    for (int u = 0; u < KL / 4; ++u) {
-      const f32x4 sv = *(const f32x4 *)(sr + 4 * u);
+    for (int u = 0; u < NU; ++u) {
+      const f32x4 x0 = *(const f32x4 *)(sr + 32 * u), x1 = *(const f32x4 *)(sr + 32 * u + 4);
+      bf16x8_t shi, slo;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.m[u][q], sv[q], acc[q], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const float x = j < 4 ? x0[j] : x1[j - 4];
+        const __bf16 hx = (__bf16)x;
+        shi[j] = hx;
+        slo[j] = (__bf16)(x - (float)hx);
+      }
+      const bf16x8_t mhi = __builtin_bit_cast(bf16x8_t, o.m[u][0]), mlo = __builtin_bit_cast(bf16x8_t, o.m[u][1]);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mhi, shi, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mhi, slo, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mlo, shi, acc[2], 0, 0, 0);
     }
-    if (real) s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (real) s = acc[0] + (acc[1] + acc[2]);
   };
   if (s_lo < s_hi) {
     // the start tile has landed before the prefetches are issued (a wait for it
