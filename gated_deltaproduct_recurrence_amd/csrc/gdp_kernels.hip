@@ -1740,6 +1740,12 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     //                consumers read after that barrier.
     // The loads are spread over the four helpers as well.
     const int hw = w - NCW;
+    // In summary mode each SIMD runs two consumer waves and one helper, and the
+    // WY helpers are the critical path (their Gram, block and merge stages take
+    // longer than the consumers' phases): they issue first
+    if constexpr (SUM) {
+      if (hw != 0) __builtin_amdgcn_s_setprio(1);
+    }
     const bf16 *qg = (const bf16 *)a.q + hq * a.q_sh;
     const bf16 *kg = (const bf16 *)a.k + hk * a.k_sh;
     const bf16 *vg = (const bf16 *)a.v + h * a.v_sh + vt * BV;
