@@ -464,13 +464,15 @@ def test_graph_capture_replay(gdp, path):
         assert torch.equal(go, o) and torch.equal(gs, fs), f"replay differs from eager for {lens}"
 
 
-def test_segmented_long_sequence(gdp, monkeypatch):
+@pytest.mark.parametrize("d", [128, 64])
+def test_segmented_long_sequence(gdp, monkeypatch, d):
     """A sequence long enough for several segments, with GQA, chunk states and a
-    cache slot: the automatic choice is the segmented path (4 chains); every
-    output, the final state, the chunk-state rows and the cache slot match the
-    oracle, and the fused path on the same inputs."""
+    cache slot: the automatic choice is the segmented path (4 chains, a dozen
+    segments for the longer sequence, so the combine steps through many maps);
+    every output, the final state, the chunk-state rows and the cache slot match
+    the oracle, and the fused path on the same inputs."""
     monkeypatch.delenv("GDP_PREFILL_PATH", raising=False)
-    w = workloads.custom([3000, 1500], 2, 1, 2, 128, 128, dtype=torch.bfloat16, l2norm_in_kernel=True, init_std=0.2,
+    w = workloads.custom([3000, 1500], 2, 1, 2, d, d, dtype=torch.bfloat16, l2norm_in_kernel=True, init_std=0.2,
                          seed=31, state_cache_slots=3)
     inp = workloads.generate(w, "cpu")
     inp["state_indices"] = torch.tensor([2, 0], dtype=torch.int32)
