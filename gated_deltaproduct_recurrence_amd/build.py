@@ -10,7 +10,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdp.so")
 SOURCES = [os.path.join(CSRC, "gdp_kernels.hip"), os.path.join(CSRC, "gdp_decode.hip"),
            os.path.join(CSRC, "gdp_segments.hip"), os.path.join(CSRC, "gdp_frontend.hip"),
-           os.path.join(CSRC, "gdp_backward.hip"), os.path.join(CSRC, "gdp_validate.hip"),
+           os.path.join(CSRC, "gdp_backward.hip"), os.path.join(CSRC, "gdp_bwd_chunk.hip"),
+           os.path.join(CSRC, "gdp_validate.hip"),
            os.path.join(CSRC, "gdp_noalloc.hip"),
            os.path.join(CSRC, "gdp_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -683,8 +683,15 @@ int gdp_chunk_prefill_noalloc(const gdp_tensor *q, const gdp_tensor *k, const gd
 }
 
 namespace {
+// Workspace of the backward call.  Recurrent path: descriptors, the state
+// entering every token chunk, the forward's outputs, the rows' norm factors,
+// the forward's own workspace.  Chunked path: descriptors, the state entering
+// and the state gradient leaving every expanded chunk, the prep bundles.  The
+// size is the larger of the two for inputs the chunked path serves, so either
+// path runs in it.
 struct BwdLayout {
   size_t desc = 0, cs = 0, o = 0, rn = 0, fwd = 0, total = 0;
+  size_t xs = 0, xd = 0, xb = 0, xtotal = 0;  // chunked path
   int64_t nt_cap = 0, ntdp_cap = 0;
 };
 static BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V, int32_t dtype) {
@@ -699,15 +706,60 @@ static BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_
   // the rows' norm factors: q [T, Hqk], k [T*n, Hk <= Hv], then one float 1
   L.fwd = L.rn + align256((size_t)T * Hqk * 4) + align256((size_t)T * n * Hv * 4) + 256;
   L.total = L.fwd + fwd;
+  if (gdp::bwd_chunked_supported(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, K, V, n)) {
+    const size_t rows = (size_t)(L.ntdp_cap > 0 ? L.ntdp_cap : 1);
+    L.xs = L.cs;  // after the descriptors
+    L.xd = L.xs + align256(rows * Hv * K * V * 4);
+    L.xb = L.xd + align256(rows * Hv * K * V * 4);
+    L.xtotal = L.xb + align256(rows * Hv * gdp::bwd_bundle_bytes(n));
+  }
   return L;
 }
+// GDP_BACKWARD_PATH=recurrent keeps the per-token kernel for inputs the chunked
+// path serves (for comparison); any other value or none picks the chunked path.
+static bool env_backward_recurrent() {
+  const char *s = std::getenv("GDP_BACKWARD_PATH");
+  return s && std::strcmp(s, "recurrent") == 0;
+}
 }  // namespace
+
+// The backward's last steps on both paths: zero rows of dv outside every
+// sequence, and (with the in-kernel norm) the gradients by the raw q and k rows
+// from those by their normalised rows.
+static int bwd_finish(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *dq, const gdp_tensor *dk,
+                      const gdp_tensor *dv, const gdp_tensor *cu_seqlens, int64_t T, int64_t N, int32_t n, int64_t Hqk,
+                      int64_t Hk, int64_t Hv, int64_t K, int64_t V, int idt, int32_t use_qk_l2norm, void *stream) {
+  hipError_t e;
+  {  // the rows of dv no sequence covers (before cu[0] or from cu[N] on) are zero
+    gdp::ZeroOutsideArgs z;
+    z.p = (float *)dv->data; z.st = dv->stride[0]; z.sh = dv->stride[1];
+    z.cu = cu_seqlens->data; z.cu_is64 = cu_seqlens->dtype == GDP_I64;
+    z.T = T; z.N = (int)N; z.n = n; z.heads = (int)Hv; z.D = (int)V;
+    if ((e = gdp::launch_zero_outside(z, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
+  }
+  if (use_qk_l2norm) {
+    gdp::NormGradArgs na;
+    na.x = q->data; na.x_st = q->stride[0]; na.x_sh = q->stride[1];
+    na.g = (float *)dq->data; na.g_st = dq->stride[0]; na.g_sh = dq->stride[1];
+    na.rows = T * Hqk; na.heads = (int)Hqk;
+    if ((e = gdp::launch_l2norm_grad(na, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "norm gradient launch: %s", hipGetErrorString(e));
+    na.x = k->data; na.x_st = k->stride[0]; na.x_sh = k->stride[1];
+    na.g = (float *)dk->data; na.g_st = dk->stride[0]; na.g_sh = dk->stride[1];
+    na.rows = T * n * Hk; na.heads = (int)Hk;
+    if ((e = gdp::launch_l2norm_grad(na, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "norm gradient launch: %s", hipGetErrorString(e));
+  }
+  return GDP_OK;
+}
 
 size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_t Hv, int32_t K, int32_t V,
                                     int32_t dtype) {
   if (T < 0 || N < 0 || n < 1 || Hqk < 1 || Hv < 1 || K < 1 || V < 1) return 0;
   if (dtype != GDP_F32 && dtype != GDP_BF16) return 0;
-  return bwd_layout(T, N, n, Hqk, Hv, K, V, dtype).total;
+  const BwdLayout L = bwd_layout(T, N, n, Hqk, Hv, K, V, dtype);
+  return std::max(L.total, L.xtotal);
 }
 
 int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,
@@ -772,8 +824,13 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
       if (overlap(outs[i], outs[j])) return fail(GDP_EALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
   const BwdLayout L = bwd_layout(T, N, n, (int32_t)Hqk, (int32_t)Hv, (int32_t)K, (int32_t)V, dt);
   if (!L.total) return fail(GDP_EINVAL, "bad sizes");
-  if (!workspace || workspace_bytes < L.total)
-    return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  const size_t need = std::max(L.total, L.xtotal);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDP_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  bool chunked = L.xtotal > 0 && !env_backward_recurrent();
+  // (the chunked kernels read q, k, v and d_o rows in 16-byte pieces)
+  for (const gdp_tensor *t : {q, k, v, d_o})
+    if (((uintptr_t)t->data & 15) || (t->stride[0] % 8) || (t->stride[1] % 8)) chunked = false;
   if ((uintptr_t)workspace & 255) return fail(GDP_EWORKSPACE, "workspace must be 256-byte aligned");
   char *ws = (char *)workspace;
 
@@ -787,24 +844,57 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   d.nt_cap = L.nt_cap; d.ntdp_cap = L.ntdp_cap;
   gdp_tensor cu = *cu_seqlens;
   if ((rc = gdp_build_descriptors(&cu, n, T, &d, stream)) != GDP_OK) return rc;
-  const int64_t csr = L.nt_cap > 0 ? L.nt_cap : 1;
-  gdp_tensor tcs{ws + L.cs, GDP_F32, 4, {csr, Hv, K, V}, {Hv * K * V, K * V, V, 1}};
-  gdp_tensor to{ws + L.o, dt, 3, {T, Hv, V}, {Hv * V, V, 1}};
   gdp_tensor none{};
-  if ((rc = prefill_impl(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, 0, use_qk_l2norm, &none, &none, 1,
-                         &to, &none, &tcs, &d, ws + L.fwd, workspace_bytes - L.fwd, stream, false, true)) != GDP_OK)
-    return rc;
   hipError_t e;
+  const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
+  const int64_t csr = L.nt_cap > 0 ? L.nt_cap : 1;
+  if (!chunked) {  // the forward pass leaving the state entering every token chunk
+    gdp_tensor tcs{ws + L.cs, GDP_F32, 4, {csr, Hv, K, V}, {Hv * K * V, K * V, V, 1}};
+    gdp_tensor to{ws + L.o, dt, 3, {T, Hv, V}, {Hv * V, V, 1}};
+    if ((rc = prefill_impl(q, k, v, g_log, beta, n, cu_seqlens, scale, initial_state, 0, use_qk_l2norm, &none, &none,
+                           1, &to, &none, &tcs, &d, ws + L.fwd, workspace_bytes - L.fwd, stream, false, true)) != GDP_OK)
+      return rc;
+  }
   for (const gdp_tensor *t : {dq, dk, dg_log, dbeta}) {
     int64_t cnt = 1;
     for (int i = 0; i < t->ndim; ++i) cnt *= t->shape[i];
     if ((e = gdp::launch_fill((int32_t *)t->data, cnt, 0, (hipStream_t)stream)) != hipSuccess)
       return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
   }
+  if (chunked) {
+    gdp::BwdChunkArgs c;
+    std::memset(&c, 0, sizeof c);
+    c.q = q->data; c.q_st = q->stride[0]; c.q_sh = q->stride[1];
+    c.k = k->data; c.k_st = k->stride[0]; c.k_sh = k->stride[1];
+    c.v = v->data; c.v_st = v->stride[0]; c.v_sh = v->stride[1];
+    c.g = (const float *)g_log->data; c.g_st = g_log->stride[0]; c.g_sh = g_log->stride[1];
+    c.beta = (const float *)beta->data; c.b_st = beta->stride[0]; c.b_sh = beta->stride[1];
+    c.cu = cu_seqlens->data; c.cu_is64 = cu_seqlens->dtype == GDP_I64;
+    c.T = T; c.N = (int)N; c.n = n; c.Hqk = (int)Hqk; c.Hv = (int)Hv; c.Hk = (int)Hk;
+    c.scale = (scale == 0.0f) ? (float)(1.0 / std::sqrt((double)K)) : scale;
+    c.l2norm = use_qk_l2norm ? 1 : 0;
+    c.chunk_indices_dp = d.chunk_indices_dp;
+    c.chunk_offsets_dp = d.chunk_offsets_dp;
+    c.ntdp_rows = L.ntdp_cap;
+    c.bundle = ws + L.xb;
+    c.s0 = present(initial_state) ? (const float *)initial_state->data : nullptr;
+    c.states = (float *)(ws + L.xs);
+    c.dstates = (float *)(ws + L.xd);
+    c.dout = d_o->data; c.do_st = d_o->stride[0]; c.do_sh = d_o->stride[1];
+    c.dfinal = present(d_final_state) ? (const float *)d_final_state->data : nullptr;
+    c.ds0 = present(d_initial_state) ? (float *)d_initial_state->data : nullptr;
+    c.dq = (float *)dq->data; c.dq_st = dq->stride[0]; c.dq_sh = dq->stride[1];
+    c.dk = (float *)dk->data; c.dk_st = dk->stride[0]; c.dk_sh = dk->stride[1];
+    c.dv = (float *)dv->data; c.dv_st = dv->stride[0]; c.dv_sh = dv->stride[1];
+    c.dg = (float *)dg_log->data; c.dg_st = dg_log->stride[0]; c.dg_sh = dg_log->stride[1];
+    c.dbeta = (float *)dbeta->data; c.db_st = dbeta->stride[0]; c.db_sh = dbeta->stride[1];
+    if ((e = gdp::launch_bwd_chunked(c, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDP_EHIP, "chunked backward launch: %s", hipGetErrorString(e));
+    return bwd_finish(q, k, dq, dk, dv, cu_seqlens, T, N, n, Hqk, Hk, Hv, K, V, idt, use_qk_l2norm, stream);
+  }
   // the rows' L2-norm factors (or a single 1 read with zero strides)
   float *rq = (float *)(ws + L.rn), *rk = (float *)(ws + L.rn + align256((size_t)T * Hqk * 4));
   float *one = (float *)(ws + L.fwd - 256);
-  const int idt = dt == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32;
   if (use_qk_l2norm) {
     gdp::NormGradArgs ra;
     ra.x = q->data; ra.x_st = q->stride[0]; ra.x_sh = q->stride[1];
@@ -847,28 +937,7 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
   a.ds0 = present(d_initial_state) ? (float *)d_initial_state->data : nullptr;
   if ((e = gdp::launch_backward(a, idt, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
     return fail(GDP_EHIP, "backward launch: %s", hipGetErrorString(e));
-  {  // the rows of dv no sequence covers (before cu[0] or from cu[N] on) are zero
-    gdp::ZeroOutsideArgs z;
-    z.p = (float *)dv->data; z.st = dv->stride[0]; z.sh = dv->stride[1];
-    z.cu = cu_seqlens->data; z.cu_is64 = cu_seqlens->dtype == GDP_I64;
-    z.T = T; z.N = (int)N; z.n = n; z.heads = (int)Hv; z.D = (int)V;
-    if ((e = gdp::launch_zero_outside(z, (hipStream_t)stream)) != hipSuccess)
-      return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
-  }
-  if (use_qk_l2norm) {
-    gdp::NormGradArgs na;
-    na.x = q->data; na.x_st = q->stride[0]; na.x_sh = q->stride[1];
-    na.g = (float *)dq->data; na.g_st = dq->stride[0]; na.g_sh = dq->stride[1];
-    na.rows = T * Hqk; na.heads = (int)Hqk;
-    if ((e = gdp::launch_l2norm_grad(na, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
-      return fail(GDP_EHIP, "norm gradient launch: %s", hipGetErrorString(e));
-    na.x = k->data; na.x_st = k->stride[0]; na.x_sh = k->stride[1];
-    na.g = (float *)dk->data; na.g_st = dk->stride[0]; na.g_sh = dk->stride[1];
-    na.rows = T * n * Hk; na.heads = (int)Hk;
-    if ((e = gdp::launch_l2norm_grad(na, idt, (int)K, (hipStream_t)stream)) != hipSuccess)
-      return fail(GDP_EHIP, "norm gradient launch: %s", hipGetErrorString(e));
-  }
-  return GDP_OK;
+  return bwd_finish(q, k, dq, dk, dv, cu_seqlens, T, N, n, Hqk, Hk, Hv, K, V, idt, use_qk_l2norm, stream);
 }
 
 int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *v, const gdp_tensor *g_log,

@@ -172,6 +172,42 @@ struct BwdArgs {
   float *ds0;                               // [N, Hv, K, V] or null
 };
 bool backward_supported(int K, int V, int n);
+
+// Chunked gradients on the matrix cores (gdp_bwd_chunk.hip): prep, reverse
+// state-gradient scan and per-chunk gradient kernels.  bf16 inputs; q, k, v and
+// d_o rows 16-byte aligned.
+struct BwdChunkArgs {
+  const void *q; int64_t q_st, q_sh;        // [T, Hqk, K]
+  const void *k; int64_t k_st, k_sh;        // [T*n, Hk, K]
+  const void *v; int64_t v_st, v_sh;        // [T*n, Hv, V]
+  const float *g; int64_t g_st, g_sh;       // [T, Hv] log decays
+  const float *beta; int64_t b_st, b_sh;    // [T*n, Hv]
+  const void *cu; int cu_is64;
+  int64_t T;
+  int N, n, Hqk, Hv, Hk;
+  float scale;
+  int l2norm;
+  const int32_t *chunk_indices_dp;          // [ntdp_rows, 2]
+  const int32_t *chunk_offsets_dp;          // [N+1]
+  int64_t ntdp_rows;
+  char *bundle;                             // [ntdp_rows, Hv] x bwd_bundle_bytes(n): prep output
+  const float *s0;                          // [N, Hv, K, V] initial states or null
+  float *states;                            // [ntdp_rows, Hv, K, V] state entering each expanded chunk
+  float *dstates;                           // [ntdp_rows, Hv, K, V] dL/d(state leaving each expanded chunk)
+  const void *dout; int64_t do_st, do_sh;   // [T, Hv, V]
+  const float *dfinal;                      // [N, Hv, K, V] or null
+  float *ds0;                               // [N, Hv, K, V] or null
+  // outputs (float32): dq and dk accumulate into zeroed buffers (the gradients by
+  // the normalised rows when the in-kernel norm is on); dv, dg, dbeta are stored
+  float *dq; int64_t dq_st, dq_sh;
+  float *dk; int64_t dk_st, dk_sh;
+  float *dv; int64_t dv_st, dv_sh;
+  float *dg; int64_t dg_st, dg_sh;
+  float *dbeta; int64_t db_st, db_sh;
+};
+size_t bwd_bundle_bytes(int n);
+bool bwd_chunked_supported(int dtype, int K, int V, int n);
+hipError_t launch_bwd_chunked(const BwdChunkArgs &a, int K, int V, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_t stream);
 
 // Zero fill of the rows of a strided [T*n, heads, D] float32 tensor that lie
