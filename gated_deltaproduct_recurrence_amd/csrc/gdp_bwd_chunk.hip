@@ -61,6 +61,7 @@ namespace gdp {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int LDT = 72;  // row of a 64-wide bf16 plane (elements)
 constexpr int LDF = 68;  // row of a 64-wide fp32 LDS tile (elements)
@@ -190,14 +191,6 @@ __device__ __forceinline__ bf16x8 hi_acc(f32x4 a0, f32x4 a1) {
   }
   return h;
 }
-// hi (and lo) bf16 of 8 consecutive fp32 values in global memory
-__device__ __forceinline__ void split_g8(bf16x8 &hi, bf16x8 &lo, const float *p) {
-  const f32x4 x = *(const f32x4 *)p, y = *(const f32x4 *)(p + 4);
-  split_acc(hi, lo, x, y);
-}
-__device__ __forceinline__ bf16x8 hi_g8(const float *p) {
-  return hi_acc(*(const f32x4 *)p, *(const f32x4 *)(p + 4));
-}
 __device__ __forceinline__ uint2 pack4(f32x4 x) {
   bf16x4 h = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
   return __builtin_bit_cast(uint2, h);
@@ -222,21 +215,54 @@ __device__ __forceinline__ float col_sum4(float x) {
   return x;
 }
 
-// rows [0, rows) of D bf16 columns (row stride rs elements) into LDS rows of
-// LD; rows >= nvalid are zero
-template <int NTH, int D, int LD>
-__device__ __forceinline__ void stage_rows(bf16 *dst, const bf16 *src, int64_t rs, int rows, int nvalid, int tid) {
-  constexpr int SEG = D / 8;
-  for (int u = tid; u < rows * SEG; u += NTH) {
-    const int r = u / SEG, s = u % SEG;
-    uint4 x = {0u, 0u, 0u, 0u};
-    if (r < nvalid) x = *(const uint4 *)(src + (int64_t)r * rs + 8 * s);
-    *(uint4 *)(dst + r * LD + 8 * s) = x;
+// A row-major tile of ROWS rows of D bf16 columns (row stride rs elements) in
+// 16-byte pieces, thread tid holding pieces tid + j NTH between their global
+// loads and their LDS stores.  The loads are unconditional -- a piece of a row
+// past the valid ones reads the last valid row, and the store writes zeros
+// there -- so that issuing them never waits.
+template <int ROWS, int D, int NTH> struct TileRegs {
+  static constexpr int SEG = D / 8, N = ROWS * SEG, J = (N + NTH - 1) / NTH;
+  u32x4 x[J];
+  __device__ __forceinline__ void load(const bf16 *src, int64_t rs, int nvalid, int tid) {
+    const int last = nvalid > 0 ? nvalid - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int u = (N % NTH == 0 || tid + j * NTH < N) ? tid + j * NTH : N - 1;
+      const int r = u / SEG, s = u % SEG;
+      x[j] = *(const u32x4 *)(src + (int64_t)(r < last ? r : last) * rs + 8 * s);
+    }
   }
-}
-template <int NTH, int BYTES> __device__ __forceinline__ void stage_block(char *dst, const char *src, int tid) {
-  for (int u = tid; u < BYTES / 16; u += NTH) *(uint4 *)(dst + 16 * u) = *(const uint4 *)(src + 16 * u);
-}
+  template <int LD> __device__ __forceinline__ void store(bf16 *dst, int nvalid, int tid) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int u = tid + j * NTH;
+      if (N % NTH == 0 || u < N) {
+        const int r = u / SEG, s = u % SEG;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *(u32x4 *)(dst + r * LD + 8 * s) = r < nvalid ? x[j] : z;
+      }
+    }
+  }
+};
+// a contiguous block of BYTES bytes, the same way
+template <int BYTES, int NTH> struct BlockRegs {
+  static constexpr int N = BYTES / 16, J = (N + NTH - 1) / NTH;
+  u32x4 x[J];
+  __device__ __forceinline__ void load(const char *src, int tid) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int u = (N % NTH == 0 || tid + j * NTH < N) ? tid + j * NTH : N - 1;
+      x[j] = *(const u32x4 *)(src + 16 * u);
+    }
+  }
+  __device__ __forceinline__ void store(char *dst, int tid) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int u = tid + j * NTH;
+      if (N % NTH == 0 || u < N) *(u32x4 *)(dst + 16 * u) = x[j];
+    }
+  }
+};
 // 1/sqrt(sum x^2 + 1e-6) of `rows` LDS rows of width D; 4 threads per row
 template <int D>
 __device__ __forceinline__ void rows_rsq(const bf16 *base, int ld, int rows, float *out, int tid, int nth) {
@@ -258,12 +284,16 @@ __device__ __forceinline__ void rows_rsq(const bf16 *base, int ld, int rows, flo
 
 template <int K, int TCM> struct PrepSmem {
   static constexpr int LDK = K + 8;
-  bf16 k[CH * LDK];
-  bf16 q[TCM * LDK];
-  float gram[CH * LDF];  // raw k_r.k_i
-  float qk[TCM * LDF];   // raw q_t.k_i
-  float a[CH * LDF];     // A = diag(beta) Abar
-  float tf[CH * LDF];    // T
+  union {
+    struct {
+      bf16 k[CH * LDK];
+      bf16 q[TCM * LDK];
+    } rows;  // raw k and q rows, until the Gram and q.k tiles are in registers
+    struct {
+      float a[CH * LDF];   // A = diag(beta) Abar
+      float tf[CH * LDF];  // T
+    } wy;                  // per state head
+  } u;
   float rk[CH], rq[TCM], g2[CH], beta[CH];
 };
 
@@ -271,7 +301,7 @@ template <int K, int TCM>
 __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
   using S = PrepSmem<K, TCM>;
   using B = Bundle<TCM>;
-  constexpr int LDK = S::LDK, KS = K / 32, LDP = B::LDP;
+  constexpr int LDK = S::LDK, KS = K / 32, LDP = B::LDP, NQT = 4 * (TCM / 16), QPW = NQT / 4;
   __shared__ __attribute__((aligned(16))) S sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int64_t p = blockIdx.x / a.Hk;
@@ -281,39 +311,50 @@ __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
   if (!row_geo(a, p, g, seq)) return;
   const int n = a.n, grp = a.Hv / a.Hk;
   const int hq = (hk * grp) / (a.Hv / a.Hqk);  // the q head of every state head of the group
-  stage_rows<NTHR, K, LDK>(sm.k, (const bf16 *)a.k + hk * a.k_sh + (g.t0 * n + g.row0) * a.k_st, a.k_st, CH, g.R, tid);
-  stage_rows<NTHR, K, LDK>(sm.q, (const bf16 *)a.q + hq * a.q_sh + (g.t0 + g.tlo) * a.q_st, a.q_st, TCM, g.Tc, tid);
+  {
+    TileRegs<CH, K, NTHR> kr;
+    TileRegs<TCM, K, NTHR> qr;
+    kr.load((const bf16 *)a.k + hk * a.k_sh + (g.t0 * n + g.row0) * a.k_st, a.k_st, g.R, tid);
+    qr.load((const bf16 *)a.q + hq * a.q_sh + (g.t0 + g.tlo) * a.q_st, a.q_st, g.Tc, tid);
+    kr.template store<LDK>(sm.u.rows.k, g.R, tid);
+    qr.template store<LDK>(sm.u.rows.q, g.Tc, tid);
+  }
   __syncthreads();
   if (a.l2norm) {
-    rows_rsq<K>(sm.k, LDK, CH, sm.rk, tid, NTHR);
-    rows_rsq<K>(sm.q, LDK, TCM, sm.rq, tid, NTHR);
+    rows_rsq<K>(sm.u.rows.k, LDK, CH, sm.rk, tid, NTHR);
+    rows_rsq<K>(sm.u.rows.q, LDK, TCM, sm.rq, tid, NTHR);
   } else {
     if (tid < CH) sm.rk[tid] = 1.f;
     if (tid < TCM) sm.rq[tid] = 1.f;
   }
-  // Gram and q.k tiles of the raw rows
-  for (int idx = w; idx < 16; idx += 4) {
-    const int ra = idx >> 2, rb = idx & 3;
-    f32x4 acc = zero4();
+  // Gram tiles (the 10 lower 16 x 16 tiles, wave w holding tiles w, w + 4, w + 8)
+  // and q.k tiles of the raw rows, kept in registers for every state head
+  f32x4 gram[3], qk[QPW];
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const int idx = w + 4 * it;
+    gram[it] = zero4();
+    if (idx < 10) {
+      const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3)), rb = idx - ra * (ra + 1) / 2;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        gram[it] = mma(ld_contig(sm.u.rows.k, LDK, 16 * ra + lr, 32 * s, lg),
+                       ld_contig(sm.u.rows.k, LDK, 16 * rb + lr, 32 * s, lg), gram[it]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < QPW; ++it) {
+    const int idx = w + 4 * it, ta = idx >> 2, ib = idx & 3;
+    qk[it] = zero4();
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      acc = mma(ld_contig(sm.k, LDK, 16 * ra + lr, 32 * s, lg), ld_contig(sm.k, LDK, 16 * rb + lr, 32 * s, lg), acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.gram[(16 * ra + 4 * lg + i) * LDF + 16 * rb + lr] = acc[i];
+      qk[it] = mma(ld_contig(sm.u.rows.q, LDK, 16 * ta + lr, 32 * s, lg),
+                   ld_contig(sm.u.rows.k, LDK, 16 * ib + lr, 32 * s, lg), qk[it]);
   }
-  for (int idx = w; idx < 4 * (TCM / 16); idx += 4) {
-    const int ta = idx >> 2, ib = idx & 3;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      acc = mma(ld_contig(sm.q, LDK, 16 * ta + lr, 32 * s, lg), ld_contig(sm.k, LDK, 16 * ib + lr, 32 * s, lg), acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.qk[(16 * ta + 4 * lg + i) * LDF + 16 * ib + lr] = acc[i];
-  }
-  __syncthreads();
   const float scale = a.scale;
   for (int hh = 0; hh < grp; ++hh) {
     const int h = hk * grp + hh;
+    __syncthreads();  // the rows (first head) or the previous head's T, g2, beta are no longer read
     if (w == 0) {
       const int r = lane;
       float gl = 0.f, bt = 0.f;
@@ -331,15 +372,24 @@ __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
       sm.beta[r] = bt;
     }
     __syncthreads();
-    for (int idx = tid; idx < CH * CH; idx += NTHR) {
-      const int r = idx >> 6, i = idx & 63;
-      float x = 0.f;
-      if (i < r && r < g.R)
-        x = sm.beta[r] * exp2f(sm.g2[r] - sm.g2[i]) * sm.rk[r] * sm.rk[i] * sm.gram[r * LDF + i];
-      sm.a[r * LDF + i] = x;
+    // A (the strictly lower part of the lower tiles; wy_inverse reads nothing else)
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const int idx = w + 4 * it;
+      if (idx < 10) {
+        const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3)), rb = idx - ra * (ra + 1) / 2;
+        const int i = 16 * rb + lr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * ra + 4 * lg + j;
+          sm.u.wy.a[r * LDF + i] = (i < r && r < g.R)
+                                       ? sm.beta[r] * exp2f(sm.g2[r] - sm.g2[i]) * sm.rk[r] * sm.rk[i] * gram[it][j]
+                                       : 0.f;
+        }
+      }
     }
     __syncthreads();
-    wy_inverse<LDF>(sm.a, sm.tf, tid);
+    wy_inverse<LDF>(sm.u.wy.a, sm.u.wy.tf, tid);
     char *out = a.bundle + ((size_t)p * a.Hv + h) * B::BYTES;
     // T^T planes: row i, columns r (8 per thread and step)
     for (int u = tid; u < CH * (LDT / 8); u += NTHR) {
@@ -347,28 +397,30 @@ __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
       bf16x8 hi, lo;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = (r0 + j < CH) ? sm.tf[(r0 + j) * LDF + i] : 0.f;
+        const float x = (r0 + j < CH) ? sm.u.wy.tf[(r0 + j) * LDF + i] : 0.f;
         hi[j] = (bf16)x;
         lo[j] = (bf16)(x - (float)hi[j]);
       }
       *(bf16x8 *)(out + B::TTH + 2 * (i * LDT + r0)) = hi;
       *(bf16x8 *)(out + B::TTL + 2 * (i * LDT + r0)) = lo;
     }
-    // P~^T: row i, token slots t
-    for (int u = tid; u < CH * (LDP / 8); u += NTHR) {
-      const int i = u / (LDP / 8), t0 = 8 * (u % (LDP / 8));
-      bf16x8 x;
+    // P~^T (row i, token slots t) from the q.k tiles: lane holds 4 consecutive slots of one row i
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = t0 + j;
+    for (int it = 0; it < QPW; ++it) {
+      const int idx = w + 4 * it, ta = idx >> 2, ib = idx & 3;
+      const int i = 16 * ib + lr;
+      bf16x4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * ta + 4 * lg + j;
         float y = 0.f;
         if (t < g.Tc && i < g.R) {
           const int rt = (g.tlo + t) * n + n - 1 - g.row0;
-          if (i <= rt) y = scale * sm.rq[t] * sm.rk[i] * exp2f(sm.g2[rt] - sm.g2[i]) * sm.qk[t * LDF + i];
+          if (i <= rt) y = scale * sm.rq[t] * sm.rk[i] * exp2f(sm.g2[rt] - sm.g2[i]) * qk[it][j];
         }
         x[j] = (bf16)y;
       }
-      *(bf16x8 *)(out + B::PTB + 2 * (i * LDP + t0)) = x;
+      *(bf16x4 *)(out + B::PTB + 2 * (i * LDP + 16 * ta + 4 * lg)) = x;
     }
     // factor rows
     float *fac = (float *)(out + B::FAC);
@@ -390,7 +442,6 @@ __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
       fac[F_E * CH + t] = tin ? ep * sm.rq[t < TCM ? t : 0] : 0.f;
       fac[F_RQ * CH + t] = tin ? sm.rq[t < TCM ? t : 0] : 0.f;
     }
-    __syncthreads();  // before the next head reuses sm.a, sm.tf, sm.g2
   }
 }
 
@@ -403,51 +454,23 @@ template <int K, int V, int TCM> struct FwdSmem {
   char bundle[Bundle<TCM>::BYTES];
 };
 
-// the next chunk's k and v rows and bundle, held in registers between their
-// global loads and their LDS stores
+// the next chunk's k and v rows and bundle, in registers between their loads
+// and their LDS stores
 template <int K, int V, int TCM, int NTH> struct FwdStage {
-  static constexpr int KSEG = CH * K / 8, VSEG = CH * V / 8, BSEG = Bundle<TCM>::BYTES / 16;
-  static constexpr int NK = (KSEG + NTH - 1) / NTH, NV = (VSEG + NTH - 1) / NTH, NB = (BSEG + NTH - 1) / NTH;
-  uint4 k[NK], v[NV], b[NB];
-
+  TileRegs<CH, K, NTH> k;
+  TileRegs<CH, V, NTH> v;
+  BlockRegs<Bundle<TCM>::BYTES, NTH> b;
+  int R;
   __device__ __forceinline__ void load(const BwdChunkArgs &a, const Geo &g, int64_t p, int h, int hk, int tid) {
-    const bf16 *kb = (const bf16 *)a.k + hk * a.k_sh + (g.t0 * a.n + g.row0) * a.k_st;
-    const bf16 *vb = (const bf16 *)a.v + h * a.v_sh + (g.t0 * a.n + g.row0) * a.v_st;
-    const char *bb = a.bundle + ((size_t)p * a.Hv + h) * Bundle<TCM>::BYTES;
-    const uint4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int u = tid + j * NTH, r = u / (K / 8), s = u % (K / 8);
-      k[j] = (u < KSEG && r < g.R) ? *(const uint4 *)(kb + (int64_t)r * a.k_st + 8 * s) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int u = tid + j * NTH, r = u / (V / 8), s = u % (V / 8);
-      v[j] = (u < VSEG && r < g.R) ? *(const uint4 *)(vb + (int64_t)r * a.v_st + 8 * s) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int u = tid + j * NTH;
-      b[j] = u < BSEG ? *(const uint4 *)(bb + 16 * u) : z;
-    }
+    R = g.R;
+    k.load((const bf16 *)a.k + hk * a.k_sh + (g.t0 * a.n + g.row0) * a.k_st, a.k_st, g.R, tid);
+    v.load((const bf16 *)a.v + h * a.v_sh + (g.t0 * a.n + g.row0) * a.v_st, a.v_st, g.R, tid);
+    b.load(a.bundle + ((size_t)p * a.Hv + h) * Bundle<TCM>::BYTES, tid);
   }
   __device__ __forceinline__ void commit(FwdSmem<K, V, TCM> &sm, int tid) const {
-    constexpr int LDK = FwdSmem<K, V, TCM>::LDK, LDV = FwdSmem<K, V, TCM>::LDV;
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int u = tid + j * NTH;
-      if (u < KSEG) *(uint4 *)(sm.k + (u / (K / 8)) * LDK + 8 * (u % (K / 8))) = k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int u = tid + j * NTH;
-      if (u < VSEG) *(uint4 *)(sm.v + (u / (V / 8)) * LDV + 8 * (u % (V / 8))) = v[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int u = tid + j * NTH;
-      if (u < BSEG) *(uint4 *)(sm.bundle + 16 * u) = b[j];
-    }
+    k.template store<FwdSmem<K, V, TCM>::LDK>(sm.k, R, tid);
+    v.template store<FwdSmem<K, V, TCM>::LDV>(sm.v, R, tid);
+    b.store(sm.bundle, tid);
   }
 };
 
@@ -579,63 +602,27 @@ template <int K, int V, int TCM> struct AdjSmem {
   char bundle[Bundle<TCM>::BYTES];
 };
 
-// the next chunk's k, q, dO rows and bundle, held in registers between their
-// global loads and their LDS stores
+// the next chunk's k, q, dO rows and bundle, in registers between their loads
+// and their LDS stores
 template <int K, int V, int TCM, int NTH> struct AdjStage {
-  static constexpr int KSEG = CH * K / 8, QSEG = TCM * K / 8, OSEG = TCM * V / 8, BSEG = Bundle<TCM>::BYTES / 16;
-  static constexpr int NK = (KSEG + NTH - 1) / NTH, NQ = (QSEG + NTH - 1) / NTH, NO = (OSEG + NTH - 1) / NTH,
-                       NB = (BSEG + NTH - 1) / NTH;
-  uint4 k[NK], q[NQ], o[NO], b[NB];
-
+  TileRegs<CH, K, NTH> k;
+  TileRegs<TCM, K, NTH> q;
+  TileRegs<TCM, V, NTH> o;
+  BlockRegs<Bundle<TCM>::BYTES, NTH> b;
+  int R, Tc;
   __device__ __forceinline__ void load(const BwdChunkArgs &a, const Geo &g, int64_t p, int h, int hk, int hq, int tid) {
-    const bf16 *kb = (const bf16 *)a.k + hk * a.k_sh + (g.t0 * a.n + g.row0) * a.k_st;
-    const bf16 *qb = (const bf16 *)a.q + hq * a.q_sh + (g.t0 + g.tlo) * a.q_st;
-    const bf16 *ob = (const bf16 *)a.dout + h * a.do_sh + (g.t0 + g.tlo) * a.do_st;
-    const char *bb = a.bundle + ((size_t)p * a.Hv + h) * Bundle<TCM>::BYTES;
-    const uint4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int u = tid + j * NTH, r = u / (K / 8), s = u % (K / 8);
-      k[j] = (u < KSEG && r < g.R) ? *(const uint4 *)(kb + (int64_t)r * a.k_st + 8 * s) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int u = tid + j * NTH, r = u / (K / 8), s = u % (K / 8);
-      q[j] = (u < QSEG && r < g.Tc) ? *(const uint4 *)(qb + (int64_t)r * a.q_st + 8 * s) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < NO; ++j) {
-      const int u = tid + j * NTH, r = u / (V / 8), s = u % (V / 8);
-      o[j] = (u < OSEG && r < g.Tc) ? *(const uint4 *)(ob + (int64_t)r * a.do_st + 8 * s) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int u = tid + j * NTH;
-      b[j] = u < BSEG ? *(const uint4 *)(bb + 16 * u) : z;
-    }
+    R = g.R;
+    Tc = g.Tc;
+    k.load((const bf16 *)a.k + hk * a.k_sh + (g.t0 * a.n + g.row0) * a.k_st, a.k_st, g.R, tid);
+    q.load((const bf16 *)a.q + hq * a.q_sh + (g.t0 + g.tlo) * a.q_st, a.q_st, g.Tc, tid);
+    o.load((const bf16 *)a.dout + h * a.do_sh + (g.t0 + g.tlo) * a.do_st, a.do_st, g.Tc, tid);
+    b.load(a.bundle + ((size_t)p * a.Hv + h) * Bundle<TCM>::BYTES, tid);
   }
   __device__ __forceinline__ void commit(AdjSmem<K, V, TCM> &sm, int tid) const {
-    constexpr int LDK = AdjSmem<K, V, TCM>::LDK, LDO = AdjSmem<K, V, TCM>::LDO;
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int u = tid + j * NTH;
-      if (u < KSEG) *(uint4 *)(sm.k + (u / (K / 8)) * LDK + 8 * (u % (K / 8))) = k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int u = tid + j * NTH;
-      if (u < QSEG) *(uint4 *)(sm.q + (u / (K / 8)) * LDK + 8 * (u % (K / 8))) = q[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NO; ++j) {
-      const int u = tid + j * NTH;
-      if (u < OSEG) *(uint4 *)(sm.o + (u / (V / 8)) * LDO + 8 * (u % (V / 8))) = o[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int u = tid + j * NTH;
-      if (u < BSEG) *(uint4 *)(sm.bundle + 16 * u) = b[j];
-    }
+    k.template store<AdjSmem<K, V, TCM>::LDK>(sm.k, R, tid);
+    q.template store<AdjSmem<K, V, TCM>::LDK>(sm.q, Tc, tid);
+    o.template store<AdjSmem<K, V, TCM>::LDO>(sm.o, Tc, tid);
+    b.store(sm.bundle, tid);
   }
 };
 
@@ -834,25 +821,38 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV;
 
   // S0 and D slabs of the wave's 16 columns, and v, in accumulator layout
+  // loads in the order they are needed: the staged rows and bundle, then the
+  // S0, D and v slabs, which stay in flight while the rows go to LDS
   f32x4 Sa[KT], Da[KT], Va[4];
+  {
+    TileRegs<CH, K, NTH> kr;
+    TileRegs<TCM, K, NTH> qr;
+    TileRegs<TCM, V, NTH> orr;
+    BlockRegs<B::BYTES, NTH> br;
+    kr.load((const bf16 *)a.k + hk * a.k_sh + krow0 * a.k_st, a.k_st, g.R, tid);
+    qr.load((const bf16 *)a.q + hq * a.q_sh + qrow0 * a.q_st, a.q_st, g.Tc, tid);
+    orr.load((const bf16 *)a.dout + h * a.do_sh + qrow0 * a.do_st, a.do_st, g.Tc, tid);
+    br.load(a.bundle + ((size_t)p * a.Hv + h) * B::BYTES, tid);
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Sa[kt][i] = S0g[(size_t)(16 * kt + 4 * lg + i) * V + col];
-      Da[kt][i] = Dg[(size_t)(16 * kt + 4 * lg + i) * V + col];
-    }
+      for (int i = 0; i < 4; ++i) {
+        Sa[kt][i] = S0g[(size_t)(16 * kt + 4 * lg + i) * V + col];
+        Da[kt][i] = Dg[(size_t)(16 * kt + 4 * lg + i) * V + col];
+      }
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * lg + i;
-      Va[rt][i] = r < g.R ? (float)((const bf16 *)a.v)[(krow0 + r) * a.v_st + h * a.v_sh + col] : 0.f;
-    }
-  stage_rows<NTH, K, LDK>(sk, (const bf16 *)a.k + hk * a.k_sh + krow0 * a.k_st, a.k_st, CH, g.R, tid);
-  stage_rows<NTH, K, LDK>(sq, (const bf16 *)a.q + hq * a.q_sh + qrow0 * a.q_st, a.q_st, TCM, g.Tc, tid);
-  stage_rows<NTH, V, LDO>(so, (const bf16 *)a.dout + h * a.do_sh + qrow0 * a.do_st, a.do_st, TCM, g.Tc, tid);
-  stage_block<NTH, B::BYTES>(smem + L::BU, a.bundle + ((size_t)p * a.Hv + h) * B::BYTES, tid);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        const float x = (float)((const bf16 *)a.v)[(krow0 + (r < g.R ? r : g.R - 1)) * a.v_st + h * a.v_sh + col];
+        Va[rt][i] = r < g.R ? x : 0.f;
+      }
+    kr.template store<LDK>(sk, g.R, tid);
+    qr.template store<LDK>(sq, g.Tc, tid);
+    orr.template store<LDO>(so, g.Tc, tid);
+    br.store(smem + L::BU, tid);
+  }
   for (int u = tid; u < NRED * CH; u += NTH) red[u] = 0.f;
   __syncthreads();
 
@@ -905,6 +905,23 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
         X[rt] = mma(kf, Dh[s], X[rt]);
         X[rt] = mma(kf, Dl[s], X[rt]);
       }
+    }
+  }
+  // the S0 and D rows of this wave's k tiles (for the products reducing over V),
+  // loaded now so that they arrive while E and dU are formed
+  constexpr int NKW = (KT + NW - 1) / NW;
+  f32x4 Ks[NKW][VS][2], Kd[NKW][VS][2];
+#pragma unroll
+  for (int m = 0; m < NKW; ++m) {
+    const int kt = (w + m * NW) < KT ? w + m * NW : KT - 1;
+    const int kc = 16 * kt + lr;
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      const float *ps = S0g + (size_t)kc * V + 32 * s + 8 * lg, *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
+      Ks[m][s][0] = *(const f32x4 *)ps;
+      Ks[m][s][1] = *(const f32x4 *)(ps + 4);
+      Kd[m][s][0] = *(const f32x4 *)pd;
+      Kd[m][s][1] = *(const f32x4 *)(pd + 4);
     }
   }
   // U = V - Gamma rk W, Ut = beta U;  E = T Ut (both split)
@@ -1070,7 +1087,6 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
     }
   }
   // dK1 = dU S0^T (hi), dK2 = E D^T (split), dQ1 = dO S0^T (hi) on the wave's k tiles
-  constexpr int NKW = (KT + NW - 1) / NW;
   f32x4 dK[NKW][4], dQ[NKW][TT16];
 #pragma unroll
   for (int m = 0; m < NKW; ++m) {
@@ -1084,9 +1100,9 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
     for (int ta = 0; ta < TT16; ++ta) dQ[m][ta] = zero4();
 #pragma unroll
     for (int s = 0; s < VS; ++s) {
-      const bf16x8 sh = hi_g8(S0g + (size_t)kc * V + 32 * s + 8 * lg);
+      const bf16x8 sh = hi_acc(Ks[m][s][0], Ks[m][s][1]);
       bf16x8 dh, dl;
-      split_g8(dh, dl, Dg + (size_t)kc * V + 32 * s + 8 * lg);
+      split_acc(dh, dl, Kd[m][s][0], Kd[m][s][1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         k1[rt] = mma(tr_contig(puh, LDT, 32 * s, 16 * rt, lr, lg), sh, k1[rt]);
