@@ -723,9 +723,10 @@ static bool env_backward_recurrent() {
 }
 }  // namespace
 
-// The backward's last steps on both paths: zero rows of dv outside every
-// sequence, and (with the in-kernel norm) the gradients by the raw q and k rows
-// from those by their normalised rows.
+// The backward's last steps: zero rows of dv outside every sequence, and (with
+// the in-kernel norm, on the recurrent path; the chunked gradient kernel applies
+// it itself) the gradients by the raw q and k rows from those by their
+// normalised rows.
 static int bwd_finish(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *dq, const gdp_tensor *dk,
                       const gdp_tensor *dv, const gdp_tensor *cu_seqlens, int64_t T, int64_t N, int32_t n, int64_t Hqk,
                       int64_t Hk, int64_t Hv, int64_t K, int64_t V, int idt, int32_t use_qk_l2norm, void *stream) {
@@ -890,7 +891,7 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
     c.dbeta = (float *)dbeta->data; c.db_st = dbeta->stride[0]; c.db_sh = dbeta->stride[1];
     if ((e = gdp::launch_bwd_chunked(c, (int)K, (int)V, (hipStream_t)stream)) != hipSuccess)
       return fail(GDP_EHIP, "chunked backward launch: %s", hipGetErrorString(e));
-    return bwd_finish(q, k, dq, dk, dv, cu_seqlens, T, N, n, Hqk, Hk, Hv, K, V, idt, use_qk_l2norm, stream);
+    return bwd_finish(q, k, dq, dk, dv, cu_seqlens, T, N, n, Hqk, Hk, Hv, K, V, idt, 0, stream);
   }
   // the rows' L2-norm factors (or a single 1 read with zero strides)
   float *rq = (float *)(ws + L.rn), *rk = (float *)(ws + L.rn + align256((size_t)T * Hqk * 4));

@@ -215,6 +215,43 @@ __device__ __forceinline__ float col_sum4(float x) {
   return x;
 }
 
+// Sums over the 16 lanes of each 16-lane row of the 16 values x[4 rt + i]
+// (rows 16 rt + 4 lg + i of an accumulator layout): a reduce-scatter over lane
+// bits 3, 2, 1, 0 that leaves lane (lg, lr) with the sum for row
+// 16 (lr >> 2) + 4 lg + (lr & 3)  (x index lr).
+__device__ __forceinline__ float rowsum_scatter(float (&x)[16], int lr) {
+  float y8[8];
+  {
+    const bool hi = lr & 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float keep = hi ? x[k + 8] : x[k], send = hi ? x[k] : x[k + 8];
+      y8[k] = keep + __shfl_xor(send, 8, 64);
+    }
+  }
+  float y4[4];
+  {
+    const bool hi = lr & 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float keep = hi ? y8[k + 4] : y8[k], send = hi ? y8[k] : y8[k + 4];
+      y4[k] = keep + __shfl_xor(send, 4, 64);
+    }
+  }
+  float y2[2];
+  {
+    const bool hi = lr & 2;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float keep = hi ? y4[k + 2] : y4[k], send = hi ? y4[k] : y4[k + 2];
+      y2[k] = keep + __shfl_xor(send, 2, 64);
+    }
+  }
+  const bool hi = lr & 1;
+  const float keep = hi ? y2[1] : y2[0], send = hi ? y2[0] : y2[1];
+  return keep + __shfl_xor(send, 1, 64);
+}
+
 // A row-major tile of ROWS rows of D bf16 columns (row stride rs elements) in
 // 16-byte pieces, thread tid holding pieces tid + j NTH between their global
 // loads and their LDS stores.  The loads are unconditional -- a piece of a row
@@ -763,40 +800,101 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_adjoint_kernel(BwdChunkArgs 
 
 // ---------------------------------------------------------------- gradient kernel
 
-// row partial sums of the gradient kernel
-enum Red { R_DB = 0, R_DL, R_XE, R_DS, NRED };
+// Store the rows [0, nvalid) of a gradient held as 16-column tiles (tile kt =
+// w + m NW of wave w, rows 16 rt + 4 lg + i in accumulator layout) by the
+// normalised rows of a raw bf16 tile x (LDS, row stride ldx) with norm factors
+// rn: with the in-kernel norm, g_raw = rn (g - xhat (xhat.g)), xhat = rn x; the
+// row dots go through `dots` (64 zeroed floats, read after a barrier).  Called
+// by every thread of the workgroup.
+template <int NKW, int NRT, int K>
+__device__ __forceinline__ void store_rows(float *out, int64_t row0, int64_t st, int64_t head_off, int nvalid,
+                                           f32x4 (&acc)[NKW][NRT], const bf16 *x, int ldx, const float *rn, float *dots,
+                                           int l2norm, int w, int NW, int lr, int lg) {
+  constexpr int KT = K / 16;
+  if (l2norm) {
+#pragma unroll
+    for (int m = 0; m < NKW; ++m) {
+      const int kt = w + m * NW;
+      if (kt >= KT) continue;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i;
+          const float d = row_sum16(acc[m][rt][i] * (float)x[r * ldx + 16 * kt + lr]);
+          if (lr == 15) atomicAdd(dots + r, d);
+        }
+    }
+    __syncthreads();
+  }
+  float *ol = out + (row0 + 4 * lg) * st + head_off + lr;
+#pragma unroll
+  for (int m = 0; m < NKW; ++m) {
+    const int kt = w + m * NW;
+    if (kt >= KT) continue;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        float y = acc[m][rt][i];
+        if (l2norm) {
+          const float f = rn[r];
+          y = f * (y - f * f * (float)x[r * ldx + 16 * kt + lr] * dots[r]);
+        }
+        if (r < nvalid) ol[(16 * rt + i) * st + 16 * kt] = y;
+      }
+  }
+}
+
+// row partial sums of the gradient kernel (per state head), and the row dots
+// of the norm gradients (per workgroup)
+enum Red { R_DB = 0, R_DL, R_XE, R_DS, R_QN, R_KN, NRED };
 
 template <int K, int V, int TCM> struct GradLds {
   using B = Bundle<TCM>;
-  static constexpr int LDK = K + 8, LDO = V + 8, LDW = TCM + 8;
+  static constexpr int LDK = K + 8, LDO = V + 8, LDV = V + 8, LDW = TCM + 8;
   static constexpr int K_ = 0;                               // bf16 [64][LDK] raw k rows
   static constexpr int Q_ = K_ + CH * LDK * 2;               // bf16 [TCM][LDK] raw q rows
   static constexpr int O_ = Q_ + TCM * LDK * 2;              // bf16 [TCM][LDO] dO rows
   static constexpr int AB = O_ + TCM * LDO * 2;              // fp32 [64][LDF] Abar, then A~
   static constexpr int RD = AB + CH * LDF * 4;               // fp32 [NRED][64]
-  static constexpr int BU = RD + NRED * CH * 4;              // the bundle
-  // planes, over the bundle's T^T planes (dead once dU is formed):
+  static constexpr int SL = RD + NRED * CH * 4;              // fp32 [3][V / 16][64]: per-wave row partials
+  static constexpr int BU = SL + 3 * (V / 16) * CH * 4;      // the bundle
+  // the rest lies over the bundle's T^T planes, which are dead once dU is formed:
   static constexpr int PL = BU + B::TTH;
+  static constexpr int VR = PL + 2 * CH * LDT * 2;           // bf16 [64][LDV] v rows (until U is formed)
   static constexpr int EH = PL, EL = EH + V * LDT * 2, UH = EL + V * LDT * 2, UL = UH + V * LDT * 2;  // E^T, dU^T [v][r]
   static constexpr int P1_END = UL + V * LDT * 2;
-  static constexpr int MH = PL, ML = MH + CH * LDT * 2;      // M' = (A~ + A~^T) diag(rk) [r][i]
-  static constexpr int W1 = ML + CH * LDT * 2;               // W~ diag(rq) transposed: [i][t]
-  static constexpr int W2 = W1 + CH * LDW * 2;               // W~^T diag(rk) ... as [i][t] with rk_i
+  static constexpr int MH = PL, ML = MH + CH * LDT * 2;      // M' = (A~ + A~^T) diag(rk), [r][i]
+  static constexpr int W1 = ML + CH * LDT * 2;               // W~ diag(rq), stored [i][t]
+  static constexpr int W2 = W1 + CH * LDW * 2;               // diag(rk) W~^T, stored [i][t]
   static constexpr int P2_END = W2 + CH * LDW * 2;
-  static constexpr int BYTES = (P1_END > P2_END ? P1_END : P2_END) > BU + B::BYTES
-                                   ? (P1_END > P2_END ? P1_END : P2_END) : BU + B::BYTES;
+  static constexpr int V_END = VR + CH * LDV * 2;
+  static constexpr int M1 = P1_END > P2_END ? P1_END : P2_END, M2 = V_END > BU + B::BYTES ? V_END : BU + B::BYTES;
+  static constexpr int BYTES = M1 > M2 ? M1 : M2;
   static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
+
+// One workgroup per (expanded chunk, q/k head): the state heads of the group in
+// turn, each wave owning 16 state columns for the products over rows and one or
+// more 16-column k tiles for the products over V.  dq (and dk when the group
+// shares its k rows) accumulate in registers over the heads and are stored
+// once, through the L2-norm gradient when the in-kernel norm is on; the next
+// head's slabs, rows and bundle are loaded while the current head finishes.
 template <int K, int V, int TCM>
 __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) {
   constexpr int NW = V / 16, NTH = 64 * NW, KT = K / 16, KS = K / 32, VS = V / 32, TS = TCM / 32, TT16 = TCM / 16;
+  constexpr int NKW = (KT + NW - 1) / NW;
   using L = GradLds<K, V, TCM>;
   using B = Bundle<TCM>;
-  constexpr int LDK = L::LDK, LDO = L::LDO, LDP = B::LDP, LDW = L::LDW;
+  constexpr int LDK = L::LDK, LDO = L::LDO, LDV = L::LDV, LDP = B::LDP, LDW = L::LDW;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   bf16 *sk = (bf16 *)(smem + L::K_), *sq = (bf16 *)(smem + L::Q_), *so = (bf16 *)(smem + L::O_);
-  float *abar = (float *)(smem + L::AB), *red = (float *)(smem + L::RD);
+  bf16 *sv = (bf16 *)(smem + L::VR);
+  float *abar = (float *)(smem + L::AB), *red = (float *)(smem + L::RD), *slots = (float *)(smem + L::SL);
   const bf16 *tth = (const bf16 *)(smem + L::BU + B::TTH), *ttl = (const bf16 *)(smem + L::BU + B::TTL);
   const bf16 *ptb = (const bf16 *)(smem + L::BU + B::PTB);
   const float *fac = (const float *)(smem + L::BU + B::FAC);
@@ -805,434 +903,478 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   bf16 *pmh = (bf16 *)(smem + L::MH), *pml = (bf16 *)(smem + L::ML), *pw1 = (bf16 *)(smem + L::W1),
        *pw2 = (bf16 *)(smem + L::W2);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const int64_t p = blockIdx.x / a.Hv;
-  const int h = (int)(blockIdx.x % a.Hv);
+  int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: w-derived offsets stay scalar
+  const int64_t p = blockIdx.x / a.Hqk;
+  const int hq = (int)(blockIdx.x % a.Hqk);
   Geo g;
   int seq;
   if (!row_geo(a, p, g, seq)) return;
-  const int n = a.n;
-  const int hk = h / (a.Hv / a.Hk), hq = h / (a.Hv / a.Hqk);
+  const int n = a.n, G = a.Hv / a.Hqk;
+  const bool kshared = a.Hk == a.Hqk;  // else one k head per state head
   const int64_t krow0 = g.t0 * n + g.row0;  // first k/v/beta row of the chunk
   const int64_t qrow0 = g.t0 + g.tlo;       // first output token
-  const int col = 16 * w + lr;
   const size_t KV = (size_t)K * V;
-  const float *S0g = a.states + ((size_t)p * a.Hv + h) * KV;
-  const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV;
+  int lane = tid & 63, lr = lane & 15, lg = lane >> 4, col = 16 * w + lr;
 
-  // S0 and D slabs of the wave's 16 columns, and v, in accumulator layout
-  // loads in the order they are needed: the staged rows and bundle, then the
-  // S0, D and v slabs, which stay in flight while the rows go to LDS
-  f32x4 Sa[KT], Da[KT], Va[4];
-  {
-    TileRegs<CH, K, NTH> kr;
-    TileRegs<TCM, K, NTH> qr;
-    TileRegs<TCM, V, NTH> orr;
-    BlockRegs<B::BYTES, NTH> br;
-    kr.load((const bf16 *)a.k + hk * a.k_sh + krow0 * a.k_st, a.k_st, g.R, tid);
-    qr.load((const bf16 *)a.q + hq * a.q_sh + qrow0 * a.q_st, a.q_st, g.Tc, tid);
+  // head-dependent operands: S0 and D slabs (this wave's 16 columns, accumulator
+  // layout) in registers; dO rows, v rows, bundle (and k rows when not shared)
+  // staged through registers into LDS
+  f32x4 Sa[KT], Da[KT];
+  TileRegs<CH, K, NTH> kr;
+  TileRegs<TCM, V, NTH> orr;
+  TileRegs<CH, V, NTH> vr;
+  BlockRegs<B::BYTES, NTH> br;
+  auto load_head = [&](int h, bool with_k) {
+    const int hk = h / (a.Hv / a.Hk);
+    if (with_k) kr.load((const bf16 *)a.k + hk * a.k_sh + krow0 * a.k_st, a.k_st, g.R, tid);
     orr.load((const bf16 *)a.dout + h * a.do_sh + qrow0 * a.do_st, a.do_st, g.Tc, tid);
     br.load(a.bundle + ((size_t)p * a.Hv + h) * B::BYTES, tid);
+    vr.load((const bf16 *)a.v + h * a.v_sh + krow0 * a.v_st, a.v_st, g.R, tid);
+    const float *S0g = a.states + ((size_t)p * a.Hv + h) * KV + (size_t)(4 * lg) * V + col;
+    const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV + (size_t)(4 * lg) * V + col;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Sa[kt][i] = S0g[(size_t)(16 * kt + 4 * lg + i) * V + col];
-        Da[kt][i] = Dg[(size_t)(16 * kt + 4 * lg + i) * V + col];
+        Sa[kt][i] = S0g[(16 * kt + i) * V];
+        Da[kt][i] = Dg[(16 * kt + i) * V];
       }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        const float x = (float)((const bf16 *)a.v)[(krow0 + (r < g.R ? r : g.R - 1)) * a.v_st + h * a.v_sh + col];
-        Va[rt][i] = r < g.R ? x : 0.f;
-      }
-    kr.template store<LDK>(sk, g.R, tid);
-    qr.template store<LDK>(sq, g.Tc, tid);
+  };
+  auto commit_head = [&](bool with_k) {
+    if (with_k) kr.template store<LDK>(sk, g.R, tid);
     orr.template store<LDO>(so, g.Tc, tid);
     br.store(smem + L::BU, tid);
-  }
-  for (int u = tid; u < NRED * CH; u += NTH) red[u] = 0.f;
-  __syncthreads();
-
-  // <D, S0>
+    vr.template store<LDV>(sv, g.R, tid);
+    for (int u = tid; u < 4 * CH; u += NTH) red[u] = 0.f;  // R_DB .. R_DS
+    if (tid < CH) red[R_KN * CH + tid] = 0.f;              // (the k-row dots when dk is stored per head)
+  };
   {
-    float x = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x += Da[kt][i] * Sa[kt][i];
-    x = row_sum16(x);
-    x = __shfl(x, 15, 16);
-    x = col_sum4(x);
-    if (lane == 0) atomicAdd(red + R_DS * CH, x);
+    TileRegs<TCM, K, NTH> qr;
+    qr.load((const bf16 *)a.q + hq * a.q_sh + qrow0 * a.q_st, a.q_st, g.Tc, tid);
+    load_head(hq * G, true);
+    qr.template store<LDK>(sq, g.Tc, tid);
+    commit_head(true);
+    if (tid < CH) red[R_QN * CH + tid] = 0.f;
   }
-  // Abar (strictly lower) from the Gram tiles of the raw rows
-  for (int idx = w; idx < 10; idx += NW) {
-    const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
-    const int rb = idx - ra * (ra + 1) / 2;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      acc = mma(ld_contig(sk, LDK, 16 * ra + lr, 32 * s, lg), ld_contig(sk, LDK, 16 * rb + lr, 32 * s, lg), acc);
-    const int i = 16 * rb + lr;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * ra + 4 * lg + j;
-      abar[r * LDF + i] = (i < r && r < g.R) ? exp2f(fac[F_G2 * CH + r] - fac[F_G2 * CH + i]) * fac[F_RK * CH + r] *
-                                                   fac[F_RK * CH + i] * acc[j]
-                                             : 0.f;
-    }
-  }
-  // W = K S0 (S0 hi), X = K D (D split)
-  f32x4 W[4], X[4];
-  {
-    bf16x8 Sh[KS], Dh[KS], Dl[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      Sh[s] = hi_acc(Sa[2 * s], Sa[2 * s + 1]);
-      split_acc(Dh[s], Dl[s], Da[2 * s], Da[2 * s + 1]);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      W[rt] = zero4();
-      X[rt] = zero4();
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = ld_perm(sk, LDK, 16 * rt + lr, 32 * s, lg);
-        W[rt] = mma(kf, Sh[s], W[rt]);
-        X[rt] = mma(kf, Dh[s], X[rt]);
-        X[rt] = mma(kf, Dl[s], X[rt]);
-      }
-    }
-  }
-  // the S0 and D rows of this wave's k tiles (for the products reducing over V),
-  // loaded now so that they arrive while E and dU are formed
-  constexpr int NKW = (KT + NW - 1) / NW;
-  f32x4 Ks[NKW][VS][2], Kd[NKW][VS][2];
+  f32x4 dK[NKW][4], dQ[NKW][TT16];
 #pragma unroll
   for (int m = 0; m < NKW; ++m) {
-    const int kt = (w + m * NW) < KT ? w + m * NW : KT - 1;
-    const int kc = 16 * kt + lr;
 #pragma unroll
-    for (int s = 0; s < VS; ++s) {
-      const float *ps = S0g + (size_t)kc * V + 32 * s + 8 * lg, *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
-      Ks[m][s][0] = *(const f32x4 *)ps;
-      Ks[m][s][1] = *(const f32x4 *)(ps + 4);
-      Kd[m][s][0] = *(const f32x4 *)pd;
-      Kd[m][s][1] = *(const f32x4 *)(pd + 4);
-    }
+    for (int rt = 0; rt < 4; ++rt) dK[m][rt] = zero4();
+#pragma unroll
+    for (int ta = 0; ta < TT16; ++ta) dQ[m][ta] = zero4();
   }
-  // U = V - Gamma rk W, Ut = beta U;  E = T Ut (both split)
-  f32x4 U[4], E[4];
-  {
-    f32x4 Ut[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        U[rt][i] = Va[rt][i] - exp2f(fac[F_G2 * CH + r]) * fac[F_RK * CH + r] * W[rt][i];
-        Ut[rt][i] = fac[F_BETA * CH + r] * U[rt][i];
-      }
-    bf16x8 Uh[2], Ul[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) split_acc(Uh[s], Ul[s], Ut[2 * s], Ut[2 * s + 1]);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      E[rt] = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = tr_perm(tth, LDT, 32 * s, 16 * rt, lr, lg), al = tr_perm(ttl, LDT, 32 * s, 16 * rt, lr, lg);
-        E[rt] = mma(ah, Uh[s], E[rt]);
-        E[rt] = mma(ah, Ul[s], E[rt]);
-        E[rt] = mma(al, Uh[s], E[rt]);
-      }
-    }
-  }
-  // xe_r = c_r X_r.E_r (this wave's columns)
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * lg + i;
-      const float x = row_sum16(X[rt][i] * E[rt][i]);
-      if (lr == 15) atomicAdd(red + R_XE * CH + r, fac[F_C * CH + r] * x);
-    }
-  // dE = c X + P~^T dO;  dU = T^T dE (both split)
-  f32x4 dU[4];
-  {
-    bf16x8 of[TS];
-#pragma unroll
-    for (int s = 0; s < TS; ++s) of[s] = tr_contig(so, LDO, 32 * s, 16 * w, lr, lg);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[rt][i] *= fac[F_C * CH + 16 * rt + 4 * lg + i];
-#pragma unroll
-      for (int s = 0; s < TS; ++s) X[rt] = mma(ld_contig(ptb, LDP, 16 * rt + lr, 32 * s, lg), of[s], X[rt]);
-    }
-    bf16x8 Eh[2], El[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) split_acc(Eh[s], El[s], X[2 * s], X[2 * s + 1]);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      dU[rt] = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = ld_perm(tth, LDT, 16 * rt + lr, 32 * s, lg), al = ld_perm(ttl, LDT, 16 * rt + lr, 32 * s, lg);
-        dU[rt] = mma(ah, Eh[s], dU[rt]);
-        dU[rt] = mma(ah, El[s], dU[rt]);
-        dU[rt] = mma(al, Eh[s], dU[rt]);
-      }
-    }
-  }
-  // dv, and the row partials dU.U (dbeta) and -Gamma beta rk dU.W (decay)
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * lg + i;
-      const float bt = fac[F_BETA * CH + r];
-      if (r < g.R) a.dv[(krow0 + r) * a.dv_st + h * a.dv_sh + col] = bt * dU[rt][i];
-      const float xb = row_sum16(dU[rt][i] * U[rt][i]);
-      const float xw = row_sum16(dU[rt][i] * W[rt][i]);
-      if (lr == 15) {
-        atomicAdd(red + R_DB * CH + r, xb);
-        atomicAdd(red + R_DL * CH + r, -exp2f(fac[F_G2 * CH + r]) * bt * fac[F_RK * CH + r] * xw);
-      }
-    }
-  __syncthreads();  // every wave is done with the T^T planes
-  // E^T and dU^T planes [v][r] (hi, lo)
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int off = col * LDT + 16 * rt + 4 * lg;
-    f32x4 eh, uh;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      eh[i] = (float)(bf16)E[rt][i];
-      uh[i] = (float)(bf16)dU[rt][i];
-    }
-    *(uint2 *)(peh + off) = pack4(eh);
-    *(uint2 *)(pel + off) = pack4(E[rt] - eh);
-    *(uint2 *)(puh + off) = pack4(uh);
-    *(uint2 *)(pul + off) = pack4(dU[rt] - uh);
-  }
-  __syncthreads();
+  const float scale = a.scale;
 
-  // ---- products reducing over V
-  // dA = -dU E^T (strictly lower tiles): dbeta and decay terms, then A~ into abar
-  for (int idx = w; idx < 10; idx += NW) {
-    const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
-    const int ib = idx - ra * (ra + 1) / 2;
-    f32x4 acc = zero4();
+#pragma unroll 1
+  for (int j = 0; j < G; ++j) {
+    const int h = hq * G + j;
+    // the lane index is made opaque every head so that the compiler forms each
+    // LDS address where it is used instead of keeping dozens of them live
+    tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    lr = lane & 15;
+    lg = lane >> 4;
+    col = 16 * w + lr;
+    const float *S0g = a.states + ((size_t)p * a.Hv + h) * KV;
+    const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV;
+    __syncthreads();  // this head's rows, bundle and zeroed partial sums are in LDS
+
+    // <D, S0>
+    {
+      float x = 0.f;
 #pragma unroll
-    for (int s = 0; s < VS; ++s) {
-      const bf16x8 uh = tr_contig(puh, LDT, 32 * s, 16 * ra, lr, lg), ul = tr_contig(pul, LDT, 32 * s, 16 * ra, lr, lg);
-      const bf16x8 eh = tr_contig(peh, LDT, 32 * s, 16 * ib, lr, lg), el = tr_contig(pel, LDT, 32 * s, 16 * ib, lr, lg);
-      acc = mma(uh, eh, acc);
-      acc = mma(uh, el, acc);
-      acc = mma(ul, eh, acc);
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x += Da[kt][i] * Sa[kt][i];
+      x = row_sum16(x);
+      x = __shfl(x, 15, 16);
+      x = col_sum4(x);
+      if (lane == 0) atomicAdd(red + R_DS * CH, x);
     }
-    const int i = 16 * ib + lr;
-    float csum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * ra + 4 * lg + j;
-      const bool in = i < r && r < g.R;
-      const float da = in ? -acc[j] : 0.f;
-      const float ab = in ? abar[r * LDF + i] : 0.f;
-      const float br = fac[F_BETA * CH + r];
-      const float xr = row_sum16(da * ab);  // sum_i dA Abar (dbeta) ; times beta_r: sum_i dA A
-      if (lr == 15) {
-        atomicAdd(red + R_DB * CH + r, xr);
-        atomicAdd(red + R_DL * CH + r, br * xr);
-      }
-      csum += da * ab * br;
-      if (in) abar[r * LDF + i] = da * br * exp2f(fac[F_G2 * CH + r] - fac[F_G2 * CH + i]);
-    }
-    csum = col_sum4(csum);
-    if (lg == 0) atomicAdd(red + R_DL * CH + i, -csum);
-  }
-  // Z = dO E^T (E hi): W~ and its decay terms, kept in registers for the planes
-  constexpr int NZ = (TT16 * 4 + NW - 1) / NW;
-  f32x4 Zw[NZ];
-#pragma unroll
-  for (int m = 0; m < NZ; ++m) {
-    const int idx = w + m * NW;
-    Zw[m] = zero4();
-    if (idx < TT16 * 4) {
-      const int ta = idx >> 2, ib = idx & 3;
+    // Abar (strictly lower) from the Gram tiles of the raw rows
+    for (int idx = w; idx < 10; idx += NW) {
+      const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
+      const int rb = idx - ra * (ra + 1) / 2;
       f32x4 acc = zero4();
 #pragma unroll
-      for (int s = 0; s < VS; ++s)
-        acc = mma(ld_contig(so, LDO, 16 * ta + lr, 32 * s, lg), tr_contig(peh, LDT, 32 * s, 16 * ib, lr, lg), acc);
+      for (int s = 0; s < KS; ++s)
+        acc = mma(ld_contig(sk, LDK, 16 * ra + lr, 32 * s, lg), ld_contig(sk, LDK, 16 * rb + lr, 32 * s, lg), acc);
+      const int i = 16 * rb + lr;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * ra + 4 * lg + jj;
+        abar[r * LDF + i] = (i < r && r < g.R) ? fexp2(fac[F_G2 * CH + r] - fac[F_G2 * CH + i]) * fac[F_RK * CH + r] *
+                                                      fac[F_RK * CH + i] * acc[jj]
+                                                : 0.f;
+      }
+    }
+    // W = K S0 (S0 hi), X = K D (D split)
+    f32x4 W[4], X[4];
+    {
+      bf16x8 Sh[KS], Dh[KS], Dl[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Sh[s] = hi_acc(Sa[2 * s], Sa[2 * s + 1]);
+        split_acc(Dh[s], Dl[s], Da[2 * s], Da[2 * s + 1]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        W[rt] = zero4();
+        X[rt] = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 kf = ld_perm(sk, LDK, 16 * rt + lr, 32 * s, lg);
+          W[rt] = mma(kf, Sh[s], W[rt]);
+          X[rt] = mma(kf, Dh[s], X[rt]);
+          X[rt] = mma(kf, Dl[s], X[rt]);
+        }
+      }
+    }
+    // U = V - Gamma rk W, Ut = beta U;  E = T Ut (both split)
+    f32x4 U[4], E[4];
+    {
+      f32x4 Ut[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const bf16x4 vv = tr4(sv, LDV, 16 * rt + 4 * lg, 16 * w, lr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i;
+          U[rt][i] = (float)vv[i] - fexp2(fac[F_G2 * CH + r]) * fac[F_RK * CH + r] * W[rt][i];
+          Ut[rt][i] = fac[F_BETA * CH + r] * U[rt][i];
+        }
+      }
+      bf16x8 Uh[2], Ul[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split_acc(Uh[s], Ul[s], Ut[2 * s], Ut[2 * s + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        E[rt] = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 ah = tr_perm(tth, LDT, 32 * s, 16 * rt, lr, lg), al = tr_perm(ttl, LDT, 32 * s, 16 * rt, lr, lg);
+          E[rt] = mma(ah, Uh[s], E[rt]);
+          E[rt] = mma(ah, Ul[s], E[rt]);
+          E[rt] = mma(al, Uh[s], E[rt]);
+        }
+      }
+    }
+    // row partials over this wave's 16 columns go to per-wave slots: lane
+    // (lg, lr) holds row 16 (lr >> 2) + 4 lg + (lr & 3)
+    const int prow = 16 * (lr >> 2) + 4 * lg + (lr & 3);
+    {  // xe_r = c_r X_r.E_r
+      float x[16];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * rt + i] = X[rt][i] * E[rt][i];
+      slots[(R_XE * NW + w) * CH + prow] = fac[F_C * CH + prow] * rowsum_scatter(x, lr);
+    }
+    // dE = c X + P~^T dO;  dU = T^T dE (both split)
+    f32x4 dU[4];
+    {
+      bf16x8 of[TS];
+#pragma unroll
+      for (int s = 0; s < TS; ++s) of[s] = tr_contig(so, LDO, 32 * s, 16 * w, lr, lg);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[rt][i] *= fac[F_C * CH + 16 * rt + 4 * lg + i];
+#pragma unroll
+        for (int s = 0; s < TS; ++s) X[rt] = mma(ld_contig(ptb, LDP, 16 * rt + lr, 32 * s, lg), of[s], X[rt]);
+      }
+      bf16x8 Eh[2], El[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split_acc(Eh[s], El[s], X[2 * s], X[2 * s + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        dU[rt] = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 ah = ld_perm(tth, LDT, 16 * rt + lr, 32 * s, lg), al = ld_perm(ttl, LDT, 16 * rt + lr, 32 * s, lg);
+          dU[rt] = mma(ah, Eh[s], dU[rt]);
+          dU[rt] = mma(ah, El[s], dU[rt]);
+          dU[rt] = mma(al, Eh[s], dU[rt]);
+        }
+      }
+    }
+    // dv, and the row partials dU.U (dbeta) and -Gamma beta rk dU.W (decay)
+    {
+      float *dvl = a.dv + (krow0 + 4 * lg) * a.dv_st + h * a.dv_sh + col;
+      float xb[16], xw[16];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i;
+          if (r < g.R) dvl[(16 * rt + i) * a.dv_st] = fac[F_BETA * CH + r] * dU[rt][i];
+          xb[4 * rt + i] = dU[rt][i] * U[rt][i];
+          xw[4 * rt + i] = dU[rt][i] * W[rt][i];
+        }
+      slots[(R_DB * NW + w) * CH + prow] = rowsum_scatter(xb, lr);
+      slots[(R_DL * NW + w) * CH + prow] = -fexp2(fac[F_G2 * CH + prow]) * fac[F_BETA * CH + prow] *
+                                           fac[F_RK * CH + prow] * rowsum_scatter(xw, lr);
+    }
+    __syncthreads();  // every wave is done with the T^T planes and the v rows
+    // the per-wave row partials (dbeta, decay, xe) summed over the waves
+    if (tid < 3 * CH) {
+      const int q = tid / CH, r = tid % CH;
+      float x = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) x += slots[(q * NW + ww) * CH + r];
+      red[q * CH + r] += x;
+    }
+    // E^T and dU^T planes [v][r] (hi, lo)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int off = col * LDT + 16 * rt + 4 * lg;
+      f32x4 eh, uh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        eh[i] = (float)(bf16)E[rt][i];
+        uh[i] = (float)(bf16)dU[rt][i];
+      }
+      *(uint2 *)(peh + off) = pack4(eh);
+      *(uint2 *)(pel + off) = pack4(E[rt] - eh);
+      *(uint2 *)(puh + off) = pack4(uh);
+      *(uint2 *)(pul + off) = pack4(dU[rt] - uh);
+    }
+    __syncthreads();
+
+    // ---- products over V
+    // dA = -dU E^T (strictly lower tiles): dbeta and decay terms, then A~ into abar
+    for (int idx = w; idx < 10; idx += NW) {
+      const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
+      const int ib = idx - ra * (ra + 1) / 2;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        const bf16x8 uh = tr_contig(puh, LDT, 32 * s, 16 * ra, lr, lg), ul = tr_contig(pul, LDT, 32 * s, 16 * ra, lr, lg);
+        const bf16x8 eh = tr_contig(peh, LDT, 32 * s, 16 * ib, lr, lg), el = tr_contig(pel, LDT, 32 * s, 16 * ib, lr, lg);
+        acc = mma(uh, eh, acc);
+        acc = mma(uh, el, acc);
+        acc = mma(ul, eh, acc);
+      }
       const int i = 16 * ib + lr;
       float csum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * ta + 4 * lg + j;
-        const int rt = min((g.tlo + t) * n + n - 1 - g.row0, CH - 1);  // (exact for t < Tc)
-        const bool in = t < g.Tc && i <= rt && i < g.R;
-        const float z = in ? acc[j] : 0.f;
-        const float zp = z * (float)ptb[i * LDP + t];
-        const float xr = row_sum16(zp);
-        if (lr == 15 && t < g.Tc) atomicAdd(red + R_DL * CH + rt, xr);
-        csum += zp;
-        Zw[m][j] = in ? a.scale * exp2f(fac[F_G2 * CH + rt] - fac[F_G2 * CH + i]) * z : 0.f;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * ra + 4 * lg + jj;
+        const bool in = i < r && r < g.R;
+        const float da = in ? -acc[jj] : 0.f;
+        const float ab = in ? abar[r * LDF + i] : 0.f;
+        const float br_ = fac[F_BETA * CH + r];
+        const float xr = row_sum16(da * ab);  // sum_i dA Abar (dbeta); times beta_r: sum_i dA A
+        if (lr == 15) {
+          atomicAdd(red + R_DB * CH + r, xr);
+          atomicAdd(red + R_DL * CH + r, br_ * xr);
+        }
+        csum += da * ab * br_;
+        if (in) abar[r * LDF + i] = da * br_ * fexp2(fac[F_G2 * CH + r] - fac[F_G2 * CH + i]);
       }
       csum = col_sum4(csum);
       if (lg == 0) atomicAdd(red + R_DL * CH + i, -csum);
     }
-  }
-  // dK1 = dU S0^T (hi), dK2 = E D^T (split), dQ1 = dO S0^T (hi) on the wave's k tiles
-  f32x4 dK[NKW][4], dQ[NKW][TT16];
+    // Z = dO E^T (E hi): W~ and its decay terms, kept in registers for the planes
+    constexpr int NZ = (TT16 * 4 + NW - 1) / NW;
+    f32x4 Zw[NZ];
 #pragma unroll
-  for (int m = 0; m < NKW; ++m) {
-    const int kt = w + m * NW;
-    if (kt >= KT) continue;
-    const int kc = 16 * kt + lr;  // this lane's column k
-    f32x4 k1[4], k2[4];
+    for (int m = 0; m < NZ; ++m) {
+      const int idx = w + m * NW;
+      Zw[m] = zero4();
+      if (idx < TT16 * 4) {
+        const int ta = idx >> 2, ib = idx & 3;
+        f32x4 acc = zero4();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) k1[rt] = k2[rt] = zero4();
+        for (int s = 0; s < VS; ++s)
+          acc = mma(ld_contig(so, LDO, 16 * ta + lr, 32 * s, lg), tr_contig(peh, LDT, 32 * s, 16 * ib, lr, lg), acc);
+        const int i = 16 * ib + lr;
+        float csum = 0.f;
 #pragma unroll
-    for (int ta = 0; ta < TT16; ++ta) dQ[m][ta] = zero4();
+        for (int jj = 0; jj < 4; ++jj) {
+          const int t = 16 * ta + 4 * lg + jj;
+          const int rt = min((g.tlo + t) * n + n - 1 - g.row0, CH - 1);  // (exact for t < Tc)
+          const bool in = t < g.Tc && i <= rt && i < g.R;
+          const float z = in ? acc[jj] : 0.f;
+          const float zp = z * (float)ptb[i * LDP + t];
+          const float xr = row_sum16(zp);
+          if (lr == 15 && t < g.Tc) atomicAdd(red + R_DL * CH + rt, xr);
+          csum += zp;
+          Zw[m][jj] = in ? scale * fexp2(fac[F_G2 * CH + rt] - fac[F_G2 * CH + i]) * z : 0.f;
+        }
+        csum = col_sum4(csum);
+        if (lg == 0) atomicAdd(red + R_DL * CH + i, -csum);
+      }
+    }
+    // dK += -diag(Gamma beta) dU S0^T (hi) + diag(Gend / Gamma) E D^T (split);
+    // dQ += diag(e') dO S0^T (hi), with the decay term of the outputs
 #pragma unroll
-    for (int s = 0; s < VS; ++s) {
-      const bf16x8 sh = hi_acc(Ks[m][s][0], Ks[m][s][1]);
-      bf16x8 dh, dl;
-      split_acc(dh, dl, Kd[m][s][0], Kd[m][s][1]);
+    for (int m = 0; m < NKW; ++m) {
+      const int kt = w + m * NW;
+      if (kt >= KT) continue;
+      const int kc = 16 * kt + lr;
+      // the S0 and D rows of this k tile (L2 hits: the V slabs were just read),
+      // all issued before the first product
+      f32x4 Ks[VS][2], Kd[VS][2];
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        const float *ps = S0g + (size_t)kc * V + 32 * s + 8 * lg, *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
+        Ks[s][0] = *(const f32x4 *)ps;
+        Ks[s][1] = *(const f32x4 *)(ps + 4);
+        Kd[s][0] = *(const f32x4 *)pd;
+        Kd[s][1] = *(const f32x4 *)(pd + 4);
+      }
+      f32x4 k1[4], k2[4], q1[TT16];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) k1[rt] = k2[rt] = zero4();
+#pragma unroll
+      for (int ta = 0; ta < TT16; ++ta) q1[ta] = zero4();
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        const bf16x8 sh = hi_acc(Ks[s][0], Ks[s][1]);
+        bf16x8 dh, dl;
+        split_acc(dh, dl, Kd[s][0], Kd[s][1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          k1[rt] = mma(tr_contig(puh, LDT, 32 * s, 16 * rt, lr, lg), sh, k1[rt]);
+          const bf16x8 eh = tr_contig(peh, LDT, 32 * s, 16 * rt, lr, lg), el = tr_contig(pel, LDT, 32 * s, 16 * rt, lr, lg);
+          k2[rt] = mma(eh, dh, k2[rt]);
+          k2[rt] = mma(eh, dl, k2[rt]);
+          k2[rt] = mma(el, dh, k2[rt]);
+        }
+#pragma unroll
+        for (int ta = 0; ta < TT16; ++ta) q1[ta] = mma(ld_contig(so, LDO, 16 * ta + lr, 32 * s, lg), sh, q1[ta]);
+      }
+      const float g2e = fac[F_G2 * CH + CH - 1];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i;
+          const float g2r = fac[F_G2 * CH + r];
+          dK[m][rt][i] += -fexp2(g2r) * fac[F_BETA * CH + r] * k1[rt][i] + fexp2(g2e - g2r) * k2[rt][i];
+        }
+      // output decay term scale Gamma_{r_t} qhat_t.(S0 dO_t) = e_t q_t.dQ1_t
+#pragma unroll
+      for (int ta = 0; ta < TT16; ++ta)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int t = 16 * ta + 4 * lg + jj;
+          const float x = row_sum16(q1[ta][jj] * (float)sq[t * LDK + kc]);
+          if (lr == 15 && t < g.Tc) {
+            const int rt = (g.tlo + t) * n + n - 1 - g.row0;  // < R for t < Tc
+            atomicAdd(red + R_DL * CH + rt, fac[F_E * CH + t] * x);
+          }
+          dQ[m][ta][jj] += fac[F_EP * CH + t] * q1[ta][jj];
+        }
+    }
+    __syncthreads();  // E/dU planes dead; abar holds A~
+      // W~ planes [i][t]: w1 = W~ rq_t (for W~^T Qhat), w2 = W~ rk_i (for W~ Khat)
+#pragma unroll
+    for (int m = 0; m < NZ; ++m) {
+      const int idx = w + m * NW;
+      if (idx < TT16 * 4) {
+        const int ta = idx >> 2, ib = idx & 3;
+        const int i = 16 * ib + lr, t = 16 * ta + 4 * lg;
+        f32x4 x1, x2;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x1[jj] = Zw[m][jj] * fac[F_RQ * CH + t + jj];
+          x2[jj] = Zw[m][jj] * fac[F_RK * CH + i];
+        }
+        *(uint2 *)(pw1 + i * LDW + t) = pack4(x1);
+        *(uint2 *)(pw2 + i * LDW + t) = pack4(x2);
+      }
+    }
+    // M' = (A~ + A~^T) diag(rk), split
+    for (int u = tid; u < CH * (CH / 8); u += NTH) {
+      const int r = u >> 3, i0 = 8 * (u & 7);
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i = i0 + jj;
+        float m_ = 0.f;
+        if (i < r) m_ = abar[r * LDF + i];
+        else if (r < i) m_ = abar[i * LDF + r];
+        m_ *= fac[F_RK * CH + i];
+        hi[jj] = (bf16)m_;
+        lo[jj] = (bf16)(m_ - (float)hi[jj]);
+      }
+      *(bf16x8 *)(pmh + r * LDT + i0) = hi;
+      *(bf16x8 *)(pml + r * LDT + i0) = lo;
+    }
+    __syncthreads();
+    // dK += M' K + W1 Q;  dQ += W2^T K
+#pragma unroll
+    for (int m = 0; m < NKW; ++m) {
+      const int kt = w + m * NW;
+      if (kt >= KT) continue;
+      bf16x8 kb[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) kb[s] = tr_contig(sk, LDK, 32 * s, 16 * kt, lr, lg);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        k1[rt] = mma(tr_contig(puh, LDT, 32 * s, 16 * rt, lr, lg), sh, k1[rt]);
-        const bf16x8 eh = tr_contig(peh, LDT, 32 * s, 16 * rt, lr, lg), el = tr_contig(pel, LDT, 32 * s, 16 * rt, lr, lg);
-        k2[rt] = mma(eh, dh, k2[rt]);
-        k2[rt] = mma(eh, dl, k2[rt]);
-        k2[rt] = mma(el, dh, k2[rt]);
-      }
 #pragma unroll
-      for (int ta = 0; ta < TT16; ++ta) dQ[m][ta] = mma(ld_contig(so, LDO, 16 * ta + lr, 32 * s, lg), sh, dQ[m][ta]);
-    }
-    const float g2e = fac[F_G2 * CH + 63];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        const float g2r = fac[F_G2 * CH + r];
-        dK[m][rt][i] = -exp2f(g2r) * fac[F_BETA * CH + r] * k1[rt][i] + exp2f(g2e - g2r) * k2[rt][i];
-      }
-    // output decay term scale Gamma_{r_t} qhat_t.(S0 dO_t) = e'_t rq_t q_t.dQ1_t
-#pragma unroll
-    for (int ta = 0; ta < TT16; ++ta)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * ta + 4 * lg + j;
-        const float x = row_sum16(dQ[m][ta][j] * (float)sq[t * LDK + kc]);
-        if (lr == 15 && t < g.Tc) {
-          const int rt = (g.tlo + t) * n + n - 1 - g.row0;  // < R for t < Tc
-          atomicAdd(red + R_DL * CH + rt, fac[F_E * CH + t] * x);
+        for (int s = 0; s < 2; ++s) {
+          dK[m][rt] = mma(ld_contig(pmh, LDT, 16 * rt + lr, 32 * s, lg), kb[s], dK[m][rt]);
+          dK[m][rt] = mma(ld_contig(pml, LDT, 16 * rt + lr, 32 * s, lg), kb[s], dK[m][rt]);
         }
-        dQ[m][ta][j] *= fac[F_EP * CH + t];
-      }
-  }
-  __syncthreads();  // E/dU planes dead; abar holds A~
-  // W~ planes [i][t]: w1 = W~ rq_t (for W~^T Qhat), w2 = W~ rk_i (for W~ Khat)
 #pragma unroll
-  for (int m = 0; m < NZ; ++m) {
-    const int idx = w + m * NW;
-    if (idx < TT16 * 4) {
-      const int ta = idx >> 2, ib = idx & 3;
-      const int i = 16 * ib + lr, t = 16 * ta + 4 * lg;
-      f32x4 x1, x2;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x1[j] = Zw[m][j] * fac[F_RQ * CH + t + j];
-        x2[j] = Zw[m][j] * fac[F_RK * CH + i];
-      }
-      *(uint2 *)(pw1 + i * LDW + t) = pack4(x1);
-      *(uint2 *)(pw2 + i * LDW + t) = pack4(x2);
-    }
-  }
-  // M' = (A~ + A~^T) diag(rk), split
-  for (int u = tid; u < CH * (CH / 8); u += NTH) {
-    const int r = u >> 3, i0 = 8 * (u & 7);
-    bf16x8 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + j;
-      float m = 0.f;
-      if (i < r) m = abar[r * LDF + i];
-      else if (r < i) m = abar[i * LDF + r];
-      m *= fac[F_RK * CH + i];
-      hi[j] = (bf16)m;
-      lo[j] = (bf16)(m - (float)hi[j]);
-    }
-    *(bf16x8 *)(pmh + r * LDT + i0) = hi;
-    *(bf16x8 *)(pml + r * LDT + i0) = lo;
-  }
-  __syncthreads();
-  // dK += M' K + W1 Q;  dQ += W2^T K;  then the atomics
-#pragma unroll
-  for (int m = 0; m < NKW; ++m) {
-    const int kt = w + m * NW;
-    if (kt >= KT) continue;
-    const int kc = 16 * kt + lr;
-    bf16x8 kb[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) kb[s] = tr_contig(sk, LDK, 32 * s, 16 * kt, lr, lg);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        dK[m][rt] = mma(ld_contig(pmh, LDT, 16 * rt + lr, 32 * s, lg), kb[s], dK[m][rt]);
-        dK[m][rt] = mma(ld_contig(pml, LDT, 16 * rt + lr, 32 * s, lg), kb[s], dK[m][rt]);
+        for (int s = 0; s < TS; ++s)
+          dK[m][rt] = mma(ld_contig(pw1, LDW, 16 * rt + lr, 32 * s, lg), tr_contig(sq, LDK, 32 * s, 16 * kt, lr, lg),
+                          dK[m][rt]);
       }
 #pragma unroll
-      for (int s = 0; s < TS; ++s)
-        dK[m][rt] = mma(ld_contig(pw1, LDW, 16 * rt + lr, 32 * s, lg), tr_contig(sq, LDK, 32 * s, 16 * kt, lr, lg),
-                        dK[m][rt]);
+      for (int ta = 0; ta < TT16; ++ta)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        if (r < g.R) atomicAdd(a.dk + (krow0 + r) * a.dk_st + hk * a.dk_sh + kc, dK[m][rt][i]);
-      }
+        for (int s = 0; s < 2; ++s) dQ[m][ta] = mma(tr_contig(pw2, LDW, 32 * s, 16 * ta, lr, lg), kb[s], dQ[m][ta]);
     }
+    // the next head's slabs and rows
+    const bool more = j + 1 < G;
+    if (more) load_head(h + 1, !kshared);
+    // this head's decay gradients (suffix sums from each token's first row) and dbeta
+    if (w == 0) {
+      const int r = lane;
+      const bool in = r < g.R;
+      const float xe = in ? red[R_XE * CH + r] : 0.f;
+      float tot = xe;
 #pragma unroll
-    for (int ta = 0; ta < TT16; ++ta) {
+      for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+      float x = in ? red[R_DL * CH + r] - xe : 0.f;
+      if (r == g.R - 1) x += fac[F_META * CH] * red[R_DS * CH] + tot;
+      float pre = x;  // suffix sum: total minus the exclusive prefix
 #pragma unroll
-      for (int s = 0; s < 2; ++s) dQ[m][ta] = mma(tr_contig(pw2, LDW, 32 * s, 16 * ta, lr, lg), kb[s], dQ[m][ta]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * ta + 4 * lg + j;
-        if (t < g.Tc) atomicAdd(a.dq + (qrow0 + t) * a.dq_st + hq * a.dq_sh + kc, dQ[m][ta][j]);
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(pre, off, 64);
+        if (lane >= off) pre += y;
       }
+      const float suf = __shfl(pre, 63, 64) - pre + x;
+      if (in && (g.row0 + r) % n == 0) a.dg[(g.t0 + (g.row0 + r) / n) * a.dg_st + h * a.dg_sh] = suf;
+      if (in) a.dbeta[(krow0 + r) * a.db_st + h * a.db_sh] = red[R_DB * CH + r];
+    }
+    // with one k head per state head, this head's dk rows are complete
+    if (!kshared) {
+      store_rows<NKW, 4, K>(a.dk, krow0, a.dk_st, (h / (a.Hv / a.Hk)) * a.dk_sh, g.R, dK, sk, LDK, fac + F_RK * CH,
+                            red + R_KN * CH, a.l2norm, w, NW, lr, lg);
+#pragma unroll
+      for (int m = 0; m < NKW; ++m)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) dK[m][rt] = zero4();
+    }
+    if (more) {
+      __syncthreads();  // every wave is past this head's LDS reads
+      commit_head(!kshared);
     }
   }
-  // decay gradients (suffix sums from each token's first row) and dbeta
-  if (w == 0) {
-    const int r = lane;
-    const bool in = r < g.R;
-    const float xe = in ? red[R_XE * CH + r] : 0.f;
-    float tot = xe;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
-    float x = in ? red[R_DL * CH + r] - xe : 0.f;
-    if (r == g.R - 1) x += fac[F_META * CH] * red[R_DS * CH] + tot;
-    // suffix sum: total minus the exclusive prefix
-    float pre = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(pre, off, 64);
-      if (lane >= off) pre += y;
-    }
-    float all = pre;
-    all = __shfl(all, 63, 64);
-    const float suf = all - pre + x;
-    if (in && (g.row0 + r) % n == 0) a.dg[(g.t0 + (g.row0 + r) / n) * a.dg_st + h * a.dg_sh] = suf;
-    if (in) a.dbeta[(krow0 + r) * a.db_st + h * a.db_sh] = red[R_DB * CH + r];
-  }
+  // dq (and the shared dk), through the norm gradient
+  store_rows<NKW, TT16, K>(a.dq, qrow0, a.dq_st, hq * a.dq_sh, g.Tc, dQ, sq, LDK, fac + F_RQ * CH, red + R_QN * CH,
+                           a.l2norm, w, NW, lr, lg);
+  if (kshared)
+    store_rows<NKW, 4, K>(a.dk, krow0, a.dk_st, (hq * G / (a.Hv / a.Hk)) * a.dk_sh, g.R, dK, sk, LDK, fac + F_RK * CH,
+                          red + R_KN * CH, a.l2norm, w, NW, lr, lg);
 }
 
 template <int K, int V, int TCM> hipError_t launch_kv(const BwdChunkArgs &a, hipStream_t stream) {
@@ -1249,8 +1391,8 @@ template <int K, int V, int TCM> hipError_t launch_kv(const BwdChunkArgs &a, hip
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   if (a.ntdp_rows > 0) {
-    hipLaunchKernelGGL((gdp_bwd_grad_kernel<K, V, TCM>), dim3((unsigned)(a.ntdp_rows * a.Hv)), dim3(4 * V), 0, stream,
-                       a);
+    hipLaunchKernelGGL((gdp_bwd_grad_kernel<K, V, TCM>), dim3((unsigned)(a.ntdp_rows * a.Hqk)), dim3(4 * V), 0,
+                       stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   return hipSuccess;
