@@ -32,23 +32,25 @@
 // The gradients by q and k are the ones by their normalised rows; a later
 // kernel maps them through the norm.
 //
-// Kernels, in launch order (after the forward pass has left the state entering
-// every expanded chunk):
+// Kernels, in launch order:
 //   gdp_bwd_prep_kernel     one workgroup per (expanded chunk, k head): Gram and
 //                           q.k tiles once, then per state head of the group T in
-//                           fp32 (the WY inverse), stored as T^T in bf16 hi/lo
-//                           planes, P~^T and the per-row factors ("bundle")
-//   gdp_bwd_adjoint_kernel  one workgroup per (sequence, state head), one wave per
-//                           16 state columns: walks the expanded chunks backwards
-//                           with D in fp32 accumulators, storing D at each chunk's
-//                           end; the next chunk's rows and bundle are loaded into
+//                           fp32 (the WY inverse), stored as T^T in bf16 with
+//                           P~^T and the per-row factors (the chunk's "bundle")
+//   gdp_bwd_state_kernel    one workgroup per (sequence, state head), one wave per
+//                           16 state columns: walks the expanded chunks forwards
+//                           and stores the state entering each one (fp32)
+//   gdp_bwd_adjoint_kernel  the same shape, walking backwards with D in fp32
+//                           accumulators and storing D at each chunk's end; both
+//                           walks load the next chunk's rows and bundle into
 //                           registers while the current one is multiplied
-//   gdp_bwd_grad_kernel     one workgroup per (expanded chunk, state head): every
-//                           gradient of the chunk from S0, D, the bundle and the
-//                           inputs, with no sequential dependency; dq and dk are
-//                           added with float atomics (state heads share q/k heads)
-// Products whose operands carry D, E, dU or T use split bf16 operands (x = hi +
-// lo, three products: hi.hi + hi.lo + lo.hi), the others plain bf16; all on
+//   gdp_bwd_grad_kernel     one workgroup per (expanded chunk, q/k head): every
+//                           gradient of the chunk for each state head of the
+//                           group in turn, from S0, D, the bundle and the inputs,
+//                           with no sequential dependency
+// Products whose operands carry D, E or dU use split bf16 operands (x = hi + lo:
+// hi.hi + hi.lo + lo.hi, or hi.hi + hi.lo when the other operand is exact in
+// bf16 or is T, which is kept in bf16), the others plain bf16; all on
 // v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 
 #include <hip/hip_runtime.h>
@@ -86,9 +88,8 @@ template <int TCM> struct Bundle {
   static constexpr int LDP = TCM + 8;
   static constexpr int PTB = 0;                       // bf16 [64][LDP]: P~^T (row i, token slot t)
   static constexpr int FAC = PTB + CH * LDP * 2;      // fp32 [NFAC][64]
-  static constexpr int TTH = FAC + NFAC * CH * 4;     // bf16 [64][LDT]: hi part of T^T (row i, column r)
-  static constexpr int TTL = TTH + CH * LDT * 2;      // bf16 [64][LDT]: lo part
-  static constexpr int BYTES = TTL + CH * LDT * 2;
+  static constexpr int TTH = FAC + NFAC * CH * 4;     // bf16 [64][LDT]: T^T (row i, column r)
+  static constexpr int BYTES = TTH + CH * LDT * 2;
   static_assert(BYTES % 16 == 0, "whole 16-byte segments");
 };
 
@@ -428,18 +429,13 @@ __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
     __syncthreads();
     wy_inverse<LDF>(sm.u.wy.a, sm.u.wy.tf, tid);
     char *out = a.bundle + ((size_t)p * a.Hv + h) * B::BYTES;
-    // T^T planes: row i, columns r (8 per thread and step)
+    // T^T plane: row i, columns r (8 per thread and step)
     for (int u = tid; u < CH * (LDT / 8); u += NTHR) {
       const int i = u / (LDT / 8), r0 = 8 * (u % (LDT / 8));
-      bf16x8 hi, lo;
+      bf16x8 hi;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = (r0 + j < CH) ? sm.u.wy.tf[(r0 + j) * LDF + i] : 0.f;
-        hi[j] = (bf16)x;
-        lo[j] = (bf16)(x - (float)hi[j]);
-      }
+      for (int j = 0; j < 8; ++j) hi[j] = (bf16)((r0 + j < CH) ? sm.u.wy.tf[(r0 + j) * LDF + i] : 0.f);
       *(bf16x8 *)(out + B::TTH + 2 * (i * LDT + r0)) = hi;
-      *(bf16x8 *)(out + B::TTL + 2 * (i * LDT + r0)) = lo;
     }
     // P~^T (row i, token slots t) from the q.k tiles: lane holds 4 consecutive slots of one row i
 #pragma unroll
@@ -550,7 +546,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
     st.commit(sm, tid);
   }
   __syncthreads();
-  const bf16 *tth = (const bf16 *)(sm.bundle + B::TTH), *ttl = (const bf16 *)(sm.bundle + B::TTL);
+  const bf16 *tth = (const bf16 *)(sm.bundle + B::TTH);
   const float *fac = (const float *)(sm.bundle + B::FAC);
   for (int e = 0; e < nexp; ++e) {
     if (e + 1 < nexp) st.load(a, chunk_geo(t0, nsub, a.n, e + 1), p0 + e + 1, h, hk, tid);
@@ -584,7 +580,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
         }
       }
     }
-    // E = T Ut (both split), scaled by c
+    // E = T Ut (Ut split), scaled by c
     f32x4 E[4];
     {
       bf16x8 Uh[2], Ul[2];
@@ -595,10 +591,9 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
         E[rt] = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 ah = tr_perm(tth, LDT, 32 * s, 16 * rt, lr, lg), al = tr_perm(ttl, LDT, 32 * s, 16 * rt, lr, lg);
+          const bf16x8 ah = tr_perm(tth, LDT, 32 * s, 16 * rt, lr, lg);
           E[rt] = mma(ah, Uh[s], E[rt]);
           E[rt] = mma(ah, Ul[s], E[rt]);
-          E[rt] = mma(al, Uh[s], E[rt]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) E[rt][i] *= fac[F_C * CH + 16 * rt + 4 * lg + i];
@@ -700,7 +695,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_adjoint_kernel(BwdChunkArgs 
     st.commit(sm, tid);
   }
   __syncthreads();
-  const bf16 *tth = (const bf16 *)(sm.bundle + B::TTH), *ttl = (const bf16 *)(sm.bundle + B::TTL);
+  const bf16 *tth = (const bf16 *)(sm.bundle + B::TTH);
   const bf16 *ptb = (const bf16 *)(sm.bundle + B::PTB);
   const float *fac = (const float *)(sm.bundle + B::FAC);
   for (int e = nexp - 1; e >= 0; --e) {
@@ -740,7 +735,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_adjoint_kernel(BwdChunkArgs 
 #pragma unroll
       for (int s = 0; s < TS; ++s) X[rt] = mma(ld_contig(ptb, LDP, 16 * rt + lr, 32 * s, lg), of[s], X[rt]);
     }
-    // dU = T^T dE (both split), then dW' = -d dU
+    // dU = T^T dE (dE split), then dW' = -d dU
     f32x4 U[4];
     {
       bf16x8 Eh[2], El[2];
@@ -751,10 +746,9 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_adjoint_kernel(BwdChunkArgs 
         U[rt] = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 ah = ld_perm(tth, LDT, 16 * rt + lr, 32 * s, lg), al = ld_perm(ttl, LDT, 16 * rt + lr, 32 * s, lg);
+          const bf16x8 ah = ld_perm(tth, LDT, 16 * rt + lr, 32 * s, lg);
           U[rt] = mma(ah, Eh[s], U[rt]);
           U[rt] = mma(ah, El[s], U[rt]);
-          U[rt] = mma(al, Eh[s], U[rt]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) U[rt][i] *= -fac[F_D * CH + 16 * rt + 4 * lg + i];
@@ -863,7 +857,7 @@ template <int K, int V, int TCM> struct GradLds {
   static constexpr int BU = SL + 3 * (V / 16) * CH * 4;      // the bundle
   // the rest lies over the bundle's T^T planes, which are dead once dU is formed:
   static constexpr int PL = BU + B::TTH;
-  static constexpr int VR = PL + 2 * CH * LDT * 2;           // bf16 [64][LDV] v rows (until U is formed)
+  static constexpr int VR = PL + CH * LDT * 2;               // bf16 [64][LDV] v rows (until U is formed)
   static constexpr int EH = PL, EL = EH + V * LDT * 2, UH = EL + V * LDT * 2, UL = UH + V * LDT * 2;  // E^T, dU^T [v][r]
   static constexpr int P1_END = UL + V * LDT * 2;
   static constexpr int MH = PL, ML = MH + CH * LDT * 2;      // M' = (A~ + A~^T) diag(rk), [r][i]
@@ -895,7 +889,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   bf16 *sk = (bf16 *)(smem + L::K_), *sq = (bf16 *)(smem + L::Q_), *so = (bf16 *)(smem + L::O_);
   bf16 *sv = (bf16 *)(smem + L::VR);
   float *abar = (float *)(smem + L::AB), *red = (float *)(smem + L::RD), *slots = (float *)(smem + L::SL);
-  const bf16 *tth = (const bf16 *)(smem + L::BU + B::TTH), *ttl = (const bf16 *)(smem + L::BU + B::TTL);
+  const bf16 *tth = (const bf16 *)(smem + L::BU + B::TTH);
   const bf16 *ptb = (const bf16 *)(smem + L::BU + B::PTB);
   const float *fac = (const float *)(smem + L::BU + B::FAC);
   bf16 *peh = (bf16 *)(smem + L::EH), *pel = (bf16 *)(smem + L::EL), *puh = (bf16 *)(smem + L::UH),
@@ -1033,7 +1027,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
         }
       }
     }
-    // U = V - Gamma rk W, Ut = beta U;  E = T Ut (both split)
+    // U = V - Gamma rk W, Ut = beta U;  E = T Ut (Ut split)
     f32x4 U[4], E[4];
     {
       f32x4 Ut[4];
@@ -1055,10 +1049,9 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
         E[rt] = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 ah = tr_perm(tth, LDT, 32 * s, 16 * rt, lr, lg), al = tr_perm(ttl, LDT, 32 * s, 16 * rt, lr, lg);
+          const bf16x8 ah = tr_perm(tth, LDT, 32 * s, 16 * rt, lr, lg);
           E[rt] = mma(ah, Uh[s], E[rt]);
           E[rt] = mma(ah, Ul[s], E[rt]);
-          E[rt] = mma(al, Uh[s], E[rt]);
         }
       }
     }
@@ -1073,7 +1066,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
         for (int i = 0; i < 4; ++i) x[4 * rt + i] = X[rt][i] * E[rt][i];
       slots[(R_XE * NW + w) * CH + prow] = fac[F_C * CH + prow] * rowsum_scatter(x, lr);
     }
-    // dE = c X + P~^T dO;  dU = T^T dE (both split)
+    // dE = c X + P~^T dO;  dU = T^T dE (dE split)
     f32x4 dU[4];
     {
       bf16x8 of[TS];
@@ -1094,10 +1087,9 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
         dU[rt] = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 ah = ld_perm(tth, LDT, 16 * rt + lr, 32 * s, lg), al = ld_perm(ttl, LDT, 16 * rt + lr, 32 * s, lg);
+          const bf16x8 ah = ld_perm(tth, LDT, 16 * rt + lr, 32 * s, lg);
           dU[rt] = mma(ah, Eh[s], dU[rt]);
           dU[rt] = mma(ah, El[s], dU[rt]);
-          dU[rt] = mma(al, Eh[s], dU[rt]);
         }
       }
     }
