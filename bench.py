@@ -362,10 +362,12 @@ def bench_flashinfer(args, gdp, workloads):
 
 def bench_backward(args, gdp, workloads):
     """Gradients of the long-context prefill (its shape and inputs, one call per
-    step, including the forward rerun that leaves the chunk states).  The
-    recurrent reverse pass is bound by its per-token vector arithmetic; the line
-    reports its HBM bytes (inputs read once, float32 gradients written once) so
-    that the fraction shows how far it is from the bandwidth bound."""
+    step: the chunked path's prep, state walk, reverse state-gradient walk and
+    per-chunk gradient kernels, or with GDP_BACKWARD_PATH=recurrent the forward
+    rerun and the per-token reverse kernel).  The line reports the algorithmic
+    HBM bytes (inputs read once, float32 gradients written once) so that the
+    fraction shows how far the call is from the bandwidth bound; the chunked
+    path also moves the per-chunk states and state gradients through HBM."""
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -410,7 +412,10 @@ def bench_backward(args, gdp, workloads):
                                    "K=V=128, bf16, in-kernel L2 norm", "real_tokens": T},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "gdp_chunk_prefill_backward (forward rerun + gdp_backward_kernel)",
+                         "kernel": ("gdp_chunk_prefill_backward (forward rerun + gdp_backward_kernel)"
+                                    if os.environ.get("GDP_BACKWARD_PATH") == "recurrent" else
+                                    "gdp_chunk_prefill_backward (gdp_bwd_prep, gdp_bwd_state, gdp_bwd_adjoint, "
+                                    "gdp_bwd_grad kernels)"),
                          "kernel_ms": kern_ms, "algorithmic_bytes_per_launch": alg},
             "cpu_baseline": None}
     if not args.no_cpu_baseline:

@@ -53,18 +53,52 @@ def run_case(gdp, ci, seed=0):
     return res, ref, TOL[dt]
 
 
-@pytest.mark.parametrize("kpath", ["fused", "split"])
+@pytest.mark.parametrize("kpath", ["chunked", "recurrent-fused", "recurrent-split"])
 @pytest.mark.parametrize("ci", range(len(CASES)))
 def test_backward_parity(gdp, ci, kpath, monkeypatch):
-    if CASES[ci][7] == torch.float32 and kpath == "fused":
+    """Every case on the chunked path (the default for bfloat16 inputs; float32
+    inputs always take the recurrent one) and on the recurrent path with either
+    forward rerun."""
+    if kpath == "recurrent-fused" and CASES[ci][7] == torch.float32:
         pytest.skip("float32 inputs run the split forward only")
-    monkeypatch.setenv("GDP_PREFILL_PATH", kpath)
+    if kpath.startswith("recurrent"):
+        monkeypatch.setenv("GDP_BACKWARD_PATH", "recurrent")
+        monkeypatch.setenv("GDP_PREFILL_PATH", kpath.split("-")[1])
     res, ref, tol = run_case(gdp, ci)
     names = ["dq", "dk", "dv", "dg_log", "dbeta"] + (["d_initial_state"] if res["d_initial_state"] is not None else [])
     for name in names:
         key = "dinitial_state" if name == "d_initial_state" else name
         e = rel_err(to_np(res[name]), ref[key])
         assert e <= tol, f"case {ci} {kpath}: {name} err {e:.3e}"
+
+
+def test_backward_strong_decays(gdp):
+    """Decays down to g_log = -40 on some tokens (the chunk's cumulative decay
+    underflows): the chunked path's decay ratios and factors stay finite and the
+    gradients match the oracle."""
+    lens, n, Hqk, Hv, K, V = [150, 70], 2, 2, 4, 128, 128
+    w = workloads.custom(lens, n, Hqk, Hv, K, V, dtype=torch.bfloat16, l2norm_in_kernel=True, init_std=0.2,
+                         seed=91)
+    inp = workloads.generate(w, "cpu")
+    gen = torch.Generator().manual_seed(92)
+    g = -torch.nn.functional.softplus(torch.randn(w.T, Hv, generator=gen) + 2.0)
+    g[torch.rand(w.T, Hv, generator=gen) < 0.05] = -40.0
+    inp["g_log"] = g
+    d_o = torch.randn(w.T, Hv, V, generator=gen).to(torch.bfloat16)
+    ref = obwd.backward(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(g), to_np(inp["beta"]), n,
+                        inp["cu_seqlens"].numpy(), to_np(d_o), None, initial_state=to_np(inp["initial_state"]),
+                        use_qk_l2norm=True)
+    dev = lambda x: None if x is None else x.cuda()
+    res = gdp.chunk_prefill_backward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(g), dev(inp["beta"]), n,
+                                     dev(inp["cu_seqlens"]), dev(d_o), None, initial_state=dev(inp["initial_state"]),
+                                     use_qk_l2norm=True)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg_log", "dbeta", "d_initial_state"):
+        key = "dinitial_state" if name == "d_initial_state" else name
+        x = to_np(res[name])
+        assert np.isfinite(x).all(), name
+        e = rel_err(x, ref[key])
+        assert e <= TOL[torch.bfloat16], f"{name} err {e:.3e}"
 
 
 def test_backward_zero_length_and_padding_rows(gdp):
