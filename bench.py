@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_long_context_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "gated_deltaproduct_recurrence_amd", "csrc", "gdp_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltaproduct_recurrence_amd", "csrc", f)
+                  for f in ("gdp_kernels.hip", "gdp_common.h")]
 
 
 def algorithmic_bytes(w, slots=None):
@@ -73,8 +74,11 @@ def check_against_oracle(what, err, tol):
 
 
 def source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(wid):

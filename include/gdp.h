@@ -229,7 +229,11 @@ int gdp_recurrent_decode(const gdp_tensor *q, const gdp_tensor *k, const gdp_ten
                          float scale, int32_t use_qk_l2norm, const gdp_tensor *state_cache,
                          const gdp_tensor *state_indices, const gdp_tensor *o, void *stream);
 
-/* Host-only.  Workspace bytes gdp_chunk_prefill_backward needs: the
+/* Host-only.  Workspace bytes gdp_chunk_prefill_backward needs, the larger of
+ * its two paths' needs.  The chunked path: the descriptors, then per expanded
+ * 64-row chunk and state head the float32 entering state and end-of-chunk state
+ * gradient (2 x ntdp_cap x Hv x K x V floats) and a prep bundle (T^T and the
+ * decayed scores in bfloat16, per-row factors).  The recurrent path: the
  * descriptors, the float32 state entering every token chunk (nt_cap x Hv x K x V),
  * an output buffer of the forward pass it reruns, the float32 L2-norm factors of
  * the q and k rows (T x Hqk and T*n x Hv at most), and that pass's workspace
@@ -245,15 +249,25 @@ size_t gdp_backward_workspace_bytes(int64_t T, int64_t N, int32_t num_householde
  * The pages give no backward formulas (the blog page "Attention Cache and
  * Sequence Parallelism", section "GDN: pass the state, not the KV", notes only
  * that the dependencies run in reverse); these are the gradients of the
- * recurrence itself, by reverse-mode differentiation token by token.  The call
- * reruns the forward pass to obtain the state entering every 64-token chunk,
- * then walks each chain backwards, recomputing the states in between.
+ * recurrence itself, by reverse-mode differentiation.  Two paths give them:
+ *   chunked (bfloat16 inputs, q/k/v/d_o 16-byte aligned with row and head
+ *   strides multiples of 8): per
+ *   64-row expanded chunk, a prep kernel forms the chunk's WY inverse and decayed
+ *   scores, a forward walk stores each chunk's entering state and a reverse walk
+ *   each chunk's end-of-chunk state gradient (both float32), and a gradient
+ *   kernel forms every gradient of a chunk with matrix-core products;
+ *   recurrent (everything else, or GDP_BACKWARD_PATH=recurrent in the
+ *   environment): reruns the forward pass to obtain the state entering every
+ *   64-token chunk, then walks each chain backwards token by token, recomputing
+ *   the states in between.
  *   d_o            [T, Hv, V]      q's dtype, rows may be strided
  *   d_final_state  [N, Hv, K, V]   float32 contiguous, or data == NULL (zero)
  *   dq [T, Hqk, K], dk [T*n, Hk, K], dg_log [T, Hv], dbeta [T*n, Hv]
- *                                  float32, contiguous: they are accumulated with
- *                                  float atomics over state heads and V tiles, so
- *                                  their last bits depend on the order of the adds
+ *                                  float32, contiguous: the recurrent path
+ *                                  accumulates them with float atomics over state
+ *                                  heads and V tiles, so their last bits depend on
+ *                                  the order of the adds; the chunked path stores
+ *                                  each entry once
  *   dv [T*n, Hv, V]                float32, rows may be strided; the sub-rows no
  *                                  sequence covers (before cu_seqlens[0]*n or from
  *                                  cu_seqlens[N]*n on) are written as zeros, like
