@@ -727,18 +727,25 @@ static bool env_backward_recurrent() {
 // the in-kernel norm, on the recurrent path; the chunked gradient kernel applies
 // it itself) the gradients by the raw q and k rows from those by their
 // normalised rows.
+// Zeroes the rows of a float32 gradient [T * per_token, heads, D] (D = 1 for a
+// 2-d [T * per_token, heads] one) that no sequence covers: before cu[0] or from
+// cu[N] on.
+static int zero_rows_outside(const gdp_tensor *t, const gdp_tensor *cu_seqlens, int64_t T, int64_t N,
+                             int32_t per_token, int64_t heads, int64_t D, void *stream) {
+  gdp::ZeroOutsideArgs z;
+  z.p = (float *)t->data; z.st = t->stride[0]; z.sh = t->ndim > 1 ? t->stride[1] : 0;
+  z.cu = cu_seqlens->data; z.cu_is64 = cu_seqlens->dtype == GDP_I64;
+  z.T = T; z.N = (int)N; z.n = per_token; z.heads = (int)heads; z.D = (int)D;
+  const hipError_t e = gdp::launch_zero_outside(z, (hipStream_t)stream);
+  return e == hipSuccess ? GDP_OK : fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
+}
+
 static int bwd_finish(const gdp_tensor *q, const gdp_tensor *k, const gdp_tensor *dq, const gdp_tensor *dk,
                       const gdp_tensor *dv, const gdp_tensor *cu_seqlens, int64_t T, int64_t N, int32_t n, int64_t Hqk,
                       int64_t Hk, int64_t Hv, int64_t K, int64_t V, int idt, int32_t use_qk_l2norm, void *stream) {
   hipError_t e;
-  {  // the rows of dv no sequence covers (before cu[0] or from cu[N] on) are zero
-    gdp::ZeroOutsideArgs z;
-    z.p = (float *)dv->data; z.st = dv->stride[0]; z.sh = dv->stride[1];
-    z.cu = cu_seqlens->data; z.cu_is64 = cu_seqlens->dtype == GDP_I64;
-    z.T = T; z.N = (int)N; z.n = n; z.heads = (int)Hv; z.D = (int)V;
-    if ((e = gdp::launch_zero_outside(z, (hipStream_t)stream)) != hipSuccess)
-      return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
-  }
+  int rc;
+  if ((rc = zero_rows_outside(dv, cu_seqlens, T, N, n, Hv, V, stream)) != GDP_OK) return rc;
   if (use_qk_l2norm) {
     gdp::NormGradArgs na;
     na.x = q->data; na.x_st = q->stride[0]; na.x_sh = q->stride[1];
@@ -856,13 +863,22 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
                            1, &to, &none, &tcs, &d, ws + L.fwd, workspace_bytes - L.fwd, stream, false, true)) != GDP_OK)
       return rc;
   }
-  for (const gdp_tensor *t : {dq, dk, dg_log, dbeta}) {
-    int64_t cnt = 1;
-    for (int i = 0; i < t->ndim; ++i) cnt *= t->shape[i];
-    if ((e = gdp::launch_fill((int32_t *)t->data, cnt, 0, (hipStream_t)stream)) != hipSuccess)
-      return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
+  if (!chunked) {  // the per-token kernel accumulates dq, dk, dg_log and dbeta with atomics
+    for (const gdp_tensor *t : {dq, dk, dg_log, dbeta}) {
+      int64_t cnt = 1;
+      for (int i = 0; i < t->ndim; ++i) cnt *= t->shape[i];
+      if ((e = gdp::launch_fill((int32_t *)t->data, cnt, 0, (hipStream_t)stream)) != hipSuccess)
+        return fail(GDP_EHIP, "zero fill launch: %s", hipGetErrorString(e));
+    }
   }
   if (chunked) {
+    // the chunked kernels store every entry inside the sequences once; only the
+    // rows outside them are zeroed here
+    if ((rc = zero_rows_outside(dq, cu_seqlens, T, N, 1, Hqk, K, stream)) != GDP_OK ||
+        (rc = zero_rows_outside(dk, cu_seqlens, T, N, n, Hk, K, stream)) != GDP_OK ||
+        (rc = zero_rows_outside(dg_log, cu_seqlens, T, N, 1, Hv, 1, stream)) != GDP_OK ||
+        (rc = zero_rows_outside(dbeta, cu_seqlens, T, N, n, Hv, 1, stream)) != GDP_OK)
+      return rc;
     gdp::BwdChunkArgs c;
     std::memset(&c, 0, sizeof c);
     c.q = q->data; c.q_st = q->stride[0]; c.q_sh = q->stride[1];

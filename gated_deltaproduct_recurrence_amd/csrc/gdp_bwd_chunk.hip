@@ -90,7 +90,7 @@ template <int TCM> struct Bundle {
   static constexpr int FAC = PTB + CH * LDP * 2;      // fp32 [NFAC][64]
   static constexpr int TTH = FAC + NFAC * CH * 4;     // bf16 [64][LDT]: T^T (row i, column r)
   static constexpr int BYTES = TTH + CH * LDT * 2;
-  static_assert(BYTES % 16 == 0, "whole 16-byte segments");
+  static_assert(BYTES % 16 == 0 && FAC % 16 == 0, "whole 16-byte segments");
 };
 
 struct Geo {
@@ -131,6 +131,14 @@ __device__ __forceinline__ bool row_geo(const BwdChunkArgs &a, int64_t p, Geo &g
   if ((int64_t)CH * cc >= nsub) return false;
   g = chunk_geo(t0, nsub, a.n, cc);
   return true;
+}
+
+// The walks' (sequence, state head) of this workgroup.  Workgroups are dealt to
+// the 8 XCDs round-robin; the remap gives each XCD a contiguous range, so that
+// the state heads sharing a k head read its rows through one L2.
+__device__ __forceinline__ int64_t walk_chain() {
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
 }
 
 // ---------------------------------------------------------------- fragments
@@ -492,18 +500,20 @@ template <int K, int V, int TCM> struct FwdSmem {
 template <int K, int V, int TCM, int NTH> struct FwdStage {
   TileRegs<CH, K, NTH> k;
   TileRegs<CH, V, NTH> v;
-  BlockRegs<Bundle<TCM>::BYTES, NTH> b;
+  // the factor rows and T^T (the forward walk does not read the scores P~^T)
+  static constexpr int B0 = Bundle<TCM>::FAC;
+  BlockRegs<Bundle<TCM>::BYTES - B0, NTH> b;
   int R;
   __device__ __forceinline__ void load(const BwdChunkArgs &a, const Geo &g, int64_t p, int h, int hk, int tid) {
     R = g.R;
     k.load((const bf16 *)a.k + hk * a.k_sh + (g.t0 * a.n + g.row0) * a.k_st, a.k_st, g.R, tid);
     v.load((const bf16 *)a.v + h * a.v_sh + (g.t0 * a.n + g.row0) * a.v_st, a.v_st, g.R, tid);
-    b.load(a.bundle + ((size_t)p * a.Hv + h) * Bundle<TCM>::BYTES, tid);
+    b.load(a.bundle + ((size_t)p * a.Hv + h) * Bundle<TCM>::BYTES + B0, tid);
   }
   __device__ __forceinline__ void commit(FwdSmem<K, V, TCM> &sm, int tid) const {
     k.template store<FwdSmem<K, V, TCM>::LDK>(sm.k, R, tid);
     v.template store<FwdSmem<K, V, TCM>::LDV>(sm.v, R, tid);
-    b.store(sm.bundle, tid);
+    b.store(sm.bundle + B0, tid);
   }
 };
 
@@ -519,7 +529,8 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
   constexpr int LDK = S::LDK, LDV = S::LDV;
   __shared__ __attribute__((aligned(16))) S sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const int seq = (int)(blockIdx.x / a.Hv), h = (int)(blockIdx.x % a.Hv);
+  const int64_t chain = walk_chain();
+  const int seq = (int)(chain / a.Hv), h = (int)(chain % a.Hv);
   if (seq >= a.N) return;
   const int hk = h / (a.Hv / a.Hk);
   int64_t t0, t1;
@@ -666,7 +677,8 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_adjoint_kernel(BwdChunkArgs 
   constexpr int LDK = S::LDK, LDO = S::LDO, LDP = B::LDP;
   __shared__ __attribute__((aligned(16))) S sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const int seq = (int)(blockIdx.x / a.Hv), h = (int)(blockIdx.x % a.Hv);
+  const int64_t chain = walk_chain();
+  const int seq = (int)(chain / a.Hv), h = (int)(chain % a.Hv);
   if (seq >= a.N) return;
   const int hk = h / (a.Hv / a.Hk), hq = h / (a.Hv / a.Hqk);
   int64_t t0, t1;
