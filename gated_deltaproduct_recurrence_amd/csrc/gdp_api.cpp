@@ -709,7 +709,7 @@ static BwdLayout bwd_layout(int64_t T, int64_t N, int32_t n, int32_t Hqk, int32_
   if (gdp::bwd_chunked_supported(dtype == GDP_BF16 ? gdp::IN_BF16 : gdp::IN_F32, K, V, n)) {
     const size_t rows = (size_t)(L.ntdp_cap > 0 ? L.ntdp_cap : 1);
     L.xs = L.cs;  // after the descriptors
-    L.xd = L.xs + align256(rows * Hv * K * V * 4);
+    L.xd = L.xs + align256(rows * Hv * gdp::bwd_state_record_bytes((int)K, (int)V));
     L.xb = L.xd + align256(rows * Hv * K * V * 4);
     L.xtotal = L.xb + align256(rows * Hv * gdp::bwd_bundle_bytes(n));
   }
@@ -895,7 +895,7 @@ int gdp_chunk_prefill_backward(const gdp_tensor *q, const gdp_tensor *k, const g
     c.ntdp_rows = L.ntdp_cap;
     c.bundle = ws + L.xb;
     c.s0 = present(initial_state) ? (const float *)initial_state->data : nullptr;
-    c.states = (float *)(ws + L.xs);
+    c.states = ws + L.xs;
     c.dstates = (float *)(ws + L.xd);
     c.dout = d_o->data; c.do_st = d_o->stride[0]; c.do_sh = d_o->stride[1];
     c.dfinal = present(d_final_state) ? (const float *)d_final_state->data : nullptr;

@@ -93,6 +93,18 @@ template <int TCM> struct Bundle {
   static_assert(BYTES % 16 == 0 && FAC % 16 == 0, "whole 16-byte segments");
 };
 
+// What the forward walk keeps of each expanded chunk and state head (the
+// "state record"): W = K S0 of the raw k rows in float32, in the accumulator
+// order of the gradient kernel's waves (wave w, row tile rt, lane, 4 rows), then
+// S0 rounded to bfloat16, row-major [K][V].  The gradient kernel reads W into
+// its registers with 16-byte loads and S0 in k-row slabs; it uses S0 only in
+// bfloat16 (its products with S0 and the decay term <D, S0>).
+template <int K, int V> struct StateRec {
+  static constexpr int WB = CH * V * 4;          // W, float32
+  static constexpr int BYTES = WB + K * V * 2;   // then S0, bfloat16
+  __device__ static int w_off(int w, int rt, int lane) { return ((w * 4 + rt) * 64 + lane) * 4; }  // floats
+};
+
 struct Geo {
   int64_t t0;  // first token of the sequence
   int row0;    // first sub-token row of the chunk, relative to the sequence
@@ -190,15 +202,6 @@ __device__ __forceinline__ void split_acc(bf16x8 &hi, bf16x8 &lo, f32x4 a0, f32x
     lo[i] = (bf16)(a0[i] - (float)h0);
     lo[4 + i] = (bf16)(a1[i] - (float)h1);
   }
-}
-__device__ __forceinline__ bf16x8 hi_acc(f32x4 a0, f32x4 a1) {
-  bf16x8 h;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = (bf16)a0[i];
-    h[4 + i] = (bf16)a1[i];
-  }
-  return h;
 }
 __device__ __forceinline__ uint2 pack4(f32x4 x) {
   bf16x4 h = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
@@ -526,6 +529,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
   constexpr int NW = V / 16, NTH = 64 * NW, KT = K / 16, KS = K / 32;
   using S = FwdSmem<K, V, TCM>;
   using B = Bundle<TCM>;
+  using SR = StateRec<K, V>;
   constexpr int LDK = S::LDK, LDV = S::LDV;
   __shared__ __attribute__((aligned(16))) S sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -561,14 +565,15 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
   const float *fac = (const float *)(sm.bundle + B::FAC);
   for (int e = 0; e < nexp; ++e) {
     if (e + 1 < nexp) st.load(a, chunk_geo(t0, nsub, a.n, e + 1), p0 + e + 1, h, hk, tid);
+    char *rec = (char *)a.states + ((size_t)(p0 + e) * a.Hv + h) * SR::BYTES;
     {
-      float *dst = (float *)a.states + ((size_t)(p0 + e) * a.Hv + h) * KV;
+      bf16 *dst = (bf16 *)(rec + SR::WB);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * kt + 4 * lg + i) * V + col] = Sa[kt][i];
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * kt + 4 * lg + i) * V + col] = (bf16)Sa[kt][i];
     }
-    // W = K S (S split), then Ut = beta (V - Gamma rk W)
+    // W = K S (S split), stored, then Ut = beta (V - Gamma rk W)
     f32x4 X[4];
     {
       bf16x8 Sh[KS], Sl[KS];
@@ -583,6 +588,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_state_kernel(BwdChunkArgs a)
           X[rt] = mma(kf, Sh[s], X[rt]);
           X[rt] = mma(kf, Sl[s], X[rt]);
         }
+        *(f32x4 *)((float *)rec + SR::w_off(w, rt, lane)) = X[rt];
         const bf16x4 vv = tr4(sm.v, LDV, 16 * rt + 4 * lg, 16 * w, lr);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -896,6 +902,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   constexpr int NKW = (KT + NW - 1) / NW;
   using L = GradLds<K, V, TCM>;
   using B = Bundle<TCM>;
+  using SR = StateRec<K, V>;
   constexpr int LDK = L::LDK, LDO = L::LDO, LDV = L::LDV, LDP = B::LDP, LDW = L::LDW;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   bf16 *sk = (bf16 *)(smem + L::K_), *sq = (bf16 *)(smem + L::Q_), *so = (bf16 *)(smem + L::O_);
@@ -923,10 +930,10 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   const size_t KV = (size_t)K * V;
   int lane = tid & 63, lr = lane & 15, lg = lane >> 4, col = 16 * w + lr;
 
-  // head-dependent operands: S0 and D slabs (this wave's 16 columns, accumulator
-  // layout) in registers; dO rows, v rows, bundle (and k rows when not shared)
-  // staged through registers into LDS
-  f32x4 Sa[KT], Da[KT];
+  // head-dependent operands: W = K S0 and the D slab (this wave's 16 columns,
+  // accumulator layout) in registers; dO rows, v rows, bundle (and k rows when
+  // not shared) staged through registers into LDS
+  f32x4 Wa[4], Da[KT];
   TileRegs<CH, K, NTH> kr;
   TileRegs<TCM, V, NTH> orr;
   TileRegs<CH, V, NTH> vr;
@@ -937,15 +944,14 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
     orr.load((const bf16 *)a.dout + h * a.do_sh + qrow0 * a.do_st, a.do_st, g.Tc, tid);
     br.load(a.bundle + ((size_t)p * a.Hv + h) * B::BYTES, tid);
     vr.load((const bf16 *)a.v + h * a.v_sh + krow0 * a.v_st, a.v_st, g.R, tid);
-    const float *S0g = a.states + ((size_t)p * a.Hv + h) * KV + (size_t)(4 * lg) * V + col;
+    const float *Wg = (const float *)((const char *)a.states + ((size_t)p * a.Hv + h) * SR::BYTES);
     const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV + (size_t)(4 * lg) * V + col;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Wa[rt] = *(const f32x4 *)(Wg + SR::w_off(w, rt, lane));
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Sa[kt][i] = S0g[(16 * kt + i) * V];
-        Da[kt][i] = Dg[(16 * kt + i) * V];
-      }
+      for (int i = 0; i < 4; ++i) Da[kt][i] = Dg[(16 * kt + i) * V];
   };
   auto commit_head = [&](bool with_k) {
     if (with_k) kr.template store<LDK>(sk, g.R, tid);
@@ -984,22 +990,10 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
     lr = lane & 15;
     lg = lane >> 4;
     col = 16 * w + lr;
-    const float *S0g = a.states + ((size_t)p * a.Hv + h) * KV;
+    const bf16 *S0g = (const bf16 *)((const char *)a.states + ((size_t)p * a.Hv + h) * SR::BYTES + SR::WB);
     const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV;
     __syncthreads();  // this head's rows, bundle and zeroed partial sums are in LDS
 
-    // <D, S0>
-    {
-      float x = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x += Da[kt][i] * Sa[kt][i];
-      x = row_sum16(x);
-      x = __shfl(x, 15, 16);
-      x = col_sum4(x);
-      if (lane == 0) atomicAdd(red + R_DS * CH, x);
-    }
     // Abar (strictly lower) from the Gram tiles of the raw rows
     for (int idx = w; idx < 10; idx += NW) {
       const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
@@ -1017,23 +1011,18 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
                                                 : 0.f;
       }
     }
-    // W = K S0 (S0 hi), X = K D (D split)
-    f32x4 W[4], X[4];
+    // W = K S0 from the forward walk; X = K D (D split)
+    f32x4 *W = Wa, X[4];
     {
-      bf16x8 Sh[KS], Dh[KS], Dl[KS];
+      bf16x8 Dh[KS], Dl[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        Sh[s] = hi_acc(Sa[2 * s], Sa[2 * s + 1]);
-        split_acc(Dh[s], Dl[s], Da[2 * s], Da[2 * s + 1]);
-      }
+      for (int s = 0; s < KS; ++s) split_acc(Dh[s], Dl[s], Da[2 * s], Da[2 * s + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        W[rt] = zero4();
         X[rt] = zero4();
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const bf16x8 kf = ld_perm(sk, LDK, 16 * rt + lr, 32 * s, lg);
-          W[rt] = mma(kf, Sh[s], W[rt]);
           X[rt] = mma(kf, Dh[s], X[rt]);
           X[rt] = mma(kf, Dl[s], X[rt]);
         }
@@ -1220,14 +1209,13 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       const int kt = w + m * NW;
       if (kt >= KT) continue;
       const int kc = 16 * kt + lr;
-      // the S0 and D rows of this k tile (L2 hits: the V slabs were just read),
-      // all issued before the first product
-      f32x4 Ks[VS][2], Kd[VS][2];
+      // the S0 and D rows of this k tile, all issued before the first product
+      bf16x8 Ks[VS];
+      f32x4 Kd[VS][2];
 #pragma unroll
       for (int s = 0; s < VS; ++s) {
-        const float *ps = S0g + (size_t)kc * V + 32 * s + 8 * lg, *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
-        Ks[s][0] = *(const f32x4 *)ps;
-        Ks[s][1] = *(const f32x4 *)(ps + 4);
+        const float *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
+        Ks[s] = *(const bf16x8 *)(S0g + (size_t)kc * V + 32 * s + 8 * lg);
         Kd[s][0] = *(const f32x4 *)pd;
         Kd[s][1] = *(const f32x4 *)(pd + 4);
       }
@@ -1236,9 +1224,12 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       for (int rt = 0; rt < 4; ++rt) k1[rt] = k2[rt] = zero4();
 #pragma unroll
       for (int ta = 0; ta < TT16; ++ta) q1[ta] = zero4();
+      float ds = 0.f;  // this lane's part of <D, S0>
 #pragma unroll
       for (int s = 0; s < VS; ++s) {
-        const bf16x8 sh = hi_acc(Ks[s][0], Ks[s][1]);
+        const bf16x8 sh = Ks[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds += Kd[s][0][i] * (float)sh[i] + Kd[s][1][i] * (float)sh[4 + i];
         bf16x8 dh, dl;
         split_acc(dh, dl, Kd[s][0], Kd[s][1]);
 #pragma unroll
@@ -1252,6 +1243,10 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
 #pragma unroll
         for (int ta = 0; ta < TT16; ++ta) q1[ta] = mma(ld_contig(so, LDO, 16 * ta + lr, 32 * s, lg), sh, q1[ta]);
       }
+      ds = row_sum16(ds);
+      ds = __shfl(ds, 15, 16);
+      ds = col_sum4(ds);
+      if (lane == 0) atomicAdd(red + R_DS * CH, ds);
       const float g2e = fac[F_G2 * CH + CH - 1];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -1409,6 +1404,8 @@ template <int K, int V> hipError_t launch_k(const BwdChunkArgs &a, hipStream_t s
 }  // namespace
 
 size_t bwd_bundle_bytes(int n) { return n == 1 ? (size_t)Bundle<64>::BYTES : (size_t)Bundle<32>::BYTES; }
+
+size_t bwd_state_record_bytes(int K, int V) { return (size_t)CH * V * 4 + (size_t)K * V * 2; }
 
 bool bwd_chunked_supported(int dtype, int K, int V, int n) {
   return dtype == IN_BF16 && (K == 64 || K == 128) && (V == 64 || V == 128) && n >= 1 && n <= 64;

@@ -192,13 +192,14 @@ struct BwdChunkArgs {
   int64_t ntdp_rows;
   char *bundle;                             // [ntdp_rows, Hv] x bwd_bundle_bytes(n): prep output
   const float *s0;                          // [N, Hv, K, V] initial states or null
-  float *states;                            // [ntdp_rows, Hv, K, V] state entering each expanded chunk
+  char *states;                             // [ntdp_rows, Hv] x bwd_state_record_bytes(K, V): W = K S0 and
+                                            // S0 (bf16) of the state entering each expanded chunk
   float *dstates;                           // [ntdp_rows, Hv, K, V] dL/d(state leaving each expanded chunk)
   const void *dout; int64_t do_st, do_sh;   // [T, Hv, V]
   const float *dfinal;                      // [N, Hv, K, V] or null
   float *ds0;                               // [N, Hv, K, V] or null
-  // outputs (float32): dq and dk accumulate into zeroed buffers (the gradients by
-  // the normalised rows when the in-kernel norm is on); dv, dg, dbeta are stored
+  // outputs (float32), each entry inside the sequences stored once (dq and dk
+  // through the L2-norm gradient when the in-kernel norm is on)
   float *dq; int64_t dq_st, dq_sh;
   float *dk; int64_t dk_st, dk_sh;
   float *dv; int64_t dv_st, dv_sh;
@@ -206,6 +207,7 @@ struct BwdChunkArgs {
   float *dbeta; int64_t db_st, db_sh;
 };
 size_t bwd_bundle_bytes(int n);
+size_t bwd_state_record_bytes(int K, int V);
 bool bwd_chunked_supported(int dtype, int K, int V, int n);
 hipError_t launch_bwd_chunked(const BwdChunkArgs &a, int K, int V, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, int dtype, int K, int V, hipStream_t stream);
