@@ -938,12 +938,14 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   TileRegs<TCM, V, NTH> orr;
   TileRegs<CH, V, NTH> vr;
   BlockRegs<B::BYTES, NTH> br;
-  auto load_head = [&](int h, bool with_k) {
+  auto load_rows = [&](int h, bool with_k) {
     const int hk = h / (a.Hv / a.Hk);
     if (with_k) kr.load((const bf16 *)a.k + hk * a.k_sh + krow0 * a.k_st, a.k_st, g.R, tid);
     orr.load((const bf16 *)a.dout + h * a.do_sh + qrow0 * a.do_st, a.do_st, g.Tc, tid);
     br.load(a.bundle + ((size_t)p * a.Hv + h) * B::BYTES, tid);
     vr.load((const bf16 *)a.v + h * a.v_sh + krow0 * a.v_st, a.v_st, g.R, tid);
+  };
+  auto load_slabs = [&](int h) {
     const float *Wg = (const float *)((const char *)a.states + ((size_t)p * a.Hv + h) * SR::BYTES);
     const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV + (size_t)(4 * lg) * V + col;
 #pragma unroll
@@ -964,7 +966,8 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
   {
     TileRegs<TCM, K, NTH> qr;
     qr.load((const bf16 *)a.q + hq * a.q_sh + qrow0 * a.q_st, a.q_st, g.Tc, tid);
-    load_head(hq * G, true);
+    load_rows(hq * G, true);
+    load_slabs(hq * G);
     qr.template store<LDK>(sq, g.Tc, tid);
     commit_head(true);
     if (tid < CH) red[R_QN * CH + tid] = 0.f;
@@ -1111,6 +1114,10 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       slots[(R_DL * NW + w) * CH + prow] = -fexp2(fac[F_G2 * CH + prow]) * fac[F_BETA * CH + prow] *
                                            fac[F_RK * CH + prow] * rowsum_scatter(xw, lr);
     }
+    // the next head's W and D slabs (this head's are dead); its rows follow
+    // at the end of the head, when fewer registers are live
+    const bool more = j + 1 < G;
+    if (more) load_slabs(h + 1);
     __syncthreads();  // every wave is done with the T^T planes and the v rows
     // the per-wave row partials (dbeta, decay, xe) summed over the waves
     if (tid < 3 * CH) {
@@ -1331,9 +1338,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
 #pragma unroll
         for (int s = 0; s < 2; ++s) dQ[m][ta] = mma(tr_contig(pw2, LDW, 32 * s, 16 * ta, lr, lg), kb[s], dQ[m][ta]);
     }
-    // the next head's slabs and rows
-    const bool more = j + 1 < G;
-    if (more) load_head(h + 1, !kshared);
+    if (more) load_rows(h + 1, !kshared);
     // this head's decay gradients (suffix sums from each token's first row) and dbeta
     if (w == 0) {
       const int r = lane;
