@@ -1413,10 +1413,24 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         }
       }
       // R = diag(beta) (V + Y) with Y = -lam diag(2^G rk) X; the beta sits in the
-      // WY matrix (T diag(beta)) and V enters the E product as it is, so only Y
-      // is formed here, in bf16
+      // WY matrix (T diag(beta)), so V + Y is formed here in fp32 and rounded to
+      // bf16 once (the residual of the delta rule, often much smaller than V or
+      // Y), which halves the E product after the barrier.  The chunk's v rows
+      // landed before the last barrier.  V + Y is read in the slot order of
+      // two stacked accumulator tiles (the B operand's "perm" order).
       Frag<bf16> Yb[2][NB];
       {
+        Frag<bf16> vfr[2][NB];
+        if constexpr (!MP) {
+          const uint32_t vb = off_of(sm.v[ts]) + lcolv.l;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const uint32_t va = (lcolv.x ^ (uint32_t)(2 * wcol + 32 * b)) + vb;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              vfr[s][b].v = __builtin_shufflevector(tr8(va + 32 * s * VW), tr8(va + (32 * s + 16) * VW), 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
         const float *cf = sm.c1[ts];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
@@ -1427,13 +1441,23 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) from_acc(Yb[s][b], X[2 * s][b], X[2 * s + 1][b]);
+          for (int b = 0; b < NB; ++b) {
+            if constexpr (MP) {  // zero values
+              from_acc(Yb[s][b], X[2 * s][b], X[2 * s + 1][b]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                Yb[s][b].v[i] = (bf16)(X[2 * s][b][i] + (float)vfr[s][b].v[i]);
+                Yb[s][b].v[4 + i] = (bf16)(X[2 * s + 1][b][i] + (float)vfr[s][b].v[4 + i]);
+              }
+            }
+          }
       }
       lds_barrier();  // P complete
       // ---- phase B: E = T R, O^T += E^T P^T, state update, outputs
       // fragments of T diag(beta) (A operand, from its transpose through the
-      // transposing read) and of V (B operand, rows in the order of Y's slots)
-      Frag<bf16> tfr[6], vfr[2][NB];
+      // transposing read)
+      Frag<bf16> tfr[6];
       {
         const uint32_t tb = off_of(sm.t) + lt;
 #pragma unroll
@@ -1442,33 +1466,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           tfr[fi].v = __builtin_shufflevector(tr8(tb + (32 * s * LDT + 16 * a4) * 2), tr8(tb + ((32 * s + 16) * LDT + 16 * a4) * 2),
                                               0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const uint32_t vb = off_of(sm.v[ts]) + lcolv.l;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if constexpr (MP) continue;  // zero values
-          const uint32_t va = (lcolv.x ^ (uint32_t)(2 * wcol + 32 * b)) + vb;
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            vfr[s][b].v = __builtin_shufflevector(tr8(va + 32 * s * VW), tr8(va + (32 * s + 16) * VW), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 E[4][NB];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const Frag<bf16> &t0f = tfr[a4 < 2 ? a4 : 2 * a4 - 2];
-          f32x4 acc = MP ? zero4() : mma(t0f, vfr[0][b], zero4());
-          acc = mma(t0f, Yb[0][b], acc);
-          if (a4 >= 2) {
-            if constexpr (!MP) acc = mma(tfr[2 * a4 - 1], vfr[1][b], acc);
-            acc = mma(tfr[2 * a4 - 1], Yb[1][b], acc);
-          }
-          E[a4][b] = acc;
-        }
-      // while E forms: the P fragments of the first token block and the k^T
-      // fragments of the first state row block
+      // the P fragments of the first token block and the k^T fragments of the
+      // first state row block
       // first token of each 32-row half (with LT the rows 32 s.. hold tokens 16 s..)
       const int tokb0 = (SUM || LT) ? 0 : tokr[0], tokb1 = SUM ? 0 : (LT ? 16 : tokr[32]);
       Frag<bf16> pf[2][2];
@@ -1478,7 +1478,6 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         for (int s = 0; s < 2; ++s)
           pf[buf][s].v = rd16(pr + (16 * a4 * LDC + 32 * s) * 2);
       };
-      if constexpr (!SUM) load_pf(0, 0);
       const uint32_t kcb = kt + lcolk.l;
       Frag<bf16> kc[2][2];
       auto load_kc = [&](int at, int buf) {  // lane lr of tile at: key kap(at, lr / 4, lr % 4)
@@ -1487,6 +1486,18 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         for (int h2 = 0; h2 < 2; ++h2)
           kc[buf][h2].v = __builtin_shufflevector(tr8(x + 32 * h2 * KW), tr8(x + (32 * h2 + 16) * KW), 0, 1, 2, 3, 4, 5, 6, 7);
       };
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 E[4][NB];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          f32x4 acc = mma(tfr[a4 < 2 ? a4 : 2 * a4 - 2], Yb[0][b], zero4());
+          if (a4 >= 2) acc = mma(tfr[2 * a4 - 1], Yb[1][b], acc);
+          E[a4][b] = acc;
+        }
+      // (read while E forms)
+      if constexpr (!SUM) load_pf(0, 0);
       load_kc(0, 0);
       __builtin_amdgcn_sched_barrier(0);
       // E: the v_new rows, or (chunks whose WY matrix carries the state-update
