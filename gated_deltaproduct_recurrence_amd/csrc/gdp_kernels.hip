@@ -1928,22 +1928,27 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     }
     // Work per helper and chunk e = (token chunk c, sub-chunk j) (WY stages for
     // chunk e+1), before || after the mid-chunk barrier:
-    //   helper 0: k rows and betas/decays of chunk e+2   || v rows of chunk e+1,
-    //                                                       q rows of token chunk c+2
-    //   helper 1: merge stage                            || scale scalars and row
-    //                                                       block 3 of chunk e+1
-    //   helper 2: Gram tiles 0-4, masked betas and decay || row blocks 0, 1
-    //             cumsum of chunk e+1, and at j = n-1 the
+    //   helper 0: k rows and betas/decays of chunk e+2,  || q rows of token chunk c+2
+    //             v rows of chunk e+1                       (per-expanded-chunk outputs:
+    //                                                       first the scale scalars and
+    //                                                       row block 0 of chunk e+1)
+    //   helper 1: merge stage                            || row block 3 of chunk e+1
+    //                                                       (and otherwise the scale
+    //                                                       scalars)
+    //   helper 2: Gram tiles 0-4, masked betas and decay || row block 1 (and otherwise
+    //             cumsum of chunk e+1, and at j = n-1 the     row block 0)
     //             q norms and token decay cumsum of token
     //             chunk c+1
     //   helper 3: Gram tiles 5-9                         || row block 2, row tables
     //                                                       of chunk e+1
-    // Helper 0 issues every direct-to-LDS load and never touches LDS: the
-    // compiler makes any LDS access that follows such a load in the same wave
-    // wait for it, which would stall that wave on HBM latency.  The q rows of
-    // token chunk c+1 are issued at the end of token chunk c-1 and read at its
-    // sub-chunk n-1: for n >= 2 they are waited for only with the next chunk's
-    // loads.
+    // Each row block inverts its diagonal block by a dependent chain of DPP
+    // steps, which makes two of them on one wave the longest helper phase.
+    // Helper 0 issues every direct-to-LDS load; the compiler makes any LDS
+    // access that follows such a load in the same wave wait for it, so its
+    // own LDS work comes after the barrier that follows its phase-A loads and
+    // before the q loads.  The q rows of token chunk c+1 are issued at the end
+    // of token chunk c-1 and read at its sub-chunk n-1: for n >= 2 they are
+    // waited for only with the next chunk's loads.
     // Each helper runs its own loop (the same barrier sequence as the consumers:
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
@@ -1970,6 +1975,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       };
       const TileOffs<KW, 1> koffs = tile_offs<KW, 1>(kst, lane), qoffs = tile_offs<KW, 1>(qst, lane);
       const TileOffs<VW> voffs = tile_offs<VW>(vst, lane);
+      float lam_h = 1.f;    // (LT) the lazy state scale, tracked as the consumers apply it
+      bool fast_h = false;
       if (nexp > 0) {
         load_k(0, koffs);
         if (nexp > 1) load_k(1, koffs);
@@ -1983,6 +1990,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         wait_vm();
         lds_barrier();
         lds_barrier();
+        if constexpr (LT) {
+          scalars(0, lam_h, fast_h);
+          block(0, IC<0>{});
+        }
         lds_barrier();
       }
       for (int e = 0; e < nexp; ++e) {
@@ -1990,20 +2001,29 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         const int j = e - c * n;
         asm volatile("" : "+v"(hl));
         // phase A: k rows and scalars of chunk e+2 (the Gram stage reads them in
-        // chunk e+1)
+        // chunk e+1), and v rows of chunk e+1 into the slot of chunk e-1 (the
+        // consumers read v before the mid-chunk barrier)
         if (e + 2 < nexp) {
           load_k(e + 2, koffs);
           load_scalars(e + 2);
         }
-        lds_barrier();
-        // phase B.  The v tile of chunk e-1 and, after the last expanded chunk
-        // of token chunk c, its q tile are free: refill
-        // them with chunk e+1 and token chunk c+2, then wait for everything but
-        // the q rows when n >= 2 (they are read at the end of token chunk c+1; a
-        // later wait for newer loads covers them): the consumers read the v rows
-        // after the next barrier and the Gram stage the k rows of chunk e+2.
-        const bool lq = !SUM && j == n - 1 && c + 2 < ntc;
         if (e + 1 < nexp) load_v(e + 1, voffs);
+        lds_barrier();
+        // phase B.  With per-expanded-chunk outputs the loader also takes the
+        // scale scalars and row block 0 of chunk e+1 (its first LDS access waits
+        // for the loads of phase A, which the next phase needs anyway).  After
+        // the last expanded chunk of token chunk c its q tile is free: refill it
+        // with token chunk c+2, then wait for everything but the q rows when
+        // n >= 2 (they are read at the end of token chunk c+1; a later wait for
+        // newer loads covers them): the consumers read the v rows and the Gram
+        // stage the k rows of chunk e+2 after the next barrier.
+        if constexpr (LT) {
+          if (e + 1 < nexp) {
+            scalars(e + 1, lam_h, fast_h);
+            block(e + 1, IC<0>{});
+          }
+        }
+        const bool lq = !SUM && j == n - 1 && c + 2 < ntc;
         if (lq) load_q(c + 2, qoffs);
         if (lq && n >= 2) {
           wait_vm_keep<NLQ>();
@@ -2020,7 +2040,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       if (nexp > 0) {
         lds_barrier();
         lds_barrier();
-        scalars(0, lam_h, fast_h);
+        if constexpr (!LT) scalars(0, lam_h, fast_h);
         block(0, IC<3>{});
         lds_barrier();
       }
@@ -2028,7 +2048,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         merge(e);
         lds_barrier();
         if (e + 1 < nexp) {
-          scalars(e + 1, lam_h, fast_h);
+          if constexpr (!LT) scalars(e + 1, lam_h, fast_h);
           block(e + 1, IC<3>{});
         }
         lds_barrier();
@@ -2040,7 +2060,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         if constexpr (!SUM && !LT) finish_q(0);
         gram(0, 0, 5, 3);
         lds_barrier();
-        block(0, IC<0>{});
+        if constexpr (!LT) block(0, IC<0>{});
         block(0, IC<1>{});
         lds_barrier();
       }
@@ -2057,7 +2077,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         if (!SUM && !LT && j == n - 1 && c + 1 < ntc) finish_q(c + 1);
         lds_barrier();
         if (e + 1 < nexp) {
-          block(e + 1, IC<0>{});
+          if constexpr (!LT) block(e + 1, IC<0>{});
           block(e + 1, IC<1>{});
         }
         lds_barrier();
