@@ -1028,7 +1028,7 @@ template <int K, int V> struct FusedSmem {
                             // an MFMA operand are one 16-byte read
   float gram[10][64 * 4];   // Gram tiles of the next chunk, lane order; the diagonal
                             // ones are then reused for the rows of -L
-  bf16 alow[6][64 * 4];     // A below the diagonal blocks (A-operand layout, lane order)
+  bf16 alow[6][256];        // A below the diagonal blocks, row-major 16 x 16
   bf16 tdiag[4][64 * 4];    // diagonal blocks of T (A-operand layout, lane order)
   bf16 tdrow[4][256];       // diagonal blocks of T, row-major
   float rawb[2][CH], rawg[2][CH];          // raw betas / decays
@@ -1227,6 +1227,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         // step s multiplies
         Frag<bf16> kf[4], qf[2][2];
         float qs2[2] = {0.f, 0.f};
+        // token block 0 meets row blocks 0-1 only: the wave holding its row
+        // blocks 2-3 forms no score tiles (O += E P^T never reads them)
+        const bool ptiles = !(tb == 0 && rb0 >= 2);
         auto load_kf = [&](int s, int a4) {
           const uint32_t xs = lcont.x ^ (uint32_t)(64 * s);
           kf[a4].v = rd16(xs + (kt + lcont.l) + 16 * a4 * KW);
@@ -1251,7 +1254,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) X[a4][b] = mma(kf[a4], Sb[b], s == 0 ? zero4() : X[a4][b]);
-            if (a4 >= rb0 && a4 < rb0 + RBW) Pacc[a4 - rb0] = mma(kf[a4], qw, s == 0 ? zero4() : Pacc[a4 - rb0]);
+            if (ptiles && a4 >= rb0 && a4 < rb0 + RBW) Pacc[a4 - rb0] = mma(kf[a4], qw, s == 0 ? zero4() : Pacc[a4 - rb0]);
             if (s + 1 < KS) load_kf(s + 1, a4);
           }
 #pragma unroll
@@ -1361,7 +1364,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       // When the token chunk's decay cumsum stays above -100 the decay factor is
       // the product qfac_t rkg_r of per-token and per-row factors (both finite and
       // normal); otherwise it is formed per entry.
-      if constexpr (!SUM) {
+      if (!SUM && !(LT && tb == 0 && rb0 >= 2)) {
         const int t = 16 * tb + lr;  // (with LT: the token inside the expanded chunk)
         const int rlim = LT ? 2 * (t + 1) : n * (t + 1) - CH * j;
         const bool fact = !LT && sm.qsafe[qs] != 0;
@@ -1837,7 +1840,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = fr * rc[i] * fexp2(gr - gc[i]) * g[i];
         if (b < hb) {
-          *(bf16x4 *)(sm.alow[idx - hb] + 4 * lane) = bf4(v);  // idx - hb enumerates (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+          *(bf16x4 *)(sm.alow[idx - hb] + lr * 16 + 4 * lg) = bf4(v);  // idx - hb enumerates (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
         } else {  // rows of -L of the diagonal block over the Gram tile just read: the
                   // 16-byte piece q of row lr at lr * 64 + 16 (q ^ (lr / 4 mod 4)), so that
                   // 16 lanes writing one piece of 16 rows meet distinct banks
@@ -1868,14 +1871,17 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         sm.wgt[x & 1][r] = fexp2(glast - gr) * rk[r];
       }
     };
-    // merge stage of chunk x: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb below the
-    // diagonal, and (T diag(beta))^T into the consumers' buffer (entry (r, c) of
-    // T diag(beta) at [c * LDT + r])
+    // merge stage of chunk x: the blocks of T below the diagonal, and (T diag(beta))^T
+    // into the consumers' buffer (entry (r, c) of T diag(beta) at [c * LDT + r]).
+    // With D = diag(T_aa) and A_off the blocks of A below the diagonal,
+    // I + A = D^-1 (I + N) with N = D A_off, so T_ab = -sum_{c=b}^{a-1} N_ac T_cb:
+    // the six N_ab are independent products, and the substitution that follows
+    // is three products deep (T_10, then T_20, then T_30) instead of six.
     auto merge = [&](int x) {
       bf16 *tt = sm.t;
       const int tsw = 8 * ((lr >> 3) & 1);  // the T^T swizzle of this lane's rows
       // every input is read first, so that the merge waits for one LDS round trip
-      bf16x4 tc[4], tn[4], al[6];
+      bf16x4 tc[4], td[4], ab[6];
       float bcol[4];  // beta of the column this lane writes in each column block
       f32x4 w4[4];    // state-update weights of rows 16 ra + 4 lg + i
 #pragma unroll
@@ -1886,11 +1892,11 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       const int fl = sm.sflag[x & 1];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        tc[b] = tr_col4(sm.tdrow[b], 16, 4 * lg, 0, lr);  // T_b[4lg + i][lr]
-        tn[b] = -*(const bf16x4 *)(sm.tdiag[b] + 4 * lane);
+        tc[b] = tr_col4(sm.tdrow[b], 16, 4 * lg, 0, lr);      // T_b[4lg + i][lr] (B operand)
+        td[b] = *(const bf16x4 *)(sm.tdiag[b] + 4 * lane);    // T_b[lr][4lg + i]
       }
 #pragma unroll
-      for (int i = 0; i < 6; ++i) al[i] = *(const bf16x4 *)(sm.alow[i] + 4 * lane);
+      for (int i = 0; i < 6; ++i) ab[i] = tr_col4(sm.alow[i], 16, 4 * lg, 0, lr);  // A_blk[4lg + i][lr]
       // on SF_TF chunks the rows are scaled by the state-update weights f = w rl,
       // which makes the consumers' product E_w = diag(f) E directly
       const bool tf = __builtin_amdgcn_readfirstlane(fl) & SF_TF;
@@ -1907,15 +1913,20 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
         *(bf16x4 *)(tt + (16 * rb + lr) * LDT + 16 * ra + ((4 * lg) ^ tsw)) = bf4(v * (frow[ra] * bcol[rb]));
         return bf4(v);
       };
+      // -N_ab = -T_aa A_ab as an A operand: the product A_ab^T T_aa^T leaves
+      // lane (lg, lr) with N_ab[lr][4lg + i]
+      auto negn = [&](int i, int a_) { return bf4(-mma16(ab[i], td[a_], zero4())); };
+      const bf16x4 n10 = negn(0, 1), n20 = negn(1, 2), n21 = negn(2, 2), n30 = negn(3, 3), n31 = negn(4, 3),
+                   n32 = negn(5, 3);
       // distance 1
-      const bf16x4 t10 = put(1, 0, mma16(tn[1], bf4(mma16(al[0], tc[0], zero4())), zero4()));
-      const bf16x4 t21 = put(2, 1, mma16(tn[2], bf4(mma16(al[2], tc[1], zero4())), zero4()));
-      put(3, 2, mma16(tn[3], bf4(mma16(al[5], tc[2], zero4())), zero4()));
+      const bf16x4 t10 = put(1, 0, mma16(n10, tc[0], zero4()));
+      const bf16x4 t21 = put(2, 1, mma16(n21, tc[1], zero4()));
+      put(3, 2, mma16(n32, tc[2], zero4()));
       // distance 2
-      const bf16x4 t20 = put(2, 0, mma16(tn[2], bf4(mma16(al[2], t10, mma16(al[1], tc[0], zero4()))), zero4()));
-      put(3, 1, mma16(tn[3], bf4(mma16(al[5], t21, mma16(al[4], tc[1], zero4()))), zero4()));
+      const bf16x4 t20 = put(2, 0, mma16(n21, t10, mma16(n20, tc[0], zero4())));
+      put(3, 1, mma16(n32, t21, mma16(n31, tc[1], zero4())));
       // distance 3
-      put(3, 0, mma16(tn[3], bf4(mma16(al[5], t20, mma16(al[4], t10, mma16(al[3], tc[0], zero4())))), zero4()));
+      put(3, 0, mma16(n32, t20, mma16(n31, t10, mma16(n30, tc[0], zero4()))));
     };
     if (hw == 0) {
       // the two T^T blocks above the diagonal that the consumers' fragments cover
