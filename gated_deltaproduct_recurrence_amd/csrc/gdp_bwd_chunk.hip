@@ -230,7 +230,12 @@ __device__ __forceinline__ float col_sum4(float x) {
 // Sums over the 16 lanes of each 16-lane row of the 16 values x[4 rt + i]
 // (rows 16 rt + 4 lg + i of an accumulator layout): a reduce-scatter over lane
 // bits 3, 2, 1, 0 that leaves lane (lg, lr) with the sum for row
-// 16 (lr >> 2) + 4 lg + (lr & 3)  (x index lr).
+// 16 (lr >> 2) + 4 lg + (lr & 3)  (x index lr).  Every exchange is a DPP move
+// inside the 16-lane row (xor 8 = row_ror:8; xor 4 from row_shl:4 / row_shr:4;
+// xor 2 and xor 1 by quad_perm), so nothing goes through the LDS.
+template <int CTRL> __device__ __forceinline__ float dppm(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float rowsum_scatter(float (&x)[16], int lr) {
   float y8[8];
   {
@@ -238,7 +243,7 @@ __device__ __forceinline__ float rowsum_scatter(float (&x)[16], int lr) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float keep = hi ? x[k + 8] : x[k], send = hi ? x[k] : x[k + 8];
-      y8[k] = keep + __shfl_xor(send, 8, 64);
+      y8[k] = keep + dppm<0x128>(send);  // row_ror:8
     }
   }
   float y4[4];
@@ -247,7 +252,8 @@ __device__ __forceinline__ float rowsum_scatter(float (&x)[16], int lr) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float keep = hi ? y8[k + 4] : y8[k], send = hi ? y8[k] : y8[k + 4];
-      y4[k] = keep + __shfl_xor(send, 4, 64);
+      const float up = dppm<0x104>(send), dn = dppm<0x114>(send);  // row_shl:4, row_shr:4
+      y4[k] = keep + (hi ? dn : up);
     }
   }
   float y2[2];
@@ -256,12 +262,12 @@ __device__ __forceinline__ float rowsum_scatter(float (&x)[16], int lr) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const float keep = hi ? y4[k + 2] : y4[k], send = hi ? y4[k] : y4[k + 2];
-      y2[k] = keep + __shfl_xor(send, 2, 64);
+      y2[k] = keep + dppm<0x4E>(send);  // quad_perm [2, 3, 0, 1]
     }
   }
   const bool hi = lr & 1;
   const float keep = hi ? y2[1] : y2[0], send = hi ? y2[0] : y2[1];
-  return keep + __shfl_xor(send, 1, 64);
+  return keep + dppm<0xB1>(send);  // quad_perm [1, 0, 3, 2]
 }
 
 // A row-major tile of ROWS rows of D bf16 columns (row stride rs elements) in
@@ -1145,6 +1151,22 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
     __syncthreads();
 
     // ---- products over V
+    // the S0 and D rows of this wave's k tiles for the dK products below, issued
+    // here so that their HBM latency passes while dA and Z are formed (every load
+    // unconditional: a wave past the last k tile reads the last one)
+    bf16x8 Ks[NKW][VS];
+    f32x4 Kd[NKW][VS][2];
+#pragma unroll
+    for (int m = 0; m < NKW; ++m) {
+      const int kc = 16 * min(w + m * NW, KT - 1) + lr;
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        const float *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
+        Ks[m][s] = *(const bf16x8 *)(S0g + (size_t)kc * V + 32 * s + 8 * lg);
+        Kd[m][s][0] = *(const f32x4 *)pd;
+        Kd[m][s][1] = *(const f32x4 *)(pd + 4);
+      }
+    }
     // dA = -dU E^T (strictly lower tiles): dbeta and decay terms, then A~ into abar
     for (int idx = w; idx < 10; idx += NW) {
       const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
@@ -1216,16 +1238,6 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       const int kt = w + m * NW;
       if (kt >= KT) continue;
       const int kc = 16 * kt + lr;
-      // the S0 and D rows of this k tile, all issued before the first product
-      bf16x8 Ks[VS];
-      f32x4 Kd[VS][2];
-#pragma unroll
-      for (int s = 0; s < VS; ++s) {
-        const float *pd = Dg + (size_t)kc * V + 32 * s + 8 * lg;
-        Ks[s] = *(const bf16x8 *)(S0g + (size_t)kc * V + 32 * s + 8 * lg);
-        Kd[s][0] = *(const f32x4 *)pd;
-        Kd[s][1] = *(const f32x4 *)(pd + 4);
-      }
       f32x4 k1[4], k2[4], q1[TT16];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) k1[rt] = k2[rt] = zero4();
@@ -1234,11 +1246,11 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       float ds = 0.f;  // this lane's part of <D, S0>
 #pragma unroll
       for (int s = 0; s < VS; ++s) {
-        const bf16x8 sh = Ks[s];
+        const bf16x8 sh = Ks[m][s];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ds += Kd[s][0][i] * (float)sh[i] + Kd[s][1][i] * (float)sh[4 + i];
+        for (int i = 0; i < 4; ++i) ds += Kd[m][s][0][i] * (float)sh[i] + Kd[m][s][1][i] * (float)sh[4 + i];
         bf16x8 dh, dl;
-        split_acc(dh, dl, Kd[s][0], Kd[s][1]);
+        split_acc(dh, dl, Kd[m][s][0], Kd[m][s][1]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           k1[rt] = mma(tr_contig(puh, LDT, 32 * s, 16 * rt, lr, lg), sh, k1[rt]);
