@@ -1201,11 +1201,15 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       if (lg == 0) atomicAdd(red + R_DL * CH + i, -csum);
     }
     // Z = dO E^T (E hi): W~ and its decay terms, kept in registers for the planes
-    constexpr int NZ = (TT16 * 4 + NW - 1) / NW;
+    // With eight waves the first two formed two dA tiles each (ten tiles): with
+    // 32 output tokens (eight Z tiles) the Z tiles go to the other six,
+    // round-robin
+    constexpr int ZW0 = (NW == 8 && TT16 == 2) ? 10 - NW : 0, NZW = NW - ZW0;
+    constexpr int NZ = (TT16 * 4 + NZW - 1) / NZW;
     f32x4 Zw[NZ];
 #pragma unroll
     for (int m = 0; m < NZ; ++m) {
-      const int idx = w + m * NW;
+      const int idx = w < ZW0 ? TT16 * 4 : (w - ZW0) + m * NZW;
       Zw[m] = zero4();
       if (idx < TT16 * 4) {
         const int ta = idx >> 2, ib = idx & 3;
@@ -1293,7 +1297,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       // W~ planes [i][t]: w1 = W~ rq_t (for W~^T Qhat), w2 = W~ rk_i (for W~ Khat)
 #pragma unroll
     for (int m = 0; m < NZ; ++m) {
-      const int idx = w + m * NW;
+      const int idx = w < ZW0 ? TT16 * 4 : (w - ZW0) + m * NZW;
       if (idx < TT16 * 4) {
         const int ta = idx >> 2, ib = idx & 3;
         const int i = 16 * ib + lr, t = 16 * ta + 4 * lg;
