@@ -220,11 +220,33 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp<0x118>(x);  // row_shr:8
   return x;
 }
-// sum over the four lanes lr, lr + 16, lr + 32, lr + 48, in every lane
+// sum over the four lanes lr, lr + 16, lr + 32, lr + 48, in every lane: the
+// gfx950 row swaps (v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap
+// the two halves), with no LDS traffic
 __device__ __forceinline__ float col_sum4(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
+  const int xi = __builtin_bit_cast(int, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  const float y = __builtin_bit_cast(float, (int)p[0]) + __builtin_bit_cast(float, (int)p[1]);
+  const int yi = __builtin_bit_cast(int, y);
+  const auto q = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return __builtin_bit_cast(float, (int)q[0]) + __builtin_bit_cast(float, (int)q[1]);
+}
+// inclusive prefix sum over the 64 lanes: shifts inside each 16-lane row, then
+// row 0's total into row 1 (and row 2's into row 3), then lane 31 into rows 2, 3
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_rows(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ float wave_prefix(float x) {
+  x += dpp<0x111>(x);            // row_shr:1
+  x += dpp<0x112>(x);            // row_shr:2
+  x += dpp<0x114>(x);            // row_shr:4
+  x += dpp<0x118>(x);            // row_shr:8
+  x += dpp_rows<0x142, 0xA>(x);  // row_bcast:15
+  x += dpp_rows<0x143, 0xC>(x);  // row_bcast:31
   return x;
+}
+__device__ __forceinline__ float lane63(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // Sums over the 16 lanes of each 16-lane row of the 16 values x[4 rt + i]
@@ -418,11 +440,7 @@ __global__ void __launch_bounds__(NTHR) gdp_bwd_prep_kernel(BwdChunkArgs a) {
         bt = a.beta[row * a.b_st + h * a.b_sh];
         if ((g.row0 + r) % n == 0) gl = a.g[(g.t0 + (g.row0 + r) / n) * a.g_st + h * a.g_sh] * LOG2E;
       }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(gl, off, 64);
-        if (lane >= off) gl += y;
-      }
+      gl = wave_prefix(gl);
       sm.g2[r] = gl;
       sm.beta[r] = bt;
     }
@@ -1266,9 +1284,7 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
 #pragma unroll
         for (int ta = 0; ta < TT16; ++ta) q1[ta] = mma(ld_contig(so, LDO, 16 * ta + lr, 32 * s, lg), sh, q1[ta]);
       }
-      ds = row_sum16(ds);
-      ds = __shfl(ds, 15, 16);
-      ds = col_sum4(ds);
+      ds = lane63(wave_prefix(ds));
       if (lane == 0) atomicAdd(red + R_DS * CH, ds);
       const float g2e = fac[F_G2 * CH + CH - 1];
 #pragma unroll
@@ -1360,18 +1376,11 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
       const int r = lane;
       const bool in = r < g.R;
       const float xe = in ? red[R_XE * CH + r] : 0.f;
-      float tot = xe;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+      const float tot = lane63(wave_prefix(xe));
       float x = in ? red[R_DL * CH + r] - xe : 0.f;
       if (r == g.R - 1) x += fac[F_META * CH] * red[R_DS * CH] + tot;
-      float pre = x;  // suffix sum: total minus the exclusive prefix
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(pre, off, 64);
-        if (lane >= off) pre += y;
-      }
-      const float suf = __shfl(pre, 63, 64) - pre + x;
+      const float pre = wave_prefix(x);  // suffix sum: total minus the exclusive prefix
+      const float suf = lane63(pre) - pre + x;
       if (in && (g.row0 + r) % n == 0) a.dg[(g.t0 + (g.row0 + r) / n) * a.dg_st + h * a.dg_sh] = suf;
       if (in) a.dbeta[(krow0 + r) * a.db_st + h * a.db_sh] = red[R_DB * CH + r];
     }
