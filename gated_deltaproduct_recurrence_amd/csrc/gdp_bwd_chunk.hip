@@ -908,7 +908,9 @@ template <int K, int V, int TCM> struct GradLds {
   static constexpr int P2_END = W2 + CH * LDW * 2;
   static constexpr int V_END = VR + CH * LDV * 2;
   static constexpr int M1 = P1_END > P2_END ? P1_END : P2_END, M2 = V_END > BU + B::BYTES ? V_END : BU + B::BYTES;
-  static constexpr int BYTES = M1 > M2 ? M1 : M2;
+  static constexpr int GR = M1 > M2 ? M1 : M2;                // fp32 [10][64 lanes][4]: raw Gram tiles,
+  static constexpr bool KEEP_GRAM = GR + 10 * 64 * 4 * 4 <= 160 * 1024;  // where they fit
+  static constexpr int BYTES = KEEP_GRAM ? GR + 10 * 64 * 4 * 4 : GR;
   static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -1021,14 +1023,23 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
     const float *Dg = a.dstates + ((size_t)p * a.Hv + h) * KV;
     __syncthreads();  // this head's rows, bundle and zeroed partial sums are in LDS
 
-    // Abar (strictly lower) from the Gram tiles of the raw rows
+    // Abar (strictly lower) from the Gram tiles of the raw rows.  When the group's
+    // state heads share the k rows, the tiles of the first head are kept (each by
+    // the lane that formed it, so no barrier is needed) and the later heads only
+    // rescale them.
     for (int idx = w; idx < 10; idx += NW) {
       const int ra = idx < 1 ? 0 : (idx < 3 ? 1 : (idx < 6 ? 2 : 3));
       const int rb = idx - ra * (ra + 1) / 2;
       f32x4 acc = zero4();
+      f32x4 *gsave = (f32x4 *)(smem + L::GR) + idx * 64 + lane;
+      if (!L::KEEP_GRAM || j == 0 || !kshared) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = mma(ld_contig(sk, LDK, 16 * ra + lr, 32 * s, lg), ld_contig(sk, LDK, 16 * rb + lr, 32 * s, lg), acc);
+        for (int s = 0; s < KS; ++s)
+          acc = mma(ld_contig(sk, LDK, 16 * ra + lr, 32 * s, lg), ld_contig(sk, LDK, 16 * rb + lr, 32 * s, lg), acc);
+        if (L::KEEP_GRAM && kshared) *gsave = acc;
+      } else {
+        acc = *gsave;
+      }
       const int i = 16 * rb + lr;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -1309,6 +1320,9 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
           dQ[m][ta][jj] += fac[F_EP * CH + t] * q1[ta][jj];
         }
     }
+    // the next head's rows, bundle (and k rows when not shared), in registers
+    // until the end of this head
+    if (more) load_rows(h + 1, !kshared);
     __syncthreads();  // E/dU planes dead; abar holds A~
       // W~ planes [i][t]: w1 = W~ rq_t (for W~^T Qhat), w2 = W~ rk_i (for W~ Khat)
 #pragma unroll
@@ -1370,7 +1384,6 @@ __global__ void __launch_bounds__(V * 4, 1) gdp_bwd_grad_kernel(BwdChunkArgs a) 
 #pragma unroll
         for (int s = 0; s < 2; ++s) dQ[m][ta] = mma(tr_contig(pw2, LDW, 32 * s, 16 * ta, lr, lg), kb[s], dQ[m][ta]);
     }
-    if (more) load_rows(h + 1, !kshared);
     // this head's decay gradients (suffix sums from each token's first row) and dbeta
     if (w == 0) {
       const int r = lane;
