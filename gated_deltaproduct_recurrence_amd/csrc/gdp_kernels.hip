@@ -2019,6 +2019,14 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           load_scalars(e + 2);
         }
         if (e + 1 < nexp) load_v(e + 1, voffs);
+        // (per-expanded-chunk outputs) q rows of token chunk c+1 at the start of
+        // token chunk c, into the slot of token chunk c-1, read last before the
+        // previous mid-chunk barrier (the prologue loaded token chunks 0 and 1):
+        // after the mid-chunk barrier the consumers' output stores then share
+        // the vector memory path with no q loads
+        if constexpr (LT) {
+          if (j == 0 && c >= 1 && c + 1 < ntc) load_q(c + 1, qoffs);
+        }
         lds_barrier();
         // phase B.  With per-expanded-chunk outputs the loader also takes the
         // scale scalars and row block 0 of chunk e+1 (its first LDS access waits
@@ -2034,7 +2042,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             block(e + 1, IC<0>{});
           }
         }
-        const bool lq = !SUM && j == n - 1 && c + 2 < ntc;
+        const bool lq = !SUM && !LT && j == n - 1 && c + 2 < ntc;
         if (lq) load_q(c + 2, qoffs);
         if (lq && n >= 2) {
           wait_vm_keep<NLQ>();
