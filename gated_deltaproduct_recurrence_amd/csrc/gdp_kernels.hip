@@ -1940,9 +1940,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // Work per helper and chunk e = (token chunk c, sub-chunk j) (WY stages for
     // chunk e+1), before || after the mid-chunk barrier:
     //   helper 0: k rows and betas/decays of chunk e+2,  || q rows of token chunk c+2
-    //             v rows of chunk e+1                       (per-expanded-chunk outputs:
-    //                                                       first the scale scalars and
-    //                                                       row block 0 of chunk e+1)
+    //             v rows of chunk e+1 (per-expanded-        (per-expanded-chunk outputs:
+    //             chunk outputs: and at j = 0 the q rows    the scale scalars and row
+    //             of token chunk c+1)                       block 0 of chunk e+1, and no
+    //                                                       loads)
     //   helper 1: merge stage                            || row block 3 of chunk e+1
     //                                                       (and otherwise the scale
     //                                                       scalars)
@@ -1956,10 +1957,12 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // steps, which makes two of them on one wave the longest helper phase.
     // Helper 0 issues every direct-to-LDS load; the compiler makes any LDS
     // access that follows such a load in the same wave wait for it, so its
-    // own LDS work comes after the barrier that follows its phase-A loads and
-    // before the q loads.  The q rows of token chunk c+1 are issued at the end
-    // of token chunk c-1 and read at its sub-chunk n-1: for n >= 2 they are
-    // waited for only with the next chunk's loads.
+    // own LDS work comes after the barrier that follows its phase-A loads.
+    // With per-expanded-chunk outputs it issues no load after the mid-chunk
+    // barrier (the consumers' output stores would queue behind them).
+    // Otherwise the q rows of token chunk c+2 are issued at the end of token
+    // chunk c, after the mid-chunk barrier: for n >= 2 they are waited for only
+    // with the next chunk's loads.
     // Each helper runs its own loop (the same barrier sequence as the consumers:
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
