@@ -990,12 +990,6 @@ __device__ __forceinline__ void scalar_load(float *dst, const float *src) {
                                    (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
 }
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations (the
-// most recently issued ones; loads complete in issue order) still in flight
-template <int N> __device__ __forceinline__ void wait_vm_keep() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 // Workgroup barrier for LDS traffic only: this wave's LDS accesses are complete
 // (lgkmcnt(0)) and no memory access moves across it, but outstanding global
 // loads and stores stay in flight (__syncthreads would wait for them, which
@@ -1958,15 +1952,13 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     // Helper 0 issues every direct-to-LDS load; the compiler makes any LDS
     // access that follows such a load in the same wave wait for it, so its
     // own LDS work comes after the barrier that follows its phase-A loads.
-    // With per-expanded-chunk outputs it issues no load after the mid-chunk
-    // barrier (the consumers' output stores would queue behind them).
-    // Otherwise the q rows of token chunk c+2 are issued at the end of token
-    // chunk c, after the mid-chunk barrier: for n >= 2 they are waited for only
-    // with the next chunk's loads.
+    // For n >= 2 it issues no load after the mid-chunk barrier (the consumers'
+    // output stores would queue behind them in the vector memory path); for
+    // n = 1 the q rows of token chunk c+2 follow that barrier, because the token
+    // decay cumsum of token chunk c+1 is formed in the next chunk's phase A.
     // Each helper runs its own loop (the same barrier sequence as the consumers:
     // three in the prologue, two per chunk) so that its registers are its own.
     if (hw == 0) {
-      constexpr int NLQ = KW / 16 + 1;  // loads per q tile and its token decays
       // Pacing inside the group of state heads sharing q/k head hq (the group
       // shares one sequence, hence one chunk count).  Every PACE_EVERY chunks,
       // at the end of a chunk whose loads have all completed (the loader waits
@@ -2022,38 +2014,30 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           load_scalars(e + 2);
         }
         if (e + 1 < nexp) load_v(e + 1, voffs);
-        // (per-expanded-chunk outputs) q rows of token chunk c+1 at the start of
-        // token chunk c, into the slot of token chunk c-1, read last before the
-        // previous mid-chunk barrier (the prologue loaded token chunks 0 and 1):
-        // after the mid-chunk barrier the consumers' output stores then share
-        // the vector memory path with no q loads
-        if constexpr (LT) {
-          if (j == 0 && c >= 1 && c + 1 < ntc) load_q(c + 1, qoffs);
-        }
+        // (n >= 2) q rows of token chunk c+1 at the start of token chunk c, into
+        // the slot of token chunk c-1, read last before the previous mid-chunk
+        // barrier (the prologue loaded token chunks 0 and 1); they land before
+        // the chunk ends, ahead of the token decay cumsum of token chunk c+1 at
+        // sub-chunk n-1.  After the mid-chunk barrier the consumers' output
+        // stores then share the vector memory path with no q loads.
+        if (!SUM && n >= 2 && j == 0 && c >= 1 && c + 1 < ntc) load_q(c + 1, qoffs);
         lds_barrier();
         // phase B.  With per-expanded-chunk outputs the loader also takes the
         // scale scalars and row block 0 of chunk e+1 (its first LDS access waits
-        // for the loads of phase A, which the next phase needs anyway).  After
-        // the last expanded chunk of token chunk c its q tile is free: refill it
-        // with token chunk c+2, then wait for everything but the q rows when
-        // n >= 2 (they are read at the end of token chunk c+1; a later wait for
-        // newer loads covers them): the consumers read the v rows and the Gram
-        // stage the k rows of chunk e+2 after the next barrier.
+        // for the loads of phase A, which the next phase needs anyway).  With
+        // n = 1 the q tile of token chunk c is free now: refill it with token
+        // chunk c+2.  Then wait for every load: the consumers read the v rows and
+        // the Gram stage the k rows of chunk e+2 after the next barrier.
         if constexpr (LT) {
           if (e + 1 < nexp) {
             scalars(e + 1, lam_h, fast_h);
             block(e + 1, IC<0>{});
           }
         }
-        const bool lq = !SUM && !LT && j == n - 1 && c + 2 < ntc;
-        if (lq) load_q(c + 2, qoffs);
-        if (lq && n >= 2) {
-          wait_vm_keep<NLQ>();
-        } else {
-          wait_vm();
-          // nothing of this wave is in flight: the polls wait for themselves only
-          if (prog && e % PACE_EVERY == 0) pace(e);
-        }
+        if (!SUM && n == 1 && c + 2 < ntc) load_q(c + 2, qoffs);
+        wait_vm();
+        // nothing of this wave is in flight: the polls wait for themselves only
+        if (prog && e % PACE_EVERY == 0) pace(e);
         lds_barrier();
       }
     } else if (hw == 1) {
