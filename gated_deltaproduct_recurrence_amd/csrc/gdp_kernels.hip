@@ -1735,7 +1735,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       const char *g = (const char *)(qg + tokbase * a.q_st);
       if (toks_of(c) == CH) tile_load_full<KW, 1>(sm.q[c & 1], g, offs);
       else tile_load<KW, 1>(sm.q[c & 1], g, qst, toks_of(c), hl);
-      scalar_load(sm.rawt[c & 1], gg + (tokbase + min(hl, toks_of(c) - 1)) * a.g_st);
+      // with n = 1 the token decays are the sub-row decays of the scalar ring
+      if (n != 1) scalar_load(sm.rawt[c & 1], gg + (tokbase + min(hl, toks_of(c) - 1)) * a.g_st);
     };
     auto tables = [&](int e) {  // token of each row of chunk e inside its token chunk, and its decay cumsum
       const int c = e / n, j = e - c * n;
@@ -1747,7 +1748,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
     };
     auto finish_q = [&](int c) {  // after load_q(c) has landed: token decay cumsum of token chunk c
       const int sl = c & 1, ntok = toks_of(c);
-      const float gt = wave_scan(hl < ntok ? sm.rawt[sl][hl] * LOG2E : 0.f);
+      // n = 1: token chunk c is chunk c, whose raw decays are in the scalar ring
+      const float raw = n == 1 ? sm.rawg[sl][hl] : sm.rawt[sl][hl];
+      const float gt = wave_scan(hl < ntok ? raw * LOG2E : 0.f);
       sm.gtok[sl][hl] = gt;
       sm.qfac[sl][hl] = a.scale * fexp2(gt);
       // the cumsum is non-increasing, so its last valid entry is its minimum
@@ -2021,27 +2024,27 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           load_scalars(e + 2);
         }
         if (e + 1 < nexp) load_v(e + 1, voffs);
-        // (n >= 2) q rows of token chunk c+1 at the start of token chunk c, into
-        // the slot of token chunk c-1, read last before the previous mid-chunk
-        // barrier (the prologue loaded token chunks 0 and 1); they land before
-        // the chunk ends, ahead of the token decay cumsum of token chunk c+1 at
-        // sub-chunk n-1.  After the mid-chunk barrier the consumers' output
-        // stores then share the vector memory path with no q loads.
-        if (!SUM && n >= 2 && j == 0 && c >= 1 && c + 1 < ntc) load_q(c + 1, qoffs);
+        // q rows of token chunk c+1 at the start of token chunk c, into the slot
+        // of token chunk c-1, read last before the previous mid-chunk barrier
+        // (the prologue loaded token chunks 0 and 1); with n >= 2 they land
+        // before the chunk ends, ahead of the token decay cumsum of token chunk
+        // c+1 at sub-chunk n-1 (with n = 1 that cumsum takes its decays from
+        // the scalar ring, loaded a chunk earlier).  After the mid-chunk barrier
+        // the consumers' output stores then share the vector memory path with
+        // no q loads.
+        if (!SUM && j == 0 && c >= 1 && c + 1 < ntc) load_q(c + 1, qoffs);
         lds_barrier();
         // phase B.  With per-expanded-chunk outputs the loader also takes the
         // scale scalars and row block 0 of chunk e+1 (its first LDS access waits
-        // for the loads of phase A, which the next phase needs anyway).  With
-        // n = 1 the q tile of token chunk c is free now: refill it with token
-        // chunk c+2.  Then wait for every load: the consumers read the v rows and
-        // the Gram stage the k rows of chunk e+2 after the next barrier.
+        // for the loads of phase A, which the next phase needs anyway).  Then
+        // wait for every load: the consumers read the v rows and q rows and the
+        // Gram stage the k rows of chunk e+2 after the next barrier.
         if constexpr (LT) {
           if (e + 1 < nexp) {
             scalars(e + 1, lam_h, fast_h);
             block(e + 1, IC<0>{});
           }
         }
-        if (!SUM && n == 1 && c + 2 < ntc) load_q(c + 2, qoffs);
         wait_vm();
         // nothing of this wave is in flight: the polls wait for themselves only
         if (prog && e % PACE_EVERY == 0) pace(e);
@@ -2085,8 +2088,8 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
           gram(e + 1, 0, 5, 3);
           prep_scalars(e + 1);
         }
-        // token chunk c+1: its q rows landed with the loads of a chunk before
-        // (n >= 2) or before the last barrier (n = 1)
+        // token chunk c+1: its token decays landed with the loads of a chunk
+        // before (the q-row loads with n >= 2, the scalar ring with n = 1)
         if (!SUM && !LT && j == n - 1 && c + 1 < ntc) finish_q(c + 1);
         lds_barrier();
         if (e + 1 < nexp) {
