@@ -1089,7 +1089,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
   const int h = (int)((chain / NVT) % a.Hv);
   const int seq = (int)(chain / ((int64_t)NVT * a.Hv));
   const int hq = h / (a.Hv / a.Hqk), hk = h / (a.Hv / a.Hk);
-  const int n = a.n;
+  const int n = LT ? LT : a.n;  // per-expanded-chunk outputs are launched for n = 2 only
 
   int64_t t0 = load_index(a.cu, a.cu_is64, seq), t1 = load_index(a.cu, a.cu_is64, seq + 1);
   t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
@@ -1165,11 +1165,15 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             for (int i = 0; i < 4; ++i) dst[kap(at, 0, i) * V + 16 * b] = lam * Sacc[at][b][i];
       }
     };
-    // token chunk 0 enters with the start state; the state entering token chunk
-    // c + 1 is stored at the end of token chunk c, after its last state update,
-    // where no load of the loader shares the vector memory path with the stores
-    // (lam Sst is unchanged by the rescale that may open the next chunk)
-    if (a.chunk_states && nexp > 0) store_chunk_state(0);
+    // With per-token-chunk outputs, token chunk 0 enters with the start state
+    // and the state entering token chunk c + 1 is stored at the end of token
+    // chunk c, after its last state update, where no load of the loader shares
+    // the vector memory path with the stores (lam Sst is unchanged by the
+    // rescale that may open the next chunk).  With per-expanded-chunk outputs
+    // it is stored at the start of each token chunk.
+    if constexpr (!LT) {
+      if (a.chunk_states && nexp > 0) store_chunk_state(0);
+    }
     // wait for the start state here: a wait placed by the compiler at its first
     // use inside the loop would also wait, every chunk, for the output stores
     wait_vm();
@@ -1211,6 +1215,25 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
       const float *rk = sm.rk[ts], *gkr = sm.gkr[ts];
       const int *tokr = sm.tokr[ts];
       // ---- phase A: X = K Sst (and at a token-chunk start O^T = Sst^T Q^T), scores, R
+      if constexpr (LT) {
+        // state entering token chunk c (written out here rather than through
+        // store_chunk_state: the call form changes this instantiation's
+        // register allocation, and it ran 3-4% slower)
+        if (j == 0 && a.chunk_states) {
+          const int64_t row = cs_row0 + c;
+          if (row >= 0 && row < a.cs_rows) {
+            uint32_t lo = (uint32_t)(8 * lg * V + gcol + lr);
+            asm volatile("" : "+v"(lo));
+            float *dst = a.chunk_states + ((size_t)row * a.Hv + h) * KV + lo;
+#pragma unroll
+            for (int at = 0; at < KT16; ++at)
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[kap(at, 0, i) * V + 16 * b] = lam * Sacc[at][b][i];
+          }
+        }
+      }
       f32x4 X[4][NB];
       // Scores, transposed, of the wave's token block tb against its row blocks:
       // lane (lg, lr) of tile pa holds Sc[r = 16 (rb0 + pa) + 4 lg + i][t = 16 tb + lr]
@@ -1639,7 +1662,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4), 1) gdp_fused_kernel(PrefillArg
             }
         }
       }
-      if (a.chunk_states && j == n - 1 && c + 1 < ntc) store_chunk_state(c + 1);
+      if constexpr (!LT) {
+        if (a.chunk_states && j == n - 1 && c + 1 < ntc) store_chunk_state(c + 1);
+      }
       lds_barrier();
     }
     float *fdst = MP ? a.msum + state_off : (a.final_state ? a.final_state + state_off : nullptr);
