@@ -74,10 +74,13 @@ def check_against_oracle(what, err, tol):
 
 
 def source_hash():
+    """Hash of the fused kernel's sources and of the compiler flags they are built with."""
+    from gated_deltaproduct_recurrence_amd import build as kbuild
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
+    h.update(" ".join(kbuild.DEVICE_FLAGS + kbuild.SOURCE_FLAGS.get("gdp_kernels.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
